@@ -1,0 +1,184 @@
+"""CPU oracle for the MoE grouped matmul -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  It is a plain, slow fp64 reference of
+what the GPU library computes and shares no code with it (the C source in
+``gmm_oracle.c`` has its own FP8 codec, quantiser and reference loops).
+
+Functions take numpy arrays (fp32 values; bf16 tensors are passed widened to
+fp32, which is exact) and return numpy arrays.  Sources are cited in
+``gmm_oracle.c``; all functions are pinned by tests/test_oracle_*.py.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "_build", "liboracle.so")
+_lib = None
+
+QBLOCK = 128
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        from . import build as _b
+        _b.build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.c_void_p
+    I = ctypes.c_int64
+    lib.oracle_e4m3_decode.restype = ctypes.c_double
+    lib.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
+    lib.oracle_e4m3_encode.restype = ctypes.c_uint8
+    lib.oracle_e4m3_encode.argtypes = [ctypes.c_float]
+    lib.oracle_e4m3_encode_array.argtypes = [P, I, P]
+    lib.oracle_quantize_lhs.argtypes = [P, I, I, P, P]
+    lib.oracle_quantize_rhs.argtypes = [P, I, I, I, P, P]
+    lib.oracle_group_offsets.restype = ctypes.c_int
+    lib.oracle_group_offsets.argtypes = [P, I, I, P]
+    lib.oracle_work_list.restype = ctypes.c_int64
+    lib.oracle_work_list.argtypes = [P, I, I, I, P, I]
+    lib.oracle_gmm_fp8.argtypes = [P, P, P, P, P, I, I, I, I, P]
+    lib.oracle_gmm_f64.argtypes = [P, P, P, I, I, I, I, P]
+    lib.oracle_tgmm_f64.argtypes = [P, P, P, I, I, I, I, P]
+    lib.oracle_dx_f64.argtypes = [P, P, P, I, I, I, I, P]
+    lib.oracle_num_threads.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _c(a, dtype):
+    a = np.ascontiguousarray(a, dtype=dtype)
+    return a, a.ctypes.data_as(ctypes.c_void_p)
+
+
+def num_threads() -> int:
+    return _load().oracle_num_threads()
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """Values (fp64) of E4M3 codes."""
+    lib = _load()
+    codes = np.asarray(codes, dtype=np.uint8)
+    lut = np.array([lib.oracle_e4m3_decode(c) for c in range(256)])
+    return lut[codes]
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """RNE, saturating E4M3 codes of fp32 values."""
+    lib = _load()
+    x, px = _c(x, np.float32)
+    out = np.empty(x.shape, dtype=np.uint8)
+    lib.oracle_e4m3_encode_array(px, x.size, out.ctypes.data_as(ctypes.c_void_p))
+    return out
+
+
+def quantize_lhs(x):
+    """1x128 quantisation of x [M,K] -> (codes uint8 [M,K], scales f32 [M,K/128])."""
+    lib = _load()
+    x, px = _c(x, np.float32)
+    M, K = x.shape
+    assert K % QBLOCK == 0
+    q = np.empty((M, K), dtype=np.uint8)
+    s = np.empty((M, K // QBLOCK), dtype=np.float32)
+    lib.oracle_quantize_lhs(px, M, K, q.ctypes.data_as(ctypes.c_void_p),
+                            s.ctypes.data_as(ctypes.c_void_p))
+    return q, s
+
+
+def quantize_rhs(w):
+    """128x128 quantisation of w [G,K,N] -> (codes [G,K,N], scales [G,K/128,N/128])."""
+    lib = _load()
+    w, pw = _c(w, np.float32)
+    G, K, N = w.shape
+    assert K % QBLOCK == 0 and N % QBLOCK == 0
+    q = np.empty((G, K, N), dtype=np.uint8)
+    s = np.empty((G, K // QBLOCK, N // QBLOCK), dtype=np.float32)
+    lib.oracle_quantize_rhs(pw, G, K, N, q.ctypes.data_as(ctypes.c_void_p),
+                            s.ctypes.data_as(ctypes.c_void_p))
+    return q, s
+
+
+def group_offsets(group_sizes, M):
+    lib = _load()
+    gs, pg = _c(group_sizes, np.int32)
+    off = np.empty(gs.size + 1, dtype=np.int64)
+    rc = lib.oracle_group_offsets(pg, gs.size, M, off.ctypes.data_as(ctypes.c_void_p))
+    if rc != 0:
+        raise ValueError("group sizes negative or summing past M")
+    return off
+
+
+def work_list(group_sizes, M, tm):
+    """(g, tile, row_lo, row_hi) entries of the grouped GEMM, int32 [n,4]."""
+    lib = _load()
+    gs, pg = _c(group_sizes, np.int32)
+    cap = -(-M // tm) + gs.size + 2
+    work = np.zeros((cap, 4), dtype=np.int32)
+    n = lib.oracle_work_list(pg, gs.size, M, tm, work.ctypes.data_as(ctypes.c_void_p), cap)
+    if n < 0:
+        raise ValueError("work list overflow")
+    return work[:n].copy()
+
+
+def gmm_fp8(ql, sl, qr, sr, group_sizes):
+    """fp64 blockwise-FP8 GMM; ql [M,K], sl [M,K/128], qr [G,K,N] (codes), sr [G,K/128,N/128]."""
+    lib = _load()
+    ql, pql = _c(ql, np.uint8)
+    sl, psl = _c(sl, np.float32)
+    qr, pqr = _c(qr, np.uint8)
+    sr, psr = _c(sr, np.float32)
+    gs, pg = _c(group_sizes, np.int32)
+    M, K = ql.shape
+    G, K2, N = qr.shape
+    assert K == K2 and gs.size == G and int(gs.sum()) <= M
+    out = np.empty((M, N), dtype=np.float64)
+    lib.oracle_gmm_fp8(pql, psl, pqr, psr, pg, M, K, N, G, out.ctypes.data_as(ctypes.c_void_p))
+    return out
+
+
+def gmm(x, w, group_sizes):
+    """fp64 GMM: out[m] = x[m] . w[g(m)]; x [M,K], w [G,K,N]."""
+    lib = _load()
+    x, px = _c(x, np.float32)
+    w, pw = _c(w, np.float32)
+    gs, pg = _c(group_sizes, np.int32)
+    M, K = x.shape
+    G, K2, N = w.shape
+    assert K == K2 and gs.size == G and int(gs.sum()) <= M
+    out = np.empty((M, N), dtype=np.float64)
+    lib.oracle_gmm_f64(px, pw, pg, M, K, N, G, out.ctypes.data_as(ctypes.c_void_p))
+    return out
+
+
+def tgmm(x, dy, group_sizes):
+    """fp64 dW[g] = X_g^T dY_g; x [M,K], dy [M,N] -> [G,K,N]."""
+    lib = _load()
+    x, px = _c(x, np.float32)
+    dy, pd = _c(dy, np.float32)
+    gs, pg = _c(group_sizes, np.int32)
+    M, K = x.shape
+    M2, N = dy.shape
+    G = gs.size
+    assert M == M2 and int(gs.sum()) <= M
+    out = np.empty((G, K, N), dtype=np.float64)
+    lib.oracle_tgmm_f64(px, pd, pg, M, K, N, G, out.ctypes.data_as(ctypes.c_void_p))
+    return out
+
+
+def gmm_dx(dy, w, group_sizes):
+    """fp64 dX[m] = dY[m] . w[g(m)]^T; dy [M,N], w [G,K,N] -> [M,K]."""
+    lib = _load()
+    dy, pd = _c(dy, np.float32)
+    w, pw = _c(w, np.float32)
+    gs, pg = _c(group_sizes, np.int32)
+    M, N = dy.shape
+    G, K, N2 = w.shape
+    assert N == N2 and gs.size == G and int(gs.sum()) <= M
+    out = np.empty((M, K), dtype=np.float64)
+    lib.oracle_dx_f64(pd, pw, pg, M, K, N, G, out.ctypes.data_as(ctypes.c_void_p))
+    return out
