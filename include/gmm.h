@@ -1,0 +1,183 @@
+/*
+ * gmm.h -- C ABI of the MI355X (gfx950) MoE grouped matrix multiply library.
+ *
+ * A grouped matmul (GMM) multiplies the rows of a token matrix that is
+ * sorted by expert by that expert's weights: rows [o_g, o_g + s_g) with
+ * o_g = s_0 + ... + s_{g-1} use W[g].  ("MoE 优化的探索：从 MiniMax-01、
+ * Comet、FlashMoE 到 DeepSeek-V4", section 3.7.2: one independent GEMM per
+ * expert, every tile carries its expert id.)
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - All tensors are dense and row-major, in device memory of the current
+ *    HIP device, and owned by the caller.  The library allocates nothing and
+ *    keeps no state between calls.
+ *  - `group_sizes` is a device array of G int32 values, read only on the
+ *    device (the host never synchronises).  Contract: every s_g >= 0 and
+ *    s_0 + ... + s_{G-1} <= M.  Rows at or past that total are written as
+ *    zeros by the calls that produce rows ("实现差距：GMM Kernel（V1 vs V2）",
+ *    section 3.6).  A total above M is outside the contract (rows past M are
+ *    never touched, results are unspecified).
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *    enqueues work on it and returns.
+ *  - Inputs must be finite.  A quantisation block whose non-zero abs-max is
+ *    below 2^-100 is outside the contract.
+ *  - Pointers must be 16-byte aligned.  Sizes are element counts.
+ *  - Errors: every argument check runs on the host before anything is
+ *    launched; on failure the call returns a non-zero gmm_status and
+ *    enqueues nothing.  A launch failure returns GMM_ERR_HIP.
+ *    gmm_last_error() returns a message for the calling thread's last
+ *    failure.
+ */
+#ifndef GMM_H_
+#define GMM_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define GMM_API __attribute__((visibility("default")))
+#else
+#define GMM_API
+#endif
+
+typedef enum {
+    GMM_OK = 0,
+    GMM_ERR_NULL = 1,      /* a required pointer is NULL */
+    GMM_ERR_SHAPE = 2,     /* a size is out of range or not a multiple of 128 */
+    GMM_ERR_ALIGN = 3,     /* a pointer is not 16-byte aligned */
+    GMM_ERR_DTYPE = 4,     /* unsupported dtype for this argument */
+    GMM_ERR_HIP = 6        /* the HIP runtime reported an error at launch */
+} gmm_status;
+
+typedef enum {
+    GMM_F32 = 0,           /* IEEE binary32 */
+    GMM_BF16 = 1,          /* bfloat16 */
+    GMM_E4M3 = 2           /* OCP FP8 E4M3 ("fn"): bias 7, max 448, 0x7F NaN */
+} gmm_dtype;
+
+/* Largest expert count accepted by the grouped calls. */
+#define GMM_MAX_GROUPS 4096
+
+GMM_API const char *gmm_status_string(int status);
+GMM_API const char *gmm_last_error(void);
+
+/*
+ * gmm_group_metadata -- the device-side work list every grouped kernel
+ * builds in its prologue, written out for inspection.
+ *   Row tiles of height tile_m are aligned to absolute row indices.  For
+ *   every non-empty group g (in order) and every tile t that intersects its
+ *   rows, one entry {g, t, row_lo, row_hi} with row_lo = max(o_g, t*tile_m)
+ *   and row_hi = min(o_g + s_g, (t+1)*tile_m); then one entry {G, t, lo, hi}
+ *   per tile holding rows at or past the total (the rows to zero).
+ *   ("GEMM Kernel 性能优化十问", Q7 names group indexing among the GMM's
+ *   costs; "实现差距：GMM Kernel（V1 vs V2）", gap table: the metadata is
+ *   filled inside the kernel.)
+ * offsets:  device int32 [G+1], exclusive prefix sums of group_sizes.
+ * work:     device int32 [capacity][4].
+ * num_work: device int32 [1], number of entries written.
+ * capacity must be >= ceil(M/tile_m) + G + 1; tile_m in {16,...,1024}, a
+ * power of two.
+ */
+GMM_API int gmm_group_metadata(const int32_t *group_sizes, int64_t G, int64_t M,
+                       int64_t tile_m, int32_t *offsets, int32_t *work,
+                       int64_t capacity, int32_t *num_work, void *stream);
+
+/*
+ * gmm_quantize_lhs -- 1x128 dynamic quantisation of the activations.
+ *   For every row m and 128-wide block b: a = max |x[m, 128b:128b+128]|,
+ *   s = a/448, inv = (s == 0 ? 0 : 1/s), q = e4m3_rne(x * inv), each step
+ *   one correctly rounded fp32 operation ("GEMM Kernel 性能优化十问", Q2:
+ *   one scale per row per 128 elements; "实现差距：GMM Kernel（V1 vs V2）",
+ *   section 3.3: abs-max, scale, guarded inverse, cast).
+ * x:     [M,K], x_dtype GMM_BF16 or GMM_F32.
+ * q:     [M,K] E4M3 codes.
+ * scale: [M,K/128] fp32, the s of each block.
+ * K must be a multiple of 128; M >= 1.
+ */
+GMM_API int gmm_quantize_lhs(const void *x, int x_dtype, int64_t M, int64_t K,
+                     uint8_t *q, float *scale, void *stream);
+
+/*
+ * gmm_quantize_rhs -- 128x128 block quantisation of the expert weights
+ * (done once, offline: "GEMM Kernel 性能优化十问", Q2 and Q5).
+ *   Same recipe as gmm_quantize_lhs over each 128x128 block (g, kb, nb).
+ * w:     [G,K,N], w_dtype GMM_BF16 or GMM_F32.
+ * q:     [G,N,K] E4M3 codes, stored K-contiguous (the transpose of w per
+ *        expert), which is the layout gmm_fp8_fwd reads.
+ * scale: [G,K/128,N/128] fp32.
+ * K and N must be multiples of 128.
+ */
+GMM_API int gmm_quantize_rhs(const void *w, int w_dtype, int64_t G, int64_t K,
+                     int64_t N, uint8_t *q, float *scale, void *stream);
+
+/*
+ * gmm_fp8_fwd -- blockwise-FP8 grouped matmul forward.
+ *   out[m,n] = sum_b ( sum_{k in block b} ql[m,k] qr[g,n,k] )
+ *                    * sl[m,b] * sr[g,b,n/128]        for m in group g,
+ *   with fp32 accumulation of exact FP8 products; rows past the total are 0.
+ *   ("GEMM Kernel 性能优化十问", Q3: each 128-wide K subchannel is scaled and
+ *   accumulated separately while the K loop runs over many subchannels;
+ *   "实现差距：GMM Kernel（V1 vs V2）", sections 2.1 and 3.3.)
+ * lhs:       [M,K].  lhs_dtype GMM_BF16 or GMM_F32: quantised inside the
+ *            kernel with the gmm_quantize_lhs recipe (bit-identical codes
+ *            and scales); GMM_E4M3: codes, with lhs_scale [M,K/128].
+ * lhs_scale: NULL unless lhs_dtype == GMM_E4M3.
+ * rhs:       [G,N,K] E4M3 codes; rhs_scale [G,K/128,N/128] fp32 (as written
+ *            by gmm_quantize_rhs).
+ * out:       [M,N], out_dtype GMM_BF16 (round to nearest even) or GMM_F32.
+ * q_out, scale_out: NULL, or [M,K] codes and [M,K/128] scales that receive
+ *            the in-kernel quantisation of lhs (only with bf16/f32 lhs).
+ * K and N must be multiples of 128; 1 <= G <= GMM_MAX_GROUPS.
+ */
+GMM_API int gmm_fp8_fwd(const void *lhs, int lhs_dtype, const float *lhs_scale,
+                const uint8_t *rhs, const float *rhs_scale,
+                const int32_t *group_sizes, int64_t M, int64_t K, int64_t N,
+                int64_t G, void *out, int out_dtype, uint8_t *q_out,
+                float *scale_out, void *stream);
+
+/*
+ * gmm_bf16_fwd -- unquantised grouped matmul (the bf16 baseline).
+ *   out[m,:] = lhs[m,:] . rhs[g(m)] with fp32 accumulation; rows past the
+ *   total are 0.  ("GEMM Kernel 性能优化十问", Q10: the BF16 kernel is the
+ *   baseline the FP8 kernel is measured against.)
+ * lhs: [M,K] bf16.  rhs: [G,K,N] bf16.  out: [M,N] bf16 or f32.
+ * K and N must be multiples of 64 (K) and 128 (N).
+ */
+GMM_API int gmm_bf16_fwd(const void *lhs, const void *rhs, const int32_t *group_sizes,
+                 int64_t M, int64_t K, int64_t N, int64_t G, void *out,
+                 int out_dtype, void *stream);
+
+/*
+ * tgmm_bf16 -- weight gradient of the grouped matmul.
+ *   dw[g] = sum over rows m of group g of x[m,:]^T dy[m,:], fp32
+ *   accumulation; an empty group gives exactly 0.  The reduction runs over
+ *   M, so tiles are chosen separately from the forward pass
+ *   ("GEMM Kernel 性能优化十问", Q4; Q5: the backward pass is bf16).
+ * x: [M,K] bf16.  dy: [M,N] bf16.  dw: [G,K,N] bf16 or f32.
+ * K and N must be multiples of 128.  Rows past the total are ignored.
+ */
+GMM_API int tgmm_bf16(const void *x, const void *dy, const int32_t *group_sizes,
+              int64_t M, int64_t K, int64_t N, int64_t G, void *dw,
+              int out_dtype, void *stream);
+
+/*
+ * gmm_bf16_dx -- input gradient of the grouped matmul.
+ *   dx[m,:] = dy[m,:] . w[g(m)]^T (contracting over N), fp32 accumulation;
+ *   rows past the total are 0.  ("GEMM Kernel 性能优化十问", Q5.)
+ * dy: [M,N] bf16.  w: [G,K,N] bf16 (the forward weights, not transposed).
+ * dx: [M,K] bf16 or f32.  K multiple of 128, N multiple of 64.
+ */
+GMM_API int gmm_bf16_dx(const void *dy, const void *w, const int32_t *group_sizes,
+                int64_t M, int64_t K, int64_t N, int64_t G, void *dx,
+                int out_dtype, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GMM_H_ */

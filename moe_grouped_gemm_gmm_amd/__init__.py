@@ -1,0 +1,187 @@
+"""Python binding of the gfx950 grouped-matmul library (libgmm.so, include/gmm.h).
+
+Argument marshalling only: every function checks nothing that the C ABI does
+not already check, allocates outputs with torch (device memory), and calls
+the library on torch's current stream.  All compute runs in the HIP kernels;
+there is no CPU or eager-PyTorch fallback.  If libgmm.so is missing or cannot
+be loaded, every call raises.
+"""
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgmm.so")
+
+GMM_F32, GMM_BF16, GMM_E4M3 = 0, 1, 2
+GMM_MAX_GROUPS = 4096
+EXPORTS = ("gmm_status_string", "gmm_last_error", "gmm_group_metadata", "gmm_quantize_lhs",
+           "gmm_quantize_rhs", "gmm_fp8_fwd", "gmm_bf16_fwd", "tgmm_bf16", "gmm_bf16_dx")
+
+_lib = None
+
+
+class GmmError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("gmm status %d: %s" % (status, message))
+        self.status = status
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libgmm.so (raises if it is absent: build it with build.py first)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError("libgmm.so not found at %s; run moe_grouped_gemm_gmm_amd/build.py" % path)
+    lib = ctypes.CDLL(path)
+    P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.gmm_status_string.restype = ctypes.c_char_p
+    lib.gmm_status_string.argtypes = [I]
+    lib.gmm_last_error.restype = ctypes.c_char_p
+    lib.gmm_last_error.argtypes = []
+    lib.gmm_group_metadata.argtypes = [P, I64, I64, I64, P, P, I64, P, P]
+    lib.gmm_quantize_lhs.argtypes = [P, I, I64, I64, P, P, P]
+    lib.gmm_quantize_rhs.argtypes = [P, I, I64, I64, I64, P, P, P]
+    lib.gmm_fp8_fwd.argtypes = [P, I, P, P, P, P, I64, I64, I64, I64, P, I, P, P, P]
+    lib.gmm_bf16_fwd.argtypes = [P, P, P, I64, I64, I64, I64, P, I, P]
+    lib.tgmm_bf16.argtypes = [P, P, P, I64, I64, I64, I64, P, I, P]
+    lib.gmm_bf16_dx.argtypes = [P, P, P, I64, I64, I64, I64, P, I, P]
+    for name in EXPORTS[2:]:
+        getattr(lib, name).restype = I
+    _lib = lib
+    return lib
+
+
+def _check(rc: int) -> None:
+    if rc != 0:
+        lib = load_library()
+        raise GmmError(rc, lib.gmm_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+_DT = {torch.float32: GMM_F32, torch.bfloat16: GMM_BF16, torch.uint8: GMM_E4M3,
+       torch.float8_e4m3fn: GMM_E4M3}
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype not in _DT:
+        raise TypeError("unsupported dtype %s" % t.dtype)
+    return _DT[t.dtype]
+
+
+def gmm_group_metadata(group_sizes: torch.Tensor, M: int, tile_m: int = 128
+                       ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Device work list of the grouped kernels: (offsets [G+1], work [cap,4], num_work [1])."""
+    lib = load_library()
+    G = group_sizes.numel()
+    cap = -(-M // tile_m) + G + 1
+    dev = group_sizes.device
+    offsets = torch.empty(G + 1, dtype=torch.int32, device=dev)
+    work = torch.empty((cap, 4), dtype=torch.int32, device=dev)
+    num = torch.empty(1, dtype=torch.int32, device=dev)
+    _check(lib.gmm_group_metadata(_ptr(group_sizes), G, M, tile_m, _ptr(offsets), _ptr(work),
+                                  cap, _ptr(num), _stream(group_sizes)))
+    return offsets, work, num
+
+
+def gmm_quantize_lhs(x: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
+    """1x128 quantisation of x [M,K] (bf16/fp32) -> (codes uint8 [M,K], scales f32 [M,K/128])."""
+    lib = load_library()
+    M, K = x.shape
+    q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    s = torch.empty((M, max(K // 128, 0)), dtype=torch.float32, device=x.device)
+    _check(lib.gmm_quantize_lhs(_ptr(x), _dt(x), M, K, _ptr(q), _ptr(s), _stream(x)))
+    return q, s
+
+
+def gmm_quantize_rhs(w: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
+    """128x128 quantisation of w [G,K,N] -> (codes uint8 [G,N,K] K-contiguous, scales [G,K/128,N/128])."""
+    lib = load_library()
+    G, K, N = w.shape
+    q = torch.empty((G, N, K), dtype=torch.uint8, device=w.device)
+    s = torch.empty((G, max(K // 128, 0), max(N // 128, 0)), dtype=torch.float32, device=w.device)
+    _check(lib.gmm_quantize_rhs(_ptr(w), _dt(w), G, K, N, _ptr(q), _ptr(s), _stream(w)))
+    return q, s
+
+
+def gmm_fp8_fwd(lhs: torch.Tensor, rhs_q: torch.Tensor, rhs_scale: torch.Tensor,
+                group_sizes: torch.Tensor, lhs_scale: Optional[torch.Tensor] = None,
+                out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None,
+                q_out: Optional[torch.Tensor] = None, scale_out: Optional[torch.Tensor] = None
+                ) -> torch.Tensor:
+    """Blockwise-FP8 GMM.  lhs [M,K] bf16/fp32 (quantised in-kernel) or uint8 codes
+    with lhs_scale; rhs_q [G,N,K] codes, rhs_scale [G,K/128,N/128]."""
+    lib = load_library()
+    M, K = lhs.shape
+    G, N, K2 = rhs_q.shape
+    if K2 != K:
+        raise ValueError("lhs K=%d but rhs K=%d" % (K, K2))
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=lhs.device)
+    _check(lib.gmm_fp8_fwd(_ptr(lhs), _dt(lhs), _ptr(lhs_scale), _ptr(rhs_q), _ptr(rhs_scale),
+                           _ptr(group_sizes), M, K, N, G, _ptr(out), _dt(out), _ptr(q_out),
+                           _ptr(scale_out), _stream(lhs)))
+    return out
+
+
+def gmm_bf16_fwd(lhs: torch.Tensor, rhs: torch.Tensor, group_sizes: torch.Tensor,
+                 out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None
+                 ) -> torch.Tensor:
+    """bf16 GMM: out [M,N] = lhs [M,K] . rhs[g] [K,N] per group."""
+    lib = load_library()
+    M, K = lhs.shape
+    G, K2, N = rhs.shape
+    if K2 != K:
+        raise ValueError("lhs K=%d but rhs K=%d" % (K, K2))
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=lhs.device)
+    _check(lib.gmm_bf16_fwd(_ptr(lhs), _ptr(rhs), _ptr(group_sizes), M, K, N, G, _ptr(out),
+                            _dt(out), _stream(lhs)))
+    return out
+
+
+def tgmm_bf16(x: torch.Tensor, dy: torch.Tensor, group_sizes: torch.Tensor,
+              out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None
+              ) -> torch.Tensor:
+    """dW [G,K,N]: dW[g] = X_g^T dY_g for x [M,K], dy [M,N]."""
+    lib = load_library()
+    M, K = x.shape
+    M2, N = dy.shape
+    if M2 != M:
+        raise ValueError("x has %d rows but dy has %d" % (M, M2))
+    G = group_sizes.numel()
+    if out is None:
+        out = torch.empty((G, K, N), dtype=out_dtype, device=x.device)
+    _check(lib.tgmm_bf16(_ptr(x), _ptr(dy), _ptr(group_sizes), M, K, N, G, _ptr(out), _dt(out),
+                         _stream(x)))
+    return out
+
+
+def gmm_bf16_dx(dy: torch.Tensor, w: torch.Tensor, group_sizes: torch.Tensor,
+                out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None
+                ) -> torch.Tensor:
+    """dX [M,K] = dY [M,N] . w[g]^T per group, w [G,K,N]."""
+    lib = load_library()
+    M, N = dy.shape
+    G, K, N2 = w.shape
+    if N2 != N:
+        raise ValueError("dy N=%d but w N=%d" % (N, N2))
+    if out is None:
+        out = torch.empty((M, K), dtype=out_dtype, device=dy.device)
+    _check(lib.gmm_bf16_dx(_ptr(dy), _ptr(w), _ptr(group_sizes), M, K, N, G, _ptr(out),
+                           _dt(out), _stream(dy)))
+    return out

@@ -1,0 +1,226 @@
+// C ABI of the grouped-matmul library (declared in include/gmm.h): host-side
+// argument checks, then one launch on the caller's stream.  Nothing here
+// allocates, synchronises or reads device memory.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+
+#include "../../include/gmm.h"
+#include "gmm_launch.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1024;
+
+int check_ptr(const void* p, const char* name) {
+    if (p == nullptr) return fail(GMM_ERR_NULL, "%s is NULL", name);
+    if (!aligned16(p)) return fail(GMM_ERR_ALIGN, "%s is not 16-byte aligned", name);
+    return GMM_OK;
+}
+
+int check_opt_ptr(const void* p, const char* name) {
+    if (p != nullptr && !aligned16(p)) return fail(GMM_ERR_ALIGN, "%s is not 16-byte aligned", name);
+    return GMM_OK;
+}
+
+int check_groups(int64_t M, int64_t G) {
+    if (M < 0 || M > kMaxDim) return fail(GMM_ERR_SHAPE, "M=%lld out of range", (long long)M);
+    if (G < 1 || G > GMM_MAX_GROUPS)
+        return fail(GMM_ERR_SHAPE, "G=%lld outside [1, %d]", (long long)G, GMM_MAX_GROUPS);
+    return GMM_OK;
+}
+
+int check_mult(int64_t v, int64_t mult, const char* name) {
+    if (v < mult || v > kMaxDim || v % mult != 0)
+        return fail(GMM_ERR_SHAPE, "%s=%lld must be a positive multiple of %lld", name,
+                    (long long)v, (long long)mult);
+    return GMM_OK;
+}
+
+int check_out_dtype(int dt, const char* name) {
+    if (dt != GMM_BF16 && dt != GMM_F32)
+        return fail(GMM_ERR_DTYPE, "%s dtype %d is not GMM_BF16 or GMM_F32", name, dt);
+    return GMM_OK;
+}
+
+int hip_status(hipError_t e) {
+    if (e != hipSuccess) return fail(GMM_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(e));
+    return GMM_OK;
+}
+
+#define GMM_TRY(expr)                 \
+    do {                              \
+        int _rc = (expr);             \
+        if (_rc != GMM_OK) return _rc; \
+    } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* gmm_status_string(int status) {
+    switch (status) {
+        case GMM_OK: return "ok";
+        case GMM_ERR_NULL: return "null pointer";
+        case GMM_ERR_SHAPE: return "invalid shape";
+        case GMM_ERR_ALIGN: return "misaligned pointer";
+        case GMM_ERR_DTYPE: return "unsupported dtype";
+        case GMM_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+const char* gmm_last_error(void) { return g_last_error; }
+
+int gmm_group_metadata(const int32_t* group_sizes, int64_t G, int64_t M, int64_t tile_m,
+                       int32_t* offsets, int32_t* work, int64_t capacity, int32_t* num_work,
+                       void* stream) {
+    GMM_TRY(check_groups(M, G));
+    GMM_TRY(check_ptr(group_sizes, "group_sizes"));
+    GMM_TRY(check_ptr(offsets, "offsets"));
+    GMM_TRY(check_ptr(work, "work"));
+    GMM_TRY(check_ptr(num_work, "num_work"));
+    int tm_log2 = -1;
+    for (int l = 4; l <= 10; ++l)
+        if (tile_m == (int64_t(1) << l)) tm_log2 = l;
+    if (tm_log2 < 0) return fail(GMM_ERR_SHAPE, "tile_m=%lld is not a power of two in [16,1024]", (long long)tile_m);
+    const int64_t need = (M + tile_m - 1) / tile_m + G + 1;
+    if (capacity < need || capacity > kMaxDim)
+        return fail(GMM_ERR_SHAPE, "capacity=%lld, need >= %lld", (long long)capacity, (long long)need);
+    return hip_status(gmm::launch_group_metadata(group_sizes, (int)G, (int)M, tm_log2, offsets,
+                                                 work, (int)capacity, num_work,
+                                                 (hipStream_t)stream));
+}
+
+int gmm_quantize_lhs(const void* x, int x_dtype, int64_t M, int64_t K, uint8_t* q, float* scale,
+                     void* stream) {
+    if (x_dtype != GMM_BF16 && x_dtype != GMM_F32)
+        return fail(GMM_ERR_DTYPE, "x dtype %d is not GMM_BF16 or GMM_F32", x_dtype);
+    if (M < 0 || M > kMaxDim) return fail(GMM_ERR_SHAPE, "M=%lld out of range", (long long)M);
+    GMM_TRY(check_mult(K, 128, "K"));
+    GMM_TRY(check_ptr(x, "x"));
+    GMM_TRY(check_ptr(q, "q"));
+    GMM_TRY(check_ptr(scale, "scale"));
+    if (M == 0) return GMM_OK;
+    return hip_status(gmm::launch_quantize_lhs(x, x_dtype == GMM_BF16, M, K, q, scale,
+                                               (hipStream_t)stream));
+}
+
+int gmm_quantize_rhs(const void* w, int w_dtype, int64_t G, int64_t K, int64_t N, uint8_t* q,
+                     float* scale, void* stream) {
+    if (w_dtype != GMM_BF16 && w_dtype != GMM_F32)
+        return fail(GMM_ERR_DTYPE, "w dtype %d is not GMM_BF16 or GMM_F32", w_dtype);
+    if (G < 1 || G > GMM_MAX_GROUPS)
+        return fail(GMM_ERR_SHAPE, "G=%lld outside [1, %d]", (long long)G, GMM_MAX_GROUPS);
+    GMM_TRY(check_mult(K, 128, "K"));
+    GMM_TRY(check_mult(N, 128, "N"));
+    if (G * (K / 128) * (N / 128) > kMaxDim) return fail(GMM_ERR_SHAPE, "too many blocks");
+    GMM_TRY(check_ptr(w, "w"));
+    GMM_TRY(check_ptr(q, "q"));
+    GMM_TRY(check_ptr(scale, "scale"));
+    return hip_status(gmm::launch_quantize_rhs(w, w_dtype == GMM_BF16, G, K, N, q, scale,
+                                               (hipStream_t)stream));
+}
+
+int gmm_fp8_fwd(const void* lhs, int lhs_dtype, const float* lhs_scale, const uint8_t* rhs,
+                const float* rhs_scale, const int32_t* group_sizes, int64_t M, int64_t K,
+                int64_t N, int64_t G, void* out, int out_dtype, uint8_t* q_out,
+                float* scale_out, void* stream) {
+    int kind;
+    if (lhs_dtype == GMM_E4M3) kind = 0;
+    else if (lhs_dtype == GMM_BF16) kind = 1;
+    else if (lhs_dtype == GMM_F32) kind = 2;
+    else return fail(GMM_ERR_DTYPE, "lhs dtype %d unsupported", lhs_dtype);
+    GMM_TRY(check_out_dtype(out_dtype, "out"));
+    GMM_TRY(check_groups(M, G));
+    GMM_TRY(check_mult(K, 128, "K"));
+    GMM_TRY(check_mult(N, 128, "N"));
+    GMM_TRY(check_ptr(lhs, "lhs"));
+    GMM_TRY(check_ptr(rhs, "rhs"));
+    GMM_TRY(check_ptr(rhs_scale, "rhs_scale"));
+    GMM_TRY(check_ptr(group_sizes, "group_sizes"));
+    GMM_TRY(check_ptr(out, "out"));
+    if (kind == 0) {
+        GMM_TRY(check_ptr(lhs_scale, "lhs_scale"));
+        if (q_out != nullptr || scale_out != nullptr)
+            return fail(GMM_ERR_DTYPE, "q_out/scale_out need a bf16 or fp32 lhs");
+    } else {
+        if (lhs_scale != nullptr) return fail(GMM_ERR_DTYPE, "lhs_scale given with an unquantised lhs");
+        if ((q_out == nullptr) != (scale_out == nullptr))
+            return fail(GMM_ERR_NULL, "q_out and scale_out must both be set or both NULL");
+        GMM_TRY(check_opt_ptr(q_out, "q_out"));
+        GMM_TRY(check_opt_ptr(scale_out, "scale_out"));
+    }
+    const int64_t blocks = ((M + 127) / 128 + G + 1) * (N / 128);
+    if (blocks > kMaxDim) return fail(GMM_ERR_SHAPE, "grid too large");
+    if (M == 0) return GMM_OK;
+    return hip_status(gmm::launch_fp8_fwd(lhs, kind, lhs_scale, rhs, rhs_scale, group_sizes,
+                                          (int)M, (int)K, (int)N, (int)G, out,
+                                          out_dtype == GMM_BF16, q_out, scale_out,
+                                          (hipStream_t)stream));
+}
+
+int gmm_bf16_fwd(const void* lhs, const void* rhs, const int32_t* group_sizes, int64_t M,
+                 int64_t K, int64_t N, int64_t G, void* out, int out_dtype, void* stream) {
+    GMM_TRY(check_out_dtype(out_dtype, "out"));
+    GMM_TRY(check_groups(M, G));
+    GMM_TRY(check_mult(K, 64, "K"));
+    GMM_TRY(check_mult(N, 128, "N"));
+    GMM_TRY(check_ptr(lhs, "lhs"));
+    GMM_TRY(check_ptr(rhs, "rhs"));
+    GMM_TRY(check_ptr(group_sizes, "group_sizes"));
+    GMM_TRY(check_ptr(out, "out"));
+    const int64_t blocks = ((M + 127) / 128 + G + 1) * (N / 128);
+    if (blocks > kMaxDim) return fail(GMM_ERR_SHAPE, "grid too large");
+    if (M == 0) return GMM_OK;
+    return hip_status(gmm::launch_bf16_fwd(lhs, rhs, group_sizes, (int)M, (int)K, (int)N, (int)G,
+                                           out, out_dtype == GMM_BF16, (hipStream_t)stream));
+}
+
+int tgmm_bf16(const void* x, const void* dy, const int32_t* group_sizes, int64_t M, int64_t K,
+              int64_t N, int64_t G, void* dw, int out_dtype, void* stream) {
+    GMM_TRY(check_out_dtype(out_dtype, "dw"));
+    GMM_TRY(check_groups(M, G));
+    GMM_TRY(check_mult(K, 128, "K"));
+    GMM_TRY(check_mult(N, 128, "N"));
+    GMM_TRY(check_ptr(x, "x"));
+    GMM_TRY(check_ptr(dy, "dy"));
+    GMM_TRY(check_ptr(group_sizes, "group_sizes"));
+    GMM_TRY(check_ptr(dw, "dw"));
+    if (G * (K / 128) * (N / 128) > kMaxDim) return fail(GMM_ERR_SHAPE, "grid too large");
+    return hip_status(gmm::launch_tgmm(x, dy, group_sizes, (int)M, (int)K, (int)N, (int)G, dw,
+                                       out_dtype == GMM_BF16, (hipStream_t)stream));
+}
+
+int gmm_bf16_dx(const void* dy, const void* w, const int32_t* group_sizes, int64_t M, int64_t K,
+                int64_t N, int64_t G, void* dx, int out_dtype, void* stream) {
+    GMM_TRY(check_out_dtype(out_dtype, "dx"));
+    GMM_TRY(check_groups(M, G));
+    GMM_TRY(check_mult(K, 128, "K"));
+    GMM_TRY(check_mult(N, 64, "N"));
+    GMM_TRY(check_ptr(dy, "dy"));
+    GMM_TRY(check_ptr(w, "w"));
+    GMM_TRY(check_ptr(group_sizes, "group_sizes"));
+    GMM_TRY(check_ptr(dx, "dx"));
+    const int64_t blocks = ((M + 127) / 128 + G + 1) * (K / 128);
+    if (blocks > kMaxDim) return fail(GMM_ERR_SHAPE, "grid too large");
+    if (M == 0) return GMM_OK;
+    return hip_status(gmm::launch_bf16_dx(dy, w, group_sizes, (int)M, (int)K, (int)N, (int)G, dx,
+                                          out_dtype == GMM_BF16, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,283 @@
+// Unquantised (bf16) grouped matmuls for gfx950: forward, dX and tgmm.
+//
+//   forward  out[m,:] = x[m,:] . w[g(m)]                (reduce over K)
+//   dX       dx[m,:]  = dy[m,:] . w[g(m)]^T             (reduce over N)
+//   tgmm     dw[g]    = sum_{m in g} x[m,:]^T dy[m,:]   (reduce over M)
+//
+// "GEMM Kernel 性能优化十问", Q5: the backward pass stays in bf16; Q4: fwd
+// reduces over K while tgmm reduces over M, so the same physical M is an
+// output dimension in one and the reduction dimension in the other, and each
+// phase gets its own tiling.
+//
+// All three are C[rows][cols] = sum_r A(row, r) B(r, col) on a 128x128 tile
+// per workgroup (4 waves, 2x2, each 64x64 = 4x4 v_mfma_f32_16x16x32_bf16
+// blocks), staging 64-deep slices of both operands in LDS per step.  An
+// operand whose memory layout is contiguous along the reduction index
+// (x and dy in forward/dX, w in dX) is read from LDS with ds_read_b128; one
+// that is contiguous along the output index (w in forward; x and dy in tgmm,
+// where the reduction index M is the row index) is stored as it sits in
+// memory and read transposed with ds_read_b64_tr_b16, the in-LDS transpose of
+// gfx950.  tgmm walks the expert's rows 64 at a time, so its reduction tile
+// is 64 rows while the forward's is 64 K-columns.
+#include "gmm_device.hpp"
+#include "gmm_launch.hpp"
+
+namespace gmm {
+
+namespace {
+
+constexpr int kT = 128;      // output tile (rows and cols)
+constexpr int kR = 64;       // reduction depth per LDS stage
+constexpr int kPadD = 8;     // bf16 padding of a direct [128][64] tile (144-byte rows)
+constexpr int kPadT = 16;    // bf16 padding of a transposed [64][128] tile (288-byte rows: the
+                             // four rows one 16-lane group reads land on disjoint banks)
+
+enum Mode { kFwd = 0, kDx = 1, kTgmm = 2 };
+
+// Transposed fragment: 8 reduction-consecutive values of column `col` from a
+// [r][col] LDS tile via two ds_read_b64_tr_b16.  Within each 16-lane group,
+// lane i supplies the address of row r0 + i/4, columns c0 + 4*(i%4) .. +3 and
+// receives column c0 + i of rows r0 .. r0+3.
+__device__ __forceinline__ v8bf read_tr(const uint16_t* tile, int stride, int r0, int c0, int lr) {
+    const uint16_t* p0 = tile + (r0 + (lr >> 2)) * stride + c0 + (lr & 3) * 4;
+    const uint16_t* p1 = p0 + 4 * stride;
+    const v4bf lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((GMM_LDS v4bf*)(p0));
+    const v4bf hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((GMM_LDS v4bf*)(p1));
+    return v8bf{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+__device__ __forceinline__ v8bf read_direct(const uint16_t* tile, int stride, int row, int r0) {
+    return *reinterpret_cast<const v8bf*>(tile + row * stride + r0);
+}
+
+// Copy a [128 rows][64] bf16 slice (row-major source, leading dimension ld)
+// into a direct LDS tile; rows with !valid become zeros.
+__device__ __forceinline__ void stage_direct(uint16_t* tile, const uint16_t* src, int64_t ld,
+                                             bool valid) {
+    const int t = threadIdx.x, row = t >> 1, h = t & 1;
+    uint4 d[4];
+    if (valid) {
+        const uint4* p = reinterpret_cast<const uint4*>(src + (int64_t)row * ld + h * 32);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) d[c] = p[c];
+    } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) d[c] = make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+        *reinterpret_cast<uint4*>(tile + row * (kR + kPadD) + h * 32 + 8 * c) = d[c];
+}
+
+// Copy a [64 rows][128] bf16 slice into a transposed-layout LDS tile.
+__device__ __forceinline__ void stage_trans(uint16_t* tile, const uint16_t* src, int64_t ld,
+                                            bool valid) {
+    const int t = threadIdx.x, row = t >> 2, q = t & 3;
+    uint4 d[4];
+    if (valid) {
+        const uint4* p = reinterpret_cast<const uint4*>(src + (int64_t)row * ld + q * 32);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) d[c] = p[c];
+    } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) d[c] = make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+        *reinterpret_cast<uint4*>(tile + row * (kT + kPadT) + q * 32 + 8 * c) = d[c];
+}
+
+// Offset of group g: sum of group_sizes[0..g), computed by one wave.
+__device__ inline int group_offset(const int32_t* __restrict__ group_sizes, int g) {
+    const int lane = lane_id();
+    int acc = 0;
+    for (int base = 0; base < g; base += 64) {
+        const int i = base + lane;
+        acc += i < g ? group_sizes[i] : 0;
+    }
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) acc += __shfl_xor(acc, d, 64);
+    return acc;
+}
+
+constexpr int kTileElems = (kT * (kR + kPadD) > kR * (kT + kPadT)) ? kT * (kR + kPadD) : kR * (kT + kPadT);
+
+template <int MODE, bool OUT_BF16>
+__global__ __launch_bounds__(256, 2) void bf16_gemm_kernel(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
+    const int32_t* __restrict__ group_sizes, int M, int K, int N, int G, void* __restrict__ out,
+    int ntiles_c, int ntiles_r, int nblocks) {
+    constexpr bool A_TR = MODE == kTgmm;
+    constexpr bool B_TR = MODE != kDx;
+    __shared__ __attribute__((aligned(16))) uint16_t sA[kTileElems];
+    __shared__ __attribute__((aligned(16))) uint16_t sB[kTileElems];
+    __shared__ int s_info[4];
+
+    const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+    const int L = xcd_remap(blockIdx.x, nblocks);
+    const int out_cols = MODE == kDx ? K : N;
+
+    // ---- what this workgroup computes
+    int g, row0, lo, hi, c0, red_lo, red_hi;
+    if constexpr (MODE == kTgmm) {
+        g = L / (ntiles_r * ntiles_c);
+        row0 = ((L / ntiles_c) % ntiles_r) * kT;   // k tile
+        c0 = (L % ntiles_c) * kT;                  // n tile
+        if (wave == 0) {
+            const int o = group_offset(group_sizes, g);
+            if (lane == 0) { s_info[0] = o; s_info[1] = o + group_sizes[g]; }
+        }
+        __syncthreads();
+        red_lo = s_info[0];
+        red_hi = s_info[1];
+        lo = row0;
+        hi = row0 + kT;
+    } else {
+        const int w = L / ntiles_c;
+        c0 = (L % ntiles_c) * kT;
+        if (wave == 0) {
+            const WorkItem it = find_work_item(group_sizes, G, M, 7, w);
+            if (lane == 0) { s_info[0] = it.g; s_info[1] = it.tile; s_info[2] = it.lo; s_info[3] = it.hi; }
+        }
+        __syncthreads();
+        g = s_info[0];
+        if (g < 0) return;
+        row0 = s_info[1] * kT;
+        lo = s_info[2];
+        hi = s_info[3];
+        red_lo = 0;
+        red_hi = MODE == kFwd ? K : N;
+        if (g == G) {  // rows past the last group: zeros
+            const int rows = hi - lo;
+            for (int e = tid; e < rows * (kT / 8); e += 256) {
+                const int r = lo + e / (kT / 8), c = c0 + (e % (kT / 8)) * 8;
+                if constexpr (OUT_BF16)
+                    *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + (int64_t)r * out_cols + c) = make_uint4(0, 0, 0, 0);
+                else {
+                    float4* p = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + (int64_t)r * out_cols + c);
+                    p[0] = make_float4(0, 0, 0, 0);
+                    p[1] = make_float4(0, 0, 0, 0);
+                }
+            }
+            return;
+        }
+    }
+
+    const int wm = wave >> 1, wn = wave & 1;
+    const int lr = lane & 15, lg = lane >> 4;
+    v4f acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    for (int r0 = red_lo; r0 < red_hi; r0 += kR) {
+        // ---- stage the A and B slices of reduction range [r0, r0 + 64)
+        if constexpr (MODE == kTgmm) {
+            const int m = r0 + (tid >> 2);
+            const bool valid = m < red_hi;
+            stage_trans(sA, A + (int64_t)r0 * K + row0, K, valid);   // x[m][k0..k0+128]
+            stage_trans(sB, B + (int64_t)r0 * N + c0, N, valid);     // dy[m][n0..n0+128]
+        } else {
+            const int arow = row0 + (tid >> 1);
+            const bool avalid = arow >= lo && arow < hi;
+            const int lda = MODE == kFwd ? K : N;
+            stage_direct(sA, A + (int64_t)row0 * lda + r0, lda, avalid);
+            const uint16_t* wg = B + (int64_t)g * K * N;
+            if constexpr (MODE == kFwd)
+                stage_trans(sB, wg + (int64_t)r0 * N + c0, N, true);  // w[g][k][n0..n0+128]
+            else
+                stage_direct(sB, wg + (int64_t)c0 * N + r0, N, true); // w[g][k0+c][n]
+        }
+        __syncthreads();
+
+#pragma unroll
+        for (int s = 0; s < kR / 32; ++s) {
+            v8bf af[4], bf[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if constexpr (A_TR)
+                    af[i] = read_tr(sA, kT + kPadT, s * 32 + lg * 8, wm * 64 + i * 16, lr);
+                else
+                    af[i] = read_direct(sA, kR + kPadD, wm * 64 + i * 16 + lr, s * 32 + lg * 8);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if constexpr (B_TR)
+                    bf[j] = read_tr(sB, kT + kPadT, s * 32 + lg * 8, wn * 64 + j * 16, lr);
+                else
+                    bf[j] = read_direct(sB, kR + kPadD, wn * 64 + j * 16 + lr, s * 32 + lg * 8);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+        }
+        __syncthreads();
+    }
+
+    // ---- epilogue: masked stores
+    const int64_t obase = MODE == kTgmm ? (int64_t)g * K * N : 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = row0 + wm * 64 + i * 16 + lg * 4 + r;
+            if (row < lo || row >= hi) continue;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int col = c0 + wn * 64 + j * 16 + lr;
+                const int64_t idx = obase + (int64_t)row * out_cols + col;
+                if constexpr (OUT_BF16)
+                    reinterpret_cast<uint16_t*>(out)[idx] = (uint16_t)f32_to_bf16_bits(acc[i][j][r]);
+                else
+                    reinterpret_cast<float*>(out)[idx] = acc[i][j][r];
+            }
+        }
+}
+
+template <int MODE>
+hipError_t launch_mode(const void* A, const void* B, const int32_t* group_sizes, int M, int K,
+                       int N, int G, void* out, bool out_bf16, hipStream_t stream) {
+    int ntiles_c, ntiles_r = 0;
+    int64_t nblocks;
+    if constexpr (MODE == kTgmm) {
+        ntiles_r = K / kT;
+        ntiles_c = N / kT;
+        nblocks = (int64_t)G * ntiles_r * ntiles_c;
+    } else {
+        ntiles_c = (MODE == kFwd ? N : K) / kT;
+        nblocks = max_work_items(M, G, kT) * ntiles_c;
+    }
+    const uint16_t* a = reinterpret_cast<const uint16_t*>(A);
+    const uint16_t* b = reinterpret_cast<const uint16_t*>(B);
+    if (out_bf16)
+        hipLaunchKernelGGL((bf16_gemm_kernel<MODE, true>), dim3((unsigned)nblocks), dim3(256), 0,
+                           stream, a, b, group_sizes, M, K, N, G, out, ntiles_c, ntiles_r,
+                           (int)nblocks);
+    else
+        hipLaunchKernelGGL((bf16_gemm_kernel<MODE, false>), dim3((unsigned)nblocks), dim3(256), 0,
+                           stream, a, b, group_sizes, M, K, N, G, out, ntiles_c, ntiles_r,
+                           (int)nblocks);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bf16_fwd(const void* lhs, const void* rhs, const int32_t* group_sizes, int M,
+                           int K, int N, int G, void* out, bool out_bf16, hipStream_t stream) {
+    return launch_mode<kFwd>(lhs, rhs, group_sizes, M, K, N, G, out, out_bf16, stream);
+}
+
+hipError_t launch_bf16_dx(const void* dy, const void* w, const int32_t* group_sizes, int M,
+                          int K, int N, int G, void* dx, bool out_bf16, hipStream_t stream) {
+    return launch_mode<kDx>(dy, w, group_sizes, M, K, N, G, dx, out_bf16, stream);
+}
+
+hipError_t launch_tgmm(const void* x, const void* dy, const int32_t* group_sizes, int M, int K,
+                       int N, int G, void* dw, bool out_bf16, hipStream_t stream) {
+    return launch_mode<kTgmm>(x, dy, group_sizes, M, K, N, G, dw, out_bf16, stream);
+}
+
+}  // namespace gmm

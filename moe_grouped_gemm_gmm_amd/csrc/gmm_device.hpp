@@ -1,0 +1,145 @@
+// Device helpers shared by the gfx950 grouped-matmul kernels: bf16 and FP8
+// conversions, the 1x128 quantiser, the in-kernel group metadata routine and
+// the XCD-aware workgroup remap.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gmm {
+
+constexpr int kQBlock = 128;        // quantisation block along K
+constexpr float kE4M3Max = 448.0f;  // largest finite OCP E4M3 magnitude
+constexpr int kNumXcd = 8;          // MI355X: 8 accelerator complex dies
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
+
+#define GMM_LDS __attribute__((address_space(3)))
+
+// ---------------------------------------------------------------- bf16 --
+
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xffff0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// ------------------------------------------------------------ quantiser --
+// One 1x128 (or 128x128) block: s = a/448 and inv = (s == 0 ? 0 : 1/s), each
+// a correctly rounded fp32 division (hipcc's default fp32 divide is IEEE; the
+// library is built without fast-math), then code = e4m3_rne(x * inv).  The
+// product x*inv is one fp32 multiply; |x*inv| <= 448(1+2^-22) so clamping to
+// +-448 before the conversion only removes the overflow case and never
+// changes a round-to-nearest-even result.
+
+__device__ __forceinline__ float quant_scale(float absmax) { return absmax / kE4M3Max; }
+
+__device__ __forceinline__ float quant_inv(float s) { return s == 0.0f ? 0.0f : 1.0f / s; }
+
+__device__ __forceinline__ float clamp448(float y) { return fminf(fmaxf(y, -kE4M3Max), kE4M3Max); }
+
+// Four fp32 values (already multiplied by inv) -> four E4M3 codes, byte i = value i.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+    int r = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(a), clamp448(b), 0, false);
+    r = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(c), clamp448(d), r, true);
+    return (uint32_t)r;
+}
+
+// --------------------------------------------------------- wave helpers --
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+__device__ __forceinline__ int wave_incl_scan(int v) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        int t = __shfl_up(v, d, 64);
+        if (lane >= d) v += t;
+    }
+    return v;
+}
+
+// ------------------------------------------------------- group metadata --
+// Work item w of a grouped kernel with row tiles of height 2^tm_log2, tiles
+// aligned to absolute rows.  Items are ordered group by group; each non-empty
+// group g owns the tiles that intersect rows [o_g, o_g + s_g), the item's row
+// range being that intersection.  After the groups come the items that zero
+// the rows at or past the total (g == G).  g < 0 means "no item" (the grid is
+// sized for the worst case).  Every lane of the calling wave gets the result.
+
+struct WorkItem {
+    int g, tile, lo, hi;
+};
+
+__device__ inline WorkItem find_work_item(const int32_t* __restrict__ group_sizes, int G, int M,
+                                          int tm_log2, int w) {
+    const int lane = lane_id();
+    int carry_rows = 0, carry_items = 0;
+    for (int base = 0; base < G; base += 64) {
+        const int g = base + lane;
+        const int s = g < G ? group_sizes[g] : 0;
+        const int incl = wave_incl_scan(s);
+        const int o = carry_rows + incl - s;
+        const int c = s > 0 ? ((o + s - 1) >> tm_log2) - (o >> tm_log2) + 1 : 0;
+        const int inclc = wave_incl_scan(c);
+        const int W = carry_items + inclc - c;
+        const bool own = c > 0 && w >= W && w < W + c;
+        const unsigned long long mask = __ballot(own);
+        if (mask) {
+            const int src = __ffsll((long long)mask) - 1;
+            const int go = __shfl(o, src, 64);
+            const int gsz = __shfl(s, src, 64);
+            const int gW = __shfl(W, src, 64);
+            const int t = (go >> tm_log2) + (w - gW);
+            WorkItem it;
+            it.g = base + src;
+            it.tile = t;
+            it.lo = max(go, t << tm_log2);
+            it.hi = min(go + gsz, (t + 1) << tm_log2);
+            return it;
+        }
+        carry_rows += __shfl(incl, 63, 64);
+        carry_items += __shfl(inclc, 63, 64);
+    }
+    WorkItem it;
+    const int total = carry_rows;
+    const int t = (total >> tm_log2) + (w - carry_items);
+    it.g = G;
+    it.tile = t;
+    it.lo = max(total, t << tm_log2);
+    it.hi = min(M, (t + 1) << tm_log2);
+    if (it.lo >= it.hi) it.g = -1;
+    return it;
+}
+
+// Upper bound of the work-item count for M rows, G groups, tile height tm.
+__host__ __device__ inline int64_t max_work_items(int64_t M, int64_t G, int64_t tm) {
+    return (M + tm - 1) / tm + G + 1;
+}
+
+// ----------------------------------------------------------- XCD remap --
+// Workgroups are dispatched round-robin over the 8 XCDs (block b runs on XCD
+// b % 8), each with its own L2.  Remap so that consecutive logical ids run on
+// the same XCD: neighbours (the N-tiles of one row tile, the row tiles of one
+// expert) then share that XCD's L2.  A bijection on [0, nblocks).
+__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
+    const int per = nblocks / kNumXcd, rem = nblocks % kNumXcd;
+    const int x = bid % kNumXcd, i = bid / kNumXcd;
+    const int start = x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per;
+    return start + i;
+}
+
+}  // namespace gmm

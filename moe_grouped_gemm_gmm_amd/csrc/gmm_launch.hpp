@@ -1,0 +1,36 @@
+// Internal launchers behind the C ABI of gmm.h.  Arguments are already
+// validated by gmm_api.cpp; each launcher only enqueues kernels on `stream`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gmm {
+
+hipError_t launch_group_metadata(const int32_t* group_sizes, int G, int M, int tm_log2,
+                                 int32_t* offsets, int32_t* work, int capacity,
+                                 int32_t* num_work, hipStream_t stream);
+
+// x_bf16: true for bf16 input, false for fp32.
+hipError_t launch_quantize_lhs(const void* x, bool x_bf16, int64_t M, int64_t K, uint8_t* q,
+                               float* scale, hipStream_t stream);
+
+hipError_t launch_quantize_rhs(const void* w, bool w_bf16, int64_t G, int64_t K, int64_t N,
+                               uint8_t* q, float* scale, hipStream_t stream);
+
+// lhs_kind: 0 = E4M3 codes + lhs_scale, 1 = bf16, 2 = fp32.
+hipError_t launch_fp8_fwd(const void* lhs, int lhs_kind, const float* lhs_scale,
+                          const uint8_t* rhs, const float* rhs_scale,
+                          const int32_t* group_sizes, int M, int K, int N, int G, void* out,
+                          bool out_bf16, uint8_t* q_out, float* scale_out, hipStream_t stream);
+
+hipError_t launch_bf16_fwd(const void* lhs, const void* rhs, const int32_t* group_sizes, int M,
+                           int K, int N, int G, void* out, bool out_bf16, hipStream_t stream);
+
+hipError_t launch_bf16_dx(const void* dy, const void* w, const int32_t* group_sizes, int M,
+                          int K, int N, int G, void* dx, bool out_bf16, hipStream_t stream);
+
+hipError_t launch_tgmm(const void* x, const void* dy, const int32_t* group_sizes, int M, int K,
+                       int N, int G, void* dw, bool out_bf16, hipStream_t stream);
+
+}  // namespace gmm

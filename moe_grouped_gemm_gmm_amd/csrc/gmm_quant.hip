@@ -1,0 +1,200 @@
+// Blockwise FP8 quantisation kernels and the group-metadata exposer.
+//
+// LHS: one scale per row per 128 K-elements, computed from the data on every
+// call; RHS: one scale per 128x128 block, computed once offline
+// ("GEMM Kernel 性能优化十问", Q2).  The recipe (abs-max, s = a/448, guarded
+// inverse, x*inv cast to E4M3) follows "实现差距：GMM Kernel（V1 vs V2）",
+// section 3.3.
+#include "gmm_device.hpp"
+#include "gmm_launch.hpp"
+
+namespace gmm {
+
+// ------------------------------------------------------------ metadata --
+
+__global__ __launch_bounds__(256) void group_metadata_kernel(const int32_t* __restrict__ group_sizes,
+                                                             int G, int M, int tm_log2,
+                                                             int32_t* __restrict__ offsets,
+                                                             int32_t* __restrict__ work,
+                                                             int capacity,
+                                                             int32_t* __restrict__ num_work) {
+    const int wave = threadIdx.x >> 6, lane = lane_id();
+    const int w = blockIdx.x * 4 + wave;
+    if (w < capacity) {
+        const WorkItem it = find_work_item(group_sizes, G, M, tm_log2, w);
+        if (lane == 0) {
+            work[4 * w + 0] = it.g;
+            work[4 * w + 1] = it.g < 0 ? 0 : it.tile;
+            work[4 * w + 2] = it.g < 0 ? 0 : it.lo;
+            work[4 * w + 3] = it.g < 0 ? 0 : it.hi;
+        }
+    }
+    if (blockIdx.x == 0 && wave == 0) {
+        int carry_rows = 0, carry_items = 0;
+        for (int base = 0; base < G; base += 64) {
+            const int g = base + lane;
+            const int s = g < G ? group_sizes[g] : 0;
+            const int incl = wave_incl_scan(s);
+            const int o = carry_rows + incl - s;
+            const int c = s > 0 ? ((o + s - 1) >> tm_log2) - (o >> tm_log2) + 1 : 0;
+            if (g < G) offsets[g] = o;
+            carry_rows += __shfl(incl, 63, 64);
+            carry_items += __shfl(wave_incl_scan(c), 63, 64);
+        }
+        if (lane == 0) {
+            const int total = carry_rows;
+            const int tm = 1 << tm_log2;
+            const int tail = total < M ? (M + tm - 1) / tm - total / tm : 0;
+            offsets[G] = total;
+            num_work[0] = carry_items + tail;
+        }
+    }
+}
+
+hipError_t launch_group_metadata(const int32_t* group_sizes, int G, int M, int tm_log2,
+                                 int32_t* offsets, int32_t* work, int capacity,
+                                 int32_t* num_work, hipStream_t stream) {
+    const int blocks = (capacity + 3) / 4;
+    hipLaunchKernelGGL(group_metadata_kernel, dim3(blocks), dim3(256), 0, stream, group_sizes, G,
+                       M, tm_log2, offsets, work, capacity, num_work);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------ LHS 1x128 --
+// 16 lanes own one 128-element block (8 elements each, one 16-byte load for
+// bf16); the abs-max is reduced across those 16 lanes.  Each lane works on
+// kUnroll blocks at once to keep several loads in flight (HBM-bound pass).
+
+constexpr int kQuantUnroll = 4;
+
+template <bool BF16>
+__device__ __forceinline__ void load8(const void* __restrict__ x, int64_t elem, float (&v)[8]) {
+    if constexpr (BF16) {
+        const uint4 d = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + elem);
+        v[0] = bf16_lo(d.x); v[1] = bf16_hi(d.x);
+        v[2] = bf16_lo(d.y); v[3] = bf16_hi(d.y);
+        v[4] = bf16_lo(d.z); v[5] = bf16_hi(d.z);
+        v[6] = bf16_lo(d.w); v[7] = bf16_hi(d.w);
+    } else {
+        const float4 a = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + elem);
+        const float4 b = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + elem + 4);
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void quantize_lhs_kernel(const void* __restrict__ x,
+                                                           int64_t nblk, uint8_t* __restrict__ q,
+                                                           float* __restrict__ scale) {
+    const int sub = threadIdx.x & 15;
+    const int64_t group = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+    const int64_t stride = (int64_t)gridDim.x * 16;
+    for (int64_t b0 = group; b0 < nblk; b0 += stride * kQuantUnroll) {
+        float v[kQuantUnroll][8];
+#pragma unroll
+        for (int u = 0; u < kQuantUnroll; ++u) {
+            const int64_t blk = b0 + u * stride;
+            if (blk < nblk) {
+                load8<BF16>(x, blk * kQBlock + sub * 8, v[u]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) v[u][i] = 0.0f;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kQuantUnroll; ++u) {
+            const int64_t blk = b0 + u * stride;
+            float a = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(v[u][i]));
+            a = fmaxf(a, __shfl_xor(a, 1, 16));
+            a = fmaxf(a, __shfl_xor(a, 2, 16));
+            a = fmaxf(a, __shfl_xor(a, 4, 16));
+            a = fmaxf(a, __shfl_xor(a, 8, 16));
+            const float s = quant_scale(a);
+            const float inv = quant_inv(s);
+            uint2 codes;
+            codes.x = e4m3x4(v[u][0] * inv, v[u][1] * inv, v[u][2] * inv, v[u][3] * inv);
+            codes.y = e4m3x4(v[u][4] * inv, v[u][5] * inv, v[u][6] * inv, v[u][7] * inv);
+            if (blk < nblk) {
+                *reinterpret_cast<uint2*>(q + blk * kQBlock + sub * 8) = codes;
+                if (sub == 0) scale[blk] = s;
+            }
+        }
+    }
+}
+
+hipError_t launch_quantize_lhs(const void* x, bool x_bf16, int64_t M, int64_t K, uint8_t* q,
+                               float* scale, hipStream_t stream) {
+    const int64_t nblk = M * (K / kQBlock);
+    int64_t blocks = (nblk + 16 * kQuantUnroll - 1) / (16 * kQuantUnroll);
+    if (blocks > 4096) blocks = 4096;
+    if (x_bf16)
+        hipLaunchKernelGGL(quantize_lhs_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                           x, nblk, q, scale);
+    else
+        hipLaunchKernelGGL(quantize_lhs_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                           x, nblk, q, scale);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------- RHS 128x128 --
+// One workgroup per (g, kb, nb) block.  Thread t owns column n = t % 128 and
+// the 64 K-rows of half t / 128; its 64 codes are contiguous in the K-major
+// output q[g][n][k], so they are stored with four 16-byte writes.
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void quantize_rhs_kernel(const void* __restrict__ w, int K,
+                                                           int N, uint8_t* __restrict__ q,
+                                                           float* __restrict__ scale) {
+    __shared__ float wave_max[4];
+    const int nkb = K / kQBlock, nnb = N / kQBlock;
+    const int blk = blockIdx.x;
+    const int g = blk / (nkb * nnb), kb = (blk / nnb) % nkb, nb = blk % nnb;
+    const int t = threadIdx.x, n = nb * kQBlock + (t & 127), k0 = kb * kQBlock + (t >> 7) * 64;
+    float v[64];
+    const int64_t base = ((int64_t)g * K + k0) * N + n;
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+        if constexpr (BF16)
+            v[i] = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(w)[base + (int64_t)i * N] << 16);
+        else
+            v[i] = reinterpret_cast<const float*>(w)[base + (int64_t)i * N];
+    }
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 64; ++i) a = fmaxf(a, fabsf(v[i]));
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) a = fmaxf(a, __shfl_xor(a, d, 64));
+    if (lane_id() == 0) wave_max[t >> 6] = a;
+    __syncthreads();
+    a = fmaxf(fmaxf(wave_max[0], wave_max[1]), fmaxf(wave_max[2], wave_max[3]));
+    const float s = quant_scale(a);
+    const float inv = quant_inv(s);
+    uint8_t* dst = q + ((int64_t)g * N + n) * K + k0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        uint4 o;
+        o.x = e4m3x4(v[16 * c + 0] * inv, v[16 * c + 1] * inv, v[16 * c + 2] * inv, v[16 * c + 3] * inv);
+        o.y = e4m3x4(v[16 * c + 4] * inv, v[16 * c + 5] * inv, v[16 * c + 6] * inv, v[16 * c + 7] * inv);
+        o.z = e4m3x4(v[16 * c + 8] * inv, v[16 * c + 9] * inv, v[16 * c + 10] * inv, v[16 * c + 11] * inv);
+        o.w = e4m3x4(v[16 * c + 12] * inv, v[16 * c + 13] * inv, v[16 * c + 14] * inv, v[16 * c + 15] * inv);
+        *reinterpret_cast<uint4*>(dst + 16 * c) = o;
+    }
+    if (t == 0) scale[blk] = s;
+}
+
+hipError_t launch_quantize_rhs(const void* w, bool w_bf16, int64_t G, int64_t K, int64_t N,
+                               uint8_t* q, float* scale, hipStream_t stream) {
+    const int64_t blocks = G * (K / kQBlock) * (N / kQBlock);
+    if (w_bf16)
+        hipLaunchKernelGGL(quantize_rhs_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                           w, (int)K, (int)N, q, scale);
+    else
+        hipLaunchKernelGGL(quantize_rhs_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                           w, (int)K, (int)N, q, scale);
+    return hipGetLastError();
+}
+
+}  // namespace gmm

@@ -1,0 +1,54 @@
+"""Shared comparison helpers for the parity tests."""
+import numpy as np
+import torch
+
+# FP8 forward vs the fp64 oracle on the same codes ("GEMM Kernel 性能优化十问",
+# Q9: kernel vs CPU reference of the same quantised computation).
+FP8_ATOL, FP8_RTOL, FP8_MIN_SQNR_DB = 1e-3, 1e-2, 40.0
+# bf16 paths: |gpu - ref| <= 1e-3 + 2e-2 |ref| (fp32 accumulation, bf16 output).
+BF16_ATOL, BF16_RTOL = 1e-3, 2e-2
+
+
+def to_np64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def sqnr_db(ref: np.ndarray, out: np.ndarray) -> float:
+    noise = np.sum((ref - out) ** 2)
+    sig = np.sum(ref ** 2)
+    if noise == 0:
+        return float("inf")
+    return float(10.0 * np.log10(sig / noise))
+
+
+def assert_close(out: np.ndarray, ref: np.ndarray, atol: float, rtol: float, what: str = ""):
+    err = np.abs(out - ref)
+    bound = atol + rtol * np.abs(ref)
+    bad = ~(err <= bound)
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        raise AssertionError("%s: %d of %d elements out of tolerance; first %s: out=%s ref=%s" % (
+            what, int(bad.sum()), bad.size, idx.tolist(),
+            [out[tuple(i)] for i in idx], [ref[tuple(i)] for i in idx]))
+
+
+def assert_fp8_parity(out: np.ndarray, ref: np.ndarray, what: str = ""):
+    assert_close(out, ref, FP8_ATOL, FP8_RTOL, what)
+    if np.any(ref != 0):
+        s = sqnr_db(ref, out)
+        assert s > FP8_MIN_SQNR_DB, "%s: SQNR %.1f dB" % (what, s)
+
+
+def assert_bf16_parity(out: np.ndarray, ref: np.ndarray, what: str = ""):
+    assert_close(out, ref, BF16_ATOL, BF16_RTOL, what)
+
+
+def sample_rows_problem(group_sizes: np.ndarray, rows: np.ndarray):
+    """For sorted absolute row indices, the group sizes of the sub-problem made
+    of just those rows (rows keep their group)."""
+    off = np.concatenate([[0], np.cumsum(group_sizes)])
+    gid = np.searchsorted(off, rows, side="right") - 1
+    G = group_sizes.size
+    gid = np.minimum(gid, G)            # rows past the total -> tail
+    sub = np.bincount(gid[gid < G], minlength=G).astype(np.int32)
+    return sub, gid

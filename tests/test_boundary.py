@@ -1,0 +1,110 @@
+"""The C ABI on the CPU: the library loads, exports every symbol that
+include/gmm.h declares, and rejects bad arguments on the host before any
+launch (no call here reaches the GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import moe_grouped_gemm_gmm_amd as gmm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, NULL, SHAPE, ALIGN, DTYPE = 0, 1, 2, 3, 4
+
+# fake device addresses: never dereferenced, the checks fail first
+A = 0x10000
+MIS = 0x10008
+
+
+def declared_symbols():
+    text = open(os.path.join(ROOT, "include", "gmm.h")).read()
+    text = text.replace("#define GMM_API", "")
+    return sorted(set(re.findall(r"GMM_API\s+[\w\s\*]*?\b(\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return gmm.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_symbols()
+    assert len(names) == 9
+    assert sorted(names) == sorted(gmm.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    assert lib.gmm_status_string(0) == b"ok"
+    assert lib.gmm_status_string(2) == b"invalid shape"
+    assert lib.gmm_status_string(99) == b"unknown status"
+
+
+def P(x):
+    return ctypes.c_void_p(x) if x else None
+
+
+def fp8(lib, lhs=A, lhs_dt=1, lhs_scale=0, rhs=A, rhs_scale=A, gs=A, M=256, K=256, N=256, G=4,
+        out=A, out_dt=1, q=0, s=0):
+    return lib.gmm_fp8_fwd(P(lhs), lhs_dt, P(lhs_scale), P(rhs), P(rhs_scale), P(gs), M, K, N, G,
+                           P(out), out_dt, P(q), P(s), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(lhs=0), NULL), (dict(rhs=0), NULL), (dict(rhs_scale=0), NULL), (dict(gs=0), NULL),
+    (dict(out=0), NULL),
+    (dict(lhs=MIS), ALIGN), (dict(out=MIS), ALIGN), (dict(q=MIS, s=A), ALIGN),
+    (dict(q=A), NULL),
+    (dict(K=200), SHAPE), (dict(N=100), SHAPE), (dict(K=0), SHAPE), (dict(G=0), SHAPE),
+    (dict(G=5000), SHAPE), (dict(M=-1), SHAPE),
+    (dict(lhs_dt=7), DTYPE), (dict(out_dt=2), DTYPE),
+    (dict(lhs_dt=2), NULL),                       # E4M3 lhs needs lhs_scale
+    (dict(lhs_dt=2, lhs_scale=A, q=A, s=A), DTYPE),
+    (dict(lhs_scale=A), DTYPE),
+    (dict(M=0), OK),                              # empty input: nothing to do
+])
+def test_fp8_fwd_rejections(lib, kw, status):
+    assert fp8(lib, **kw) == status
+    if status:
+        assert lib.gmm_last_error()
+
+
+def test_quantize_rejections(lib):
+    q = lib.gmm_quantize_lhs
+    assert q(P(A), 1, 16, 100, P(A), P(A), None) == SHAPE
+    assert q(P(A), 2, 16, 128, P(A), P(A), None) == DTYPE
+    assert q(None, 1, 16, 128, P(A), P(A), None) == NULL
+    assert q(P(A), 1, 16, 128, P(MIS), P(A), None) == ALIGN
+    assert q(P(A), 1, 0, 128, P(A), P(A), None) == OK
+    r = lib.gmm_quantize_rhs
+    assert r(P(A), 1, 2, 128, 200, P(A), P(A), None) == SHAPE
+    assert r(P(A), 1, 0, 128, 128, P(A), P(A), None) == SHAPE
+    assert r(P(A), 0, 2, 128, 128, None, P(A), None) == NULL
+
+
+def test_bf16_rejections(lib):
+    f, t, d = lib.gmm_bf16_fwd, lib.tgmm_bf16, lib.gmm_bf16_dx
+    assert f(P(A), P(A), P(A), 64, 100, 128, 2, P(A), 1, None) == SHAPE
+    assert f(P(A), P(A), P(A), 64, 128, 64, 2, P(A), 1, None) == SHAPE
+    assert f(P(A), P(A), P(A), 64, 128, 128, 2, P(A), 3, None) == DTYPE
+    assert f(P(A), None, P(A), 64, 128, 128, 2, P(A), 1, None) == NULL
+    assert f(P(A), P(A), P(A), 0, 128, 128, 2, P(A), 1, None) == OK
+    assert t(P(A), P(A), P(A), 64, 64, 128, 2, P(A), 1, None) == SHAPE
+    assert t(P(A), P(MIS), P(A), 64, 128, 128, 2, P(A), 1, None) == ALIGN
+    assert d(P(A), P(A), P(A), 64, 128, 96, 2, P(A), 1, None) == SHAPE
+    assert d(P(A), P(A), P(A), 64, 128, 128, 0, P(A), 1, None) == SHAPE
+
+
+def test_metadata_rejections(lib):
+    m = lib.gmm_group_metadata
+    assert m(P(A), 4, 100, 100, P(A), P(A), 100, P(A), None) == SHAPE   # tile not a power of two
+    assert m(P(A), 4, 1000, 128, P(A), P(A), 5, P(A), None) == SHAPE    # capacity too small
+    assert m(P(A), 4, 1000, 128, P(A), None, 20, P(A), None) == NULL
+
+
+def test_binding_raises_on_error(lib):
+    with pytest.raises(gmm.GmmError) as e:
+        gmm._check(SHAPE)
+    assert e.value.status == SHAPE

@@ -1,0 +1,141 @@
+"""GPU parity of the bf16 grouped matmuls (forward baseline, tgmm, dX) against
+the fp64 oracle: |gpu - ref| <= 1e-3 + 2e-2 |ref| ("GEMM Kernel 性能优化十问",
+Q5: the backward pass is unquantised bf16 with fp32 accumulation)."""
+import numpy as np
+import pytest
+import torch
+
+import moe_grouped_gemm_gmm_amd as gmm
+import oracle
+import workloads
+from helpers import assert_bf16_parity, sample_rows_problem, to_np64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+EDGE = [
+    (1, 128, 128, [1]),
+    (7, 256, 256, [3, 0, 4]),
+    (129, 384, 128, [0, 129]),
+    (300, 256, 384, [100, 0, 0, 150]),
+    (1000, 512, 256, [1] * 200 + [800]),
+    (513, 128, 256, [0, 0, 513, 0]),
+    (640, 256, 128, [128, 128, 128, 128, 128]),
+]
+
+
+def _gs(wl):
+    return torch.from_numpy(wl.group_sizes).to(DEV)
+
+
+@pytest.mark.parametrize("M,K,N,gs", EDGE)
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_bf16_fwd_edges(M, K, N, gs, out_dtype):
+    wl = workloads.custom(M, K, N, gs, seed=M + 3 * K, w_std=0.05)
+    out = torch.full((M, N), float("nan"), dtype=out_dtype, device=DEV)
+    gmm.gmm_bf16_fwd(wl.x.to(DEV), wl.w.to(DEV), _gs(wl), out=out)
+    ref = oracle.gmm(workloads.as_f32(wl.x), workloads.as_f32(wl.w), wl.group_sizes)
+    o = to_np64(out)
+    assert (o[int(wl.group_sizes.sum()):] == 0).all()
+    assert_bf16_parity(o, ref, "bf16 fwd")
+
+
+@pytest.mark.parametrize("M,K,N,gs", EDGE)
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_dx_edges(M, K, N, gs, out_dtype):
+    wl = workloads.custom(M, K, N, gs, seed=M + 5 * K, w_std=0.05, with_dy=True)
+    out = torch.full((M, K), float("nan"), dtype=out_dtype, device=DEV)
+    gmm.gmm_bf16_dx(wl.dy.to(DEV), wl.w.to(DEV), _gs(wl), out=out)
+    ref = oracle.gmm_dx(workloads.as_f32(wl.dy), workloads.as_f32(wl.w), wl.group_sizes)
+    o = to_np64(out)
+    assert (o[int(wl.group_sizes.sum()):] == 0).all()
+    assert_bf16_parity(o, ref, "dx")
+
+
+@pytest.mark.parametrize("M,K,N,gs", EDGE)
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_tgmm_edges(M, K, N, gs, out_dtype):
+    wl = workloads.custom(M, K, N, gs, seed=M + 7 * K, with_dy=True)
+    G = len(gs)
+    out = torch.full((G, K, N), float("nan"), dtype=out_dtype, device=DEV)
+    gmm.tgmm_bf16(wl.x.to(DEV), wl.dy.to(DEV), _gs(wl), out=out)
+    ref = oracle.tgmm(workloads.as_f32(wl.x), workloads.as_f32(wl.dy), wl.group_sizes)
+    o = to_np64(out)
+    for g in range(G):
+        if gs[g] == 0:
+            assert (o[g] == 0).all(), "empty group must give exactly zero"
+    assert_bf16_parity(o, ref, "tgmm")
+
+
+def test_tgmm_ignores_tail_rows():
+    wl = workloads.custom(300, 128, 128, [100, 150], seed=31, with_dy=True)
+    x = wl.x.clone()
+    x[250:] = 1e30
+    a = gmm.tgmm_bf16(wl.x.to(DEV), wl.dy.to(DEV), _gs(wl), out_dtype=torch.float32)
+    b = gmm.tgmm_bf16(x.to(DEV), wl.dy.to(DEV), _gs(wl), out_dtype=torch.float32)
+    assert torch.equal(a, b)
+
+
+def test_exact_integers_bitwise():
+    """Small-integer inputs: every fp32 partial sum is exact, so fwd, dX and tgmm
+    must equal the oracle bit for bit."""
+    r = workloads.rng(41, 0)
+    M, K, N = 300, 256, 256
+    gs = np.array([120, 0, 180], np.int32)
+    x = torch.from_numpy(r.integers(-8, 9, (M, K)).astype(np.float32)).to(torch.bfloat16)
+    w = torch.from_numpy(r.integers(-8, 9, (3, K, N)).astype(np.float32)).to(torch.bfloat16)
+    dy = torch.from_numpy(r.integers(-8, 9, (M, N)).astype(np.float32)).to(torch.bfloat16)
+    g = torch.from_numpy(gs).to(DEV)
+    xf, wf, dyf = workloads.as_f32(x), workloads.as_f32(w), workloads.as_f32(dy)
+    assert np.array_equal(to_np64(gmm.gmm_bf16_fwd(x.to(DEV), w.to(DEV), g, out_dtype=torch.float32)),
+                          oracle.gmm(xf, wf, gs))
+    assert np.array_equal(to_np64(gmm.gmm_bf16_dx(dy.to(DEV), w.to(DEV), g, out_dtype=torch.float32)),
+                          oracle.gmm_dx(dyf, wf, gs))
+    assert np.array_equal(to_np64(gmm.tgmm_bf16(x.to(DEV), dy.to(DEV), g, out_dtype=torch.float32)),
+                          oracle.tgmm(xf, dyf, gs))
+
+
+def test_bwd_config_full():
+    """Backward at the wi shape (M=8192, G=32, K=2048, N=512), all bf16 N(0,1)."""
+    wl = workloads.make("bwd", seed=0)
+    g = _gs(wl)
+    x, w, dy = wl.x.to(DEV), wl.w.to(DEV), wl.dy.to(DEV)
+    xf, wf, dyf = workloads.as_f32(wl.x), workloads.as_f32(wl.w), workloads.as_f32(wl.dy)
+    for out_dtype in (torch.bfloat16, torch.float32):
+        dw = gmm.tgmm_bf16(x, dy, g, out_dtype=out_dtype)
+        assert_bf16_parity(to_np64(dw), oracle.tgmm(xf, dyf, wl.group_sizes), "tgmm bwd")
+    dx = gmm.gmm_bf16_dx(dy, w, g)
+    assert_bf16_parity(to_np64(dx), oracle.gmm_dx(dyf, wf, wl.group_sizes), "dx bwd")
+    y = gmm.gmm_bf16_fwd(x, w, g)
+    assert_bf16_parity(to_np64(y), oracle.gmm(xf, wf, wl.group_sizes), "fwd bwd-shape")
+
+
+def test_wi_bf16_baseline_full():
+    wl = workloads.make("wi", seed=0, with_dy=False)
+    y = gmm.gmm_bf16_fwd(wl.x.to(DEV), wl.w.to(DEV), _gs(wl))
+    assert_bf16_parity(to_np64(y), oracle.gmm(workloads.as_f32(wl.x), workloads.as_f32(wl.w),
+                                               wl.group_sizes), "bf16 wi")
+
+
+def test_full_config_backward_sampled():
+    """Production shape: tgmm checked on a sample of experts (including the
+    heaviest and an empty one if any), dX on a row sample."""
+    wl = workloads.make("full", seed=0)
+    g = _gs(wl)
+    x, w, dy = wl.x.to(DEV), wl.w.to(DEV), wl.dy.to(DEV)
+    dw = gmm.tgmm_bf16(x, dy, g)
+    dx = gmm.gmm_bf16_dx(dy, w, g)
+    torch.cuda.synchronize()
+    gs = wl.group_sizes
+    off = np.concatenate([[0], np.cumsum(gs)])
+    r = workloads.rng(77, 0)
+    experts = sorted(set([int(np.argmax(gs)), int(np.argmin(gs))] + r.choice(wl.G, 6, replace=False).tolist()))
+    xf, dyf = workloads.as_f32(wl.x), workloads.as_f32(wl.dy)
+    for e in experts:
+        rows = slice(off[e], off[e + 1])
+        ref = oracle.tgmm(xf[rows], dyf[rows], np.array([gs[e]], np.int32))[0]
+        assert_bf16_parity(to_np64(dw[e]), ref, "tgmm full expert %d" % e)
+    rows = np.array(sorted(set(r.choice(wl.M, 384, replace=False).tolist())))
+    sub_gs, _ = sample_rows_problem(gs, rows)
+    ref = oracle.gmm_dx(dyf[rows], workloads.as_f32(wl.w), sub_gs)
+    assert_bf16_parity(to_np64(dx)[rows], ref, "dx full sampled")
