@@ -107,8 +107,10 @@ GMM_API int gmm_quantize_lhs(const void *x, int x_dtype, int64_t M, int64_t K,
  * (done once, offline: "GEMM Kernel 性能优化十问", Q2 and Q5).
  *   Same recipe as gmm_quantize_lhs over each 128x128 block (g, kb, nb).
  * w:     [G,K,N], w_dtype GMM_BF16 or GMM_F32.
- * q:     [G,N,K] E4M3 codes, stored K-contiguous (the transpose of w per
- *        expert), which is the layout gmm_fp8_fwd reads.
+ * q:     G*N*K bytes of E4M3 codes in the packed order gmm_fp8_fwd reads
+ *        (the MFMA operand layout): [G][N/16][K/128][2][64][16], where byte
+ *        (h, l, e) of slab (g, nb, kb) is the code of column n = 16*nb + l%16,
+ *        k = 128*kb + 32*(l/16) + 16*h + e.
  * scale: [G,K/128,N/128] fp32.
  * K and N must be multiples of 128.
  */
@@ -117,7 +119,7 @@ GMM_API int gmm_quantize_rhs(const void *w, int w_dtype, int64_t G, int64_t K,
 
 /*
  * gmm_fp8_fwd -- blockwise-FP8 grouped matmul forward.
- *   out[m,n] = sum_b ( sum_{k in block b} ql[m,k] qr[g,n,k] )
+ *   out[m,n] = sum_b ( sum_{k in block b} ql[m,k] qr[g,k,n] )
  *                    * sl[m,b] * sr[g,b,n/128]        for m in group g,
  *   with fp32 accumulation of exact FP8 products; rows past the total are 0.
  *   ("GEMM Kernel 性能优化十问", Q3: each 128-wide K subchannel is scaled and
@@ -127,8 +129,8 @@ GMM_API int gmm_quantize_rhs(const void *w, int w_dtype, int64_t G, int64_t K,
  *            kernel with the gmm_quantize_lhs recipe (bit-identical codes
  *            and scales); GMM_E4M3: codes, with lhs_scale [M,K/128].
  * lhs_scale: NULL unless lhs_dtype == GMM_E4M3.
- * rhs:       [G,N,K] E4M3 codes; rhs_scale [G,K/128,N/128] fp32 (as written
- *            by gmm_quantize_rhs).
+ * rhs:       packed E4M3 codes and rhs_scale [G,K/128,N/128] fp32, exactly as
+ *            written by gmm_quantize_rhs.
  * out:       [M,N], out_dtype GMM_BF16 (round to nearest even) or GMM_F32.
  * q_out, scale_out: NULL, or [M,K] codes and [M,K/128] scales that receive
  *            the in-kernel quantisation of lhs (only with bf16/f32 lhs).

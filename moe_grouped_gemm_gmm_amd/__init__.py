@@ -109,10 +109,12 @@ def gmm_quantize_lhs(x: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
 
 
 def gmm_quantize_rhs(w: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
-    """128x128 quantisation of w [G,K,N] -> (codes uint8 [G,N,K] K-contiguous, scales [G,K/128,N/128])."""
+    """128x128 quantisation of w [G,K,N] -> (packed codes uint8 [G, N/16, K/128, 2048],
+    scales f32 [G, K/128, N/128]).  The packed order is the one gmm_fp8_fwd reads
+    (include/gmm.h, gmm_quantize_rhs)."""
     lib = load_library()
     G, K, N = w.shape
-    q = torch.empty((G, N, K), dtype=torch.uint8, device=w.device)
+    q = torch.empty((G, max(N // 16, 0), max(K // 128, 0), 2048), dtype=torch.uint8, device=w.device)
     s = torch.empty((G, max(K // 128, 0), max(N // 128, 0)), dtype=torch.float32, device=w.device)
     _check(lib.gmm_quantize_rhs(_ptr(w), _dt(w), G, K, N, _ptr(q), _ptr(s), _stream(w)))
     return q, s
@@ -124,12 +126,13 @@ def gmm_fp8_fwd(lhs: torch.Tensor, rhs_q: torch.Tensor, rhs_scale: torch.Tensor,
                 q_out: Optional[torch.Tensor] = None, scale_out: Optional[torch.Tensor] = None
                 ) -> torch.Tensor:
     """Blockwise-FP8 GMM.  lhs [M,K] bf16/fp32 (quantised in-kernel) or uint8 codes
-    with lhs_scale; rhs_q [G,N,K] codes, rhs_scale [G,K/128,N/128]."""
+    with lhs_scale [M,K/128]; rhs_q, rhs_scale as returned by gmm_quantize_rhs."""
     lib = load_library()
     M, K = lhs.shape
-    G, N, K2 = rhs_q.shape
-    if K2 != K:
-        raise ValueError("lhs K=%d but rhs K=%d" % (K, K2))
+    G, N16, KB, slab = rhs_q.shape
+    N = N16 * 16
+    if slab != 2048 or KB * 128 != K:
+        raise ValueError("rhs_q shape %s does not match K=%d" % (tuple(rhs_q.shape), K))
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=lhs.device)
     _check(lib.gmm_fp8_fwd(_ptr(lhs), _dt(lhs), _ptr(lhs_scale), _ptr(rhs_q), _ptr(rhs_scale),

@@ -8,229 +8,369 @@
 // （V1 vs V2）", section 2.1).  The LHS arrives either as bf16/fp32 and is
 // quantised here, per row and subchannel, with the same recipe as
 // gmm_quantize_lhs (section 3.3 of the same page), or as E4M3 codes with
-// their scales.  The RHS is E4M3 codes stored K-contiguous per expert
-// ([G,N,K]) with 128x128 block scales.
+// their scales.  The RHS is E4M3 codes with 128x128 block scales, stored by
+// gmm_quantize_rhs in the MFMA operand order: per expert, 16-column block and
+// subchannel, 2 KB holding the 32 K-values each of the 64 lanes needs as two
+// 16-byte runs (byte h*1024 + lane*16 + e is column 16*blk + lane%16,
+// k = 128*kb + 32*(lane/16) + 16*h + e).
 //
-// One workgroup (4 waves) computes a 128x128 output tile of one work item
-// (an expert's rows within a 128-row tile, from the in-kernel metadata).
-// Per subchannel both operands are staged in LDS as E4M3 codes; each wave
-// multiplies a 64x64 sub-tile with 16 v_mfma_scale_f32_16x16x128_f8f6f4
-// (neutral E8M0 scales: the products are exact), and folds each 16x16
-// partial into the fp32 accumulator with one FMA per element:
-// acc += p * (sl[row] * sr).  Rows outside the item's range are zero codes in
-// LDS and are never stored.
+// Work decomposition.  A workgroup of 8 waves (two per SIMD, so one wave's
+// VALU work issues while the other's MFMAs run) owns 64 rows of one work item
+// (an expert's rows inside a 64-row tile, from the in-kernel metadata
+// routine) and TN = 8*WN output columns; wave w owns columns [w*WN, (w+1)*WN)
+// of the tile.  Per 128-wide subchannel:
+//  - A: wave w quantises rows 8w..8w+7; a lane holds 8 consecutive K values
+//    of two rows (16 lanes per row, so each load reads whole 128-byte lines)
+//    and the row's abs-max is reduced over those 16 lanes.  Every row is
+//    quantised once per workgroup.  Codes go to a double-buffered LDS tile,
+//    and with them the products sl[row] * sr[n-block] for each 128-column
+//    block of the tile, so the MFMA waves read their per-row factors
+//    ready-made.
+//  - B: each wave loads its own columns straight from global memory into the
+//    MFMA operand registers: two 16-byte loads per lane per 16-column block,
+//    each instruction reading one contiguous kilobyte of the packed RHS.  No
+//    two waves share B, so it never goes through LDS.  Each column block is
+//    reloaded with the next subchannel as soon as its MFMAs are issued.
+//  - Raw A is loaded two subchannels ahead and quantised one ahead of the
+//    MFMAs that use it; one barrier per subchannel.  The loop body has no
+//    branches (prefetch indices are clamped), so loads stay in flight across
+//    iterations instead of being drained at control-flow joins.
+//  - Each 16x16 block is one v_mfma_scale_f32_16x16x128_f8f6f4 (neutral E8M0
+//    scales: the FP8 products are exact) into a zero temporary, folded into
+//    the fp32 accumulator with one FMA per element: acc += p * (sl * sr).
+//  - The tile is written through LDS so that global stores are full rows.
 #include "gmm_device.hpp"
 #include "gmm_launch.hpp"
+
+#include <cstdio>
+#include <cstdlib>
 
 namespace gmm {
 
 namespace {
 
-constexpr int kTM = 128, kTN = 128, kTK = 128;
-constexpr int kPad = 16;  // LDS row padding (bytes): 144-byte rows are bank-conflict free for
-                          // the 16-lane ds_read_b128 pattern below
+constexpr int kTM = 64;            // rows per workgroup
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kTK = 128;           // one subchannel
+constexpr int kLdsRow = kTK + 16;  // 144-byte LDS rows: conflict-free 16-lane ds_read_b128
 
 enum LhsKind { kLhsE4M3 = 0, kLhsBF16 = 1, kLhsF32 = 2 };
 
-// Quantise 64 consecutive K-elements of one row (this thread's half of a
-// 128-wide subchannel; the partner half is in lane ^ 1) into 64 codes.
+// Raw LHS registers of one subchannel for this lane: rows r and r+4 of the
+// wave's 8 rows, 8 consecutive K values of each (16 lanes cover a row's 128
+// values, so every load instruction reads whole 128-byte lines).
 template <int KIND>
-__device__ __forceinline__ float quantize_half_row(const void* __restrict__ lhs, int64_t elem,
-                                                   bool valid, uint4 (&codes)[4]) {
-    float v[64];
-    if (valid) {
-        if constexpr (KIND == kLhsBF16) {
-            const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(lhs) + elem);
+struct RawA;
+template <>
+struct RawA<kLhsBF16> { uint4 d[2]; };
+template <>
+struct RawA<kLhsF32> { uint4 d[2][2]; };
+template <>
+struct RawA<kLhsE4M3> { uint2 d[2]; float s[2]; };
+
+// `row[p]` is always an in-bounds row (invalid lanes pass a clamped one) and
+// the loaded values are zeroed by a select, so the loads are unconditional and
+// the main loop stays free of divergent branches.
+template <int KIND>
+__device__ __forceinline__ void load_raw(RawA<KIND>& r, const void* __restrict__ lhs,
+                                         const float* __restrict__ lhs_scale,
+                                         const int64_t (&row)[2], int K, int kb, int chunk,
+                                         const bool (&valid)[2]) {
 #pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                const uint4 d = p[c];
-                v[8 * c + 0] = bf16_lo(d.x); v[8 * c + 1] = bf16_hi(d.x);
-                v[8 * c + 2] = bf16_lo(d.y); v[8 * c + 3] = bf16_hi(d.y);
-                v[8 * c + 4] = bf16_lo(d.z); v[8 * c + 5] = bf16_hi(d.z);
-                v[8 * c + 6] = bf16_lo(d.w); v[8 * c + 7] = bf16_hi(d.w);
+    for (int p = 0; p < 2; ++p) {
+        const int64_t e = row[p] * K + kb * kTK + chunk * 8;
+        if constexpr (KIND == kLhsBF16) {
+            const uint4 d = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(lhs) + e);
+            r.d[p] = make_uint4(valid[p] ? d.x : 0u, valid[p] ? d.y : 0u, valid[p] ? d.z : 0u, valid[p] ? d.w : 0u);
+        } else if constexpr (KIND == kLhsF32) {
+            const uint4* q = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(lhs) + e);
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                const uint4 d = q[c];
+                r.d[p][c] = make_uint4(valid[p] ? d.x : 0u, valid[p] ? d.y : 0u, valid[p] ? d.z : 0u, valid[p] ? d.w : 0u);
             }
         } else {
-            const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(lhs) + elem);
-#pragma unroll
-            for (int c = 0; c < 16; ++c) {
-                const float4 d = p[c];
-                v[4 * c + 0] = d.x; v[4 * c + 1] = d.y; v[4 * c + 2] = d.z; v[4 * c + 3] = d.w;
-            }
+            const uint2 d = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(lhs) + e);
+            r.d[p] = make_uint2(valid[p] ? d.x : 0u, valid[p] ? d.y : 0u);
+            const float s = lhs_scale[row[p] * (K / kTK) + kb];
+            r.s[p] = valid[p] ? s : 0.0f;
         }
-    } else {
-#pragma unroll
-        for (int i = 0; i < 64; ++i) v[i] = 0.0f;
     }
-    float a = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 64; ++i) a = fmaxf(a, fabsf(v[i]));
-    a = fmaxf(a, __shfl_xor(a, 1, 64));
-    const float s = quant_scale(a);
-    const float inv = quant_inv(s);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        codes[c].x = e4m3x4(v[16 * c + 0] * inv, v[16 * c + 1] * inv, v[16 * c + 2] * inv, v[16 * c + 3] * inv);
-        codes[c].y = e4m3x4(v[16 * c + 4] * inv, v[16 * c + 5] * inv, v[16 * c + 6] * inv, v[16 * c + 7] * inv);
-        codes[c].z = e4m3x4(v[16 * c + 8] * inv, v[16 * c + 9] * inv, v[16 * c + 10] * inv, v[16 * c + 11] * inv);
-        codes[c].w = e4m3x4(v[16 * c + 12] * inv, v[16 * c + 13] * inv, v[16 * c + 14] * inv, v[16 * c + 15] * inv);
-    }
-    return s;
 }
 
-template <int KIND, bool OUT_BF16>
-__global__ __launch_bounds__(256, 1) void fp8_fwd_kernel(
+// 8 values of row p -> 8 codes, and the row's scale (the abs-max is reduced
+// over the 16 lanes lane ^ {1, 2, 4, 8} that hold the row).
+template <int KIND>
+__device__ __forceinline__ float quantize_raw(const RawA<KIND>& r, int p, uint2& codes) {
+    if constexpr (KIND == kLhsE4M3) {
+        codes = r.d[p];
+        return r.s[p];
+    } else {
+        float v[8];
+        if constexpr (KIND == kLhsBF16) {
+            v[0] = bf16_lo(r.d[p].x); v[1] = bf16_hi(r.d[p].x);
+            v[2] = bf16_lo(r.d[p].y); v[3] = bf16_hi(r.d[p].y);
+            v[4] = bf16_lo(r.d[p].z); v[5] = bf16_hi(r.d[p].z);
+            v[6] = bf16_lo(r.d[p].w); v[7] = bf16_hi(r.d[p].w);
+        } else {
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                v[4 * c + 0] = __uint_as_float(r.d[p][c].x); v[4 * c + 1] = __uint_as_float(r.d[p][c].y);
+                v[4 * c + 2] = __uint_as_float(r.d[p][c].z); v[4 * c + 3] = __uint_as_float(r.d[p][c].w);
+            }
+        }
+        float a = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(v[i]));
+        a = fmaxf(a, __shfl_xor(a, 1, 64));
+        a = fmaxf(a, __shfl_xor(a, 2, 64));
+        a = fmaxf(a, __shfl_xor(a, 4, 64));
+        a = fmaxf(a, __shfl_xor(a, 8, 64));
+        const float s = quant_scale(a);
+        const float inv = quant_inv(s);
+        codes.x = e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+        codes.y = e4m3x4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
+        return s;
+    }
+}
+
+template <int WN>
+struct Smem {
+    static constexpr int TN = kWaves * WN;
+    static constexpr int NBLK = TN / 128 > 0 ? TN / 128 : 1;   // 128-column scale blocks per tile
+    uint8_t a[2][kTM][kLdsRow];         // E4M3 codes of the current and next subchannel
+    float c[2][NBLK][kTM];              // sl[row] * sr[n-block]
+};
+
+template <int KIND, bool OUT_BF16, int WN, bool WRITE_Q>
+__global__ __launch_bounds__(kThreads, 1) void fp8_fwd_kernel(
     const void* __restrict__ lhs, const float* __restrict__ lhs_scale,
     const uint8_t* __restrict__ rhs, const float* __restrict__ rhs_scale,
     const int32_t* __restrict__ group_sizes, int M, int K, int N, int G, void* __restrict__ out,
     uint8_t* __restrict__ q_out, float* __restrict__ s_out, int ntiles_n, int nblocks) {
-    __shared__ WorkItem s_item;
-    __shared__ __attribute__((aligned(16))) uint8_t sA[kTM][kTK + kPad];
-    __shared__ __attribute__((aligned(16))) uint8_t sB[kTN][kTK + kPad];
-    __shared__ float sSl[kTM];
+    constexpr int MB = kTM / 16;  // 16-row blocks
+    constexpr int NB = WN / 16;   // 16-column blocks per wave
+    constexpr int TN = kWaves * WN;
+    constexpr int NBLK = Smem<WN>::NBLK;
+    constexpr int OUT_BYTES = OUT_BF16 ? 2 : 4;
+    constexpr int OUT_ROW = TN * OUT_BYTES + 16;   // padded output staging row
+    constexpr int SMEM_MAIN = sizeof(Smem<WN>);
+    constexpr int SMEM_OUT = kTM * OUT_ROW;
+    constexpr int SMEM = SMEM_MAIN > SMEM_OUT ? SMEM_MAIN : SMEM_OUT;
 
-    const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+    __shared__ WorkItem s_item;
+    __shared__ __attribute__((aligned(16))) uint8_t smem_raw[SMEM];
+    Smem<WN>& sm = *reinterpret_cast<Smem<WN>*>(smem_raw);
+
+    const int tid = threadIdx.x, lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int L = xcd_remap(blockIdx.x, nblocks);
     const int w = L / ntiles_n, nt = L % ntiles_n;
     if (wave == 0) {
-        const WorkItem it = find_work_item(group_sizes, G, M, 7, w);
+        const WorkItem it = find_work_item(group_sizes, G, M, 6, w);
         if (lane == 0) s_item = it;
     }
     __syncthreads();
     const WorkItem it = s_item;
     if (it.g < 0) return;
-    const int n0 = nt * kTN;
+    const int n0 = nt * TN;
 
     if (it.g == G) {  // rows past the last group: zeros
         const int rows = it.hi - it.lo;
-        for (int e = tid; e < rows * (kTN / 8); e += 256) {
-            const int r = it.lo + e / (kTN / 8), c = n0 + (e % (kTN / 8)) * 8;
-            if constexpr (OUT_BF16)
-                *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + (int64_t)r * N + c) = make_uint4(0, 0, 0, 0);
-            else {
-                float4* p = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + (int64_t)r * N + c);
-                p[0] = make_float4(0, 0, 0, 0);
-                p[1] = make_float4(0, 0, 0, 0);
-            }
+        constexpr int V = 16 / OUT_BYTES;  // elements per 16-byte store
+        for (int e = tid; e < rows * (TN / V); e += kThreads) {
+            const int r = it.lo + e / (TN / V), c = n0 + (e % (TN / V)) * V;
+            *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(out) + ((int64_t)r * N + c) * OUT_BYTES) =
+                make_uint4(0, 0, 0, 0);
         }
         return;
     }
 
     const int g = it.g, row0 = it.tile * kTM;
-    const int nkb = K / kQBlock, nnb = N / kQBlock;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int lr = lane & 15, lk = (lane >> 4) * 32;
+    const int nkb = K / kTK, nnb = N / kQBlock;
 
-    // staging roles: thread -> (row or column, K half)
-    const int st_r = tid >> 1, st_h = tid & 1;
-    const int a_row = row0 + st_r;
-    const bool a_valid = a_row >= it.lo && a_row < it.hi;
-    const bool write_q = q_out != nullptr && nt == 0 && a_valid;
-    const uint8_t* b_src = rhs + ((int64_t)g * N + n0 + st_r) * K + st_h * 64;
-
-    v4f acc[4][4];
+    // ---- quantiser role: rows 8*wave + (lane >> 4) + 4p (p = 0, 1), K values
+    //      8*(lane & 15) .. +7 of each
+    const int qchunk = lane & 15;
+    int qrow[2];
+    int64_t qgrow[2], qlrow[2];
+    bool qvalid[2], write_q[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int p = 0; p < 2; ++p) {
+        qrow[p] = 8 * wave + (lane >> 4) + 4 * p;
+        qgrow[p] = row0 + qrow[p];
+        qvalid[p] = qgrow[p] >= it.lo && qgrow[p] < it.hi;
+        qlrow[p] = qvalid[p] ? qgrow[p] : it.lo;    // in-bounds row the loads use
+        write_q[p] = WRITE_Q && nt == 0 && qvalid[p];
+    }
+    const float* srg = rhs_scale + (int64_t)g * nkb * nnb + n0 / kQBlock;  // + kb*nnb + nblk
 
+    // ---- MFMA role: columns [n0 + wave*WN, +WN); lane = row/col lr, K chunk lc.
+    //      B is the packed RHS: 2 KB per (16-column block, subchannel), this
+    //      lane's 32 codes at byte lane*16 of each 1 KB half.
+    const int lr = lane & 15, lc = lane >> 4;
+    const int ncol0 = n0 + wave * WN;
+    const int my_nblk = (wave * WN) / 128;
+    const uint8_t* bptr = rhs + ((int64_t)g * (N / 16) + ncol0 / 16) * nkb * 2048 + lane * 16;
+
+    v4f acc[MB][NB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    RawA<KIND> raw;
+    v8i b[NB];
+
+    // Quantise the raw registers (subchannel kb) into LDS buffer buf.  The
+    // RHS scales of the tile's 128-column blocks are wave-uniform scalar loads.
+    auto quant_store = [&](int kb, int buf) {
+        const float* srk = srg + kb * nnb;   // wave-uniform: scalar loads
+        float srv[NBLK];
+#pragma unroll
+        for (int q = 0; q < NBLK; ++q) srv[q] = srk[q];
+        float sr = srv[0];
+#pragma unroll
+        for (int q = 1; q < NBLK; ++q) sr = qchunk == q ? srv[q] : sr;
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            uint2 codes;
+            const float s = quantize_raw<KIND>(raw, p, codes);
+            *reinterpret_cast<uint2*>(&sm.a[buf][qrow[p]][qchunk * 8]) = codes;
+            if (qchunk < NBLK) sm.c[buf][qchunk][qrow[p]] = s * sr;
+            if (write_q[p]) {
+                *reinterpret_cast<uint2*>(q_out + qgrow[p] * K + kb * kTK + qchunk * 8) = codes;
+                if (qchunk == 0) s_out[qgrow[p] * nkb + kb] = s;
+            }
+        }
+    };
+    auto load_b = [&](int j, int kb) {
+        const uint8_t* p = bptr + ((int64_t)j * nkb + kb) * 2048;
+        const uint4 lo = *reinterpret_cast<const uint4*>(p);
+        const uint4 hi = *reinterpret_cast<const uint4*>(p + 1024);
+        b[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    };
+
+    // ---- prologue: subchannel 0 quantised in LDS, raw subchannel 1 and B(0) in registers
+    load_raw<KIND>(raw, lhs, lhs_scale, qlrow, K, 0, qchunk, qvalid);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) load_b(j, 0);
+    quant_store(0, 0);
+    load_raw<KIND>(raw, lhs, lhs_scale, qlrow, K, min(1, nkb - 1), qchunk, qvalid);
+    __syncthreads();
+
+    // Iteration kb (straight-line code, so loads stay in flight across it):
+    // MFMAs of kb from LDS buffer kb&1, each B column block reloaded with
+    // kb+1 right after its MFMAs; raw(kb+1) quantised into buffer (kb+1)&1;
+    // raw(kb+2) loads issued.  Prefetch indices are clamped to the last
+    // subchannel (a redundant reload) instead of branching.
     for (int kb = 0; kb < nkb; ++kb) {
-        // ---- stage A (quantise or copy codes) and B codes into LDS
-        uint4 ac[4];
-        float sl;
-        if constexpr (KIND == kLhsE4M3) {
-            if (a_valid) {
-                const uint4* p = reinterpret_cast<const uint4*>(
-                    reinterpret_cast<const uint8_t*>(lhs) + (int64_t)a_row * K + kb * kTK + st_h * 64);
+        const int buf = kb & 1;
+        const int kb1 = min(kb + 1, nkb - 1), kb2 = min(kb + 2, nkb - 1);
+        v8i af[MB];
+        v4f cf[MB];
 #pragma unroll
-                for (int c = 0; c < 4; ++c) ac[c] = p[c];
-                sl = lhs_scale[(int64_t)a_row * nkb + kb];
-            } else {
-#pragma unroll
-                for (int c = 0; c < 4; ++c) ac[c] = make_uint4(0, 0, 0, 0);
-                sl = 0.0f;
-            }
-        } else {
-            sl = quantize_half_row<KIND>(lhs, (int64_t)a_row * K + kb * kTK + st_h * 64, a_valid, ac);
-            if (write_q) {
-                uint4* p = reinterpret_cast<uint4*>(q_out + (int64_t)a_row * K + kb * kTK + st_h * 64);
-#pragma unroll
-                for (int c = 0; c < 4; ++c) p[c] = ac[c];
-                if (st_h == 0) s_out[(int64_t)a_row * nkb + kb] = sl;
-            }
+        for (int i = 0; i < MB; ++i) {
+            af[i] = *reinterpret_cast<const v8i*>(&sm.a[buf][16 * i + lr][lc * 32]);
+            cf[i] = *reinterpret_cast<const v4f*>(&sm.c[buf][my_nblk][16 * i + 4 * lc]);
         }
-        uint4 bc[4];
-        {
-            const uint4* p = reinterpret_cast<const uint4*>(b_src + kb * kTK);
+        quant_store(kb1, buf ^ 1);
+        load_raw<KIND>(raw, lhs, lhs_scale, qlrow, K, kb2, qchunk, qvalid);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) bc[c] = p[c];
-        }
-        const float sr = rhs_scale[((int64_t)g * nkb + kb) * nnb + n0 / kQBlock];
+        for (int j = 0; j < NB; ++j) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            *reinterpret_cast<uint4*>(&sA[st_r][st_h * 64 + 16 * c]) = ac[c];
-            *reinterpret_cast<uint4*>(&sB[st_r][st_h * 64 + 16 * c]) = bc[c];
-        }
-        if (st_h == 0) sSl[st_r] = sl;
-        __syncthreads();
-
-        // ---- MFMA: 4x4 blocks of 16x16, K = 128 each
-        v8i af[4], bf[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const v8i*>(&sA[wm * 64 + i * 16 + lr][lk]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) bf[j] = *reinterpret_cast<const v8i*>(&sB[wn * 64 + j * 16 + lr][lk]);
-        float cs[4][4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) cs[i][r] = sSl[wm * 64 + i * 16 + (lane >> 4) * 4 + r] * sr;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int i = 0; i < MB; ++i) {
                 const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                    af[i], bf[j], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+                    af[i], b[j], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(p[r], cs[i][r], acc[i][j][r]);
+                for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(p[r], cf[i][r], acc[i][j][r]);
             }
+            load_b(j, kb1);
+        }
         __syncthreads();
     }
 
-    // ---- epilogue: masked stores of the item's rows
+    // ---- epilogue: stage the tile in LDS (reusing the A buffers), then store full rows
+    uint8_t* so = smem_raw;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MB; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int row = row0 + wm * 64 + i * 16 + (lane >> 4) * 4 + r;
-            if (row < it.lo || row >= it.hi) continue;
+            const int row = 16 * i + 4 * lc + r;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int col = n0 + wn * 64 + j * 16 + lr;
+            for (int j = 0; j < NB; ++j) {
+                const int col = wave * WN + 16 * j + lr;
                 if constexpr (OUT_BF16)
-                    reinterpret_cast<uint16_t*>(out)[(int64_t)row * N + col] = (uint16_t)f32_to_bf16_bits(acc[i][j][r]);
+                    *reinterpret_cast<uint16_t*>(so + row * OUT_ROW + col * 2) = (uint16_t)f32_to_bf16_bits(acc[i][j][r]);
                 else
-                    reinterpret_cast<float*>(out)[(int64_t)row * N + col] = acc[i][j][r];
+                    *reinterpret_cast<float*>(so + row * OUT_ROW + col * 4) = acc[i][j][r];
             }
         }
+    __syncthreads();
+    constexpr int CH = TN * OUT_BYTES / 16;  // 16-byte chunks per row
+    for (int e = tid; e < kTM * CH; e += kThreads) {
+        const int row = e / CH, ch = e % CH;
+        const int grow = row0 + row;
+        if (grow < it.lo || grow >= it.hi) continue;
+        *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(out) + ((int64_t)grow * N + n0) * OUT_BYTES + ch * 16) =
+            *reinterpret_cast<const uint4*>(so + row * OUT_ROW + ch * 16);
+    }
 }
 
+template <int KIND, int WN, bool WRITE_Q>
+hipError_t launch_cfg(const void* lhs, const float* lhs_scale, const uint8_t* rhs,
+                      const float* rhs_scale, const int32_t* group_sizes, int M, int K, int N,
+                      int G, void* out, bool out_bf16, uint8_t* q_out, float* scale_out,
+                      hipStream_t stream) {
+    const int ntiles_n = N / (kWaves * WN);
+    const int64_t items = max_work_items(M, G, kTM);
+    const int nblocks = (int)(items * ntiles_n);
+    if (out_bf16)
+        hipLaunchKernelGGL((fp8_fwd_kernel<KIND, true, WN, WRITE_Q>), dim3(nblocks), dim3(kThreads),
+                           0, stream, lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N, G, out,
+                           q_out, scale_out, ntiles_n, nblocks);
+    else
+        hipLaunchKernelGGL((fp8_fwd_kernel<KIND, false, WN, WRITE_Q>), dim3(nblocks), dim3(kThreads),
+                           0, stream, lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N, G, out,
+                           q_out, scale_out, ntiles_n, nblocks);
+    return hipGetLastError();
+}
+
+template <int KIND, int WN>
+hipError_t launch_wn(const void* lhs, const float* lhs_scale, const uint8_t* rhs,
+                     const float* rhs_scale, const int32_t* group_sizes, int M, int K, int N,
+                     int G, void* out, bool out_bf16, uint8_t* q_out, float* scale_out,
+                     hipStream_t stream) {
+    if (KIND != kLhsE4M3 && q_out != nullptr)
+        return launch_cfg<KIND, WN, true>(lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N, G,
+                                          out, out_bf16, q_out, scale_out, stream);
+    return launch_cfg<KIND, WN, false>(lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N, G,
+                                       out, out_bf16, q_out, scale_out, stream);
+}
+
+// Tile width: the widest of 512/256/128 columns that divides N (fewest
+// re-quantisations of each LHS row).  GMM_FP8_WN=<16|32|64> overrides the
+// per-wave width (tuning sweeps only).
 template <int KIND>
 hipError_t launch_kind(const void* lhs, const float* lhs_scale, const uint8_t* rhs,
                        const float* rhs_scale, const int32_t* group_sizes, int M, int K, int N,
                        int G, void* out, bool out_bf16, uint8_t* q_out, float* scale_out,
                        hipStream_t stream) {
-    const int ntiles_n = N / kTN;
-    const int64_t items = max_work_items(M, G, kTM);
-    const int nblocks = (int)(items * ntiles_n);
-    if (out_bf16)
-        hipLaunchKernelGGL((fp8_fwd_kernel<KIND, true>), dim3(nblocks), dim3(256), 0, stream, lhs,
-                           lhs_scale, rhs, rhs_scale, group_sizes, M, K, N, G, out, q_out,
-                           scale_out, ntiles_n, nblocks);
-    else
-        hipLaunchKernelGGL((fp8_fwd_kernel<KIND, false>), dim3(nblocks), dim3(256), 0, stream, lhs,
-                           lhs_scale, rhs, rhs_scale, group_sizes, M, K, N, G, out, q_out,
-                           scale_out, ntiles_n, nblocks);
-    return hipGetLastError();
+    static const int forced = [] {
+        const char* e = std::getenv("GMM_FP8_WN");
+        return e ? std::atoi(e) : 0;
+    }();
+    int wn = N % 512 == 0 ? 64 : (N % 256 == 0 ? 32 : 16);
+    if ((forced == 16 || forced == 32 || forced == 64) && N % (kWaves * forced) == 0) wn = forced;
+    if (wn == 64)
+        return launch_wn<KIND, 64>(lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N, G, out,
+                                    out_bf16, q_out, scale_out, stream);
+    if (wn == 32)
+        return launch_wn<KIND, 32>(lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N, G, out,
+                                    out_bf16, q_out, scale_out, stream);
+    return launch_wn<KIND, 16>(lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N, G, out,
+                                out_bf16, q_out, scale_out, stream);
 }
 
 }  // namespace

@@ -140,9 +140,20 @@ hipError_t launch_quantize_lhs(const void* x, bool x_bf16, int64_t M, int64_t K,
 }
 
 // ---------------------------------------------------------- RHS 128x128 --
-// One workgroup per (g, kb, nb) block.  Thread t owns column n = t % 128 and
-// the 64 K-rows of half t / 128; its 64 codes are contiguous in the K-major
-// output q[g][n][k], so they are stored with four 16-byte writes.
+// One workgroup per (g, kb, nb) block.  Thread t owns column n = nb*128 +
+// t % 128 and the 64 K-rows of half t / 128.  The codes are written in the
+// MFMA operand order gmm_fp8_fwd loads (see rhs_packed_offset): each 16-column
+// by 128-K slab is 2 KB, and the 32 K-values one lane of the MFMA needs for
+// one column sit as two 16-byte runs, so the forward reads whole contiguous
+// kilobytes.
+
+// Byte offset of the 16-byte run holding codes k0 .. k0+15 (k0 % 16 == 0) of
+// column n in the packed RHS: [G][N/16][K/128][2][64][16], with lane
+// l = 16 * ((k % 128) / 32) + n % 16 and half h = (k % 32) / 16.
+__device__ __forceinline__ int64_t rhs_packed_offset(int g, int n, int k0, int N, int K) {
+    const int nb16 = n >> 4, lr = n & 15, kb = k0 >> 7, lc = (k0 & 127) >> 5, h = (k0 & 31) >> 4;
+    return ((((int64_t)g * (N >> 4) + nb16) * (K >> 7) + kb) * 2 + h) * 1024 + (lc * 16 + lr) * 16;
+}
 
 template <bool BF16>
 __global__ __launch_bounds__(256) void quantize_rhs_kernel(const void* __restrict__ w, int K,
@@ -172,7 +183,6 @@ __global__ __launch_bounds__(256) void quantize_rhs_kernel(const void* __restric
     a = fmaxf(fmaxf(wave_max[0], wave_max[1]), fmaxf(wave_max[2], wave_max[3]));
     const float s = quant_scale(a);
     const float inv = quant_inv(s);
-    uint8_t* dst = q + ((int64_t)g * N + n) * K + k0;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
         uint4 o;
@@ -180,7 +190,7 @@ __global__ __launch_bounds__(256) void quantize_rhs_kernel(const void* __restric
         o.y = e4m3x4(v[16 * c + 4] * inv, v[16 * c + 5] * inv, v[16 * c + 6] * inv, v[16 * c + 7] * inv);
         o.z = e4m3x4(v[16 * c + 8] * inv, v[16 * c + 9] * inv, v[16 * c + 10] * inv, v[16 * c + 11] * inv);
         o.w = e4m3x4(v[16 * c + 12] * inv, v[16 * c + 13] * inv, v[16 * c + 14] * inv, v[16 * c + 15] * inv);
-        *reinterpret_cast<uint4*>(dst + 16 * c) = o;
+        *reinterpret_cast<uint4*>(q + rhs_packed_offset(g, n, k0 + 16 * c, N, K)) = o;
     }
     if (t == 0) scale[blk] = s;
 }

@@ -52,3 +52,17 @@ def sample_rows_problem(group_sizes: np.ndarray, rows: np.ndarray):
     gid = np.minimum(gid, G)            # rows past the total -> tail
     sub = np.bincount(gid[gid < G], minlength=G).astype(np.int32)
     return sub, gid
+
+
+def unpack_rhs(qp: np.ndarray) -> np.ndarray:
+    """Packed RHS codes [G, N/16, K/128, 2048] (gmm_quantize_rhs order) -> [G, K, N]."""
+    G, N16, KB, _ = qp.shape
+    a = qp.reshape(G, N16, KB, 2, 4, 16, 16)          # g, nb16, kb, h, lc, lr, e
+    return np.ascontiguousarray(a.transpose(0, 2, 4, 3, 6, 1, 5)).reshape(G, KB * 128, N16 * 16)
+
+
+def pack_rhs(q: np.ndarray) -> np.ndarray:
+    """Inverse of unpack_rhs: codes [G, K, N] -> packed [G, N/16, K/128, 2048]."""
+    G, K, N = q.shape
+    a = q.reshape(G, K // 128, 4, 2, 16, N // 16, 16)  # g, kb, lc, h, e, nb16, lr
+    return np.ascontiguousarray(a.transpose(0, 5, 1, 3, 2, 6, 4)).reshape(G, N // 16, K // 128, 2048)

@@ -13,7 +13,7 @@ import torch
 import moe_grouped_gemm_gmm_amd as gmm
 import oracle
 import workloads
-from helpers import assert_fp8_parity, sample_rows_problem, sqnr_db, to_np64
+from helpers import assert_fp8_parity, pack_rhs, sample_rows_problem, sqnr_db, to_np64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -117,7 +117,7 @@ def test_exact_integer_case_bitwise():
     sl = np.ones((M, K // 128), np.float32)
     sr = np.ones((4, K // 128, N // 128), np.float32)
     out = gmm.gmm_fp8_fwd(torch.from_numpy(ql).to(DEV),
-                          torch.from_numpy(np.ascontiguousarray(qr.transpose(0, 2, 1))).to(DEV),
+                          torch.from_numpy(pack_rhs(qr)).to(DEV),
                           torch.from_numpy(sr).to(DEV), torch.from_numpy(gs).to(DEV),
                           lhs_scale=torch.from_numpy(sl).to(DEV), out_dtype=torch.float32)
     ref = oracle.gmm_fp8(ql, sl, qr, sr, gs)

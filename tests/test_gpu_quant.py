@@ -6,6 +6,7 @@ import torch
 import moe_grouped_gemm_gmm_amd as gmm
 import oracle
 import workloads
+from helpers import unpack_rhs
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -114,7 +115,7 @@ def test_quantize_rhs(G, K, N, dtype):
     q, s = gmm.gmm_quantize_rhs(w.to(DEV))
     rq, rs = oracle.quantize_rhs(workloads.as_f32(w))
     assert np.array_equal(s.cpu().numpy(), rs)
-    assert np.array_equal(q.cpu().numpy(), rq.transpose(0, 2, 1))   # stored [G,N,K]
+    assert np.array_equal(unpack_rhs(q.cpu().numpy()), rq)          # packed MFMA order
 
 
 def test_quantize_wi_config_bitexact():
@@ -123,4 +124,4 @@ def test_quantize_wi_config_bitexact():
     q, s = gmm.gmm_quantize_rhs(wl.w.to(DEV))
     rq, rs = oracle.quantize_rhs(workloads.as_f32(wl.w))
     assert np.array_equal(s.cpu().numpy(), rs)
-    assert np.array_equal(q.cpu().numpy(), rq.transpose(0, 2, 1))
+    assert np.array_equal(unpack_rhs(q.cpu().numpy()), rq)
