@@ -46,9 +46,28 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // going to 448, so no clamp is needed before the conversion (the GPU tests
 // sweep every rounding boundary and compare with the oracle bit for bit).
 
-__device__ __forceinline__ float quant_scale(float absmax) { return absmax / kE4M3Max; }
+// s = RN(a / 448).  448 = 7 * 2^6, so a/448 = RN(a/7) * 2^-6 exactly for every
+// in-contract a; RN(a/7) is y = RN(a * RN(1/7)) corrected once with the exact
+// residual a - 7y (one FMA) and one more FMA.  This equals the IEEE quotient
+// for every fp32 significand (checked exhaustively over a binade, which
+// covers every exponent since division by 7 commutes with powers of two).
+__device__ __forceinline__ float quant_scale(float a) {
+    constexpr float kInv7 = 0.142857149243354797363281250f;  // RN(1/7)
+    const float y = __fmul_rn(a, kInv7);
+    const float r = __builtin_fmaf(-y, 7.0f, a);
+    return __fmul_rn(__builtin_fmaf(r, kInv7, y), 0.015625f);
+}
 
-__device__ __forceinline__ float quant_inv(float s) { return s == 0.0f ? 0.0f : 1.0f / s; }
+// inv = RN(1/s), or 0 when s == 0.  The hardware reciprocal estimate refined
+// by one FMA Newton step equals the IEEE quotient 1/s for every significand
+// whenever 1/s is a normal number, which holds for every s = a/448 with fp32
+// a in the contract (checked exhaustively on gfx950).
+__device__ __forceinline__ float quant_inv(float s) {
+    const float r0 = __builtin_amdgcn_rcpf(s);
+    const float e = __builtin_fmaf(-s, r0, 1.0f);
+    const float r1 = __builtin_fmaf(e, r0, r0);
+    return s == 0.0f ? 0.0f : r1;
+}
 
 // Four fp32 values (already multiplied by inv) -> four E4M3 codes, byte i = value i.
 __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
@@ -60,6 +79,30 @@ __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
 // --------------------------------------------------------- wave helpers --
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// DPP lane permutations (within rows of 16 lanes).
+constexpr int kDppXor1 = 0xB1;           // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;           // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;    // lane i <-> 7-i within each 8 lanes
+constexpr int kDppMirror = 0x140;        // lane i <-> 15-i within each 16 lanes
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Maximum over each aligned group of 8 lanes (register-only, no LDS).
+__device__ __forceinline__ float max_over_8(float x) {
+    x = fmaxf(x, dpp<kDppXor1>(x));
+    x = fmaxf(x, dpp<kDppXor2>(x));
+    return fmaxf(x, dpp<kDppHalfMirror>(x));
+}
+
+// Maximum over each aligned group of 16 lanes.
+__device__ __forceinline__ float max_over_16(float x) {
+    x = max_over_8(x);
+    return fmaxf(x, dpp<kDppMirror>(x));
+}
 
 __device__ __forceinline__ int wave_incl_scan(int v) {
     const int lane = lane_id();

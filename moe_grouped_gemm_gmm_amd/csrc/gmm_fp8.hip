@@ -19,9 +19,9 @@
 // (an expert's rows inside a 64-row tile, from the in-kernel metadata
 // routine) and TN = 8*WN output columns; wave w owns columns [w*WN, (w+1)*WN)
 // of the tile.  Per 128-wide subchannel:
-//  - A: wave w quantises rows 8w..8w+7; a lane holds 8 consecutive K values
-//    of two rows (16 lanes per row, so each load reads whole 128-byte lines)
-//    and the row's abs-max is reduced over those 16 lanes.  Every row is
+//  - A: wave w quantises rows 8w..8w+7; a lane holds 16 K values of one row
+//    (8 lanes per row; each load instruction reads whole 128-byte lines) and
+//    the row's abs-max is reduced over those 8 lanes with DPP.  Every row is
 //    quantised once per workgroup.  Codes go to a double-buffered LDS tile,
 //    and with them the products sl[row] * sr[n-block] for each 128-column
 //    block of the tile, so the MFMA waves read their per-row factors
@@ -38,7 +38,10 @@
 //  - Each 16x16 block is one v_mfma_scale_f32_16x16x128_f8f6f4 (neutral E8M0
 //    scales: the FP8 products are exact) into a zero temporary, folded into
 //    the fp32 accumulator with one FMA per element: acc += p * (sl * sr).
-//  - The tile is written through LDS so that global stores are full rows.
+//  - The MFMA operands are swapped so every 16x16 block comes out transposed:
+//    a lane owns one output row and four consecutive columns, which makes the
+//    row factor one scalar per block and lets the epilogue store 8-byte (bf16)
+//    or 16-byte (fp32) runs directly.
 #include "gmm_device.hpp"
 #include "gmm_launch.hpp"
 
@@ -57,80 +60,79 @@ constexpr int kLdsRow = kTK + 16;  // 144-byte LDS rows: conflict-free 16-lane d
 
 enum LhsKind { kLhsE4M3 = 0, kLhsBF16 = 1, kLhsF32 = 2 };
 
-// Raw LHS registers of one subchannel for this lane: rows r and r+4 of the
-// wave's 8 rows, 8 consecutive K values of each (16 lanes cover a row's 128
-// values, so every load instruction reads whole 128-byte lines).
+// Raw LHS registers of one subchannel for this lane: one row, K values
+// 8c..8c+7 and 64+8c..64+8c+7 (c = lane % 8), so that each load instruction of
+// the wave reads the same 128-byte half of 8 rows.  Lanes of rows outside the
+// work item load a clamped in-bounds row; their codes only reach output rows
+// that are never stored.
 template <int KIND>
 struct RawA;
 template <>
 struct RawA<kLhsBF16> { uint4 d[2]; };
 template <>
-struct RawA<kLhsF32> { uint4 d[2][2]; };
+struct RawA<kLhsF32> { uint4 d[4]; };
 template <>
-struct RawA<kLhsE4M3> { uint2 d[2]; float s[2]; };
+struct RawA<kLhsE4M3> { uint2 d[2]; float s; };
 
-// `row[p]` is always an in-bounds row (invalid lanes pass a clamped one) and
-// the loaded values are zeroed by a select, so the loads are unconditional and
-// the main loop stays free of divergent branches.
 template <int KIND>
 __device__ __forceinline__ void load_raw(RawA<KIND>& r, const void* __restrict__ lhs,
-                                         const float* __restrict__ lhs_scale,
-                                         const int64_t (&row)[2], int K, int kb, int chunk,
-                                         const bool (&valid)[2]) {
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-        const int64_t e = row[p] * K + kb * kTK + chunk * 8;
-        if constexpr (KIND == kLhsBF16) {
-            const uint4 d = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(lhs) + e);
-            r.d[p] = make_uint4(valid[p] ? d.x : 0u, valid[p] ? d.y : 0u, valid[p] ? d.z : 0u, valid[p] ? d.w : 0u);
-        } else if constexpr (KIND == kLhsF32) {
-            const uint4* q = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(lhs) + e);
-#pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                const uint4 d = q[c];
-                r.d[p][c] = make_uint4(valid[p] ? d.x : 0u, valid[p] ? d.y : 0u, valid[p] ? d.z : 0u, valid[p] ? d.w : 0u);
-            }
-        } else {
-            const uint2 d = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(lhs) + e);
-            r.d[p] = make_uint2(valid[p] ? d.x : 0u, valid[p] ? d.y : 0u);
-            const float s = lhs_scale[row[p] * (K / kTK) + kb];
-            r.s[p] = valid[p] ? s : 0.0f;
-        }
+                                         const float* __restrict__ lhs_scale, int64_t row, int K,
+                                         int kb, int chunk) {
+    const int64_t e = row * K + kb * kTK + chunk * 8;
+    if constexpr (KIND == kLhsBF16) {
+        const uint16_t* p = reinterpret_cast<const uint16_t*>(lhs) + e;
+        r.d[0] = *reinterpret_cast<const uint4*>(p);
+        r.d[1] = *reinterpret_cast<const uint4*>(p + 64);
+    } else if constexpr (KIND == kLhsF32) {
+        const float* p = reinterpret_cast<const float*>(lhs) + e;
+        r.d[0] = *reinterpret_cast<const uint4*>(p);
+        r.d[1] = *reinterpret_cast<const uint4*>(p + 4);
+        r.d[2] = *reinterpret_cast<const uint4*>(p + 64);
+        r.d[3] = *reinterpret_cast<const uint4*>(p + 68);
+    } else {
+        const uint8_t* p = reinterpret_cast<const uint8_t*>(lhs) + e;
+        r.d[0] = *reinterpret_cast<const uint2*>(p);
+        r.d[1] = *reinterpret_cast<const uint2*>(p + 64);
+        r.s = lhs_scale[row * (K / kTK) + kb];
     }
 }
 
-// 8 values of row p -> 8 codes, and the row's scale (the abs-max is reduced
-// over the 16 lanes lane ^ {1, 2, 4, 8} that hold the row).
+// 16 values -> 16 codes (two 8-byte runs) and the row's scale; the abs-max is
+// reduced over the 8 lanes that hold the row (DPP, no LDS round trip).
 template <int KIND>
-__device__ __forceinline__ float quantize_raw(const RawA<KIND>& r, int p, uint2& codes) {
+__device__ __forceinline__ float quantize_raw(const RawA<KIND>& r, uint2 (&codes)[2]) {
     if constexpr (KIND == kLhsE4M3) {
-        codes = r.d[p];
-        return r.s[p];
+        codes[0] = r.d[0];
+        codes[1] = r.d[1];
+        return r.s;
     } else {
-        float v[8];
+        float v[16];
         if constexpr (KIND == kLhsBF16) {
-            v[0] = bf16_lo(r.d[p].x); v[1] = bf16_hi(r.d[p].x);
-            v[2] = bf16_lo(r.d[p].y); v[3] = bf16_hi(r.d[p].y);
-            v[4] = bf16_lo(r.d[p].z); v[5] = bf16_hi(r.d[p].z);
-            v[6] = bf16_lo(r.d[p].w); v[7] = bf16_hi(r.d[p].w);
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                v[8 * q + 0] = bf16_lo(r.d[q].x); v[8 * q + 1] = bf16_hi(r.d[q].x);
+                v[8 * q + 2] = bf16_lo(r.d[q].y); v[8 * q + 3] = bf16_hi(r.d[q].y);
+                v[8 * q + 4] = bf16_lo(r.d[q].z); v[8 * q + 5] = bf16_hi(r.d[q].z);
+                v[8 * q + 6] = bf16_lo(r.d[q].w); v[8 * q + 7] = bf16_hi(r.d[q].w);
+            }
         } else {
 #pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                v[4 * c + 0] = __uint_as_float(r.d[p][c].x); v[4 * c + 1] = __uint_as_float(r.d[p][c].y);
-                v[4 * c + 2] = __uint_as_float(r.d[p][c].z); v[4 * c + 3] = __uint_as_float(r.d[p][c].w);
+            for (int q = 0; q < 4; ++q) {
+                v[4 * q + 0] = __uint_as_float(r.d[q].x); v[4 * q + 1] = __uint_as_float(r.d[q].y);
+                v[4 * q + 2] = __uint_as_float(r.d[q].z); v[4 * q + 3] = __uint_as_float(r.d[q].w);
             }
         }
         float a = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(v[i]));
-        a = fmaxf(a, __shfl_xor(a, 1, 64));
-        a = fmaxf(a, __shfl_xor(a, 2, 64));
-        a = fmaxf(a, __shfl_xor(a, 4, 64));
-        a = fmaxf(a, __shfl_xor(a, 8, 64));
+        for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(v[i]));
+        a = max_over_8(a);
         const float s = quant_scale(a);
         const float inv = quant_inv(s);
-        codes.x = e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
-        codes.y = e4m3x4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            codes[q].x = e4m3x4(v[8 * q + 0] * inv, v[8 * q + 1] * inv, v[8 * q + 2] * inv, v[8 * q + 3] * inv);
+            codes[q].y = e4m3x4(v[8 * q + 4] * inv, v[8 * q + 5] * inv, v[8 * q + 6] * inv, v[8 * q + 7] * inv);
+        }
         return s;
     }
 }
@@ -154,14 +156,9 @@ __global__ __launch_bounds__(kThreads, 1) void fp8_fwd_kernel(
     constexpr int TN = kWaves * WN;
     constexpr int NBLK = Smem<WN>::NBLK;
     constexpr int OUT_BYTES = OUT_BF16 ? 2 : 4;
-    constexpr int OUT_ROW = TN * OUT_BYTES + 16;   // padded output staging row
-    constexpr int SMEM_MAIN = sizeof(Smem<WN>);
-    constexpr int SMEM_OUT = kTM * OUT_ROW;
-    constexpr int SMEM = SMEM_MAIN > SMEM_OUT ? SMEM_MAIN : SMEM_OUT;
 
     __shared__ WorkItem s_item;
-    __shared__ __attribute__((aligned(16))) uint8_t smem_raw[SMEM];
-    Smem<WN>& sm = *reinterpret_cast<Smem<WN>*>(smem_raw);
+    __shared__ __attribute__((aligned(16))) Smem<WN> sm;
 
     const int tid = threadIdx.x, lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -190,20 +187,14 @@ __global__ __launch_bounds__(kThreads, 1) void fp8_fwd_kernel(
     const int g = it.g, row0 = it.tile * kTM;
     const int nkb = K / kTK, nnb = N / kQBlock;
 
-    // ---- quantiser role: rows 8*wave + (lane >> 4) + 4p (p = 0, 1), K values
-    //      8*(lane & 15) .. +7 of each
-    const int qchunk = lane & 15;
-    int qrow[2];
-    int64_t qgrow[2], qlrow[2];
-    bool qvalid[2], write_q[2];
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-        qrow[p] = 8 * wave + (lane >> 4) + 4 * p;
-        qgrow[p] = row0 + qrow[p];
-        qvalid[p] = qgrow[p] >= it.lo && qgrow[p] < it.hi;
-        qlrow[p] = qvalid[p] ? qgrow[p] : it.lo;    // in-bounds row the loads use
-        write_q[p] = WRITE_Q && nt == 0 && qvalid[p];
-    }
+    // ---- quantiser role: row 8*wave + lane/8, K values 8c..8c+7 and
+    //      64+8c..64+8c+7 with c = lane % 8
+    const int qchunk = lane & 7;
+    const int qrow = 8 * wave + (lane >> 3);
+    const int64_t qgrow = row0 + qrow;
+    const bool qvalid = qgrow >= it.lo && qgrow < it.hi;
+    const int64_t qlrow = qvalid ? qgrow : it.lo;    // in-bounds row the loads use
+    const bool write_q = WRITE_Q && nt == 0 && qvalid;
     const float* srg = rhs_scale + (int64_t)g * nkb * nnb + n0 / kQBlock;  // + kb*nnb + nblk
 
     // ---- MFMA role: columns [n0 + wave*WN, +WN); lane = row/col lr, K chunk lc.
@@ -233,16 +224,15 @@ __global__ __launch_bounds__(kThreads, 1) void fp8_fwd_kernel(
         float sr = srv[0];
 #pragma unroll
         for (int q = 1; q < NBLK; ++q) sr = qchunk == q ? srv[q] : sr;
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            uint2 codes;
-            const float s = quantize_raw<KIND>(raw, p, codes);
-            *reinterpret_cast<uint2*>(&sm.a[buf][qrow[p]][qchunk * 8]) = codes;
-            if (qchunk < NBLK) sm.c[buf][qchunk][qrow[p]] = s * sr;
-            if (write_q[p]) {
-                *reinterpret_cast<uint2*>(q_out + qgrow[p] * K + kb * kTK + qchunk * 8) = codes;
-                if (qchunk == 0) s_out[qgrow[p] * nkb + kb] = s;
-            }
+        uint2 codes[2];
+        const float s = quantize_raw<KIND>(raw, codes);
+        *reinterpret_cast<uint2*>(&sm.a[buf][qrow][qchunk * 8]) = codes[0];
+        *reinterpret_cast<uint2*>(&sm.a[buf][qrow][64 + qchunk * 8]) = codes[1];
+        if (qchunk < NBLK) sm.c[buf][qchunk][qrow] = s * sr;
+        if (write_q) {
+            *reinterpret_cast<uint2*>(q_out + qgrow * K + kb * kTK + qchunk * 8) = codes[0];
+            *reinterpret_cast<uint2*>(q_out + qgrow * K + kb * kTK + 64 + qchunk * 8) = codes[1];
+            if (qchunk == 0) s_out[qgrow * nkb + kb] = s;
         }
     };
     auto load_b = [&](int j, int kb) {
@@ -253,11 +243,11 @@ __global__ __launch_bounds__(kThreads, 1) void fp8_fwd_kernel(
     };
 
     // ---- prologue: subchannel 0 quantised in LDS, raw subchannel 1 and B(0) in registers
-    load_raw<KIND>(raw, lhs, lhs_scale, qlrow, K, 0, qchunk, qvalid);
+    load_raw<KIND>(raw, lhs, lhs_scale, qlrow, K, 0, qchunk);
 #pragma unroll
     for (int j = 0; j < NB; ++j) load_b(j, 0);
     quant_store(0, 0);
-    load_raw<KIND>(raw, lhs, lhs_scale, qlrow, K, min(1, nkb - 1), qchunk, qvalid);
+    load_raw<KIND>(raw, lhs, lhs_scale, qlrow, K, min(1, nkb - 1), qchunk);
     __syncthreads();
 
     // Iteration kb (straight-line code, so loads stay in flight across it):
@@ -268,53 +258,49 @@ __global__ __launch_bounds__(kThreads, 1) void fp8_fwd_kernel(
     for (int kb = 0; kb < nkb; ++kb) {
         const int buf = kb & 1;
         const int kb1 = min(kb + 1, nkb - 1), kb2 = min(kb + 2, nkb - 1);
+        // Operands are swapped so each 16x16 block comes out transposed: lane
+        // (lr, lc) holds row 16i + lr and the four consecutive columns
+        // 16j + 4lc .. +3, so its per-row factor sl * sr is one scalar per row
+        // block.
         v8i af[MB];
-        v4f cf[MB];
+        float cf[MB];
 #pragma unroll
         for (int i = 0; i < MB; ++i) {
             af[i] = *reinterpret_cast<const v8i*>(&sm.a[buf][16 * i + lr][lc * 32]);
-            cf[i] = *reinterpret_cast<const v4f*>(&sm.c[buf][my_nblk][16 * i + 4 * lc]);
+            cf[i] = sm.c[buf][my_nblk][16 * i + lr];
         }
         quant_store(kb1, buf ^ 1);
-        load_raw<KIND>(raw, lhs, lhs_scale, qlrow, K, kb2, qchunk, qvalid);
+        load_raw<KIND>(raw, lhs, lhs_scale, qlrow, K, kb2, qchunk);
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
 #pragma unroll
             for (int i = 0; i < MB; ++i) {
                 const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                    af[i], b[j], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+                    b[j], af[i], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(p[r], cf[i][r], acc[i][j][r]);
+                for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(p[r], cf[i], acc[i][j][r]);
             }
             load_b(j, kb1);
         }
         __syncthreads();
     }
 
-    // ---- epilogue: stage the tile in LDS (reusing the A buffers), then store full rows
-    uint8_t* so = smem_raw;
+    // ---- epilogue: each lane stores 4 consecutive outputs of its rows directly
+    //      (8 bytes for bf16, 16 for fp32); rows outside the item are skipped
 #pragma unroll
-    for (int i = 0; i < MB; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = 16 * i + 4 * lc + r;
-#pragma unroll
-            for (int j = 0; j < NB; ++j) {
-                const int col = wave * WN + 16 * j + lr;
-                if constexpr (OUT_BF16)
-                    *reinterpret_cast<uint16_t*>(so + row * OUT_ROW + col * 2) = (uint16_t)f32_to_bf16_bits(acc[i][j][r]);
-                else
-                    *reinterpret_cast<float*>(so + row * OUT_ROW + col * 4) = acc[i][j][r];
-            }
-        }
-    __syncthreads();
-    constexpr int CH = TN * OUT_BYTES / 16;  // 16-byte chunks per row
-    for (int e = tid; e < kTM * CH; e += kThreads) {
-        const int row = e / CH, ch = e % CH;
-        const int grow = row0 + row;
+    for (int i = 0; i < MB; ++i) {
+        const int grow = row0 + 16 * i + lr;
         if (grow < it.lo || grow >= it.hi) continue;
-        *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(out) + ((int64_t)grow * N + n0) * OUT_BYTES + ch * 16) =
-            *reinterpret_cast<const uint4*>(so + row * OUT_ROW + ch * 16);
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            const int64_t o = (int64_t)grow * N + ncol0 + 16 * j + 4 * lc;
+            if constexpr (OUT_BF16)
+                *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + o) =
+                    make_uint2(pack_bf16x2(acc[i][j][0], acc[i][j][1]), pack_bf16x2(acc[i][j][2], acc[i][j][3]));
+            else
+                *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + o) =
+                    make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+        }
     }
 }
 

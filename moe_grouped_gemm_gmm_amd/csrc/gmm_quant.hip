@@ -108,10 +108,7 @@ __global__ __launch_bounds__(256) void quantize_lhs_kernel(const void* __restric
             float a = 0.0f;
 #pragma unroll
             for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(v[u][i]));
-            a = fmaxf(a, __shfl_xor(a, 1, 16));
-            a = fmaxf(a, __shfl_xor(a, 2, 16));
-            a = fmaxf(a, __shfl_xor(a, 4, 16));
-            a = fmaxf(a, __shfl_xor(a, 8, 16));
+            a = max_over_16(a);
             const float s = quant_scale(a);
             const float inv = quant_inv(s);
             uint2 codes;
