@@ -146,7 +146,7 @@ struct Smem {
 };
 
 template <int KIND, bool OUT_BF16, int WN, bool WRITE_Q>
-__global__ __launch_bounds__(kThreads, 1) void fp8_fwd_kernel(
+__global__ __launch_bounds__(kThreads, WN <= 32 ? 2 : 1) void fp8_fwd_kernel(
     const void* __restrict__ lhs, const float* __restrict__ lhs_scale,
     const uint8_t* __restrict__ rhs, const float* __restrict__ rhs_scale,
     const int32_t* __restrict__ group_sizes, int M, int K, int N, int G, void* __restrict__ out,
