@@ -40,3 +40,42 @@ def test_bf16_rounding_is_rne():
     a = np.array([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -(1.0 + 2 ** -8)], np.float32)
     b = workloads.to_bf16(a).float().numpy()
     assert b.tolist() == [1.0, 1.0 + 2 ** -6, -1.0]
+
+
+def _golden():
+    import os
+    vals = {}
+    path = os.path.join(os.path.dirname(__file__), "golden", "shapes_and_tolerances.txt")
+    for line in open(path, encoding="utf-8"):
+        line = line.split("#", 1)[0].strip()
+        if line:
+            k, v = (p.strip() for p in line.split("="))
+            vals[k] = float(v)
+    return vals
+
+
+def test_shapes_follow_the_pages_derivation():
+    """Production and development shapes ("GEMM Kernel 性能优化十问", Q6)."""
+    g = _golden()
+    assert g["per_device_batch"] * g["seq_len"] * g["top_k"] == g["prod_wi_M"]
+    full, wi, wo = (workloads.CONFIGS[n] for n in ("full", "wi", "wo"))
+    assert (full["M"], full["K"], full["N"], full["G"]) == (
+        g["prod_wi_M"], g["emb_dim"], g["moe_mlp_dim"], g["num_experts"])
+    assert wi["M"] == g["prod_wi_M"] / g["expert_parallel"] == g["dev_M"]
+    assert wi["G"] == g["num_experts"] / g["expert_parallel"] == g["dev_G"]
+    assert (wi["K"], wi["N"]) == (g["prod_wi_K"], g["prod_wi_N"])
+    assert (wo["M"], wo["G"], wo["K"], wo["N"]) == (g["dev_M"], g["dev_G"], g["prod_wo_K"], g["prod_wo_N"])
+    # the full workload's routing: top-8 of (2 x 4096) tokens fills every row
+    wl_gs = workloads.topk_routing_counts(int(g["per_device_batch"] * g["seq_len"]), full["G"],
+                                          int(g["top_k"]), 0, workloads.zipf_log_popularity(full["G"], 1.1, 0))
+    assert wl_gs.sum() == full["M"]
+
+
+def test_tolerances_follow_the_pages():
+    """The parity bar is the pages' FP8-vs-reference check, SQNR held above
+    their 'good' threshold ("GEMM Kernel 性能优化十问", Q9.2)."""
+    import helpers
+    g = _golden()
+    assert helpers.FP8_ATOL == g["fp8_vs_ref_atol"] and helpers.FP8_RTOL == g["fp8_vs_ref_rtol"]
+    assert helpers.FP8_MIN_SQNR_DB >= g["sqnr_good_db"]
+    assert (g["lhs_block_rows"], g["lhs_block_cols"], g["rhs_block_rows"], g["rhs_block_cols"]) == (1, 128, 128, 128)
