@@ -92,6 +92,12 @@ __device__ __forceinline__ float dpp(float x) {
 }
 
 // Maximum over each aligned group of 8 lanes (register-only, no LDS).
+// Maximum over each aligned group of 4 lanes.
+__device__ __forceinline__ float max_over_4(float x) {
+    x = fmaxf(x, dpp<kDppXor1>(x));
+    return fmaxf(x, dpp<kDppXor2>(x));
+}
+
 __device__ __forceinline__ float max_over_8(float x) {
     x = fmaxf(x, dpp<kDppXor1>(x));
     x = fmaxf(x, dpp<kDppXor2>(x));

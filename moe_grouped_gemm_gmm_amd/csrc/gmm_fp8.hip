@@ -29,12 +29,17 @@
 //  - B: each wave loads its own columns straight from global memory into the
 //    MFMA operand registers: two 16-byte loads per lane per 16-column block,
 //    each instruction reading one contiguous kilobyte of the packed RHS.  No
-//    two waves share B, so it never goes through LDS.  Each column block is
-//    reloaded with the next subchannel as soon as its MFMAs are issued.
-//  - Raw A is loaded two subchannels ahead and quantised one ahead of the
-//    MFMAs that use it; one barrier per subchannel.  The loop body has no
-//    branches (prefetch indices are clamped), so loads stay in flight across
-//    iterations instead of being drained at control-flow joins.
+//    two waves share B, so it never goes through LDS.  B is double-buffered
+//    in registers: the next subchannel's B is requested at the start of a
+//    step, a whole step before its MFMAs.
+//  - Raw A (with the RHS scale its lane folds in) is loaded two subchannels
+//    ahead and quantised one ahead of the MFMAs that use it; one barrier per
+//    subchannel.  The loop body has no branches (prefetch indices are
+//    clamped) and issues its loads in the same order every step, so the
+//    compiler's waits are counts rather than full drains.
+//  - Inside a step each MFMA is followed by a slice of independent VALU work
+//    (the next subchannel's quantiser, earlier blocks' scale FMAs), so the
+//    VALU and the matrix core run side by side.
 //  - Each 16x16 block is one v_mfma_scale_f32_16x16x128_f8f6f4 (neutral E8M0
 //    scales: the FP8 products are exact) into a zero temporary, folded into
 //    the fp32 accumulator with one FMA per element: acc += p * (sl * sr).
@@ -52,64 +57,72 @@ namespace gmm {
 
 namespace {
 
+constexpr int kTK = 128;           // one subchannel
 constexpr int kTM = 64;            // rows per workgroup
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kTK = 128;           // one subchannel
 constexpr int kLdsRow = kTK + 16;  // 144-byte LDS rows: conflict-free 16-lane ds_read_b128
 
 enum LhsKind { kLhsE4M3 = 0, kLhsBF16 = 1, kLhsF32 = 2 };
 
-// Raw LHS registers of one subchannel for this lane: one row, K values
-// 8c..8c+7 and 64+8c..64+8c+7 (c = lane % 8), so that each load instruction of
-// the wave reads the same 128-byte half of 8 rows.  Lanes of rows outside the
-// work item load a clamped in-bounds row; their codes only reach output rows
-// that are never stored.
+#ifndef GMM_FP8_VALU_PER_MFMA
+#define GMM_FP8_VALU_PER_MFMA 8   // VALU instructions scheduled after each MFMA
+#endif
+
+// Quantiser geometry: the 64 x 128 subchannel tile is split evenly over the
+// 512 lanes, 8 lanes per row, 16 values per lane in two runs of 8; run p of
+// lane chunk c holds the K values 8c + 64p .. +7, so each load instruction of a
+// wave reads the same 128-byte half of 8 rows.
+constexpr int kLPR = 8;                 // lanes per row
+constexpr int kRPW = 64 / kLPR;         // rows per wave
+constexpr int kNP = 2;                  // runs of 8 values per lane
+
+// Raw LHS registers of one subchannel for this lane.  Lanes of rows outside
+// the work item load a clamped in-bounds row; their codes only reach output
+// rows that are never stored.
 template <int KIND>
 struct RawA;
 template <>
-struct RawA<kLhsBF16> { uint4 d[2]; };
+struct RawA<kLhsBF16> { uint4 d[kNP]; };
 template <>
-struct RawA<kLhsF32> { uint4 d[4]; };
+struct RawA<kLhsF32> { uint4 d[2 * kNP]; };
 template <>
-struct RawA<kLhsE4M3> { uint2 d[2]; float s; };
+struct RawA<kLhsE4M3> { uint2 d[kNP]; float s; };
 
 template <int KIND>
 __device__ __forceinline__ void load_raw(RawA<KIND>& r, const void* __restrict__ lhs,
                                          const float* __restrict__ lhs_scale, int64_t row, int K,
                                          int kb, int chunk) {
     const int64_t e = row * K + kb * kTK + chunk * 8;
-    if constexpr (KIND == kLhsBF16) {
-        const uint16_t* p = reinterpret_cast<const uint16_t*>(lhs) + e;
-        r.d[0] = *reinterpret_cast<const uint4*>(p);
-        r.d[1] = *reinterpret_cast<const uint4*>(p + 64);
-    } else if constexpr (KIND == kLhsF32) {
-        const float* p = reinterpret_cast<const float*>(lhs) + e;
-        r.d[0] = *reinterpret_cast<const uint4*>(p);
-        r.d[1] = *reinterpret_cast<const uint4*>(p + 4);
-        r.d[2] = *reinterpret_cast<const uint4*>(p + 64);
-        r.d[3] = *reinterpret_cast<const uint4*>(p + 68);
-    } else {
-        const uint8_t* p = reinterpret_cast<const uint8_t*>(lhs) + e;
-        r.d[0] = *reinterpret_cast<const uint2*>(p);
-        r.d[1] = *reinterpret_cast<const uint2*>(p + 64);
-        r.s = lhs_scale[row * (K / kTK) + kb];
+#pragma unroll
+    for (int p = 0; p < kNP; ++p) {
+        const int64_t ep = e + p * 8 * kLPR;
+        if constexpr (KIND == kLhsBF16) {
+            r.d[p] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(lhs) + ep);
+        } else if constexpr (KIND == kLhsF32) {
+            const float* q = reinterpret_cast<const float*>(lhs) + ep;
+            r.d[2 * p] = *reinterpret_cast<const uint4*>(q);
+            r.d[2 * p + 1] = *reinterpret_cast<const uint4*>(q + 4);
+        } else {
+            r.d[p] = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(lhs) + ep);
+        }
     }
+    if constexpr (KIND == kLhsE4M3) r.s = lhs_scale[row * (K / kTK) + kb];
 }
 
-// 16 values -> 16 codes (two 8-byte runs) and the row's scale; the abs-max is
+// 16 values -> 16 codes (two runs of 8) and the row's scale; the abs-max is
 // reduced over the 8 lanes that hold the row (DPP, no LDS round trip).
 template <int KIND>
-__device__ __forceinline__ float quantize_raw(const RawA<KIND>& r, uint2 (&codes)[2]) {
+__device__ __forceinline__ float quantize_raw(const RawA<KIND>& r, uint2 (&codes)[kNP]) {
     if constexpr (KIND == kLhsE4M3) {
-        codes[0] = r.d[0];
-        codes[1] = r.d[1];
+#pragma unroll
+        for (int p = 0; p < kNP; ++p) codes[p] = r.d[p];
         return r.s;
     } else {
-        float v[16];
+        float v[8 * kNP];
         if constexpr (KIND == kLhsBF16) {
 #pragma unroll
-            for (int q = 0; q < 2; ++q) {
+            for (int q = 0; q < kNP; ++q) {
                 v[8 * q + 0] = bf16_lo(r.d[q].x); v[8 * q + 1] = bf16_hi(r.d[q].x);
                 v[8 * q + 2] = bf16_lo(r.d[q].y); v[8 * q + 3] = bf16_hi(r.d[q].y);
                 v[8 * q + 4] = bf16_lo(r.d[q].z); v[8 * q + 5] = bf16_hi(r.d[q].z);
@@ -117,19 +130,19 @@ __device__ __forceinline__ float quantize_raw(const RawA<KIND>& r, uint2 (&codes
             }
         } else {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
+            for (int q = 0; q < 2 * kNP; ++q) {
                 v[4 * q + 0] = __uint_as_float(r.d[q].x); v[4 * q + 1] = __uint_as_float(r.d[q].y);
                 v[4 * q + 2] = __uint_as_float(r.d[q].z); v[4 * q + 3] = __uint_as_float(r.d[q].w);
             }
         }
         float a = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(v[i]));
+        for (int i = 0; i < 8 * kNP; ++i) a = fmaxf(a, fabsf(v[i]));
         a = max_over_8(a);
         const float s = quant_scale(a);
         const float inv = quant_inv(s);
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
+        for (int q = 0; q < kNP; ++q) {
             codes[q].x = e4m3x4(v[8 * q + 0] * inv, v[8 * q + 1] * inv, v[8 * q + 2] * inv, v[8 * q + 3] * inv);
             codes[q].y = e4m3x4(v[8 * q + 4] * inv, v[8 * q + 5] * inv, v[8 * q + 6] * inv, v[8 * q + 7] * inv);
         }
@@ -141,12 +154,22 @@ template <int WN>
 struct Smem {
     static constexpr int TN = kWaves * WN;
     static constexpr int NBLK = TN / 128 > 0 ? TN / 128 : 1;   // 128-column scale blocks per tile
+    static_assert(NBLK <= kLPR, "one quantiser lane per 128-column block");
     uint8_t a[2][kTM][kLdsRow];         // E4M3 codes of the current and next subchannel
-    float c[2][NBLK][kTM];              // sl[row] * sr[n-block]
+    float c[2][kLPR][kTM];              // sl[row] * sr[n-block]; one slot per quantiser lane
+                                        // (slots >= NBLK are written, never read)
+};
+
+// What one lane needs to quantise one subchannel: its raw LHS values and the
+// RHS scale of the 128-column block whose per-row factor it writes.
+template <int KIND>
+struct Stage {
+    RawA<KIND> raw;
+    float sr;
 };
 
 template <int KIND, bool OUT_BF16, int WN, bool WRITE_Q>
-__global__ __launch_bounds__(kThreads, WN <= 32 ? 2 : 1) void fp8_fwd_kernel(
+__global__ __launch_bounds__(kThreads, 2) void fp8_fwd_kernel(
     const void* __restrict__ lhs, const float* __restrict__ lhs_scale,
     const uint8_t* __restrict__ rhs, const float* __restrict__ rhs_scale,
     const int32_t* __restrict__ group_sizes, int M, int K, int N, int G, void* __restrict__ out,
@@ -187,15 +210,16 @@ __global__ __launch_bounds__(kThreads, WN <= 32 ? 2 : 1) void fp8_fwd_kernel(
     const int g = it.g, row0 = it.tile * kTM;
     const int nkb = K / kTK, nnb = N / kQBlock;
 
-    // ---- quantiser role: row 8*wave + lane/8, K values 8c..8c+7 and
-    //      64+8c..64+8c+7 with c = lane % 8
-    const int qchunk = lane & 7;
-    const int qrow = 8 * wave + (lane >> 3);
+    // ---- quantiser role: row 8*wave + lane/8, chunk c = lane % 8
+    const int qchunk = lane % kLPR;
+    const int qrow = kRPW * wave + lane / kLPR;
     const int64_t qgrow = row0 + qrow;
     const bool qvalid = qgrow >= it.lo && qgrow < it.hi;
     const int64_t qlrow = qvalid ? qgrow : it.lo;    // in-bounds row the loads use
     const bool write_q = WRITE_Q && nt == 0 && qvalid;
-    const float* srg = rhs_scale + (int64_t)g * nkb * nnb + n0 / kQBlock;  // + kb*nnb + nblk
+    // RHS scale this lane folds into its row factor: 128-column block qchunk
+    // of the tile (clamped; lanes past NBLK write an unused slot)
+    const float* srl = rhs_scale + (int64_t)g * nkb * nnb + n0 / kQBlock + min(qchunk, NBLK - 1);
 
     // ---- MFMA role: columns [n0 + wave*WN, +WN); lane = row/col lr, K chunk lc.
     //      B is the packed RHS: 2 KB per (16-column block, subchannel), this
@@ -211,79 +235,117 @@ __global__ __launch_bounds__(kThreads, WN <= 32 ? 2 : 1) void fp8_fwd_kernel(
 #pragma unroll
         for (int j = 0; j < NB; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    RawA<KIND> raw;
-    v8i b[NB];
-
-    // Quantise the raw registers (subchannel kb) into LDS buffer buf.  The
-    // RHS scales of the tile's 128-column blocks are wave-uniform scalar loads.
-    auto quant_store = [&](int kb, int buf) {
-        const float* srk = srg + kb * nnb;   // wave-uniform: scalar loads
-        float srv[NBLK];
+    auto load_stage = [&](Stage<KIND>& st, int kb) {
+        load_raw<KIND>(st.raw, lhs, lhs_scale, qlrow, K, kb, qchunk);
+        st.sr = srl[kb * nnb];
+    };
+    // Quantise a stage (subchannel kb) into LDS buffer buf.
+    auto quant_store = [&](int kb, int buf, const Stage<KIND>& st) {
+        uint2 codes[kNP];
+        const float s = quantize_raw<KIND>(st.raw, codes);
 #pragma unroll
-        for (int q = 0; q < NBLK; ++q) srv[q] = srk[q];
-        float sr = srv[0];
-#pragma unroll
-        for (int q = 1; q < NBLK; ++q) sr = qchunk == q ? srv[q] : sr;
-        uint2 codes[2];
-        const float s = quantize_raw<KIND>(raw, codes);
-        *reinterpret_cast<uint2*>(&sm.a[buf][qrow][qchunk * 8]) = codes[0];
-        *reinterpret_cast<uint2*>(&sm.a[buf][qrow][64 + qchunk * 8]) = codes[1];
-        if (qchunk < NBLK) sm.c[buf][qchunk][qrow] = s * sr;
+        for (int p = 0; p < kNP; ++p)
+            *reinterpret_cast<uint2*>(&sm.a[buf][qrow][qchunk * 8 + p * 8 * kLPR]) = codes[p];
+        sm.c[buf][qchunk][qrow] = s * st.sr;
         if (write_q) {
-            *reinterpret_cast<uint2*>(q_out + qgrow * K + kb * kTK + qchunk * 8) = codes[0];
-            *reinterpret_cast<uint2*>(q_out + qgrow * K + kb * kTK + 64 + qchunk * 8) = codes[1];
+#pragma unroll
+            for (int p = 0; p < kNP; ++p)
+                *reinterpret_cast<uint2*>(q_out + qgrow * K + kb * kTK + qchunk * 8 + p * 8 * kLPR) = codes[p];
             if (qchunk == 0) s_out[qgrow * nkb + kb] = s;
         }
     };
-    auto load_b = [&](int j, int kb) {
-        const uint8_t* p = bptr + ((int64_t)j * nkb + kb) * 2048;
-        const uint4 lo = *reinterpret_cast<const uint4*>(p);
-        const uint4 hi = *reinterpret_cast<const uint4*>(p + 1024);
-        b[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    auto load_b = [&](v8i (&b)[NB], int kb) {
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            const uint8_t* p = bptr + ((int64_t)j * nkb + kb) * 2048;
+            const uint4 lo = *reinterpret_cast<const uint4*>(p);
+            const uint4 hi = *reinterpret_cast<const uint4*>(p + 1024);
+            b[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        }
     };
 
-    // ---- prologue: subchannel 0 quantised in LDS, raw subchannel 1 and B(0) in registers
-    load_raw<KIND>(raw, lhs, lhs_scale, qlrow, K, 0, qchunk);
-#pragma unroll
-    for (int j = 0; j < NB; ++j) load_b(j, 0);
-    quant_store(0, 0);
-    load_raw<KIND>(raw, lhs, lhs_scale, qlrow, K, min(1, nkb - 1), qchunk);
-    __syncthreads();
-
-    // Iteration kb (straight-line code, so loads stay in flight across it):
-    // MFMAs of kb from LDS buffer kb&1, each B column block reloaded with
-    // kb+1 right after its MFMAs; raw(kb+1) quantised into buffer (kb+1)&1;
-    // raw(kb+2) loads issued.  Prefetch indices are clamped to the last
-    // subchannel (a redundant reload) instead of branching.
-    for (int kb = 0; kb < nkb; ++kb) {
+    // Step kb.  B of kb+1 is requested first, into the register set the MFMAs
+    // of this step do not use; the A fragments of kb are read from LDS; the
+    // stage quantised now (kb+1, into the other LDS buffer) was loaded two
+    // steps earlier and is reloaded at once with kb+3.  The loads are issued
+    // in the same order every step (B, then the stage) and the prologue issues
+    // them in that order too, so the waits the compiler places are counts,
+    // not full drains.  Indices past the last subchannel are clamped to it
+    // (redundant reloads instead of branches).
+    auto step = [&](int kb, v8i (&bc)[NB], v8i (&bn)[NB], Stage<KIND>& sq) {
         const int buf = kb & 1;
-        const int kb1 = min(kb + 1, nkb - 1), kb2 = min(kb + 2, nkb - 1);
+        const int kb1 = min(kb + 1, nkb - 1), kb3 = min(kb + 3, nkb - 1);
+        load_b(bn, kb1);
+        __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead of the quantiser's VALU work
         // Operands are swapped so each 16x16 block comes out transposed: lane
         // (lr, lc) holds row 16i + lr and the four consecutive columns
         // 16j + 4lc .. +3, so its per-row factor sl * sr is one scalar per row
         // block.
-        v8i af[MB];
-        float cf[MB];
-#pragma unroll
-        for (int i = 0; i < MB; ++i) {
-            af[i] = *reinterpret_cast<const v8i*>(&sm.a[buf][16 * i + lr][lc * 32]);
-            cf[i] = sm.c[buf][my_nblk][16 * i + lr];
-        }
-        quant_store(kb1, buf ^ 1);
-        load_raw<KIND>(raw, lhs, lhs_scale, qlrow, K, kb2, qchunk);
-#pragma unroll
-        for (int j = 0; j < NB; ++j) {
+        // All A fragments are read up front, except in the code-writing
+        // variant, which reads one row block at a time to stay within the
+        // register budget.
+        constexpr bool kAllA = !WRITE_Q;
+        v8i af[kAllA ? MB : 1];
+        float cf[kAllA ? MB : 1];
+        if constexpr (kAllA) {
 #pragma unroll
             for (int i = 0; i < MB; ++i) {
-                const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                    b[j], af[i], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(p[r], cf[i], acc[i][j][r]);
+                af[i] = *reinterpret_cast<const v8i*>(&sm.a[buf][16 * i + lr][lc * 32]);
+                cf[i] = sm.c[buf][my_nblk][16 * i + lr];
             }
-            load_b(j, kb1);
         }
+        quant_store(kb1, buf ^ 1, sq);
+#pragma unroll
+        for (int i = 0; i < MB; ++i) {
+            const int ia = kAllA ? i : 0;
+            if constexpr (!kAllA) {
+                af[0] = *reinterpret_cast<const v8i*>(&sm.a[buf][16 * i + lr][lc * 32]);
+                cf[0] = sm.c[buf][my_nblk][16 * i + lr];
+            }
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    bc[j], af[ia], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(p[r], cf[ia], acc[i][j][r]);
+            }
+        }
+        load_stage(sq, kb3);
+        // Issue order inside the step: the A-fragment reads, then each MFMA
+        // followed by a slice of VALU work (the next subchannel's quantiser
+        // and earlier blocks' scale FMAs) so that VALU issues while the
+        // matrix core runs, then the LDS stores and the stage loads.
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * MB + MB / 2, 0);
+#pragma unroll
+        for (int q = 0; q < MB * NB; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, GMM_FP8_VALU_PER_MFMA, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x200, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 4, 0);
         __syncthreads();
+    };
+
+    // ---- prologue: subchannel 0 quantised in LDS; in flight, in steady-state
+    //      order: stage 1, B(0), stage 2
+    Stage<KIND> st0, st1;
+    v8i bA[NB], bB[NB];
+    load_stage(st0, 0);
+    quant_store(0, 0, st0);
+    load_stage(st1, min(1, nkb - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    load_b(bA, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_stage(st0, min(2, nkb - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+
+    int kb = 0;
+    for (; kb + 1 < nkb; kb += 2) {
+        step(kb, bA, bB, st1);
+        step(kb + 1, bB, bA, st0);
     }
+    if (kb < nkb) step(kb, bA, bB, st1);
 
     // ---- epilogue: each lane stores 4 consecutive outputs of its rows directly
     //      (8 bytes for bf16, 16 for fp32); rows outside the item are skipped
@@ -328,9 +390,11 @@ hipError_t launch_wn(const void* lhs, const float* lhs_scale, const uint8_t* rhs
                      const float* rhs_scale, const int32_t* group_sizes, int M, int K, int N,
                      int G, void* out, bool out_bf16, uint8_t* q_out, float* scale_out,
                      hipStream_t stream) {
-    if (KIND != kLhsE4M3 && q_out != nullptr)
-        return launch_cfg<KIND, WN, true>(lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N, G,
-                                          out, out_bf16, q_out, scale_out, stream);
+    if constexpr (KIND != kLhsE4M3) {
+        if (q_out != nullptr)
+            return launch_cfg<KIND, WN, true>(lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N,
+                                              G, out, out_bf16, q_out, scale_out, stream);
+    }
     return launch_cfg<KIND, WN, false>(lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N, G,
                                        out, out_bf16, q_out, scale_out, stream);
 }
@@ -351,12 +415,12 @@ hipError_t launch_kind(const void* lhs, const float* lhs_scale, const uint8_t* r
     if ((forced == 16 || forced == 32 || forced == 64) && N % (kWaves * forced) == 0) wn = forced;
     if (wn == 64)
         return launch_wn<KIND, 64>(lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N, G, out,
-                                    out_bf16, q_out, scale_out, stream);
+                                   out_bf16, q_out, scale_out, stream);
     if (wn == 32)
         return launch_wn<KIND, 32>(lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N, G, out,
-                                    out_bf16, q_out, scale_out, stream);
+                                   out_bf16, q_out, scale_out, stream);
     return launch_wn<KIND, 16>(lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N, G, out,
-                                out_bf16, q_out, scale_out, stream);
+                               out_bf16, q_out, scale_out, stream);
 }
 
 }  // namespace

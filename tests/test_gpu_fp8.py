@@ -87,8 +87,10 @@ def test_many_groups_with_empties():
     check_full(wl, torch.bfloat16)
 
 
-def test_prequantised_lhs_path():
-    wl = workloads.custom(333, 512, 256, [100, 0, 200, 13], seed=9)
+@pytest.mark.parametrize("N", [256, 512, 1024])
+def test_prequantised_lhs_path(N):
+    """N = 512, 1024 run the 16-wave tiles, N = 256 the 8-wave ones."""
+    wl = workloads.custom(333, 512, N, [100, 0, 200, 13], seed=9)
     ql, sl = oracle.quantize_lhs(workloads.as_f32(wl.x))
     qr_o, sr_o = oracle.quantize_rhs(workloads.as_f32(wl.w))
     rq, rs = gmm.gmm_quantize_rhs(wl.w.to(DEV))
@@ -97,9 +99,14 @@ def test_prequantised_lhs_path():
                           lhs_scale=torch.from_numpy(sl).to(DEV), out_dtype=torch.float32)
     ref = oracle.gmm_fp8(ql, sl, qr_o, sr_o, wl.group_sizes)
     assert_fp8_parity(to_np64(out), ref, "pre-quantised")
-    # the fused path gives the same codes, so the same result up to fp32 order
+    # the fused path gives the same codes, hence bit-identical results (same
+    # tile shape, same accumulation order)
     fused, _, _ = run_fp8(wl, torch.float32)
     assert np.array_equal(to_np64(fused), to_np64(out))
+    fused_bf, _, _ = run_fp8(wl, torch.bfloat16)
+    pre_bf = gmm.gmm_fp8_fwd(torch.from_numpy(ql).to(DEV), rq, rs, gs,
+                             lhs_scale=torch.from_numpy(sl).to(DEV), out_dtype=torch.bfloat16)
+    assert torch.equal(fused_bf, pre_bf)
 
 
 def test_exact_integer_case_bitwise():
