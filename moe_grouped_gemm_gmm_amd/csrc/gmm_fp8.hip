@@ -160,6 +160,16 @@ struct Smem {
                                         // (slots >= NBLK are written, never read)
 };
 
+// Shared memory of a workgroup: the loop's A tiles, or, after the loop, each
+// wave's bf16 output block (64 rows x WN columns, rows padded by 16 bytes) for
+// the row-contiguous write-back.
+template <int WN>
+union SmemAll {
+    static constexpr int kEpiRow = WN * 2 + 16;
+    Smem<WN> m;
+    uint8_t epi[kWaves][kTM][kEpiRow];
+};
+
 // What one lane needs to quantise one subchannel: its raw LHS values and the
 // RHS scale of the 128-column block whose per-row factor it writes.
 template <int KIND>
@@ -181,7 +191,8 @@ __global__ __launch_bounds__(kThreads, 2) void fp8_fwd_kernel(
     constexpr int OUT_BYTES = OUT_BF16 ? 2 : 4;
 
     __shared__ WorkItem s_item;
-    __shared__ __attribute__((aligned(16))) Smem<WN> sm;
+    __shared__ __attribute__((aligned(16))) SmemAll<WN> smu;
+    Smem<WN>& sm = smu.m;
 
     const int tid = threadIdx.x, lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -347,21 +358,44 @@ __global__ __launch_bounds__(kThreads, 2) void fp8_fwd_kernel(
     }
     if (kb < nkb) step(kb, bA, bB, st1);
 
-    // ---- epilogue: each lane stores 4 consecutive outputs of its rows directly
-    //      (8 bytes for bf16, 16 for fp32); rows outside the item are skipped
+    // ---- epilogue.  bf16: each wave writes its 64 x WN block to its own LDS
+    //      region (the loop's last barrier has retired every read of the A
+    //      tiles) and stores it back row by row, 16 bytes per lane, so every
+    //      store instruction writes whole WN*2-byte row segments.  fp32: each
+    //      lane stores its 4 consecutive outputs directly.  Rows outside the
+    //      item are skipped.
+    if constexpr (OUT_BF16) {
+        constexpr int ROWB = WN * 2;              // bytes of a row segment
+        constexpr int LPRO = ROWB / 16;           // lanes per row on the way out
+        constexpr int RPI = 64 / LPRO;            // rows per store instruction
+        uint8_t (*ep)[SmemAll<WN>::kEpiRow] = smu.epi[wave];
 #pragma unroll
-    for (int i = 0; i < MB; ++i) {
-        const int grow = row0 + 16 * i + lr;
-        if (grow < it.lo || grow >= it.hi) continue;
+        for (int i = 0; i < MB; ++i)
 #pragma unroll
-        for (int j = 0; j < NB; ++j) {
-            const int64_t o = (int64_t)grow * N + ncol0 + 16 * j + 4 * lc;
-            if constexpr (OUT_BF16)
-                *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + o) =
+            for (int j = 0; j < NB; ++j)
+                *reinterpret_cast<uint2*>(&ep[16 * i + lr][(16 * j + 4 * lc) * 2]) =
                     make_uint2(pack_bf16x2(acc[i][j][0], acc[i][j][1]), pack_bf16x2(acc[i][j][2], acc[i][j][3]));
-            else
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");   // this wave's writes before its reads
+        const int orow = lane / LPRO, ocol = (lane % LPRO) * 16;
+#pragma unroll
+        for (int q = 0; q < kTM / RPI; ++q) {
+            const int r = RPI * q + orow;
+            const uint4 v = *reinterpret_cast<const uint4*>(&ep[r][ocol]);
+            const int grow = row0 + r;
+            if (grow >= it.lo && grow < it.hi)
+                *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(out) + ((int64_t)grow * N + ncol0) * 2 + ocol) = v;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < MB; ++i) {
+            const int grow = row0 + 16 * i + lr;
+            if (grow < it.lo || grow >= it.hi) continue;
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                const int64_t o = (int64_t)grow * N + ncol0 + 16 * j + 4 * lc;
                 *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + o) =
                     make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+            }
         }
     }
 }
