@@ -80,8 +80,8 @@ GMM_API const char *gmm_last_error(void);
  * offsets:  device int32 [G+1], exclusive prefix sums of group_sizes.
  * work:     device int32 [capacity][4].
  * num_work: device int32 [1], number of entries written.
- * capacity must be >= ceil(M/tile_m) + G + 1; tile_m in {16,...,1024}, a
- * power of two.
+ * capacity must be >= ceil(M/tile_m) + G + 1; tile_m a multiple of 16 in
+ * [16, 1024].
  */
 GMM_API int gmm_group_metadata(const int32_t *group_sizes, int64_t G, int64_t M,
                        int64_t tile_m, int32_t *offsets, int32_t *work,

@@ -94,14 +94,12 @@ int gmm_group_metadata(const int32_t* group_sizes, int64_t G, int64_t M, int64_t
     GMM_TRY(check_ptr(offsets, "offsets"));
     GMM_TRY(check_ptr(work, "work"));
     GMM_TRY(check_ptr(num_work, "num_work"));
-    int tm_log2 = -1;
-    for (int l = 4; l <= 10; ++l)
-        if (tile_m == (int64_t(1) << l)) tm_log2 = l;
-    if (tm_log2 < 0) return fail(GMM_ERR_SHAPE, "tile_m=%lld is not a power of two in [16,1024]", (long long)tile_m);
+    if (tile_m < 16 || tile_m > 1024 || tile_m % 16 != 0)
+        return fail(GMM_ERR_SHAPE, "tile_m=%lld is not a multiple of 16 in [16,1024]", (long long)tile_m);
     const int64_t need = (M + tile_m - 1) / tile_m + G + 1;
     if (capacity < need || capacity > kMaxDim)
         return fail(GMM_ERR_SHAPE, "capacity=%lld, need >= %lld", (long long)capacity, (long long)need);
-    return hip_status(gmm::launch_group_metadata(group_sizes, (int)G, (int)M, tm_log2, offsets,
+    return hip_status(gmm::launch_group_metadata(group_sizes, (int)G, (int)M, (int)tile_m, offsets,
                                                  work, (int)capacity, num_work,
                                                  (hipStream_t)stream));
 }

@@ -50,41 +50,39 @@ __device__ __forceinline__ v8bf read_direct(const uint16_t* tile, int stride, in
     return *reinterpret_cast<const v8bf*>(tile + row * stride + r0);
 }
 
-// Copy a [128 rows][64] bf16 slice (row-major source, leading dimension ld)
-// into a direct LDS tile; rows with !valid become zeros.
-__device__ __forceinline__ void stage_direct(uint16_t* tile, const uint16_t* src, int64_t ld,
-                                             bool valid) {
-    const int t = threadIdx.x, row = t >> 1, h = t & 1;
-    uint4 d[4];
-    if (valid) {
-        const uint4* p = reinterpret_cast<const uint4*>(src + (int64_t)row * ld + h * 32);
+// One thread's share of a staged slice: 4 x 16 bytes.  Loads are always
+// issued from in-bounds addresses (callers clamp the row) and never consumed
+// before the slice is written to LDS, so a prefetch stays in flight while the
+// MFMAs of the current slice run; rows that must read as zero are masked when
+// written to LDS.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+struct Frag4 {
+    u32x4 d[4];
+};
+
+__device__ __forceinline__ void fetch4(Frag4& f, const uint16_t* p) {
+    const u32x4* q = reinterpret_cast<const u32x4*>(p);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) d[c] = p[c];
-    } else {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) d[c] = make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-        *reinterpret_cast<uint4*>(tile + row * (kR + kPadD) + h * 32 + 8 * c) = d[c];
+    for (int c = 0; c < 4; ++c) f.d[c] = q[c];
 }
 
-// Copy a [64 rows][128] bf16 slice into a transposed-layout LDS tile.
-__device__ __forceinline__ void stage_trans(uint16_t* tile, const uint16_t* src, int64_t ld,
-                                            bool valid) {
-    const int t = threadIdx.x, row = t >> 2, q = t & 3;
-    uint4 d[4];
-    if (valid) {
-        const uint4* p = reinterpret_cast<const uint4*>(src + (int64_t)row * ld + q * 32);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) d[c] = p[c];
-    } else {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) d[c] = make_uint4(0, 0, 0, 0);
-    }
+// Direct LDS tile [128 rows][64]: thread t holds row t/2, columns 32*(t%2) .. +31.
+__device__ __forceinline__ void put_direct(uint16_t* tile, const Frag4& f) {
+    const int t = threadIdx.x, row = t >> 1, h = t & 1;
 #pragma unroll
     for (int c = 0; c < 4; ++c)
-        *reinterpret_cast<uint4*>(tile + row * (kT + kPadT) + q * 32 + 8 * c) = d[c];
+        *reinterpret_cast<u32x4*>(tile + row * (kR + kPadD) + h * 32 + 8 * c) = f.d[c];
+}
+
+// Transposed-layout LDS tile [64 rows][128]: thread t holds row t/4,
+// columns 32*(t%4) .. +31; rows with !valid are written as zeros.
+__device__ __forceinline__ void put_trans(uint16_t* tile, const Frag4& f, bool valid) {
+    const int t = threadIdx.x, row = t >> 2, q = t & 3;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+        *reinterpret_cast<u32x4*>(tile + row * (kT + kPadT) + q * 32 + 8 * c) =
+            valid ? f.d[c] : u32x4{0u, 0u, 0u, 0u};
 }
 
 // Offset of group g: sum of group_sizes[0..g), computed by one wave.
@@ -136,7 +134,7 @@ __global__ __launch_bounds__(256, 2) void bf16_gemm_kernel(
         const int w = L / ntiles_c;
         c0 = (L % ntiles_c) * kT;
         if (wave == 0) {
-            const WorkItem it = find_work_item(group_sizes, G, M, 7, w);
+            const WorkItem it = find_work_item(group_sizes, G, M, kT, w);
             if (lane == 0) { s_info[0] = it.g; s_info[1] = it.tile; s_info[2] = it.lo; s_info[3] = it.hi; }
         }
         __syncthreads();
@@ -171,26 +169,44 @@ __global__ __launch_bounds__(256, 2) void bf16_gemm_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    for (int r0 = red_lo; r0 < red_hi; r0 += kR) {
-        // ---- stage the A and B slices of reduction range [r0, r0 + 64)
+    // Global -> registers for reduction range [r0, r0 + 64) of both operands.
+    // Direct slices: thread t reads row t/2 (clamped into the item for A; its
+    // values only reach output rows that are never stored), columns
+    // 32*(t%2) .. +31.  Transposed slices: row t/4, columns 32*(t%4) .. +31;
+    // in tgmm rows past the group's end are clamped to its last row here and
+    // zeroed when written to LDS.
+    const int lda = MODE == kFwd ? K : N;
+    const uint16_t* wg = B + (int64_t)(MODE == kTgmm ? 0 : g) * K * N;
+    const int trow = tid >> 2, tq = tid & 3;
+    const int drow = tid >> 1, dh = tid & 1;
+    const int arow = min(max(row0 + drow, lo), hi - 1);
+    auto fetch = [&](Frag4& fa, Frag4& fb, int r0) {
         if constexpr (MODE == kTgmm) {
-            const int m = r0 + (tid >> 2);
-            const bool valid = m < red_hi;
-            stage_trans(sA, A + (int64_t)r0 * K + row0, K, valid);   // x[m][k0..k0+128]
-            stage_trans(sB, B + (int64_t)r0 * N + c0, N, valid);     // dy[m][n0..n0+128]
+            const int m = min(r0 + trow, red_hi - 1);
+            fetch4(fa, A + (int64_t)m * K + row0 + tq * 32);   // x[m][k0..k0+128]
+            fetch4(fb, B + (int64_t)m * N + c0 + tq * 32);     // dy[m][n0..n0+128]
         } else {
-            const int arow = row0 + (tid >> 1);
-            const bool avalid = arow >= lo && arow < hi;
-            const int lda = MODE == kFwd ? K : N;
-            stage_direct(sA, A + (int64_t)row0 * lda + r0, lda, avalid);
-            const uint16_t* wg = B + (int64_t)g * K * N;
+            fetch4(fa, A + (int64_t)arow * lda + r0 + dh * 32);
             if constexpr (MODE == kFwd)
-                stage_trans(sB, wg + (int64_t)r0 * N + c0, N, true);  // w[g][k][n0..n0+128]
+                fetch4(fb, wg + (int64_t)(r0 + trow) * N + c0 + tq * 32);    // w[g][k][n0..n0+128]
             else
-                stage_direct(sB, wg + (int64_t)c0 * N + r0, N, true); // w[g][k0+c][n]
+                fetch4(fb, wg + (int64_t)(c0 + drow) * N + r0 + dh * 32);    // w[g][k0+c][n]
         }
-        __syncthreads();
+    };
 
+    // Software pipeline: the next slice is fetched into registers while the
+    // MFMAs of the current one run; one LDS buffer, two barriers per slice.
+    // The MFMA operands are swapped (B fragment first) so that each 16x16
+    // block comes out transposed: lane (lr, lg) holds row 16i + lr and the
+    // four consecutive columns 16j + 4lg .. +3.
+    Frag4 fa, fb;
+    if (red_lo < red_hi) fetch(fa, fb, red_lo);
+    for (int r0 = red_lo; r0 < red_hi; r0 += kR) {
+        const bool tvalid = MODE != kTgmm || r0 + trow < red_hi;
+        if constexpr (A_TR) put_trans(sA, fa, tvalid); else put_direct(sA, fa);
+        if constexpr (B_TR) put_trans(sB, fb, tvalid); else put_direct(sB, fb);
+        __syncthreads();
+        if (r0 + kR < red_hi) fetch(fa, fb, r0 + kR);
 #pragma unroll
         for (int s = 0; s < kR / 32; ++s) {
             v8bf af[4], bf[4];
@@ -212,29 +228,49 @@ __global__ __launch_bounds__(256, 2) void bf16_gemm_kernel(
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
         }
         __syncthreads();
     }
 
-    // ---- epilogue: masked stores
+    // ---- epilogue.  bf16: each wave writes its 64 x 64 block into its own
+    //      part of the (now idle) LDS tiles and stores it back row by row,
+    //      8 lanes x 16 bytes per 128-byte row segment.  fp32: each lane
+    //      stores its four consecutive columns (16 bytes).  Rows outside
+    //      [lo, hi) are skipped.
     const int64_t obase = MODE == kTgmm ? (int64_t)g * K * N : 0;
+    const int col0 = c0 + wn * 64;
+    if constexpr (OUT_BF16) {
+        constexpr int kEpiRow = 64 + 8;   // bf16 elements per staged row (144 bytes)
+        static_assert(4 * 64 * kEpiRow <= 2 * kTileElems, "epilogue staging fits the LDS tiles");
+        uint16_t* ep = (wave < 2 ? sA : sB) + (wave & 1) * 64 * kEpiRow;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = row0 + wm * 64 + i * 16 + lg * 4 + r;
+            for (int j = 0; j < 4; ++j)
+                *reinterpret_cast<uint2*>(ep + (16 * i + lr) * kEpiRow + 16 * j + 4 * lg) =
+                    make_uint2(pack_bf16x2(acc[i][j][0], acc[i][j][1]), pack_bf16x2(acc[i][j][2], acc[i][j][3]));
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");   // this wave's writes before its reads
+        const int orow = lane >> 3, ocol = (lane & 7) * 8;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int r = 8 * q + orow;
+            const uint4 v = *reinterpret_cast<const uint4*>(ep + r * kEpiRow + ocol);
+            const int row = row0 + wm * 64 + r;
+            if (row >= lo && row < hi)
+                *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + obase + (int64_t)row * out_cols + col0 + ocol) = v;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = row0 + wm * 64 + i * 16 + lr;
             if (row < lo || row >= hi) continue;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int col = c0 + wn * 64 + j * 16 + lr;
-                const int64_t idx = obase + (int64_t)row * out_cols + col;
-                if constexpr (OUT_BF16)
-                    reinterpret_cast<uint16_t*>(out)[idx] = (uint16_t)f32_to_bf16_bits(acc[i][j][r]);
-                else
-                    reinterpret_cast<float*>(out)[idx] = acc[i][j][r];
-            }
+            for (int j = 0; j < 4; ++j)
+                *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + obase + (int64_t)row * out_cols + col0 + 16 * j + 4 * lg) =
+                    make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
         }
+    }
 }
 
 template <int MODE>

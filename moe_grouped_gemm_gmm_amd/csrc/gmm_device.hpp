@@ -121,19 +121,21 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 }
 
 // ------------------------------------------------------- group metadata --
-// Work item w of a grouped kernel with row tiles of height 2^tm_log2, tiles
-// aligned to absolute rows.  Items are ordered group by group; each non-empty
-// group g owns the tiles that intersect rows [o_g, o_g + s_g), the item's row
-// range being that intersection.  After the groups come the items that zero
-// the rows at or past the total (g == G).  g < 0 means "no item" (the grid is
-// sized for the worst case).  Every lane of the calling wave gets the result.
+// Work item w of a grouped kernel with row tiles of height tm (a multiple of
+// 16), tiles aligned to absolute rows.  Items are ordered group by group;
+// each non-empty group g owns the tiles that intersect rows [o_g, o_g + s_g),
+// the item's row range being that intersection.  After the groups come the
+// items that zero the rows at or past the total (g == G).  g < 0 means "no
+// item" (the grid is sized for the worst case).  Every lane of the calling
+// wave gets the result.  Callers pass a compile-time tm, so the divisions
+// become multiply-shifts.
 
 struct WorkItem {
     int g, tile, lo, hi;
 };
 
-__device__ inline WorkItem find_work_item(const int32_t* __restrict__ group_sizes, int G, int M,
-                                          int tm_log2, int w) {
+__device__ __forceinline__ WorkItem find_work_item(const int32_t* __restrict__ group_sizes, int G,
+                                                   int M, int tm, int w) {
     const int lane = lane_id();
     int carry_rows = 0, carry_items = 0;
     for (int base = 0; base < G; base += 64) {
@@ -141,7 +143,7 @@ __device__ inline WorkItem find_work_item(const int32_t* __restrict__ group_size
         const int s = g < G ? group_sizes[g] : 0;
         const int incl = wave_incl_scan(s);
         const int o = carry_rows + incl - s;
-        const int c = s > 0 ? ((o + s - 1) >> tm_log2) - (o >> tm_log2) + 1 : 0;
+        const int c = s > 0 ? (o + s - 1) / tm - o / tm + 1 : 0;
         const int inclc = wave_incl_scan(c);
         const int W = carry_items + inclc - c;
         const bool own = c > 0 && w >= W && w < W + c;
@@ -151,12 +153,12 @@ __device__ inline WorkItem find_work_item(const int32_t* __restrict__ group_size
             const int go = __shfl(o, src, 64);
             const int gsz = __shfl(s, src, 64);
             const int gW = __shfl(W, src, 64);
-            const int t = (go >> tm_log2) + (w - gW);
+            const int t = go / tm + (w - gW);
             WorkItem it;
             it.g = base + src;
             it.tile = t;
-            it.lo = max(go, t << tm_log2);
-            it.hi = min(go + gsz, (t + 1) << tm_log2);
+            it.lo = max(go, t * tm);
+            it.hi = min(go + gsz, (t + 1) * tm);
             return it;
         }
         carry_rows += __shfl(incl, 63, 64);
@@ -164,11 +166,11 @@ __device__ inline WorkItem find_work_item(const int32_t* __restrict__ group_size
     }
     WorkItem it;
     const int total = carry_rows;
-    const int t = (total >> tm_log2) + (w - carry_items);
+    const int t = total / tm + (w - carry_items);
     it.g = G;
     it.tile = t;
-    it.lo = max(total, t << tm_log2);
-    it.hi = min(M, (t + 1) << tm_log2);
+    it.lo = max(total, t * tm);
+    it.hi = min(M, (t + 1) * tm);
     if (it.lo >= it.hi) it.g = -1;
     return it;
 }

@@ -58,7 +58,7 @@ namespace gmm {
 namespace {
 
 constexpr int kTK = 128;           // one subchannel
-constexpr int kTM = 64;            // rows per workgroup
+constexpr int kTM = 64;            // rows the quantiser covers (LDS tile height)
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kLdsRow = kTK + 16;  // 144-byte LDS rows: conflict-free 16-lane ds_read_b128
@@ -178,13 +178,19 @@ struct Stage {
     float sr;
 };
 
-template <int KIND, bool OUT_BF16, int WN, bool WRITE_Q>
+// TM (64 or 48) is the row-tile height.  With 48-row tiles the quantiser
+// still covers 64 rows: the last 16 lie past the tile, are never valid for the
+// item and are never read by an MFMA, so the quantiser and the LDS layout stay
+// the same while each workgroup does three quarters of the MFMA work and more
+// workgroups share the chip.
+template <int KIND, bool OUT_BF16, int WN, int TM, bool WRITE_Q>
 __global__ __launch_bounds__(kThreads, 2) void fp8_fwd_kernel(
     const void* __restrict__ lhs, const float* __restrict__ lhs_scale,
     const uint8_t* __restrict__ rhs, const float* __restrict__ rhs_scale,
     const int32_t* __restrict__ group_sizes, int M, int K, int N, int G, void* __restrict__ out,
     uint8_t* __restrict__ q_out, float* __restrict__ s_out, int ntiles_n, int nblocks) {
-    constexpr int MB = kTM / 16;  // 16-row blocks
+    static_assert(TM == 64 || TM == 48, "64- or 48-row tiles");
+    constexpr int MB = TM / 16;   // 16-row blocks of the tile
     constexpr int NB = WN / 16;   // 16-column blocks per wave
     constexpr int TN = kWaves * WN;
     constexpr int NBLK = Smem<WN>::NBLK;
@@ -199,7 +205,7 @@ __global__ __launch_bounds__(kThreads, 2) void fp8_fwd_kernel(
     const int L = xcd_remap(blockIdx.x, nblocks);
     const int w = L / ntiles_n, nt = L % ntiles_n;
     if (wave == 0) {
-        const WorkItem it = find_work_item(group_sizes, G, M, 6, w);
+        const WorkItem it = find_work_item(group_sizes, G, M, TM, w);
         if (lane == 0) s_item = it;
     }
     __syncthreads();
@@ -218,7 +224,7 @@ __global__ __launch_bounds__(kThreads, 2) void fp8_fwd_kernel(
         return;
     }
 
-    const int g = it.g, row0 = it.tile * kTM;
+    const int g = it.g, row0 = it.tile * TM;
     const int nkb = K / kTK, nnb = N / kQBlock;
 
     // ---- quantiser role: row 8*wave + lane/8, chunk c = lane % 8
@@ -378,7 +384,7 @@ __global__ __launch_bounds__(kThreads, 2) void fp8_fwd_kernel(
         __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");   // this wave's writes before its reads
         const int orow = lane / LPRO, ocol = (lane % LPRO) * 16;
 #pragma unroll
-        for (int q = 0; q < kTM / RPI; ++q) {
+        for (int q = 0; q < (TM + RPI - 1) / RPI; ++q) {   // rows past the tile fail the row check
             const int r = RPI * q + orow;
             const uint4 v = *reinterpret_cast<const uint4*>(&ep[r][ocol]);
             const int grow = row0 + r;
@@ -400,61 +406,86 @@ __global__ __launch_bounds__(kThreads, 2) void fp8_fwd_kernel(
     }
 }
 
-template <int KIND, int WN, bool WRITE_Q>
+template <int KIND, int WN, int TM, bool WRITE_Q>
 hipError_t launch_cfg(const void* lhs, const float* lhs_scale, const uint8_t* rhs,
                       const float* rhs_scale, const int32_t* group_sizes, int M, int K, int N,
                       int G, void* out, bool out_bf16, uint8_t* q_out, float* scale_out,
                       hipStream_t stream) {
     const int ntiles_n = N / (kWaves * WN);
-    const int64_t items = max_work_items(M, G, kTM);
+    const int64_t items = max_work_items(M, G, TM);
     const int nblocks = (int)(items * ntiles_n);
     if (out_bf16)
-        hipLaunchKernelGGL((fp8_fwd_kernel<KIND, true, WN, WRITE_Q>), dim3(nblocks), dim3(kThreads),
+        hipLaunchKernelGGL((fp8_fwd_kernel<KIND, true, WN, TM, WRITE_Q>), dim3(nblocks), dim3(kThreads),
                            0, stream, lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N, G, out,
                            q_out, scale_out, ntiles_n, nblocks);
     else
-        hipLaunchKernelGGL((fp8_fwd_kernel<KIND, false, WN, WRITE_Q>), dim3(nblocks), dim3(kThreads),
+        hipLaunchKernelGGL((fp8_fwd_kernel<KIND, false, WN, TM, WRITE_Q>), dim3(nblocks), dim3(kThreads),
                            0, stream, lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N, G, out,
                            q_out, scale_out, ntiles_n, nblocks);
     return hipGetLastError();
 }
 
-template <int KIND, int WN>
+template <int KIND, int WN, int TM>
 hipError_t launch_wn(const void* lhs, const float* lhs_scale, const uint8_t* rhs,
                      const float* rhs_scale, const int32_t* group_sizes, int M, int K, int N,
                      int G, void* out, bool out_bf16, uint8_t* q_out, float* scale_out,
                      hipStream_t stream) {
     if constexpr (KIND != kLhsE4M3) {
         if (q_out != nullptr)
-            return launch_cfg<KIND, WN, true>(lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N,
-                                              G, out, out_bf16, q_out, scale_out, stream);
+            return launch_cfg<KIND, WN, TM, true>(lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K,
+                                                  N, G, out, out_bf16, q_out, scale_out, stream);
     }
-    return launch_cfg<KIND, WN, false>(lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N, G,
-                                       out, out_bf16, q_out, scale_out, stream);
+    return launch_cfg<KIND, WN, TM, false>(lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N,
+                                           G, out, out_bf16, q_out, scale_out, stream);
 }
 
-// Tile width: the widest of 512/256/128 columns that divides N (fewest
-// re-quantisations of each LHS row).  GMM_FP8_WN=<16|32|64> overrides the
-// per-wave width (tuning sweeps only).
+// Compute units of the current device (queried once).
+inline int device_cus() {
+    static const int cus = [] {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        return n;
+    }();
+    return cus;
+}
+
+// Tile: the widest of 512/256/128 columns that divides N (fewest
+// re-quantisations of each LHS row); 48 rows when even the worst-case number
+// of 48-row workgroups fits on the chip at once (more of the chip busy, less
+// work per workgroup), else 64.  GMM_FP8_WN=<16|32|64> and GMM_FP8_TM=<64|48>
+// override them (tuning sweeps only).
 template <int KIND>
 hipError_t launch_kind(const void* lhs, const float* lhs_scale, const uint8_t* rhs,
                        const float* rhs_scale, const int32_t* group_sizes, int M, int K, int N,
                        int G, void* out, bool out_bf16, uint8_t* q_out, float* scale_out,
                        hipStream_t stream) {
-    static const int forced = [] {
+    static const int forced_wn = [] {
         const char* e = std::getenv("GMM_FP8_WN");
         return e ? std::atoi(e) : 0;
     }();
+    static const int forced_tm = [] {
+        const char* e = std::getenv("GMM_FP8_TM");
+        return e ? std::atoi(e) : 0;
+    }();
     int wn = N % 512 == 0 ? 64 : (N % 256 == 0 ? 32 : 16);
-    if ((forced == 16 || forced == 32 || forced == 64) && N % (kWaves * forced) == 0) wn = forced;
-    if (wn == 64)
-        return launch_wn<KIND, 64>(lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N, G, out,
+    if ((forced_wn == 16 || forced_wn == 32 || forced_wn == 64) && N % (kWaves * forced_wn) == 0)
+        wn = forced_wn;
+    int tm = max_work_items(M, G, 48) * (N / (kWaves * wn)) <= device_cus() ? 48 : 64;
+    if (forced_tm == 48 || forced_tm == 64) tm = forced_tm;
+#define GMM_FP8_WN_TM(WN_, TM_)                                                                  \
+    if (wn == WN_ && tm == TM_)                                                                  \
+        return launch_wn<KIND, WN_, TM_>(lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N, G, \
+                                         out, out_bf16, q_out, scale_out, stream);
+    GMM_FP8_WN_TM(64, 64)
+    GMM_FP8_WN_TM(64, 48)
+    GMM_FP8_WN_TM(32, 64)
+    GMM_FP8_WN_TM(32, 48)
+    GMM_FP8_WN_TM(16, 48)
+#undef GMM_FP8_WN_TM
+    return launch_wn<KIND, 16, 64>(lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N, G, out,
                                    out_bf16, q_out, scale_out, stream);
-    if (wn == 32)
-        return launch_wn<KIND, 32>(lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N, G, out,
-                                   out_bf16, q_out, scale_out, stream);
-    return launch_wn<KIND, 16>(lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N, G, out,
-                               out_bf16, q_out, scale_out, stream);
 }
 
 }  // namespace

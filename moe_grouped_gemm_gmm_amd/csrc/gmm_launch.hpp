@@ -7,7 +7,7 @@
 
 namespace gmm {
 
-hipError_t launch_group_metadata(const int32_t* group_sizes, int G, int M, int tm_log2,
+hipError_t launch_group_metadata(const int32_t* group_sizes, int G, int M, int tm,
                                  int32_t* offsets, int32_t* work, int capacity,
                                  int32_t* num_work, hipStream_t stream);
 

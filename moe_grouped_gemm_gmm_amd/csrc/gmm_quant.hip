@@ -13,7 +13,7 @@ namespace gmm {
 // ------------------------------------------------------------ metadata --
 
 __global__ __launch_bounds__(256) void group_metadata_kernel(const int32_t* __restrict__ group_sizes,
-                                                             int G, int M, int tm_log2,
+                                                             int G, int M, int tm,
                                                              int32_t* __restrict__ offsets,
                                                              int32_t* __restrict__ work,
                                                              int capacity,
@@ -21,7 +21,7 @@ __global__ __launch_bounds__(256) void group_metadata_kernel(const int32_t* __re
     const int wave = threadIdx.x >> 6, lane = lane_id();
     const int w = blockIdx.x * 4 + wave;
     if (w < capacity) {
-        const WorkItem it = find_work_item(group_sizes, G, M, tm_log2, w);
+        const WorkItem it = find_work_item(group_sizes, G, M, tm, w);
         if (lane == 0) {
             work[4 * w + 0] = it.g;
             work[4 * w + 1] = it.g < 0 ? 0 : it.tile;
@@ -36,14 +36,13 @@ __global__ __launch_bounds__(256) void group_metadata_kernel(const int32_t* __re
             const int s = g < G ? group_sizes[g] : 0;
             const int incl = wave_incl_scan(s);
             const int o = carry_rows + incl - s;
-            const int c = s > 0 ? ((o + s - 1) >> tm_log2) - (o >> tm_log2) + 1 : 0;
+            const int c = s > 0 ? (o + s - 1) / tm - o / tm + 1 : 0;
             if (g < G) offsets[g] = o;
             carry_rows += __shfl(incl, 63, 64);
             carry_items += __shfl(wave_incl_scan(c), 63, 64);
         }
         if (lane == 0) {
             const int total = carry_rows;
-            const int tm = 1 << tm_log2;
             const int tail = total < M ? (M + tm - 1) / tm - total / tm : 0;
             offsets[G] = total;
             num_work[0] = carry_items + tail;
@@ -51,12 +50,12 @@ __global__ __launch_bounds__(256) void group_metadata_kernel(const int32_t* __re
     }
 }
 
-hipError_t launch_group_metadata(const int32_t* group_sizes, int G, int M, int tm_log2,
+hipError_t launch_group_metadata(const int32_t* group_sizes, int G, int M, int tm,
                                  int32_t* offsets, int32_t* work, int capacity,
                                  int32_t* num_work, hipStream_t stream) {
     const int blocks = (capacity + 3) / 4;
     hipLaunchKernelGGL(group_metadata_kernel, dim3(blocks), dim3(256), 0, stream, group_sizes, G,
-                       M, tm_log2, offsets, work, capacity, num_work);
+                       M, tm, offsets, work, capacity, num_work);
     return hipGetLastError();
 }
 

@@ -99,7 +99,8 @@ def test_bf16_rejections(lib):
 
 def test_metadata_rejections(lib):
     m = lib.gmm_group_metadata
-    assert m(P(A), 4, 100, 100, P(A), P(A), 100, P(A), None) == SHAPE   # tile not a power of two
+    assert m(P(A), 4, 100, 100, P(A), P(A), 100, P(A), None) == SHAPE   # tile not a multiple of 16
+    assert m(P(A), 4, 100, 2048, P(A), P(A), 100, P(A), None) == SHAPE  # tile above 1024
     assert m(P(A), 4, 1000, 128, P(A), P(A), 5, P(A), None) == SHAPE    # capacity too small
     assert m(P(A), 4, 1000, 128, P(A), None, 20, P(A), None) == NULL
 

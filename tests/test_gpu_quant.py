@@ -21,6 +21,8 @@ DEV = "cuda:0"
     ([127, 1, 128, 0, 129], 400, 128),
     ([0, 0, 0], 5, 16),
     ([3, 5, 0, 7], 15, 16),
+    ([47, 1, 48, 0, 97], 400, 48),
+    ([0, 200, 0, 13], 300, 80),
 ])
 def test_metadata_matches_oracle(gs, M, tm):
     gs = np.array(gs, np.int32)
@@ -41,8 +43,9 @@ def test_metadata_random_and_large_G():
         tail = int(r.integers(0, min(M, 300)))
         cuts = np.sort(r.integers(0, M - tail + 1, size=G - 1))
         gs = np.diff(np.concatenate([[0], cuts, [M - tail]])).astype(np.int32)
-        cases.append((gs, M, int(r.choice([16, 64, 128, 256]))))
+        cases.append((gs, M, int(r.choice([16, 48, 64, 128, 256, 1008]))))
     cases.append((workloads.make("full", with_dy=False).group_sizes, 65536, 128))
+    cases.append((workloads.make("full", with_dy=False).group_sizes, 65536, 48))
     for gs, M, tm in cases:
         off, work, num = gmm.gmm_group_metadata(torch.from_numpy(gs).to(DEV), M, tm)
         ref = oracle.work_list(gs, M, tm)
