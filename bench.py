@@ -221,7 +221,7 @@ def main() -> int:
                      "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                      "traffic": None if traffic is None else int(traffic),
                      "algorithmic_bytes": alg_bytes,
-                     "kernel": "fp8_fwd_kernel<bf16 lhs, bf16 out, 64x512 tile>",
+                     "kernel": "fp8_fwd_kernel<bf16 lhs, bf16 out> (48x512 tiles at this shape)",
                      "kernel_avg_us": round(ms * 1e3, 3),
                      "mfma_tflops": round(tflops, 2), "mfma_peak": PEAK_FP8_TFLOPS,
                      "mfma_frac": round(tflops / PEAK_FP8_TFLOPS, 4)},
