@@ -253,6 +253,24 @@ def main() -> int:
         ops["dx_bf16"] = {"us": round(d_us, 3), "tflops": round(flops / (d_us * 1e-6) / 1e12, 2),
                           "frac_bf16_peak": round(flops / (d_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4)}
         ops["fp8_over_bf16_fwd"] = round(b_us / (ms * 1e3), 3)
+        # fused gate+up wi layer (weights [G,K,2x512], silu(gate)*up epilogue),
+        # with and without the 1x128 re-quantisation of the activation, and
+        # the plain forward over the same 1024 columns for comparison
+        gu = workloads.make("wi_gate_up", seed=0, with_dy=False)
+        guq, gus = gmm.gmm_quantize_rhs(gu.w.to(dev))
+        del gu
+        act = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        aq = torch.empty((M, N), dtype=torch.uint8, device=dev)
+        asc = torch.empty((M, N // 128), dtype=torch.float32, device=dev)
+        wide = torch.empty((M, 2 * N), dtype=torch.bfloat16, device=dev)
+        gflops = 2.0 * total * K * 2 * N
+        for name, fn in [
+                ("fp8_fwd_swiglu_gate_up", lambda: gmm.gmm_fp8_fwd_swiglu(x, guq, gus, gs, out=act)),
+                ("fp8_fwd_swiglu_gate_up_requant",
+                 lambda: gmm.gmm_fp8_fwd_swiglu(x, guq, gus, gs, out=act, act_q=aq, act_scale=asc)),
+                ("fp8_fwd_gate_up_plain", lambda: gmm.gmm_fp8_fwd(x, guq, gus, gs, out=wide))]:
+            f_us = graph_time_ms(fn, 100, 10) * 1e3
+            ops[name] = {"us": round(f_us, 3), "tflops": round(gflops / (f_us * 1e-6) / 1e12, 2)}
         result["ops"] = ops
 
     if not args.no_cpu_baseline:

@@ -143,6 +143,32 @@ GMM_API int gmm_fp8_fwd(const void *lhs, int lhs_dtype, const float *lhs_scale,
                 float *scale_out, void *stream);
 
 /*
+ * gmm_fp8_fwd_swiglu -- blockwise-FP8 grouped matmul with the gate and up
+ *   projections fused into one call and the activation applied in the
+ *   kernel ("实现差距：GMM Kernel（V1 vs V2）", sections 3.5 and 4.2: the RHS
+ *   concatenates the gate weights (first N columns) and the up weights (next
+ *   N columns); the kernel returns silu(gate) * up).
+ *   With P = the gmm_fp8_fwd product against the 2N-column RHS:
+ *     out[m,j] = silu(P[m,j]) * P[m,N+j],  silu(z) = z / (1 + exp(-z)),
+ *   computed in fp32; rows past the total are 0.
+ * lhs, lhs_dtype, lhs_scale: as for gmm_fp8_fwd.
+ * rhs, rhs_scale: gmm_quantize_rhs output for the [G,K,2N] fused weights.
+ * out:       [M,N], GMM_BF16 or GMM_F32.
+ * act_q, act_scale: NULL, or [M,N] E4M3 codes and [M,N/128] fp32 scales that
+ *            receive the 1x128 quantisation of the fp32 activation (the
+ *            gmm_quantize_lhs recipe), ready to be the next layer's LHS.
+ *            Rows past the total get code 0 and scale 0.
+ * K must be a multiple of 128 and N of 256; 1 <= G <= GMM_MAX_GROUPS.
+ * Errors: as for gmm_fp8_fwd; act_q and act_scale must both be set or both
+ * NULL (GMM_ERR_NULL).
+ */
+GMM_API int gmm_fp8_fwd_swiglu(const void *lhs, int lhs_dtype, const float *lhs_scale,
+                               const uint8_t *rhs, const float *rhs_scale,
+                               const int32_t *group_sizes, int64_t M, int64_t K, int64_t N,
+                               int64_t G, void *out, int out_dtype, uint8_t *act_q,
+                               float *act_scale, void *stream);
+
+/*
  * gmm_bf16_fwd -- unquantised grouped matmul (the bf16 baseline).
  *   out[m,:] = lhs[m,:] . rhs[g(m)] with fp32 accumulation; rows past the
  *   total are 0.  ("GEMM Kernel 性能优化十问", Q10: the BF16 kernel is the

@@ -18,7 +18,8 @@ LIB_PATH = os.path.join(_HERE, "libgmm.so")
 GMM_F32, GMM_BF16, GMM_E4M3 = 0, 1, 2
 GMM_MAX_GROUPS = 4096
 EXPORTS = ("gmm_status_string", "gmm_last_error", "gmm_group_metadata", "gmm_quantize_lhs",
-           "gmm_quantize_rhs", "gmm_fp8_fwd", "gmm_bf16_fwd", "tgmm_bf16", "gmm_bf16_dx")
+           "gmm_quantize_rhs", "gmm_fp8_fwd", "gmm_fp8_fwd_swiglu", "gmm_bf16_fwd", "tgmm_bf16",
+           "gmm_bf16_dx")
 
 _lib = None
 
@@ -46,6 +47,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gmm_quantize_lhs.argtypes = [P, I, I64, I64, P, P, P]
     lib.gmm_quantize_rhs.argtypes = [P, I, I64, I64, I64, P, P, P]
     lib.gmm_fp8_fwd.argtypes = [P, I, P, P, P, P, I64, I64, I64, I64, P, I, P, P, P]
+    lib.gmm_fp8_fwd_swiglu.argtypes = [P, I, P, P, P, P, I64, I64, I64, I64, P, I, P, P, P]
     lib.gmm_bf16_fwd.argtypes = [P, P, P, I64, I64, I64, I64, P, I, P]
     lib.tgmm_bf16.argtypes = [P, P, P, I64, I64, I64, I64, P, I, P]
     lib.gmm_bf16_dx.argtypes = [P, P, P, I64, I64, I64, I64, P, I, P]
@@ -138,6 +140,29 @@ def gmm_fp8_fwd(lhs: torch.Tensor, rhs_q: torch.Tensor, rhs_scale: torch.Tensor,
     _check(lib.gmm_fp8_fwd(_ptr(lhs), _dt(lhs), _ptr(lhs_scale), _ptr(rhs_q), _ptr(rhs_scale),
                            _ptr(group_sizes), M, K, N, G, _ptr(out), _dt(out), _ptr(q_out),
                            _ptr(scale_out), _stream(lhs)))
+    return out
+
+
+def gmm_fp8_fwd_swiglu(lhs: torch.Tensor, rhs_q: torch.Tensor, rhs_scale: torch.Tensor,
+                       group_sizes: torch.Tensor, lhs_scale: Optional[torch.Tensor] = None,
+                       out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None,
+                       act_q: Optional[torch.Tensor] = None, act_scale: Optional[torch.Tensor] = None
+                       ) -> torch.Tensor:
+    """Fused gate+up blockwise-FP8 GMM: rhs_q/rhs_scale quantise the [G,K,2N]
+    concatenation (gate columns first); returns silu(gate) * up, [M,N].
+    act_q [M,N] uint8 / act_scale [M,N/128] f32 optionally receive its 1x128
+    quantisation."""
+    lib = load_library()
+    M, K = lhs.shape
+    G, N16, KB, slab = rhs_q.shape
+    if slab != 2048 or KB * 128 != K or N16 % 2:
+        raise ValueError("rhs_q shape %s does not match K=%d" % (tuple(rhs_q.shape), K))
+    N = N16 * 16 // 2
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=lhs.device)
+    _check(lib.gmm_fp8_fwd_swiglu(_ptr(lhs), _dt(lhs), _ptr(lhs_scale), _ptr(rhs_q),
+                                  _ptr(rhs_scale), _ptr(group_sizes), M, K, N, G, _ptr(out),
+                                  _dt(out), _ptr(act_q), _ptr(act_scale), _stream(lhs)))
     return out
 
 

@@ -163,13 +163,46 @@ int gmm_fp8_fwd(const void* lhs, int lhs_dtype, const float* lhs_scale, const ui
         GMM_TRY(check_opt_ptr(q_out, "q_out"));
         GMM_TRY(check_opt_ptr(scale_out, "scale_out"));
     }
-    const int64_t blocks = ((M + 127) / 128 + G + 1) * (N / 128);
+    const int64_t blocks = ((M + 47) / 48 + G + 1) * (N / 128);   // worst case over tile shapes
     if (blocks > kMaxDim) return fail(GMM_ERR_SHAPE, "grid too large");
     if (M == 0) return GMM_OK;
     return hip_status(gmm::launch_fp8_fwd(lhs, kind, lhs_scale, rhs, rhs_scale, group_sizes,
                                           (int)M, (int)K, (int)N, (int)G, out,
                                           out_dtype == GMM_BF16, q_out, scale_out,
                                           (hipStream_t)stream));
+}
+
+int gmm_fp8_fwd_swiglu(const void* lhs, int lhs_dtype, const float* lhs_scale, const uint8_t* rhs,
+                       const float* rhs_scale, const int32_t* group_sizes, int64_t M, int64_t K,
+                       int64_t N, int64_t G, void* out, int out_dtype, uint8_t* act_q,
+                       float* act_scale, void* stream) {
+    int kind;
+    if (lhs_dtype == GMM_E4M3) kind = 0;
+    else if (lhs_dtype == GMM_BF16) kind = 1;
+    else if (lhs_dtype == GMM_F32) kind = 2;
+    else return fail(GMM_ERR_DTYPE, "lhs dtype %d unsupported", lhs_dtype);
+    GMM_TRY(check_out_dtype(out_dtype, "out"));
+    GMM_TRY(check_groups(M, G));
+    GMM_TRY(check_mult(K, 128, "K"));
+    GMM_TRY(check_mult(N, 256, "N"));
+    GMM_TRY(check_ptr(lhs, "lhs"));
+    GMM_TRY(check_ptr(rhs, "rhs"));
+    GMM_TRY(check_ptr(rhs_scale, "rhs_scale"));
+    GMM_TRY(check_ptr(group_sizes, "group_sizes"));
+    GMM_TRY(check_ptr(out, "out"));
+    if (kind == 0) GMM_TRY(check_ptr(lhs_scale, "lhs_scale"));
+    else if (lhs_scale != nullptr) return fail(GMM_ERR_DTYPE, "lhs_scale given with an unquantised lhs");
+    if ((act_q == nullptr) != (act_scale == nullptr))
+        return fail(GMM_ERR_NULL, "act_q and act_scale must both be set or both NULL");
+    GMM_TRY(check_opt_ptr(act_q, "act_q"));
+    GMM_TRY(check_opt_ptr(act_scale, "act_scale"));
+    const int64_t blocks = ((M + 47) / 48 + G + 1) * (N / 256);
+    if (blocks > kMaxDim) return fail(GMM_ERR_SHAPE, "grid too large");
+    if (M == 0) return GMM_OK;
+    return hip_status(gmm::launch_fp8_fwd_swiglu(lhs, kind, lhs_scale, rhs, rhs_scale,
+                                                 group_sizes, (int)M, (int)K, (int)N, (int)G, out,
+                                                 out_dtype == GMM_BF16, act_q, act_scale,
+                                                 (hipStream_t)stream));
 }
 
 int gmm_bf16_fwd(const void* lhs, const void* rhs, const int32_t* group_sizes, int64_t M,

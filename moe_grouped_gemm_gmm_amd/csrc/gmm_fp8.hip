@@ -183,7 +183,17 @@ struct Stage {
 // item and are never read by an MFMA, so the quantiser and the LDS layout stay
 // the same while each workgroup does three quarters of the MFMA work and more
 // workgroups share the chip.
-template <int KIND, bool OUT_BF16, int WN, int TM, bool WRITE_Q>
+//
+// SWIGLU: the fused gate+up projection ("实现差距：GMM Kernel（V1 vs V2）",
+// sections 3.5 and 4.2).  The RHS has 2N columns, the gate projection in the
+// first N and the up projection in the next N; the output is
+// silu(gate) * up, N columns.  A workgroup covers 256 output columns: wave w
+// owns gate columns n0 + 32w .. +31 (its B blocks 0, 1) and the matching up
+// columns N + n0 + 32w .. +31 (blocks 2, 3), so the activation is formed in
+// registers.  With act_q non-null the activation is also quantised 1x128
+// (same recipe as the LHS) for the next layer: each 128-column block spans
+// four waves, whose row maxima meet in LDS.
+template <int KIND, bool OUT_BF16, int WN, int TM, bool WRITE_Q, bool SWIGLU>
 __global__ __launch_bounds__(kThreads, 2) void fp8_fwd_kernel(
     const void* __restrict__ lhs, const float* __restrict__ lhs_scale,
     const uint8_t* __restrict__ rhs, const float* __restrict__ rhs_scale,
@@ -192,12 +202,14 @@ __global__ __launch_bounds__(kThreads, 2) void fp8_fwd_kernel(
     static_assert(TM == 64 || TM == 48, "64- or 48-row tiles");
     constexpr int MB = TM / 16;   // 16-row blocks of the tile
     constexpr int NB = WN / 16;   // 16-column blocks per wave
-    constexpr int TN = kWaves * WN;
+    static_assert(!SWIGLU || (WN == 64 && !WRITE_Q), "fused gate+up uses 64-column waves");
+    constexpr int TN = SWIGLU ? kWaves * WN / 2 : kWaves * WN;   // output columns per tile
     constexpr int NBLK = Smem<WN>::NBLK;
     constexpr int OUT_BYTES = OUT_BF16 ? 2 : 4;
 
     __shared__ WorkItem s_item;
     __shared__ __attribute__((aligned(16))) SmemAll<WN> smu;
+    __shared__ float s_rmax[SWIGLU ? kWaves : 1][SWIGLU ? kTM : 1];   // activation row maxima
     Smem<WN>& sm = smu.m;
 
     const int tid = threadIdx.x, lane = lane_id();
@@ -221,11 +233,22 @@ __global__ __launch_bounds__(kThreads, 2) void fp8_fwd_kernel(
             *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(out) + ((int64_t)r * N + c) * OUT_BYTES) =
                 make_uint4(0, 0, 0, 0);
         }
+        if (SWIGLU && q_out != nullptr) {   // their activation codes and scales too
+            for (int e = tid; e < rows * (TN / 16); e += kThreads) {
+                const int r = it.lo + e / (TN / 16), c = n0 + (e % (TN / 16)) * 16;
+                *reinterpret_cast<uint4*>(q_out + (int64_t)r * N + c) = make_uint4(0, 0, 0, 0);
+            }
+            for (int e = tid; e < rows * (TN / kQBlock); e += kThreads) {
+                const int r = it.lo + e / (TN / kQBlock), b = n0 / kQBlock + e % (TN / kQBlock);
+                s_out[(int64_t)r * (N / kQBlock) + b] = 0.0f;
+            }
+        }
         return;
     }
 
     const int g = it.g, row0 = it.tile * TM;
-    const int nkb = K / kTK, nnb = N / kQBlock;
+    const int NR = SWIGLU ? 2 * N : N;            // RHS columns
+    const int nkb = K / kTK, nnb = NR / kQBlock;
 
     // ---- quantiser role: row 8*wave + lane/8, chunk c = lane % 8
     const int qchunk = lane % kLPR;
@@ -236,15 +259,24 @@ __global__ __launch_bounds__(kThreads, 2) void fp8_fwd_kernel(
     const bool write_q = WRITE_Q && nt == 0 && qvalid;
     // RHS scale this lane folds into its row factor: 128-column block qchunk
     // of the tile (clamped; lanes past NBLK write an unused slot)
-    const float* srl = rhs_scale + (int64_t)g * nkb * nnb + n0 / kQBlock + min(qchunk, NBLK - 1);
+    // (fused gate+up: slots 0, 1 are the tile's gate blocks, 2, 3 its up blocks)
+    const int qslot = min(qchunk, NBLK - 1);
+    const int qblk = !SWIGLU ? n0 / kQBlock + qslot
+                             : (qslot < 2 ? n0 / kQBlock + qslot : (N + n0) / kQBlock + qslot - 2);
+    const float* srl = rhs_scale + (int64_t)g * nkb * nnb + qblk;
 
     // ---- MFMA role: columns [n0 + wave*WN, +WN); lane = row/col lr, K chunk lc.
     //      B is the packed RHS: 2 KB per (16-column block, subchannel), this
     //      lane's 32 codes at byte lane*16 of each 1 KB half.
     const int lr = lane & 15, lc = lane >> 4;
-    const int ncol0 = n0 + wave * WN;
-    const int my_nblk = (wave * WN) / 128;
-    const uint8_t* bptr = rhs + ((int64_t)g * (N / 16) + ncol0 / 16) * nkb * 2048 + lane * 16;
+    const int ncol0 = SWIGLU ? n0 + 32 * wave : n0 + wave * WN;    // first output column
+    // factor slots of the wave's column blocks (j < NB/2 and j >= NB/2 for
+    // the fused projection)
+    const int slot_lo = SWIGLU ? wave / 4 : (wave * WN) / 128;
+    const int slot_hi = SWIGLU ? 2 + wave / 4 : slot_lo;
+    const uint8_t* bptr = rhs + ((int64_t)g * (NR / 16) + ncol0 / 16) * nkb * 2048 + lane * 16;
+    // B block j >= NB/2 of the fused projection: the up columns, N further on
+    const int64_t bup = SWIGLU ? (int64_t)(N / 16) * nkb * 2048 - (int64_t)(NB / 2) * nkb * 2048 : 0;
 
     v4f acc[MB][NB];
 #pragma unroll
@@ -274,7 +306,7 @@ __global__ __launch_bounds__(kThreads, 2) void fp8_fwd_kernel(
     auto load_b = [&](v8i (&b)[NB], int kb) {
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
-            const uint8_t* p = bptr + ((int64_t)j * nkb + kb) * 2048;
+            const uint8_t* p = bptr + ((int64_t)j * nkb + kb) * 2048 + (j >= NB / 2 ? bup : 0);
             const uint4 lo = *reinterpret_cast<const uint4*>(p);
             const uint4 hi = *reinterpret_cast<const uint4*>(p + 1024);
             b[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
@@ -302,13 +334,18 @@ __global__ __launch_bounds__(kThreads, 2) void fp8_fwd_kernel(
         // variant, which reads one row block at a time to stay within the
         // register budget.
         constexpr bool kAllA = !WRITE_Q;
+        constexpr int NF = SWIGLU ? 2 : 1;      // row factors per row block (gate, up)
         v8i af[kAllA ? MB : 1];
-        float cf[kAllA ? MB : 1];
+        float cf[kAllA ? MB : 1][NF];
+        auto read_cf = [&](float (&c)[NF], int i) {
+            c[0] = sm.c[buf][slot_lo][16 * i + lr];
+            if constexpr (SWIGLU) c[1] = sm.c[buf][slot_hi][16 * i + lr];
+        };
         if constexpr (kAllA) {
 #pragma unroll
             for (int i = 0; i < MB; ++i) {
                 af[i] = *reinterpret_cast<const v8i*>(&sm.a[buf][16 * i + lr][lc * 32]);
-                cf[i] = sm.c[buf][my_nblk][16 * i + lr];
+                read_cf(cf[i], i);
             }
         }
         quant_store(kb1, buf ^ 1, sq);
@@ -317,14 +354,15 @@ __global__ __launch_bounds__(kThreads, 2) void fp8_fwd_kernel(
             const int ia = kAllA ? i : 0;
             if constexpr (!kAllA) {
                 af[0] = *reinterpret_cast<const v8i*>(&sm.a[buf][16 * i + lr][lc * 32]);
-                cf[0] = sm.c[buf][my_nblk][16 * i + lr];
+                read_cf(cf[0], i);
             }
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
                 const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                     bc[j], af[ia], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+                const float f = cf[ia][SWIGLU && j >= NB / 2 ? 1 : 0];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(p[r], cf[ia], acc[i][j][r]);
+                for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(p[r], f, acc[i][j][r]);
             }
         }
         load_stage(sq, kb3);
@@ -363,6 +401,84 @@ __global__ __launch_bounds__(kThreads, 2) void fp8_fwd_kernel(
         step(kb + 1, bB, bA, st0);
     }
     if (kb < nkb) step(kb, bA, bB, st1);
+
+    if constexpr (SWIGLU) {
+        // ---- fused gate+up epilogue: h = silu(gate) * up, silu(z) = z / (1 + e^-z)
+        //      (hardware exp and reciprocal: a few ulp, far inside the tolerance)
+        float h[MB][2][4];
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float gt = acc[i][jj][r], up = acc[i][jj + 2][r];
+                    h[i][jj][r] = gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up;
+                }
+        if constexpr (OUT_BF16) {
+            // through this wave's LDS block: 64-byte row segments, 4 lanes per row
+            uint8_t (*ep)[SmemAll<WN>::kEpiRow] = smu.epi[wave];
+#pragma unroll
+            for (int i = 0; i < MB; ++i)
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj)
+                    *reinterpret_cast<uint2*>(&ep[16 * i + lr][(16 * jj + 4 * lc) * 2]) =
+                        make_uint2(pack_bf16x2(h[i][jj][0], h[i][jj][1]), pack_bf16x2(h[i][jj][2], h[i][jj][3]));
+            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+            const int orow = lane >> 2, ocol = (lane & 3) * 16;
+#pragma unroll
+            for (int q = 0; q < (TM + 15) / 16; ++q) {
+                const int r = 16 * q + orow;
+                const uint4 v = *reinterpret_cast<const uint4*>(&ep[r][ocol]);
+                const int grow = row0 + r;
+                if (grow >= it.lo && grow < it.hi)
+                    *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(out) + ((int64_t)grow * N + ncol0) * 2 + ocol) = v;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < MB; ++i) {
+                const int grow = row0 + 16 * i + lr;
+                if (grow < it.lo || grow >= it.hi) continue;
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj)
+                    *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + (int64_t)grow * N + ncol0 + 16 * jj + 4 * lc) =
+                        make_float4(h[i][jj][0], h[i][jj][1], h[i][jj][2], h[i][jj][3]);
+            }
+        }
+        if (q_out != nullptr) {
+            // 1x128 quantisation of the fp32 activation for the next layer:
+            // the block's row abs-max over the lane's 8 values, the row's 4
+            // lanes and the 4 waves of the block (LDS), then the LHS recipe.
+#pragma unroll
+            for (int i = 0; i < MB; ++i) {
+                float m = 0.0f;
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) m = fmaxf(m, fabsf(h[i][jj][r]));
+                m = fmaxf(m, __shfl_xor(m, 16, 64));
+                m = fmaxf(m, __shfl_xor(m, 32, 64));
+                if (lc == 0) s_rmax[wave][16 * i + lr] = m;
+            }
+            __syncthreads();
+            const int w0 = (wave / 4) * 4;
+#pragma unroll
+            for (int i = 0; i < MB; ++i) {
+                const float a = fmaxf(fmaxf(s_rmax[w0][16 * i + lr], s_rmax[w0 + 1][16 * i + lr]),
+                                      fmaxf(s_rmax[w0 + 2][16 * i + lr], s_rmax[w0 + 3][16 * i + lr]));
+                const float sa = quant_scale(a);
+                const float inv = quant_inv(sa);
+                const int grow = row0 + 16 * i + lr;
+                if (grow < it.lo || grow >= it.hi) continue;
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj)
+                    *reinterpret_cast<uint32_t*>(q_out + (int64_t)grow * N + ncol0 + 16 * jj + 4 * lc) =
+                        e4m3x4(h[i][jj][0] * inv, h[i][jj][1] * inv, h[i][jj][2] * inv, h[i][jj][3] * inv);
+                if (wave == w0 && lc == 0) s_out[(int64_t)grow * (N / kQBlock) + n0 / kQBlock + wave / 4] = sa;
+            }
+        }
+        return;
+    }
 
     // ---- epilogue.  bf16: each wave writes its 64 x WN block to its own LDS
     //      region (the loop's last barrier has retired every read of the A
@@ -406,20 +522,20 @@ __global__ __launch_bounds__(kThreads, 2) void fp8_fwd_kernel(
     }
 }
 
-template <int KIND, int WN, int TM, bool WRITE_Q>
+template <int KIND, int WN, int TM, bool WRITE_Q, bool SWIGLU = false>
 hipError_t launch_cfg(const void* lhs, const float* lhs_scale, const uint8_t* rhs,
                       const float* rhs_scale, const int32_t* group_sizes, int M, int K, int N,
                       int G, void* out, bool out_bf16, uint8_t* q_out, float* scale_out,
                       hipStream_t stream) {
-    const int ntiles_n = N / (kWaves * WN);
+    const int ntiles_n = N / (SWIGLU ? kWaves * WN / 2 : kWaves * WN);
     const int64_t items = max_work_items(M, G, TM);
     const int nblocks = (int)(items * ntiles_n);
     if (out_bf16)
-        hipLaunchKernelGGL((fp8_fwd_kernel<KIND, true, WN, TM, WRITE_Q>), dim3(nblocks), dim3(kThreads),
+        hipLaunchKernelGGL((fp8_fwd_kernel<KIND, true, WN, TM, WRITE_Q, SWIGLU>), dim3(nblocks), dim3(kThreads),
                            0, stream, lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N, G, out,
                            q_out, scale_out, ntiles_n, nblocks);
     else
-        hipLaunchKernelGGL((fp8_fwd_kernel<KIND, false, WN, TM, WRITE_Q>), dim3(nblocks), dim3(kThreads),
+        hipLaunchKernelGGL((fp8_fwd_kernel<KIND, false, WN, TM, WRITE_Q, SWIGLU>), dim3(nblocks), dim3(kThreads),
                            0, stream, lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N, G, out,
                            q_out, scale_out, ntiles_n, nblocks);
     return hipGetLastError();
@@ -488,7 +604,39 @@ hipError_t launch_kind(const void* lhs, const float* lhs_scale, const uint8_t* r
                                    out_bf16, q_out, scale_out, stream);
 }
 
+// Fused gate+up: 256 output columns per workgroup; 48-row tiles under the
+// same rule as the plain forward.
+template <int KIND>
+hipError_t launch_swiglu_kind(const void* lhs, const float* lhs_scale, const uint8_t* rhs,
+                              const float* rhs_scale, const int32_t* group_sizes, int M, int K,
+                              int N, int G, void* out, bool out_bf16, uint8_t* act_q,
+                              float* act_scale, hipStream_t stream) {
+    if (max_work_items(M, G, 48) * (N / 256) <= device_cus())
+        return launch_cfg<KIND, 64, 48, false, true>(lhs, lhs_scale, rhs, rhs_scale, group_sizes, M,
+                                                     K, N, G, out, out_bf16, act_q, act_scale, stream);
+    return launch_cfg<KIND, 64, 64, false, true>(lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K,
+                                                 N, G, out, out_bf16, act_q, act_scale, stream);
+}
+
 }  // namespace
+
+hipError_t launch_fp8_fwd_swiglu(const void* lhs, int lhs_kind, const float* lhs_scale,
+                                 const uint8_t* rhs, const float* rhs_scale,
+                                 const int32_t* group_sizes, int M, int K, int N, int G,
+                                 void* out, bool out_bf16, uint8_t* act_q, float* act_scale,
+                                 hipStream_t stream) {
+    switch (lhs_kind) {
+        case kLhsE4M3:
+            return launch_swiglu_kind<kLhsE4M3>(lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N,
+                                                G, out, out_bf16, act_q, act_scale, stream);
+        case kLhsBF16:
+            return launch_swiglu_kind<kLhsBF16>(lhs, nullptr, rhs, rhs_scale, group_sizes, M, K, N,
+                                                G, out, out_bf16, act_q, act_scale, stream);
+        default:
+            return launch_swiglu_kind<kLhsF32>(lhs, nullptr, rhs, rhs_scale, group_sizes, M, K, N,
+                                               G, out, out_bf16, act_q, act_scale, stream);
+    }
+}
 
 hipError_t launch_fp8_fwd(const void* lhs, int lhs_kind, const float* lhs_scale,
                           const uint8_t* rhs, const float* rhs_scale,

@@ -24,6 +24,14 @@ hipError_t launch_fp8_fwd(const void* lhs, int lhs_kind, const float* lhs_scale,
                           const int32_t* group_sizes, int M, int K, int N, int G, void* out,
                           bool out_bf16, uint8_t* q_out, float* scale_out, hipStream_t stream);
 
+// Fused gate+up: rhs has 2N columns (gate, then up); out = silu(gate) * up,
+// [M,N]; act_q/act_scale (both or neither) the 1x128 quantised activation.
+hipError_t launch_fp8_fwd_swiglu(const void* lhs, int lhs_kind, const float* lhs_scale,
+                                 const uint8_t* rhs, const float* rhs_scale,
+                                 const int32_t* group_sizes, int M, int K, int N, int G,
+                                 void* out, bool out_bf16, uint8_t* act_q, float* act_scale,
+                                 hipStream_t stream);
+
 hipError_t launch_bf16_fwd(const void* lhs, const void* rhs, const int32_t* group_sizes, int M,
                            int K, int N, int G, void* out, bool out_bf16, hipStream_t stream);
 

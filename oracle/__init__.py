@@ -46,6 +46,7 @@ def _load():
     lib.oracle_gmm_f64.argtypes = [P, P, P, I, I, I, I, P]
     lib.oracle_tgmm_f64.argtypes = [P, P, P, I, I, I, I, P]
     lib.oracle_dx_f64.argtypes = [P, P, P, I, I, I, I, P]
+    lib.oracle_swiglu.argtypes = [P, I, I, P]
     lib.oracle_num_threads.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -139,6 +140,23 @@ def gmm_fp8(ql, sl, qr, sr, group_sizes):
     out = np.empty((M, N), dtype=np.float64)
     lib.oracle_gmm_fp8(pql, psl, pqr, psr, pg, M, K, N, G, out.ctypes.data_as(ctypes.c_void_p))
     return out
+
+
+def swiglu(gu):
+    """fp64 silu(gate) * up of a [M,2N] array whose first N columns are the
+    gate projection and the next N the up projection -> [M,N]."""
+    lib = _load()
+    gu, pg = _c(gu, np.float64)
+    M, N2 = gu.shape
+    assert N2 % 2 == 0
+    out = np.empty((M, N2 // 2), dtype=np.float64)
+    lib.oracle_swiglu(pg, M, N2 // 2, out.ctypes.data_as(ctypes.c_void_p))
+    return out
+
+
+def gmm_fp8_swiglu(ql, sl, qr, sr, group_sizes):
+    """Fused gate+up FP8 GMM: qr/sr quantise the [G,K,2N] concatenation."""
+    return swiglu(gmm_fp8(ql, sl, qr, sr, group_sizes))
 
 
 def gmm(x, w, group_sizes):

@@ -26,6 +26,9 @@
  *  [V1s] same page, section 2.1: subchannel loop, one dot per quant block,
  *        scaled, then added to the accumulator.
  *  [V2z] same page, section 3.6: output rows past the last group are zero.
+ *  [V2a] same page, sections 3.5 and 4.2: the gate and up projections are
+ *        one GMM against weights concatenated along N (gate columns first,
+ *        then up), and the kernel returns silu(gate) * up.
  *  [GG]  "MoE 优化的探索：从 MiniMax-01、Comet、FlashMoE 到 DeepSeek-V4",
  *        section 3.7.2: a grouped GEMM is one independent GEMM per expert,
  *        X_e W_e, over that expert's contiguous rows.
@@ -332,6 +335,20 @@ void oracle_gmm_fp8(const uint8_t *ql, const float *sl, const uint8_t *qr,
         free(lrow);
     }
     free(gid);
+}
+
+/* ---------------------------------------------- gate+up activation -- */
+
+/* out[m,j] = silu(gu[m,j]) * gu[m,N+j], silu(z) = z / (1 + exp(-z)), in fp64
+ * ([V2a]).  gu: [M,2N] (gate columns, then up columns), out: [M,N]. */
+void oracle_swiglu(const double *gu, int64_t M, int64_t N, double *out)
+{
+    int64_t m, j;
+    for (m = 0; m < M; ++m)
+        for (j = 0; j < N; ++j) {
+            double gate = gu[m * 2 * N + j], up = gu[m * 2 * N + N + j];
+            out[m * N + j] = gate / (1.0 + exp(-gate)) * up;
+        }
 }
 
 /* ------------------------------------------------- unquantised (bf16) -- */

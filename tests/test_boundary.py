@@ -30,7 +30,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_symbols()
-    assert len(names) == 9
+    assert len(names) == 10
     assert sorted(names) == sorted(gmm.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
@@ -67,6 +67,28 @@ def fp8(lib, lhs=A, lhs_dt=1, lhs_scale=0, rhs=A, rhs_scale=A, gs=A, M=256, K=25
 ])
 def test_fp8_fwd_rejections(lib, kw, status):
     assert fp8(lib, **kw) == status
+    if status:
+        assert lib.gmm_last_error()
+
+
+def swiglu(lib, lhs=A, lhs_dt=1, lhs_scale=0, rhs=A, rhs_scale=A, gs=A, M=256, K=256, N=256, G=4,
+           out=A, out_dt=1, q=0, s=0):
+    return lib.gmm_fp8_fwd_swiglu(P(lhs), lhs_dt, P(lhs_scale), P(rhs), P(rhs_scale), P(gs), M, K,
+                                  N, G, P(out), out_dt, P(q), P(s), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(lhs=0), NULL), (dict(rhs=0), NULL), (dict(out=0), NULL),
+    (dict(out=MIS), ALIGN), (dict(q=MIS, s=A), ALIGN),
+    (dict(q=A), NULL), (dict(s=A), NULL),           # act_q and act_scale together
+    (dict(N=128), SHAPE),                           # 256 output columns per tile
+    (dict(K=200), SHAPE), (dict(G=0), SHAPE),
+    (dict(lhs_dt=2), NULL),                         # E4M3 lhs needs lhs_scale
+    (dict(lhs_scale=A), DTYPE), (dict(out_dt=2), DTYPE),
+    (dict(M=0), OK),
+])
+def test_fp8_fwd_swiglu_rejections(lib, kw, status):
+    assert swiglu(lib, **kw) == status
     if status:
         assert lib.gmm_last_error()
 

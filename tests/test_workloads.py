@@ -79,3 +79,13 @@ def test_tolerances_follow_the_pages():
     assert helpers.FP8_ATOL == g["fp8_vs_ref_atol"] and helpers.FP8_RTOL == g["fp8_vs_ref_rtol"]
     assert helpers.FP8_MIN_SQNR_DB >= g["sqnr_good_db"]
     assert (g["lhs_block_rows"], g["lhs_block_cols"], g["rhs_block_rows"], g["rhs_block_cols"]) == (1, 128, 128, 128)
+
+
+def test_wi_gate_up_gate_half_is_the_wi_layer():
+    a = workloads.make("wi", seed=0, with_dy=False)
+    b = workloads.make("wi_gate_up", seed=0, with_dy=False)
+    assert np.array_equal(a.group_sizes, b.group_sizes)
+    assert torch.equal(a.x, b.x)
+    assert b.w.shape == (32, 2048, 1024)
+    assert torch.equal(b.w[:, :, :512], a.w)
+    assert not torch.equal(b.w[:, :, 512:], a.w)

@@ -16,7 +16,7 @@ from typing import Optional
 import numpy as np
 import torch
 
-STREAM_ROUTING, STREAM_LHS, STREAM_RHS, STREAM_DY = 0, 1, 2, 3
+STREAM_ROUTING, STREAM_LHS, STREAM_RHS, STREAM_DY, STREAM_UP = 0, 1, 2, 3, 4
 
 
 def rng(seed: int, stream: int) -> np.random.Generator:
@@ -106,6 +106,9 @@ CONFIGS = {
     "bwd": dict(M=8192, G=32, K=2048, N=512),
     # full production wi layer on one GPU: Zipf(1.1) top-8 of 8192 tokens
     "full": dict(M=65536, G=256, K=2048, N=512),
+    # wi layer with the gate and up projections fused: weights [G,K,2x512],
+    # gate columns first (the wi layer's own weights), then the up columns
+    "wi_gate_up": dict(M=8192, G=32, K=2048, N=1024),
 }
 
 
@@ -122,7 +125,7 @@ def make(name: str, seed: int = 0, with_dy: Optional[bool] = None) -> Workload:
         if with_dy:
             wl.dy = to_bf16(rng(seed, STREAM_DY).standard_normal((M, N), dtype=np.float32))
         return wl
-    if name in ("wi", "bwd"):
+    if name in ("wi", "bwd", "wi_gate_up"):
         gs = topk_routing_counts(M // 8, G, 8, seed)
     elif name == "wo":
         gs = skew_counts(topk_routing_counts(M // 8, G, 8, seed), M, 2, 0.3, seed)
@@ -133,7 +136,12 @@ def make(name: str, seed: int = 0, with_dy: Optional[bool] = None) -> Workload:
     assert int(gs.sum()) == M
     x = to_bf16(rng(seed, STREAM_LHS).standard_normal((M, K), dtype=np.float32))
     w_std = 1.0 if name == "bwd" else 0.02
-    w = to_bf16(rng(seed, STREAM_RHS).standard_normal((G, K, N), dtype=np.float32) * np.float32(w_std))
+    if name == "wi_gate_up":   # gate = the wi layer's weights; up from its own stream
+        gate = rng(seed, STREAM_RHS).standard_normal((G, K, N // 2), dtype=np.float32)
+        up = rng(seed, STREAM_UP).standard_normal((G, K, N // 2), dtype=np.float32)
+        w = to_bf16(np.concatenate([gate, up], axis=2) * np.float32(w_std))
+    else:
+        w = to_bf16(rng(seed, STREAM_RHS).standard_normal((G, K, N), dtype=np.float32) * np.float32(w_std))
     wl = Workload(name, M, K, N, G, gs, x, w)
     if with_dy is None:
         with_dy = name in ("bwd", "full")
