@@ -50,39 +50,52 @@ __device__ __forceinline__ v8bf read_direct(const uint16_t* tile, int stride, in
     return *reinterpret_cast<const v8bf*>(tile + row * stride + r0);
 }
 
-// One thread's share of a staged slice: 4 x 16 bytes.  Loads are always
-// issued from in-bounds addresses (callers clamp the row) and never consumed
-// before the slice is written to LDS, so a prefetch stays in flight while the
-// MFMAs of the current slice run; rows that must read as zero are masked when
-// written to LDS.
+// One thread's share of a staged slice: 4 x 16-byte chunks, chunk c of
+// thread t being chunk c*256 + t of the slice in a layout chosen so that
+//  - each load instruction reads whole 128-byte lines (8 or 16 lanes per row)
+//  - each 16-lane group of an LDS store hits 16 distinct 16-byte bank groups.
+// Loads are always issued from in-bounds addresses (callers clamp the row)
+// and never consumed before the slice is written to LDS, so a prefetch stays
+// in flight while the MFMAs of the current slice run; rows that must read as
+// zero are masked when written to LDS.
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 struct Frag4 {
     u32x4 d[4];
 };
 
-__device__ __forceinline__ void fetch4(Frag4& f, const uint16_t* p) {
-    const u32x4* q = reinterpret_cast<const u32x4*>(p);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) f.d[c] = q[c];
+// Direct [128 rows][64] slice (8 chunks per row, LDS rows of 144 bytes):
+// instruction c of wave w covers rows R..R+3 and R+8..R+11 with
+// R = 16*((4w+c)/2) + 4*((4w+c)%2); lanes 8q..8q+7 take row
+// R + q/2 + 8*(q%2), chunks 0..7 (a 16-lane group: rows R+p and R+p+8, whose
+// 144-byte pitches put them 8 bank groups apart).
+__device__ __forceinline__ int direct_row(int c) {
+    const int t = threadIdx.x, combo = (t >> 6) * 4 + c, q = (t & 63) >> 3;
+    return 16 * (combo >> 1) + 4 * (combo & 1) + (q >> 1) + 8 * (q & 1);
 }
+__device__ __forceinline__ int direct_chunk() { return threadIdx.x & 7; }
 
-// Direct LDS tile [128 rows][64]: thread t holds row t/2, columns 32*(t%2) .. +31.
+// Transposed-layout [64 rows][128] slice (16 chunks per row, LDS rows of 288
+// bytes): chunk c*256 + t is row (c*256 + t)/16, chunk t%16 (a 16-lane group
+// is one row).
+__device__ __forceinline__ int trans_row(int c) { return (c * 256 + (int)threadIdx.x) >> 4; }
+__device__ __forceinline__ int trans_chunk() { return threadIdx.x & 15; }
+
 __device__ __forceinline__ void put_direct(uint16_t* tile, const Frag4& f) {
-    const int t = threadIdx.x, row = t >> 1, h = t & 1;
 #pragma unroll
     for (int c = 0; c < 4; ++c)
-        *reinterpret_cast<u32x4*>(tile + row * (kR + kPadD) + h * 32 + 8 * c) = f.d[c];
+        *reinterpret_cast<u32x4*>(tile + direct_row(c) * (kR + kPadD) + direct_chunk() * 8) = f.d[c];
 }
 
-// Transposed-layout LDS tile [64 rows][128]: thread t holds row t/4,
-// columns 32*(t%4) .. +31; rows with !valid are written as zeros.
-__device__ __forceinline__ void put_trans(uint16_t* tile, const Frag4& f, bool valid) {
-    const int t = threadIdx.x, row = t >> 2, q = t & 3;
+// Rows r with !valid(r) are written as zeros.
+template <typename Valid>
+__device__ __forceinline__ void put_trans(uint16_t* tile, const Frag4& f, Valid valid) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
-        *reinterpret_cast<u32x4*>(tile + row * (kT + kPadT) + q * 32 + 8 * c) =
-            valid ? f.d[c] : u32x4{0u, 0u, 0u, 0u};
+    for (int c = 0; c < 4; ++c) {
+        const int r = trans_row(c);
+        *reinterpret_cast<u32x4*>(tile + r * (kT + kPadT) + trans_chunk() * 8) =
+            valid(r) ? f.d[c] : u32x4{0u, 0u, 0u, 0u};
+    }
 }
 
 // Offset of group g: sum of group_sizes[0..g), computed by one wave.
@@ -169,28 +182,29 @@ __global__ __launch_bounds__(256, 2) void bf16_gemm_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    // Global -> registers for reduction range [r0, r0 + 64) of both operands.
-    // Direct slices: thread t reads row t/2 (clamped into the item for A; its
-    // values only reach output rows that are never stored), columns
-    // 32*(t%2) .. +31.  Transposed slices: row t/4, columns 32*(t%4) .. +31;
-    // in tgmm rows past the group's end are clamped to its last row here and
-    // zeroed when written to LDS.
+    // Global -> registers for reduction range [r0, r0 + 64) of both operands,
+    // in the chunk layouts above.  Direct A rows are clamped into the item
+    // (their values only reach output rows that are never stored); in tgmm
+    // rows past the group's end are clamped to its last row here and zeroed
+    // when written to LDS.
     const int lda = MODE == kFwd ? K : N;
     const uint16_t* wg = B + (int64_t)(MODE == kTgmm ? 0 : g) * K * N;
-    const int trow = tid >> 2, tq = tid & 3;
-    const int drow = tid >> 1, dh = tid & 1;
-    const int arow = min(max(row0 + drow, lo), hi - 1);
+    const int dch = direct_chunk() * 8, tch = trans_chunk() * 8;
     auto fetch = [&](Frag4& fa, Frag4& fb, int r0) {
-        if constexpr (MODE == kTgmm) {
-            const int m = min(r0 + trow, red_hi - 1);
-            fetch4(fa, A + (int64_t)m * K + row0 + tq * 32);   // x[m][k0..k0+128]
-            fetch4(fb, B + (int64_t)m * N + c0 + tq * 32);     // dy[m][n0..n0+128]
-        } else {
-            fetch4(fa, A + (int64_t)arow * lda + r0 + dh * 32);
-            if constexpr (MODE == kFwd)
-                fetch4(fb, wg + (int64_t)(r0 + trow) * N + c0 + tq * 32);    // w[g][k][n0..n0+128]
-            else
-                fetch4(fb, wg + (int64_t)(c0 + drow) * N + r0 + dh * 32);    // w[g][k0+c][n]
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            if constexpr (MODE == kTgmm) {
+                const int m = min(r0 + trans_row(c), red_hi - 1);
+                fa.d[c] = *reinterpret_cast<const u32x4*>(A + (int64_t)m * K + row0 + tch);   // x[m][k0..]
+                fb.d[c] = *reinterpret_cast<const u32x4*>(B + (int64_t)m * N + c0 + tch);     // dy[m][n0..]
+            } else {
+                const int arow = min(max(row0 + direct_row(c), lo), hi - 1);
+                fa.d[c] = *reinterpret_cast<const u32x4*>(A + (int64_t)arow * lda + r0 + dch);
+                if constexpr (MODE == kFwd)   // w[g][k][n0..n0+128]
+                    fb.d[c] = *reinterpret_cast<const u32x4*>(wg + (int64_t)(r0 + trans_row(c)) * N + c0 + tch);
+                else                          // w[g][k0+c][n]
+                    fb.d[c] = *reinterpret_cast<const u32x4*>(wg + (int64_t)(c0 + direct_row(c)) * N + r0 + dch);
+            }
         }
     };
 
@@ -202,7 +216,7 @@ __global__ __launch_bounds__(256, 2) void bf16_gemm_kernel(
     Frag4 fa, fb;
     if (red_lo < red_hi) fetch(fa, fb, red_lo);
     for (int r0 = red_lo; r0 < red_hi; r0 += kR) {
-        const bool tvalid = MODE != kTgmm || r0 + trow < red_hi;
+        auto tvalid = [&](int r) { return MODE != kTgmm || r0 + r < red_hi; };
         if constexpr (A_TR) put_trans(sA, fa, tvalid); else put_direct(sA, fa);
         if constexpr (B_TR) put_trans(sB, fb, tvalid); else put_direct(sB, fb);
         __syncthreads();

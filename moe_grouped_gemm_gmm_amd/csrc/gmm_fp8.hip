@@ -522,6 +522,235 @@ __global__ __launch_bounds__(kThreads, 2) void fp8_fwd_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// Warp-specialised variant for 512-column tiles.  Waves 0-3 (one per SIMD)
+// are consumers: wave c owns output columns n0 + 128c .. +127 (one 128-column
+// scale block), keeps its B operand in registers (reloading each 16-column
+// block with the next subchannel right after its MFMAs) and only issues
+// MFMAs and scale FMAs.  Waves 4-7 (one per SIMD) are producers: they load
+// the raw LHS two subchannels ahead and quantise the next subchannel into
+// the other LDS buffer.  Every SIMD thus has one wave feeding the matrix core
+// and one feeding the VALU in the same step; one workgroup barrier per step,
+// executed the same number of times by both roles (their loops are
+// separate, so no role waits on the other's loads at a control-flow join).
+// Producer lane (p, l): 16 values of each of rows 16p + l/8 and
+// 16p + 8 + l/8 (runs at 8c and 64 + 8c, c = l % 8) — the same per-row
+// recipe and lane layout as the plain kernel, two rows per lane.
+template <int KIND, bool OUT_BF16, int TM, bool WRITE_Q>
+__global__ __launch_bounds__(kThreads, 2) void fp8_fwd_ws_kernel(   // TM = 48 (64 spills)
+    const void* __restrict__ lhs, const float* __restrict__ lhs_scale,
+    const uint8_t* __restrict__ rhs, const float* __restrict__ rhs_scale,
+    const int32_t* __restrict__ group_sizes, int M, int K, int N, int G, void* __restrict__ out,
+    uint8_t* __restrict__ q_out, float* __restrict__ s_out, int ntiles_n, int nblocks) {
+    static_assert(TM == 64 || TM == 48, "64- or 48-row tiles");
+    constexpr int MB = TM / 16;
+    constexpr int NBC = 8;                 // 16-column blocks per consumer wave
+    constexpr int TN = 512;
+    constexpr int OUT_BYTES = OUT_BF16 ? 2 : 4;
+    constexpr int kEpiRow = 128 * OUT_BYTES + 16;   // staged output row (bytes)
+
+    struct Tiles {
+        uint8_t a[2][kTM][kLdsRow];
+        float c[2][kLPR][kTM];
+    };
+    union SmemWs {
+        Tiles t;
+        uint8_t epi[4][TM][kEpiRow];
+    };
+    __shared__ WorkItem s_item;
+    __shared__ __attribute__((aligned(16))) SmemWs smw;
+
+    const int tid = threadIdx.x, lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int L = xcd_remap(blockIdx.x, nblocks);
+    const int w = L / ntiles_n, nt = L % ntiles_n;
+    if (wave == 0) {
+        const WorkItem it = find_work_item(group_sizes, G, M, TM, w);
+        if (lane == 0) s_item = it;
+    }
+    __syncthreads();
+    const WorkItem it = s_item;
+    if (it.g < 0) return;
+    const int n0 = nt * TN;
+    if (it.g == G) {  // rows past the last group: zeros
+        const int rows = it.hi - it.lo;
+        constexpr int V = 16 / OUT_BYTES;
+        for (int e = tid; e < rows * (TN / V); e += kThreads) {
+            const int r = it.lo + e / (TN / V), c = n0 + (e % (TN / V)) * V;
+            *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(out) + ((int64_t)r * N + c) * OUT_BYTES) =
+                make_uint4(0, 0, 0, 0);
+        }
+        return;
+    }
+    const int g = it.g, row0 = it.tile * TM;
+    const int nkb = K / kTK, nnb = N / kQBlock;
+
+    if (wave >= 4) {
+        // ------------------------------------------------------ producer
+        const int p = wave - 4;
+        const int qchunk = lane % kLPR;
+        int qrow[2];
+        int64_t qgrow[2], qlrow[2];
+        bool qvalid[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            qrow[h] = 16 * p + 8 * h + lane / kLPR;
+            qgrow[h] = row0 + qrow[h];
+            qvalid[h] = qgrow[h] >= it.lo && qgrow[h] < it.hi;
+            qlrow[h] = qvalid[h] ? qgrow[h] : it.lo;
+        }
+        const float* srl = rhs_scale + (int64_t)g * nkb * nnb + n0 / kQBlock + min(qchunk, 3);
+        struct Stage2 {
+            RawA<KIND> raw[2];
+            float sr;
+        };
+        auto load_stage = [&](Stage2& st, int kb) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) load_raw<KIND>(st.raw[h], lhs, lhs_scale, qlrow[h], K, kb, qchunk);
+            st.sr = srl[kb * nnb];
+        };
+        auto quant_store = [&](int kb, int buf, const Stage2& st) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                uint2 codes[kNP];
+                const float s = quantize_raw<KIND>(st.raw[h], codes);
+#pragma unroll
+                for (int q = 0; q < kNP; ++q)
+                    *reinterpret_cast<uint2*>(&smw.t.a[buf][qrow[h]][qchunk * 8 + q * 8 * kLPR]) = codes[q];
+                smw.t.c[buf][qchunk][qrow[h]] = s * st.sr;
+                if (WRITE_Q && nt == 0 && qvalid[h]) {
+#pragma unroll
+                    for (int q = 0; q < kNP; ++q)
+                        *reinterpret_cast<uint2*>(q_out + qgrow[h] * K + kb * kTK + qchunk * 8 + q * 8 * kLPR) = codes[q];
+                    if (qchunk == 0) s_out[qgrow[h] * nkb + kb] = s;
+                }
+            }
+        };
+        Stage2 st0, st1;
+        load_stage(st0, 0);
+        quant_store(0, 0, st0);
+        load_stage(st1, min(1, nkb - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        load_stage(st0, min(2, nkb - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+        // step k: quantise k+1 (loaded two steps ago) into buffer (k+1)&1,
+        // reload that stage with k+3
+        auto pstep = [&](int k, Stage2& sq) {
+            quant_store(min(k + 1, nkb - 1), (k + 1) & 1, sq);
+            load_stage(sq, min(k + 3, nkb - 1));
+            __builtin_amdgcn_sched_barrier(0);
+            __syncthreads();
+        };
+        int k = 0;
+        for (; k + 1 < nkb; k += 2) {
+            pstep(k, st1);
+            pstep(k + 1, st0);
+        }
+        if (k < nkb) pstep(k, st1);
+        return;
+    }
+
+    // ---------------------------------------------------------- consumer
+    const int cw = wave;                          // 0..3
+    const int lr = lane & 15, lc = lane >> 4;
+    const int ncol0 = n0 + 128 * cw;
+    const uint8_t* bptr = rhs + ((int64_t)g * (N / 16) + ncol0 / 16) * nkb * 2048 + lane * 16;
+    v4f acc[MB][NBC];
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NBC; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    v8i b[NBC];
+    auto load_b1 = [&](int j, int kb) {
+        const uint8_t* q = bptr + ((int64_t)j * nkb + kb) * 2048;
+        const uint4 lo = *reinterpret_cast<const uint4*>(q);
+        const uint4 hi = *reinterpret_cast<const uint4*>(q + 1024);
+        b[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    };
+#pragma unroll
+    for (int j = 0; j < NBC; ++j) load_b1(j, 0);
+    __syncthreads();
+    // step k: fragments and factors of k from buffer k&1, MFMAs of k with b,
+    // each B block reloaded with k+1 right after its MFMAs
+    auto cstep = [&](int k) {
+        const int buf = k & 1, k1 = min(k + 1, nkb - 1);
+        v8i af[MB];
+        float cf[MB];
+#pragma unroll
+        for (int i = 0; i < MB; ++i) {
+            af[i] = *reinterpret_cast<const v8i*>(&smw.t.a[buf][16 * i + lr][lc * 32]);
+            cf[i] = smw.t.c[buf][cw][16 * i + lr];
+        }
+#pragma unroll
+        for (int j = 0; j < NBC; ++j) {
+#pragma unroll
+            for (int i = 0; i < MB; ++i) {
+                const v4f pr = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    b[j], af[i], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(pr[r], cf[i], acc[i][j][r]);
+            }
+            load_b1(j, k1);
+        }
+        __syncthreads();
+    };
+    int k = 0;
+    for (; k + 1 < nkb; k += 2) {
+        cstep(k);
+        cstep(k + 1);
+    }
+    if (k < nkb) cstep(k);
+
+    // ---- epilogue: this wave's TM x 128 block through its LDS region (the
+    //      last barrier retired every read of the A tiles), stored back as
+    //      whole rows (256 bytes bf16 / 512 bytes fp32); rows outside the
+    //      item are skipped
+    uint8_t (*ep)[kEpiRow] = smw.epi[cw];
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NBC; ++j) {
+            uint8_t* d = &ep[16 * i + lr][(16 * j + 4 * lc) * OUT_BYTES];
+            if constexpr (OUT_BF16)
+                *reinterpret_cast<uint2*>(d) =
+                    make_uint2(pack_bf16x2(acc[i][j][0], acc[i][j][1]), pack_bf16x2(acc[i][j][2], acc[i][j][3]));
+            else
+                *reinterpret_cast<float4*>(d) = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+        }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    constexpr int LPRO = 128 * OUT_BYTES / 16;   // lanes per row on the way out
+    constexpr int RPI = 64 / LPRO;
+    const int orow = lane / LPRO, ocol = (lane % LPRO) * 16;
+#pragma unroll
+    for (int q = 0; q < (TM + RPI - 1) / RPI; ++q) {
+        const int r = RPI * q + orow;
+        if (r >= TM) break;
+        const uint4 v = *reinterpret_cast<const uint4*>(&ep[r][ocol]);
+        const int grow = row0 + r;
+        if (grow >= it.lo && grow < it.hi)
+            *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(out) + ((int64_t)grow * N + ncol0) * OUT_BYTES + ocol) = v;
+    }
+}
+
+template <int KIND, int TM, bool WRITE_Q>
+hipError_t launch_ws(const void* lhs, const float* lhs_scale, const uint8_t* rhs,
+                     const float* rhs_scale, const int32_t* group_sizes, int M, int K, int N, int G,
+                     void* out, bool out_bf16, uint8_t* q_out, float* scale_out, hipStream_t stream) {
+    const int ntiles_n = N / 512;
+    const int64_t items = max_work_items(M, G, TM);
+    const int nblocks = (int)(items * ntiles_n);
+    if (out_bf16)
+        hipLaunchKernelGGL((fp8_fwd_ws_kernel<KIND, true, TM, WRITE_Q>), dim3(nblocks), dim3(kThreads),
+                           0, stream, lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N, G, out,
+                           q_out, scale_out, ntiles_n, nblocks);
+    else
+        hipLaunchKernelGGL((fp8_fwd_ws_kernel<KIND, false, TM, WRITE_Q>), dim3(nblocks), dim3(kThreads),
+                           0, stream, lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N, G, out,
+                           q_out, scale_out, ntiles_n, nblocks);
+    return hipGetLastError();
+}
+
 template <int KIND, int WN, int TM, bool WRITE_Q, bool SWIGLU = false>
 hipError_t launch_cfg(const void* lhs, const float* lhs_scale, const uint8_t* rhs,
                       const float* rhs_scale, const int32_t* group_sizes, int M, int K, int N,
@@ -590,6 +819,19 @@ hipError_t launch_kind(const void* lhs, const float* lhs_scale, const uint8_t* r
         wn = forced_wn;
     int tm = max_work_items(M, G, 48) * (N / (kWaves * wn)) <= device_cus() ? 48 : 64;
     if (forced_tm == 48 || forced_tm == 64) tm = forced_tm;
+    // 512-column, 48-row tiles run the warp-specialised kernel (GMM_FP8_WS=0
+    // selects the uniform one, for comparison sweeps)
+    static const bool use_ws = [] {
+        const char* e = std::getenv("GMM_FP8_WS");
+        return !(e && std::atoi(e) == 0);
+    }();
+    if (use_ws && wn == 64 && tm == 48) {
+        if (q_out != nullptr && KIND != kLhsE4M3)
+            return launch_ws<KIND, 48, true>(lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N,
+                                             G, out, out_bf16, q_out, scale_out, stream);
+        return launch_ws<KIND, 48, false>(lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N, G,
+                                          out, out_bf16, q_out, scale_out, stream);
+    }
 #define GMM_FP8_WN_TM(WN_, TM_)                                                                  \
     if (wn == WN_ && tm == TM_)                                                                  \
         return launch_wn<KIND, WN_, TM_>(lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N, G, \
