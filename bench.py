@@ -76,9 +76,12 @@ def copy_reference() -> int:
     return 0
 
 
-def graph_time_ms(fn, steps: int, warmup: int) -> float:
+def graph_time_ms(fn, steps: int, warmup: int, settle_s: float = 0.06) -> float:
     """Average ms per call: W eager calls, then K calls captured in one HIP
-    graph and replayed once between events on the capture stream."""
+    graph, replayed untimed for at least `settle_s` seconds (the GPU clock
+    ramps up over the first ~15 ms of work after idle; launches in that window
+    run up to 15% slower), then replayed once between events on the capture
+    stream."""
     import torch
     for _ in range(warmup):
         fn()
@@ -92,8 +95,12 @@ def graph_time_ms(fn, steps: int, warmup: int) -> float:
             for _ in range(steps):
                 fn()
     torch.cuda.synchronize()
-    graph.replay()                             # untimed replay (warm instruction caches)
-    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while True:                                # untimed replays: caches warm, clock settled
+        graph.replay()
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= settle_s:
+            break
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     with torch.cuda.stream(stream):
@@ -221,7 +228,7 @@ def main() -> int:
                      "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                      "traffic": None if traffic is None else int(traffic),
                      "algorithmic_bytes": alg_bytes,
-                     "kernel": "fp8_fwd_kernel<bf16 lhs, bf16 out> (48x512 tiles at this shape)",
+                     "kernel": "fp8_fwd_ws_kernel<bf16 lhs, bf16 out, 48-row tiles, 16 waves>",
                      "kernel_avg_us": round(ms * 1e3, 3),
                      "mfma_tflops": round(tflops, 2), "mfma_peak": PEAK_FP8_TFLOPS,
                      "mfma_frac": round(tflops / PEAK_FP8_TFLOPS, 4)},

@@ -535,19 +535,27 @@ __global__ __launch_bounds__(kThreads, 2) void fp8_fwd_kernel(
 // separate, so no role waits on the other's loads at a control-flow join).
 // Producer lane (p, l): 16 values of each of rows 16p + l/8 and
 // 16p + 8 + l/8 (runs at 8c and 64 + 8c, c = l % 8) — the same per-row
-// recipe and lane layout as the plain kernel, two rows per lane.
-template <int KIND, bool OUT_BF16, int TM, bool WRITE_Q>
-__global__ __launch_bounds__(kThreads, 2) void fp8_fwd_ws_kernel(   // TM = 48 (64 spills)
+// recipe and lane layout as the plain kernel, two rows per lane.  NW = 16
+// doubles both roles: 8 consumers of 64 columns (two per SIMD, one scale
+// block per pair) and 8 producers of one row per lane (row 8p + l/8).
+// Producers whose rows all lie past a 48-row tile only take the barriers.
+template <int KIND, bool OUT_BF16, int TM, bool WRITE_Q, int NW = 8>
+__global__ __launch_bounds__(64 * NW, NW == 16 ? 4 : 2) void fp8_fwd_ws_kernel(   // TM = 48 (64 spills)
     const void* __restrict__ lhs, const float* __restrict__ lhs_scale,
     const uint8_t* __restrict__ rhs, const float* __restrict__ rhs_scale,
     const int32_t* __restrict__ group_sizes, int M, int K, int N, int G, void* __restrict__ out,
     uint8_t* __restrict__ q_out, float* __restrict__ s_out, int ntiles_n, int nblocks) {
     static_assert(TM == 64 || TM == 48, "64- or 48-row tiles");
+    static_assert(NW == 8 || NW == 16, "8 or 16 waves");
     constexpr int MB = TM / 16;
-    constexpr int NBC = 8;                 // 16-column blocks per consumer wave
+    constexpr int NC = NW / 2;             // consumer waves (and producer waves)
+    constexpr int CWID = 512 / NC;         // output columns per consumer wave
+    constexpr int NBC = CWID / 16;         // 16-column blocks per consumer wave
+    constexpr int HP = 8 / NC;             // rows per producer lane
     constexpr int TN = 512;
+    constexpr int kThr = 64 * NW;
     constexpr int OUT_BYTES = OUT_BF16 ? 2 : 4;
-    constexpr int kEpiRow = 128 * OUT_BYTES + 16;   // staged output row (bytes)
+    constexpr int kEpiRow = CWID * OUT_BYTES + 16;  // staged output row (bytes)
 
     struct Tiles {
         uint8_t a[2][kTM][kLdsRow];
@@ -555,7 +563,7 @@ __global__ __launch_bounds__(kThreads, 2) void fp8_fwd_ws_kernel(   // TM = 48 (
     };
     union SmemWs {
         Tiles t;
-        uint8_t epi[4][TM][kEpiRow];
+        uint8_t epi[NC][TM][kEpiRow];
     };
     __shared__ WorkItem s_item;
     __shared__ __attribute__((aligned(16))) SmemWs smw;
@@ -575,7 +583,7 @@ __global__ __launch_bounds__(kThreads, 2) void fp8_fwd_ws_kernel(   // TM = 48 (
     if (it.g == G) {  // rows past the last group: zeros
         const int rows = it.hi - it.lo;
         constexpr int V = 16 / OUT_BYTES;
-        for (int e = tid; e < rows * (TN / V); e += kThreads) {
+        for (int e = tid; e < rows * (TN / V); e += kThr) {
             const int r = it.lo + e / (TN / V), c = n0 + (e % (TN / V)) * V;
             *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(out) + ((int64_t)r * N + c) * OUT_BYTES) =
                 make_uint4(0, 0, 0, 0);
@@ -585,33 +593,39 @@ __global__ __launch_bounds__(kThreads, 2) void fp8_fwd_ws_kernel(   // TM = 48 (
     const int g = it.g, row0 = it.tile * TM;
     const int nkb = K / kTK, nnb = N / kQBlock;
 
-    if (wave >= 4) {
+    if (wave >= NC) {
         // ------------------------------------------------------ producer
-        const int p = wave - 4;
+        const int p = wave - NC;
+        if (8 * HP * p >= TM) {
+            // every row of this producer lies past the tile: only keep the
+            // barrier count (prologue + one per step)
+            for (int k = 0; k <= nkb; ++k) __syncthreads();
+            return;
+        }
         const int qchunk = lane % kLPR;
-        int qrow[2];
-        int64_t qgrow[2], qlrow[2];
-        bool qvalid[2];
+        int qrow[HP];
+        int64_t qgrow[HP], qlrow[HP];
+        bool qvalid[HP];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            qrow[h] = 16 * p + 8 * h + lane / kLPR;
+        for (int h = 0; h < HP; ++h) {
+            qrow[h] = 8 * HP * p + 8 * h + lane / kLPR;
             qgrow[h] = row0 + qrow[h];
             qvalid[h] = qgrow[h] >= it.lo && qgrow[h] < it.hi;
             qlrow[h] = qvalid[h] ? qgrow[h] : it.lo;
         }
         const float* srl = rhs_scale + (int64_t)g * nkb * nnb + n0 / kQBlock + min(qchunk, 3);
         struct Stage2 {
-            RawA<KIND> raw[2];
+            RawA<KIND> raw[HP];
             float sr;
         };
         auto load_stage = [&](Stage2& st, int kb) {
 #pragma unroll
-            for (int h = 0; h < 2; ++h) load_raw<KIND>(st.raw[h], lhs, lhs_scale, qlrow[h], K, kb, qchunk);
+            for (int h = 0; h < HP; ++h) load_raw<KIND>(st.raw[h], lhs, lhs_scale, qlrow[h], K, kb, qchunk);
             st.sr = srl[kb * nnb];
         };
         auto quant_store = [&](int kb, int buf, const Stage2& st) {
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
+            for (int h = 0; h < HP; ++h) {
                 uint2 codes[kNP];
                 const float s = quantize_raw<KIND>(st.raw[h], codes);
 #pragma unroll
@@ -652,9 +666,10 @@ __global__ __launch_bounds__(kThreads, 2) void fp8_fwd_ws_kernel(   // TM = 48 (
     }
 
     // ---------------------------------------------------------- consumer
-    const int cw = wave;                          // 0..3
+    const int cw = wave;                          // 0 .. NC-1
     const int lr = lane & 15, lc = lane >> 4;
-    const int ncol0 = n0 + 128 * cw;
+    const int ncol0 = n0 + CWID * cw;
+    const int cslot = (CWID * cw) / 128;          // the wave's 128-column scale block
     const uint8_t* bptr = rhs + ((int64_t)g * (N / 16) + ncol0 / 16) * nkb * 2048 + lane * 16;
     v4f acc[MB][NBC];
 #pragma unroll
@@ -680,7 +695,7 @@ __global__ __launch_bounds__(kThreads, 2) void fp8_fwd_ws_kernel(   // TM = 48 (
 #pragma unroll
         for (int i = 0; i < MB; ++i) {
             af[i] = *reinterpret_cast<const v8i*>(&smw.t.a[buf][16 * i + lr][lc * 32]);
-            cf[i] = smw.t.c[buf][cw][16 * i + lr];
+            cf[i] = smw.t.c[buf][cslot][16 * i + lr];
         }
 #pragma unroll
         for (int j = 0; j < NBC; ++j) {
@@ -702,7 +717,7 @@ __global__ __launch_bounds__(kThreads, 2) void fp8_fwd_ws_kernel(   // TM = 48 (
     }
     if (k < nkb) cstep(k);
 
-    // ---- epilogue: this wave's TM x 128 block through its LDS region (the
+    // ---- epilogue: this wave's TM x CWID block through its LDS region (the
     //      last barrier retired every read of the A tiles), stored back as
     //      whole rows (256 bytes bf16 / 512 bytes fp32); rows outside the
     //      item are skipped
@@ -719,7 +734,7 @@ __global__ __launch_bounds__(kThreads, 2) void fp8_fwd_ws_kernel(   // TM = 48 (
                 *reinterpret_cast<float4*>(d) = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
         }
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    constexpr int LPRO = 128 * OUT_BYTES / 16;   // lanes per row on the way out
+    constexpr int LPRO = CWID * OUT_BYTES / 16;  // lanes per row on the way out
     constexpr int RPI = 64 / LPRO;
     const int orow = lane / LPRO, ocol = (lane % LPRO) * 16;
 #pragma unroll
@@ -733,7 +748,7 @@ __global__ __launch_bounds__(kThreads, 2) void fp8_fwd_ws_kernel(   // TM = 48 (
     }
 }
 
-template <int KIND, int TM, bool WRITE_Q>
+template <int KIND, int TM, bool WRITE_Q, int NW = 8>
 hipError_t launch_ws(const void* lhs, const float* lhs_scale, const uint8_t* rhs,
                      const float* rhs_scale, const int32_t* group_sizes, int M, int K, int N, int G,
                      void* out, bool out_bf16, uint8_t* q_out, float* scale_out, hipStream_t stream) {
@@ -741,11 +756,11 @@ hipError_t launch_ws(const void* lhs, const float* lhs_scale, const uint8_t* rhs
     const int64_t items = max_work_items(M, G, TM);
     const int nblocks = (int)(items * ntiles_n);
     if (out_bf16)
-        hipLaunchKernelGGL((fp8_fwd_ws_kernel<KIND, true, TM, WRITE_Q>), dim3(nblocks), dim3(kThreads),
+        hipLaunchKernelGGL((fp8_fwd_ws_kernel<KIND, true, TM, WRITE_Q, NW>), dim3(nblocks), dim3(64 * NW),
                            0, stream, lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N, G, out,
                            q_out, scale_out, ntiles_n, nblocks);
     else
-        hipLaunchKernelGGL((fp8_fwd_ws_kernel<KIND, false, TM, WRITE_Q>), dim3(nblocks), dim3(kThreads),
+        hipLaunchKernelGGL((fp8_fwd_ws_kernel<KIND, false, TM, WRITE_Q, NW>), dim3(nblocks), dim3(64 * NW),
                            0, stream, lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N, G, out,
                            q_out, scale_out, ntiles_n, nblocks);
     return hipGetLastError();
@@ -819,12 +834,22 @@ hipError_t launch_kind(const void* lhs, const float* lhs_scale, const uint8_t* r
         wn = forced_wn;
     int tm = max_work_items(M, G, 48) * (N / (kWaves * wn)) <= device_cus() ? 48 : 64;
     if (forced_tm == 48 || forced_tm == 64) tm = forced_tm;
-    // 512-column, 48-row tiles run the warp-specialised kernel (GMM_FP8_WS=0
-    // selects the uniform one, for comparison sweeps)
+    // 512-column, 48-row tiles run the warp-specialised kernel: 16 waves (8
+    // MFMA waves of 64 columns, 6 quantiser waves of 8 rows each) unless the
+    // kernel also writes the LHS codes, which takes the 8-wave form.
+    // GMM_FP8_WS=0 selects the uniform kernel and GMM_FP8_WS_WAVES=8 the
+    // 8-wave form everywhere (comparison sweeps only).
     static const bool use_ws = [] {
         const char* e = std::getenv("GMM_FP8_WS");
         return !(e && std::atoi(e) == 0);
     }();
+    static const int ws_waves = [] {
+        const char* e = std::getenv("GMM_FP8_WS_WAVES");
+        return e && std::atoi(e) == 8 ? 8 : 16;
+    }();
+    if (use_ws && wn == 64 && tm == 48 && ws_waves == 16 && (q_out == nullptr || KIND == kLhsE4M3))
+        return launch_ws<KIND, 48, false, 16>(lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N,
+                                              G, out, out_bf16, q_out, scale_out, stream);
     if (use_ws && wn == 64 && tm == 48) {
         if (q_out != nullptr && KIND != kLhsE4M3)
             return launch_ws<KIND, 48, true>(lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N,
