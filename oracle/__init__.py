@@ -47,6 +47,12 @@ def _load():
     lib.oracle_tgmm_f64.argtypes = [P, P, P, I, I, I, I, P]
     lib.oracle_dx_f64.argtypes = [P, P, P, I, I, I, I, P]
     lib.oracle_swiglu.argtypes = [P, I, I, P]
+    lib.oracle_e2m1_decode.restype = ctypes.c_double
+    lib.oracle_e2m1_decode.argtypes = [ctypes.c_uint8]
+    lib.oracle_e2m1_encode.restype = ctypes.c_uint8
+    lib.oracle_e2m1_encode.argtypes = [ctypes.c_double]
+    lib.oracle_quantize_rhs_mxfp4.argtypes = [P, I, I, I, P, P]
+    lib.oracle_gmm_fp8_mxfp4.argtypes = [P, P, P, P, P, I, I, I, I, P]
     lib.oracle_num_threads.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -139,6 +145,53 @@ def gmm_fp8(ql, sl, qr, sr, group_sizes):
     assert K == K2 and gs.size == G and int(gs.sum()) <= M
     out = np.empty((M, N), dtype=np.float64)
     lib.oracle_gmm_fp8(pql, psl, pqr, psr, pg, M, K, N, G, out.ctypes.data_as(ctypes.c_void_p))
+    return out
+
+
+def e2m1_decode(codes) -> np.ndarray:
+    """E2M1 code (low 4 bits) -> fp64 value."""
+    lib = _load()
+    c = np.asarray(codes, dtype=np.uint8)
+    return np.array([lib.oracle_e2m1_decode(int(v)) for v in c.ravel()]).reshape(c.shape)
+
+
+def e2m1_encode(y) -> np.ndarray:
+    """fp64 values -> E2M1 codes (nearest, ties to even mantissa, saturating)."""
+    lib = _load()
+    y = np.asarray(y, dtype=np.float64)
+    return np.array([lib.oracle_e2m1_encode(float(v)) for v in y.ravel()],
+                    dtype=np.uint8).reshape(y.shape)
+
+
+def quantize_rhs_mxfp4(w):
+    """MXFP4 weights: w [G,K,N] -> (codes [G,K,N] uint8, E8M0 [G,K/32,N] uint8),
+    one block of 32 consecutive k per (expert, column)."""
+    lib = _load()
+    w, pw = _c(w, np.float32)
+    G, K, N = w.shape
+    assert K % 32 == 0
+    q = np.empty((G, K, N), dtype=np.uint8)
+    e8 = np.empty((G, K // 32, N), dtype=np.uint8)
+    lib.oracle_quantize_rhs_mxfp4(pw, G, K, N, q.ctypes.data_as(ctypes.c_void_p),
+                                  e8.ctypes.data_as(ctypes.c_void_p))
+    return q, e8
+
+
+def gmm_fp8_mxfp4(ql, sl, q4, e8, group_sizes):
+    """fp64 GMM of FP8 1x128 LHS codes/scales against MXFP4 weights."""
+    lib = _load()
+    ql, pql = _c(ql, np.uint8)
+    sl, psl = _c(sl, np.float32)
+    q4, pq4 = _c(q4, np.uint8)
+    e8, pe8 = _c(e8, np.uint8)
+    gs, pg = _c(group_sizes, np.int32)
+    M, K = ql.shape
+    G, K2, N = q4.shape
+    assert K == K2 and K % QBLOCK == 0 and e8.shape == (G, K // 32, N)
+    assert gs.size == G and int(gs.sum()) <= M
+    out = np.empty((M, N), dtype=np.float64)
+    lib.oracle_gmm_fp8_mxfp4(pql, psl, pq4, pe8, pg, M, K, N, G,
+                             out.ctypes.data_as(ctypes.c_void_p))
     return out
 
 

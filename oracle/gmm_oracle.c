@@ -32,6 +32,15 @@
  *  [GG]  "MoE 优化的探索：从 MiniMax-01、Comet、FlashMoE 到 DeepSeek-V4",
  *        section 3.7.2: a grouped GEMM is one independent GEMM per expert,
  *        X_e W_e, over that expert's contiguous rows.
+ *  [V2s] "实现差距：GMM Kernel（V1 vs V2）", sections 3.4 and 4.1: V2 takes
+ *        RHS weights in sub-byte types (int4, float4_e2m1fn) and unpacks
+ *        them in the kernel; MXFP4 weights are the high-priority case.
+ *  [MX]  OCP Microscaling Formats (MX) specification v1.0: an MXFP4 block
+ *        is 32 E2M1 elements (sign, 2 exponent bits with bias 1, 1 mantissa
+ *        bit; values 0, 0.5, 1, 1.5, 2, 3, 4, 6) sharing one E8M0 scale
+ *        2^(e-127); a block V is converted with shared exponent
+ *        floor(log2(max|V|)) - 2 (2 = the largest E2M1 exponent) and each
+ *        element rounded to E2M1, clamped to +-6.
  *
  * Readings where the pages are silent (the same list is kept with the
  * design notes):
@@ -46,6 +55,16 @@
  *    and 128 of them need at most 43 bits).
  *  - A block with a non-zero abs-max below 2^-100 is outside the contract
  *    (its inverse scale may overflow fp32); such inputs are not tested.
+ *  - MXFP4 weights ([V2s], [MX]): blocks of 32 run along K (the reduction
+ *    index) for each expert and column; the LHS keeps the FP8 1x128 recipe,
+ *    so a forward block product is the 1x128 LHS block against four MXFP4
+ *    blocks.  E2M1 rounding is to nearest, ties to the even mantissa, the
+ *    sign of zero is kept (code 8), the shared exponent is clamped to
+ *    [-127, 127], and an all-zero block gets E8M0 code 0 with zero codes.
+ *    The division by the power-of-two scale is exact (done in fp64).  The
+ *    per-block inner sum is exact in fp64 here too (each product has at
+ *    most 6 significant bits and the exponents of 128 of them span far
+ *    fewer than 53 - 6 - 7 binades for any finite scaled input).
  *
  * Parity pins: every function here is checked in tests/test_oracle_*.py
  * against something other than itself (torch's float8_e4m3fn cast, numpy
@@ -333,6 +352,123 @@ void oracle_gmm_fp8(const uint8_t *ql, const float *sl, const uint8_t *qr,
         }
         free(part);
         free(lrow);
+    }
+    free(gid);
+}
+
+/* ------------------------------------------------- MXFP4 weights -- */
+
+/* E2M1 code (low 4 bits) -> value ([MX]). */
+double oracle_e2m1_decode(uint8_t code)
+{
+    int e = (code >> 1) & 3, m = code & 1;
+    double v = e == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    return (code & 8) ? -v : v;
+}
+
+/* Nearest E2M1 value to y, ties to the code with mantissa bit 0, |y| >= 6
+ * saturating to 6, sign kept ([MX]; reading above). */
+uint8_t oracle_e2m1_encode(double y)
+{
+    uint8_t sign = (y < 0 || (y == 0 && signbit(y))) ? 8 : 0;
+    double a = fabs(y), best_d = 1e300;
+    uint8_t best = 0, c;
+    if (a >= 6.0)
+        return sign | 7;
+    for (c = 0; c < 8; ++c) {
+        double d = fabs(a - oracle_e2m1_decode(c));
+        if (d < best_d || (d == best_d && (c & 1) == 0 && (best & 1) == 1)) {
+            best_d = d;
+            best = c;
+        }
+    }
+    return sign | best;
+}
+
+/* One MXFP4 block of n values: E8M0 code of the shared scale, element
+ * codes ([MX]). */
+static uint8_t mx_block(const float *vals, int64_t stride, int n, uint8_t *codes,
+                        int64_t cstride)
+{
+    double amax = 0.0;
+    int i, e;
+    for (i = 0; i < n; ++i)
+        if (fabs((double)vals[i * stride]) > amax)
+            amax = fabs((double)vals[i * stride]);
+    if (amax == 0.0) {
+        for (i = 0; i < n; ++i)
+            codes[i * cstride] = 0;
+        return 0;
+    }
+    frexp(amax, &e);          /* amax = f 2^e, f in [0.5, 1): floor(log2) = e-1 */
+    e = e - 1 - 2;
+    if (e < -127)
+        e = -127;
+    if (e > 127)
+        e = 127;
+    for (i = 0; i < n; ++i)
+        codes[i * cstride] = oracle_e2m1_encode(ldexp((double)vals[i * stride], -e));
+    return (uint8_t)(e + 127);
+}
+
+/* w: [G,K,N] -> codes [G,K,N] (one E2M1 code per byte) and E8M0 scales
+ * [G,K/32,N]: blocks of 32 consecutive k for each (g, n) ([V2s], [MX]). */
+void oracle_quantize_rhs_mxfp4(const float *w, int64_t G, int64_t K, int64_t N,
+                               uint8_t *q, uint8_t *e8)
+{
+    int64_t nb = K / 32, g;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (g = 0; g < G; ++g)
+        for (int64_t b = 0; b < nb; ++b)
+            for (int64_t n = 0; n < N; ++n) {
+                int64_t off = (g * K + b * 32) * N + n;
+                e8[(g * nb + b) * N + n] = mx_block(w + off, N, 32, q + off, N);
+            }
+}
+
+/* out[m,n] = sum_b scale_l[m,b] * sum_{k in 128-block b}
+ *            dec8(ql[m,k]) * dec4(q4[g,k,n]) * 2^(e8[g,k/32,n] - 127)
+ * for m in group g; rows past the total are 0 ([Q2], [Q3], [V2s], [MX],
+ * [GG], [V2z]).  ql [M,K], sl [M,K/128], q4 [G,K,N] codes, e8 [G,K/32,N]. */
+void oracle_gmm_fp8_mxfp4(const uint8_t *ql, const float *sl, const uint8_t *q4,
+                          const uint8_t *e8, const int32_t *group_sizes, int64_t M,
+                          int64_t K, int64_t N, int64_t G, double *out)
+{
+    int64_t nkb = K / QBLOCK, m;
+    int32_t *gid = (int32_t *)malloc(sizeof(int32_t) * (M > 0 ? M : 1));
+    double lut8[256], lut4[16];
+    int c;
+    for (c = 0; c < 256; ++c)
+        lut8[c] = oracle_e4m3_decode((uint8_t)c);
+    for (c = 0; c < 16; ++c)
+        lut4[c] = oracle_e2m1_decode((uint8_t)c);
+    row_groups(group_sizes, G, M, gid);
+#pragma omp parallel
+    {
+        double *part = (double *)malloc(sizeof(double) * N);
+#pragma omp for schedule(dynamic, 4)
+        for (m = 0; m < M; ++m) {
+            int64_t g = gid[m], b, k, n;
+            double *o = out + m * N;
+            for (n = 0; n < N; ++n)
+                o[n] = 0.0;
+            if (g >= G)
+                continue;
+            for (b = 0; b < nkb; ++b) {
+                for (n = 0; n < N; ++n)
+                    part[n] = 0.0;
+                for (k = b * QBLOCK; k < (b + 1) * QBLOCK; ++k) {
+                    double a = lut8[ql[m * K + k]];
+                    const uint8_t *wr = q4 + (g * K + k) * N;
+                    const uint8_t *er = e8 + (g * (K / 32) + k / 32) * N;
+                    for (n = 0; n < N; ++n)
+                        part[n] += a * ldexp(lut4[wr[n] & 15], (int)er[n] - 127);
+                }
+                for (n = 0; n < N; ++n)
+                    o[n] += part[n] * (double)sl[m * nkb + b];
+            }
+        }
+        free(part);
     }
     free(gid);
 }
