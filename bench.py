@@ -278,6 +278,16 @@ def main() -> int:
                 ("fp8_fwd_gate_up_plain", lambda: gmm.gmm_fp8_fwd(x, guq, gus, gs, out=wide))]:
             f_us = graph_time_ms(fn, 100, 10) * 1e3
             ops[name] = {"us": round(f_us, 3), "tflops": round(gflops / (f_us * 1e-6) / 1e12, 2)}
+        del guq, gus, wide
+        # the same wi forward against MXFP4 weights (E2M1 codes, E8M0 scales
+        # per 32 k): half the weight bytes of FP8
+        q4, s4 = gmm.gmm_quantize_rhs_mxfp4(w)
+        out4 = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        m_us = graph_time_ms(lambda: gmm.gmm_fp8_mxfp4_fwd(x, q4, s4, gs, out=out4), 100, 10) * 1e3
+        mbytes = total * K * 2 + G * K * N // 2 + G * K * N // 32 + M * N * 2 + G * 4
+        ops["fp8_mxfp4_fwd"] = {"us": round(m_us, 3), "tflops": round(flops / (m_us * 1e-6) / 1e12, 2),
+                                "GB/s": round(mbytes / (m_us * 1e-6) / 1e9, 1),
+                                "frac_hbm": round(mbytes / (m_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
         result["ops"] = ops
 
     if not args.no_cpu_baseline:

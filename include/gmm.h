@@ -118,6 +118,48 @@ GMM_API int gmm_quantize_rhs(const void *w, int w_dtype, int64_t G, int64_t K,
                      int64_t N, uint8_t *q, float *scale, void *stream);
 
 /*
+ * gmm_quantize_rhs_mxfp4 -- MXFP4 quantisation of the expert weights (done
+ *   once, offline).  "实现差距：GMM Kernel（V1 vs V2）", sections 3.4 and 4.1:
+ *   the RHS may be a sub-byte type, MXFP4 first.  Format and conversion are
+ *   the OCP Microscaling (MX) specification v1.0's: each block of 32
+ *   consecutive k of one (expert g, column n) shares an E8M0 scale
+ *   2^(e-127), e = floor(log2(max |w|)) - 2 clamped to [-127, 127] (code 0
+ *   for an all-zero block), and each element is the E2M1 value (0, 0.5, 1,
+ *   1.5, 2, 3, 4, 6 and negatives) nearest to w / 2^e, ties to the even
+ *   mantissa, clamped to +-6, sign kept.
+ * w:     [G,K,N], w_dtype GMM_BF16 or GMM_F32.
+ * q:     G*K*N/2 bytes of E2M1 codes in the packed order gmm_fp8_mxfp4_fwd
+ *        reads: chunk c = (g*N/16 + n/16)*K/128 + k/128 is 1024 bytes; lane
+ *        l = 16*swap2((k%128)/32) + n%16 (swap2 exchanges the two bits of a
+ *        2-bit value) owns bytes c*1024 + 16l .. +15, the 32 codes of its
+ *        block in k order, two per byte, even k in the low nibble.
+ * scale: G*K*N/32 bytes: byte c*64 + l is the E8M0 code of lane l's block.
+ * K and N must be multiples of 128.  Errors as for gmm_quantize_rhs.
+ */
+GMM_API int gmm_quantize_rhs_mxfp4(const void *w, int w_dtype, int64_t G, int64_t K,
+                     int64_t N, uint8_t *q, uint8_t *scale, void *stream);
+
+/*
+ * gmm_fp8_mxfp4_fwd -- grouped matmul forward of a 1x128 FP8 LHS against
+ *   MXFP4 weights.
+ *   out[m,n] = sum_b sl[m,b] * sum_{k in 128-block b}
+ *                ql[m,k] * e2m1(q4[g,k,n]) * 2^(e8[g,k/32,n] - 127)
+ *   for m in group g, fp32 accumulation of exact products; rows past the
+ *   total are 0.  (The forward of gmm_fp8_fwd with the weights in the
+ *   sub-byte type of "实现差距：GMM Kernel（V1 vs V2）", sections 3.4 and 4.1.)
+ * lhs, lhs_dtype, lhs_scale: as for gmm_fp8_fwd (bf16/fp32 quantised in the
+ *            kernel with the gmm_quantize_lhs recipe, or E4M3 codes + scales).
+ * rhs_q, rhs_scale: exactly as written by gmm_quantize_rhs_mxfp4.
+ * out:       [M,N], GMM_BF16 or GMM_F32.
+ * K and N must be multiples of 128; 1 <= G <= GMM_MAX_GROUPS.
+ * Errors: as for gmm_fp8_fwd.
+ */
+GMM_API int gmm_fp8_mxfp4_fwd(const void *lhs, int lhs_dtype, const float *lhs_scale,
+                const uint8_t *rhs_q, const uint8_t *rhs_scale,
+                const int32_t *group_sizes, int64_t M, int64_t K, int64_t N,
+                int64_t G, void *out, int out_dtype, void *stream);
+
+/*
  * gmm_fp8_fwd -- blockwise-FP8 grouped matmul forward.
  *   out[m,n] = sum_b ( sum_{k in block b} ql[m,k] qr[g,k,n] )
  *                    * sl[m,b] * sr[g,b,n/128]        for m in group g,

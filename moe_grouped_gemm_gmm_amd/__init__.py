@@ -19,7 +19,7 @@ GMM_F32, GMM_BF16, GMM_E4M3 = 0, 1, 2
 GMM_MAX_GROUPS = 4096
 EXPORTS = ("gmm_status_string", "gmm_last_error", "gmm_group_metadata", "gmm_quantize_lhs",
            "gmm_quantize_rhs", "gmm_fp8_fwd", "gmm_fp8_fwd_swiglu", "gmm_bf16_fwd", "tgmm_bf16",
-           "gmm_bf16_dx")
+           "gmm_bf16_dx", "gmm_quantize_rhs_mxfp4", "gmm_fp8_mxfp4_fwd")
 
 _lib = None
 
@@ -51,6 +51,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gmm_bf16_fwd.argtypes = [P, P, P, I64, I64, I64, I64, P, I, P]
     lib.tgmm_bf16.argtypes = [P, P, P, I64, I64, I64, I64, P, I, P]
     lib.gmm_bf16_dx.argtypes = [P, P, P, I64, I64, I64, I64, P, I, P]
+    lib.gmm_quantize_rhs_mxfp4.argtypes = [P, I, I64, I64, I64, P, P, P]
+    lib.gmm_fp8_mxfp4_fwd.argtypes = [P, I, P, P, P, P, I64, I64, I64, I64, P, I, P]
     for name in EXPORTS[2:]:
         getattr(lib, name).restype = I
     _lib = lib
@@ -120,6 +122,39 @@ def gmm_quantize_rhs(w: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
     s = torch.empty((G, max(K // 128, 0), max(N // 128, 0)), dtype=torch.float32, device=w.device)
     _check(lib.gmm_quantize_rhs(_ptr(w), _dt(w), G, K, N, _ptr(q), _ptr(s), _stream(w)))
     return q, s
+
+
+def gmm_quantize_rhs_mxfp4(w: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
+    """MXFP4 quantisation of w [G,K,N] -> (packed E2M1 codes uint8 [G, N/16, K/128, 1024],
+    E8M0 scales uint8 [G, N/16, K/128, 64]), in the order gmm_fp8_mxfp4_fwd reads
+    (include/gmm.h, gmm_quantize_rhs_mxfp4)."""
+    lib = load_library()
+    G, K, N = w.shape
+    q = torch.empty((G, max(N // 16, 0), max(K // 128, 0), 1024), dtype=torch.uint8, device=w.device)
+    s = torch.empty((G, max(N // 16, 0), max(K // 128, 0), 64), dtype=torch.uint8, device=w.device)
+    _check(lib.gmm_quantize_rhs_mxfp4(_ptr(w), _dt(w), G, K, N, _ptr(q), _ptr(s), _stream(w)))
+    return q, s
+
+
+def gmm_fp8_mxfp4_fwd(lhs: torch.Tensor, rhs_q: torch.Tensor, rhs_scale: torch.Tensor,
+                      group_sizes: torch.Tensor, lhs_scale: Optional[torch.Tensor] = None,
+                      out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None
+                      ) -> torch.Tensor:
+    """GMM of a 1x128 FP8 LHS (bf16/fp32 quantised in-kernel, or uint8 codes with
+    lhs_scale [M,K/128]) against MXFP4 weights from gmm_quantize_rhs_mxfp4."""
+    lib = load_library()
+    M, K = lhs.shape
+    G, N16, KB, chunk = rhs_q.shape
+    N = N16 * 16
+    if chunk != 1024 or KB * 128 != K or tuple(rhs_scale.shape) != (G, N16, KB, 64):
+        raise ValueError("rhs_q %s / rhs_scale %s do not match K=%d"
+                         % (tuple(rhs_q.shape), tuple(rhs_scale.shape), K))
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=lhs.device)
+    _check(lib.gmm_fp8_mxfp4_fwd(_ptr(lhs), _dt(lhs), _ptr(lhs_scale), _ptr(rhs_q),
+                                 _ptr(rhs_scale), _ptr(group_sizes), M, K, N, G, _ptr(out),
+                                 _dt(out), _stream(lhs)))
+    return out
 
 
 def gmm_fp8_fwd(lhs: torch.Tensor, rhs_q: torch.Tensor, rhs_scale: torch.Tensor,

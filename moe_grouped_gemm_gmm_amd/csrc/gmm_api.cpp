@@ -134,6 +134,50 @@ int gmm_quantize_rhs(const void* w, int w_dtype, int64_t G, int64_t K, int64_t N
                                                (hipStream_t)stream));
 }
 
+int gmm_quantize_rhs_mxfp4(const void* w, int w_dtype, int64_t G, int64_t K, int64_t N,
+                           uint8_t* q, uint8_t* scale, void* stream) {
+    if (w_dtype != GMM_BF16 && w_dtype != GMM_F32)
+        return fail(GMM_ERR_DTYPE, "w dtype %d is not GMM_BF16 or GMM_F32", w_dtype);
+    if (G < 1 || G > GMM_MAX_GROUPS)
+        return fail(GMM_ERR_SHAPE, "G=%lld outside [1, %d]", (long long)G, GMM_MAX_GROUPS);
+    GMM_TRY(check_mult(K, 128, "K"));
+    GMM_TRY(check_mult(N, 128, "N"));
+    if (G * (K / 128) * (N / 64) > kMaxDim) return fail(GMM_ERR_SHAPE, "too many blocks");
+    GMM_TRY(check_ptr(w, "w"));
+    GMM_TRY(check_ptr(q, "q"));
+    GMM_TRY(check_ptr(scale, "scale"));
+    return hip_status(gmm::launch_quantize_rhs_mxfp4(w, w_dtype == GMM_BF16, G, K, N, q, scale,
+                                                     (hipStream_t)stream));
+}
+
+int gmm_fp8_mxfp4_fwd(const void* lhs, int lhs_dtype, const float* lhs_scale,
+                      const uint8_t* rhs_q, const uint8_t* rhs_scale, const int32_t* group_sizes,
+                      int64_t M, int64_t K, int64_t N, int64_t G, void* out, int out_dtype,
+                      void* stream) {
+    int kind;
+    if (lhs_dtype == GMM_E4M3) kind = 0;
+    else if (lhs_dtype == GMM_BF16) kind = 1;
+    else if (lhs_dtype == GMM_F32) kind = 2;
+    else return fail(GMM_ERR_DTYPE, "lhs dtype %d unsupported", lhs_dtype);
+    GMM_TRY(check_out_dtype(out_dtype, "out"));
+    GMM_TRY(check_groups(M, G));
+    GMM_TRY(check_mult(K, 128, "K"));
+    GMM_TRY(check_mult(N, 128, "N"));
+    GMM_TRY(check_ptr(lhs, "lhs"));
+    GMM_TRY(check_ptr(rhs_q, "rhs_q"));
+    GMM_TRY(check_ptr(rhs_scale, "rhs_scale"));
+    GMM_TRY(check_ptr(group_sizes, "group_sizes"));
+    GMM_TRY(check_ptr(out, "out"));
+    if (kind == 0) GMM_TRY(check_ptr(lhs_scale, "lhs_scale"));
+    else if (lhs_scale != nullptr) return fail(GMM_ERR_DTYPE, "lhs_scale given with an unquantised lhs");
+    const int64_t blocks = ((M + 47) / 48 + G + 1) * (N / 128);
+    if (blocks > kMaxDim) return fail(GMM_ERR_SHAPE, "grid too large");
+    if (M == 0) return GMM_OK;
+    return hip_status(gmm::launch_fp8_mxfp4_fwd(lhs, kind, lhs_scale, rhs_q, rhs_scale, group_sizes,
+                                                (int)M, (int)K, (int)N, (int)G, out,
+                                                out_dtype == GMM_BF16, (hipStream_t)stream));
+}
+
 int gmm_fp8_fwd(const void* lhs, int lhs_dtype, const float* lhs_scale, const uint8_t* rhs,
                 const float* rhs_scale, const int32_t* group_sizes, int64_t M, int64_t K,
                 int64_t N, int64_t G, void* out, int out_dtype, uint8_t* q_out,

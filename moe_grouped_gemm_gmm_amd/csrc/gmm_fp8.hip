@@ -539,20 +539,32 @@ __global__ __launch_bounds__(kThreads, 2) void fp8_fwd_kernel(
 // doubles both roles: 8 consumers of 64 columns (two per SIMD, one scale
 // block per pair) and 8 producers of one row per lane (row 8p + l/8).
 // Producers whose rows all lie past a 48-row tile only take the barriers.
-template <int KIND, bool OUT_BF16, int TM, bool WRITE_Q, int NW = 8>
+//
+// B4: MXFP4 weights ("实现差距：GMM Kernel（V1 vs V2）", sections 3.4 and 4.1;
+// OCP MX v1.0) in the packed order of quantize_rhs_mxfp4_kernel, TN = 512,
+// 256 or 128 columns.  Each consumer block step loads 16 bytes of E2M1 codes
+// and one E8M0 byte per lane and hands the byte to the MFMA as the first
+// operand's scale, so the MFMA returns the MX-dequantised block product and
+// the FMA factor is the LHS scale alone.  The producers store the LHS codes
+// with K runs 1<->2 and 5<->6 of 16 exchanged (the MFMA's K grouping for an
+// FP4 first operand, which the packed weights follow).
+template <int KIND, bool OUT_BF16, int TM, bool WRITE_Q, int NW = 8, int TN = 512, bool B4 = false>
 __global__ __launch_bounds__(64 * NW, NW == 16 ? 4 : 2) void fp8_fwd_ws_kernel(   // TM = 48 (64 spills)
     const void* __restrict__ lhs, const float* __restrict__ lhs_scale,
-    const uint8_t* __restrict__ rhs, const float* __restrict__ rhs_scale,
+    const uint8_t* __restrict__ rhs, const void* __restrict__ rhs_scale_v,
     const int32_t* __restrict__ group_sizes, int M, int K, int N, int G, void* __restrict__ out,
     uint8_t* __restrict__ q_out, float* __restrict__ s_out, int ntiles_n, int nblocks) {
     static_assert(TM == 64 || TM == 48, "64- or 48-row tiles");
     static_assert(NW == 8 || NW == 16, "8 or 16 waves");
+    static_assert(B4 ? (NW == 16 && (TN == 512 || TN == 256 || TN == 128)) : TN == 512,
+                  "FP8 weights: 512 columns; MXFP4: 16 waves, 512/256/128 columns");
     constexpr int MB = TM / 16;
     constexpr int NC = NW / 2;             // consumer waves (and producer waves)
-    constexpr int CWID = 512 / NC;         // output columns per consumer wave
+    constexpr int CWID = TN / NC;          // output columns per consumer wave
     constexpr int NBC = CWID / 16;         // 16-column blocks per consumer wave
     constexpr int HP = 8 / NC;             // rows per producer lane
-    constexpr int TN = 512;
+    const float* __restrict__ rhs_scale = reinterpret_cast<const float*>(rhs_scale_v);
+    const uint8_t* __restrict__ rhs_e8 = reinterpret_cast<const uint8_t*>(rhs_scale_v);
     constexpr int kThr = 64 * NW;
     constexpr int OUT_BYTES = OUT_BF16 ? 2 : 4;
     constexpr int kEpiRow = CWID * OUT_BYTES + 16;  // staged output row (bytes)
@@ -613,7 +625,7 @@ __global__ __launch_bounds__(64 * NW, NW == 16 ? 4 : 2) void fp8_fwd_ws_kernel( 
             qvalid[h] = qgrow[h] >= it.lo && qgrow[h] < it.hi;
             qlrow[h] = qvalid[h] ? qgrow[h] : it.lo;
         }
-        const float* srl = rhs_scale + (int64_t)g * nkb * nnb + n0 / kQBlock + min(qchunk, 3);
+        const float* srl = B4 ? nullptr : rhs_scale + (int64_t)g * nkb * nnb + n0 / kQBlock + min(qchunk, 3);
         struct Stage2 {
             RawA<KIND> raw[HP];
             float sr;
@@ -621,7 +633,13 @@ __global__ __launch_bounds__(64 * NW, NW == 16 ? 4 : 2) void fp8_fwd_ws_kernel( 
         auto load_stage = [&](Stage2& st, int kb) {
 #pragma unroll
             for (int h = 0; h < HP; ++h) load_raw<KIND>(st.raw[h], lhs, lhs_scale, qlrow[h], K, kb, qchunk);
-            st.sr = srl[kb * nnb];
+            if constexpr (!B4) st.sr = srl[kb * nnb];
+        };
+        // LDS position of the 8-byte run of codes k0 .. k0+7 of a row
+        auto lds_pos = [](int k0) {
+            if constexpr (!B4) return k0;
+            const int r = (k0 >> 4) & 3;
+            return (k0 & ~63) | ((r == 1 || r == 2 ? 3 - r : r) << 4) | (k0 & 15);
         };
         auto quant_store = [&](int kb, int buf, const Stage2& st) {
 #pragma unroll
@@ -630,8 +648,12 @@ __global__ __launch_bounds__(64 * NW, NW == 16 ? 4 : 2) void fp8_fwd_ws_kernel( 
                 const float s = quantize_raw<KIND>(st.raw[h], codes);
 #pragma unroll
                 for (int q = 0; q < kNP; ++q)
-                    *reinterpret_cast<uint2*>(&smw.t.a[buf][qrow[h]][qchunk * 8 + q * 8 * kLPR]) = codes[q];
-                smw.t.c[buf][qchunk][qrow[h]] = s * st.sr;
+                    *reinterpret_cast<uint2*>(&smw.t.a[buf][qrow[h]][lds_pos(qchunk * 8 + q * 8 * kLPR)]) = codes[q];
+                if constexpr (B4) {
+                    if (qchunk == 0) smw.t.c[buf][0][qrow[h]] = s;
+                } else {
+                    smw.t.c[buf][qchunk][qrow[h]] = s * st.sr;
+                }
                 if (WRITE_Q && nt == 0 && qvalid[h]) {
 #pragma unroll
                     for (int q = 0; q < kNP; ++q)
@@ -669,19 +691,27 @@ __global__ __launch_bounds__(64 * NW, NW == 16 ? 4 : 2) void fp8_fwd_ws_kernel( 
     const int cw = wave;                          // 0 .. NC-1
     const int lr = lane & 15, lc = lane >> 4;
     const int ncol0 = n0 + CWID * cw;
-    const int cslot = (CWID * cw) / 128;          // the wave's 128-column scale block
-    const uint8_t* bptr = rhs + ((int64_t)g * (N / 16) + ncol0 / 16) * nkb * 2048 + lane * 16;
+    const int cslot = B4 ? 0 : (CWID * cw) / 128;   // the wave's 128-column scale block
+    const uint8_t* bptr = rhs + ((int64_t)g * (N / 16) + ncol0 / 16) * nkb * (B4 ? 1024 : 2048) + lane * 16;
+    const uint8_t* eptr = B4 ? rhs_e8 + ((int64_t)g * (N / 16) + ncol0 / 16) * nkb * 64 + lane : nullptr;
     v4f acc[MB][NBC];
 #pragma unroll
     for (int i = 0; i < MB; ++i)
 #pragma unroll
         for (int j = 0; j < NBC; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
     v8i b[NBC];
+    int be[NBC];
     auto load_b1 = [&](int j, int kb) {
-        const uint8_t* q = bptr + ((int64_t)j * nkb + kb) * 2048;
-        const uint4 lo = *reinterpret_cast<const uint4*>(q);
-        const uint4 hi = *reinterpret_cast<const uint4*>(q + 1024);
-        b[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        if constexpr (B4) {
+            const v4i lo = *reinterpret_cast<const v4i*>(bptr + ((int64_t)j * nkb + kb) * 1024);
+            b[j] = __builtin_shufflevector(lo, lo, 0, 1, 2, 3, -1, -1, -1, -1);
+            be[j] = eptr[((int64_t)j * nkb + kb) * 64];
+        } else {
+            const uint8_t* q = bptr + ((int64_t)j * nkb + kb) * 2048;
+            const uint4 lo = *reinterpret_cast<const uint4*>(q);
+            const uint4 hi = *reinterpret_cast<const uint4*>(q + 1024);
+            b[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        }
     };
 #pragma unroll
     for (int j = 0; j < NBC; ++j) load_b1(j, 0);
@@ -701,8 +731,13 @@ __global__ __launch_bounds__(64 * NW, NW == 16 ? 4 : 2) void fp8_fwd_ws_kernel( 
         for (int j = 0; j < NBC; ++j) {
 #pragma unroll
             for (int i = 0; i < MB; ++i) {
-                const v4f pr = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                    b[j], af[i], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+                v4f pr;
+                if constexpr (B4)   // first operand E2M1 with its E8M0 scale
+                    pr = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        b[j], af[i], v4f{0.f, 0.f, 0.f, 0.f}, 4, 0, 0, be[j], 0, 127);
+                else
+                    pr = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        b[j], af[i], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(pr[r], cf[i], acc[i][j][r]);
             }
@@ -748,22 +783,40 @@ __global__ __launch_bounds__(64 * NW, NW == 16 ? 4 : 2) void fp8_fwd_ws_kernel( 
     }
 }
 
-template <int KIND, int TM, bool WRITE_Q, int NW = 8>
+template <int KIND, int TM, bool WRITE_Q, int NW = 8, int TN = 512, bool B4 = false>
 hipError_t launch_ws(const void* lhs, const float* lhs_scale, const uint8_t* rhs,
-                     const float* rhs_scale, const int32_t* group_sizes, int M, int K, int N, int G,
+                     const void* rhs_scale, const int32_t* group_sizes, int M, int K, int N, int G,
                      void* out, bool out_bf16, uint8_t* q_out, float* scale_out, hipStream_t stream) {
-    const int ntiles_n = N / 512;
+    const int ntiles_n = N / TN;
     const int64_t items = max_work_items(M, G, TM);
     const int nblocks = (int)(items * ntiles_n);
     if (out_bf16)
-        hipLaunchKernelGGL((fp8_fwd_ws_kernel<KIND, true, TM, WRITE_Q, NW>), dim3(nblocks), dim3(64 * NW),
-                           0, stream, lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N, G, out,
-                           q_out, scale_out, ntiles_n, nblocks);
+        hipLaunchKernelGGL((fp8_fwd_ws_kernel<KIND, true, TM, WRITE_Q, NW, TN, B4>), dim3(nblocks),
+                           dim3(64 * NW), 0, stream, lhs, lhs_scale, rhs, rhs_scale, group_sizes, M,
+                           K, N, G, out, q_out, scale_out, ntiles_n, nblocks);
     else
-        hipLaunchKernelGGL((fp8_fwd_ws_kernel<KIND, false, TM, WRITE_Q, NW>), dim3(nblocks), dim3(64 * NW),
-                           0, stream, lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N, G, out,
-                           q_out, scale_out, ntiles_n, nblocks);
+        hipLaunchKernelGGL((fp8_fwd_ws_kernel<KIND, false, TM, WRITE_Q, NW, TN, B4>), dim3(nblocks),
+                           dim3(64 * NW), 0, stream, lhs, lhs_scale, rhs, rhs_scale, group_sizes, M,
+                           K, N, G, out, q_out, scale_out, ntiles_n, nblocks);
     return hipGetLastError();
+}
+
+// MXFP4 weights: 48-row tiles of the widest of 512/256/128 columns dividing N.
+template <int KIND>
+hipError_t launch_mxfp4_kind(const void* lhs, const float* lhs_scale, const uint8_t* rhs_q,
+                             const uint8_t* rhs_e8, const int32_t* group_sizes, int M, int K,
+                             int N, int G, void* out, bool out_bf16, hipStream_t stream) {
+    if (N % 512 == 0)
+        return launch_ws<KIND, 48, false, 16, 512, true>(lhs, lhs_scale, rhs_q, rhs_e8, group_sizes,
+                                                         M, K, N, G, out, out_bf16, nullptr,
+                                                         nullptr, stream);
+    if (N % 256 == 0)
+        return launch_ws<KIND, 48, false, 16, 256, true>(lhs, lhs_scale, rhs_q, rhs_e8, group_sizes,
+                                                         M, K, N, G, out, out_bf16, nullptr,
+                                                         nullptr, stream);
+    return launch_ws<KIND, 48, false, 16, 128, true>(lhs, lhs_scale, rhs_q, rhs_e8, group_sizes, M,
+                                                     K, N, G, out, out_bf16, nullptr, nullptr,
+                                                     stream);
 }
 
 template <int KIND, int WN, int TM, bool WRITE_Q, bool SWIGLU = false>
@@ -902,6 +955,23 @@ hipError_t launch_fp8_fwd_swiglu(const void* lhs, int lhs_kind, const float* lhs
         default:
             return launch_swiglu_kind<kLhsF32>(lhs, nullptr, rhs, rhs_scale, group_sizes, M, K, N,
                                                G, out, out_bf16, act_q, act_scale, stream);
+    }
+}
+
+hipError_t launch_fp8_mxfp4_fwd(const void* lhs, int lhs_kind, const float* lhs_scale,
+                                const uint8_t* rhs_q, const uint8_t* rhs_scale,
+                                const int32_t* group_sizes, int M, int K, int N, int G, void* out,
+                                bool out_bf16, hipStream_t stream) {
+    switch (lhs_kind) {
+        case kLhsE4M3:
+            return launch_mxfp4_kind<kLhsE4M3>(lhs, lhs_scale, rhs_q, rhs_scale, group_sizes, M, K,
+                                               N, G, out, out_bf16, stream);
+        case kLhsBF16:
+            return launch_mxfp4_kind<kLhsBF16>(lhs, nullptr, rhs_q, rhs_scale, group_sizes, M, K, N,
+                                               G, out, out_bf16, stream);
+        default:
+            return launch_mxfp4_kind<kLhsF32>(lhs, nullptr, rhs_q, rhs_scale, group_sizes, M, K, N,
+                                              G, out, out_bf16, stream);
     }
 }
 

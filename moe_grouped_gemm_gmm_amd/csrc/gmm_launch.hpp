@@ -18,6 +18,11 @@ hipError_t launch_quantize_lhs(const void* x, bool x_bf16, int64_t M, int64_t K,
 hipError_t launch_quantize_rhs(const void* w, bool w_bf16, int64_t G, int64_t K, int64_t N,
                                uint8_t* q, float* scale, hipStream_t stream);
 
+// MXFP4 weights in the forward's packed operand order (codes G*K*N/2 bytes,
+// E8M0 scales G*K*N/32 bytes).
+hipError_t launch_quantize_rhs_mxfp4(const void* w, bool w_bf16, int64_t G, int64_t K, int64_t N,
+                                     uint8_t* q, uint8_t* scale, hipStream_t stream);
+
 // lhs_kind: 0 = E4M3 codes + lhs_scale, 1 = bf16, 2 = fp32.
 hipError_t launch_fp8_fwd(const void* lhs, int lhs_kind, const float* lhs_scale,
                           const uint8_t* rhs, const float* rhs_scale,
@@ -31,6 +36,12 @@ hipError_t launch_fp8_fwd_swiglu(const void* lhs, int lhs_kind, const float* lhs
                                  const int32_t* group_sizes, int M, int K, int N, int G,
                                  void* out, bool out_bf16, uint8_t* act_q, float* act_scale,
                                  hipStream_t stream);
+
+// FP8 (1x128) LHS against packed MXFP4 weights.
+hipError_t launch_fp8_mxfp4_fwd(const void* lhs, int lhs_kind, const float* lhs_scale,
+                                const uint8_t* rhs_q, const uint8_t* rhs_scale,
+                                const int32_t* group_sizes, int M, int K, int N, int G, void* out,
+                                bool out_bf16, hipStream_t stream);
 
 hipError_t launch_bf16_fwd(const void* lhs, const void* rhs, const int32_t* group_sizes, int M,
                            int K, int N, int G, void* out, bool out_bf16, hipStream_t stream);

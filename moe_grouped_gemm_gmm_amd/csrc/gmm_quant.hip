@@ -191,6 +191,85 @@ __global__ __launch_bounds__(256) void quantize_rhs_kernel(const void* __restric
     if (t == 0) scale[blk] = s;
 }
 
+// --------------------------------------------------------- MXFP4 RHS --
+//
+// "实现差距：GMM Kernel（V1 vs V2）", sections 3.4 and 4.1: RHS weights in a
+// sub-byte type, MXFP4 first.  Format and conversion follow the OCP MX
+// specification v1.0: blocks of 32 consecutive k of one (expert, column)
+// share an E8M0 scale 2^(e-127) with e = floor(log2(max|w|)) - 2, clamped to
+// [-127, 127] (code 0 for an all-zero block); each element becomes the E2M1
+// value nearest to w / 2^e (ties to the even mantissa, clamped to +-6,
+// sign kept).
+//
+// Packed layout, the operand order of the forward's MFMA: per (expert g,
+// 16-column block, 128-K step) a 1 KB chunk of codes and a 64-byte chunk of
+// scales, chunk index c = (g * N/16 + n/16) * K/128 + k/128.  Lane
+// l = 16 * swap2((k % 128) / 32) + n % 16 (swap2 exchanges the two bits of a
+// 2-bit index) owns bytes c*1024 + 16l .. +15, holding the 32 codes of its
+// MX block in k order, two per byte, even k in the low nibble; scale byte
+// c*64 + l is that block's E8M0 code.  (With an FP4 first operand the MFMA
+// groups K so that lane group q pairs with K positions 64(q%2) + 16(q/2) +
+// {0..15, 32..47}; the forward stores the LHS with K runs 1<->2 and 5<->6 of
+// 16 exchanged, which makes lane group q's positions hold MX block swap2(q)
+// contiguously.)
+
+__device__ __forceinline__ int swap2(int q) { return ((q & 1) << 1) | (q >> 1); }
+
+__device__ __forceinline__ uint32_t e2m1_code(float y) {
+    const float a = fabsf(y);
+    const uint32_t c = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) +
+                       (a >= 3.5f) + (a > 5.0f);
+    return c | (signbit(y) ? 8u : 0u);
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void quantize_rhs_mxfp4_kernel(const void* __restrict__ w, int K,
+                                                                 int N, uint8_t* __restrict__ q,
+                                                                 uint8_t* __restrict__ scale) {
+    const int nkb = K / kQBlock, nb64 = N / 64;
+    const int blk = blockIdx.x;
+    const int g = blk / (nkb * nb64), kb = (blk / nb64) % nkb, nbl = blk % nb64;
+    const int t = threadIdx.x, n = nbl * 64 + (t & 63), sub = t >> 6;
+    const int64_t base = ((int64_t)g * K + kb * kQBlock + sub * 32) * N + n;
+    float v[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        if constexpr (BF16)
+            v[i] = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(w)[base + (int64_t)i * N] << 16);
+        else
+            v[i] = reinterpret_cast<const float*>(w)[base + (int64_t)i * N];
+    }
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) a = fmaxf(a, fabsf(v[i]));
+    uint32_t words[4] = {0u, 0u, 0u, 0u};
+    uint32_t e8 = 0;
+    if (a > 0.0f) {
+        int ex;
+        frexpf(a, &ex);                       // a = f 2^ex, f in [0.5, 1)
+        const int e = min(max(ex - 1 - 2, -127), 127);
+#pragma unroll
+        for (int i = 0; i < 32; ++i) words[i / 8] |= e2m1_code(ldexpf(v[i], -e)) << (4 * (i % 8));
+        e8 = (uint32_t)(e + 127);
+    }
+    const int64_t chunk = ((int64_t)g * (N / 16) + n / 16) * nkb + kb;
+    const int lane = 16 * swap2(sub) + (n & 15);
+    *reinterpret_cast<uint4*>(q + chunk * 1024 + lane * 16) = make_uint4(words[0], words[1], words[2], words[3]);
+    scale[chunk * 64 + lane] = (uint8_t)e8;
+}
+
+hipError_t launch_quantize_rhs_mxfp4(const void* w, bool w_bf16, int64_t G, int64_t K, int64_t N,
+                                     uint8_t* q, uint8_t* scale, hipStream_t stream) {
+    const int64_t blocks = G * (K / kQBlock) * (N / 64);
+    if (w_bf16)
+        hipLaunchKernelGGL(quantize_rhs_mxfp4_kernel<true>, dim3((unsigned)blocks), dim3(256), 0,
+                           stream, w, (int)K, (int)N, q, scale);
+    else
+        hipLaunchKernelGGL(quantize_rhs_mxfp4_kernel<false>, dim3((unsigned)blocks), dim3(256), 0,
+                           stream, w, (int)K, (int)N, q, scale);
+    return hipGetLastError();
+}
+
 hipError_t launch_quantize_rhs(const void* w, bool w_bf16, int64_t G, int64_t K, int64_t N,
                                uint8_t* q, float* scale, hipStream_t stream) {
     const int64_t blocks = G * (K / kQBlock) * (N / kQBlock);

@@ -66,3 +66,36 @@ def pack_rhs(q: np.ndarray) -> np.ndarray:
     G, K, N = q.shape
     a = q.reshape(G, K // 128, 4, 2, 16, N // 16, 16)  # g, kb, lc, h, e, nb16, lr
     return np.ascontiguousarray(a.transpose(0, 5, 1, 3, 2, 6, 4)).reshape(G, N // 16, K // 128, 2048)
+
+
+# Lane group q of the MXFP4 operand holds MX block swap2(q) of its 128-K step.
+_SWAP2 = np.array([0, 2, 1, 3])
+
+
+def unpack_mxfp4(qp: np.ndarray, sp: np.ndarray):
+    """Packed MXFP4 weights (include/gmm.h, gmm_quantize_rhs_mxfp4) ->
+    (codes [G, K, N] one per byte, E8M0 [G, K/32, N]).
+    qp: [G, N/16, K/128, 1024]; sp: [G, N/16, K/128, 64]."""
+    G, N16, KB, _ = qp.shape
+    b = qp.reshape(G, N16, KB, 4, 16, 16)                       # lane group q, column lr, byte
+    nib = np.stack([b & 15, b >> 4], axis=-1).reshape(G, N16, KB, 4, 16, 32)   # j = 2*byte + hi
+    blocks = np.empty_like(nib)
+    blocks[:, :, :, _SWAP2] = nib                                # index by MX block instead of q
+    codes = blocks.transpose(0, 2, 3, 5, 1, 4).reshape(G, KB * 128, N16 * 16)
+    s = sp.reshape(G, N16, KB, 4, 16)
+    sb = np.empty_like(s)
+    sb[:, :, :, _SWAP2] = s
+    e8 = sb.transpose(0, 2, 3, 1, 4).reshape(G, KB * 4, N16 * 16)
+    return codes, e8
+
+
+def pack_mxfp4(codes: np.ndarray, e8: np.ndarray):
+    """Inverse of unpack_mxfp4."""
+    G, K, N = codes.shape
+    KB, N16 = K // 128, N // 16
+    blocks = codes.reshape(G, KB, 4, 32, N16, 16).transpose(0, 4, 1, 2, 5, 3)   # g nb kb blk lr j
+    lanes = blocks[:, :, :, _SWAP2]                                             # by lane group q
+    pairs = lanes.reshape(G, N16, KB, 4, 16, 16, 2)
+    qp = (pairs[..., 0] | (pairs[..., 1] << 4)).astype(np.uint8).reshape(G, N16, KB, 1024)
+    s = e8.reshape(G, KB, 4, N16, 16).transpose(0, 3, 1, 2, 4)[:, :, :, _SWAP2]
+    return qp, np.ascontiguousarray(s).reshape(G, N16, KB, 64).astype(np.uint8)

@@ -30,7 +30,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_symbols()
-    assert len(names) == 10
+    assert len(names) == 12
     assert sorted(names) == sorted(gmm.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
@@ -91,6 +91,35 @@ def test_fp8_fwd_swiglu_rejections(lib, kw, status):
     assert swiglu(lib, **kw) == status
     if status:
         assert lib.gmm_last_error()
+
+
+def mx(lib, lhs=A, lhs_dt=1, lhs_scale=0, rhs=A, rhs_scale=A, gs=A, M=256, K=256, N=256, G=4,
+       out=A, out_dt=1):
+    return lib.gmm_fp8_mxfp4_fwd(P(lhs), lhs_dt, P(lhs_scale), P(rhs), P(rhs_scale), P(gs), M, K,
+                                 N, G, P(out), out_dt, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(lhs=0), NULL), (dict(rhs=0), NULL), (dict(rhs_scale=0), NULL), (dict(gs=0), NULL),
+    (dict(out=0), NULL), (dict(out=MIS), ALIGN), (dict(rhs_scale=MIS), ALIGN),
+    (dict(K=200), SHAPE), (dict(N=100), SHAPE), (dict(G=0), SHAPE), (dict(M=-1), SHAPE),
+    (dict(lhs_dt=2), NULL), (dict(lhs_scale=A), DTYPE), (dict(out_dt=2), DTYPE),
+    (dict(M=0), OK),
+])
+def test_fp8_mxfp4_fwd_rejections(lib, kw, status):
+    assert mx(lib, **kw) == status
+    if status:
+        assert lib.gmm_last_error()
+
+
+def test_quantize_mxfp4_rejections(lib):
+    r = lib.gmm_quantize_rhs_mxfp4
+    assert r(P(A), 1, 2, 128, 200, P(A), P(A), None) == SHAPE
+    assert r(P(A), 1, 2, 100, 128, P(A), P(A), None) == SHAPE
+    assert r(P(A), 1, 0, 128, 128, P(A), P(A), None) == SHAPE
+    assert r(P(A), 2, 2, 128, 128, P(A), P(A), None) == DTYPE
+    assert r(P(A), 0, 2, 128, 128, None, P(A), None) == NULL
+    assert r(P(A), 0, 2, 128, 128, P(A), P(MIS), None) == ALIGN
 
 
 def test_quantize_rejections(lib):
