@@ -801,16 +801,24 @@ hipError_t launch_ws(const void* lhs, const float* lhs_scale, const uint8_t* rhs
     return hipGetLastError();
 }
 
-// MXFP4 weights: 48-row tiles of the widest of 512/256/128 columns dividing N.
+// MXFP4 weights: 48-row tiles of the widest of 512/256/128 columns dividing N
+// (GMM_MXFP4_TN=<512|256|128> narrows it, for tile sweeps).
 template <int KIND>
 hipError_t launch_mxfp4_kind(const void* lhs, const float* lhs_scale, const uint8_t* rhs_q,
                              const uint8_t* rhs_e8, const int32_t* group_sizes, int M, int K,
                              int N, int G, void* out, bool out_bf16, hipStream_t stream) {
-    if (N % 512 == 0)
+    static const int forced_tn = [] {
+        const char* e = std::getenv("GMM_MXFP4_TN");
+        return e ? std::atoi(e) : 0;
+    }();
+    const int tn = (forced_tn == 128 || forced_tn == 256 || forced_tn == 512) && N % forced_tn == 0
+                       ? forced_tn
+                       : (N % 512 == 0 ? 512 : (N % 256 == 0 ? 256 : 128));
+    if (tn == 512)
         return launch_ws<KIND, 48, false, 16, 512, true>(lhs, lhs_scale, rhs_q, rhs_e8, group_sizes,
                                                          M, K, N, G, out, out_bf16, nullptr,
                                                          nullptr, stream);
-    if (N % 256 == 0)
+    if (tn == 256)
         return launch_ws<KIND, 48, false, 16, 256, true>(lhs, lhs_scale, rhs_q, rhs_e8, group_sizes,
                                                          M, K, N, G, out, out_bf16, nullptr,
                                                          nullptr, stream);
@@ -931,7 +939,12 @@ hipError_t launch_swiglu_kind(const void* lhs, const float* lhs_scale, const uin
                               const float* rhs_scale, const int32_t* group_sizes, int M, int K,
                               int N, int G, void* out, bool out_bf16, uint8_t* act_q,
                               float* act_scale, hipStream_t stream) {
-    if (max_work_items(M, G, 48) * (N / 256) <= device_cus())
+    static const int forced_tm = [] {   // GMM_SWIGLU_TM=<48|64>, for tile sweeps
+        const char* e = std::getenv("GMM_SWIGLU_TM");
+        return e ? std::atoi(e) : 0;
+    }();
+    const bool tm48 = forced_tm == 48 || (forced_tm != 64 && max_work_items(M, G, 48) * (N / 256) <= device_cus());
+    if (tm48)
         return launch_cfg<KIND, 64, 48, false, true>(lhs, lhs_scale, rhs, rhs_scale, group_sizes, M,
                                                      K, N, G, out, out_bf16, act_q, act_scale, stream);
     return launch_cfg<KIND, 64, 64, false, true>(lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K,

@@ -1,0 +1,237 @@
+"""Offline tile-configuration sweep for the grouped-matmul kernels.
+
+"GEMM Kernel 性能优化十问", Q8: the block/tile choice per phase was the
+largest single performance lever and was found by searching the tiling
+space per phase and shape; Q9.4: every candidate kernel must pass a
+numerical gate before its speed counts, first on a small problem, then on
+the real one.  This harness does that for the tile choices the kernels
+expose through environment variables (read once per process, so every
+candidate runs in a process of its own):
+
+  fp8_fwd, fp8_fwd_prequant   GMM_FP8_WS (warp-specialised or uniform kernel),
+                              GMM_FP8_WS_WAVES (8 or 16 waves),
+                              GMM_FP8_WN (16/32/64 columns per wave),
+                              GMM_FP8_TM (48- or 64-row tiles)
+  mxfp4_fwd                   GMM_MXFP4_TN (512/256/128-column tiles)
+  swiglu                      GMM_SWIGLU_TM (48- or 64-row tiles)
+
+Gate: a candidate's output must match the default configuration's output
+(itself parity-tested against the CPU oracle) within the FP8 tolerance,
+|a - b| <= 1e-3 + 1e-2 |b| element-wise, on the small problem and on the
+target problem; only gated candidates are timed (HIP graph replay, as in
+the benchmark).  The result is a JSON table with the fastest gated
+configuration; export its variables to use it.
+
+    python -m moe_grouped_gemm_gmm_amd.tune --phase fp8_fwd --shape 8192,2048,512,32
+"""
+import argparse
+import json
+import os
+import subprocess
+import sys
+import tempfile
+import time
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+PHASES = ("fp8_fwd", "fp8_fwd_prequant", "mxfp4_fwd", "swiglu")
+ATOL, RTOL = 1e-3, 1e-2
+
+
+def candidates(phase: str, N: int) -> List[Dict[str, str]]:
+    """Tile configurations of one phase for output width N (the first, empty,
+    one is the library's default choice)."""
+    if phase not in PHASES:
+        raise ValueError("unknown phase %r" % phase)
+    out: List[Dict[str, str]] = [{}]
+    if phase in ("fp8_fwd", "fp8_fwd_prequant"):
+        if N % 512 == 0:
+            for waves in ("16", "8"):
+                out.append({"GMM_FP8_WS": "1", "GMM_FP8_WS_WAVES": waves, "GMM_FP8_WN": "64",
+                            "GMM_FP8_TM": "48"})
+        for wn in ("64", "32", "16"):
+            if N % (8 * int(wn)) == 0:
+                for tm in ("48", "64"):
+                    out.append({"GMM_FP8_WS": "0", "GMM_FP8_WN": wn, "GMM_FP8_TM": tm})
+    elif phase == "mxfp4_fwd":
+        for tn in ("512", "256", "128"):
+            if N % int(tn) == 0:
+                out.append({"GMM_MXFP4_TN": tn})
+    else:
+        for tm in ("48", "64"):
+            out.append({"GMM_SWIGLU_TM": tm})
+    return out
+
+
+def gate_excess(out: np.ndarray, ref: np.ndarray) -> float:
+    """Largest amount by which |out - ref| exceeds atol + rtol |ref| (<= 0: pass;
+    inf when the shapes differ or a value is not finite)."""
+    if out.shape != ref.shape or not np.isfinite(out).all():
+        return float("inf")
+    return float(np.max(np.abs(out - ref) - (ATOL + RTOL * np.abs(ref)), initial=-np.inf))
+
+
+def env_name(env: Dict[str, str]) -> str:
+    return ",".join("%s=%s" % kv for kv in sorted(env.items())) or "default"
+
+
+# ------------------------------------------------------------------ worker --
+
+def _group_sizes(M: int, G: int, seed: int) -> np.ndarray:
+    r = np.random.default_rng([seed, 7])
+    return r.multinomial(M, np.full(G, 1.0 / G)).astype(np.int32)
+
+
+def _worker(phase: str, shape: Tuple[int, int, int, int], seed: int, steps: int,
+            save: Optional[str]) -> dict:
+    import torch
+    import moe_grouped_gemm_gmm_amd as gmm
+    M, K, N, G = shape
+    dev = torch.device("cuda:0")
+    gen = torch.Generator().manual_seed(seed)
+    x = torch.randn(M, K, generator=gen).to(torch.bfloat16).to(dev)
+    gs = torch.from_numpy(_group_sizes(M, G, seed)).to(dev)
+    wcols = 2 * N if phase == "swiglu" else N
+    w = (torch.randn(G, K, wcols, generator=gen) * 0.02).to(torch.bfloat16).to(dev)
+    out = torch.empty((M, N), dtype=torch.float32, device=dev)
+    if phase == "mxfp4_fwd":
+        q, s = gmm.gmm_quantize_rhs_mxfp4(w)
+        fn = lambda: gmm.gmm_fp8_mxfp4_fwd(x, q, s, gs, out=out)
+    else:
+        q, s = gmm.gmm_quantize_rhs(w)
+        if phase == "fp8_fwd":
+            fn = lambda: gmm.gmm_fp8_fwd(x, q, s, gs, out=out)
+        elif phase == "fp8_fwd_prequant":
+            ql, sl = gmm.gmm_quantize_lhs(x)
+            fn = lambda: gmm.gmm_fp8_fwd(ql, q, s, gs, lhs_scale=sl, out=out)
+        else:
+            fn = lambda: gmm.gmm_fp8_fwd_swiglu(x, q, s, gs, out=out)
+    del w
+    fn()
+    torch.cuda.synchronize()
+    if save:
+        np.save(save, out.cpu().numpy())
+    result = {"phase": phase, "shape": list(shape)}
+    if steps > 0:
+        stream = torch.cuda.Stream()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            fn()
+            torch.cuda.synchronize()
+            with torch.cuda.graph(graph, stream=stream):
+                for _ in range(steps):
+                    fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 0.06:     # caches warm, clock settled
+            graph.replay()
+            torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            start.record(stream)
+            graph.replay()
+            end.record(stream)
+        end.synchronize()
+        result["us"] = start.elapsed_time(end) * 1e3 / steps
+    return result
+
+
+# ------------------------------------------------------------------ driver --
+
+def run_candidate(phase: str, shape: Sequence[int], env: Dict[str, str], seed: int, steps: int,
+                  save: Optional[str], timeout: float = 300.0) -> dict:
+    """One candidate in a child process with its variables set; returns the
+    worker's JSON (with "error" on failure)."""
+    cmd = [sys.executable, "-m", "moe_grouped_gemm_gmm_amd.tune", "--worker", "--phase", phase,
+           "--shape", ",".join(str(v) for v in shape), "--seed", str(seed), "--steps", str(steps)]
+    if save:
+        cmd += ["--save", save]
+    full_env = dict(os.environ)
+    for k in ("GMM_FP8_WS", "GMM_FP8_WS_WAVES", "GMM_FP8_WN", "GMM_FP8_TM", "GMM_MXFP4_TN",
+              "GMM_SWIGLU_TM"):
+        full_env.pop(k, None)
+    full_env.update(env)
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    full_env["PYTHONPATH"] = root + os.pathsep + full_env.get("PYTHONPATH", "")
+    p = subprocess.run(cmd, env=full_env, capture_output=True, text=True, timeout=timeout)
+    try:
+        return json.loads(p.stdout.strip().splitlines()[-1])
+    except (IndexError, ValueError):
+        return {"error": (p.stderr or p.stdout)[-2000:], "returncode": p.returncode}
+
+
+def sweep(phase: str, shape: Sequence[int], seed: int = 0, steps: int = 200,
+          small_rows: int = 512, runner=run_candidate) -> dict:
+    """Staged gate (small problem, then the target) and timing of every
+    candidate; returns the table with the fastest gated configuration."""
+    M, K, N, G = shape
+    small = (min(M, small_rows), K, N, min(G, 4))
+    cands = candidates(phase, N)
+    rows = []
+    with tempfile.TemporaryDirectory() as tmp:
+        refs = {}
+        for stage, shp in (("small", small), ("target", tuple(shape))):
+            path = os.path.join(tmp, "ref_%s.npy" % stage)
+            r = runner(phase, shp, {}, seed, 0, path)
+            if "error" in r:
+                raise RuntimeError("default configuration failed at %s: %s" % (stage, r["error"]))
+            refs[stage] = np.load(path)
+        for i, env in enumerate(cands):
+            row = {"config": env_name(env), "env": env}
+            for stage, shp in (("small", small), ("target", tuple(shape))):
+                path = os.path.join(tmp, "c%d_%s.npy" % (i, stage))
+                r = runner(phase, shp, env, seed, steps if stage == "target" else 0, path)
+                if "error" in r:
+                    row["error"] = r["error"]
+                    row["gate_" + stage] = False
+                    break
+                exc = gate_excess(np.load(path), refs[stage])
+                row["gate_" + stage] = bool(exc <= 0)
+                row["excess_" + stage] = exc
+                if exc > 0:
+                    break
+                if stage == "target":
+                    row["us"] = r["us"]
+            rows.append(row)
+    gated = [r for r in rows if r.get("gate_target") and "us" in r]
+    best = min(gated, key=lambda r: r["us"]) if gated else None
+    default = next((r for r in rows if r["config"] == "default"), None)
+    return {"phase": phase, "shape": list(shape), "small_shape": list(small), "seed": seed,
+            "steps": steps, "tolerance": {"atol": ATOL, "rtol": RTOL}, "candidates": rows,
+            "best": best, "default_us": default.get("us") if default else None}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--phase", choices=PHASES, required=True)
+    ap.add_argument("--shape", required=True, help="M,K,N,G")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--out", help="write the JSON table here")
+    ap.add_argument("--worker", action="store_true", help=argparse.SUPPRESS)
+    ap.add_argument("--save", help=argparse.SUPPRESS)
+    a = ap.parse_args(argv)
+    shape = tuple(int(v) for v in a.shape.split(","))
+    if len(shape) != 4:
+        ap.error("--shape needs M,K,N,G")
+    if a.worker:
+        print(json.dumps(_worker(a.phase, shape, a.seed, a.steps, a.save)))
+        return 0
+    table = sweep(a.phase, shape, a.seed, a.steps)
+    text = json.dumps(table, indent=1)
+    if a.out:
+        with open(a.out, "w") as f:
+            f.write(text + "\n")
+    for r in table["candidates"]:
+        print("%-70s gate %s/%s  %s" % (r["config"], r.get("gate_small"), r.get("gate_target"),
+                                        "%.2f us" % r["us"] if "us" in r else r.get("error", "")[:60]),
+              flush=True)
+    best = table["best"]
+    print("best:", best["config"] if best else None, "%.2f us" % best["us"] if best else "")
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
