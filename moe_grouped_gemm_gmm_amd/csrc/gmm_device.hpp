@@ -71,7 +71,10 @@ __device__ __forceinline__ float quant_inv(float s) {
 
 // Four fp32 values (already multiplied by inv) -> four E4M3 codes, byte i = value i.
 __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
-    int r = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    // the first conversion fills bytes 0-1 and keeps the rest of its "old"
+    // operand, which the second conversion then overwrites: any register
+    // already live will do (here a's bits), so no zero has to be set up
+    int r = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __float_as_int(a), false);
     r = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, r, true);
     return (uint32_t)r;
 }
@@ -87,27 +90,32 @@ constexpr int kDppHalfMirror = 0x141;    // lane i <-> 7-i within each 8 lanes
 constexpr int kDppMirror = 0x140;        // lane i <-> 15-i within each 16 lanes
 
 template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+__device__ __forceinline__ uint32_t dpp(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
 }
 
-// Maximum over each aligned group of 8 lanes (register-only, no LDS).
-// Maximum over each aligned group of 4 lanes.
-__device__ __forceinline__ float max_over_4(float x) {
-    x = fmaxf(x, dpp<kDppXor1>(x));
-    return fmaxf(x, dpp<kDppXor2>(x));
+// Lane-group maxima of NON-NEGATIVE floats (abs-max reductions), register
+// only.  For x >= 0 the order of the bit patterns as unsigned integers is the
+// order of the values, so the reduction runs as unsigned max, whose identity
+// 0 lets each DPP move fold into the max instruction.
+template <int... CTRLS>
+__device__ __forceinline__ float max_nonneg_dpp(float x) {
+    uint32_t u = __float_as_uint(x);
+    ((u = max(u, dpp<CTRLS>(u))), ...);
+    return __uint_as_float(u);
 }
 
+// Maximum over each aligned group of 4 lanes (x >= 0).
+__device__ __forceinline__ float max_over_4(float x) { return max_nonneg_dpp<kDppXor1, kDppXor2>(x); }
+
+// Maximum over each aligned group of 8 lanes (x >= 0).
 __device__ __forceinline__ float max_over_8(float x) {
-    x = fmaxf(x, dpp<kDppXor1>(x));
-    x = fmaxf(x, dpp<kDppXor2>(x));
-    return fmaxf(x, dpp<kDppHalfMirror>(x));
+    return max_nonneg_dpp<kDppXor1, kDppXor2, kDppHalfMirror>(x);
 }
 
-// Maximum over each aligned group of 16 lanes.
+// Maximum over each aligned group of 16 lanes (x >= 0).
 __device__ __forceinline__ float max_over_16(float x) {
-    x = max_over_8(x);
-    return fmaxf(x, dpp<kDppMirror>(x));
+    return max_nonneg_dpp<kDppXor1, kDppXor2, kDppHalfMirror, kDppMirror>(x);
 }
 
 __device__ __forceinline__ int wave_incl_scan(int v) {
