@@ -1,0 +1,68 @@
+"""The kernels under HIP-graph capture, as the benchmark runs them: one graph
+holding the FP8 forward (with the in-kernel codes written out), the MXFP4
+forward, the fused gate+up forward and the bf16 forward / dX / tgmm is
+replayed several times with eager work and synchronisation in between;
+every replay must reproduce the eager results bit for bit (the kernels read
+group_sizes on the device and clear nothing with memset, so a replay is the
+same launch sequence)."""
+import pytest
+import torch
+
+import moe_grouped_gemm_gmm_amd as gmm
+import workloads
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def test_graph_replays_match_eager():
+    wl = workloads.custom(700, 512, 512, [200, 0, 300, 77], seed=31, w_std=0.05, with_dy=True)
+    x = wl.x.to(DEV)
+    w = wl.w.to(DEV)
+    dy = wl.dy.to(DEV)
+    gs = torch.from_numpy(wl.group_sizes).to(DEV)
+    M, K, N, G = wl.M, wl.K, wl.N, wl.G
+    rq, rs = gmm.gmm_quantize_rhs(w)
+    q4, s4 = gmm.gmm_quantize_rhs_mxfp4(w)
+    gq, gsc = gmm.gmm_quantize_rhs(torch.cat([w, w.flip(1)], dim=2).contiguous())
+    outs = {
+        "fp8": torch.empty((M, N), dtype=torch.bfloat16, device=DEV),
+        "q": torch.empty((M, K), dtype=torch.uint8, device=DEV),
+        "s": torch.empty((M, K // 128), dtype=torch.float32, device=DEV),
+        "mx": torch.empty((M, N), dtype=torch.float32, device=DEV),
+        "act": torch.empty((M, N), dtype=torch.bfloat16, device=DEV),
+        "bf": torch.empty((M, N), dtype=torch.bfloat16, device=DEV),
+        "dx": torch.empty((M, K), dtype=torch.bfloat16, device=DEV),
+        "dw": torch.empty((G, K, N), dtype=torch.float32, device=DEV),
+    }
+
+    def run():
+        gmm.gmm_fp8_fwd(x, rq, rs, gs, out=outs["fp8"], q_out=outs["q"], scale_out=outs["s"])
+        gmm.gmm_fp8_mxfp4_fwd(x, q4, s4, gs, out=outs["mx"])
+        gmm.gmm_fp8_fwd_swiglu(x, gq, gsc, gs, out=outs["act"])
+        gmm.gmm_bf16_fwd(x, w, gs, out=outs["bf"])
+        gmm.gmm_bf16_dx(dy, w, gs, out=outs["dx"])
+        gmm.tgmm_bf16(x, dy, gs, out=outs["dw"])
+
+    run()
+    torch.cuda.synchronize()
+    eager = {k: v.clone() for k, v in outs.items()}
+
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        run()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=stream):
+            run()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for v in outs.values():
+            v.zero_()                                   # eager work between replays
+        junk = (torch.randn(1 << 20, device=DEV) * 3).sum()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.isfinite(junk)
+        for k in outs:
+            assert torch.equal(outs[k], eager[k]), "replay %d: %s differs from the eager result" % (rep, k)
