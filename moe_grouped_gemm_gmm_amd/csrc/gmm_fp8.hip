@@ -47,6 +47,8 @@
 //    a lane owns one output row and four consecutive columns, which makes the
 //    row factor one scalar per block and lets the epilogue store 8-byte (bf16)
 //    or 16-byte (fp32) runs directly.
+#include <type_traits>
+
 #include "gmm_device.hpp"
 #include "gmm_launch.hpp"
 
@@ -783,6 +785,207 @@ __global__ __launch_bounds__(64 * NW, NW == 16 ? 4 : 2) void fp8_fwd_ws_kernel( 
     }
 }
 
+// ---------------------------------------------------------------------------
+// Row-resident variant for wide, shallow shapes (N a multiple of 512 with
+// several 512-column tiles, K <= 128 * KBM): one workgroup per 48-row item
+// sweeps every 512-column tile of N.  The producers quantise the item's rows
+// once, for all K, into LDS slots of their own (one per 128-K step), then
+// exit; the consumers run the K loop once per column tile against those
+// resident codes, streaming only the weights, and write each tile through
+// their own LDS staging rows.  Compared with one workgroup per (item, tile)
+// this quantises and loads the LHS once instead of N/512 times and pays one
+// prologue per item.  16 waves (8 consumers of 64 columns, 8 producers of one
+// row per lane).  The first column tile keeps one barrier per K step (step
+// k's codes ready); its loop is separate from the later tiles', which have
+// no barrier at all.
+template <int KIND, bool OUT_BF16, int KBM>
+__global__ __launch_bounds__(1024, 4) void fp8_fwd_wsn_kernel(
+    const void* __restrict__ lhs, const float* __restrict__ lhs_scale,
+    const uint8_t* __restrict__ rhs, const float* __restrict__ rhs_scale,
+    const int32_t* __restrict__ group_sizes, int M, int K, int N, int G, void* __restrict__ out,
+    int nblocks) {
+    constexpr int TM = 48, MB = TM / 16, NC = 8, CWID = 64, NBC = CWID / 16, TN = 512;
+    constexpr int kThr = 1024;
+    constexpr int OUT_BYTES = OUT_BF16 ? 2 : 4;
+    constexpr int kEpiRow = CWID * OUT_BYTES + 16;
+    struct SmemRes {
+        uint8_t a[KBM][TM][kLdsRow];     // resident codes, one slot per 128-K step
+        float sa[KBM][TM];               // their 1x128 scales
+        uint8_t epi[NC][TM][kEpiRow];    // per-consumer output staging
+    };
+    __shared__ WorkItem s_item;
+    __shared__ __attribute__((aligned(16))) SmemRes sm;
+
+    const int tid = threadIdx.x, lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int w = xcd_remap(blockIdx.x, nblocks);
+    if (wave == 0) {
+        const WorkItem it = find_work_item(group_sizes, G, M, TM, w);
+        if (lane == 0) s_item = it;
+    }
+    __syncthreads();
+    const WorkItem it = s_item;
+    if (it.g < 0) return;
+    if (it.g == G) {  // rows past the last group: zeros over all N
+        const int rows = it.hi - it.lo;
+        const int per_row = N * OUT_BYTES / 16;
+        for (int e = tid; e < rows * per_row; e += kThr) {
+            const int r = it.lo + e / per_row, c = e % per_row;
+            *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(out) + (int64_t)r * N * OUT_BYTES + c * 16) =
+                make_uint4(0, 0, 0, 0);
+        }
+        return;
+    }
+    const int g = it.g, row0 = it.tile * TM;
+    const int nkb = K / kTK, nnb = N / kQBlock, ntiles = N / TN;
+
+    if (wave >= NC) {
+        // ------------------------------------------------------ producer
+        const int p = wave - NC;
+        if (8 * p >= TM) {
+            for (int k = 0; k <= nkb; ++k) __syncthreads();
+            return;
+        }
+        const int qchunk = lane % kLPR;
+        const int qrow = 8 * p + lane / kLPR;
+        const int64_t qgrow = row0 + qrow;
+        const int64_t qlrow = qgrow >= it.lo && qgrow < it.hi ? qgrow : it.lo;
+        auto quant_store = [&](int kb, const RawA<KIND>& raw) {
+            uint2 codes[kNP];
+            const float s = quantize_raw<KIND>(raw, codes);
+#pragma unroll
+            for (int q = 0; q < kNP; ++q)
+                *reinterpret_cast<uint2*>(&sm.a[kb][qrow][qchunk * 8 + q * 8 * kLPR]) = codes[q];
+            if (qchunk == 0) sm.sa[kb][qrow] = s;
+        };
+        RawA<KIND> st0, st1;
+        load_raw<KIND>(st0, lhs, lhs_scale, qlrow, K, 0, qchunk);
+        quant_store(0, st0);
+        load_raw<KIND>(st1, lhs, lhs_scale, qlrow, K, min(1, nkb - 1), qchunk);
+        __builtin_amdgcn_sched_barrier(0);
+        load_raw<KIND>(st0, lhs, lhs_scale, qlrow, K, min(2, nkb - 1), qchunk);
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+        // step k: quantise k+1 (loaded two steps ago) into its slot, reload
+        // that stage with k+3
+        auto pstep = [&](int k, RawA<KIND>& sq) {
+            if (k + 1 < nkb) quant_store(k + 1, sq);
+            load_raw<KIND>(sq, lhs, lhs_scale, qlrow, K, min(k + 3, nkb - 1), qchunk);
+            __builtin_amdgcn_sched_barrier(0);
+            __syncthreads();
+        };
+        int k = 0;
+        for (; k + 1 < nkb; k += 2) {
+            pstep(k, st1);
+            pstep(k + 1, st0);
+        }
+        if (k < nkb) pstep(k, st1);
+        return;
+    }
+
+    // ---------------------------------------------------------- consumer
+    const int cw = wave;
+    const int lr = lane & 15, lc = lane >> 4;
+    v4f acc[MB][NBC];
+    v8i b[NBC];
+    // B block j of column tile t at K step kb: the expert's packed codes from
+    // a scalar base, a wave-uniform 32-bit offset (one expert's codes are
+    // N*K bytes) and the lane's 16 bytes
+    const uint8_t* __restrict__ rg = rhs + (int64_t)g * N * K;
+    const uint32_t lane_off = (uint32_t)lane * 16u;
+    auto load_b1 = [&](int j, int t, int kb) {
+        const uint32_t blk = (uint32_t)__builtin_amdgcn_readfirstlane(
+            (((t * TN + CWID * cw) / 16 + j) * nkb + kb) * 2048);
+        const uint4 lo = *reinterpret_cast<const uint4*>(rg + (blk + lane_off));
+        const uint4 hi = *reinterpret_cast<const uint4*>(rg + (blk + 1024u + lane_off));
+        b[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    };
+#pragma unroll
+    for (int j = 0; j < NBC; ++j) load_b1(j, 0, 0);
+    __syncthreads();
+    uint8_t (*ep)[kEpiRow] = sm.epi[cw];
+    // one column tile: K loop (with the producers' step barrier on the first
+    // tile only), then the epilogue through this wave's staging rows
+    auto tile = [&](int t, auto first_tile) {
+        constexpr bool FIRST = decltype(first_tile)::value;
+        const int cslot = (t * TN + CWID * cw) / kQBlock;
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+            for (int j = 0; j < NBC; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+        for (int kb = 0; kb < nkb; ++kb) {
+            const int nt = kb + 1 < nkb ? t : min(t + 1, ntiles - 1);
+            const int nk = kb + 1 < nkb ? kb + 1 : (t + 1 < ntiles ? 0 : kb);
+            const float sr = rhs_scale[((int64_t)g * nkb + kb) * nnb + cslot];
+            v8i af[MB];
+            float cf[MB];
+#pragma unroll
+            for (int i = 0; i < MB; ++i) {
+                af[i] = *reinterpret_cast<const v8i*>(&sm.a[kb][16 * i + lr][lc * 32]);
+                cf[i] = sm.sa[kb][16 * i + lr] * sr;
+            }
+#pragma unroll
+            for (int j = 0; j < NBC; ++j) {
+#pragma unroll
+                for (int i = 0; i < MB; ++i) {
+                    const v4f pr = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        b[j], af[i], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(pr[r], cf[i], acc[i][j][r]);
+                }
+                load_b1(j, nt, nk);
+            }
+            if constexpr (FIRST) __syncthreads();   // step kb + 1's codes ready
+        }
+        const int ncol0 = t * TN + CWID * cw;
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+            for (int j = 0; j < NBC; ++j) {
+                uint8_t* d = &ep[16 * i + lr][(16 * j + 4 * lc) * OUT_BYTES];
+                if constexpr (OUT_BF16)
+                    *reinterpret_cast<uint2*>(d) =
+                        make_uint2(pack_bf16x2(acc[i][j][0], acc[i][j][1]), pack_bf16x2(acc[i][j][2], acc[i][j][3]));
+                else
+                    *reinterpret_cast<float4*>(d) = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+            }
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        constexpr int LPRO = CWID * OUT_BYTES / 16;
+        constexpr int RPI = 64 / LPRO;
+        const int orow = lane / LPRO, ocol = (lane % LPRO) * 16;
+#pragma unroll
+        for (int q = 0; q < (TM + RPI - 1) / RPI; ++q) {
+            const int r = RPI * q + orow;
+            if (r >= TM) break;
+            const uint4 v = *reinterpret_cast<const uint4*>(&ep[r][ocol]);
+            const int grow = row0 + r;
+            if (grow >= it.lo && grow < it.hi)
+                *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(out) + ((int64_t)grow * N + ncol0) * OUT_BYTES + ocol) = v;
+        }
+        // the staging rows are rewritten by the next tile's epilogue only
+        // after this wave's reads above (program order within the wave)
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    };
+    tile(0, std::true_type{});
+    for (int t = 1; t < ntiles; ++t) tile(t, std::false_type{});
+}
+
+template <int KIND, int KBM>
+hipError_t launch_wsn(const void* lhs, const float* lhs_scale, const uint8_t* rhs,
+                      const float* rhs_scale, const int32_t* group_sizes, int M, int K, int N,
+                      int G, void* out, bool out_bf16, hipStream_t stream) {
+    const int nblocks = (int)max_work_items(M, G, 48);
+    if (out_bf16)
+        hipLaunchKernelGGL((fp8_fwd_wsn_kernel<KIND, true, KBM>), dim3(nblocks), dim3(1024), 0,
+                           stream, lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N, G, out,
+                           nblocks);
+    else
+        hipLaunchKernelGGL((fp8_fwd_wsn_kernel<KIND, false, KBM>), dim3(nblocks), dim3(1024), 0,
+                           stream, lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N, G, out,
+                           nblocks);
+    return hipGetLastError();
+}
+
 template <int KIND, int TM, bool WRITE_Q, int NW = 8, int TN = 512, bool B4 = false>
 hipError_t launch_ws(const void* lhs, const float* lhs_scale, const uint8_t* rhs,
                      const void* rhs_scale, const int32_t* group_sizes, int M, int K, int N, int G,
@@ -908,6 +1111,21 @@ hipError_t launch_kind(const void* lhs, const float* lhs_scale, const uint8_t* r
         const char* e = std::getenv("GMM_FP8_WS_WAVES");
         return e && std::atoi(e) == 8 ? 8 : 16;
     }();
+    // wide, shallow shapes: one workgroup per 48-row item sweeps all the
+    // 512-column tiles with its LHS rows quantised once and kept in LDS
+    // (GMM_FP8_WSN=0 turns this off, for comparison sweeps)
+    static const bool use_wsn = [] {
+        const char* e = std::getenv("GMM_FP8_WSN");
+        return !(e && std::atoi(e) == 0);
+    }();
+    if (use_wsn && forced_wn == 0 && forced_tm == 0 && N % 512 == 0 && N >= 1024 && K <= 1024 &&
+        (q_out == nullptr || KIND == kLhsE4M3)) {
+        if (K <= 512)
+            return launch_wsn<KIND, 4>(lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N, G, out,
+                                       out_bf16, stream);
+        return launch_wsn<KIND, 8>(lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N, G, out,
+                                   out_bf16, stream);
+    }
     if (use_ws && wn == 64 && tm == 48 && ws_waves == 16 && (q_out == nullptr || KIND == kLhsE4M3))
         return launch_ws<KIND, 48, false, 16>(lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N,
                                               G, out, out_bf16, q_out, scale_out, stream);

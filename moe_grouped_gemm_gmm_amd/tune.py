@@ -8,7 +8,9 @@ the real one.  This harness does that for the tile choices the kernels
 expose through environment variables (read once per process, so every
 candidate runs in a process of its own):
 
-  fp8_fwd, fp8_fwd_prequant   GMM_FP8_WS (warp-specialised or uniform kernel),
+  fp8_fwd, fp8_fwd_prequant   default (row-resident sweep of all column tiles
+                              for N >= 1024, K <= 1024; else as below),
+                              GMM_FP8_WS (warp-specialised or uniform kernel),
                               GMM_FP8_WS_WAVES (8 or 16 waves),
                               GMM_FP8_WN (16/32/64 columns per wave),
                               GMM_FP8_TM (48- or 64-row tiles)
@@ -149,8 +151,8 @@ def run_candidate(phase: str, shape: Sequence[int], env: Dict[str, str], seed: i
     if save:
         cmd += ["--save", save]
     full_env = dict(os.environ)
-    for k in ("GMM_FP8_WS", "GMM_FP8_WS_WAVES", "GMM_FP8_WN", "GMM_FP8_TM", "GMM_MXFP4_TN",
-              "GMM_SWIGLU_TM"):
+    for k in ("GMM_FP8_WS", "GMM_FP8_WS_WAVES", "GMM_FP8_WN", "GMM_FP8_TM", "GMM_FP8_WSN",
+              "GMM_MXFP4_TN", "GMM_SWIGLU_TM"):
         full_env.pop(k, None)
     full_env.update(env)
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
