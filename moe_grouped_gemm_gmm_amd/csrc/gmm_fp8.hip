@@ -797,17 +797,20 @@ __global__ __launch_bounds__(64 * NW, NW == 16 ? 4 : 2) void fp8_fwd_ws_kernel( 
 // prologue per item.  16 waves (8 consumers of 64 columns, 8 producers of one
 // row per lane).  The first column tile keeps one barrier per K step (step
 // k's codes ready); its loop is separate from the later tiles', which have
-// no barrier at all.
-template <int KIND, bool OUT_BF16, int KBM>
+// no barrier at all.  B4: MXFP4 weights as in fp8_fwd_ws_kernel (codes in
+// the MFMA's FP4 K grouping, E8M0 scales on the MFMA, LHS scale on the FMA).
+template <int KIND, bool OUT_BF16, int KBM, bool B4 = false>
 __global__ __launch_bounds__(1024, 4) void fp8_fwd_wsn_kernel(
     const void* __restrict__ lhs, const float* __restrict__ lhs_scale,
-    const uint8_t* __restrict__ rhs, const float* __restrict__ rhs_scale,
+    const uint8_t* __restrict__ rhs, const void* __restrict__ rhs_scale_v,
     const int32_t* __restrict__ group_sizes, int M, int K, int N, int G, void* __restrict__ out,
     int nblocks) {
     constexpr int TM = 48, MB = TM / 16, NC = 8, CWID = 64, NBC = CWID / 16, TN = 512;
     constexpr int kThr = 1024;
     constexpr int OUT_BYTES = OUT_BF16 ? 2 : 4;
     constexpr int kEpiRow = CWID * OUT_BYTES + 16;
+    const float* __restrict__ rhs_scale = reinterpret_cast<const float*>(rhs_scale_v);
+    const uint8_t* __restrict__ rhs_e8 = reinterpret_cast<const uint8_t*>(rhs_scale_v);
     struct SmemRes {
         uint8_t a[KBM][TM][kLdsRow];     // resident codes, one slot per 128-K step
         float sa[KBM][TM];               // their 1x128 scales
@@ -850,12 +853,18 @@ __global__ __launch_bounds__(1024, 4) void fp8_fwd_wsn_kernel(
         const int qrow = 8 * p + lane / kLPR;
         const int64_t qgrow = row0 + qrow;
         const int64_t qlrow = qgrow >= it.lo && qgrow < it.hi ? qgrow : it.lo;
+        // LDS position of the 8-byte run of codes k0 .. k0+7 of a row
+        auto lds_pos = [](int k0) {
+            if constexpr (!B4) return k0;
+            const int r = (k0 >> 4) & 3;
+            return (k0 & ~63) | ((r == 1 || r == 2 ? 3 - r : r) << 4) | (k0 & 15);
+        };
         auto quant_store = [&](int kb, const RawA<KIND>& raw) {
             uint2 codes[kNP];
             const float s = quantize_raw<KIND>(raw, codes);
 #pragma unroll
             for (int q = 0; q < kNP; ++q)
-                *reinterpret_cast<uint2*>(&sm.a[kb][qrow][qchunk * 8 + q * 8 * kLPR]) = codes[q];
+                *reinterpret_cast<uint2*>(&sm.a[kb][qrow][lds_pos(qchunk * 8 + q * 8 * kLPR)]) = codes[q];
             if (qchunk == 0) sm.sa[kb][qrow] = s;
         };
         RawA<KIND> st0, st1;
@@ -888,17 +897,25 @@ __global__ __launch_bounds__(1024, 4) void fp8_fwd_wsn_kernel(
     const int lr = lane & 15, lc = lane >> 4;
     v4f acc[MB][NBC];
     v8i b[NBC];
+    int be[NBC];
     // B block j of column tile t at K step kb: the expert's packed codes from
     // a scalar base, a wave-uniform 32-bit offset (one expert's codes are
-    // N*K bytes) and the lane's 16 bytes
-    const uint8_t* __restrict__ rg = rhs + (int64_t)g * N * K;
+    // N*K bytes, N*K/2 for MXFP4) and the lane's 16 bytes
+    const uint8_t* __restrict__ rg = rhs + (int64_t)g * N * K / (B4 ? 2 : 1);
+    const uint8_t* __restrict__ eg = B4 ? rhs_e8 + (int64_t)g * N * K / 32 : nullptr;
     const uint32_t lane_off = (uint32_t)lane * 16u;
     auto load_b1 = [&](int j, int t, int kb) {
-        const uint32_t blk = (uint32_t)__builtin_amdgcn_readfirstlane(
-            (((t * TN + CWID * cw) / 16 + j) * nkb + kb) * 2048);
-        const uint4 lo = *reinterpret_cast<const uint4*>(rg + (blk + lane_off));
-        const uint4 hi = *reinterpret_cast<const uint4*>(rg + (blk + 1024u + lane_off));
-        b[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        const uint32_t chunk = (uint32_t)__builtin_amdgcn_readfirstlane(
+            ((t * TN + CWID * cw) / 16 + j) * nkb + kb);
+        if constexpr (B4) {
+            const v4i lo = *reinterpret_cast<const v4i*>(rg + (chunk * 1024u + lane_off));
+            b[j] = __builtin_shufflevector(lo, lo, 0, 1, 2, 3, -1, -1, -1, -1);
+            be[j] = eg[chunk * 64u + (uint32_t)lane];
+        } else {
+            const uint4 lo = *reinterpret_cast<const uint4*>(rg + (chunk * 2048u + lane_off));
+            const uint4 hi = *reinterpret_cast<const uint4*>(rg + (chunk * 2048u + 1024u + lane_off));
+            b[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        }
     };
 #pragma unroll
     for (int j = 0; j < NBC; ++j) load_b1(j, 0, 0);
@@ -916,7 +933,7 @@ __global__ __launch_bounds__(1024, 4) void fp8_fwd_wsn_kernel(
         for (int kb = 0; kb < nkb; ++kb) {
             const int nt = kb + 1 < nkb ? t : min(t + 1, ntiles - 1);
             const int nk = kb + 1 < nkb ? kb + 1 : (t + 1 < ntiles ? 0 : kb);
-            const float sr = rhs_scale[((int64_t)g * nkb + kb) * nnb + cslot];
+            const float sr = B4 ? 1.0f : rhs_scale[((int64_t)g * nkb + kb) * nnb + cslot];
             v8i af[MB];
             float cf[MB];
 #pragma unroll
@@ -928,8 +945,13 @@ __global__ __launch_bounds__(1024, 4) void fp8_fwd_wsn_kernel(
             for (int j = 0; j < NBC; ++j) {
 #pragma unroll
                 for (int i = 0; i < MB; ++i) {
-                    const v4f pr = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        b[j], af[i], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+                    v4f pr;
+                    if constexpr (B4)
+                        pr = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                            b[j], af[i], v4f{0.f, 0.f, 0.f, 0.f}, 4, 0, 0, be[j], 0, 127);
+                    else
+                        pr = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                            b[j], af[i], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(pr[r], cf[i], acc[i][j][r]);
                 }
@@ -970,17 +992,17 @@ __global__ __launch_bounds__(1024, 4) void fp8_fwd_wsn_kernel(
     for (int t = 1; t < ntiles; ++t) tile(t, std::false_type{});
 }
 
-template <int KIND, int KBM>
+template <int KIND, int KBM, bool B4 = false>
 hipError_t launch_wsn(const void* lhs, const float* lhs_scale, const uint8_t* rhs,
-                      const float* rhs_scale, const int32_t* group_sizes, int M, int K, int N,
+                      const void* rhs_scale, const int32_t* group_sizes, int M, int K, int N,
                       int G, void* out, bool out_bf16, hipStream_t stream) {
     const int nblocks = (int)max_work_items(M, G, 48);
     if (out_bf16)
-        hipLaunchKernelGGL((fp8_fwd_wsn_kernel<KIND, true, KBM>), dim3(nblocks), dim3(1024), 0,
+        hipLaunchKernelGGL((fp8_fwd_wsn_kernel<KIND, true, KBM, B4>), dim3(nblocks), dim3(1024), 0,
                            stream, lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N, G, out,
                            nblocks);
     else
-        hipLaunchKernelGGL((fp8_fwd_wsn_kernel<KIND, false, KBM>), dim3(nblocks), dim3(1024), 0,
+        hipLaunchKernelGGL((fp8_fwd_wsn_kernel<KIND, false, KBM, B4>), dim3(nblocks), dim3(1024), 0,
                            stream, lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N, G, out,
                            nblocks);
     return hipGetLastError();
@@ -1017,6 +1039,19 @@ hipError_t launch_mxfp4_kind(const void* lhs, const float* lhs_scale, const uint
     const int tn = (forced_tn == 128 || forced_tn == 256 || forced_tn == 512) && N % forced_tn == 0
                        ? forced_tn
                        : (N % 512 == 0 ? 512 : (N % 256 == 0 ? 256 : 128));
+    // wide, shallow shapes: the row-resident sweep over all 512-column tiles
+    // (GMM_FP8_WSN=0 turns it off)
+    static const bool use_wsn = [] {
+        const char* e = std::getenv("GMM_FP8_WSN");
+        return !(e && std::atoi(e) == 0);
+    }();
+    if (use_wsn && forced_tn == 0 && N % 512 == 0 && N >= 1024 && K <= 1024) {
+        if (K <= 512)
+            return launch_wsn<KIND, 4, true>(lhs, lhs_scale, rhs_q, rhs_e8, group_sizes, M, K, N, G,
+                                             out, out_bf16, stream);
+        return launch_wsn<KIND, 8, true>(lhs, lhs_scale, rhs_q, rhs_e8, group_sizes, M, K, N, G, out,
+                                         out_bf16, stream);
+    }
     if (tn == 512)
         return launch_ws<KIND, 48, false, 16, 512, true>(lhs, lhs_scale, rhs_q, rhs_e8, group_sizes,
                                                          M, K, N, G, out, out_bf16, nullptr,
