@@ -10,8 +10,11 @@ resident in HBM, and the K timed steps are replayed from one HIP graph so
 that host launch overhead is not measured.
 
 The other calls of the library (bf16 forward baseline, tgmm, dX, standalone
-quantisers) are timed the same way and reported under "ops".  The oracle
-(CPU, fp64) is timed on the host for the same forward: "cpu_baseline".
+quantisers, pre-quantised and MXFP4-weight forwards, the fused gate+up
+forward) and the FP8 forward at the wo-layer shape (K=512, N=2048) and the
+production shape (M=65536, G=256) are timed the same way and reported under
+"ops".  The oracle (CPU, fp64) is timed on the host for the same forward:
+"cpu_baseline".
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -288,6 +291,23 @@ def main() -> int:
         ops["fp8_mxfp4_fwd"] = {"us": round(m_us, 3), "tflops": round(flops / (m_us * 1e-6) / 1e12, 2),
                                 "GB/s": round(mbytes / (m_us * 1e-6) / 1e9, 1),
                                 "frac_hbm": round(mbytes / (m_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+        # the other forward configurations: wo layer (K=512, N=2048; the
+        # row-resident sweep) and the production shape (M=65536, G=256,
+        # Zipf routing; 604 MB, beyond the 256 MB Infinity Cache)
+        for name, cfg, steps in (("fp8_fwd_wo", "wo", 100), ("fp8_fwd_full", "full", 20)):
+            wc = workloads.make(cfg, seed=0, with_dy=False)
+            xc = wc.x.to(dev)
+            gc = torch.from_numpy(wc.group_sizes).to(dev)
+            qc, sc = gmm.gmm_quantize_rhs(wc.w.to(dev))
+            oc = torch.empty((wc.M, wc.N), dtype=torch.bfloat16, device=dev)
+            c_us = graph_time_ms(lambda: gmm.gmm_fp8_fwd(xc, qc, sc, gc, out=oc), steps, 3) * 1e3
+            tot = int(wc.group_sizes.sum())
+            cbytes = (tot * wc.K * 2 + wc.G * wc.K * wc.N + wc.G * (wc.K // 128) * (wc.N // 128) * 4
+                      + wc.M * wc.N * 2 + wc.G * 4)
+            ops[name] = {"us": round(c_us, 3), "shape": [wc.M, wc.K, wc.N, wc.G],
+                         "tflops": round(2.0 * tot * wc.K * wc.N / (c_us * 1e-6) / 1e12, 2),
+                         "frac_hbm": round(cbytes / (c_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+            del wc, xc, gc, qc, sc, oc
         result["ops"] = ops
 
     if not args.no_cpu_baseline:
