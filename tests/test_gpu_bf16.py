@@ -139,3 +139,39 @@ def test_full_config_backward_sampled():
     sub_gs, _ = sample_rows_problem(gs, rows)
     ref = oracle.gmm_dx(dyf[rows], workloads.as_f32(wl.w), sub_gs)
     assert_bf16_parity(to_np64(dx)[rows], ref, "dx full sampled")
+
+
+def test_tgmm_many_groups_mixed_sizes_every_group_written():
+    """76 groups (more than one 64-lane scan chunk) of mixed sizes: over 2048
+    rows, a few hundred, a single row, empty, and sizes one below or at a
+    multiple of the 64-row reduction step.  Every dW[g] must be written (the
+    output starts as NaN), empty groups exactly zero, all matching the
+    oracle."""
+    sizes = [5, 2100, 0, 130, 600, 1, 0, 2048, 127, 511, 512, 128] + [3, 70, 0, 200] * 16
+    M = int(sum(sizes)) + 37
+    wl = workloads.custom(M, 128, 256, sizes, seed=97, with_dy=True)
+    G = len(sizes)
+    out = torch.full((G, 128, 256), float("nan"), dtype=torch.float32, device=DEV)
+    gmm.tgmm_bf16(wl.x.to(DEV), wl.dy.to(DEV), _gs(wl), out=out)
+    ref = oracle.tgmm(workloads.as_f32(wl.x), workloads.as_f32(wl.dy), wl.group_sizes)
+    o = to_np64(out)
+    assert not np.isnan(o).any()
+    for g in range(G):
+        if sizes[g] == 0:
+            assert (o[g] == 0).all()
+    assert_bf16_parity(o, ref, "tgmm mixed sizes")
+
+
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_dx_straddling_tiles_ragged_tail(out_dtype):
+    """dX over several 128-row tiles with straddling groups, a ragged tail and
+    K spanning several column tiles; rows past the total are zero."""
+    gs = [70, 0, 129, 200, 1, 0, 33]
+    M = int(sum(gs)) + 50
+    wl = workloads.custom(M, 512, 384, gs, seed=123, w_std=0.05, with_dy=True)
+    out = torch.full((M, 512), float("nan"), dtype=out_dtype, device=DEV)
+    gmm.gmm_bf16_dx(wl.dy.to(DEV), wl.w.to(DEV), _gs(wl), out=out)
+    ref = oracle.gmm_dx(workloads.as_f32(wl.dy), workloads.as_f32(wl.w), wl.group_sizes)
+    o = to_np64(out)
+    assert (o[int(sum(gs)):] == 0).all()
+    assert_bf16_parity(o, ref, "dx register path")
