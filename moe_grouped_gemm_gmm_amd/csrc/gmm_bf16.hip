@@ -98,17 +98,150 @@ __device__ __forceinline__ void put_trans(uint16_t* tile, const Frag4& f, Valid 
     }
 }
 
-// Offset of group g: sum of group_sizes[0..g), computed by one wave.
-__device__ inline int group_offset(const int32_t* __restrict__ group_sizes, int g) {
+// tgmm work placement.  A tgmm workgroup owns one 128 x 128 tile of one
+// group's dW and walks all of that group's rows, so its cost is the group's
+// size.  Blocks run on XCD b % 8 in the order of b.  By default logical ids
+// are remapped so that each XCD takes a contiguous run of groups in index
+// order, all T tiles of a group on one XCD (its rows of X and dY then fill
+// one L2).  Under a skewed routing (the largest group holding more than four
+// times the mean rows, e.g. Zipf-popular experts) that leaves some XCD with
+// far more rows than the others (1.4x the mean for the production routing),
+// so there
+//  - every group's T tiles are spread evenly over the 8 XCDs (XCD x takes
+//    tiles x*T/8 .. (x+1)*T/8 - 1: with N/128 column tiles per K tile a
+//    contiguous band of K tiles, so each column of X is still read by one
+//    XCD), and each XCD carries exactly an eighth of the work;
+//  - within an XCD, groups go in decreasing size class (>= 2048, >= 512,
+//    >= 128 rows, the rest; index order within a class), an approximation of
+//    longest-processing-time-first: each freed slot takes the next block, so
+//    long tiles started last would set the finishing time.
+// Every workgroup derives the same choice and the same order from
+// group_sizes alone (a size class depends only on the group's own size), so
+// both mappings are bijections from blocks to (group, tile).
+__device__ __forceinline__ int tgmm_size_class(int s) {
+    return s >= 2048 ? 0 : (s >= 512 ? 1 : (s >= 128 ? 2 : 3));
+}
+
+struct TgmmTile {
+    int g, t, row_lo, row_hi;
+};
+
+// The r-th group of size class cls (cls < 0: of all groups) in index order
+// among chunks whose sizes and inclusive row scans the caller supplies, with
+// its row range; true when found (r is decremented past each chunk).
+__device__ __forceinline__ bool tgmm_pick(int base, int G, int sz, int incl, int cls, int& r,
+                                          int& carry, TgmmTile& out) {
     const int lane = lane_id();
-    int acc = 0;
-    for (int base = 0; base < g; base += 64) {
-        const int i = base + lane;
-        acc += i < g ? group_sizes[i] : 0;
+    const bool in = base + lane < G && (cls < 0 || tgmm_size_class(sz) == cls);
+    const unsigned long long mask = __ballot(in);
+    const int n = __popcll(mask);
+    if (r < n) {
+        const unsigned long long sel = __ballot(in && __popcll(mask & ((1ull << lane) - 1ull)) == r);
+        const int src = __ffsll((long long)sel) - 1;
+        out.g = base + src;
+        out.row_lo = carry + lane_value(incl - sz, src);
+        out.row_hi = out.row_lo + lane_value(sz, src);
+        return true;
     }
+    r -= n;
+    carry += lane_value(incl, 63);
+    return false;
+}
+
+// One wave; every lane gets the result.  T = tiles per group, L = the
+// block's id after the default XCD remap.  Up to 256 groups the sizes and
+// their scans stay in registers (one load, one scan per 64 groups); beyond,
+// the second pass reads and scans them again.
+__device__ inline TgmmTile tgmm_tile(const int32_t* __restrict__ group_sizes, int G, int T, int L) {
+    const int lane = lane_id();
+    const bool inreg = G <= 256;
+    int szr[4], inc[4];
 #pragma unroll
-    for (int d = 1; d < 64; d <<= 1) acc += __shfl_xor(acc, d, 64);
-    return acc;
+    for (int c = 0; c < 4; ++c) {
+        const int g = 64 * c + lane;
+        szr[c] = (inreg && g < G) ? group_sizes[g] : 0;
+    }
+    // pass 1: class counts and the total
+    int cnt0 = 0, cnt1 = 0, cnt2 = 0, tot = 0;
+    auto count = [&](int base, int sz) {
+        const int c = base + lane < G ? tgmm_size_class(sz) : 4;
+        cnt0 += __popcll(__ballot(c == 0));
+        cnt1 += __popcll(__ballot(c == 1));
+        cnt2 += __popcll(__ballot(c == 2));
+    };
+    if (inreg) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            inc[c] = 0;
+            if (64 * c < G) {
+                inc[c] = wave_incl_scan(szr[c]);
+                count(64 * c, szr[c]);
+                tot += lane_value(inc[c], 63);
+            }
+        }
+    } else {
+        for (int base = 0; base < G; base += 64) {
+            const int sz = base + lane < G ? group_sizes[base + lane] : 0;
+            count(base, sz);
+            tot += lane_value(wave_incl_scan(sz), 63);
+        }
+    }
+    // skewed: some group holds more than four times the mean
+    const bool skewed = T % kNumXcd == 0 && [&] {
+        bool big = false;
+        if (inreg) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) big = big || (int64_t)szr[c] * G > 4 * (int64_t)tot;
+        } else {
+            for (int base = 0; base < G; base += 64) {
+                const int sz = base + lane < G ? group_sizes[base + lane] : 0;
+                big = big || (int64_t)sz * G > 4 * (int64_t)tot;
+            }
+        }
+        return __ballot(big) != 0ull;
+    }();
+    TgmmTile out;
+    out.g = -1;   // stays so only for blocks >= G * T (none are launched)
+    out.row_lo = out.row_hi = 0;
+    int r, cls = -1;   // cls < 0: index order
+    if (skewed) {
+        const int tx = T / kNumXcd, i = (int)blockIdx.x / kNumXcd;
+        r = i / tx;
+        out.t = ((int)blockIdx.x % kNumXcd) * tx + i % tx;
+        cls = 0;
+        if (r >= cnt0) { r -= cnt0; cls = 1;
+            if (r >= cnt1) { r -= cnt1; cls = 2;
+                if (r >= cnt2) { r -= cnt2; cls = 3; } } }
+    } else {
+        r = L / T;
+        out.t = L % T;
+        if (inreg) {   // group r itself: its rows from the scans in registers
+            const int c = r >> 6, l = r & 63;
+            int carry = 0;
+#pragma unroll
+            for (int cc = 0; cc < 3; ++cc)
+                if (cc < c) carry += lane_value(inc[cc], 63);
+            const int incl = c == 0 ? inc[0] : (c == 1 ? inc[1] : (c == 2 ? inc[2] : inc[3]));
+            const int sz = c == 0 ? szr[0] : (c == 1 ? szr[1] : (c == 2 ? szr[2] : szr[3]));
+            out.g = r;
+            out.row_lo = carry + lane_value(incl - sz, l);
+            out.row_hi = out.row_lo + lane_value(sz, l);
+            return out;
+        }
+    }
+    // pass 2: the group at that position and its rows
+    int carry = 0;
+    if (inreg) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            if (64 * c < G && tgmm_pick(64 * c, G, szr[c], inc[c], cls, r, carry, out)) break;
+    } else {
+        for (int base = 0; base < G; base += 64) {
+            const int sz = base + lane < G ? group_sizes[base + lane] : 0;
+            if (tgmm_pick(base, G, sz, wave_incl_scan(sz), cls, r, carry, out)) break;
+        }
+    }
+    return out;
 }
 
 constexpr int kTileElems = (kT * (kR + kPadD) > kR * (kT + kPadT)) ? kT * (kR + kPadD) : kR * (kT + kPadT);
@@ -131,16 +264,17 @@ __global__ __launch_bounds__(256, 2) void bf16_gemm_kernel(
     // ---- what this workgroup computes
     int g, row0, lo, hi, c0, red_lo, red_hi;
     if constexpr (MODE == kTgmm) {
-        g = L / (ntiles_r * ntiles_c);
-        row0 = ((L / ntiles_c) % ntiles_r) * kT;   // k tile
-        c0 = (L % ntiles_c) * kT;                  // n tile
         if (wave == 0) {
-            const int o = group_offset(group_sizes, g);
-            if (lane == 0) { s_info[0] = o; s_info[1] = o + group_sizes[g]; }
+            const TgmmTile tt = tgmm_tile(group_sizes, G, ntiles_r * ntiles_c, L);
+            if (lane == 0) { s_info[0] = tt.row_lo; s_info[1] = tt.row_hi; s_info[2] = tt.g; s_info[3] = tt.t; }
         }
         __syncthreads();
         red_lo = s_info[0];
         red_hi = s_info[1];
+        g = s_info[2];
+        if (g < 0) return;
+        row0 = (s_info[3] / ntiles_c) * kT;   // k tile
+        c0 = (s_info[3] % ntiles_c) * kT;     // n tile
         lo = row0;
         hi = row0 + kT;
     } else {

@@ -118,15 +118,23 @@ __device__ __forceinline__ float max_over_16(float x) {
     return max_nonneg_dpp<kDppXor1, kDppXor2, kDppHalfMirror, kDppMirror>(x);
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave, on DPP lane moves only
+// (no LDS-crossbar round trips): Hillis-Steele within each row of 16 lanes
+// (row_shr 1, 2, 4, 8; lanes shifted in from outside the row read 0), then
+// row_bcast:15 adds lane 15's sum (row 0) to row 1 and lane 47's (row 2) to
+// row 3, and row_bcast:31 adds lane 31's sum (rows 0-1) to rows 2 and 3.
 __device__ __forceinline__ int wave_incl_scan(int v) {
-    const int lane = lane_id();
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        int t = __shfl_up(v, d, 64);
-        if (lane >= d) v += t;
-    }
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);   // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);   // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);   // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);   // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);   // row_bcast:15 -> rows 1, 3
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);   // row_bcast:31 -> rows 2, 3
     return v;
 }
+
+// Value of v in lane `lane`, which must be the same in every lane of the wave.
+__device__ __forceinline__ int lane_value(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
 
 // ------------------------------------------------------- group metadata --
 // Work item w of a grouped kernel with row tiles of height tm (a multiple of
@@ -158,9 +166,9 @@ __device__ __forceinline__ WorkItem find_work_item(const int32_t* __restrict__ g
         const unsigned long long mask = __ballot(own);
         if (mask) {
             const int src = __ffsll((long long)mask) - 1;
-            const int go = __shfl(o, src, 64);
-            const int gsz = __shfl(s, src, 64);
-            const int gW = __shfl(W, src, 64);
+            const int go = lane_value(o, src);
+            const int gsz = lane_value(s, src);
+            const int gW = lane_value(W, src);
             const int t = go / tm + (w - gW);
             WorkItem it;
             it.g = base + src;
@@ -169,8 +177,8 @@ __device__ __forceinline__ WorkItem find_work_item(const int32_t* __restrict__ g
             it.hi = min(go + gsz, (t + 1) * tm);
             return it;
         }
-        carry_rows += __shfl(incl, 63, 64);
-        carry_items += __shfl(inclc, 63, 64);
+        carry_rows += lane_value(incl, 63);
+        carry_items += lane_value(inclc, 63);
     }
     WorkItem it;
     const int total = carry_rows;

@@ -38,8 +38,8 @@ __global__ __launch_bounds__(256) void group_metadata_kernel(const int32_t* __re
             const int o = carry_rows + incl - s;
             const int c = s > 0 ? (o + s - 1) / tm - o / tm + 1 : 0;
             if (g < G) offsets[g] = o;
-            carry_rows += __shfl(incl, 63, 64);
-            carry_items += __shfl(wave_incl_scan(c), 63, 64);
+            carry_rows += lane_value(incl, 63);
+            carry_items += lane_value(wave_incl_scan(c), 63);
         }
         if (lane == 0) {
             const int total = carry_rows;

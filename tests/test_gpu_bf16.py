@@ -144,14 +144,18 @@ def test_full_config_backward_sampled():
 def test_tgmm_many_groups_mixed_sizes_every_group_written():
     """76 groups (more than one 64-lane scan chunk) of mixed sizes: over 2048
     rows, a few hundred, a single row, empty, and sizes one below or at a
-    multiple of the 64-row reduction step.  Every dW[g] must be written (the
-    output starts as NaN), empty groups exactly zero, all matching the
-    oracle."""
+    multiple of the 64-row reduction step.  The largest group holds more
+    than four times the mean and there are 8 tiles per group, so tgmm takes
+    its skewed-routing placement (tiles spread over the XCDs, groups by size
+    class).  Every dW[g] must be written (the output starts as NaN), empty
+    groups exactly zero, all matching the oracle; the uniform-routing
+    placement is covered by the wi-shape backward test."""
     sizes = [5, 2100, 0, 130, 600, 1, 0, 2048, 127, 511, 512, 128] + [3, 70, 0, 200] * 16
     M = int(sum(sizes)) + 37
-    wl = workloads.custom(M, 128, 256, sizes, seed=97, with_dy=True)
+    assert max(sizes) * len(sizes) > 4 * sum(sizes)
+    wl = workloads.custom(M, 512, 256, sizes, seed=97, with_dy=True)
     G = len(sizes)
-    out = torch.full((G, 128, 256), float("nan"), dtype=torch.float32, device=DEV)
+    out = torch.full((G, 512, 256), float("nan"), dtype=torch.float32, device=DEV)
     gmm.tgmm_bf16(wl.x.to(DEV), wl.dy.to(DEV), _gs(wl), out=out)
     ref = oracle.tgmm(workloads.as_f32(wl.x), workloads.as_f32(wl.dy), wl.group_sizes)
     o = to_np64(out)
@@ -175,3 +179,30 @@ def test_dx_straddling_tiles_ragged_tail(out_dtype):
     o = to_np64(out)
     assert (o[int(sum(gs)):] == 0).all()
     assert_bf16_parity(o, ref, "dx register path")
+
+
+@pytest.mark.parametrize("skewed", [True, False])
+def test_tgmm_more_than_256_groups(skewed):
+    """300 groups: tgmm's placement reads the sizes chunk by chunk from
+    memory (above 256 groups), both with the skewed-routing placement (one
+    group of 3000 rows, 8 tiles per group) and the default one."""
+    r = workloads.rng(131, 0)
+    sizes = r.integers(0, 12, 300).astype(np.int64)
+    sizes[::17] = 0
+    if skewed:
+        sizes[211] = 3000
+    else:
+        sizes[211] = 20
+    assert (sizes.max() * len(sizes) > 4 * sizes.sum()) == skewed
+    M = int(sizes.sum()) + 5
+    wl = workloads.custom(M, 512, 256, sizes.tolist(), seed=133, with_dy=True)
+    G = len(sizes)
+    out = torch.full((G, 512, 256), float("nan"), dtype=torch.float32, device=DEV)
+    gmm.tgmm_bf16(wl.x.to(DEV), wl.dy.to(DEV), _gs(wl), out=out)
+    ref = oracle.tgmm(workloads.as_f32(wl.x), workloads.as_f32(wl.dy), wl.group_sizes)
+    o = to_np64(out)
+    assert not np.isnan(o).any()
+    for g in range(G):
+        if sizes[g] == 0:
+            assert (o[g] == 0).all()
+    assert_bf16_parity(o, ref, "tgmm 300 groups")
