@@ -195,3 +195,36 @@ def test_full_config_sampled_rows():
     qr, sr = oracle.quantize_rhs(workloads.as_f32(wl.w))
     ref = oracle.gmm_fp8(ql, sl, qr, sr, sub_gs)
     assert_fp8_parity(to_np64(out)[rows], ref, "full sampled")
+
+
+@pytest.mark.parametrize("name", ["wi", "wo"])
+def test_bench_launch_configuration(name):
+    """The call the benchmark times (bf16 LHS quantised in the kernel, bf16
+    out, no code output: the 16-wave warp-specialised kernel at the wi shape,
+    the row-resident sweep at the wo shape), full output against the oracle."""
+    wl = workloads.make(name, seed=0, with_dy=False)
+    out, _, _ = run_fp8(wl, torch.bfloat16)
+    ref, _, _ = oracle_fp8(wl)
+    o = to_np64(out)
+    total = int(wl.group_sizes.sum())
+    assert (o[total:] == 0).all()
+    assert_fp8_parity(o, ref, name + " bench launch")
+
+
+def test_bench_launch_configuration_full_sampled():
+    """The benchmark's production-shape call (M=65536, G=256, bf16 in and out,
+    no code output) on a row sample covering every group boundary."""
+    wl = workloads.make("full", seed=0, with_dy=False)
+    out, _, _ = run_fp8(wl, torch.bfloat16)
+    gs = wl.group_sizes
+    off = np.concatenate([[0], np.cumsum(gs)])
+    r = workloads.rng(101, 0)
+    rows = set(r.choice(wl.M, 512, replace=False).tolist())
+    for o in off[1:-1]:
+        rows.update([int(o) - 1, int(o)])
+    rows = np.array(sorted(x for x in rows if 0 <= x < wl.M))
+    sub_gs, _ = sample_rows_problem(gs, rows)
+    ql, sl = oracle.quantize_lhs(workloads.as_f32(wl.x)[rows])
+    qr, sr = oracle.quantize_rhs(workloads.as_f32(wl.w))
+    ref = oracle.gmm_fp8(ql, sl, qr, sr, sub_gs)
+    assert_fp8_parity(to_np64(out)[rows], ref, "full bench launch sampled")

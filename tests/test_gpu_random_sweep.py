@@ -2,7 +2,7 @@
 random M, K, N, G, group-size patterns (empty groups, size-1 groups, one
 dominant group, rows past the total), LHS dtype and output dtype, for the
 FP8-weight and MXFP4-weight forwards.  In-kernel codes and scales bit for
-bit; outputs within |gpu - ref| <= 1e-3 max(1, rms(ref)) + 1e-2 |ref| and
+bit (in the half of the FP8 cases that ask for them); outputs within |gpu - ref| <= 1e-3 max(1, rms(ref)) + 1e-2 |ref| and
 SQNR > 40 dB (the weights' scale is drawn up to N(0, 1), where outputs are
 ~20x those of the pages' normalised data, so the absolute term scales with
 the output's RMS); rows past the total zero.
@@ -55,16 +55,22 @@ def test_fp8_forward_random(seed):
     wl, out_dtype = random_problem(seed)
     rq, rs = gmm.gmm_quantize_rhs(wl.w.to(DEV))
     gs = torch.from_numpy(wl.group_sizes).to(DEV)
-    q = torch.zeros((wl.M, wl.K), dtype=torch.uint8, device=DEV)
-    s = torch.zeros((wl.M, wl.K // 128), dtype=torch.float32, device=DEV)
+    # every other case also asks for the in-kernel codes (a kernel variant of
+    # its own); the others run the kernels that write only the output
+    want_q = seed % 4 < 2
+    q = s = None
+    if want_q:
+        q = torch.zeros((wl.M, wl.K), dtype=torch.uint8, device=DEV)
+        s = torch.zeros((wl.M, wl.K // 128), dtype=torch.float32, device=DEV)
     out = torch.full((wl.M, wl.N), float("nan"), dtype=out_dtype, device=DEV)
     gmm.gmm_fp8_fwd(wl.x.to(DEV), rq, rs, gs, out=out, q_out=q, scale_out=s)
     torch.cuda.synchronize()
     ql, sl = oracle.quantize_lhs(workloads.as_f32(wl.x))
     qr, sr = oracle.quantize_rhs(workloads.as_f32(wl.w))
     total = int(wl.group_sizes.sum())
-    assert np.array_equal(q[:total].cpu().numpy(), ql[:total])
-    assert np.array_equal(s[:total].cpu().numpy(), sl[:total])
+    if want_q:
+        assert np.array_equal(q[:total].cpu().numpy(), ql[:total])
+        assert np.array_equal(s[:total].cpu().numpy(), sl[:total])
     ref = oracle.gmm_fp8(ql, sl, qr, sr, wl.group_sizes)
     o = to_np64(out)
     assert (o[total:] == 0).all()
