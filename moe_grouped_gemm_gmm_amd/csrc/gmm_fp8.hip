@@ -975,14 +975,26 @@ __global__ __launch_bounds__(1024, 4) void fp8_fwd_wsn_kernel(
         constexpr int LPRO = CWID * OUT_BYTES / 16;
         constexpr int RPI = 64 / LPRO;
         const int orow = lane / LPRO, ocol = (lane % LPRO) * 16;
+        // FP8 weights: the destination is a wave-uniform base per store plus
+        // one per-lane byte offset, so no per-row 64-bit address stays live
+        // across the tile loop (spilled, its reload made every store wait for
+        // all outstanding memory operations, the next tile's weights
+        // included).  MXFP4 keeps per-row addresses: the other form moves
+        // its register pressure into the K loop.
+        const uint32_t olane = (uint32_t)orow * (uint32_t)N * OUT_BYTES + (uint32_t)ocol;
+        uint8_t* const obase = reinterpret_cast<uint8_t*>(out) + ((int64_t)row0 * N + ncol0) * OUT_BYTES;
 #pragma unroll
         for (int q = 0; q < (TM + RPI - 1) / RPI; ++q) {
             const int r = RPI * q + orow;
             if (r >= TM) break;
             const uint4 v = *reinterpret_cast<const uint4*>(&ep[r][ocol]);
             const int grow = row0 + r;
-            if (grow >= it.lo && grow < it.hi)
-                *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(out) + ((int64_t)grow * N + ncol0) * OUT_BYTES + ocol) = v;
+            if (grow >= it.lo && grow < it.hi) {
+                if constexpr (B4)
+                    *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(out) + ((int64_t)grow * N + ncol0) * OUT_BYTES + ocol) = v;
+                else
+                    *reinterpret_cast<uint4*>(obase + (int64_t)(RPI * q) * N * OUT_BYTES + olane) = v;
+            }
         }
         // the staging rows are rewritten by the next tile's epilogue only
         // after this wave's reads above (program order within the wave)
