@@ -990,7 +990,7 @@ __global__ __launch_bounds__(1024, 4) void fp8_fwd_wsn_kernel(
             const uint4 v = *reinterpret_cast<const uint4*>(&ep[r][ocol]);
             const int grow = row0 + r;
             if (grow >= it.lo && grow < it.hi) {
-                if constexpr (B4)
+                if constexpr (B4 && !FIRST && OUT_BF16)
                     *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(out) + ((int64_t)grow * N + ncol0) * OUT_BYTES + ocol) = v;
                 else
                     *reinterpret_cast<uint4*>(obase + (int64_t)(RPI * q) * N * OUT_BYTES + olane) = v;
