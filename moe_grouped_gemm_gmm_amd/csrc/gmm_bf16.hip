@@ -246,8 +246,14 @@ __device__ inline TgmmTile tgmm_tile(const int32_t* __restrict__ group_sizes, in
 
 constexpr int kTileElems = (kT * (kR + kPadD) > kR * (kT + kPadT)) ? kT * (kR + kPadD) : kR * (kT + kPadT);
 
-template <int MODE, bool OUT_BF16>
-__global__ __launch_bounds__(256, 2) void bf16_gemm_kernel(
+// MINB: workgroups per CU the register allocation must allow.  3 (at most
+// 168 VGPRs; without the bound the forward with bf16 output takes 172) for
+// grids of several rounds, where more resident workgroups hide more memory
+// latency; 2 for grids that fit the chip at two per CU, where a third
+// resident workgroup only lets the dispatcher stack work unevenly (measured:
+// production-shape forward 279 -> 266 us with 3; wi forward 40.7 -> 42.2 us).
+template <int MODE, bool OUT_BF16, int MINB>
+__global__ __launch_bounds__(256, MINB) void bf16_gemm_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
     const int32_t* __restrict__ group_sizes, int M, int K, int N, int G, void* __restrict__ out,
     int ntiles_c, int ntiles_r, int nblocks) {
@@ -436,14 +442,22 @@ hipError_t launch_mode(const void* A, const void* B, const int32_t* group_sizes,
     }
     const uint16_t* a = reinterpret_cast<const uint16_t*>(A);
     const uint16_t* b = reinterpret_cast<const uint16_t*>(B);
-    if (out_bf16)
-        hipLaunchKernelGGL((bf16_gemm_kernel<MODE, true>), dim3((unsigned)nblocks), dim3(256), 0,
-                           stream, a, b, group_sizes, M, K, N, G, out, ntiles_c, ntiles_r,
-                           (int)nblocks);
-    else
-        hipLaunchKernelGGL((bf16_gemm_kernel<MODE, false>), dim3((unsigned)nblocks), dim3(256), 0,
-                           stream, a, b, group_sizes, M, K, N, G, out, ntiles_c, ntiles_r,
-                           (int)nblocks);
+    const dim3 grid((unsigned)nblocks), block(256);
+    if (nblocks <= 2 * (int64_t)device_cus()) {
+        if (out_bf16)
+            hipLaunchKernelGGL((bf16_gemm_kernel<MODE, true, 2>), grid, block, 0, stream, a, b,
+                               group_sizes, M, K, N, G, out, ntiles_c, ntiles_r, (int)nblocks);
+        else
+            hipLaunchKernelGGL((bf16_gemm_kernel<MODE, false, 2>), grid, block, 0, stream, a, b,
+                               group_sizes, M, K, N, G, out, ntiles_c, ntiles_r, (int)nblocks);
+    } else {
+        if (out_bf16)
+            hipLaunchKernelGGL((bf16_gemm_kernel<MODE, true, 3>), grid, block, 0, stream, a, b,
+                               group_sizes, M, K, N, G, out, ntiles_c, ntiles_r, (int)nblocks);
+        else
+            hipLaunchKernelGGL((bf16_gemm_kernel<MODE, false, 3>), grid, block, 0, stream, a, b,
+                               group_sizes, M, K, N, G, out, ntiles_c, ntiles_r, (int)nblocks);
+    }
     return hipGetLastError();
 }
 

@@ -1110,18 +1110,6 @@ hipError_t launch_wn(const void* lhs, const float* lhs_scale, const uint8_t* rhs
                                            G, out, out_bf16, q_out, scale_out, stream);
 }
 
-// Compute units of the current device (queried once).
-inline int device_cus() {
-    static const int cus = [] {
-        int dev = 0, n = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-            n = 256;
-        return n;
-    }();
-    return cus;
-}
-
 // Tile: the widest of 512/256/128 columns that divides N (fewest
 // re-quantisations of each LHS row); 48 rows when even the worst-case number
 // of 48-row workgroups fits on the chip at once (more of the chip busy, less

@@ -7,6 +7,18 @@
 
 namespace gmm {
 
+// Compute units of the current device (queried once).
+inline int device_cus() {
+    static const int cus = [] {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        return n;
+    }();
+    return cus;
+}
+
 hipError_t launch_group_metadata(const int32_t* group_sizes, int G, int M, int tm,
                                  int32_t* offsets, int32_t* work, int capacity,
                                  int32_t* num_work, hipStream_t stream);
