@@ -12,8 +12,8 @@ that host launch overhead is not measured.
 The other calls of the library (bf16 forward baseline, tgmm, dX, standalone
 quantisers, pre-quantised and MXFP4-weight forwards, the fused gate+up
 forward), the FP8 forward at the wo-layer shape (K=512, N=2048) and the
-production shape (M=65536, G=256), and tgmm and dX at the production shape
-are timed the same way and reported under "ops".  The oracle (CPU, fp64) is
+production shape (M=65536, G=256), and the bf16 forward, tgmm and dX at
+the production shape are timed the same way and reported under "ops".  The oracle (CPU, fp64) is
 timed on the host for the same forward: "cpu_baseline".
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -314,16 +314,18 @@ def main() -> int:
                 wbc = wc.w.to(torch.bfloat16).to(dev)
                 dwc = torch.empty((wc.G, wc.K, wc.N), dtype=torch.bfloat16, device=dev)
                 dxc = torch.empty((wc.M, wc.K), dtype=torch.bfloat16, device=dev)
+                yc = torch.empty((wc.M, wc.N), dtype=torch.bfloat16, device=dev)
                 bflops = 2.0 * tot * wc.K * wc.N
                 bbytes = tot * wc.K * 2 + tot * wc.N * 2 + wc.G * wc.K * wc.N * 2
-                for bname, fn in (("tgmm_bf16_full", lambda: gmm.tgmm_bf16(xc, dyc, gc, out=dwc)),
+                for bname, fn in (("bf16_fwd_full", lambda: gmm.gmm_bf16_fwd(xc, wbc, gc, out=yc)),
+                                  ("tgmm_bf16_full", lambda: gmm.tgmm_bf16(xc, dyc, gc, out=dwc)),
                                   ("dx_bf16_full", lambda: gmm.gmm_bf16_dx(dyc, wbc, gc, out=dxc))):
                     b_us = graph_time_ms(fn, steps, 3) * 1e3
                     ops[bname] = {"us": round(b_us, 3), "shape": [wc.M, wc.K, wc.N, wc.G],
                                   "tflops": round(bflops / (b_us * 1e-6) / 1e12, 2),
                                   "frac_bf16_peak": round(bflops / (b_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4),
                                   "frac_hbm": round(bbytes / (b_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
-                del dyc, wbc, dwc, dxc
+                del dyc, wbc, dwc, dxc, yc
             del wc, xc, gc, qc, sc, oc
         result["ops"] = ops
 

@@ -246,12 +246,14 @@ __device__ inline TgmmTile tgmm_tile(const int32_t* __restrict__ group_sizes, in
 
 constexpr int kTileElems = (kT * (kR + kPadD) > kR * (kT + kPadT)) ? kT * (kR + kPadD) : kR * (kT + kPadT);
 
-// MINB: workgroups per CU the register allocation must allow.  3 (at most
-// 168 VGPRs; without the bound the forward with bf16 output takes 172) for
-// grids of several rounds, where more resident workgroups hide more memory
-// latency; 2 for grids that fit the chip at two per CU, where a third
-// resident workgroup only lets the dispatcher stack work unevenly (measured:
-// production-shape forward 279 -> 266 us with 3; wi forward 40.7 -> 42.2 us).
+// MINB: the minimum waves per SIMD the register allocation must allow (the
+// second launch bound); with one wave per SIMD per workgroup it is also the
+// number of workgroups a CU can hold.  3 (at most 168 VGPRs; without the
+// bound the forward with bf16 output takes 172) for grids of several rounds,
+// where more resident workgroups hide more memory latency; 2 for grids that
+// fit the chip at two per CU, where a third resident workgroup only lets the
+// dispatcher stack work unevenly (measured: production-shape forward 284 ->
+// 264 us with 3; wi forward 40.7 -> 42.2 us).
 template <int MODE, bool OUT_BF16, int MINB>
 __global__ __launch_bounds__(256, MINB) void bf16_gemm_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
