@@ -206,3 +206,19 @@ def test_tgmm_more_than_256_groups(skewed):
         if sizes[g] == 0:
             assert (o[g] == 0).all()
     assert_bf16_parity(o, ref, "tgmm 300 groups")
+
+
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_bf16_fwd_multi_round_grid(out_dtype):
+    """A forward grid of more than two workgroups per CU (4096 rows, 2048
+    columns: 624 blocks), which takes the variant compiled for three resident
+    workgroups per CU; straddling groups, an empty one and a ragged tail."""
+    gs = [700, 0, 1313, 1, 1000, 999]
+    M = int(sum(gs)) + 83
+    wl = workloads.custom(M, 256, 2048, gs, seed=211, w_std=0.05)
+    out = torch.full((M, 2048), float("nan"), dtype=out_dtype, device=DEV)
+    gmm.gmm_bf16_fwd(wl.x.to(DEV), wl.w.to(DEV), _gs(wl), out=out)
+    ref = oracle.gmm(workloads.as_f32(wl.x), workloads.as_f32(wl.w), wl.group_sizes)
+    o = to_np64(out)
+    assert (o[int(sum(gs)):] == 0).all()
+    assert_bf16_parity(o, ref, "bf16 fwd multi-round")
