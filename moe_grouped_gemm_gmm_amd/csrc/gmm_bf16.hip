@@ -19,6 +19,8 @@
 // memory and read transposed with ds_read_b64_tr_b16, the in-LDS transpose of
 // gfx950.  tgmm walks the expert's rows 64 at a time, so its reduction tile
 // is 64 rows while the forward's is 64 K-columns.
+#include <cstdlib>
+
 #include "gmm_device.hpp"
 #include "gmm_launch.hpp"
 
@@ -445,7 +447,14 @@ hipError_t launch_mode(const void* A, const void* B, const int32_t* group_sizes,
     const uint16_t* a = reinterpret_cast<const uint16_t*>(A);
     const uint16_t* b = reinterpret_cast<const uint16_t*>(B);
     const dim3 grid((unsigned)nblocks), block(256);
-    if (nblocks <= 2 * (int64_t)device_cus()) {
+    // GMM_BF16_MINB=<2|3> forces the choice (for tile sweeps)
+    static const int forced_minb = [] {
+        const char* e = std::getenv("GMM_BF16_MINB");
+        const int v = e ? std::atoi(e) : 0;
+        return v == 2 || v == 3 ? v : 0;
+    }();
+    const bool two = forced_minb ? forced_minb == 2 : nblocks <= 2 * (int64_t)device_cus();
+    if (two) {
         if (out_bf16)
             hipLaunchKernelGGL((bf16_gemm_kernel<MODE, true, 2>), grid, block, 0, stream, a, b,
                                group_sizes, M, K, N, G, out, ntiles_c, ntiles_r, (int)nblocks);

@@ -16,6 +16,9 @@ candidate runs in a process of its own):
                               GMM_FP8_TM (48- or 64-row tiles)
   mxfp4_fwd                   GMM_MXFP4_TN (512/256/128-column tiles)
   swiglu                      GMM_SWIGLU_TM (48- or 64-row tiles)
+  bf16_fwd, tgmm, dx          GMM_BF16_MINB (registers for 2 or 3 resident
+                              workgroups per CU; default: 2 when the grid
+                              fits the chip at two per CU, else 3)
 
 Gate: a candidate's output must match the default configuration's output
 (itself parity-tested against the CPU oracle) within the FP8 tolerance,
@@ -37,7 +40,8 @@ from typing import Dict, List, Optional, Sequence, Tuple
 
 import numpy as np
 
-PHASES = ("fp8_fwd", "fp8_fwd_prequant", "mxfp4_fwd", "swiglu")
+PHASES = ("fp8_fwd", "fp8_fwd_prequant", "mxfp4_fwd", "swiglu", "bf16_fwd", "tgmm", "dx")
+BF16_PHASES = ("bf16_fwd", "tgmm", "dx")
 ATOL, RTOL = 1e-3, 1e-2
 
 
@@ -60,9 +64,12 @@ def candidates(phase: str, N: int) -> List[Dict[str, str]]:
         for tn in ("512", "256", "128"):
             if N % int(tn) == 0:
                 out.append({"GMM_MXFP4_TN": tn})
-    else:
+    elif phase == "swiglu":
         for tm in ("48", "64"):
             out.append({"GMM_SWIGLU_TM": tm})
+    else:
+        for minb in ("2", "3"):
+            out.append({"GMM_BF16_MINB": minb})
     return out
 
 
@@ -97,7 +104,17 @@ def _worker(phase: str, shape: Tuple[int, int, int, int], seed: int, steps: int,
     wcols = 2 * N if phase == "swiglu" else N
     w = (torch.randn(G, K, wcols, generator=gen) * 0.02).to(torch.bfloat16).to(dev)
     out = torch.empty((M, N), dtype=torch.float32, device=dev)
-    if phase == "mxfp4_fwd":
+    if phase in BF16_PHASES:
+        dy = torch.randn(M, N, generator=gen).to(torch.bfloat16).to(dev)
+        if phase == "bf16_fwd":
+            fn = lambda: gmm.gmm_bf16_fwd(x, w, gs, out=out)
+        elif phase == "tgmm":
+            out = torch.empty((G, K, N), dtype=torch.float32, device=dev)
+            fn = lambda: gmm.tgmm_bf16(x, dy, gs, out=out)
+        else:
+            out = torch.empty((M, K), dtype=torch.float32, device=dev)
+            fn = lambda: gmm.gmm_bf16_dx(dy, w, gs, out=out)
+    elif phase == "mxfp4_fwd":
         q, s = gmm.gmm_quantize_rhs_mxfp4(w)
         fn = lambda: gmm.gmm_fp8_mxfp4_fwd(x, q, s, gs, out=out)
     else:
@@ -109,7 +126,8 @@ def _worker(phase: str, shape: Tuple[int, int, int, int], seed: int, steps: int,
             fn = lambda: gmm.gmm_fp8_fwd(ql, q, s, gs, lhs_scale=sl, out=out)
         else:
             fn = lambda: gmm.gmm_fp8_fwd_swiglu(x, q, s, gs, out=out)
-    del w
+    if phase not in BF16_PHASES:
+        del w
     fn()
     torch.cuda.synchronize()
     if save:
@@ -152,7 +170,7 @@ def run_candidate(phase: str, shape: Sequence[int], env: Dict[str, str], seed: i
         cmd += ["--save", save]
     full_env = dict(os.environ)
     for k in ("GMM_FP8_WS", "GMM_FP8_WS_WAVES", "GMM_FP8_WN", "GMM_FP8_TM", "GMM_FP8_WSN",
-              "GMM_MXFP4_TN", "GMM_SWIGLU_TM"):
+              "GMM_MXFP4_TN", "GMM_SWIGLU_TM", "GMM_BF16_MINB"):
         full_env.pop(k, None)
     full_env.update(env)
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))

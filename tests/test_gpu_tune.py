@@ -1,6 +1,6 @@
-"""The tile sweep on the GPU: every candidate of a small MXFP4 and fused
-gate+up sweep passes the staged gate against the default configuration,
-and a fastest configuration is reported."""
+"""The tile sweep on the GPU: every candidate of a small MXFP4, fused
+gate+up and tgmm sweep passes the staged gate against the default
+configuration, and a fastest configuration is reported."""
 import pytest
 
 from moe_grouped_gemm_gmm_amd import tune
@@ -11,6 +11,7 @@ pytestmark = pytest.mark.gpu
 @pytest.mark.parametrize("phase,shape", [
     ("mxfp4_fwd", (700, 256, 1024, 6)),
     ("swiglu", (600, 256, 256, 4)),
+    ("tgmm", (700, 256, 256, 6)),
 ])
 def test_small_sweep(phase, shape):
     t = tune.sweep(phase, shape, steps=20, small_rows=256)

@@ -22,6 +22,8 @@ def test_candidates_per_phase():
     assert [e.get("GMM_MXFP4_TN") for e in tune.candidates("mxfp4_fwd", 384)] == [None, "128"]
     assert [e.get("GMM_MXFP4_TN") for e in tune.candidates("mxfp4_fwd", 1024)] == [None, "512", "256", "128"]
     assert [e.get("GMM_SWIGLU_TM") for e in tune.candidates("swiglu", 512)] == [None, "48", "64"]
+    for phase in ("bf16_fwd", "tgmm", "dx"):
+        assert [e.get("GMM_BF16_MINB") for e in tune.candidates(phase, 512)] == [None, "2", "3"]
     names = [tune.env_name(e) for e in tune.candidates("fp8_fwd", 512)]
     assert len(set(names)) == len(names) and names[0] == "default"
     with pytest.raises(ValueError):
