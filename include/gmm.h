@@ -16,8 +16,19 @@
  *    device (the host never synchronises).  Contract: every s_g >= 0 and
  *    s_0 + ... + s_{G-1} <= M.  Rows at or past that total are written as
  *    zeros by the calls that produce rows ("实现差距：GMM Kernel（V1 vs V2）",
- *    section 3.6).  A total above M is outside the contract (rows past M are
- *    never touched, results are unspecified).
+ *    section 3.6).  Sizes outside the contract never make a kernel read or
+ *    write outside the caller's buffers: a negative size is read as 0 and
+ *    every group's rows are clipped to [0, M) (results are then those of the
+ *    clipped groups, and the call's device status says what was wrong).
+ *  - Workspace: every grouped call takes `ws`, a device buffer of at least
+ *    gmm_workspace_bytes(op, M, K, N, G) bytes, 16-byte aligned, owned by
+ *    the caller, needing no initialisation.  The call writes int32 word 0 of
+ *    ws with its device status: 0, or an OR of GMM_DEV_SUM_GT_M and
+ *    GMM_DEV_NEGATIVE_SIZE (group_sizes broke the contract).  Read it with
+ *    gmm_device_status after the call.  Calls that share a workspace and may
+ *    run at the same time race on it (the kernels' results are unaffected;
+ *    only the status word is).  A missing or too small workspace is
+ *    GMM_ERR_WORKSPACE.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only
  *    enqueues work on it and returns.
  *  - Inputs must be finite.  A quantisation block whose non-zero abs-max is
@@ -51,8 +62,24 @@ typedef enum {
     GMM_ERR_SHAPE = 2,     /* a size is out of range or not a multiple of 128 */
     GMM_ERR_ALIGN = 3,     /* a pointer is not 16-byte aligned */
     GMM_ERR_DTYPE = 4,     /* unsupported dtype for this argument */
+    GMM_ERR_WORKSPACE = 5, /* ws is NULL or smaller than gmm_workspace_bytes() */
     GMM_ERR_HIP = 6        /* the HIP runtime reported an error at launch */
 } gmm_status;
+
+/* Operations, for gmm_workspace_bytes. */
+typedef enum {
+    GMM_OP_METADATA = 0,       /* gmm_group_metadata */
+    GMM_OP_FP8_FWD = 1,        /* gmm_fp8_fwd */
+    GMM_OP_FP8_FWD_SWIGLU = 2, /* gmm_fp8_fwd_swiglu */
+    GMM_OP_FP8_MXFP4_FWD = 3,  /* gmm_fp8_mxfp4_fwd */
+    GMM_OP_BF16_FWD = 4,       /* gmm_bf16_fwd */
+    GMM_OP_TGMM = 5,           /* tgmm_bf16 */
+    GMM_OP_DX = 6              /* gmm_bf16_dx */
+} gmm_op;
+
+/* Bits of the device status word a grouped call writes into its workspace. */
+#define GMM_DEV_SUM_GT_M 1       /* the sizes (negative ones read as 0) sum past M */
+#define GMM_DEV_NEGATIVE_SIZE 2  /* some group size is negative */
 
 typedef enum {
     GMM_F32 = 0,           /* IEEE binary32 */
@@ -65,6 +92,21 @@ typedef enum {
 
 GMM_API const char *gmm_status_string(int status);
 GMM_API const char *gmm_last_error(void);
+
+/*
+ * gmm_workspace_bytes -- bytes of workspace the grouped call `op` (a gmm_op)
+ *   needs for this shape (today 256 for every op: the status block); 0 for
+ *   an unknown op.  Sizes are not checked here.
+ */
+GMM_API size_t gmm_workspace_bytes(int op, int64_t M, int64_t K, int64_t N, int64_t G);
+
+/*
+ * gmm_device_status -- the device status word the last grouped call wrote
+ *   into ws (0 = group_sizes kept the contract; else GMM_DEV_* bits), copied
+ *   to *status once the work queued on `stream` before it has finished.
+ *   Unlike every other call this one synchronises the host with the stream.
+ */
+GMM_API int gmm_device_status(const void *ws, int32_t *status, void *stream);
 
 /*
  * gmm_group_metadata -- the device-side work list every grouped kernel
@@ -80,12 +122,15 @@ GMM_API const char *gmm_last_error(void);
  * offsets:  device int32 [G+1], exclusive prefix sums of group_sizes.
  * work:     device int32 [capacity][4].
  * num_work: device int32 [1], number of entries written.
+ * Group rows are the clipped ranges of the conventions above; offsets hold
+ * their first rows, clipped to M, and offsets[G] the clipped total.
  * capacity must be >= ceil(M/tile_m) + G + 1; tile_m a multiple of 16 in
- * [16, 1024].
+ * [16, 1024].  ws: as for every grouped call (GMM_OP_METADATA).
  */
 GMM_API int gmm_group_metadata(const int32_t *group_sizes, int64_t G, int64_t M,
                        int64_t tile_m, int32_t *offsets, int32_t *work,
-                       int64_t capacity, int32_t *num_work, void *stream);
+                       int64_t capacity, int32_t *num_work, void *ws, size_t ws_bytes,
+                       void *stream);
 
 /*
  * gmm_quantize_lhs -- 1x128 dynamic quantisation of the activations.
@@ -116,6 +161,33 @@ GMM_API int gmm_quantize_lhs(const void *x, int x_dtype, int64_t M, int64_t K,
  */
 GMM_API int gmm_quantize_rhs(const void *w, int w_dtype, int64_t G, int64_t K,
                      int64_t N, uint8_t *q, float *scale, void *stream);
+
+/*
+ * gmm_pack_rhs -- weights quantised elsewhere into the forward's operand
+ *   order: E4M3 codes in the logical [G,K,N] row-major layout (the RHS of
+ *   "实现差距：GMM Kernel（V1 vs V2）", section 2.1, whose 128x128 block
+ *   scales [G,K/128,N/128] gmm_fp8_fwd takes unchanged) are rewritten in the
+ *   packed order gmm_quantize_rhs writes.  A pure permutation: byte (h, l, e)
+ *   of slab (g, nb, kb) = q[g, 128*kb + 32*(l/16) + 16*h + e, 16*nb + l%16].
+ * q:      [G,K,N] E4M3 codes.     packed: G*N*K bytes, not overlapping q.
+ * K and N must be multiples of 128; 1 <= G <= GMM_MAX_GROUPS.
+ */
+GMM_API int gmm_pack_rhs(const uint8_t *q, int64_t G, int64_t K, int64_t N,
+                         uint8_t *packed, void *stream);
+
+/*
+ * gmm_quant_scales -- the scale pair of the 1x128 / 128x128 recipe for a
+ *   list of block abs-maxima: scale[i] = a/448 and inv[i] = (scale[i] == 0 ?
+ *   0 : 1/scale[i]), each correctly rounded fp32, computed by the same device
+ *   routines every quantiser of this library and the fused forward use
+ *   ("实现差距：GMM Kernel（V1 vs V2）", section 3.3: scale from the abs-max,
+ *   guarded inverse).  Exposed so the recipe's arithmetic can be checked on
+ *   its own.
+ * amax: [n] fp32, each 0 or in [2^-100, FLT_MAX] (the contract's range).
+ * scale, inv: [n] fp32.
+ */
+GMM_API int gmm_quant_scales(const float *amax, int64_t n, float *scale, float *inv,
+                             void *stream);
 
 /*
  * gmm_quantize_rhs_mxfp4 -- MXFP4 quantisation of the expert weights (done
@@ -158,7 +230,7 @@ GMM_API int gmm_quantize_rhs_mxfp4(const void *w, int w_dtype, int64_t G, int64_
 GMM_API int gmm_fp8_mxfp4_fwd(const void *lhs, int lhs_dtype, const float *lhs_scale,
                 const uint8_t *rhs_q, const uint8_t *rhs_scale,
                 const int32_t *group_sizes, int64_t M, int64_t K, int64_t N,
-                int64_t G, void *out, int out_dtype, void *stream);
+                int64_t G, void *out, int out_dtype, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * gmm_fp8_fwd -- blockwise-FP8 grouped matmul forward.
@@ -178,13 +250,15 @@ GMM_API int gmm_fp8_mxfp4_fwd(const void *lhs, int lhs_dtype, const float *lhs_s
  * out:       [M,N], out_dtype GMM_BF16 (round to nearest even) or GMM_F32.
  * q_out, scale_out: NULL, or [M,K] codes and [M,K/128] scales that receive
  *            the in-kernel quantisation of lhs (only with bf16/f32 lhs).
+ *            Only the rows of groups are written; rows at or past the total
+ *            are left as they were.
  * K and N must be multiples of 128; 1 <= G <= GMM_MAX_GROUPS.
  */
 GMM_API int gmm_fp8_fwd(const void *lhs, int lhs_dtype, const float *lhs_scale,
                 const uint8_t *rhs, const float *rhs_scale,
                 const int32_t *group_sizes, int64_t M, int64_t K, int64_t N,
                 int64_t G, void *out, int out_dtype, uint8_t *q_out,
-                float *scale_out, void *stream);
+                float *scale_out, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * gmm_fp8_fwd_swiglu -- blockwise-FP8 grouped matmul with the gate and up
@@ -210,7 +284,7 @@ GMM_API int gmm_fp8_fwd_swiglu(const void *lhs, int lhs_dtype, const float *lhs_
                                const uint8_t *rhs, const float *rhs_scale,
                                const int32_t *group_sizes, int64_t M, int64_t K, int64_t N,
                                int64_t G, void *out, int out_dtype, uint8_t *act_q,
-                               float *act_scale, void *stream);
+                               float *act_scale, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * gmm_bf16_fwd -- unquantised grouped matmul (the bf16 baseline).
@@ -222,7 +296,7 @@ GMM_API int gmm_fp8_fwd_swiglu(const void *lhs, int lhs_dtype, const float *lhs_
  */
 GMM_API int gmm_bf16_fwd(const void *lhs, const void *rhs, const int32_t *group_sizes,
                  int64_t M, int64_t K, int64_t N, int64_t G, void *out,
-                 int out_dtype, void *stream);
+                 int out_dtype, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * tgmm_bf16 -- weight gradient of the grouped matmul.
@@ -235,7 +309,7 @@ GMM_API int gmm_bf16_fwd(const void *lhs, const void *rhs, const int32_t *group_
  */
 GMM_API int tgmm_bf16(const void *x, const void *dy, const int32_t *group_sizes,
               int64_t M, int64_t K, int64_t N, int64_t G, void *dw,
-              int out_dtype, void *stream);
+              int out_dtype, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * gmm_bf16_dx -- input gradient of the grouped matmul.
@@ -246,7 +320,7 @@ GMM_API int tgmm_bf16(const void *x, const void *dy, const int32_t *group_sizes,
  */
 GMM_API int gmm_bf16_dx(const void *dy, const void *w, const int32_t *group_sizes,
                 int64_t M, int64_t K, int64_t N, int64_t G, void *dx,
-                int out_dtype, void *stream);
+                int out_dtype, void *ws, size_t ws_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -17,8 +17,13 @@ LIB_PATH = os.path.join(_HERE, "libgmm.so")
 
 GMM_F32, GMM_BF16, GMM_E4M3 = 0, 1, 2
 GMM_MAX_GROUPS = 4096
-EXPORTS = ("gmm_status_string", "gmm_last_error", "gmm_group_metadata", "gmm_quantize_lhs",
-           "gmm_quantize_rhs", "gmm_fp8_fwd", "gmm_fp8_fwd_swiglu", "gmm_bf16_fwd", "tgmm_bf16",
+# operations (gmm_workspace_bytes) and device status bits (gmm_device_status)
+(OP_METADATA, OP_FP8_FWD, OP_FP8_FWD_SWIGLU, OP_FP8_MXFP4_FWD, OP_BF16_FWD, OP_TGMM,
+ OP_DX) = range(7)
+DEV_SUM_GT_M, DEV_NEGATIVE_SIZE = 1, 2
+EXPORTS = ("gmm_status_string", "gmm_last_error", "gmm_workspace_bytes", "gmm_device_status",
+           "gmm_group_metadata", "gmm_quantize_lhs", "gmm_quantize_rhs", "gmm_pack_rhs",
+           "gmm_quant_scales", "gmm_fp8_fwd", "gmm_fp8_fwd_swiglu", "gmm_bf16_fwd", "tgmm_bf16",
            "gmm_bf16_dx", "gmm_quantize_rhs_mxfp4", "gmm_fp8_mxfp4_fwd")
 
 _lib = None
@@ -38,22 +43,27 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise ImportError("libgmm.so not found at %s; run moe_grouped_gemm_gmm_amd/build.py" % path)
     lib = ctypes.CDLL(path)
-    P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    P, I64, I, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
     lib.gmm_status_string.restype = ctypes.c_char_p
     lib.gmm_status_string.argtypes = [I]
     lib.gmm_last_error.restype = ctypes.c_char_p
     lib.gmm_last_error.argtypes = []
-    lib.gmm_group_metadata.argtypes = [P, I64, I64, I64, P, P, I64, P, P]
+    lib.gmm_workspace_bytes.restype = SZ
+    lib.gmm_workspace_bytes.argtypes = [I, I64, I64, I64, I64]
+    lib.gmm_device_status.argtypes = [P, P, P]
+    lib.gmm_group_metadata.argtypes = [P, I64, I64, I64, P, P, I64, P, P, SZ, P]
     lib.gmm_quantize_lhs.argtypes = [P, I, I64, I64, P, P, P]
     lib.gmm_quantize_rhs.argtypes = [P, I, I64, I64, I64, P, P, P]
-    lib.gmm_fp8_fwd.argtypes = [P, I, P, P, P, P, I64, I64, I64, I64, P, I, P, P, P]
-    lib.gmm_fp8_fwd_swiglu.argtypes = [P, I, P, P, P, P, I64, I64, I64, I64, P, I, P, P, P]
-    lib.gmm_bf16_fwd.argtypes = [P, P, P, I64, I64, I64, I64, P, I, P]
-    lib.tgmm_bf16.argtypes = [P, P, P, I64, I64, I64, I64, P, I, P]
-    lib.gmm_bf16_dx.argtypes = [P, P, P, I64, I64, I64, I64, P, I, P]
+    lib.gmm_pack_rhs.argtypes = [P, I64, I64, I64, P, P]
+    lib.gmm_quant_scales.argtypes = [P, I64, P, P, P]
+    lib.gmm_fp8_fwd.argtypes = [P, I, P, P, P, P, I64, I64, I64, I64, P, I, P, P, P, SZ, P]
+    lib.gmm_fp8_fwd_swiglu.argtypes = [P, I, P, P, P, P, I64, I64, I64, I64, P, I, P, P, P, SZ, P]
+    lib.gmm_bf16_fwd.argtypes = [P, P, P, I64, I64, I64, I64, P, I, P, SZ, P]
+    lib.tgmm_bf16.argtypes = [P, P, P, I64, I64, I64, I64, P, I, P, SZ, P]
+    lib.gmm_bf16_dx.argtypes = [P, P, P, I64, I64, I64, I64, P, I, P, SZ, P]
     lib.gmm_quantize_rhs_mxfp4.argtypes = [P, I, I64, I64, I64, P, P, P]
-    lib.gmm_fp8_mxfp4_fwd.argtypes = [P, I, P, P, P, P, I64, I64, I64, I64, P, I, P]
-    for name in EXPORTS[2:]:
+    lib.gmm_fp8_mxfp4_fwd.argtypes = [P, I, P, P, P, P, I64, I64, I64, I64, P, I, P, SZ, P]
+    for name in EXPORTS[3:]:
         getattr(lib, name).restype = I
     _lib = lib
     return lib
@@ -87,7 +97,33 @@ def _dt(t: torch.Tensor) -> int:
     return _DT[t.dtype]
 
 
-def gmm_group_metadata(group_sizes: torch.Tensor, M: int, tile_m: int = 128
+def workspace_bytes(op: int, M: int, K: int, N: int, G: int) -> int:
+    """Bytes of workspace the grouped call `op` (OP_*) needs for this shape."""
+    return int(load_library().gmm_workspace_bytes(op, M, K, N, G))
+
+
+def workspace(op: int, M: int, K: int, N: int, G: int, device) -> torch.Tensor:
+    """A workspace tensor (uint8, device memory) for the grouped call `op`."""
+    return torch.empty(max(workspace_bytes(op, M, K, N, G), 16), dtype=torch.uint8, device=device)
+
+
+def device_status(ws: torch.Tensor) -> int:
+    """The device status word the last grouped call wrote into ws (0, or an OR
+    of DEV_SUM_GT_M and DEV_NEGATIVE_SIZE); synchronises with the current stream."""
+    lib = load_library()
+    out = ctypes.c_int32(-1)
+    _check(lib.gmm_device_status(_ptr(ws), ctypes.byref(out), _stream(ws)))
+    return int(out.value)
+
+
+def _ws(ws: Optional[torch.Tensor], op: int, M: int, K: int, N: int, G: int, device):
+    if ws is None:
+        ws = workspace(op, M, K, N, G, device)
+    return ws, _ptr(ws), ws.numel() * ws.element_size()
+
+
+def gmm_group_metadata(group_sizes: torch.Tensor, M: int, tile_m: int = 128,
+                       ws: Optional[torch.Tensor] = None
                        ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """Device work list of the grouped kernels: (offsets [G+1], work [cap,4], num_work [1])."""
     lib = load_library()
@@ -97,8 +133,9 @@ def gmm_group_metadata(group_sizes: torch.Tensor, M: int, tile_m: int = 128
     offsets = torch.empty(G + 1, dtype=torch.int32, device=dev)
     work = torch.empty((cap, 4), dtype=torch.int32, device=dev)
     num = torch.empty(1, dtype=torch.int32, device=dev)
+    ws, wsp, wsb = _ws(ws, OP_METADATA, M, 0, 0, G, dev)
     _check(lib.gmm_group_metadata(_ptr(group_sizes), G, M, tile_m, _ptr(offsets), _ptr(work),
-                                  cap, _ptr(num), _stream(group_sizes)))
+                                  cap, _ptr(num), wsp, wsb, _stream(group_sizes)))
     return offsets, work, num
 
 
@@ -124,6 +161,27 @@ def gmm_quantize_rhs(w: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
     return q, s
 
 
+def gmm_pack_rhs(q: torch.Tensor) -> torch.Tensor:
+    """E4M3 codes [G,K,N] (uint8 or float8_e4m3fn) quantised elsewhere -> the packed
+    order gmm_fp8_fwd reads, uint8 [G, N/16, K/128, 2048] (include/gmm.h, gmm_pack_rhs)."""
+    lib = load_library()
+    G, K, N = q.shape
+    packed = torch.empty((G, max(N // 16, 0), max(K // 128, 0), 2048), dtype=torch.uint8,
+                         device=q.device)
+    _check(lib.gmm_pack_rhs(_ptr(q), G, K, N, _ptr(packed), _stream(q)))
+    return packed
+
+
+def gmm_quant_scales(amax: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
+    """The recipe's scale pair for block abs-maxima amax (fp32): (a/448, guarded inverse)."""
+    lib = load_library()
+    n = amax.numel()
+    scale = torch.empty_like(amax)
+    inv = torch.empty_like(amax)
+    _check(lib.gmm_quant_scales(_ptr(amax), n, _ptr(scale), _ptr(inv), _stream(amax)))
+    return scale, inv
+
+
 def gmm_quantize_rhs_mxfp4(w: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
     """MXFP4 quantisation of w [G,K,N] -> (packed E2M1 codes uint8 [G, N/16, K/128, 1024],
     E8M0 scales uint8 [G, N/16, K/128, 64]), in the order gmm_fp8_mxfp4_fwd reads
@@ -138,8 +196,8 @@ def gmm_quantize_rhs_mxfp4(w: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]
 
 def gmm_fp8_mxfp4_fwd(lhs: torch.Tensor, rhs_q: torch.Tensor, rhs_scale: torch.Tensor,
                       group_sizes: torch.Tensor, lhs_scale: Optional[torch.Tensor] = None,
-                      out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None
-                      ) -> torch.Tensor:
+                      out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None,
+                      ws: Optional[torch.Tensor] = None) -> torch.Tensor:
     """GMM of a 1x128 FP8 LHS (bf16/fp32 quantised in-kernel, or uint8 codes with
     lhs_scale [M,K/128]) against MXFP4 weights from gmm_quantize_rhs_mxfp4."""
     lib = load_library()
@@ -151,17 +209,18 @@ def gmm_fp8_mxfp4_fwd(lhs: torch.Tensor, rhs_q: torch.Tensor, rhs_scale: torch.T
                          % (tuple(rhs_q.shape), tuple(rhs_scale.shape), K))
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=lhs.device)
+    ws, wsp, wsb = _ws(ws, OP_FP8_MXFP4_FWD, M, K, N, G, lhs.device)
     _check(lib.gmm_fp8_mxfp4_fwd(_ptr(lhs), _dt(lhs), _ptr(lhs_scale), _ptr(rhs_q),
                                  _ptr(rhs_scale), _ptr(group_sizes), M, K, N, G, _ptr(out),
-                                 _dt(out), _stream(lhs)))
+                                 _dt(out), wsp, wsb, _stream(lhs)))
     return out
 
 
 def gmm_fp8_fwd(lhs: torch.Tensor, rhs_q: torch.Tensor, rhs_scale: torch.Tensor,
                 group_sizes: torch.Tensor, lhs_scale: Optional[torch.Tensor] = None,
                 out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None,
-                q_out: Optional[torch.Tensor] = None, scale_out: Optional[torch.Tensor] = None
-                ) -> torch.Tensor:
+                q_out: Optional[torch.Tensor] = None, scale_out: Optional[torch.Tensor] = None,
+                ws: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Blockwise-FP8 GMM.  lhs [M,K] bf16/fp32 (quantised in-kernel) or uint8 codes
     with lhs_scale [M,K/128]; rhs_q, rhs_scale as returned by gmm_quantize_rhs."""
     lib = load_library()
@@ -172,17 +231,18 @@ def gmm_fp8_fwd(lhs: torch.Tensor, rhs_q: torch.Tensor, rhs_scale: torch.Tensor,
         raise ValueError("rhs_q shape %s does not match K=%d" % (tuple(rhs_q.shape), K))
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=lhs.device)
+    ws, wsp, wsb = _ws(ws, OP_FP8_FWD, M, K, N, G, lhs.device)
     _check(lib.gmm_fp8_fwd(_ptr(lhs), _dt(lhs), _ptr(lhs_scale), _ptr(rhs_q), _ptr(rhs_scale),
                            _ptr(group_sizes), M, K, N, G, _ptr(out), _dt(out), _ptr(q_out),
-                           _ptr(scale_out), _stream(lhs)))
+                           _ptr(scale_out), wsp, wsb, _stream(lhs)))
     return out
 
 
 def gmm_fp8_fwd_swiglu(lhs: torch.Tensor, rhs_q: torch.Tensor, rhs_scale: torch.Tensor,
                        group_sizes: torch.Tensor, lhs_scale: Optional[torch.Tensor] = None,
                        out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None,
-                       act_q: Optional[torch.Tensor] = None, act_scale: Optional[torch.Tensor] = None
-                       ) -> torch.Tensor:
+                       act_q: Optional[torch.Tensor] = None, act_scale: Optional[torch.Tensor] = None,
+                       ws: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Fused gate+up blockwise-FP8 GMM: rhs_q/rhs_scale quantise the [G,K,2N]
     concatenation (gate columns first); returns silu(gate) * up, [M,N].
     act_q [M,N] uint8 / act_scale [M,N/128] f32 optionally receive its 1x128
@@ -195,15 +255,16 @@ def gmm_fp8_fwd_swiglu(lhs: torch.Tensor, rhs_q: torch.Tensor, rhs_scale: torch.
     N = N16 * 16 // 2
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=lhs.device)
+    ws, wsp, wsb = _ws(ws, OP_FP8_FWD_SWIGLU, M, K, N, G, lhs.device)
     _check(lib.gmm_fp8_fwd_swiglu(_ptr(lhs), _dt(lhs), _ptr(lhs_scale), _ptr(rhs_q),
                                   _ptr(rhs_scale), _ptr(group_sizes), M, K, N, G, _ptr(out),
-                                  _dt(out), _ptr(act_q), _ptr(act_scale), _stream(lhs)))
+                                  _dt(out), _ptr(act_q), _ptr(act_scale), wsp, wsb, _stream(lhs)))
     return out
 
 
 def gmm_bf16_fwd(lhs: torch.Tensor, rhs: torch.Tensor, group_sizes: torch.Tensor,
-                 out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None
-                 ) -> torch.Tensor:
+                 out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None,
+                 ws: Optional[torch.Tensor] = None) -> torch.Tensor:
     """bf16 GMM: out [M,N] = lhs [M,K] . rhs[g] [K,N] per group."""
     lib = load_library()
     M, K = lhs.shape
@@ -212,14 +273,15 @@ def gmm_bf16_fwd(lhs: torch.Tensor, rhs: torch.Tensor, group_sizes: torch.Tensor
         raise ValueError("lhs K=%d but rhs K=%d" % (K, K2))
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=lhs.device)
+    ws, wsp, wsb = _ws(ws, OP_BF16_FWD, M, K, N, G, lhs.device)
     _check(lib.gmm_bf16_fwd(_ptr(lhs), _ptr(rhs), _ptr(group_sizes), M, K, N, G, _ptr(out),
-                            _dt(out), _stream(lhs)))
+                            _dt(out), wsp, wsb, _stream(lhs)))
     return out
 
 
 def tgmm_bf16(x: torch.Tensor, dy: torch.Tensor, group_sizes: torch.Tensor,
-              out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None
-              ) -> torch.Tensor:
+              out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None,
+              ws: Optional[torch.Tensor] = None) -> torch.Tensor:
     """dW [G,K,N]: dW[g] = X_g^T dY_g for x [M,K], dy [M,N]."""
     lib = load_library()
     M, K = x.shape
@@ -229,14 +291,15 @@ def tgmm_bf16(x: torch.Tensor, dy: torch.Tensor, group_sizes: torch.Tensor,
     G = group_sizes.numel()
     if out is None:
         out = torch.empty((G, K, N), dtype=out_dtype, device=x.device)
+    ws, wsp, wsb = _ws(ws, OP_TGMM, M, K, N, G, x.device)
     _check(lib.tgmm_bf16(_ptr(x), _ptr(dy), _ptr(group_sizes), M, K, N, G, _ptr(out), _dt(out),
-                         _stream(x)))
+                         wsp, wsb, _stream(x)))
     return out
 
 
 def gmm_bf16_dx(dy: torch.Tensor, w: torch.Tensor, group_sizes: torch.Tensor,
-                out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None
-                ) -> torch.Tensor:
+                out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None,
+                ws: Optional[torch.Tensor] = None) -> torch.Tensor:
     """dX [M,K] = dY [M,N] . w[g]^T per group, w [G,K,N]."""
     lib = load_library()
     M, N = dy.shape
@@ -245,6 +308,7 @@ def gmm_bf16_dx(dy: torch.Tensor, w: torch.Tensor, group_sizes: torch.Tensor,
         raise ValueError("dy N=%d but w N=%d" % (N, N2))
     if out is None:
         out = torch.empty((M, K), dtype=out_dtype, device=dy.device)
+    ws, wsp, wsb = _ws(ws, OP_DX, M, K, N, G, dy.device)
     _check(lib.gmm_bf16_dx(_ptr(dy), _ptr(w), _ptr(group_sizes), M, K, N, G, _ptr(out),
-                           _dt(out), _stream(dy)))
+                           _dt(out), wsp, wsb, _stream(dy)))
     return out

@@ -1,6 +1,7 @@
 // C ABI of the grouped-matmul library (declared in include/gmm.h): host-side
 // argument checks, then one launch on the caller's stream.  Nothing here
-// allocates, synchronises or reads device memory.
+// allocates; only gmm_device_status synchronises (it reads one word of a
+// workspace back to the host).
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
@@ -57,6 +58,20 @@ int check_out_dtype(int dt, const char* name) {
     return GMM_OK;
 }
 
+// Bytes of the status block at the start of every workspace (word 0: the
+// device status of the last call that used it).
+constexpr size_t kWsStatusBytes = 256;
+
+int check_ws(const void* ws, size_t ws_bytes, size_t need) {
+    if (ws == nullptr || ws_bytes < need)
+        return fail(GMM_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed%s", ws == nullptr ? 0 : ws_bytes,
+                    need, ws == nullptr ? " (ws is NULL)" : "");
+    if (!aligned16(ws)) return fail(GMM_ERR_ALIGN, "ws is not 16-byte aligned");
+    return GMM_OK;
+}
+
+int32_t* ws_status(void* ws) { return reinterpret_cast<int32_t*>(ws); }
+
 int hip_status(hipError_t e) {
     if (e != hipSuccess) return fail(GMM_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(e));
     return GMM_OK;
@@ -79,6 +94,7 @@ const char* gmm_status_string(int status) {
         case GMM_ERR_SHAPE: return "invalid shape";
         case GMM_ERR_ALIGN: return "misaligned pointer";
         case GMM_ERR_DTYPE: return "unsupported dtype";
+        case GMM_ERR_WORKSPACE: return "workspace missing or too small";
         case GMM_ERR_HIP: return "HIP runtime error";
         default: return "unknown status";
     }
@@ -86,9 +102,54 @@ const char* gmm_status_string(int status) {
 
 const char* gmm_last_error(void) { return g_last_error; }
 
+size_t gmm_workspace_bytes(int op, int64_t M, int64_t K, int64_t N, int64_t G) {
+    (void)M; (void)K; (void)N; (void)G;
+    switch (op) {
+        case GMM_OP_METADATA:
+        case GMM_OP_FP8_FWD:
+        case GMM_OP_FP8_FWD_SWIGLU:
+        case GMM_OP_FP8_MXFP4_FWD:
+        case GMM_OP_BF16_FWD:
+        case GMM_OP_TGMM:
+        case GMM_OP_DX:
+            return kWsStatusBytes;
+        default:
+            return 0;
+    }
+}
+
+int gmm_device_status(const void* ws, int32_t* status, void* stream) {
+    GMM_TRY(check_ptr(ws, "ws"));
+    if (status == nullptr) return fail(GMM_ERR_NULL, "status is NULL");
+    hipError_t e = hipMemcpyAsync(status, ws, sizeof(int32_t), hipMemcpyDeviceToHost,
+                                  (hipStream_t)stream);
+    if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+    return hip_status(e);
+}
+
+int gmm_pack_rhs(const uint8_t* q, int64_t G, int64_t K, int64_t N, uint8_t* packed, void* stream) {
+    if (G < 1 || G > GMM_MAX_GROUPS)
+        return fail(GMM_ERR_SHAPE, "G=%lld outside [1, %d]", (long long)G, GMM_MAX_GROUPS);
+    GMM_TRY(check_mult(K, 128, "K"));
+    GMM_TRY(check_mult(N, 128, "N"));
+    if (G * (N / 16) * (K / 128) > kMaxDim) return fail(GMM_ERR_SHAPE, "too many blocks");
+    GMM_TRY(check_ptr(q, "q"));
+    GMM_TRY(check_ptr(packed, "packed"));
+    return hip_status(gmm::launch_pack_rhs(q, G, K, N, packed, (hipStream_t)stream));
+}
+
+int gmm_quant_scales(const float* amax, int64_t n, float* scale, float* inv, void* stream) {
+    if (n < 0 || n > kMaxDim) return fail(GMM_ERR_SHAPE, "n=%lld out of range", (long long)n);
+    GMM_TRY(check_ptr(amax, "amax"));
+    GMM_TRY(check_ptr(scale, "scale"));
+    GMM_TRY(check_ptr(inv, "inv"));
+    if (n == 0) return GMM_OK;
+    return hip_status(gmm::launch_quant_scales(amax, n, scale, inv, (hipStream_t)stream));
+}
+
 int gmm_group_metadata(const int32_t* group_sizes, int64_t G, int64_t M, int64_t tile_m,
                        int32_t* offsets, int32_t* work, int64_t capacity, int32_t* num_work,
-                       void* stream) {
+                       void* ws, size_t ws_bytes, void* stream) {
     GMM_TRY(check_groups(M, G));
     GMM_TRY(check_ptr(group_sizes, "group_sizes"));
     GMM_TRY(check_ptr(offsets, "offsets"));
@@ -99,8 +160,9 @@ int gmm_group_metadata(const int32_t* group_sizes, int64_t G, int64_t M, int64_t
     const int64_t need = (M + tile_m - 1) / tile_m + G + 1;
     if (capacity < need || capacity > kMaxDim)
         return fail(GMM_ERR_SHAPE, "capacity=%lld, need >= %lld", (long long)capacity, (long long)need);
+    GMM_TRY(check_ws(ws, ws_bytes, gmm_workspace_bytes(GMM_OP_METADATA, M, 0, 0, G)));
     return hip_status(gmm::launch_group_metadata(group_sizes, (int)G, (int)M, (int)tile_m, offsets,
-                                                 work, (int)capacity, num_work,
+                                                 work, (int)capacity, num_work, ws_status(ws),
                                                  (hipStream_t)stream));
 }
 
@@ -153,7 +215,7 @@ int gmm_quantize_rhs_mxfp4(const void* w, int w_dtype, int64_t G, int64_t K, int
 int gmm_fp8_mxfp4_fwd(const void* lhs, int lhs_dtype, const float* lhs_scale,
                       const uint8_t* rhs_q, const uint8_t* rhs_scale, const int32_t* group_sizes,
                       int64_t M, int64_t K, int64_t N, int64_t G, void* out, int out_dtype,
-                      void* stream) {
+                      void* ws, size_t ws_bytes, void* stream) {
     int kind;
     if (lhs_dtype == GMM_E4M3) kind = 0;
     else if (lhs_dtype == GMM_BF16) kind = 1;
@@ -172,16 +234,18 @@ int gmm_fp8_mxfp4_fwd(const void* lhs, int lhs_dtype, const float* lhs_scale,
     else if (lhs_scale != nullptr) return fail(GMM_ERR_DTYPE, "lhs_scale given with an unquantised lhs");
     const int64_t blocks = ((M + 47) / 48 + G + 1) * (N / 128);
     if (blocks > kMaxDim) return fail(GMM_ERR_SHAPE, "grid too large");
+    GMM_TRY(check_ws(ws, ws_bytes, gmm_workspace_bytes(GMM_OP_FP8_MXFP4_FWD, M, K, N, G)));
     if (M == 0) return GMM_OK;
     return hip_status(gmm::launch_fp8_mxfp4_fwd(lhs, kind, lhs_scale, rhs_q, rhs_scale, group_sizes,
                                                 (int)M, (int)K, (int)N, (int)G, out,
-                                                out_dtype == GMM_BF16, (hipStream_t)stream));
+                                                out_dtype == GMM_BF16, ws_status(ws),
+                                                (hipStream_t)stream));
 }
 
 int gmm_fp8_fwd(const void* lhs, int lhs_dtype, const float* lhs_scale, const uint8_t* rhs,
                 const float* rhs_scale, const int32_t* group_sizes, int64_t M, int64_t K,
                 int64_t N, int64_t G, void* out, int out_dtype, uint8_t* q_out,
-                float* scale_out, void* stream) {
+                float* scale_out, void* ws, size_t ws_bytes, void* stream) {
     int kind;
     if (lhs_dtype == GMM_E4M3) kind = 0;
     else if (lhs_dtype == GMM_BF16) kind = 1;
@@ -209,17 +273,18 @@ int gmm_fp8_fwd(const void* lhs, int lhs_dtype, const float* lhs_scale, const ui
     }
     const int64_t blocks = ((M + 47) / 48 + G + 1) * (N / 128);   // worst case over tile shapes
     if (blocks > kMaxDim) return fail(GMM_ERR_SHAPE, "grid too large");
+    GMM_TRY(check_ws(ws, ws_bytes, gmm_workspace_bytes(GMM_OP_FP8_FWD, M, K, N, G)));
     if (M == 0) return GMM_OK;
     return hip_status(gmm::launch_fp8_fwd(lhs, kind, lhs_scale, rhs, rhs_scale, group_sizes,
                                           (int)M, (int)K, (int)N, (int)G, out,
-                                          out_dtype == GMM_BF16, q_out, scale_out,
+                                          out_dtype == GMM_BF16, q_out, scale_out, ws_status(ws),
                                           (hipStream_t)stream));
 }
 
 int gmm_fp8_fwd_swiglu(const void* lhs, int lhs_dtype, const float* lhs_scale, const uint8_t* rhs,
                        const float* rhs_scale, const int32_t* group_sizes, int64_t M, int64_t K,
                        int64_t N, int64_t G, void* out, int out_dtype, uint8_t* act_q,
-                       float* act_scale, void* stream) {
+                       float* act_scale, void* ws, size_t ws_bytes, void* stream) {
     int kind;
     if (lhs_dtype == GMM_E4M3) kind = 0;
     else if (lhs_dtype == GMM_BF16) kind = 1;
@@ -242,15 +307,17 @@ int gmm_fp8_fwd_swiglu(const void* lhs, int lhs_dtype, const float* lhs_scale, c
     GMM_TRY(check_opt_ptr(act_scale, "act_scale"));
     const int64_t blocks = ((M + 47) / 48 + G + 1) * (N / 256);
     if (blocks > kMaxDim) return fail(GMM_ERR_SHAPE, "grid too large");
+    GMM_TRY(check_ws(ws, ws_bytes, gmm_workspace_bytes(GMM_OP_FP8_FWD_SWIGLU, M, K, N, G)));
     if (M == 0) return GMM_OK;
     return hip_status(gmm::launch_fp8_fwd_swiglu(lhs, kind, lhs_scale, rhs, rhs_scale,
                                                  group_sizes, (int)M, (int)K, (int)N, (int)G, out,
                                                  out_dtype == GMM_BF16, act_q, act_scale,
-                                                 (hipStream_t)stream));
+                                                 ws_status(ws), (hipStream_t)stream));
 }
 
 int gmm_bf16_fwd(const void* lhs, const void* rhs, const int32_t* group_sizes, int64_t M,
-                 int64_t K, int64_t N, int64_t G, void* out, int out_dtype, void* stream) {
+                 int64_t K, int64_t N, int64_t G, void* out, int out_dtype, void* ws,
+                 size_t ws_bytes, void* stream) {
     GMM_TRY(check_out_dtype(out_dtype, "out"));
     GMM_TRY(check_groups(M, G));
     GMM_TRY(check_mult(K, 64, "K"));
@@ -261,13 +328,16 @@ int gmm_bf16_fwd(const void* lhs, const void* rhs, const int32_t* group_sizes, i
     GMM_TRY(check_ptr(out, "out"));
     const int64_t blocks = ((M + 127) / 128 + G + 1) * (N / 128);
     if (blocks > kMaxDim) return fail(GMM_ERR_SHAPE, "grid too large");
+    GMM_TRY(check_ws(ws, ws_bytes, gmm_workspace_bytes(GMM_OP_BF16_FWD, M, K, N, G)));
     if (M == 0) return GMM_OK;
     return hip_status(gmm::launch_bf16_fwd(lhs, rhs, group_sizes, (int)M, (int)K, (int)N, (int)G,
-                                           out, out_dtype == GMM_BF16, (hipStream_t)stream));
+                                           out, out_dtype == GMM_BF16, ws_status(ws),
+                                           (hipStream_t)stream));
 }
 
 int tgmm_bf16(const void* x, const void* dy, const int32_t* group_sizes, int64_t M, int64_t K,
-              int64_t N, int64_t G, void* dw, int out_dtype, void* stream) {
+              int64_t N, int64_t G, void* dw, int out_dtype, void* ws, size_t ws_bytes,
+              void* stream) {
     GMM_TRY(check_out_dtype(out_dtype, "dw"));
     GMM_TRY(check_groups(M, G));
     GMM_TRY(check_mult(K, 128, "K"));
@@ -277,12 +347,14 @@ int tgmm_bf16(const void* x, const void* dy, const int32_t* group_sizes, int64_t
     GMM_TRY(check_ptr(group_sizes, "group_sizes"));
     GMM_TRY(check_ptr(dw, "dw"));
     if (G * (K / 128) * (N / 128) > kMaxDim) return fail(GMM_ERR_SHAPE, "grid too large");
+    GMM_TRY(check_ws(ws, ws_bytes, gmm_workspace_bytes(GMM_OP_TGMM, M, K, N, G)));
     return hip_status(gmm::launch_tgmm(x, dy, group_sizes, (int)M, (int)K, (int)N, (int)G, dw,
-                                       out_dtype == GMM_BF16, (hipStream_t)stream));
+                                       out_dtype == GMM_BF16, ws_status(ws), (hipStream_t)stream));
 }
 
 int gmm_bf16_dx(const void* dy, const void* w, const int32_t* group_sizes, int64_t M, int64_t K,
-                int64_t N, int64_t G, void* dx, int out_dtype, void* stream) {
+                int64_t N, int64_t G, void* dx, int out_dtype, void* ws, size_t ws_bytes,
+                void* stream) {
     GMM_TRY(check_out_dtype(out_dtype, "dx"));
     GMM_TRY(check_groups(M, G));
     GMM_TRY(check_mult(K, 128, "K"));
@@ -293,9 +365,10 @@ int gmm_bf16_dx(const void* dy, const void* w, const int32_t* group_sizes, int64
     GMM_TRY(check_ptr(dx, "dx"));
     const int64_t blocks = ((M + 127) / 128 + G + 1) * (K / 128);
     if (blocks > kMaxDim) return fail(GMM_ERR_SHAPE, "grid too large");
+    GMM_TRY(check_ws(ws, ws_bytes, gmm_workspace_bytes(GMM_OP_DX, M, K, N, G)));
     if (M == 0) return GMM_OK;
     return hip_status(gmm::launch_bf16_dx(dy, w, group_sizes, (int)M, (int)K, (int)N, (int)G, dx,
-                                          out_dtype == GMM_BF16, (hipStream_t)stream));
+                                          out_dtype == GMM_BF16, ws_status(ws), (hipStream_t)stream));
 }
 
 }  // extern "C"

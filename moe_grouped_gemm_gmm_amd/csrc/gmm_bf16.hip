@@ -129,44 +129,40 @@ struct TgmmTile {
 };
 
 // The r-th group of size class cls (cls < 0: of all groups) in index order
-// among chunks whose sizes and inclusive row scans the caller supplies, with
-// its row range; true when found (r is decremented past each chunk).
-__device__ __forceinline__ bool tgmm_pick(int base, int G, int sz, int incl, int cls, int& r,
-                                          int& carry, TgmmTile& out) {
+// among one chunk of 64 groups, whose clamped row ranges the caller
+// supplies (lane i: group base + i); true when found (r is decremented past
+// each chunk).
+__device__ __forceinline__ bool tgmm_pick(int base, int G, int lo, int hi, int cls, int& r,
+                                          TgmmTile& out) {
     const int lane = lane_id();
-    const bool in = base + lane < G && (cls < 0 || tgmm_size_class(sz) == cls);
+    const bool in = base + lane < G && (cls < 0 || tgmm_size_class(hi - lo) == cls);
     const unsigned long long mask = __ballot(in);
     const int n = __popcll(mask);
     if (r < n) {
         const unsigned long long sel = __ballot(in && __popcll(mask & ((1ull << lane) - 1ull)) == r);
         const int src = __ffsll((long long)sel) - 1;
         out.g = base + src;
-        out.row_lo = carry + lane_value(incl - sz, src);
-        out.row_hi = out.row_lo + lane_value(sz, src);
+        out.row_lo = lane_value(lo, src);
+        out.row_hi = lane_value(hi, src);
         return true;
     }
     r -= n;
-    carry += lane_value(incl, 63);
     return false;
 }
 
 // One wave; every lane gets the result.  T = tiles per group, L = the
-// block's id after the default XCD remap.  Up to 256 groups the sizes and
-// their scans stay in registers (one load, one scan per 64 groups); beyond,
-// the second pass reads and scans them again.
-__device__ inline TgmmTile tgmm_tile(const int32_t* __restrict__ group_sizes, int G, int T, int L) {
-    const int lane = lane_id();
+// block's id after the default XCD remap.  A group's rows are its clamped
+// range (group_chunk: a negative size reads as 0, rows stop at M).  Up to
+// 256 groups the ranges stay in registers (one load and one scan per 64
+// groups); beyond, the second pass reads and scans them again.
+__device__ inline TgmmTile tgmm_tile(const int32_t* __restrict__ group_sizes, int G, int M, int T,
+                                     int L) {
     const bool inreg = G <= 256;
-    int szr[4], inc[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        const int g = 64 * c + lane;
-        szr[c] = (inreg && g < G) ? group_sizes[g] : 0;
-    }
-    // pass 1: class counts and the total
-    int cnt0 = 0, cnt1 = 0, cnt2 = 0, tot = 0;
+    int glo[4], ghi[4];
+    // pass 1: clamped ranges, class counts and the total
+    int cnt0 = 0, cnt1 = 0, cnt2 = 0, carry = 0;
     auto count = [&](int base, int sz) {
-        const int c = base + lane < G ? tgmm_size_class(sz) : 4;
+        const int c = base + lane_id() < G ? tgmm_size_class(sz) : 4;
         cnt0 += __popcll(__ballot(c == 0));
         cnt1 += __popcll(__ballot(c == 1));
         cnt2 += __popcll(__ballot(c == 2));
@@ -174,30 +170,35 @@ __device__ inline TgmmTile tgmm_tile(const int32_t* __restrict__ group_sizes, in
     if (inreg) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            inc[c] = 0;
+            glo[c] = ghi[c] = 0;
             if (64 * c < G) {
-                inc[c] = wave_incl_scan(szr[c]);
-                count(64 * c, szr[c]);
-                tot += lane_value(inc[c], 63);
+                const GroupChunk ch = group_chunk(group_sizes, G, M, 64 * c, carry);
+                glo[c] = ch.lo;
+                ghi[c] = ch.hi;
+                carry = ch.next_carry;
+                count(64 * c, ch.hi - ch.lo);
             }
         }
     } else {
         for (int base = 0; base < G; base += 64) {
-            const int sz = base + lane < G ? group_sizes[base + lane] : 0;
-            count(base, sz);
-            tot += lane_value(wave_incl_scan(sz), 63);
+            const GroupChunk ch = group_chunk(group_sizes, G, M, base, carry);
+            carry = ch.next_carry;
+            count(base, ch.hi - ch.lo);
         }
     }
+    const int tot = min(carry, M);
     // skewed: some group holds more than four times the mean
     const bool skewed = T % kNumXcd == 0 && [&] {
         bool big = false;
         if (inreg) {
 #pragma unroll
-            for (int c = 0; c < 4; ++c) big = big || (int64_t)szr[c] * G > 4 * (int64_t)tot;
+            for (int c = 0; c < 4; ++c) big = big || (int64_t)(ghi[c] - glo[c]) * G > 4 * (int64_t)tot;
         } else {
+            int cr = 0;
             for (int base = 0; base < G; base += 64) {
-                const int sz = base + lane < G ? group_sizes[base + lane] : 0;
-                big = big || (int64_t)sz * G > 4 * (int64_t)tot;
+                const GroupChunk ch = group_chunk(group_sizes, G, M, base, cr);
+                cr = ch.next_carry;
+                big = big || (int64_t)(ch.hi - ch.lo) * G > 4 * (int64_t)tot;
             }
         }
         return __ballot(big) != 0ull;
@@ -217,30 +218,27 @@ __device__ inline TgmmTile tgmm_tile(const int32_t* __restrict__ group_sizes, in
     } else {
         r = L / T;
         out.t = L % T;
-        if (inreg) {   // group r itself: its rows from the scans in registers
+        if (inreg) {   // group r itself: its rows from the ranges in registers
             const int c = r >> 6, l = r & 63;
-            int carry = 0;
-#pragma unroll
-            for (int cc = 0; cc < 3; ++cc)
-                if (cc < c) carry += lane_value(inc[cc], 63);
-            const int incl = c == 0 ? inc[0] : (c == 1 ? inc[1] : (c == 2 ? inc[2] : inc[3]));
-            const int sz = c == 0 ? szr[0] : (c == 1 ? szr[1] : (c == 2 ? szr[2] : szr[3]));
+            const int lo = c == 0 ? glo[0] : (c == 1 ? glo[1] : (c == 2 ? glo[2] : glo[3]));
+            const int hi = c == 0 ? ghi[0] : (c == 1 ? ghi[1] : (c == 2 ? ghi[2] : ghi[3]));
             out.g = r;
-            out.row_lo = carry + lane_value(incl - sz, l);
-            out.row_hi = out.row_lo + lane_value(sz, l);
+            out.row_lo = lane_value(lo, l);
+            out.row_hi = lane_value(hi, l);
             return out;
         }
     }
     // pass 2: the group at that position and its rows
-    int carry = 0;
     if (inreg) {
 #pragma unroll
         for (int c = 0; c < 4; ++c)
-            if (64 * c < G && tgmm_pick(64 * c, G, szr[c], inc[c], cls, r, carry, out)) break;
+            if (64 * c < G && tgmm_pick(64 * c, G, glo[c], ghi[c], cls, r, out)) break;
     } else {
+        int cr = 0;
         for (int base = 0; base < G; base += 64) {
-            const int sz = base + lane < G ? group_sizes[base + lane] : 0;
-            if (tgmm_pick(base, G, sz, wave_incl_scan(sz), cls, r, carry, out)) break;
+            const GroupChunk ch = group_chunk(group_sizes, G, M, base, cr);
+            cr = ch.next_carry;
+            if (tgmm_pick(base, G, ch.lo, ch.hi, cls, r, out)) break;
         }
     }
     return out;
@@ -260,7 +258,7 @@ template <int MODE, bool OUT_BF16, int MINB>
 __global__ __launch_bounds__(256, MINB) void bf16_gemm_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
     const int32_t* __restrict__ group_sizes, int M, int K, int N, int G, void* __restrict__ out,
-    int ntiles_c, int ntiles_r, int nblocks) {
+    int ntiles_c, int ntiles_r, int nblocks, int32_t* __restrict__ status) {
     constexpr bool A_TR = MODE == kTgmm;
     constexpr bool B_TR = MODE != kDx;
     __shared__ __attribute__((aligned(16))) uint16_t sA[kTileElems];
@@ -270,12 +268,16 @@ __global__ __launch_bounds__(256, MINB) void bf16_gemm_kernel(
     const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
     const int L = xcd_remap(blockIdx.x, nblocks);
     const int out_cols = MODE == kDx ? K : N;
+    if (wave == 1 && blockIdx.x == 0) {   // the call's device status word
+        const int st = group_status(group_sizes, G, M);
+        if (lane == 0) status[0] = st;
+    }
 
     // ---- what this workgroup computes
     int g, row0, lo, hi, c0, red_lo, red_hi;
     if constexpr (MODE == kTgmm) {
         if (wave == 0) {
-            const TgmmTile tt = tgmm_tile(group_sizes, G, ntiles_r * ntiles_c, L);
+            const TgmmTile tt = tgmm_tile(group_sizes, G, M, ntiles_r * ntiles_c, L);
             if (lane == 0) { s_info[0] = tt.row_lo; s_info[1] = tt.row_hi; s_info[2] = tt.g; s_info[3] = tt.t; }
         }
         __syncthreads();
@@ -433,7 +435,7 @@ __global__ __launch_bounds__(256, MINB) void bf16_gemm_kernel(
 
 template <int MODE>
 hipError_t launch_mode(const void* A, const void* B, const int32_t* group_sizes, int M, int K,
-                       int N, int G, void* out, bool out_bf16, hipStream_t stream) {
+                       int N, int G, void* out, bool out_bf16, int32_t* status, hipStream_t stream) {
     int ntiles_c, ntiles_r = 0;
     int64_t nblocks;
     if constexpr (MODE == kTgmm) {
@@ -457,17 +459,17 @@ hipError_t launch_mode(const void* A, const void* B, const int32_t* group_sizes,
     if (two) {
         if (out_bf16)
             hipLaunchKernelGGL((bf16_gemm_kernel<MODE, true, 2>), grid, block, 0, stream, a, b,
-                               group_sizes, M, K, N, G, out, ntiles_c, ntiles_r, (int)nblocks);
+                               group_sizes, M, K, N, G, out, ntiles_c, ntiles_r, (int)nblocks, status);
         else
             hipLaunchKernelGGL((bf16_gemm_kernel<MODE, false, 2>), grid, block, 0, stream, a, b,
-                               group_sizes, M, K, N, G, out, ntiles_c, ntiles_r, (int)nblocks);
+                               group_sizes, M, K, N, G, out, ntiles_c, ntiles_r, (int)nblocks, status);
     } else {
         if (out_bf16)
             hipLaunchKernelGGL((bf16_gemm_kernel<MODE, true, 3>), grid, block, 0, stream, a, b,
-                               group_sizes, M, K, N, G, out, ntiles_c, ntiles_r, (int)nblocks);
+                               group_sizes, M, K, N, G, out, ntiles_c, ntiles_r, (int)nblocks, status);
         else
             hipLaunchKernelGGL((bf16_gemm_kernel<MODE, false, 3>), grid, block, 0, stream, a, b,
-                               group_sizes, M, K, N, G, out, ntiles_c, ntiles_r, (int)nblocks);
+                               group_sizes, M, K, N, G, out, ntiles_c, ntiles_r, (int)nblocks, status);
     }
     return hipGetLastError();
 }
@@ -475,18 +477,18 @@ hipError_t launch_mode(const void* A, const void* B, const int32_t* group_sizes,
 }  // namespace
 
 hipError_t launch_bf16_fwd(const void* lhs, const void* rhs, const int32_t* group_sizes, int M,
-                           int K, int N, int G, void* out, bool out_bf16, hipStream_t stream) {
-    return launch_mode<kFwd>(lhs, rhs, group_sizes, M, K, N, G, out, out_bf16, stream);
+                           int K, int N, int G, void* out, bool out_bf16, int32_t* status, hipStream_t stream) {
+    return launch_mode<kFwd>(lhs, rhs, group_sizes, M, K, N, G, out, out_bf16, status, stream);
 }
 
 hipError_t launch_bf16_dx(const void* dy, const void* w, const int32_t* group_sizes, int M,
-                          int K, int N, int G, void* dx, bool out_bf16, hipStream_t stream) {
-    return launch_mode<kDx>(dy, w, group_sizes, M, K, N, G, dx, out_bf16, stream);
+                          int K, int N, int G, void* dx, bool out_bf16, int32_t* status, hipStream_t stream) {
+    return launch_mode<kDx>(dy, w, group_sizes, M, K, N, G, dx, out_bf16, status, stream);
 }
 
 hipError_t launch_tgmm(const void* x, const void* dy, const int32_t* group_sizes, int M, int K,
-                       int N, int G, void* dw, bool out_bf16, hipStream_t stream) {
-    return launch_mode<kTgmm>(x, dy, group_sizes, M, K, N, G, dw, out_bf16, stream);
+                       int N, int G, void* dw, bool out_bf16, int32_t* status, hipStream_t stream) {
+    return launch_mode<kTgmm>(x, dy, group_sizes, M, K, N, G, dw, out_bf16, status, stream);
 }
 
 }  // namespace gmm

@@ -136,15 +136,87 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 // Value of v in lane `lane`, which must be the same in every lane of the wave.
 __device__ __forceinline__ int lane_value(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
 
+// Saturating inclusive prefix sum over the 64 lanes: every partial sum is
+// min(true sum, cap), for lane values in [0, cap] with cap < 2^31 (then two
+// operands add to less than 2^32 and the unsigned sum never wraps; a
+// saturating sum of non-negative values is still associative, so the
+// Hillis-Steele order of wave_incl_scan gives the same result).
+__device__ __forceinline__ uint32_t wave_incl_scan_sat(uint32_t v, uint32_t cap) {
+    v = min(v + (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false), cap);
+    v = min(v + (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false), cap);
+    v = min(v + (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false), cap);
+    v = min(v + (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false), cap);
+    v = min(v + (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false), cap);
+    v = min(v + (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false), cap);
+    return v;
+}
+
+// The previous lane's value (wave_shr:1); lane 0 gets 0.
+__device__ __forceinline__ uint32_t wave_shift_up(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x138, 0xF, 0xF, false);
+}
+
 // ------------------------------------------------------- group metadata --
+// Rows of group g are [o_g, o_g + s_g) with o_g = s_0 + ... + s_{g-1}.  The
+// kernels only ever touch rows inside [0, M): group_sizes that break the
+// contract (a negative size, or sizes summing past M) are read as follows,
+// so that no access leaves the caller's buffers:
+//  - a negative size counts as 0;
+//  - a group's rows are clamped to M: [min(o_g, M), min(o_g + s_g, M)).
+// GroupChunk holds, for the 64 groups base .. base+63 (one per lane), the
+// clamped row range of the lane's group; `carry` is the clamped row count
+// before the chunk (saturated at M + 1, so carry == M + 1 means the sizes so
+// far sum past M).
+struct GroupChunk {
+    int lo, hi;      // clamped rows of group base + lane (lo == hi: empty)
+    int next_carry;  // carry for the next chunk
+    bool negative;   // some group of the chunk has a negative size
+};
+
+__device__ __forceinline__ GroupChunk group_chunk(const int32_t* __restrict__ group_sizes, int G,
+                                                  int M, int base, int carry) {
+    const int lane = lane_id();
+    const uint32_t cap = (uint32_t)M + 1u;
+    const int g = base + lane;
+    const int raw = g < G ? group_sizes[g] : 0;
+    const uint32_t s = (uint32_t)min(max(raw, 0), M + 1);   // cap: a lone group past M still saturates
+    const uint32_t incl = wave_incl_scan_sat(s, cap);
+    const uint32_t excl = wave_shift_up(incl);
+    GroupChunk c;
+    c.lo = (int)min(min((uint32_t)carry + excl, cap), (uint32_t)M);
+    c.hi = (int)min(min((uint32_t)carry + incl, cap), (uint32_t)M);
+    c.next_carry = (int)min((uint32_t)carry + (uint32_t)lane_value((int)incl, 63), cap);
+    c.negative = __ballot(raw < 0) != 0ull;
+    return c;
+}
+
+// Bits of the device status word that grouped kernels write (see gmm.h).
+constexpr int kDevSumGtM = 1;
+constexpr int kDevNegativeSize = 2;
+
+// Device status of group_sizes against M, computed by one wave (every lane
+// gets it): kDevSumGtM when the sizes (negative ones read as 0) sum past M,
+// kDevNegativeSize when a size is negative.
+__device__ __forceinline__ int group_status(const int32_t* __restrict__ group_sizes, int G, int M) {
+    int carry = 0, st = 0;
+    for (int base = 0; base < G; base += 64) {
+        const GroupChunk c = group_chunk(group_sizes, G, M, base, carry);
+        carry = c.next_carry;
+        if (c.negative) st |= kDevNegativeSize;
+    }
+    if (carry > M) st |= kDevSumGtM;
+    return st;
+}
+
 // Work item w of a grouped kernel with row tiles of height tm (a multiple of
 // 16), tiles aligned to absolute rows.  Items are ordered group by group;
-// each non-empty group g owns the tiles that intersect rows [o_g, o_g + s_g),
-// the item's row range being that intersection.  After the groups come the
-// items that zero the rows at or past the total (g == G).  g < 0 means "no
-// item" (the grid is sized for the worst case).  Every lane of the calling
-// wave gets the result.  Callers pass a compile-time tm, so the divisions
-// become multiply-shifts.
+// each group g with a non-empty clamped row range owns the tiles that
+// intersect it, the item's row range being that intersection.  After the
+// groups come the items that zero the rows at or past the clamped total
+// (g == G).  g < 0 means "no item" (the grid is sized for the worst case:
+// at most ceil(M/tm) + G items, since the clamped ranges are disjoint inside
+// [0, M)).  Every lane of the calling wave gets the result.  Callers pass a
+// compile-time tm, so the divisions become multiply-shifts.
 
 struct WorkItem {
     int g, tile, lo, hi;
@@ -152,36 +224,32 @@ struct WorkItem {
 
 __device__ __forceinline__ WorkItem find_work_item(const int32_t* __restrict__ group_sizes, int G,
                                                    int M, int tm, int w) {
-    const int lane = lane_id();
     int carry_rows = 0, carry_items = 0;
     for (int base = 0; base < G; base += 64) {
-        const int g = base + lane;
-        const int s = g < G ? group_sizes[g] : 0;
-        const int incl = wave_incl_scan(s);
-        const int o = carry_rows + incl - s;
-        const int c = s > 0 ? (o + s - 1) / tm - o / tm + 1 : 0;
+        const GroupChunk ch = group_chunk(group_sizes, G, M, base, carry_rows);
+        const int c = ch.hi > ch.lo ? (ch.hi - 1) / tm - ch.lo / tm + 1 : 0;
         const int inclc = wave_incl_scan(c);
         const int W = carry_items + inclc - c;
         const bool own = c > 0 && w >= W && w < W + c;
         const unsigned long long mask = __ballot(own);
         if (mask) {
             const int src = __ffsll((long long)mask) - 1;
-            const int go = lane_value(o, src);
-            const int gsz = lane_value(s, src);
+            const int glo = lane_value(ch.lo, src);
+            const int ghi = lane_value(ch.hi, src);
             const int gW = lane_value(W, src);
-            const int t = go / tm + (w - gW);
+            const int t = glo / tm + (w - gW);
             WorkItem it;
             it.g = base + src;
             it.tile = t;
-            it.lo = max(go, t * tm);
-            it.hi = min(go + gsz, (t + 1) * tm);
+            it.lo = max(glo, t * tm);
+            it.hi = min(ghi, (t + 1) * tm);
             return it;
         }
-        carry_rows += lane_value(incl, 63);
+        carry_rows = ch.next_carry;
         carry_items += lane_value(inclc, 63);
     }
     WorkItem it;
-    const int total = carry_rows;
+    const int total = min(carry_rows, M);
     const int t = total / tm + (w - carry_items);
     it.g = G;
     it.tile = t;

@@ -200,7 +200,8 @@ __global__ __launch_bounds__(kThreads, 2) void fp8_fwd_kernel(
     const void* __restrict__ lhs, const float* __restrict__ lhs_scale,
     const uint8_t* __restrict__ rhs, const float* __restrict__ rhs_scale,
     const int32_t* __restrict__ group_sizes, int M, int K, int N, int G, void* __restrict__ out,
-    uint8_t* __restrict__ q_out, float* __restrict__ s_out, int ntiles_n, int nblocks) {
+    uint8_t* __restrict__ q_out, float* __restrict__ s_out, int ntiles_n, int nblocks,
+    int32_t* __restrict__ status) {
     static_assert(TM == 64 || TM == 48, "64- or 48-row tiles");
     constexpr int MB = TM / 16;   // 16-row blocks of the tile
     constexpr int NB = WN / 16;   // 16-column blocks per wave
@@ -221,6 +222,9 @@ __global__ __launch_bounds__(kThreads, 2) void fp8_fwd_kernel(
     if (wave == 0) {
         const WorkItem it = find_work_item(group_sizes, G, M, TM, w);
         if (lane == 0) s_item = it;
+    } else if (wave == 1 && blockIdx.x == 0) {   // the call's device status word
+        const int st = group_status(group_sizes, G, M);
+        if (lane == 0) status[0] = st;
     }
     __syncthreads();
     const WorkItem it = s_item;
@@ -555,7 +559,8 @@ __global__ __launch_bounds__(64 * NW, NW == 16 ? 4 : 2) void fp8_fwd_ws_kernel( 
     const void* __restrict__ lhs, const float* __restrict__ lhs_scale,
     const uint8_t* __restrict__ rhs, const void* __restrict__ rhs_scale_v,
     const int32_t* __restrict__ group_sizes, int M, int K, int N, int G, void* __restrict__ out,
-    uint8_t* __restrict__ q_out, float* __restrict__ s_out, int ntiles_n, int nblocks) {
+    uint8_t* __restrict__ q_out, float* __restrict__ s_out, int ntiles_n, int nblocks,
+    int32_t* __restrict__ status) {
     static_assert(TM == 64 || TM == 48, "64- or 48-row tiles");
     static_assert(NW == 8 || NW == 16, "8 or 16 waves");
     static_assert(B4 ? (NW == 16 && (TN == 512 || TN == 256 || TN == 128)) : TN == 512,
@@ -589,6 +594,9 @@ __global__ __launch_bounds__(64 * NW, NW == 16 ? 4 : 2) void fp8_fwd_ws_kernel( 
     if (wave == 0) {
         const WorkItem it = find_work_item(group_sizes, G, M, TM, w);
         if (lane == 0) s_item = it;
+    } else if (wave == 1 && blockIdx.x == 0) {   // the call's device status word
+        const int st = group_status(group_sizes, G, M);
+        if (lane == 0) status[0] = st;
     }
     __syncthreads();
     const WorkItem it = s_item;
@@ -804,7 +812,7 @@ __global__ __launch_bounds__(1024, 4) void fp8_fwd_wsn_kernel(
     const void* __restrict__ lhs, const float* __restrict__ lhs_scale,
     const uint8_t* __restrict__ rhs, const void* __restrict__ rhs_scale_v,
     const int32_t* __restrict__ group_sizes, int M, int K, int N, int G, void* __restrict__ out,
-    int nblocks) {
+    int nblocks, int32_t* __restrict__ status) {
     constexpr int TM = 48, MB = TM / 16, NC = 8, CWID = 64, NBC = CWID / 16, TN = 512;
     constexpr int kThr = 1024;
     constexpr int OUT_BYTES = OUT_BF16 ? 2 : 4;
@@ -825,6 +833,9 @@ __global__ __launch_bounds__(1024, 4) void fp8_fwd_wsn_kernel(
     if (wave == 0) {
         const WorkItem it = find_work_item(group_sizes, G, M, TM, w);
         if (lane == 0) s_item = it;
+    } else if (wave == 1 && blockIdx.x == 0) {   // the call's device status word
+        const int st = group_status(group_sizes, G, M);
+        if (lane == 0) status[0] = st;
     }
     __syncthreads();
     const WorkItem it = s_item;
@@ -1004,37 +1015,41 @@ __global__ __launch_bounds__(1024, 4) void fp8_fwd_wsn_kernel(
     for (int t = 1; t < ntiles; ++t) tile(t, std::false_type{});
 }
 
+// The row-resident kernel addresses one expert's weights with 32-bit byte
+// offsets (at most N*K bytes of codes), so it runs only when they fit.
+inline bool wsn_offsets_fit(int K, int N) { return (int64_t)N * K < (int64_t(1) << 32); }
+
 template <int KIND, int KBM, bool B4 = false>
 hipError_t launch_wsn(const void* lhs, const float* lhs_scale, const uint8_t* rhs,
                       const void* rhs_scale, const int32_t* group_sizes, int M, int K, int N,
-                      int G, void* out, bool out_bf16, hipStream_t stream) {
+                      int G, void* out, bool out_bf16, int32_t* status, hipStream_t stream) {
     const int nblocks = (int)max_work_items(M, G, 48);
     if (out_bf16)
         hipLaunchKernelGGL((fp8_fwd_wsn_kernel<KIND, true, KBM, B4>), dim3(nblocks), dim3(1024), 0,
                            stream, lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N, G, out,
-                           nblocks);
+                           nblocks, status);
     else
         hipLaunchKernelGGL((fp8_fwd_wsn_kernel<KIND, false, KBM, B4>), dim3(nblocks), dim3(1024), 0,
                            stream, lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N, G, out,
-                           nblocks);
+                           nblocks, status);
     return hipGetLastError();
 }
 
 template <int KIND, int TM, bool WRITE_Q, int NW = 8, int TN = 512, bool B4 = false>
 hipError_t launch_ws(const void* lhs, const float* lhs_scale, const uint8_t* rhs,
                      const void* rhs_scale, const int32_t* group_sizes, int M, int K, int N, int G,
-                     void* out, bool out_bf16, uint8_t* q_out, float* scale_out, hipStream_t stream) {
+                     void* out, bool out_bf16, uint8_t* q_out, float* scale_out, int32_t* status, hipStream_t stream) {
     const int ntiles_n = N / TN;
     const int64_t items = max_work_items(M, G, TM);
     const int nblocks = (int)(items * ntiles_n);
     if (out_bf16)
         hipLaunchKernelGGL((fp8_fwd_ws_kernel<KIND, true, TM, WRITE_Q, NW, TN, B4>), dim3(nblocks),
                            dim3(64 * NW), 0, stream, lhs, lhs_scale, rhs, rhs_scale, group_sizes, M,
-                           K, N, G, out, q_out, scale_out, ntiles_n, nblocks);
+                           K, N, G, out, q_out, scale_out, ntiles_n, nblocks, status);
     else
         hipLaunchKernelGGL((fp8_fwd_ws_kernel<KIND, false, TM, WRITE_Q, NW, TN, B4>), dim3(nblocks),
                            dim3(64 * NW), 0, stream, lhs, lhs_scale, rhs, rhs_scale, group_sizes, M,
-                           K, N, G, out, q_out, scale_out, ntiles_n, nblocks);
+                           K, N, G, out, q_out, scale_out, ntiles_n, nblocks, status);
     return hipGetLastError();
 }
 
@@ -1043,7 +1058,7 @@ hipError_t launch_ws(const void* lhs, const float* lhs_scale, const uint8_t* rhs
 template <int KIND>
 hipError_t launch_mxfp4_kind(const void* lhs, const float* lhs_scale, const uint8_t* rhs_q,
                              const uint8_t* rhs_e8, const int32_t* group_sizes, int M, int K,
-                             int N, int G, void* out, bool out_bf16, hipStream_t stream) {
+                             int N, int G, void* out, bool out_bf16, int32_t* status, hipStream_t stream) {
     static const int forced_tn = [] {
         const char* e = std::getenv("GMM_MXFP4_TN");
         return e ? std::atoi(e) : 0;
@@ -1057,42 +1072,42 @@ hipError_t launch_mxfp4_kind(const void* lhs, const float* lhs_scale, const uint
         const char* e = std::getenv("GMM_FP8_WSN");
         return !(e && std::atoi(e) == 0);
     }();
-    if (use_wsn && forced_tn == 0 && N % 512 == 0 && N >= 1024 && K <= 1024) {
+    if (use_wsn && forced_tn == 0 && N % 512 == 0 && N >= 1024 && K <= 1024 && wsn_offsets_fit(K, N)) {
         if (K <= 512)
             return launch_wsn<KIND, 4, true>(lhs, lhs_scale, rhs_q, rhs_e8, group_sizes, M, K, N, G,
-                                             out, out_bf16, stream);
+                                             out, out_bf16, status, stream);
         return launch_wsn<KIND, 8, true>(lhs, lhs_scale, rhs_q, rhs_e8, group_sizes, M, K, N, G, out,
-                                         out_bf16, stream);
+                                         out_bf16, status, stream);
     }
     if (tn == 512)
         return launch_ws<KIND, 48, false, 16, 512, true>(lhs, lhs_scale, rhs_q, rhs_e8, group_sizes,
                                                          M, K, N, G, out, out_bf16, nullptr,
-                                                         nullptr, stream);
+                                                         nullptr, status, stream);
     if (tn == 256)
         return launch_ws<KIND, 48, false, 16, 256, true>(lhs, lhs_scale, rhs_q, rhs_e8, group_sizes,
                                                          M, K, N, G, out, out_bf16, nullptr,
-                                                         nullptr, stream);
+                                                         nullptr, status, stream);
     return launch_ws<KIND, 48, false, 16, 128, true>(lhs, lhs_scale, rhs_q, rhs_e8, group_sizes, M,
                                                      K, N, G, out, out_bf16, nullptr, nullptr,
-                                                     stream);
+                                                     status, stream);
 }
 
 template <int KIND, int WN, int TM, bool WRITE_Q, bool SWIGLU = false>
 hipError_t launch_cfg(const void* lhs, const float* lhs_scale, const uint8_t* rhs,
                       const float* rhs_scale, const int32_t* group_sizes, int M, int K, int N,
                       int G, void* out, bool out_bf16, uint8_t* q_out, float* scale_out,
-                      hipStream_t stream) {
+                      int32_t* status, hipStream_t stream) {
     const int ntiles_n = N / (SWIGLU ? kWaves * WN / 2 : kWaves * WN);
     const int64_t items = max_work_items(M, G, TM);
     const int nblocks = (int)(items * ntiles_n);
     if (out_bf16)
         hipLaunchKernelGGL((fp8_fwd_kernel<KIND, true, WN, TM, WRITE_Q, SWIGLU>), dim3(nblocks), dim3(kThreads),
                            0, stream, lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N, G, out,
-                           q_out, scale_out, ntiles_n, nblocks);
+                           q_out, scale_out, ntiles_n, nblocks, status);
     else
         hipLaunchKernelGGL((fp8_fwd_kernel<KIND, false, WN, TM, WRITE_Q, SWIGLU>), dim3(nblocks), dim3(kThreads),
                            0, stream, lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N, G, out,
-                           q_out, scale_out, ntiles_n, nblocks);
+                           q_out, scale_out, ntiles_n, nblocks, status);
     return hipGetLastError();
 }
 
@@ -1100,14 +1115,14 @@ template <int KIND, int WN, int TM>
 hipError_t launch_wn(const void* lhs, const float* lhs_scale, const uint8_t* rhs,
                      const float* rhs_scale, const int32_t* group_sizes, int M, int K, int N,
                      int G, void* out, bool out_bf16, uint8_t* q_out, float* scale_out,
-                     hipStream_t stream) {
+                     int32_t* status, hipStream_t stream) {
     if constexpr (KIND != kLhsE4M3) {
         if (q_out != nullptr)
             return launch_cfg<KIND, WN, TM, true>(lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K,
-                                                  N, G, out, out_bf16, q_out, scale_out, stream);
+                                                  N, G, out, out_bf16, q_out, scale_out, status, stream);
     }
     return launch_cfg<KIND, WN, TM, false>(lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N,
-                                           G, out, out_bf16, q_out, scale_out, stream);
+                                           G, out, out_bf16, q_out, scale_out, status, stream);
 }
 
 // Tile: the widest of 512/256/128 columns that divides N (fewest
@@ -1119,7 +1134,7 @@ template <int KIND>
 hipError_t launch_kind(const void* lhs, const float* lhs_scale, const uint8_t* rhs,
                        const float* rhs_scale, const int32_t* group_sizes, int M, int K, int N,
                        int G, void* out, bool out_bf16, uint8_t* q_out, float* scale_out,
-                       hipStream_t stream) {
+                       int32_t* status, hipStream_t stream) {
     static const int forced_wn = [] {
         const char* e = std::getenv("GMM_FP8_WN");
         return e ? std::atoi(e) : 0;
@@ -1154,27 +1169,27 @@ hipError_t launch_kind(const void* lhs, const float* lhs_scale, const uint8_t* r
         return !(e && std::atoi(e) == 0);
     }();
     if (use_wsn && forced_wn == 0 && forced_tm == 0 && N % 512 == 0 && N >= 1024 && K <= 1024 &&
-        (q_out == nullptr || KIND == kLhsE4M3)) {
+        wsn_offsets_fit(K, N) && (q_out == nullptr || KIND == kLhsE4M3)) {
         if (K <= 512)
             return launch_wsn<KIND, 4>(lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N, G, out,
-                                       out_bf16, stream);
+                                       out_bf16, status, stream);
         return launch_wsn<KIND, 8>(lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N, G, out,
-                                   out_bf16, stream);
+                                   out_bf16, status, stream);
     }
     if (use_ws && wn == 64 && tm == 48 && ws_waves == 16 && (q_out == nullptr || KIND == kLhsE4M3))
         return launch_ws<KIND, 48, false, 16>(lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N,
-                                              G, out, out_bf16, q_out, scale_out, stream);
+                                              G, out, out_bf16, q_out, scale_out, status, stream);
     if (use_ws && wn == 64 && tm == 48) {
         if (q_out != nullptr && KIND != kLhsE4M3)
             return launch_ws<KIND, 48, true>(lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N,
-                                             G, out, out_bf16, q_out, scale_out, stream);
+                                             G, out, out_bf16, q_out, scale_out, status, stream);
         return launch_ws<KIND, 48, false>(lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N, G,
-                                          out, out_bf16, q_out, scale_out, stream);
+                                          out, out_bf16, q_out, scale_out, status, stream);
     }
 #define GMM_FP8_WN_TM(WN_, TM_)                                                                  \
     if (wn == WN_ && tm == TM_)                                                                  \
         return launch_wn<KIND, WN_, TM_>(lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N, G, \
-                                         out, out_bf16, q_out, scale_out, stream);
+                                         out, out_bf16, q_out, scale_out, status, stream);
     GMM_FP8_WN_TM(64, 64)
     GMM_FP8_WN_TM(64, 48)
     GMM_FP8_WN_TM(32, 64)
@@ -1182,7 +1197,7 @@ hipError_t launch_kind(const void* lhs, const float* lhs_scale, const uint8_t* r
     GMM_FP8_WN_TM(16, 48)
 #undef GMM_FP8_WN_TM
     return launch_wn<KIND, 16, 64>(lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N, G, out,
-                                   out_bf16, q_out, scale_out, stream);
+                                   out_bf16, q_out, scale_out, status, stream);
 }
 
 // Fused gate+up: 256 output columns per workgroup; 48-row tiles under the
@@ -1191,7 +1206,7 @@ template <int KIND>
 hipError_t launch_swiglu_kind(const void* lhs, const float* lhs_scale, const uint8_t* rhs,
                               const float* rhs_scale, const int32_t* group_sizes, int M, int K,
                               int N, int G, void* out, bool out_bf16, uint8_t* act_q,
-                              float* act_scale, hipStream_t stream) {
+                              float* act_scale, int32_t* status, hipStream_t stream) {
     // 48-row tiles while their grid is at most two rounds of the chip (the
     // tile sweep: wi gate+up, 406 workgroups on 256 CUs, 42.0 us at 48 rows
     // vs 45.9 at 64; 810 workgroups, 79.2 vs 73.1 us).  GMM_SWIGLU_TM=<48|64>
@@ -1204,9 +1219,9 @@ hipError_t launch_swiglu_kind(const void* lhs, const float* lhs_scale, const uin
                       (forced_tm != 64 && max_work_items(M, G, 48) * (N / 256) <= 2 * device_cus());
     if (tm48)
         return launch_cfg<KIND, 64, 48, false, true>(lhs, lhs_scale, rhs, rhs_scale, group_sizes, M,
-                                                     K, N, G, out, out_bf16, act_q, act_scale, stream);
+                                                     K, N, G, out, out_bf16, act_q, act_scale, status, stream);
     return launch_cfg<KIND, 64, 64, false, true>(lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K,
-                                                 N, G, out, out_bf16, act_q, act_scale, stream);
+                                                 N, G, out, out_bf16, act_q, act_scale, status, stream);
 }
 
 }  // namespace
@@ -1215,51 +1230,51 @@ hipError_t launch_fp8_fwd_swiglu(const void* lhs, int lhs_kind, const float* lhs
                                  const uint8_t* rhs, const float* rhs_scale,
                                  const int32_t* group_sizes, int M, int K, int N, int G,
                                  void* out, bool out_bf16, uint8_t* act_q, float* act_scale,
-                                 hipStream_t stream) {
+                                 int32_t* status, hipStream_t stream) {
     switch (lhs_kind) {
         case kLhsE4M3:
             return launch_swiglu_kind<kLhsE4M3>(lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N,
-                                                G, out, out_bf16, act_q, act_scale, stream);
+                                                G, out, out_bf16, act_q, act_scale, status, stream);
         case kLhsBF16:
             return launch_swiglu_kind<kLhsBF16>(lhs, nullptr, rhs, rhs_scale, group_sizes, M, K, N,
-                                                G, out, out_bf16, act_q, act_scale, stream);
+                                                G, out, out_bf16, act_q, act_scale, status, stream);
         default:
             return launch_swiglu_kind<kLhsF32>(lhs, nullptr, rhs, rhs_scale, group_sizes, M, K, N,
-                                               G, out, out_bf16, act_q, act_scale, stream);
+                                               G, out, out_bf16, act_q, act_scale, status, stream);
     }
 }
 
 hipError_t launch_fp8_mxfp4_fwd(const void* lhs, int lhs_kind, const float* lhs_scale,
                                 const uint8_t* rhs_q, const uint8_t* rhs_scale,
                                 const int32_t* group_sizes, int M, int K, int N, int G, void* out,
-                                bool out_bf16, hipStream_t stream) {
+                                bool out_bf16, int32_t* status, hipStream_t stream) {
     switch (lhs_kind) {
         case kLhsE4M3:
             return launch_mxfp4_kind<kLhsE4M3>(lhs, lhs_scale, rhs_q, rhs_scale, group_sizes, M, K,
-                                               N, G, out, out_bf16, stream);
+                                               N, G, out, out_bf16, status, stream);
         case kLhsBF16:
             return launch_mxfp4_kind<kLhsBF16>(lhs, nullptr, rhs_q, rhs_scale, group_sizes, M, K, N,
-                                               G, out, out_bf16, stream);
+                                               G, out, out_bf16, status, stream);
         default:
             return launch_mxfp4_kind<kLhsF32>(lhs, nullptr, rhs_q, rhs_scale, group_sizes, M, K, N,
-                                              G, out, out_bf16, stream);
+                                              G, out, out_bf16, status, stream);
     }
 }
 
 hipError_t launch_fp8_fwd(const void* lhs, int lhs_kind, const float* lhs_scale,
                           const uint8_t* rhs, const float* rhs_scale,
                           const int32_t* group_sizes, int M, int K, int N, int G, void* out,
-                          bool out_bf16, uint8_t* q_out, float* scale_out, hipStream_t stream) {
+                          bool out_bf16, uint8_t* q_out, float* scale_out, int32_t* status, hipStream_t stream) {
     switch (lhs_kind) {
         case kLhsE4M3:
             return launch_kind<kLhsE4M3>(lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N, G,
-                                         out, out_bf16, nullptr, nullptr, stream);
+                                         out, out_bf16, nullptr, nullptr, status, stream);
         case kLhsBF16:
             return launch_kind<kLhsBF16>(lhs, nullptr, rhs, rhs_scale, group_sizes, M, K, N, G,
-                                         out, out_bf16, q_out, scale_out, stream);
+                                         out, out_bf16, q_out, scale_out, status, stream);
         default:
             return launch_kind<kLhsF32>(lhs, nullptr, rhs, rhs_scale, group_sizes, M, K, N, G,
-                                        out, out_bf16, q_out, scale_out, stream);
+                                        out, out_bf16, q_out, scale_out, status, stream);
     }
 }
 

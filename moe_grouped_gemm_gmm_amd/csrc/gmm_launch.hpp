@@ -19,9 +19,13 @@ inline int device_cus() {
     return cus;
 }
 
+// Every grouped launcher takes `status`: a device int32 that block 0 of the
+// launch sets to the call's device status (bits kDevSumGtM, kDevNegativeSize
+// of gmm_device.hpp; 0 when group_sizes keeps the contract).
+
 hipError_t launch_group_metadata(const int32_t* group_sizes, int G, int M, int tm,
                                  int32_t* offsets, int32_t* work, int capacity,
-                                 int32_t* num_work, hipStream_t stream);
+                                 int32_t* num_work, int32_t* status, hipStream_t stream);
 
 // x_bf16: true for bf16 input, false for fp32.
 hipError_t launch_quantize_lhs(const void* x, bool x_bf16, int64_t M, int64_t K, uint8_t* q,
@@ -29,6 +33,15 @@ hipError_t launch_quantize_lhs(const void* x, bool x_bf16, int64_t M, int64_t K,
 
 hipError_t launch_quantize_rhs(const void* w, bool w_bf16, int64_t G, int64_t K, int64_t N,
                                uint8_t* q, float* scale, hipStream_t stream);
+
+// Logical [G,K,N] E4M3 codes into the packed order of launch_quantize_rhs.
+hipError_t launch_pack_rhs(const uint8_t* q, int64_t G, int64_t K, int64_t N, uint8_t* packed,
+                           hipStream_t stream);
+
+// s = a/448 and its guarded inverse for n block abs-maxima (the quantisers'
+// own device routines).
+hipError_t launch_quant_scales(const float* amax, int64_t n, float* scale, float* inv,
+                               hipStream_t stream);
 
 // MXFP4 weights in the forward's packed operand order (codes G*K*N/2 bytes,
 // E8M0 scales G*K*N/32 bytes).
@@ -39,7 +52,7 @@ hipError_t launch_quantize_rhs_mxfp4(const void* w, bool w_bf16, int64_t G, int6
 hipError_t launch_fp8_fwd(const void* lhs, int lhs_kind, const float* lhs_scale,
                           const uint8_t* rhs, const float* rhs_scale,
                           const int32_t* group_sizes, int M, int K, int N, int G, void* out,
-                          bool out_bf16, uint8_t* q_out, float* scale_out, hipStream_t stream);
+                          bool out_bf16, uint8_t* q_out, float* scale_out, int32_t* status, hipStream_t stream);
 
 // Fused gate+up: rhs has 2N columns (gate, then up); out = silu(gate) * up,
 // [M,N]; act_q/act_scale (both or neither) the 1x128 quantised activation.
@@ -47,21 +60,21 @@ hipError_t launch_fp8_fwd_swiglu(const void* lhs, int lhs_kind, const float* lhs
                                  const uint8_t* rhs, const float* rhs_scale,
                                  const int32_t* group_sizes, int M, int K, int N, int G,
                                  void* out, bool out_bf16, uint8_t* act_q, float* act_scale,
-                                 hipStream_t stream);
+                                 int32_t* status, hipStream_t stream);
 
 // FP8 (1x128) LHS against packed MXFP4 weights.
 hipError_t launch_fp8_mxfp4_fwd(const void* lhs, int lhs_kind, const float* lhs_scale,
                                 const uint8_t* rhs_q, const uint8_t* rhs_scale,
                                 const int32_t* group_sizes, int M, int K, int N, int G, void* out,
-                                bool out_bf16, hipStream_t stream);
+                                bool out_bf16, int32_t* status, hipStream_t stream);
 
 hipError_t launch_bf16_fwd(const void* lhs, const void* rhs, const int32_t* group_sizes, int M,
-                           int K, int N, int G, void* out, bool out_bf16, hipStream_t stream);
+                           int K, int N, int G, void* out, bool out_bf16, int32_t* status, hipStream_t stream);
 
 hipError_t launch_bf16_dx(const void* dy, const void* w, const int32_t* group_sizes, int M,
-                          int K, int N, int G, void* dx, bool out_bf16, hipStream_t stream);
+                          int K, int N, int G, void* dx, bool out_bf16, int32_t* status, hipStream_t stream);
 
 hipError_t launch_tgmm(const void* x, const void* dy, const int32_t* group_sizes, int M, int K,
-                       int N, int G, void* dw, bool out_bf16, hipStream_t stream);
+                       int N, int G, void* dw, bool out_bf16, int32_t* status, hipStream_t stream);
 
 }  // namespace gmm

@@ -17,7 +17,8 @@ __global__ __launch_bounds__(256) void group_metadata_kernel(const int32_t* __re
                                                              int32_t* __restrict__ offsets,
                                                              int32_t* __restrict__ work,
                                                              int capacity,
-                                                             int32_t* __restrict__ num_work) {
+                                                             int32_t* __restrict__ num_work,
+                                                             int32_t* __restrict__ status) {
     const int wave = threadIdx.x >> 6, lane = lane_id();
     const int w = blockIdx.x * 4 + wave;
     if (w < capacity) {
@@ -30,32 +31,34 @@ __global__ __launch_bounds__(256) void group_metadata_kernel(const int32_t* __re
         }
     }
     if (blockIdx.x == 0 && wave == 0) {
+        // offsets: the first row of each group's clamped range, then the
+        // clamped total; the item count: the groups' tiles plus the tail's
         int carry_rows = 0, carry_items = 0;
+        bool negative = false;
         for (int base = 0; base < G; base += 64) {
-            const int g = base + lane;
-            const int s = g < G ? group_sizes[g] : 0;
-            const int incl = wave_incl_scan(s);
-            const int o = carry_rows + incl - s;
-            const int c = s > 0 ? (o + s - 1) / tm - o / tm + 1 : 0;
-            if (g < G) offsets[g] = o;
-            carry_rows += lane_value(incl, 63);
+            const GroupChunk ch = group_chunk(group_sizes, G, M, base, carry_rows);
+            const int c = ch.hi > ch.lo ? (ch.hi - 1) / tm - ch.lo / tm + 1 : 0;
+            if (base + lane < G) offsets[base + lane] = ch.lo;
+            carry_rows = ch.next_carry;
             carry_items += lane_value(wave_incl_scan(c), 63);
+            negative = negative || ch.negative;
         }
         if (lane == 0) {
-            const int total = carry_rows;
+            const int total = min(carry_rows, M);
             const int tail = total < M ? (M + tm - 1) / tm - total / tm : 0;
             offsets[G] = total;
             num_work[0] = carry_items + tail;
+            status[0] = (carry_rows > M ? kDevSumGtM : 0) | (negative ? kDevNegativeSize : 0);
         }
     }
 }
 
 hipError_t launch_group_metadata(const int32_t* group_sizes, int G, int M, int tm,
                                  int32_t* offsets, int32_t* work, int capacity,
-                                 int32_t* num_work, hipStream_t stream) {
+                                 int32_t* num_work, int32_t* status, hipStream_t stream) {
     const int blocks = (capacity + 3) / 4;
     hipLaunchKernelGGL(group_metadata_kernel, dim3(blocks), dim3(256), 0, stream, group_sizes, G,
-                       M, tm, offsets, work, capacity, num_work);
+                       M, tm, offsets, work, capacity, num_work, status);
     return hipGetLastError();
 }
 
@@ -189,6 +192,68 @@ __global__ __launch_bounds__(256) void quantize_rhs_kernel(const void* __restric
         *reinterpret_cast<uint4*>(q + rhs_packed_offset(g, n, k0 + 16 * c, N, K)) = o;
     }
     if (t == 0) scale[blk] = s;
+}
+
+// ------------------------------------------------------ RHS code packing --
+// E4M3 codes quantised elsewhere, logical [G,K,N], into the packed order
+// above.  One workgroup per 2 KB slab (expert g, 16-column block, 128-K
+// step): thread t reads the 16 codes of row k = 128*kb + t for the slab's
+// columns into LDS, then writes one 16-byte run: half h = t / 64, lane
+// l = t % 64 holds column 16*nb + l%16, k = 128*kb + 32*(l/16) + 16*h + e.
+__global__ __launch_bounds__(128) void pack_rhs_kernel(const uint8_t* __restrict__ q, int K, int N,
+                                                       uint8_t* __restrict__ packed) {
+    __shared__ uint8_t tile[kQBlock][16 + 4];   // [k][n]; 20-byte rows spread the column reads
+    const int nkb = K / kQBlock, nn16 = N / 16;
+    const int64_t slab = blockIdx.x;               // (g * N/16 + nb) * K/128 + kb
+    const int kb = (int)(slab % nkb);
+    const int64_t gnb = slab / nkb;
+    const int nb = (int)(gnb % nn16);
+    const int64_t g = gnb / nn16;
+    const int t = threadIdx.x;
+    const uint4 row = *reinterpret_cast<const uint4*>(q + (g * K + kb * kQBlock + t) * N + nb * 16);
+    const uint32_t words[4] = {row.x, row.y, row.z, row.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint32_t*>(&tile[t][4 * i]) = words[i];
+    __syncthreads();
+    const int h = t >> 6, l = t & 63, col = l & 15, k0 = 32 * (l >> 4) + 16 * h;
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        o[i] = (uint32_t)tile[k0 + 4 * i][col] | ((uint32_t)tile[k0 + 4 * i + 1][col] << 8) |
+               ((uint32_t)tile[k0 + 4 * i + 2][col] << 16) | ((uint32_t)tile[k0 + 4 * i + 3][col] << 24);
+    *reinterpret_cast<uint4*>(packed + slab * 2048 + h * 1024 + l * 16) = make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+hipError_t launch_pack_rhs(const uint8_t* q, int64_t G, int64_t K, int64_t N, uint8_t* packed,
+                           hipStream_t stream) {
+    const int64_t slabs = G * (N / 16) * (K / kQBlock);
+    hipLaunchKernelGGL(pack_rhs_kernel, dim3((unsigned)slabs), dim3(128), 0, stream, q, (int)K,
+                       (int)N, packed);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------- the recipe's scale pair --
+// s = a/448 and inv = (s == 0 ? 0 : 1/s) for a list of block abs-maxima,
+// through the same device routines every quantiser above and the fused
+// forward use (quant_scale, quant_inv).
+__global__ __launch_bounds__(256) void quant_scales_kernel(const float* __restrict__ amax, int64_t n,
+                                                           float* __restrict__ scale,
+                                                           float* __restrict__ inv) {
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) {
+        const float s = quant_scale(amax[i]);
+        scale[i] = s;
+        inv[i] = quant_inv(s);
+    }
+}
+
+hipError_t launch_quant_scales(const float* amax, int64_t n, float* scale, float* inv,
+                               hipStream_t stream) {
+    int64_t blocks = (n + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
+    hipLaunchKernelGGL(quant_scales_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, amax, n,
+                       scale, inv);
+    return hipGetLastError();
 }
 
 // --------------------------------------------------------- MXFP4 RHS --

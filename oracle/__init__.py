@@ -53,6 +53,7 @@ def _load():
     lib.oracle_e2m1_encode.argtypes = [ctypes.c_double]
     lib.oracle_quantize_rhs_mxfp4.argtypes = [P, I, I, I, P, P]
     lib.oracle_gmm_fp8_mxfp4.argtypes = [P, P, P, P, P, I, I, I, I, P]
+    lib.oracle_quant_scales.argtypes = [P, I, P, P]
     lib.oracle_num_threads.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -118,6 +119,17 @@ def group_offsets(group_sizes, M):
     if rc != 0:
         raise ValueError("group sizes negative or summing past M")
     return off
+
+
+def quant_scales(amax):
+    """The quantiser's scale pair for block abs-maxima (fp32): (a/448, guarded 1/s)."""
+    lib = _load()
+    a, pa = _c(amax, np.float32)
+    s = np.empty_like(a)
+    inv = np.empty_like(a)
+    lib.oracle_quant_scales(pa, a.size, s.ctypes.data_as(ctypes.c_void_p),
+                            inv.ctypes.data_as(ctypes.c_void_p))
+    return s, inv
 
 
 def work_list(group_sizes, M, tm):

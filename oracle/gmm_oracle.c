@@ -164,6 +164,24 @@ void oracle_e4m3_encode_array(const float *x, int64_t n, uint8_t *out)
 /* One quantisation block per [V2q]/[Q2]: abs-max over the block's values,
  * s = a/448, inv = (s == 0 ? 0 : 1/s), code = e4m3(x*inv).  `vals` holds
  * the block's n values (already exact fp32), the codes go to `codes`. */
+/* The block scale and its guarded inverse ([V2q]): s = a/448, inv = (s == 0
+ * ? 0 : 1/s), each one IEEE fp32 division. */
+static void scale_pair(float a, float *s, float *inv)
+{
+    *s = a / E4M3_MAX;
+    *inv = (*s == 0.0f) ? 0.0f : 1.0f / *s;
+}
+
+/* scale_pair over n block abs-maxima (the step on its own, for checking a
+ * quantiser's scale arithmetic on every input it may see). */
+void oracle_quant_scales(const float *amax, int64_t n, float *scale, float *inv)
+{
+    int64_t i;
+#pragma omp parallel for schedule(static)
+    for (i = 0; i < n; ++i)
+        scale_pair(amax[i], scale + i, inv + i);
+}
+
 static float quantize_block(const float *vals, int n, uint8_t *codes)
 {
     float a = 0.0f, s, inv;
@@ -173,8 +191,7 @@ static float quantize_block(const float *vals, int n, uint8_t *codes)
         if (v > a)
             a = v;
     }
-    s = a / E4M3_MAX;
-    inv = (s == 0.0f) ? 0.0f : 1.0f / s;
+    scale_pair(a, &s, &inv);
     for (i = 0; i < n; ++i) {
         float y = vals[i] * inv;
         codes[i] = oracle_e4m3_encode(y);
@@ -248,34 +265,40 @@ int oracle_group_offsets(const int32_t *group_sizes, int64_t G, int64_t M,
 
 /* Work list of the grouped GEMM ([GG]: every tile belongs to one expert;
  * [V2z]: rows past the last group are zeroed).  Row tiles of height tm are
- * aligned to absolute row indices.  For every non-empty group g, in group
- * order, and every tile t that intersects rows [o_g, o_g + s_g), one entry
- * (g, t, max(o_g, t*tm), min(o_g+s_g, (t+1)*tm)).  Then one entry per tile
- * that holds rows >= total: (G, t, max(total, t*tm), min(M, (t+1)*tm)).
+ * aligned to absolute row indices.  For every group g whose rows
+ * [lo_g, hi_g) are non-empty, in group order, and every tile t that
+ * intersects them, one entry (g, t, max(lo_g, t*tm), min(hi_g, (t+1)*tm)).
+ * Then one entry per tile that holds rows >= total: (G, t, max(total, t*tm),
+ * min(M, (t+1)*tm)).  Inside the contract (sizes >= 0 summing to at most M)
+ * lo_g = o_g and hi_g = o_g + s_g.  Outside it the library's reading is
+ * taken: a negative size counts as 0, o_g sums the sizes so read, and every
+ * range is cut at M: lo_g = min(o_g, M), hi_g = min(o_g + s_g, M),
+ * total = min(sum, M).
  * work: [cap][4] int32; returns the entry count (or -1 on overflow). */
 int64_t oracle_work_list(const int32_t *group_sizes, int64_t G, int64_t M,
                          int64_t tm, int32_t *work, int64_t cap)
 {
-    int64_t n = 0, g, o = 0, t;
+    int64_t n = 0, g, o = 0, t, total;
     for (g = 0; g < G; ++g) {
-        int64_t s = group_sizes[g];
-        if (s > 0) {
-            for (t = o / tm; t * tm < o + s; ++t) {
-                int64_t lo = o > t * tm ? o : t * tm;
-                int64_t hi = (o + s) < (t + 1) * tm ? (o + s) : (t + 1) * tm;
-                if (n >= cap)
-                    return -1;
-                work[4 * n + 0] = (int32_t)g;
-                work[4 * n + 1] = (int32_t)t;
-                work[4 * n + 2] = (int32_t)lo;
-                work[4 * n + 3] = (int32_t)hi;
-                ++n;
-            }
+        int64_t s = group_sizes[g] > 0 ? group_sizes[g] : 0;
+        int64_t glo = o < M ? o : M;
+        int64_t ghi = o + s < M ? o + s : M;
+        for (t = glo / tm; glo < ghi && t * tm < ghi; ++t) {
+            int64_t lo = glo > t * tm ? glo : t * tm;
+            int64_t hi = ghi < (t + 1) * tm ? ghi : (t + 1) * tm;
+            if (n >= cap)
+                return -1;
+            work[4 * n + 0] = (int32_t)g;
+            work[4 * n + 1] = (int32_t)t;
+            work[4 * n + 2] = (int32_t)lo;
+            work[4 * n + 3] = (int32_t)hi;
+            ++n;
         }
         o += s;
     }
-    for (t = o / tm; t * tm < M; ++t) {
-        int64_t lo = o > t * tm ? o : t * tm;
+    total = o < M ? o : M;
+    for (t = total / tm; t * tm < M; ++t) {
+        int64_t lo = total > t * tm ? total : t * tm;
         int64_t hi = M < (t + 1) * tm ? M : (t + 1) * tm;
         if (lo >= hi)
             continue;

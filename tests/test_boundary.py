@@ -10,7 +10,8 @@ import pytest
 import moe_grouped_gemm_gmm_amd as gmm
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-OK, NULL, SHAPE, ALIGN, DTYPE = 0, 1, 2, 3, 4
+OK, NULL, SHAPE, ALIGN, DTYPE, WORKSPACE = 0, 1, 2, 3, 4, 5
+WSB = 256      # the workspace size every grouped call needs today
 
 # fake device addresses: never dereferenced, the checks fail first
 A = 0x10000
@@ -30,7 +31,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_symbols()
-    assert len(names) == 12
+    assert len(names) == 16
     assert sorted(names) == sorted(gmm.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
@@ -47,9 +48,9 @@ def P(x):
 
 
 def fp8(lib, lhs=A, lhs_dt=1, lhs_scale=0, rhs=A, rhs_scale=A, gs=A, M=256, K=256, N=256, G=4,
-        out=A, out_dt=1, q=0, s=0):
+        out=A, out_dt=1, q=0, s=0, ws=A, wsb=WSB):
     return lib.gmm_fp8_fwd(P(lhs), lhs_dt, P(lhs_scale), P(rhs), P(rhs_scale), P(gs), M, K, N, G,
-                           P(out), out_dt, P(q), P(s), None)
+                           P(out), out_dt, P(q), P(s), P(ws), wsb, None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -64,6 +65,8 @@ def fp8(lib, lhs=A, lhs_dt=1, lhs_scale=0, rhs=A, rhs_scale=A, gs=A, M=256, K=25
     (dict(lhs_dt=2, lhs_scale=A, q=A, s=A), DTYPE),
     (dict(lhs_scale=A), DTYPE),
     (dict(M=0), OK),                              # empty input: nothing to do
+    (dict(ws=0), WORKSPACE), (dict(wsb=255), WORKSPACE), (dict(ws=MIS), ALIGN),
+    (dict(M=0, ws=0), WORKSPACE),                 # checked before the empty-input return
 ])
 def test_fp8_fwd_rejections(lib, kw, status):
     assert fp8(lib, **kw) == status
@@ -72,9 +75,9 @@ def test_fp8_fwd_rejections(lib, kw, status):
 
 
 def swiglu(lib, lhs=A, lhs_dt=1, lhs_scale=0, rhs=A, rhs_scale=A, gs=A, M=256, K=256, N=256, G=4,
-           out=A, out_dt=1, q=0, s=0):
+           out=A, out_dt=1, q=0, s=0, ws=A, wsb=WSB):
     return lib.gmm_fp8_fwd_swiglu(P(lhs), lhs_dt, P(lhs_scale), P(rhs), P(rhs_scale), P(gs), M, K,
-                                  N, G, P(out), out_dt, P(q), P(s), None)
+                                  N, G, P(out), out_dt, P(q), P(s), P(ws), wsb, None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -85,7 +88,7 @@ def swiglu(lib, lhs=A, lhs_dt=1, lhs_scale=0, rhs=A, rhs_scale=A, gs=A, M=256, K
     (dict(K=200), SHAPE), (dict(G=0), SHAPE),
     (dict(lhs_dt=2), NULL),                         # E4M3 lhs needs lhs_scale
     (dict(lhs_scale=A), DTYPE), (dict(out_dt=2), DTYPE),
-    (dict(M=0), OK),
+    (dict(M=0), OK), (dict(ws=0), WORKSPACE), (dict(wsb=16), WORKSPACE),
 ])
 def test_fp8_fwd_swiglu_rejections(lib, kw, status):
     assert swiglu(lib, **kw) == status
@@ -94,9 +97,9 @@ def test_fp8_fwd_swiglu_rejections(lib, kw, status):
 
 
 def mx(lib, lhs=A, lhs_dt=1, lhs_scale=0, rhs=A, rhs_scale=A, gs=A, M=256, K=256, N=256, G=4,
-       out=A, out_dt=1):
+       out=A, out_dt=1, ws=A, wsb=WSB):
     return lib.gmm_fp8_mxfp4_fwd(P(lhs), lhs_dt, P(lhs_scale), P(rhs), P(rhs_scale), P(gs), M, K,
-                                 N, G, P(out), out_dt, None)
+                                 N, G, P(out), out_dt, P(ws), wsb, None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -104,7 +107,7 @@ def mx(lib, lhs=A, lhs_dt=1, lhs_scale=0, rhs=A, rhs_scale=A, gs=A, M=256, K=256
     (dict(out=0), NULL), (dict(out=MIS), ALIGN), (dict(rhs_scale=MIS), ALIGN),
     (dict(K=200), SHAPE), (dict(N=100), SHAPE), (dict(G=0), SHAPE), (dict(M=-1), SHAPE),
     (dict(lhs_dt=2), NULL), (dict(lhs_scale=A), DTYPE), (dict(out_dt=2), DTYPE),
-    (dict(M=0), OK),
+    (dict(M=0), OK), (dict(ws=0), WORKSPACE), (dict(ws=MIS), ALIGN),
 ])
 def test_fp8_mxfp4_fwd_rejections(lib, kw, status):
     assert mx(lib, **kw) == status
@@ -137,23 +140,62 @@ def test_quantize_rejections(lib):
 
 def test_bf16_rejections(lib):
     f, t, d = lib.gmm_bf16_fwd, lib.tgmm_bf16, lib.gmm_bf16_dx
-    assert f(P(A), P(A), P(A), 64, 100, 128, 2, P(A), 1, None) == SHAPE
-    assert f(P(A), P(A), P(A), 64, 128, 64, 2, P(A), 1, None) == SHAPE
-    assert f(P(A), P(A), P(A), 64, 128, 128, 2, P(A), 3, None) == DTYPE
-    assert f(P(A), None, P(A), 64, 128, 128, 2, P(A), 1, None) == NULL
-    assert f(P(A), P(A), P(A), 0, 128, 128, 2, P(A), 1, None) == OK
-    assert t(P(A), P(A), P(A), 64, 64, 128, 2, P(A), 1, None) == SHAPE
-    assert t(P(A), P(MIS), P(A), 64, 128, 128, 2, P(A), 1, None) == ALIGN
-    assert d(P(A), P(A), P(A), 64, 128, 96, 2, P(A), 1, None) == SHAPE
-    assert d(P(A), P(A), P(A), 64, 128, 128, 0, P(A), 1, None) == SHAPE
+    W = (P(A), WSB, None)
+    assert f(P(A), P(A), P(A), 64, 100, 128, 2, P(A), 1, *W) == SHAPE
+    assert f(P(A), P(A), P(A), 64, 128, 64, 2, P(A), 1, *W) == SHAPE
+    assert f(P(A), P(A), P(A), 64, 128, 128, 2, P(A), 3, *W) == DTYPE
+    assert f(P(A), None, P(A), 64, 128, 128, 2, P(A), 1, *W) == NULL
+    assert f(P(A), P(A), P(A), 0, 128, 128, 2, P(A), 1, *W) == OK
+    assert f(P(A), P(A), P(A), 64, 128, 128, 2, P(A), 1, None, WSB, None) == WORKSPACE
+    assert t(P(A), P(A), P(A), 64, 64, 128, 2, P(A), 1, *W) == SHAPE
+    assert t(P(A), P(MIS), P(A), 64, 128, 128, 2, P(A), 1, *W) == ALIGN
+    assert t(P(A), P(A), P(A), 64, 128, 128, 2, P(A), 1, P(A), 8, None) == WORKSPACE
+    assert d(P(A), P(A), P(A), 64, 128, 96, 2, P(A), 1, *W) == SHAPE
+    assert d(P(A), P(A), P(A), 64, 128, 128, 0, P(A), 1, *W) == SHAPE
+    assert d(P(A), P(A), P(A), 64, 128, 128, 2, P(A), 1, P(MIS), WSB, None) == ALIGN
 
 
 def test_metadata_rejections(lib):
     m = lib.gmm_group_metadata
-    assert m(P(A), 4, 100, 100, P(A), P(A), 100, P(A), None) == SHAPE   # tile not a multiple of 16
-    assert m(P(A), 4, 100, 2048, P(A), P(A), 100, P(A), None) == SHAPE  # tile above 1024
-    assert m(P(A), 4, 1000, 128, P(A), P(A), 5, P(A), None) == SHAPE    # capacity too small
-    assert m(P(A), 4, 1000, 128, P(A), None, 20, P(A), None) == NULL
+    W = (P(A), WSB, None)
+    assert m(P(A), 4, 100, 100, P(A), P(A), 100, P(A), *W) == SHAPE   # tile not a multiple of 16
+    assert m(P(A), 4, 100, 2048, P(A), P(A), 100, P(A), *W) == SHAPE  # tile above 1024
+    assert m(P(A), 4, 1000, 128, P(A), P(A), 5, P(A), *W) == SHAPE    # capacity too small
+    assert m(P(A), 4, 1000, 128, P(A), None, 20, P(A), *W) == NULL
+    assert m(P(A), 4, 1000, 128, P(A), P(A), 20, P(A), None, 0, None) == WORKSPACE
+
+
+def test_workspace_bytes(lib):
+    for op in range(7):
+        assert lib.gmm_workspace_bytes(op, 65536, 2048, 512, 256) == WSB
+    assert lib.gmm_workspace_bytes(7, 1, 128, 128, 1) == 0
+    assert lib.gmm_workspace_bytes(-1, 1, 128, 128, 1) == 0
+    assert lib.gmm_status_string(WORKSPACE) == b"workspace missing or too small"
+
+
+def test_device_status_rejections(lib):
+    st = ctypes.c_int32(0)
+    assert lib.gmm_device_status(None, ctypes.byref(st), None) == NULL
+    assert lib.gmm_device_status(P(MIS), ctypes.byref(st), None) == ALIGN
+    assert lib.gmm_device_status(P(A), None, None) == NULL
+
+
+def test_pack_rhs_rejections(lib):
+    p = lib.gmm_pack_rhs
+    assert p(P(A), 2, 128, 200, P(A), None) == SHAPE
+    assert p(P(A), 2, 100, 128, P(A), None) == SHAPE
+    assert p(P(A), 0, 128, 128, P(A), None) == SHAPE
+    assert p(P(A), 5000, 128, 128, P(A), None) == SHAPE
+    assert p(None, 2, 128, 128, P(A), None) == NULL
+    assert p(P(A), 2, 128, 128, P(MIS), None) == ALIGN
+
+
+def test_quant_scales_rejections(lib):
+    q = lib.gmm_quant_scales
+    assert q(P(A), -1, P(A), P(A), None) == SHAPE
+    assert q(None, 4, P(A), P(A), None) == NULL
+    assert q(P(A), 4, P(A), P(MIS), None) == ALIGN
+    assert q(P(A), 0, P(A), P(A), None) == OK
 
 
 def test_binding_raises_on_error(lib):

@@ -26,12 +26,48 @@ DEV = "cuda:0"
 ])
 def test_metadata_matches_oracle(gs, M, tm):
     gs = np.array(gs, np.int32)
-    off, work, num = gmm.gmm_group_metadata(torch.from_numpy(gs).to(DEV), M, tm)
+    ws = gmm.workspace(gmm.OP_METADATA, M, 0, 0, gs.size, DEV)
+    off, work, num = gmm.gmm_group_metadata(torch.from_numpy(gs).to(DEV), M, tm, ws=ws)
     ref = oracle.work_list(gs, M, tm)
     n = int(num.item())
     assert n == len(ref)
     assert np.array_equal(work[:n].cpu().numpy(), ref)
     assert np.array_equal(off.cpu().numpy(), oracle.group_offsets(gs, M).astype(np.int32))
+    assert gmm.device_status(ws) == 0
+
+
+def clipped_offsets(gs, M):
+    """First row of each group's clipped range, then the clipped total (gmm.h)."""
+    o = np.concatenate([[0], np.cumsum(np.maximum(gs.astype(np.int64), 0))])
+    return np.minimum(o, M).astype(np.int32)
+
+
+def expected_status(gs, M):
+    return ((gmm.DEV_SUM_GT_M if np.maximum(gs.astype(np.int64), 0).sum() > M else 0)
+            | (gmm.DEV_NEGATIVE_SIZE if (gs < 0).any() else 0))
+
+
+@pytest.mark.parametrize("gs,M,tm", [
+    ([128, 128], 128, 128),
+    ([100, 100, 100], 250, 64),
+    ([5, -3, 7], 20, 16),
+    ([-5, 0, 30], 16, 16),
+    ([0, 2**31 - 1, 9], 64, 16),       # the metadata kernel writes only its work list
+    ([2**31 - 1] * 70, 1000, 48),      # saturation across two chunks of 64 groups
+    ([-1] * 65 + [3], 10, 16),
+])
+def test_metadata_outside_contract(gs, M, tm):
+    """Sizes that break the contract: the work list stays inside [0, M) and
+    equals the oracle's reading; the status word names what was wrong."""
+    gs = np.array(gs, np.int32)
+    ws = gmm.workspace(gmm.OP_METADATA, M, 0, 0, gs.size, DEV)
+    off, work, num = gmm.gmm_group_metadata(torch.from_numpy(gs).to(DEV), M, tm, ws=ws)
+    ref = oracle.work_list(gs, M, tm)
+    n = int(num.item())
+    assert n == len(ref)
+    assert np.array_equal(work[:n].cpu().numpy(), ref)
+    assert np.array_equal(off.cpu().numpy(), clipped_offsets(gs, M))
+    assert gmm.device_status(ws) == expected_status(gs, M)
 
 
 def test_metadata_random_and_large_G():

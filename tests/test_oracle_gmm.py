@@ -281,8 +281,11 @@ def test_adjoint_identity_ties_fwd_dx_tgmm():
 # ------------------------------------------------------------ work list -----
 
 def bruteforce_work(gs, M, tm):
-    """Scan every row; collect (g, t) -> [min row, max row + 1]."""
-    gid = np.concatenate([np.full(s, g) for g, s in enumerate(gs)] + [np.full(M - sum(gs), len(gs))]).astype(int)
+    """Scan every row; collect (g, t) -> [min row, max row + 1].  Rows are dealt
+    to groups in order, a negative size dealing none; the rows left below M
+    belong to no group (g = G); rows dealt past M do not exist."""
+    dealt = [np.full(max(s, 0), g) for g, s in enumerate(gs)]
+    gid = np.concatenate(dealt + [np.full(M, len(gs))]).astype(int)[:M]
     seen = {}
     for row in range(M):
         key = (int(gid[row]), row // tm)
@@ -305,6 +308,23 @@ def test_work_list_bruteforce(gs, M, tm):
     assert sorted(map(tuple, wl.tolist())) == bruteforce_work(gs.tolist(), M, tm)
     # group-major order, tail (g == G) last
     assert wl[:, 0].tolist() == sorted(wl[:, 0].tolist())
+
+
+@pytest.mark.parametrize("gs,M,tm", [
+    ([128, 128], 128, 128),          # sizes sum past M: group 1 has no rows left
+    ([100, 100, 100], 250, 64),      # group 2 is cut at M
+    ([5, -3, 7], 20, 16),            # a negative size deals no rows
+    ([-5, 0, 30], 16, 16),           # negative first, then past M
+    ([0, 2**31 - 1, 9], 64, 16),     # a size far beyond M
+])
+def test_work_list_outside_contract(gs, M, tm):
+    """Out-of-contract group sizes: rows stay inside [0, M) (the boundary's
+    reading, gmm.h), checked against the row scan above."""
+    gs = np.array(gs, np.int32)
+    wl = oracle.work_list(gs, M, tm)
+    assert sorted(map(tuple, wl.tolist())) == bruteforce_work(gs.tolist(), M, tm)
+    assert (wl[:, 2] >= 0).all() and (wl[:, 3] <= M).all() and (wl[:, 2] < wl[:, 3]).all()
+    assert len(wl) <= -(-M // tm) + gs.size + 1
 
 
 def test_work_list_random_and_bound():

@@ -133,3 +133,45 @@ def test_rhs_power_of_two_block():
     assert s[0, 0, 0] == 0.25
     assert q[0, 0, :127].tolist() == list(range(0x7F))
     assert q[0, 5, 9] == 0x7E
+
+
+# ------------------------------------------------------- the scale pair ----
+
+def contract_amax_sample(seed=0, per_exp=64):
+    """Block abs-maxima across the contract's range [2^-100, FLT_MAX]: for each
+    exponent, the binade's first and last significands and random ones."""
+    r = np.random.default_rng(seed)
+    bits = []
+    for e in range(-100, 128):
+        base = (e + 127) << 23
+        sig = np.concatenate([[0, 1, (1 << 23) - 1], r.integers(0, 1 << 23, size=per_exp)])
+        bits.append(base + sig)
+    return np.concatenate(bits).astype(np.uint32).view(np.float32)
+
+
+def test_quant_scales_exact_rational():
+    """s = RN(a/448) and inv = RN(1/s), against exact rational arithmetic."""
+    a = contract_amax_sample(per_exp=6)
+    s, inv = oracle.quant_scales(a)
+    for ai, si, ii in zip(a.tolist(), s.tolist(), inv.tolist()):
+        want_s = rn_f32(Fraction(ai) / 448)
+        assert si == want_s, (ai, si, want_s)
+        assert ii == rn_f32(1 / Fraction(want_s)), (ai, ii)
+
+
+def test_quant_scales_binade_vs_numpy_division():
+    """Every significand of one binade of a (the recipe's scaling by 2^k only
+    moves the exponent inside the contract's range), against numpy's IEEE fp32
+    division."""
+    a = ((np.uint32(136) << 23) + np.arange(1 << 23, dtype=np.uint32)).view(np.float32)
+    s, inv = oracle.quant_scales(a)
+    ns = a / np.float32(448.0)
+    assert np.array_equal(s.view(np.uint32), ns.view(np.uint32))
+    assert np.array_equal(inv.view(np.uint32), (np.float32(1.0) / ns).view(np.uint32))
+
+
+def test_quant_scales_closed_forms():
+    a = np.array([0.0, 448.0, 448.0 * 2 ** -90, 448.0 * 2 ** 100, 224.0], np.float32)
+    s, inv = oracle.quant_scales(a)
+    assert s.tolist() == [0.0, 1.0, 2.0 ** -90, 2.0 ** 100, 0.5]
+    assert inv.tolist() == [0.0, 1.0, 2.0 ** 90, 2.0 ** -100, 2.0]
