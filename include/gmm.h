@@ -11,7 +11,8 @@
  * --------------------------------
  *  - All tensors are dense and row-major, in device memory of the current
  *    HIP device, and owned by the caller.  The library allocates nothing and
- *    keeps no state between calls.
+ *    keeps no state between calls (gmm_fp8_fwd_noalloc aside: it keeps a
+ *    small device array per GPU).
  *  - `group_sizes` is a device array of G int32 values, read only on the
  *    device (the host never synchronises).  Contract: every s_g >= 0 and
  *    s_0 + ... + s_{G-1} <= M.  Rows at or past that total are written as
@@ -259,6 +260,25 @@ GMM_API int gmm_fp8_fwd(const void *lhs, int lhs_dtype, const float *lhs_scale,
                 const int32_t *group_sizes, int64_t M, int64_t K, int64_t N,
                 int64_t G, void *out, int out_dtype, uint8_t *q_out,
                 float *scale_out, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * gmm_fp8_fwd_noalloc -- gmm_fp8_fwd for callers that cannot allocate device
+ *   memory or hand in a workspace: code under HIP graph capture, tight
+ *   serving loops, harnesses that forbid hipMalloc.  Same arguments, checks
+ *   and results as gmm_fp8_fwd without ws/ws_bytes; the call allocates
+ *   nothing.  Its workspace is a library-owned device array of 4096 bytes,
+ *   one per GPU, held from the first call on that GPU until the process
+ *   ends; a shape whose gmm_workspace_bytes(GMM_OP_FP8_FWD, ...) exceeds it
+ *   is rejected with GMM_ERR_WORKSPACE.  Every call on one GPU shares that
+ *   GPU's array and finds the previous call's contents in it (nothing in it
+ *   needs to start at zero): calls that may overlap on one GPU race on it.
+ *   The device status word goes to that array and is not reported.
+ */
+GMM_API int gmm_fp8_fwd_noalloc(const void *lhs, int lhs_dtype, const float *lhs_scale,
+                const uint8_t *rhs, const float *rhs_scale,
+                const int32_t *group_sizes, int64_t M, int64_t K, int64_t N,
+                int64_t G, void *out, int out_dtype, uint8_t *q_out,
+                float *scale_out, void *stream);
 
 /*
  * gmm_fp8_fwd_swiglu -- blockwise-FP8 grouped matmul with the gate and up

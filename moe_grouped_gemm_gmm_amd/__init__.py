@@ -24,7 +24,7 @@ DEV_SUM_GT_M, DEV_NEGATIVE_SIZE = 1, 2
 EXPORTS = ("gmm_status_string", "gmm_last_error", "gmm_workspace_bytes", "gmm_device_status",
            "gmm_group_metadata", "gmm_quantize_lhs", "gmm_quantize_rhs", "gmm_pack_rhs",
            "gmm_quant_scales", "gmm_fp8_fwd", "gmm_fp8_fwd_swiglu", "gmm_bf16_fwd", "tgmm_bf16",
-           "gmm_bf16_dx", "gmm_quantize_rhs_mxfp4", "gmm_fp8_mxfp4_fwd")
+           "gmm_bf16_dx", "gmm_quantize_rhs_mxfp4", "gmm_fp8_mxfp4_fwd", "gmm_fp8_fwd_noalloc")
 
 _lib = None
 
@@ -57,6 +57,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gmm_pack_rhs.argtypes = [P, I64, I64, I64, P, P]
     lib.gmm_quant_scales.argtypes = [P, I64, P, P, P]
     lib.gmm_fp8_fwd.argtypes = [P, I, P, P, P, P, I64, I64, I64, I64, P, I, P, P, P, SZ, P]
+    lib.gmm_fp8_fwd_noalloc.argtypes = [P, I, P, P, P, P, I64, I64, I64, I64, P, I, P, P, P]
     lib.gmm_fp8_fwd_swiglu.argtypes = [P, I, P, P, P, P, I64, I64, I64, I64, P, I, P, P, P, SZ, P]
     lib.gmm_bf16_fwd.argtypes = [P, P, P, I64, I64, I64, I64, P, I, P, SZ, P]
     lib.tgmm_bf16.argtypes = [P, P, P, I64, I64, I64, I64, P, I, P, SZ, P]
@@ -235,6 +236,28 @@ def gmm_fp8_fwd(lhs: torch.Tensor, rhs_q: torch.Tensor, rhs_scale: torch.Tensor,
     _check(lib.gmm_fp8_fwd(_ptr(lhs), _dt(lhs), _ptr(lhs_scale), _ptr(rhs_q), _ptr(rhs_scale),
                            _ptr(group_sizes), M, K, N, G, _ptr(out), _dt(out), _ptr(q_out),
                            _ptr(scale_out), wsp, wsb, _stream(lhs)))
+    return out
+
+
+def gmm_fp8_fwd_noalloc(lhs: torch.Tensor, rhs_q: torch.Tensor, rhs_scale: torch.Tensor,
+                        group_sizes: torch.Tensor, lhs_scale: Optional[torch.Tensor] = None,
+                        out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None,
+                        q_out: Optional[torch.Tensor] = None,
+                        scale_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """gmm_fp8_fwd without a workspace (the library's own static device scratch;
+    the C call allocates nothing).  Pass `out` to keep this wrapper from
+    allocating it."""
+    lib = load_library()
+    M, K = lhs.shape
+    G, N16, KB, slab = rhs_q.shape
+    N = N16 * 16
+    if slab != 2048 or KB * 128 != K:
+        raise ValueError("rhs_q shape %s does not match K=%d" % (tuple(rhs_q.shape), K))
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=lhs.device)
+    _check(lib.gmm_fp8_fwd_noalloc(_ptr(lhs), _dt(lhs), _ptr(lhs_scale), _ptr(rhs_q),
+                                   _ptr(rhs_scale), _ptr(group_sizes), M, K, N, G, _ptr(out),
+                                   _dt(out), _ptr(q_out), _ptr(scale_out), _stream(lhs)))
     return out
 
 

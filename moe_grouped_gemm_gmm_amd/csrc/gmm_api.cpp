@@ -242,14 +242,19 @@ int gmm_fp8_mxfp4_fwd(const void* lhs, int lhs_dtype, const float* lhs_scale,
                                                 (hipStream_t)stream));
 }
 
-int gmm_fp8_fwd(const void* lhs, int lhs_dtype, const float* lhs_scale, const uint8_t* rhs,
-                const float* rhs_scale, const int32_t* group_sizes, int64_t M, int64_t K,
-                int64_t N, int64_t G, void* out, int out_dtype, uint8_t* q_out,
-                float* scale_out, void* ws, size_t ws_bytes, void* stream) {
-    int kind;
-    if (lhs_dtype == GMM_E4M3) kind = 0;
-    else if (lhs_dtype == GMM_BF16) kind = 1;
-    else if (lhs_dtype == GMM_F32) kind = 2;
+}  // extern "C"
+
+namespace {
+
+// Argument checks of gmm_fp8_fwd (and its no-allocation variant); on success
+// *kind is the LHS kind of the launchers.
+int check_fp8_fwd(const void* lhs, int lhs_dtype, const float* lhs_scale, const uint8_t* rhs,
+                  const float* rhs_scale, const int32_t* group_sizes, int64_t M, int64_t K,
+                  int64_t N, int64_t G, void* out, int out_dtype, uint8_t* q_out,
+                  float* scale_out, int* kind) {
+    if (lhs_dtype == GMM_E4M3) *kind = 0;
+    else if (lhs_dtype == GMM_BF16) *kind = 1;
+    else if (lhs_dtype == GMM_F32) *kind = 2;
     else return fail(GMM_ERR_DTYPE, "lhs dtype %d unsupported", lhs_dtype);
     GMM_TRY(check_out_dtype(out_dtype, "out"));
     GMM_TRY(check_groups(M, G));
@@ -260,7 +265,7 @@ int gmm_fp8_fwd(const void* lhs, int lhs_dtype, const float* lhs_scale, const ui
     GMM_TRY(check_ptr(rhs_scale, "rhs_scale"));
     GMM_TRY(check_ptr(group_sizes, "group_sizes"));
     GMM_TRY(check_ptr(out, "out"));
-    if (kind == 0) {
+    if (*kind == 0) {
         GMM_TRY(check_ptr(lhs_scale, "lhs_scale"));
         if (q_out != nullptr || scale_out != nullptr)
             return fail(GMM_ERR_DTYPE, "q_out/scale_out need a bf16 or fp32 lhs");
@@ -273,8 +278,44 @@ int gmm_fp8_fwd(const void* lhs, int lhs_dtype, const float* lhs_scale, const ui
     }
     const int64_t blocks = ((M + 47) / 48 + G + 1) * (N / 128);   // worst case over tile shapes
     if (blocks > kMaxDim) return fail(GMM_ERR_SHAPE, "grid too large");
+    return GMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gmm_fp8_fwd(const void* lhs, int lhs_dtype, const float* lhs_scale, const uint8_t* rhs,
+                const float* rhs_scale, const int32_t* group_sizes, int64_t M, int64_t K,
+                int64_t N, int64_t G, void* out, int out_dtype, uint8_t* q_out,
+                float* scale_out, void* ws, size_t ws_bytes, void* stream) {
+    int kind = 0;
+    GMM_TRY(check_fp8_fwd(lhs, lhs_dtype, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N, G, out,
+                          out_dtype, q_out, scale_out, &kind));
     GMM_TRY(check_ws(ws, ws_bytes, gmm_workspace_bytes(GMM_OP_FP8_FWD, M, K, N, G)));
     if (M == 0) return GMM_OK;
+    return hip_status(gmm::launch_fp8_fwd(lhs, kind, lhs_scale, rhs, rhs_scale, group_sizes,
+                                          (int)M, (int)K, (int)N, (int)G, out,
+                                          out_dtype == GMM_BF16, q_out, scale_out, ws_status(ws),
+                                          (hipStream_t)stream));
+}
+
+int gmm_fp8_fwd_noalloc(const void* lhs, int lhs_dtype, const float* lhs_scale,
+                        const uint8_t* rhs, const float* rhs_scale, const int32_t* group_sizes,
+                        int64_t M, int64_t K, int64_t N, int64_t G, void* out, int out_dtype,
+                        uint8_t* q_out, float* scale_out, void* stream) {
+    int kind = 0;
+    GMM_TRY(check_fp8_fwd(lhs, lhs_dtype, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N, G, out,
+                          out_dtype, q_out, scale_out, &kind));
+    const size_t need = gmm_workspace_bytes(GMM_OP_FP8_FWD, M, K, N, G);
+    if (need > gmm::kNoallocScratchBytes)
+        return fail(GMM_ERR_WORKSPACE,
+                    "this shape needs %zu bytes of workspace; the library's static scratch holds %zu",
+                    need, gmm::kNoallocScratchBytes);
+    if (M == 0) return GMM_OK;
+    void* ws = nullptr;
+    size_t ws_bytes = 0;
+    GMM_TRY(hip_status(gmm::noalloc_scratch(&ws, &ws_bytes)));
     return hip_status(gmm::launch_fp8_fwd(lhs, kind, lhs_scale, rhs, rhs_scale, group_sizes,
                                           (int)M, (int)K, (int)N, (int)G, out,
                                           out_dtype == GMM_BF16, q_out, scale_out, ws_status(ws),

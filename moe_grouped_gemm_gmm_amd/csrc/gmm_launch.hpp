@@ -23,6 +23,11 @@ inline int device_cus() {
 // launch sets to the call's device status (bits kDevSumGtM, kDevNegativeSize
 // of gmm_device.hpp; 0 when group_sizes keeps the contract).
 
+// Bytes of the library-owned device scratch behind gmm_fp8_fwd_noalloc, and
+// its device address on the current device (found once per device).
+constexpr size_t kNoallocScratchBytes = 4096;
+hipError_t noalloc_scratch(void** ptr, size_t* bytes);
+
 hipError_t launch_group_metadata(const int32_t* group_sizes, int G, int M, int tm,
                                  int32_t* offsets, int32_t* work, int capacity,
                                  int32_t* num_work, int32_t* status, hipStream_t stream);

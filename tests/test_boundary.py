@@ -31,7 +31,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_symbols()
-    assert len(names) == 16
+    assert len(names) == 17
     assert sorted(names) == sorted(gmm.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
@@ -72,6 +72,23 @@ def test_fp8_fwd_rejections(lib, kw, status):
     assert fp8(lib, **kw) == status
     if status:
         assert lib.gmm_last_error()
+
+
+def fp8_noalloc(lib, lhs=A, lhs_dt=1, lhs_scale=0, rhs=A, rhs_scale=A, gs=A, M=256, K=256, N=256,
+                G=4, out=A, out_dt=1, q=0, s=0):
+    return lib.gmm_fp8_fwd_noalloc(P(lhs), lhs_dt, P(lhs_scale), P(rhs), P(rhs_scale), P(gs), M, K,
+                                   N, G, P(out), out_dt, P(q), P(s), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(lhs=0), NULL), (dict(gs=0), NULL), (dict(out=MIS), ALIGN), (dict(q=A), NULL),
+    (dict(K=200), SHAPE), (dict(G=0), SHAPE), (dict(M=-1), SHAPE), (dict(lhs_dt=7), DTYPE),
+    (dict(lhs_dt=2), NULL), (dict(lhs_scale=A), DTYPE),
+    (dict(M=0), OK),                   # nothing to do: returns before touching the device
+])
+def test_fp8_fwd_noalloc_rejections(lib, kw, status):
+    """The no-workspace variant applies gmm_fp8_fwd's checks, before any HIP call."""
+    assert fp8_noalloc(lib, **kw) == status
 
 
 def swiglu(lib, lhs=A, lhs_dt=1, lhs_scale=0, rhs=A, rhs_scale=A, gs=A, M=256, K=256, N=256, G=4,
