@@ -45,10 +45,15 @@ def assert_fp8_parity_scaled(out: np.ndarray, ref: np.ndarray, what: str = ""):
     carry an error relative to the block's largest product, so the absolute
     error scales with the data)."""
     rms = float(np.sqrt(np.mean(ref ** 2))) if ref.size else 0.0
+    # the worst excess over the unscaled bar, reported so the effect of the
+    # scaling stays visible (<= 0: the unscaled bar holds as well)
+    unscaled = float(np.max(np.abs(out - ref) - (FP8_ATOL + FP8_RTOL * np.abs(ref)), initial=-np.inf))
+    print("%s: rms(ref) %.3g, worst excess over the unscaled bar %.3g" % (what, rms, unscaled))
     assert_close(out, ref, FP8_ATOL * max(1.0, rms), FP8_RTOL, what)
     if np.any(ref != 0):
         s = sqnr_db(ref, out)
         assert s > FP8_MIN_SQNR_DB, "%s: SQNR %.1f dB" % (what, s)
+    return unscaled
 
 
 def assert_bf16_parity(out: np.ndarray, ref: np.ndarray, what: str = ""):

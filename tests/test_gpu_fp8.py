@@ -13,7 +13,7 @@ import torch
 import moe_grouped_gemm_gmm_amd as gmm
 import oracle
 import workloads
-from helpers import assert_fp8_parity, pack_rhs, sample_rows_problem, sqnr_db, to_np64
+from helpers import assert_fp8_parity, pack_rhs, sqnr_db, to_np64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -174,29 +174,6 @@ def test_dev_configs_full(name):
     print("%s SQNR vs oracle: %.1f dB" % (name, sqnr_db(ref, o)))
 
 
-def test_full_config_sampled_rows():
-    """Production shape (M=65536, G=256, Zipf routing) in the benchmark's launch
-    configuration; the oracle checks a row sample that covers every group
-    boundary, the heaviest group and random rows."""
-    wl = workloads.make("full", seed=0, with_dy=False)
-    out, q, s = run_fp8(wl, torch.bfloat16, want_q=True)
-    gs = wl.group_sizes
-    off = np.concatenate([[0], np.cumsum(gs)])
-    r = workloads.rng(99, 0)
-    rows = set(r.choice(wl.M, 512, replace=False).tolist())
-    for o in off[1:-1]:
-        rows.update([int(o) - 1, int(o)])
-    rows = np.array(sorted(x for x in rows if 0 <= x < wl.M))
-    x_s = workloads.as_f32(wl.x)[rows]
-    sub_gs, _ = sample_rows_problem(gs, rows)
-    ql, sl = oracle.quantize_lhs(x_s)
-    assert np.array_equal(q.cpu().numpy()[rows], ql)
-    assert np.array_equal(s.cpu().numpy()[rows], sl)
-    qr, sr = oracle.quantize_rhs(workloads.as_f32(wl.w))
-    ref = oracle.gmm_fp8(ql, sl, qr, sr, sub_gs)
-    assert_fp8_parity(to_np64(out)[rows], ref, "full sampled")
-
-
 @pytest.mark.parametrize("name", ["wi", "wo"])
 def test_bench_launch_configuration(name):
     """The call the benchmark times (bf16 LHS quantised in the kernel, bf16
@@ -209,22 +186,3 @@ def test_bench_launch_configuration(name):
     total = int(wl.group_sizes.sum())
     assert (o[total:] == 0).all()
     assert_fp8_parity(o, ref, name + " bench launch")
-
-
-def test_bench_launch_configuration_full_sampled():
-    """The benchmark's production-shape call (M=65536, G=256, bf16 in and out,
-    no code output) on a row sample covering every group boundary."""
-    wl = workloads.make("full", seed=0, with_dy=False)
-    out, _, _ = run_fp8(wl, torch.bfloat16)
-    gs = wl.group_sizes
-    off = np.concatenate([[0], np.cumsum(gs)])
-    r = workloads.rng(101, 0)
-    rows = set(r.choice(wl.M, 512, replace=False).tolist())
-    for o in off[1:-1]:
-        rows.update([int(o) - 1, int(o)])
-    rows = np.array(sorted(x for x in rows if 0 <= x < wl.M))
-    sub_gs, _ = sample_rows_problem(gs, rows)
-    ql, sl = oracle.quantize_lhs(workloads.as_f32(wl.x)[rows])
-    qr, sr = oracle.quantize_rhs(workloads.as_f32(wl.w))
-    ref = oracle.gmm_fp8(ql, sl, qr, sr, sub_gs)
-    assert_fp8_parity(to_np64(out)[rows], ref, "full bench launch sampled")
