@@ -102,6 +102,50 @@ GMM_API const char *gmm_last_error(void);
 GMM_API size_t gmm_workspace_bytes(int op, int64_t M, int64_t K, int64_t N, int64_t G);
 
 /*
+ * Tile configurations, for tile searches ("GEMM Kernel 性能优化十问", Q4: the
+ * forward, the dX pass and tgmm reduce over different dimensions and get
+ * tilings of their own; Q8: the tiling is found by searching).  In an
+ * override a 0 field means "the library's choice"; gmm_get_tile_config
+ * returns a resolved configuration (the fields the call uses set).
+ *   FP8 forwards (GMM_OP_FP8_FWD, _SWIGLU, _MXFP4_FWD):
+ *     kernel    1 warp-specialised (48 x 512 tiles: 8, 12 or 16 waves, MXFP4:
+ *                 16 waves of tile_n 128/256/512 columns), 2 uniform (tile_m
+ *                 48/64 rows, tile_n 128/256/512 columns; the only kernel of
+ *                 the fused gate+up forward, 256 columns), 3 row-resident
+ *                 sweep (one workgroup per 48-row item over all column
+ *                 tiles of tile_n 512 for K <= 1024, or of 256, bf16 output,
+ *                 for K <= 2048).
+ *     waves     warp-specialised: 8 (the one form that also writes the LHS
+ *                 codes), 12 or 16.
+ *     depth     warp-specialised, 12 waves: K steps of weights in flight, 1 or 2.
+ *   bf16 calls (GMM_OP_BF16_FWD, _TGMM, _DX): residency 2 or 3 (workgroups
+ *     per CU the register allocation allows); tgmm placement 1 (each XCD
+ *     takes whole groups) or 2 (every group spread over the 8 XCDs, groups
+ *     in decreasing size class; needs a multiple of 8 tiles per group).
+ */
+typedef struct {
+    int32_t kernel, waves, tile_m, tile_n, depth, residency, placement;
+} gmm_tile_config;
+
+/*
+ * gmm_set_tile_config -- replace the library's tile choice for one
+ *   operation (a gmm_op with a configuration, not GMM_OP_METADATA),
+ *   process-wide, until the next call; cfg NULL restores the library's
+ *   choice.  Field values out of range are GMM_ERR_SHAPE here; a
+ *   configuration that does not fit a later call's shape makes that call
+ *   return GMM_ERR_SHAPE (with the reason in gmm_last_error).  Not for use
+ *   while other threads call the library.
+ */
+GMM_API int gmm_set_tile_config(int op, const gmm_tile_config *cfg);
+
+/*
+ * gmm_get_tile_config -- the configuration a call of op on this shape would
+ *   run (lhs_dtype and out_dtype as for that call), override included.
+ */
+GMM_API int gmm_get_tile_config(int op, int64_t M, int64_t K, int64_t N, int64_t G,
+                                int lhs_dtype, int out_dtype, gmm_tile_config *cfg);
+
+/*
  * gmm_device_status -- the device status word the last grouped call wrote
  *   into ws (0 = group_sizes kept the contract; else GMM_DEV_* bits), copied
  *   to *status once the work queued on `stream` before it has finished.

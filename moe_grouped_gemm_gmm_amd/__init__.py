@@ -22,11 +22,22 @@ GMM_MAX_GROUPS = 4096
  OP_DX) = range(7)
 DEV_SUM_GT_M, DEV_NEGATIVE_SIZE = 1, 2
 EXPORTS = ("gmm_status_string", "gmm_last_error", "gmm_workspace_bytes", "gmm_device_status",
+           "gmm_set_tile_config", "gmm_get_tile_config",
            "gmm_group_metadata", "gmm_quantize_lhs", "gmm_quantize_rhs", "gmm_pack_rhs",
            "gmm_quant_scales", "gmm_fp8_fwd", "gmm_fp8_fwd_swiglu", "gmm_bf16_fwd", "tgmm_bf16",
            "gmm_bf16_dx", "gmm_quantize_rhs_mxfp4", "gmm_fp8_mxfp4_fwd", "gmm_fp8_fwd_noalloc")
 
 _lib = None
+
+TILE_FIELDS = ("kernel", "waves", "tile_m", "tile_n", "depth", "residency", "placement")
+
+
+class TileConfig(ctypes.Structure):
+    """gmm_tile_config (include/gmm.h); 0 in an override means the library's choice."""
+    _fields_ = [(f, ctypes.c_int32) for f in TILE_FIELDS]
+
+    def as_dict(self):
+        return {f: int(getattr(self, f)) for f in TILE_FIELDS}
 
 
 class GmmError(RuntimeError):
@@ -51,6 +62,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gmm_workspace_bytes.restype = SZ
     lib.gmm_workspace_bytes.argtypes = [I, I64, I64, I64, I64]
     lib.gmm_device_status.argtypes = [P, P, P]
+    lib.gmm_set_tile_config.argtypes = [I, P]
+    lib.gmm_get_tile_config.argtypes = [I, I64, I64, I64, I64, I, I, P]
     lib.gmm_group_metadata.argtypes = [P, I64, I64, I64, P, P, I64, P, P, SZ, P]
     lib.gmm_quantize_lhs.argtypes = [P, I, I64, I64, P, P, P]
     lib.gmm_quantize_rhs.argtypes = [P, I, I64, I64, I64, P, P, P]
@@ -115,6 +128,29 @@ def device_status(ws: torch.Tensor) -> int:
     out = ctypes.c_int32(-1)
     _check(lib.gmm_device_status(_ptr(ws), ctypes.byref(out), _stream(ws)))
     return int(out.value)
+
+
+def set_tile_config(op: int, cfg: Optional[dict]) -> None:
+    """Force a tile configuration for op (OP_*), process-wide; None restores the
+    library's choice.  Keys: TILE_FIELDS (missing keys = the library's choice)."""
+    lib = load_library()
+    if cfg is None:
+        _check(lib.gmm_set_tile_config(op, None))
+        return
+    unknown = set(cfg) - set(TILE_FIELDS)
+    if unknown:
+        raise ValueError("unknown tile fields %s" % sorted(unknown))
+    c = TileConfig(**{f: int(cfg.get(f, 0)) for f in TILE_FIELDS})
+    _check(lib.gmm_set_tile_config(op, ctypes.byref(c)))
+
+
+def get_tile_config(op: int, M: int, K: int, N: int, G: int, lhs_dtype: int = GMM_BF16,
+                    out_dtype: int = GMM_BF16) -> dict:
+    """The configuration a call of op on this shape would run."""
+    lib = load_library()
+    c = TileConfig()
+    _check(lib.gmm_get_tile_config(op, M, K, N, G, lhs_dtype, out_dtype, ctypes.byref(c)))
+    return c.as_dict()
 
 
 def _ws(ws: Optional[torch.Tensor], op: int, M: int, K: int, N: int, G: int, device):

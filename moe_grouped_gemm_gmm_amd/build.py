@@ -13,7 +13,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libgmm.so")
-SOURCES = ["gmm_api.cpp", "gmm_quant.hip", "gmm_fp8.hip", "gmm_bf16.hip", "gmm_noalloc.hip"]
+SOURCES = ["gmm_api.cpp", "gmm_config.cpp", "gmm_quant.hip", "gmm_fp8.hip", "gmm_bf16.hip",
+           "gmm_noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

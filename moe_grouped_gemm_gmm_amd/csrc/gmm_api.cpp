@@ -7,8 +7,10 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <initializer_list>
 
 #include "../../include/gmm.h"
+#include "gmm_config.hpp"
 #include "gmm_launch.hpp"
 
 namespace {
@@ -72,6 +74,34 @@ int check_ws(const void* ws, size_t ws_bytes, size_t need) {
 
 int32_t* ws_status(void* ws) { return reinterpret_cast<int32_t*>(ws); }
 
+// The tile configuration a call runs (the library's choice, or the override
+// a tile search set); an override that does not fit the shape is an error.
+int resolve(int op, int64_t M, int64_t K, int64_t N, int64_t G, int kind, bool out_bf16,
+            bool write_q, gmm::TileConfig* cfg) {
+    const char* why = "";
+    if (!gmm::resolve_tile_config(op, M, K, N, G, kind, out_bf16, write_q, cfg, &why))
+        return fail(GMM_ERR_SHAPE, "the tile configuration set for this operation does not fit: %s", why);
+    return GMM_OK;
+}
+
+static_assert(sizeof(gmm_tile_config) == sizeof(gmm::TileConfig), "tile config layouts");
+
+gmm::TileConfig to_internal(const gmm_tile_config& c) {
+    return gmm::TileConfig{c.kernel, c.waves, c.tile_m, c.tile_n, c.depth, c.residency, c.placement};
+}
+
+gmm_tile_config to_public(const gmm::TileConfig& c) {
+    gmm_tile_config o;
+    o.kernel = c.kernel;
+    o.waves = c.waves;
+    o.tile_m = c.tile_m;
+    o.tile_n = c.tile_n;
+    o.depth = c.depth;
+    o.residency = c.residency;
+    o.placement = c.placement;
+    return o;
+}
+
 int hip_status(hipError_t e) {
     if (e != hipSuccess) return fail(GMM_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(e));
     return GMM_OK;
@@ -116,6 +146,40 @@ size_t gmm_workspace_bytes(int op, int64_t M, int64_t K, int64_t N, int64_t G) {
         default:
             return 0;
     }
+}
+
+int gmm_set_tile_config(int op, const gmm_tile_config* cfg) {
+    if (op < GMM_OP_FP8_FWD || op > GMM_OP_DX)
+        return fail(GMM_ERR_SHAPE, "op %d has no tile configuration", op);
+    if (cfg == nullptr) {
+        gmm::set_tile_override(op, nullptr);
+        return GMM_OK;
+    }
+    const gmm::TileConfig c = to_internal(*cfg);
+    auto in = [](int v, std::initializer_list<int> ok) {
+        for (int o : ok)
+            if (v == o) return true;
+        return false;
+    };
+    if (!in(c.kernel, {0, 1, 2, 3}) || !in(c.waves, {0, 8, 12, 16}) || !in(c.tile_m, {0, 48, 64}) ||
+        !in(c.tile_n, {0, 128, 256, 512}) || !in(c.depth, {0, 1, 2}) || !in(c.residency, {0, 2, 3}) ||
+        !in(c.placement, {0, 1, 2}))
+        return fail(GMM_ERR_SHAPE, "a tile configuration field is out of range");
+    gmm::set_tile_override(op, &c);
+    return GMM_OK;
+}
+
+int gmm_get_tile_config(int op, int64_t M, int64_t K, int64_t N, int64_t G, int lhs_dtype,
+                        int out_dtype, gmm_tile_config* cfg) {
+    if (op < GMM_OP_FP8_FWD || op > GMM_OP_DX)
+        return fail(GMM_ERR_SHAPE, "op %d has no tile configuration", op);
+    if (cfg == nullptr) return fail(GMM_ERR_NULL, "cfg is NULL");
+    GMM_TRY(check_out_dtype(out_dtype, "out"));
+    const int kind = lhs_dtype == GMM_E4M3 ? 0 : (lhs_dtype == GMM_BF16 ? 1 : 2);
+    gmm::TileConfig c;
+    GMM_TRY(resolve(op, M, K, N, G, kind, out_dtype == GMM_BF16, false, &c));
+    *cfg = to_public(c);
+    return GMM_OK;
 }
 
 int gmm_device_status(const void* ws, int32_t* status, void* stream) {
@@ -235,8 +299,10 @@ int gmm_fp8_mxfp4_fwd(const void* lhs, int lhs_dtype, const float* lhs_scale,
     const int64_t blocks = ((M + 47) / 48 + G + 1) * (N / 128);
     if (blocks > kMaxDim) return fail(GMM_ERR_SHAPE, "grid too large");
     GMM_TRY(check_ws(ws, ws_bytes, gmm_workspace_bytes(GMM_OP_FP8_MXFP4_FWD, M, K, N, G)));
+    gmm::TileConfig cfg;
+    GMM_TRY(resolve(GMM_OP_FP8_MXFP4_FWD, M, K, N, G, kind, out_dtype == GMM_BF16, false, &cfg));
     if (M == 0) return GMM_OK;
-    return hip_status(gmm::launch_fp8_mxfp4_fwd(lhs, kind, lhs_scale, rhs_q, rhs_scale, group_sizes,
+    return hip_status(gmm::launch_fp8_mxfp4_fwd(cfg, lhs, kind, lhs_scale, rhs_q, rhs_scale, group_sizes,
                                                 (int)M, (int)K, (int)N, (int)G, out,
                                                 out_dtype == GMM_BF16, ws_status(ws),
                                                 (hipStream_t)stream));
@@ -293,8 +359,11 @@ int gmm_fp8_fwd(const void* lhs, int lhs_dtype, const float* lhs_scale, const ui
     GMM_TRY(check_fp8_fwd(lhs, lhs_dtype, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N, G, out,
                           out_dtype, q_out, scale_out, &kind));
     GMM_TRY(check_ws(ws, ws_bytes, gmm_workspace_bytes(GMM_OP_FP8_FWD, M, K, N, G)));
+    gmm::TileConfig cfg;
+    GMM_TRY(resolve(GMM_OP_FP8_FWD, M, K, N, G, kind, out_dtype == GMM_BF16,
+                    kind != 0 && q_out != nullptr, &cfg));
     if (M == 0) return GMM_OK;
-    return hip_status(gmm::launch_fp8_fwd(lhs, kind, lhs_scale, rhs, rhs_scale, group_sizes,
+    return hip_status(gmm::launch_fp8_fwd(cfg, lhs, kind, lhs_scale, rhs, rhs_scale, group_sizes,
                                           (int)M, (int)K, (int)N, (int)G, out,
                                           out_dtype == GMM_BF16, q_out, scale_out, ws_status(ws),
                                           (hipStream_t)stream));
@@ -312,11 +381,14 @@ int gmm_fp8_fwd_noalloc(const void* lhs, int lhs_dtype, const float* lhs_scale,
         return fail(GMM_ERR_WORKSPACE,
                     "this shape needs %zu bytes of workspace; the library's static scratch holds %zu",
                     need, gmm::kNoallocScratchBytes);
+    gmm::TileConfig cfg;
+    GMM_TRY(resolve(GMM_OP_FP8_FWD, M, K, N, G, kind, out_dtype == GMM_BF16,
+                    kind != 0 && q_out != nullptr, &cfg));
     if (M == 0) return GMM_OK;
     void* ws = nullptr;
     size_t ws_bytes = 0;
     GMM_TRY(hip_status(gmm::noalloc_scratch(&ws, &ws_bytes)));
-    return hip_status(gmm::launch_fp8_fwd(lhs, kind, lhs_scale, rhs, rhs_scale, group_sizes,
+    return hip_status(gmm::launch_fp8_fwd(cfg, lhs, kind, lhs_scale, rhs, rhs_scale, group_sizes,
                                           (int)M, (int)K, (int)N, (int)G, out,
                                           out_dtype == GMM_BF16, q_out, scale_out, ws_status(ws),
                                           (hipStream_t)stream));
@@ -349,8 +421,10 @@ int gmm_fp8_fwd_swiglu(const void* lhs, int lhs_dtype, const float* lhs_scale, c
     const int64_t blocks = ((M + 47) / 48 + G + 1) * (N / 256);
     if (blocks > kMaxDim) return fail(GMM_ERR_SHAPE, "grid too large");
     GMM_TRY(check_ws(ws, ws_bytes, gmm_workspace_bytes(GMM_OP_FP8_FWD_SWIGLU, M, K, N, G)));
+    gmm::TileConfig cfg;
+    GMM_TRY(resolve(GMM_OP_FP8_FWD_SWIGLU, M, K, N, G, kind, out_dtype == GMM_BF16, false, &cfg));
     if (M == 0) return GMM_OK;
-    return hip_status(gmm::launch_fp8_fwd_swiglu(lhs, kind, lhs_scale, rhs, rhs_scale,
+    return hip_status(gmm::launch_fp8_fwd_swiglu(cfg, lhs, kind, lhs_scale, rhs, rhs_scale,
                                                  group_sizes, (int)M, (int)K, (int)N, (int)G, out,
                                                  out_dtype == GMM_BF16, act_q, act_scale,
                                                  ws_status(ws), (hipStream_t)stream));
@@ -370,8 +444,10 @@ int gmm_bf16_fwd(const void* lhs, const void* rhs, const int32_t* group_sizes, i
     const int64_t blocks = ((M + 127) / 128 + G + 1) * (N / 128);
     if (blocks > kMaxDim) return fail(GMM_ERR_SHAPE, "grid too large");
     GMM_TRY(check_ws(ws, ws_bytes, gmm_workspace_bytes(GMM_OP_BF16_FWD, M, K, N, G)));
+    gmm::TileConfig cfg;
+    GMM_TRY(resolve(GMM_OP_BF16_FWD, M, K, N, G, 1, out_dtype == GMM_BF16, false, &cfg));
     if (M == 0) return GMM_OK;
-    return hip_status(gmm::launch_bf16_fwd(lhs, rhs, group_sizes, (int)M, (int)K, (int)N, (int)G,
+    return hip_status(gmm::launch_bf16_fwd(cfg, lhs, rhs, group_sizes, (int)M, (int)K, (int)N, (int)G,
                                            out, out_dtype == GMM_BF16, ws_status(ws),
                                            (hipStream_t)stream));
 }
@@ -389,7 +465,9 @@ int tgmm_bf16(const void* x, const void* dy, const int32_t* group_sizes, int64_t
     GMM_TRY(check_ptr(dw, "dw"));
     if (G * (K / 128) * (N / 128) > kMaxDim) return fail(GMM_ERR_SHAPE, "grid too large");
     GMM_TRY(check_ws(ws, ws_bytes, gmm_workspace_bytes(GMM_OP_TGMM, M, K, N, G)));
-    return hip_status(gmm::launch_tgmm(x, dy, group_sizes, (int)M, (int)K, (int)N, (int)G, dw,
+    gmm::TileConfig cfg;
+    GMM_TRY(resolve(GMM_OP_TGMM, M, K, N, G, 1, out_dtype == GMM_BF16, false, &cfg));
+    return hip_status(gmm::launch_tgmm(cfg, x, dy, group_sizes, (int)M, (int)K, (int)N, (int)G, dw,
                                        out_dtype == GMM_BF16, ws_status(ws), (hipStream_t)stream));
 }
 
@@ -407,8 +485,10 @@ int gmm_bf16_dx(const void* dy, const void* w, const int32_t* group_sizes, int64
     const int64_t blocks = ((M + 127) / 128 + G + 1) * (K / 128);
     if (blocks > kMaxDim) return fail(GMM_ERR_SHAPE, "grid too large");
     GMM_TRY(check_ws(ws, ws_bytes, gmm_workspace_bytes(GMM_OP_DX, M, K, N, G)));
+    gmm::TileConfig cfg;
+    GMM_TRY(resolve(GMM_OP_DX, M, K, N, G, 1, out_dtype == GMM_BF16, false, &cfg));
     if (M == 0) return GMM_OK;
-    return hip_status(gmm::launch_bf16_dx(dy, w, group_sizes, (int)M, (int)K, (int)N, (int)G, dx,
+    return hip_status(gmm::launch_bf16_dx(cfg, dy, w, group_sizes, (int)M, (int)K, (int)N, (int)G, dx,
                                           out_dtype == GMM_BF16, ws_status(ws), (hipStream_t)stream));
 }
 

@@ -19,8 +19,7 @@
 // memory and read transposed with ds_read_b64_tr_b16, the in-LDS transpose of
 // gfx950.  tgmm walks the expert's rows 64 at a time, so its reduction tile
 // is 64 rows while the forward's is 64 K-columns.
-#include <cstdlib>
-
+#include "gmm_config.hpp"
 #include "gmm_device.hpp"
 #include "gmm_launch.hpp"
 
@@ -156,7 +155,7 @@ __device__ __forceinline__ bool tgmm_pick(int base, int G, int lo, int hi, int c
 // 256 groups the ranges stay in registers (one load and one scan per 64
 // groups); beyond, the second pass reads and scans them again.
 __device__ inline TgmmTile tgmm_tile(const int32_t* __restrict__ group_sizes, int G, int M, int T,
-                                     int L) {
+                                     int L, int placement) {
     const bool inreg = G <= 256;
     int glo[4], ghi[4];
     // pass 1: clamped ranges, class counts and the total
@@ -187,8 +186,10 @@ __device__ inline TgmmTile tgmm_tile(const int32_t* __restrict__ group_sizes, in
         }
     }
     const int tot = min(carry, M);
-    // skewed: some group holds more than four times the mean
-    const bool skewed = T % kNumXcd == 0 && [&] {
+    // skewed: some group holds more than four times the mean (placement 0);
+    // placement 1 / 2 force the contiguous / spread mapping (the host checks
+    // that spreading has a multiple of 8 tiles per group)
+    const bool skewed = placement == 2 || (placement == 0 && T % kNumXcd == 0 && [&] {
         bool big = false;
         if (inreg) {
 #pragma unroll
@@ -202,7 +203,7 @@ __device__ inline TgmmTile tgmm_tile(const int32_t* __restrict__ group_sizes, in
             }
         }
         return __ballot(big) != 0ull;
-    }();
+    }());
     TgmmTile out;
     out.g = -1;   // stays so only for blocks >= G * T (none are launched)
     out.row_lo = out.row_hi = 0;
@@ -258,7 +259,7 @@ template <int MODE, bool OUT_BF16, int MINB>
 __global__ __launch_bounds__(256, MINB) void bf16_gemm_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
     const int32_t* __restrict__ group_sizes, int M, int K, int N, int G, void* __restrict__ out,
-    int ntiles_c, int ntiles_r, int nblocks, int32_t* __restrict__ status) {
+    int ntiles_c, int ntiles_r, int nblocks, int placement, int32_t* __restrict__ status) {
     constexpr bool A_TR = MODE == kTgmm;
     constexpr bool B_TR = MODE != kDx;
     __shared__ __attribute__((aligned(16))) uint16_t sA[kTileElems];
@@ -277,7 +278,7 @@ __global__ __launch_bounds__(256, MINB) void bf16_gemm_kernel(
     int g, row0, lo, hi, c0, red_lo, red_hi;
     if constexpr (MODE == kTgmm) {
         if (wave == 0) {
-            const TgmmTile tt = tgmm_tile(group_sizes, G, M, ntiles_r * ntiles_c, L);
+            const TgmmTile tt = tgmm_tile(group_sizes, G, M, ntiles_r * ntiles_c, L, placement);
             if (lane == 0) { s_info[0] = tt.row_lo; s_info[1] = tt.row_hi; s_info[2] = tt.g; s_info[3] = tt.t; }
         }
         __syncthreads();
@@ -434,8 +435,9 @@ __global__ __launch_bounds__(256, MINB) void bf16_gemm_kernel(
 }
 
 template <int MODE>
-hipError_t launch_mode(const void* A, const void* B, const int32_t* group_sizes, int M, int K,
-                       int N, int G, void* out, bool out_bf16, int32_t* status, hipStream_t stream) {
+hipError_t launch_mode(const TileConfig& cfg, const void* A, const void* B,
+                       const int32_t* group_sizes, int M, int K, int N, int G, void* out,
+                       bool out_bf16, int32_t* status, hipStream_t stream) {
     int ntiles_c, ntiles_r = 0;
     int64_t nblocks;
     if constexpr (MODE == kTgmm) {
@@ -449,46 +451,41 @@ hipError_t launch_mode(const void* A, const void* B, const int32_t* group_sizes,
     const uint16_t* a = reinterpret_cast<const uint16_t*>(A);
     const uint16_t* b = reinterpret_cast<const uint16_t*>(B);
     const dim3 grid((unsigned)nblocks), block(256);
-    // GMM_BF16_MINB=<2|3> forces the choice (for tile sweeps)
-    static const int forced_minb = [] {
-        const char* e = std::getenv("GMM_BF16_MINB");
-        const int v = e ? std::atoi(e) : 0;
-        return v == 2 || v == 3 ? v : 0;
-    }();
-    const bool two = forced_minb ? forced_minb == 2 : nblocks <= 2 * (int64_t)device_cus();
-    if (two) {
+    const int pl = cfg.placement;
+    // residency: workgroups per CU the register allocation allows (gmm_config.cpp)
+    if (cfg.residency == 2) {
         if (out_bf16)
             hipLaunchKernelGGL((bf16_gemm_kernel<MODE, true, 2>), grid, block, 0, stream, a, b,
-                               group_sizes, M, K, N, G, out, ntiles_c, ntiles_r, (int)nblocks, status);
+                               group_sizes, M, K, N, G, out, ntiles_c, ntiles_r, (int)nblocks, pl, status);
         else
             hipLaunchKernelGGL((bf16_gemm_kernel<MODE, false, 2>), grid, block, 0, stream, a, b,
-                               group_sizes, M, K, N, G, out, ntiles_c, ntiles_r, (int)nblocks, status);
+                               group_sizes, M, K, N, G, out, ntiles_c, ntiles_r, (int)nblocks, pl, status);
     } else {
         if (out_bf16)
             hipLaunchKernelGGL((bf16_gemm_kernel<MODE, true, 3>), grid, block, 0, stream, a, b,
-                               group_sizes, M, K, N, G, out, ntiles_c, ntiles_r, (int)nblocks, status);
+                               group_sizes, M, K, N, G, out, ntiles_c, ntiles_r, (int)nblocks, pl, status);
         else
             hipLaunchKernelGGL((bf16_gemm_kernel<MODE, false, 3>), grid, block, 0, stream, a, b,
-                               group_sizes, M, K, N, G, out, ntiles_c, ntiles_r, (int)nblocks, status);
+                               group_sizes, M, K, N, G, out, ntiles_c, ntiles_r, (int)nblocks, pl, status);
     }
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_bf16_fwd(const void* lhs, const void* rhs, const int32_t* group_sizes, int M,
+hipError_t launch_bf16_fwd(const TileConfig& cfg, const void* lhs, const void* rhs, const int32_t* group_sizes, int M,
                            int K, int N, int G, void* out, bool out_bf16, int32_t* status, hipStream_t stream) {
-    return launch_mode<kFwd>(lhs, rhs, group_sizes, M, K, N, G, out, out_bf16, status, stream);
+    return launch_mode<kFwd>(cfg, lhs, rhs, group_sizes, M, K, N, G, out, out_bf16, status, stream);
 }
 
-hipError_t launch_bf16_dx(const void* dy, const void* w, const int32_t* group_sizes, int M,
+hipError_t launch_bf16_dx(const TileConfig& cfg, const void* dy, const void* w, const int32_t* group_sizes, int M,
                           int K, int N, int G, void* dx, bool out_bf16, int32_t* status, hipStream_t stream) {
-    return launch_mode<kDx>(dy, w, group_sizes, M, K, N, G, dx, out_bf16, status, stream);
+    return launch_mode<kDx>(cfg, dy, w, group_sizes, M, K, N, G, dx, out_bf16, status, stream);
 }
 
-hipError_t launch_tgmm(const void* x, const void* dy, const int32_t* group_sizes, int M, int K,
+hipError_t launch_tgmm(const TileConfig& cfg, const void* x, const void* dy, const int32_t* group_sizes, int M, int K,
                        int N, int G, void* dw, bool out_bf16, int32_t* status, hipStream_t stream) {
-    return launch_mode<kTgmm>(x, dy, group_sizes, M, K, N, G, dw, out_bf16, status, stream);
+    return launch_mode<kTgmm>(cfg, x, dy, group_sizes, M, K, N, G, dw, out_bf16, status, stream);
 }
 
 }  // namespace gmm

@@ -1,0 +1,191 @@
+// Tile configurations: the library's choice per operation and shape, and the
+// process-wide override a tile search sets through gmm_set_tile_config.
+#include <mutex>
+
+#include "gmm_config.hpp"
+#include "gmm_launch.hpp"
+
+namespace gmm {
+
+namespace {
+
+std::mutex g_mu;
+TileConfig g_override[kNumOps] = {};
+
+int64_t items(int64_t M, int64_t G, int64_t tm) { return (M + tm - 1) / tm + G + 1; }
+
+// the row-resident FP8 kernel addresses one expert's weights with 32-bit offsets
+bool offsets_fit(int64_t K, int64_t N) { return N * K < (int64_t(1) << 32); }
+
+bool fail(const char** why, const char* w) {
+    if (why) *why = w;
+    return false;
+}
+
+bool any_set(const TileConfig& f) {
+    return f.kernel || f.waves || f.tile_m || f.tile_n || f.depth || f.residency || f.placement;
+}
+
+// Row-resident sweep: 512-column tiles hold up to 8 K steps in LDS, 256-column
+// tiles (bf16 output only) up to 16.
+bool rr_fits(int64_t K, int64_t N, int tn, bool out_bf16, bool write_q) {
+    if (write_q || !offsets_fit(K, N) || N % tn != 0) return false;
+    return tn == 512 ? K <= 1024 : (tn == 256 && K <= 2048 && out_bf16);
+}
+
+bool resolve_fp8(const TileConfig& f, int64_t M, int64_t K, int64_t N, int64_t G, bool out_bf16,
+                 bool write_q, TileConfig* c, const char** why) {
+    *c = TileConfig{};
+    if (!any_set(f)) {   // the library's own choice
+        if (N % 512 == 0 && N >= 1024 && rr_fits(K, N, 512, out_bf16, write_q)) {
+            c->kernel = kKerRowResident;
+            c->tile_m = 48;
+            c->tile_n = 512;
+            return true;
+        }
+        c->tile_n = N % 512 == 0 ? 512 : (N % 256 == 0 ? 256 : 128);
+        c->tile_m = items(M, G, 48) * (N / c->tile_n) <= device_cus() ? 48 : 64;
+        if (c->tile_n == 512 && c->tile_m == 48) {
+            c->kernel = kKerWs;
+            c->waves = write_q ? 8 : 16;
+            c->depth = 1;
+        } else {
+            c->kernel = kKerUniform;
+        }
+        return true;
+    }
+    if (f.residency || f.placement) return fail(why, "residency/placement apply to the bf16 calls");
+    switch (f.kernel) {
+        case kKerWs:
+            if (N % 512 != 0) return fail(why, "the warp-specialised kernel needs N % 512 == 0");
+            if ((f.tile_n && f.tile_n != 512) || (f.tile_m && f.tile_m != 48))
+                return fail(why, "the warp-specialised kernel has 48 x 512 tiles");
+            c->kernel = kKerWs;
+            c->tile_m = 48;
+            c->tile_n = 512;
+            c->waves = f.waves ? f.waves : (write_q ? 8 : 16);
+            c->depth = f.depth ? f.depth : 1;
+            if (write_q && c->waves != 8) return fail(why, "writing the LHS codes takes the 8-wave form");
+            if (c->depth == 2 && c->waves != 12) return fail(why, "two steps of weights in flight need 12 waves");
+            return true;
+        case kKerUniform:
+            if (f.waves || f.depth) return fail(why, "waves/depth apply to the warp-specialised kernel");
+            c->kernel = kKerUniform;
+            c->tile_n = f.tile_n ? f.tile_n : (N % 512 == 0 ? 512 : (N % 256 == 0 ? 256 : 128));
+            if (N % c->tile_n != 0) return fail(why, "tile_n must divide N");
+            if (c->tile_n != 128 && c->tile_n != 256 && c->tile_n != 512)
+                return fail(why, "tile_n is 128, 256 or 512");
+            c->tile_m = f.tile_m ? f.tile_m
+                                 : (items(M, G, 48) * (N / c->tile_n) <= device_cus() ? 48 : 64);
+            if (c->tile_m != 48 && c->tile_m != 64) return fail(why, "tile_m is 48 or 64");
+            return true;
+        case kKerRowResident:
+            if (f.waves || f.depth || (f.tile_m && f.tile_m != 48))
+                return fail(why, "the row-resident kernel has 48-row tiles of 16 waves");
+            c->kernel = kKerRowResident;
+            c->tile_m = 48;
+            c->tile_n = f.tile_n ? f.tile_n : (K <= 1024 ? 512 : 256);
+            if (!rr_fits(K, N, c->tile_n, out_bf16, write_q))
+                return fail(why, "the row-resident kernel does not fit this shape (K, N, output dtype or code output)");
+            return true;
+        default:
+            return fail(why, "an FP8 override names its kernel (1, 2 or 3)");
+    }
+}
+
+bool resolve_mxfp4(const TileConfig& f, int64_t K, int64_t N, TileConfig* c, const char** why) {
+    *c = TileConfig{};
+    if (!any_set(f)) {
+        if (N % 512 == 0 && N >= 1024 && K <= 1024 && offsets_fit(K, N)) {
+            c->kernel = kKerRowResident;
+            c->tile_n = 512;
+        } else {
+            c->kernel = kKerWs;
+            c->tile_n = N % 512 == 0 ? 512 : (N % 256 == 0 ? 256 : 128);
+        }
+        c->tile_m = 48;
+        c->waves = 16;
+        return true;
+    }
+    if (f.waves && f.waves != 16) return fail(why, "the MXFP4 forward runs 16 waves");
+    if ((f.tile_m && f.tile_m != 48) || f.depth || f.residency || f.placement)
+        return fail(why, "the MXFP4 forward sets only kernel and tile_n");
+    c->tile_m = 48;
+    c->waves = 16;
+    if (f.kernel == kKerRowResident) {
+        c->kernel = kKerRowResident;
+        c->tile_n = 512;
+        if ((f.tile_n && f.tile_n != 512) || N % 512 != 0 || K > 1024 || !offsets_fit(K, N))
+            return fail(why, "the row-resident MXFP4 kernel needs N % 512 == 0 and K <= 1024");
+        return true;
+    }
+    if (f.kernel != kKerWs && f.kernel != kKerAuto) return fail(why, "MXFP4 kernels are 1 or 3");
+    c->kernel = kKerWs;
+    c->tile_n = f.tile_n ? f.tile_n : (N % 512 == 0 ? 512 : (N % 256 == 0 ? 256 : 128));
+    if ((c->tile_n != 128 && c->tile_n != 256 && c->tile_n != 512) || N % c->tile_n != 0)
+        return fail(why, "tile_n must be 128, 256 or 512 and divide N");
+    return true;
+}
+
+bool resolve_swiglu(const TileConfig& f, int64_t M, int64_t N, int64_t G, TileConfig* c,
+                    const char** why) {
+    *c = TileConfig{};
+    c->kernel = kKerUniform;
+    c->tile_n = 256;
+    if (f.tile_m && f.tile_m != 48 && f.tile_m != 64) return fail(why, "tile_m is 48 or 64");
+    if ((f.kernel && f.kernel != kKerUniform) || f.waves || (f.tile_n && f.tile_n != 256) || f.depth ||
+        f.residency || f.placement)
+        return fail(why, "the fused gate+up forward sets only tile_m");
+    // 48-row tiles while their grid is at most two rounds of the chip
+    c->tile_m = f.tile_m ? f.tile_m : (items(M, G, 48) * (N / 256) <= 2 * device_cus() ? 48 : 64);
+    return true;
+}
+
+bool resolve_bf16(int op, const TileConfig& f, int64_t M, int64_t K, int64_t N, int64_t G,
+                  TileConfig* c, const char** why) {
+    *c = TileConfig{};
+    if (f.kernel || f.waves || f.tile_m || f.tile_n || f.depth)
+        return fail(why, "the bf16 calls set residency (and tgmm placement) only");
+    if (f.residency && f.residency != 2 && f.residency != 3) return fail(why, "residency is 2 or 3");
+    const int64_t nblocks = op == kOpTgmm ? G * (K / 128) * (N / 128)
+                                          : items(M, G, 128) * ((op == kOpDx ? K : N) / 128);
+    c->residency = f.residency ? f.residency : (nblocks <= 2 * (int64_t)device_cus() ? 2 : 3);
+    if (op == kOpTgmm) {
+        if (f.placement && f.placement != 1 && f.placement != 2) return fail(why, "placement is 1 or 2");
+        if (f.placement == 2 && ((K / 128) * (N / 128)) % 8 != 0)
+            return fail(why, "spreading a group over the XCDs needs a multiple of 8 tiles per group");
+        c->placement = f.placement;   // 0: decided in the kernel from the group sizes
+    } else if (f.placement) {
+        return fail(why, "placement applies to tgmm");
+    }
+    return true;
+}
+
+}  // namespace
+
+TileConfig tile_override(int op) {
+    std::lock_guard<std::mutex> lock(g_mu);
+    return op >= 0 && op < kNumOps ? g_override[op] : TileConfig{};
+}
+
+void set_tile_override(int op, const TileConfig* cfg) {
+    std::lock_guard<std::mutex> lock(g_mu);
+    g_override[op] = cfg ? *cfg : TileConfig{};
+}
+
+bool resolve_tile_config(int op, int64_t M, int64_t K, int64_t N, int64_t G, int lhs_kind,
+                         bool out_bf16, bool write_q, TileConfig* out, const char** why) {
+    (void)lhs_kind;
+    const TileConfig f = tile_override(op);
+    switch (op) {
+        case kOpFp8Fwd: return resolve_fp8(f, M, K, N, G, out_bf16, write_q, out, why);
+        case kOpFp8Swiglu: return resolve_swiglu(f, M, N, G, out, why);
+        case kOpFp8Mxfp4: return resolve_mxfp4(f, K, N, out, why);
+        case kOpBf16Fwd:
+        case kOpTgmm:
+        case kOpDx: return resolve_bf16(op, f, M, K, N, G, out, why);
+        default: *out = TileConfig{}; return true;
+    }
+}
+
+}  // namespace gmm

@@ -49,11 +49,9 @@
 //    or 16-byte (fp32) runs directly.
 #include <type_traits>
 
+#include "gmm_config.hpp"
 #include "gmm_device.hpp"
 #include "gmm_launch.hpp"
-
-#include <cstdio>
-#include <cstdlib>
 
 namespace gmm {
 
@@ -554,22 +552,25 @@ __global__ __launch_bounds__(kThreads, 2) void fp8_fwd_kernel(
 // the FMA factor is the LHS scale alone.  The producers store the LHS codes
 // with K runs 1<->2 and 5<->6 of 16 exchanged (the MFMA's K grouping for an
 // FP4 first operand, which the packed weights follow).
-template <int KIND, bool OUT_BF16, int TM, bool WRITE_Q, int NW = 8, int TN = 512, bool B4 = false>
-__global__ __launch_bounds__(64 * NW, NW == 16 ? 4 : 2) void fp8_fwd_ws_kernel(   // TM = 48 (64 spills)
+template <int KIND, bool OUT_BF16, int TM, bool WRITE_Q, int NW = 8, int TN = 512, bool B4 = false,
+          int NP = NW / 2, int BD = 1>
+__global__ __launch_bounds__(64 * NW, NW / 4) void fp8_fwd_ws_kernel(   // TM = 48 (64 spills)
     const void* __restrict__ lhs, const float* __restrict__ lhs_scale,
     const uint8_t* __restrict__ rhs, const void* __restrict__ rhs_scale_v,
     const int32_t* __restrict__ group_sizes, int M, int K, int N, int G, void* __restrict__ out,
     uint8_t* __restrict__ q_out, float* __restrict__ s_out, int ntiles_n, int nblocks,
     int32_t* __restrict__ status) {
     static_assert(TM == 64 || TM == 48, "64- or 48-row tiles");
-    static_assert(NW == 8 || NW == 16, "8 or 16 waves");
-    static_assert(B4 ? (NW == 16 && (TN == 512 || TN == 256 || TN == 128)) : TN == 512,
+    static_assert(NW == 8 || NW == 12 || NW == 16, "8, 12 or 16 waves");
+    static_assert(NP == 4 || NP == 8, "4 or 8 producer waves");
+    static_assert(B4 ? (NW == 16 && NP == 8 && (TN == 512 || TN == 256 || TN == 128)) : TN == 512,
                   "FP8 weights: 512 columns; MXFP4: 16 waves, 512/256/128 columns");
     constexpr int MB = TM / 16;
-    constexpr int NC = NW / 2;             // consumer waves (and producer waves)
+    constexpr int NC = NW - NP;            // consumer waves
+    static_assert(NC == 4 || NC == 8, "4 or 8 consumer waves");
     constexpr int CWID = TN / NC;          // output columns per consumer wave
     constexpr int NBC = CWID / 16;         // 16-column blocks per consumer wave
-    constexpr int HP = 8 / NC;             // rows per producer lane
+    constexpr int HP = 8 / NP;             // rows per producer lane
     const float* __restrict__ rhs_scale = reinterpret_cast<const float*>(rhs_scale_v);
     const uint8_t* __restrict__ rhs_e8 = reinterpret_cast<const uint8_t*>(rhs_scale_v);
     constexpr int kThr = 64 * NW;
@@ -709,27 +710,34 @@ __global__ __launch_bounds__(64 * NW, NW == 16 ? 4 : 2) void fp8_fwd_ws_kernel( 
     for (int i = 0; i < MB; ++i)
 #pragma unroll
         for (int j = 0; j < NBC; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-    v8i b[NBC];
-    int be[NBC];
-    auto load_b1 = [&](int j, int kb) {
+    // B of the next BD steps in registers: set s holds the steps k with
+    // k % BD == s (the loop below runs steps in pairs, so s is static)
+    v8i b[BD][NBC];
+    int be[BD][NBC];
+    auto load_b1 = [&](int s, int j, int kb) {
         if constexpr (B4) {
             const v4i lo = *reinterpret_cast<const v4i*>(bptr + ((int64_t)j * nkb + kb) * 1024);
-            b[j] = __builtin_shufflevector(lo, lo, 0, 1, 2, 3, -1, -1, -1, -1);
-            be[j] = eptr[((int64_t)j * nkb + kb) * 64];
+            b[s][j] = __builtin_shufflevector(lo, lo, 0, 1, 2, 3, -1, -1, -1, -1);
+            be[s][j] = eptr[((int64_t)j * nkb + kb) * 64];
         } else {
             const uint8_t* q = bptr + ((int64_t)j * nkb + kb) * 2048;
             const uint4 lo = *reinterpret_cast<const uint4*>(q);
             const uint4 hi = *reinterpret_cast<const uint4*>(q + 1024);
-            b[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            b[s][j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
         }
     };
 #pragma unroll
-    for (int j = 0; j < NBC; ++j) load_b1(j, 0);
+    for (int s = 0; s < BD; ++s)
+#pragma unroll
+        for (int j = 0; j < NBC; ++j) load_b1(s, j, min(s, nkb - 1));
     __syncthreads();
-    // step k: fragments and factors of k from buffer k&1, MFMAs of k with b,
-    // each B block reloaded with k+1 right after its MFMAs
-    auto cstep = [&](int k) {
-        const int buf = k & 1, k1 = min(k + 1, nkb - 1);
+    // step k: fragments and factors of k from buffer k&1, MFMAs of k with B
+    // set k % BD, each B block reloaded with step k+BD right after its MFMAs
+    auto cstep = [&](int k, auto set) {
+        constexpr int S = decltype(set)::value;
+        v8i (&bs)[NBC] = b[S];
+        int (&bes)[NBC] = be[S];
+        const int buf = k & 1, k1 = min(k + BD, nkb - 1);
         v8i af[MB];
         float cf[MB];
 #pragma unroll
@@ -744,23 +752,23 @@ __global__ __launch_bounds__(64 * NW, NW == 16 ? 4 : 2) void fp8_fwd_ws_kernel( 
                 v4f pr;
                 if constexpr (B4)   // first operand E2M1 with its E8M0 scale
                     pr = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        b[j], af[i], v4f{0.f, 0.f, 0.f, 0.f}, 4, 0, 0, be[j], 0, 127);
+                        bs[j], af[i], v4f{0.f, 0.f, 0.f, 0.f}, 4, 0, 0, bes[j], 0, 127);
                 else
                     pr = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        b[j], af[i], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+                        bs[j], af[i], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(pr[r], cf[i], acc[i][j][r]);
             }
-            load_b1(j, k1);
+            load_b1(S, j, k1);
         }
         __syncthreads();
     };
     int k = 0;
     for (; k + 1 < nkb; k += 2) {
-        cstep(k);
-        cstep(k + 1);
+        cstep(k, std::integral_constant<int, 0>{});
+        cstep(k + 1, std::integral_constant<int, 1 % BD>{});
     }
-    if (k < nkb) cstep(k);
+    if (k < nkb) cstep(k, std::integral_constant<int, 0>{});
 
     // ---- epilogue: this wave's TM x CWID block through its LDS region (the
     //      last barrier retired every read of the A tiles), stored back as
@@ -807,13 +815,14 @@ __global__ __launch_bounds__(64 * NW, NW == 16 ? 4 : 2) void fp8_fwd_ws_kernel( 
 // k's codes ready); its loop is separate from the later tiles', which have
 // no barrier at all.  B4: MXFP4 weights as in fp8_fwd_ws_kernel (codes in
 // the MFMA's FP4 K grouping, E8M0 scales on the MFMA, LHS scale on the FMA).
-template <int KIND, bool OUT_BF16, int KBM, bool B4 = false>
+template <int KIND, bool OUT_BF16, int KBM, bool B4 = false, int TN = 512>
 __global__ __launch_bounds__(1024, 4) void fp8_fwd_wsn_kernel(
     const void* __restrict__ lhs, const float* __restrict__ lhs_scale,
     const uint8_t* __restrict__ rhs, const void* __restrict__ rhs_scale_v,
     const int32_t* __restrict__ group_sizes, int M, int K, int N, int G, void* __restrict__ out,
     int nblocks, int32_t* __restrict__ status) {
-    constexpr int TM = 48, MB = TM / 16, NC = 8, CWID = 64, NBC = CWID / 16, TN = 512;
+    static_assert(TN == 512 || TN == 256, "512- or 256-column tiles");
+    constexpr int TM = 48, MB = TM / 16, NC = 8, CWID = TN / NC, NBC = CWID / 16;
     constexpr int kThr = 1024;
     constexpr int OUT_BYTES = OUT_BF16 ? 2 : 4;
     constexpr int kEpiRow = CWID * OUT_BYTES + 16;
@@ -1019,23 +1028,34 @@ __global__ __launch_bounds__(1024, 4) void fp8_fwd_wsn_kernel(
 // offsets (at most N*K bytes of codes), so it runs only when they fit.
 inline bool wsn_offsets_fit(int K, int N) { return (int64_t)N * K < (int64_t(1) << 32); }
 
-template <int KIND, int KBM, bool B4 = false>
+template <int KIND, int KBM, bool B4 = false, int TN = 512>
 hipError_t launch_wsn(const void* lhs, const float* lhs_scale, const uint8_t* rhs,
                       const void* rhs_scale, const int32_t* group_sizes, int M, int K, int N,
                       int G, void* out, bool out_bf16, int32_t* status, hipStream_t stream) {
     const int nblocks = (int)max_work_items(M, G, 48);
-    if (out_bf16)
-        hipLaunchKernelGGL((fp8_fwd_wsn_kernel<KIND, true, KBM, B4>), dim3(nblocks), dim3(1024), 0,
+    // LDS of the fp32-output form: resident codes and scales plus fp32
+    // staging rows; beyond the 160 KB of a CU only bf16 output is offered
+    constexpr int kF32Lds = KBM * 48 * (kLdsRow + 4) + 8 * 48 * ((TN / 8) * 4 + 16);
+    if constexpr (kF32Lds > 160 * 1024) {
+        if (!out_bf16) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((fp8_fwd_wsn_kernel<KIND, true, KBM, B4, TN>), dim3(nblocks), dim3(1024), 0,
                            stream, lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N, G, out,
                            nblocks, status);
-    else
-        hipLaunchKernelGGL((fp8_fwd_wsn_kernel<KIND, false, KBM, B4>), dim3(nblocks), dim3(1024), 0,
-                           stream, lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N, G, out,
-                           nblocks, status);
+    } else {
+        if (out_bf16)
+            hipLaunchKernelGGL((fp8_fwd_wsn_kernel<KIND, true, KBM, B4, TN>), dim3(nblocks), dim3(1024),
+                               0, stream, lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N, G, out,
+                               nblocks, status);
+        else
+            hipLaunchKernelGGL((fp8_fwd_wsn_kernel<KIND, false, KBM, B4, TN>), dim3(nblocks), dim3(1024),
+                               0, stream, lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N, G, out,
+                               nblocks, status);
+    }
     return hipGetLastError();
 }
 
-template <int KIND, int TM, bool WRITE_Q, int NW = 8, int TN = 512, bool B4 = false>
+template <int KIND, int TM, bool WRITE_Q, int NW = 8, int TN = 512, bool B4 = false, int NP = NW / 2,
+          int BD = 1>
 hipError_t launch_ws(const void* lhs, const float* lhs_scale, const uint8_t* rhs,
                      const void* rhs_scale, const int32_t* group_sizes, int M, int K, int N, int G,
                      void* out, bool out_bf16, uint8_t* q_out, float* scale_out, int32_t* status, hipStream_t stream) {
@@ -1043,47 +1063,35 @@ hipError_t launch_ws(const void* lhs, const float* lhs_scale, const uint8_t* rhs
     const int64_t items = max_work_items(M, G, TM);
     const int nblocks = (int)(items * ntiles_n);
     if (out_bf16)
-        hipLaunchKernelGGL((fp8_fwd_ws_kernel<KIND, true, TM, WRITE_Q, NW, TN, B4>), dim3(nblocks),
+        hipLaunchKernelGGL((fp8_fwd_ws_kernel<KIND, true, TM, WRITE_Q, NW, TN, B4, NP, BD>), dim3(nblocks),
                            dim3(64 * NW), 0, stream, lhs, lhs_scale, rhs, rhs_scale, group_sizes, M,
                            K, N, G, out, q_out, scale_out, ntiles_n, nblocks, status);
     else
-        hipLaunchKernelGGL((fp8_fwd_ws_kernel<KIND, false, TM, WRITE_Q, NW, TN, B4>), dim3(nblocks),
+        hipLaunchKernelGGL((fp8_fwd_ws_kernel<KIND, false, TM, WRITE_Q, NW, TN, B4, NP, BD>), dim3(nblocks),
                            dim3(64 * NW), 0, stream, lhs, lhs_scale, rhs, rhs_scale, group_sizes, M,
                            K, N, G, out, q_out, scale_out, ntiles_n, nblocks, status);
     return hipGetLastError();
 }
 
-// MXFP4 weights: 48-row tiles of the widest of 512/256/128 columns dividing N
-// (GMM_MXFP4_TN=<512|256|128> narrows it, for tile sweeps).
+// MXFP4 weights: the row-resident sweep (wide, shallow shapes) or the
+// warp-specialised kernel with 48-row tiles of cfg.tile_n columns.
 template <int KIND>
-hipError_t launch_mxfp4_kind(const void* lhs, const float* lhs_scale, const uint8_t* rhs_q,
-                             const uint8_t* rhs_e8, const int32_t* group_sizes, int M, int K,
-                             int N, int G, void* out, bool out_bf16, int32_t* status, hipStream_t stream) {
-    static const int forced_tn = [] {
-        const char* e = std::getenv("GMM_MXFP4_TN");
-        return e ? std::atoi(e) : 0;
-    }();
-    const int tn = (forced_tn == 128 || forced_tn == 256 || forced_tn == 512) && N % forced_tn == 0
-                       ? forced_tn
-                       : (N % 512 == 0 ? 512 : (N % 256 == 0 ? 256 : 128));
-    // wide, shallow shapes: the row-resident sweep over all 512-column tiles
-    // (GMM_FP8_WSN=0 turns it off)
-    static const bool use_wsn = [] {
-        const char* e = std::getenv("GMM_FP8_WSN");
-        return !(e && std::atoi(e) == 0);
-    }();
-    if (use_wsn && forced_tn == 0 && N % 512 == 0 && N >= 1024 && K <= 1024 && wsn_offsets_fit(K, N)) {
+hipError_t launch_mxfp4_kind(const TileConfig& cfg, const void* lhs, const float* lhs_scale,
+                             const uint8_t* rhs_q, const uint8_t* rhs_e8, const int32_t* group_sizes,
+                             int M, int K, int N, int G, void* out, bool out_bf16, int32_t* status,
+                             hipStream_t stream) {
+    if (cfg.kernel == kKerRowResident) {
         if (K <= 512)
             return launch_wsn<KIND, 4, true>(lhs, lhs_scale, rhs_q, rhs_e8, group_sizes, M, K, N, G,
                                              out, out_bf16, status, stream);
         return launch_wsn<KIND, 8, true>(lhs, lhs_scale, rhs_q, rhs_e8, group_sizes, M, K, N, G, out,
                                          out_bf16, status, stream);
     }
-    if (tn == 512)
+    if (cfg.tile_n == 512)
         return launch_ws<KIND, 48, false, 16, 512, true>(lhs, lhs_scale, rhs_q, rhs_e8, group_sizes,
                                                          M, K, N, G, out, out_bf16, nullptr,
                                                          nullptr, status, stream);
-    if (tn == 256)
+    if (cfg.tile_n == 256)
         return launch_ws<KIND, 48, false, 16, 256, true>(lhs, lhs_scale, rhs_q, rhs_e8, group_sizes,
                                                          M, K, N, G, out, out_bf16, nullptr,
                                                          nullptr, status, stream);
@@ -1125,69 +1133,48 @@ hipError_t launch_wn(const void* lhs, const float* lhs_scale, const uint8_t* rhs
                                            G, out, out_bf16, q_out, scale_out, status, stream);
 }
 
-// Tile: the widest of 512/256/128 columns that divides N (fewest
-// re-quantisations of each LHS row); 48 rows when even the worst-case number
-// of 48-row workgroups fits on the chip at once (more of the chip busy, less
-// work per workgroup), else 64.  GMM_FP8_WN=<16|32|64> and GMM_FP8_TM=<64|48>
-// override them (tuning sweeps only).
+// The FP8 forward with a resolved configuration (gmm_config.cpp: the
+// row-resident sweep for wide, shallow shapes; 48 x 512 tiles on the
+// warp-specialised kernel when even the worst-case grid fits the chip at
+// once; else the uniform kernel with the widest column tile dividing N).
 template <int KIND>
-hipError_t launch_kind(const void* lhs, const float* lhs_scale, const uint8_t* rhs,
-                       const float* rhs_scale, const int32_t* group_sizes, int M, int K, int N,
-                       int G, void* out, bool out_bf16, uint8_t* q_out, float* scale_out,
-                       int32_t* status, hipStream_t stream) {
-    static const int forced_wn = [] {
-        const char* e = std::getenv("GMM_FP8_WN");
-        return e ? std::atoi(e) : 0;
-    }();
-    static const int forced_tm = [] {
-        const char* e = std::getenv("GMM_FP8_TM");
-        return e ? std::atoi(e) : 0;
-    }();
-    int wn = N % 512 == 0 ? 64 : (N % 256 == 0 ? 32 : 16);
-    if ((forced_wn == 16 || forced_wn == 32 || forced_wn == 64) && N % (kWaves * forced_wn) == 0)
-        wn = forced_wn;
-    int tm = max_work_items(M, G, 48) * (N / (kWaves * wn)) <= device_cus() ? 48 : 64;
-    if (forced_tm == 48 || forced_tm == 64) tm = forced_tm;
-    // 512-column, 48-row tiles run the warp-specialised kernel: 16 waves (8
-    // MFMA waves of 64 columns, 6 quantiser waves of 8 rows each) unless the
-    // kernel also writes the LHS codes, which takes the 8-wave form.
-    // GMM_FP8_WS=0 selects the uniform kernel and GMM_FP8_WS_WAVES=8 the
-    // 8-wave form everywhere (comparison sweeps only).
-    static const bool use_ws = [] {
-        const char* e = std::getenv("GMM_FP8_WS");
-        return !(e && std::atoi(e) == 0);
-    }();
-    static const int ws_waves = [] {
-        const char* e = std::getenv("GMM_FP8_WS_WAVES");
-        return e && std::atoi(e) == 8 ? 8 : 16;
-    }();
-    // wide, shallow shapes: one workgroup per 48-row item sweeps all the
-    // 512-column tiles with its LHS rows quantised once and kept in LDS
-    // (GMM_FP8_WSN=0 turns this off, for comparison sweeps)
-    static const bool use_wsn = [] {
-        const char* e = std::getenv("GMM_FP8_WSN");
-        return !(e && std::atoi(e) == 0);
-    }();
-    if (use_wsn && forced_wn == 0 && forced_tm == 0 && N % 512 == 0 && N >= 1024 && K <= 1024 &&
-        wsn_offsets_fit(K, N) && (q_out == nullptr || KIND == kLhsE4M3)) {
+hipError_t launch_kind(const TileConfig& cfg, const void* lhs, const float* lhs_scale,
+                       const uint8_t* rhs, const float* rhs_scale, const int32_t* group_sizes,
+                       int M, int K, int N, int G, void* out, bool out_bf16, uint8_t* q_out,
+                       float* scale_out, int32_t* status, hipStream_t stream) {
+    const bool write_q = KIND != kLhsE4M3 && q_out != nullptr;
+    if (cfg.kernel == kKerRowResident) {
+        if (cfg.tile_n == 256)
+            return launch_wsn<KIND, 16, false, 256>(lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K,
+                                                    N, G, out, out_bf16, status, stream);
         if (K <= 512)
             return launch_wsn<KIND, 4>(lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N, G, out,
                                        out_bf16, status, stream);
         return launch_wsn<KIND, 8>(lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N, G, out,
                                    out_bf16, status, stream);
     }
-    if (use_ws && wn == 64 && tm == 48 && ws_waves == 16 && (q_out == nullptr || KIND == kLhsE4M3))
-        return launch_ws<KIND, 48, false, 16>(lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N,
-                                              G, out, out_bf16, q_out, scale_out, status, stream);
-    if (use_ws && wn == 64 && tm == 48) {
-        if (q_out != nullptr && KIND != kLhsE4M3)
-            return launch_ws<KIND, 48, true>(lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N,
-                                             G, out, out_bf16, q_out, scale_out, status, stream);
+    if (cfg.kernel == kKerWs) {
+        if (write_q)
+            return launch_ws<KIND, 48, true>(lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N, G,
+                                             out, out_bf16, q_out, scale_out, status, stream);
+        if (cfg.waves == 16)
+            return launch_ws<KIND, 48, false, 16>(lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N,
+                                                  G, out, out_bf16, nullptr, nullptr, status, stream);
+        if (cfg.waves == 12 && cfg.depth == 2)
+            return launch_ws<KIND, 48, false, 12, 512, false, 4, 2>(
+                lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N, G, out, out_bf16, nullptr,
+                nullptr, status, stream);
+        if (cfg.waves == 12)
+            return launch_ws<KIND, 48, false, 12, 512, false, 4>(lhs, lhs_scale, rhs, rhs_scale,
+                                                                 group_sizes, M, K, N, G, out,
+                                                                 out_bf16, nullptr, nullptr, status,
+                                                                 stream);
         return launch_ws<KIND, 48, false>(lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N, G,
-                                          out, out_bf16, q_out, scale_out, status, stream);
+                                          out, out_bf16, nullptr, nullptr, status, stream);
     }
+    const int wn = cfg.tile_n / kWaves;
 #define GMM_FP8_WN_TM(WN_, TM_)                                                                  \
-    if (wn == WN_ && tm == TM_)                                                                  \
+    if (wn == WN_ && cfg.tile_m == TM_)                                                          \
         return launch_wn<KIND, WN_, TM_>(lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N, G, \
                                          out, out_bf16, q_out, scale_out, status, stream);
     GMM_FP8_WN_TM(64, 64)
@@ -1200,24 +1187,13 @@ hipError_t launch_kind(const void* lhs, const float* lhs_scale, const uint8_t* r
                                    out_bf16, q_out, scale_out, status, stream);
 }
 
-// Fused gate+up: 256 output columns per workgroup; 48-row tiles under the
-// same rule as the plain forward.
+// Fused gate+up: 256 output columns per workgroup, cfg.tile_m rows.
 template <int KIND>
-hipError_t launch_swiglu_kind(const void* lhs, const float* lhs_scale, const uint8_t* rhs,
-                              const float* rhs_scale, const int32_t* group_sizes, int M, int K,
-                              int N, int G, void* out, bool out_bf16, uint8_t* act_q,
+hipError_t launch_swiglu_kind(const TileConfig& cfg, const void* lhs, const float* lhs_scale,
+                              const uint8_t* rhs, const float* rhs_scale, const int32_t* group_sizes,
+                              int M, int K, int N, int G, void* out, bool out_bf16, uint8_t* act_q,
                               float* act_scale, int32_t* status, hipStream_t stream) {
-    // 48-row tiles while their grid is at most two rounds of the chip (the
-    // tile sweep: wi gate+up, 406 workgroups on 256 CUs, 42.0 us at 48 rows
-    // vs 45.9 at 64; 810 workgroups, 79.2 vs 73.1 us).  GMM_SWIGLU_TM=<48|64>
-    // forces one (tile sweeps).
-    static const int forced_tm = [] {
-        const char* e = std::getenv("GMM_SWIGLU_TM");
-        return e ? std::atoi(e) : 0;
-    }();
-    const bool tm48 = forced_tm == 48 ||
-                      (forced_tm != 64 && max_work_items(M, G, 48) * (N / 256) <= 2 * device_cus());
-    if (tm48)
+    if (cfg.tile_m == 48)
         return launch_cfg<KIND, 64, 48, false, true>(lhs, lhs_scale, rhs, rhs_scale, group_sizes, M,
                                                      K, N, G, out, out_bf16, act_q, act_scale, status, stream);
     return launch_cfg<KIND, 64, 64, false, true>(lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K,
@@ -1226,54 +1202,54 @@ hipError_t launch_swiglu_kind(const void* lhs, const float* lhs_scale, const uin
 
 }  // namespace
 
-hipError_t launch_fp8_fwd_swiglu(const void* lhs, int lhs_kind, const float* lhs_scale,
+hipError_t launch_fp8_fwd_swiglu(const TileConfig& cfg, const void* lhs, int lhs_kind, const float* lhs_scale,
                                  const uint8_t* rhs, const float* rhs_scale,
                                  const int32_t* group_sizes, int M, int K, int N, int G,
                                  void* out, bool out_bf16, uint8_t* act_q, float* act_scale,
                                  int32_t* status, hipStream_t stream) {
     switch (lhs_kind) {
         case kLhsE4M3:
-            return launch_swiglu_kind<kLhsE4M3>(lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N,
+            return launch_swiglu_kind<kLhsE4M3>(cfg, lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N,
                                                 G, out, out_bf16, act_q, act_scale, status, stream);
         case kLhsBF16:
-            return launch_swiglu_kind<kLhsBF16>(lhs, nullptr, rhs, rhs_scale, group_sizes, M, K, N,
+            return launch_swiglu_kind<kLhsBF16>(cfg, lhs, nullptr, rhs, rhs_scale, group_sizes, M, K, N,
                                                 G, out, out_bf16, act_q, act_scale, status, stream);
         default:
-            return launch_swiglu_kind<kLhsF32>(lhs, nullptr, rhs, rhs_scale, group_sizes, M, K, N,
+            return launch_swiglu_kind<kLhsF32>(cfg, lhs, nullptr, rhs, rhs_scale, group_sizes, M, K, N,
                                                G, out, out_bf16, act_q, act_scale, status, stream);
     }
 }
 
-hipError_t launch_fp8_mxfp4_fwd(const void* lhs, int lhs_kind, const float* lhs_scale,
+hipError_t launch_fp8_mxfp4_fwd(const TileConfig& cfg, const void* lhs, int lhs_kind, const float* lhs_scale,
                                 const uint8_t* rhs_q, const uint8_t* rhs_scale,
                                 const int32_t* group_sizes, int M, int K, int N, int G, void* out,
                                 bool out_bf16, int32_t* status, hipStream_t stream) {
     switch (lhs_kind) {
         case kLhsE4M3:
-            return launch_mxfp4_kind<kLhsE4M3>(lhs, lhs_scale, rhs_q, rhs_scale, group_sizes, M, K,
+            return launch_mxfp4_kind<kLhsE4M3>(cfg, lhs, lhs_scale, rhs_q, rhs_scale, group_sizes, M, K,
                                                N, G, out, out_bf16, status, stream);
         case kLhsBF16:
-            return launch_mxfp4_kind<kLhsBF16>(lhs, nullptr, rhs_q, rhs_scale, group_sizes, M, K, N,
+            return launch_mxfp4_kind<kLhsBF16>(cfg, lhs, nullptr, rhs_q, rhs_scale, group_sizes, M, K, N,
                                                G, out, out_bf16, status, stream);
         default:
-            return launch_mxfp4_kind<kLhsF32>(lhs, nullptr, rhs_q, rhs_scale, group_sizes, M, K, N,
+            return launch_mxfp4_kind<kLhsF32>(cfg, lhs, nullptr, rhs_q, rhs_scale, group_sizes, M, K, N,
                                               G, out, out_bf16, status, stream);
     }
 }
 
-hipError_t launch_fp8_fwd(const void* lhs, int lhs_kind, const float* lhs_scale,
+hipError_t launch_fp8_fwd(const TileConfig& cfg, const void* lhs, int lhs_kind, const float* lhs_scale,
                           const uint8_t* rhs, const float* rhs_scale,
                           const int32_t* group_sizes, int M, int K, int N, int G, void* out,
                           bool out_bf16, uint8_t* q_out, float* scale_out, int32_t* status, hipStream_t stream) {
     switch (lhs_kind) {
         case kLhsE4M3:
-            return launch_kind<kLhsE4M3>(lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N, G,
+            return launch_kind<kLhsE4M3>(cfg, lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N, G,
                                          out, out_bf16, nullptr, nullptr, status, stream);
         case kLhsBF16:
-            return launch_kind<kLhsBF16>(lhs, nullptr, rhs, rhs_scale, group_sizes, M, K, N, G,
+            return launch_kind<kLhsBF16>(cfg, lhs, nullptr, rhs, rhs_scale, group_sizes, M, K, N, G,
                                          out, out_bf16, q_out, scale_out, status, stream);
         default:
-            return launch_kind<kLhsF32>(lhs, nullptr, rhs, rhs_scale, group_sizes, M, K, N, G,
+            return launch_kind<kLhsF32>(cfg, lhs, nullptr, rhs, rhs_scale, group_sizes, M, K, N, G,
                                         out, out_bf16, q_out, scale_out, status, stream);
     }
 }

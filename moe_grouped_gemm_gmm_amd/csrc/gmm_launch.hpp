@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "gmm_config.hpp"
+
 namespace gmm {
 
 // Compute units of the current device (queried once).
@@ -54,32 +56,32 @@ hipError_t launch_quantize_rhs_mxfp4(const void* w, bool w_bf16, int64_t G, int6
                                      uint8_t* q, uint8_t* scale, hipStream_t stream);
 
 // lhs_kind: 0 = E4M3 codes + lhs_scale, 1 = bf16, 2 = fp32.
-hipError_t launch_fp8_fwd(const void* lhs, int lhs_kind, const float* lhs_scale,
+hipError_t launch_fp8_fwd(const TileConfig& cfg, const void* lhs, int lhs_kind, const float* lhs_scale,
                           const uint8_t* rhs, const float* rhs_scale,
                           const int32_t* group_sizes, int M, int K, int N, int G, void* out,
                           bool out_bf16, uint8_t* q_out, float* scale_out, int32_t* status, hipStream_t stream);
 
 // Fused gate+up: rhs has 2N columns (gate, then up); out = silu(gate) * up,
 // [M,N]; act_q/act_scale (both or neither) the 1x128 quantised activation.
-hipError_t launch_fp8_fwd_swiglu(const void* lhs, int lhs_kind, const float* lhs_scale,
+hipError_t launch_fp8_fwd_swiglu(const TileConfig& cfg, const void* lhs, int lhs_kind, const float* lhs_scale,
                                  const uint8_t* rhs, const float* rhs_scale,
                                  const int32_t* group_sizes, int M, int K, int N, int G,
                                  void* out, bool out_bf16, uint8_t* act_q, float* act_scale,
                                  int32_t* status, hipStream_t stream);
 
 // FP8 (1x128) LHS against packed MXFP4 weights.
-hipError_t launch_fp8_mxfp4_fwd(const void* lhs, int lhs_kind, const float* lhs_scale,
+hipError_t launch_fp8_mxfp4_fwd(const TileConfig& cfg, const void* lhs, int lhs_kind, const float* lhs_scale,
                                 const uint8_t* rhs_q, const uint8_t* rhs_scale,
                                 const int32_t* group_sizes, int M, int K, int N, int G, void* out,
                                 bool out_bf16, int32_t* status, hipStream_t stream);
 
-hipError_t launch_bf16_fwd(const void* lhs, const void* rhs, const int32_t* group_sizes, int M,
+hipError_t launch_bf16_fwd(const TileConfig& cfg, const void* lhs, const void* rhs, const int32_t* group_sizes, int M,
                            int K, int N, int G, void* out, bool out_bf16, int32_t* status, hipStream_t stream);
 
-hipError_t launch_bf16_dx(const void* dy, const void* w, const int32_t* group_sizes, int M,
+hipError_t launch_bf16_dx(const TileConfig& cfg, const void* dy, const void* w, const int32_t* group_sizes, int M,
                           int K, int N, int G, void* dx, bool out_bf16, int32_t* status, hipStream_t stream);
 
-hipError_t launch_tgmm(const void* x, const void* dy, const int32_t* group_sizes, int M, int K,
+hipError_t launch_tgmm(const TileConfig& cfg, const void* x, const void* dy, const int32_t* group_sizes, int M, int K,
                        int N, int G, void* dw, bool out_bf16, int32_t* status, hipStream_t stream);
 
 }  // namespace gmm

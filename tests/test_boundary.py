@@ -31,7 +31,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_symbols()
-    assert len(names) == 17
+    assert len(names) == 19
     assert sorted(names) == sorted(gmm.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
@@ -219,3 +219,22 @@ def test_binding_raises_on_error(lib):
     with pytest.raises(gmm.GmmError) as e:
         gmm._check(SHAPE)
     assert e.value.status == SHAPE
+
+
+def test_tile_config_rejections(lib):
+    c = gmm.TileConfig(kernel=1, waves=16)
+    assert lib.gmm_set_tile_config(0, ctypes.byref(c)) == SHAPE      # metadata has no tiles
+    assert lib.gmm_set_tile_config(7, ctypes.byref(c)) == SHAPE
+    bad = gmm.TileConfig(kernel=4)
+    assert lib.gmm_set_tile_config(1, ctypes.byref(bad)) == SHAPE
+    assert lib.gmm_get_tile_config(1, 256, 256, 256, 4, 1, 1, None) == NULL
+    out = gmm.TileConfig()
+    assert lib.gmm_get_tile_config(1, 256, 256, 256, 4, 1, 2, ctypes.byref(out)) == DTYPE
+    # a configuration that does not fit a call's shape makes that call fail before launching
+    assert lib.gmm_set_tile_config(1, ctypes.byref(gmm.TileConfig(kernel=1))) == OK
+    try:
+        assert fp8(lib, N=256) == SHAPE                   # 48 x 512 tiles need N % 512 == 0
+        assert b"does not fit" in lib.gmm_last_error()
+    finally:
+        assert lib.gmm_set_tile_config(1, None) == OK
+    assert fp8(lib, N=256, M=0) == OK

@@ -1,91 +1,96 @@
-"""The tile-sweep harness's host logic (no GPU): candidate enumeration, the
-tolerance gate, staged gating and best-configuration choice with a fake
-runner standing in for the child processes."""
-import json
-
+"""The tile search's host logic (no GPU): the configuration space of every
+phase, which configurations fit which shapes (asked of the library's own
+resolver, which runs on the host), the staged gate, and the library's
+default choices at the benchmark's shapes."""
 import numpy as np
 import pytest
 
+import moe_grouped_gemm_gmm_amd as gmm
 from moe_grouped_gemm_gmm_amd import tune
 
 
-def test_candidates_per_phase():
-    c = tune.candidates("fp8_fwd", 512)
-    assert c[0] == {}
-    assert len(c) == 1 + 2 + 6
-    ws = [e for e in c if e.get("GMM_FP8_WS") == "1"]
-    assert {e["GMM_FP8_WS_WAVES"] for e in ws} == {"8", "16"}
-    assert all(e["GMM_FP8_WN"] == "64" and e["GMM_FP8_TM"] == "48" for e in ws)
-    c256 = tune.candidates("fp8_fwd_prequant", 256)
-    assert not any(e.get("GMM_FP8_WS") == "1" for e in c256)
-    assert {e["GMM_FP8_WN"] for e in c256[1:]} == {"32", "16"}
-    assert [e.get("GMM_MXFP4_TN") for e in tune.candidates("mxfp4_fwd", 384)] == [None, "128"]
-    assert [e.get("GMM_MXFP4_TN") for e in tune.candidates("mxfp4_fwd", 1024)] == [None, "512", "256", "128"]
-    assert [e.get("GMM_SWIGLU_TM") for e in tune.candidates("swiglu", 512)] == [None, "48", "64"]
-    for phase in ("bf16_fwd", "tgmm", "dx"):
-        assert [e.get("GMM_BF16_MINB") for e in tune.candidates(phase, 512)] == [None, "2", "3"]
-    names = [tune.env_name(e) for e in tune.candidates("fp8_fwd", 512)]
-    assert len(set(names)) == len(names) and names[0] == "default"
+def test_space_and_names():
+    for phase in tune.PHASES:
+        sp = tune.space(phase)
+        assert sp[0] == {}
+        names = [tune.config_name(c) for c in sp]
+        assert len(set(names)) == len(names) and names[0] == "default"
+    fp8 = tune.space("fp8_fwd")
+    assert {c.get("kernel") for c in fp8[1:]} == {1, 2, 3}
+    assert {c["waves"] for c in fp8 if c.get("kernel") == 1} == {8, 12, 16}
+    assert {(c["tile_m"], c["tile_n"]) for c in fp8 if c.get("kernel") == 2} == {
+        (m, n) for m in (48, 64) for n in (128, 256, 512)}
+    assert [c.get("placement") for c in tune.space("tgmm")] == [None, 1, 2, 1, 2]
     with pytest.raises(ValueError):
-        tune.candidates("nope", 512)
+        tune.space("nope")
 
 
-def test_gate_excess():
-    ref = np.array([[1.0, -2.0, 0.0]])
-    assert tune.gate_excess(ref.copy(), ref) < 0
-    ok = ref + np.array([[0.01, -0.02, 0.001]])        # at the tolerance edge: 1e-3 + 1e-2|ref|
-    assert tune.gate_excess(ok, ref) <= 1e-12
-    bad = ref + np.array([[0.0, 0.0, 0.01]])
-    assert tune.gate_excess(bad, ref) == pytest.approx(0.009)
-    assert tune.gate_excess(np.array([[1.0, np.nan, 0.0]]), ref) == float("inf")
-    assert tune.gate_excess(np.zeros((2, 3)), ref) == float("inf")
+def test_candidates_follow_the_shape():
+    wi = tune.candidates("fp8_fwd", (8192, 2048, 512, 32))
+    names = {tune.config_name(c) for c in wi}
+    assert "kernel=1,waves=16" in names and "kernel=3,tile_n=256" in names
+    assert "kernel=3,tile_n=512" not in names          # 512-column row-resident tiles need K <= 1024
+    n384 = {tune.config_name(c) for c in tune.candidates("fp8_fwd", (1024, 256, 384, 4))}
+    assert not any(n.startswith("kernel=1") for n in n384)   # warp-specialised needs N % 512 == 0
+    assert "kernel=2,tile_m=48,tile_n=128" in n384 and "kernel=2,tile_m=48,tile_n=256" not in n384
+    mx = {tune.config_name(c) for c in tune.candidates("mxfp4_fwd", (8192, 512, 2048, 32))}
+    assert "kernel=3" in mx and "kernel=1,tile_n=512" in mx
+    tg = {tune.config_name(c) for c in tune.candidates("tgmm", (700, 256, 256, 6))}
+    assert "placement=2,residency=3" not in tg         # 4 tiles per group cannot spread over 8 XCDs
+    assert "placement=1,residency=2" in tg
 
 
-class FakeRunner:
-    """Writes a deterministic output per (shape, config) and reports a time;
-    one configuration is wrong on the small problem, one only on the target,
-    one crashes."""
-
-    def __init__(self):
-        self.calls = []
-
-    def __call__(self, phase, shape, env, seed, steps, save):
-        self.calls.append((tuple(shape), tune.env_name(env), steps))
-        M, K, N, G = shape
-        out = np.arange(M * N, dtype=np.float32).reshape(M, N) / (M * N)
-        name = tune.env_name(env)
-        if name == "GMM_MXFP4_TN=256":
-            out = out + 0.5                                  # wrong everywhere
-        if name == "GMM_MXFP4_TN=128" and M > 512:
-            out = out * 1.1                                  # wrong only at the target
-        if name == "GMM_MXFP4_TN=512" and M > 512:
-            return {"error": "boom"}
-        np.save(save, out)
-        us = {"default": 10.0, "GMM_MXFP4_TN=512": 5.0, "GMM_MXFP4_TN=256": 1.0,
-              "GMM_MXFP4_TN=128": 2.0}[name]
-        return {"us": us} if steps else {}
+def test_library_default_choices():
+    """The library's own choice at the benchmark's shapes (the host resolver;
+    with no GPU the CU count is taken as 256, the MI355X's)."""
+    F, S, X, B, T, D = (gmm.OP_FP8_FWD, gmm.OP_FP8_FWD_SWIGLU, gmm.OP_FP8_MXFP4_FWD,
+                        gmm.OP_BF16_FWD, gmm.OP_TGMM, gmm.OP_DX)
+    nz = lambda d: {k: v for k, v in d.items() if v}
+    assert nz(gmm.get_tile_config(F, 8192, 2048, 512, 32)) == {
+        "kernel": 1, "waves": 16, "tile_m": 48, "tile_n": 512, "depth": 1}
+    assert nz(gmm.get_tile_config(F, 8192, 512, 2048, 32)) == {"kernel": 3, "tile_m": 48, "tile_n": 512}
+    assert nz(gmm.get_tile_config(F, 65536, 2048, 512, 256)) == {"kernel": 2, "tile_m": 64, "tile_n": 512}
+    assert nz(gmm.get_tile_config(S, 8192, 2048, 512, 32)) == {"kernel": 2, "tile_m": 48, "tile_n": 256}
+    assert nz(gmm.get_tile_config(X, 8192, 2048, 512, 32))["kernel"] == 1
+    assert nz(gmm.get_tile_config(B, 8192, 2048, 512, 32)) == {"residency": 2}
+    assert nz(gmm.get_tile_config(T, 65536, 2048, 512, 256)) == {"residency": 3}
+    assert nz(gmm.get_tile_config(D, 8192, 2048, 512, 32)) == {"residency": 3}
 
 
-def test_sweep_stages_and_best():
-    fr = FakeRunner()
-    t = tune.sweep("mxfp4_fwd", (2048, 256, 1024, 8), steps=10, runner=fr)
-    rows = {r["config"]: r for r in t["candidates"]}
-    assert rows["default"]["gate_target"] and rows["default"]["us"] == 10.0
-    assert rows["GMM_MXFP4_TN=256"]["gate_small"] is False and "gate_target" not in rows["GMM_MXFP4_TN=256"]
-    assert rows["GMM_MXFP4_TN=128"]["gate_small"] and rows["GMM_MXFP4_TN=128"]["gate_target"] is False
-    assert rows["GMM_MXFP4_TN=512"]["error"] == "boom"
-    assert t["best"]["config"] == "default" and t["default_us"] == 10.0
-    assert t["small_shape"] == [512, 256, 1024, 4]
-    # the failing-on-small candidate never ran at the target size
-    assert not any(c[1] == "GMM_MXFP4_TN=256" and c[0][0] == 2048 for c in fr.calls)
-    # only target-size runs are timed
-    assert all(shape[0] == 2048 for shape, name, steps in fr.calls if steps)
-    assert any(steps for shape, name, steps in fr.calls)
-    json.dumps(t)                                           # serialisable
+def test_set_tile_config_checks_fields_and_fit():
+    F = gmm.OP_FP8_FWD
+    try:
+        with pytest.raises(gmm.GmmError):
+            gmm.set_tile_config(F, {"waves": 10})
+        with pytest.raises(ValueError):
+            gmm.set_tile_config(F, {"wavez": 16})
+        gmm.set_tile_config(F, {"kernel": 1, "waves": 16, "depth": 2})
+        with pytest.raises(gmm.GmmError):        # two steps of weights need 12 waves
+            gmm.get_tile_config(F, 8192, 2048, 512, 32)
+        gmm.set_tile_config(F, {"kernel": 2, "tile_n": 256, "tile_m": 64})
+        assert gmm.get_tile_config(F, 8192, 2048, 512, 32)["tile_n"] == 256
+    finally:
+        gmm.set_tile_config(F, None)
+    assert gmm.get_tile_config(F, 8192, 2048, 512, 32)["waves"] == 16
 
 
-def test_default_failure_raises():
-    def runner(phase, shape, env, seed, steps, save):
-        return {"error": "no gpu"}
-    with pytest.raises(RuntimeError):
-        tune.sweep("swiglu", (600, 256, 512, 4), runner=runner)
+def test_gate_bars():
+    ref = np.linspace(-2.0, 2.0, 1001)
+    assert tune.gate(ref.copy(), ref, tune.STRICT)["pass"]
+    edge = ref + 0.999 * (1e-3 + 1e-2 * np.abs(ref))            # inside the strict bar
+    assert tune.gate(edge, ref, tune.STRICT)["excess"] <= 0
+    noisy = ref + 0.02
+    assert not tune.gate(noisy, ref, tune.STRICT)["pass"]       # beyond atol 1e-3
+    assert tune.gate(noisy, ref, tune.RELAXED)["pass"]          # within atol 1e-1, SNR > 20 dB
+    far = ref * 0.5
+    g = tune.gate(far, ref, tune.RELAXED)
+    assert not g["pass"] and g["snr_db"] == pytest.approx(10 * np.log10(4.0))
+    assert tune.gate(np.where(ref > 0, np.nan, ref), ref, tune.RELAXED)["excess"] == float("inf")
+    assert tune.gate(np.zeros(3), ref, tune.STRICT)["pass"] is False
+
+
+def test_group_sizes_routings():
+    u = tune.group_sizes(8192, 32, 0, "uniform")
+    z = tune.group_sizes(8192, 32, 0, "zipf")
+    assert u.sum() == z.sum() == 8192 and u.dtype == z.dtype == np.int32
+    assert z.max() > 4 * 8192 / 32 > u.max()
