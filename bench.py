@@ -9,12 +9,18 @@ The RHS is quantised once beforehand (weights are static), inputs are
 resident in HBM, and the K timed steps are replayed from one HIP graph so
 that host launch overhead is not measured.
 
-The other calls of the library (bf16 forward baseline, tgmm, dX, standalone
-quantisers, pre-quantised and MXFP4-weight forwards, the fused gate+up
-forward), the FP8 forward at the wo-layer shape (K=512, N=2048) and the
-production shape (M=65536, G=256), and the bf16 forward, tgmm and dX at
-the production shape are timed the same way and reported under "ops".  The oracle (CPU, fp64) is
-timed on the host for the same forward: "cpu_baseline".
+The line also carries the per-call median and minimum over 200 calls
+("per_call").  The other calls of the library (bf16 forward baseline, tgmm,
+dX, standalone quantisers, pre-quantised and MXFP4-weight forwards, the
+fused gate+up forward), the FP8 forward at the wo-layer shape (K=512,
+N=2048) and the production shape (M=65536, G=256), and the bf16 forward,
+tgmm and dX at the production shape are timed the same way and reported
+under "ops", with "ops.ceiling": what this part delivers to any kernel
+(streaming reads inside and beyond the Infinity Cache, a copy, the launch
+cost of a tiny kernel, hipBLASLt's dense FP8 GEMM of the same size).  The
+oracle (CPU, fp64) is timed on the host for the same forward and for the
+other configurations, and its result is held against the GPU's:
+"cpu_baseline".
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -115,6 +121,34 @@ def graph_time_ms(fn, steps: int, warmup: int, settle_s: float = 0.06) -> float:
     return start.elapsed_time(end) / steps
 
 
+def per_call_us(fn, calls: int = 200, replays: int = 25):
+    """Median and minimum over `replays` timed replays of one HIP graph of
+    `calls` back-to-back calls, each replay's figure being its average per
+    call (per-dispatch statistics come from the profiler's kernel trace)."""
+    import torch
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        fn()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=stream):
+            for _ in range(calls):
+                fn()
+    torch.cuda.synchronize()
+    graph.replay()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(replays)]
+    with torch.cuda.stream(stream):
+        for a, b in ev:
+            a.record(stream)
+            graph.replay()
+            b.record(stream)
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) * 1e3 / calls for a, b in ev)
+    return {"median_us": round(t[len(t) // 2], 3), "min_us": round(t[0], 3),
+            "replays": replays, "calls_per_replay": calls}
+
+
 def cold_time_ms(fn, reps: int) -> float:
     """Median ms of single calls with a 512 MiB buffer rewritten before each
     (evicts the 256 MB Infinity Cache and the L2s)."""
@@ -134,27 +168,173 @@ def cold_time_ms(fn, reps: int) -> float:
     return times[len(times) // 2]
 
 
-def cpu_baseline(wl, min_seconds: float = 10.0, max_seconds: float = 30.0):
+def bf16_ulp(x):
+    """The spacing of bfloat16 values at |x| (8 significant bits; subnormal floor)."""
+    import numpy as np
+    a = np.maximum(np.abs(x), 2.0 ** -126)
+    return 2.0 ** (np.floor(np.log2(a)) - 7)
+
+
+def parity_stats(out, ref):
+    """Max abs/rel error, SQNR and bf16 ULP error of out against ref ("GEMM
+    Kernel 性能优化十问", Q9.2's three measures).  ULP figures: percentiles
+    over all elements and the maximum over those with |ref| at least 1% of
+    rms(ref) (near zero a fixed absolute error is many ULP of a tiny value)."""
+    import numpy as np
+    err = np.abs(out - ref)
+    nz = np.abs(ref) > 1e-6
+    ulp = err / bf16_ulp(ref)
+    big = np.abs(ref) >= 0.01 * np.sqrt(np.mean(ref ** 2))
+    noise = float(np.sum((ref - out) ** 2))
+    return {"max_abs": float("%.4g" % err.max()),
+            "max_rel": float("%.4g" % (err[nz] / np.abs(ref[nz])).max()),
+            "sqnr_db": round(10 * np.log10(float(np.sum(ref ** 2)) / noise), 2) if noise else None,
+            "ulp_p99": round(float(np.percentile(ulp, 99)), 2),
+            "ulp_p999": round(float(np.percentile(ulp, 99.9)), 2),
+            "ulp_max_where_ref_ge_1pct_rms": round(float(ulp[big].max()), 2),
+            "within_1e-3_1e-2": bool(np.all(err <= 1e-3 + 1e-2 * np.abs(ref)))}
+
+
+def oracle_table(gpu_us: dict):
+    """The oracle on the host for the other configurations: the wo forward,
+    the backward pair at the wi shape and the production shape's forward,
+    tgmm and dX; seconds, fp64 GFLOP/s and the GPU's speed-up."""
+    import oracle
+    import workloads
+    rows = {}
+
+    def put(name, flops, sec):
+        r = {"s": round(sec, 3), "gflops": round(flops / sec / 1e9, 2)}
+        if name in gpu_us:
+            r["gpu_us"] = gpu_us[name]
+            r["gpu_speedup"] = round(sec / (gpu_us[name] * 1e-6), 1)
+        rows[name] = r
+
+    wo = workloads.make("wo", seed=0, with_dy=False)
+    qr, sr = oracle.quantize_rhs(workloads.as_f32(wo.w))
+    t0 = time.perf_counter()
+    ql, sl = oracle.quantize_lhs(workloads.as_f32(wo.x))
+    oracle.gmm_fp8(ql, sl, qr, sr, wo.group_sizes)
+    put("fp8_fwd_wo", 2.0 * wo.group_sizes.sum() * wo.K * wo.N, time.perf_counter() - t0)
+    del wo, qr, sr, ql, sl
+    for cfg, sfx in (("bwd", ""), ("full", "_full")):
+        wl = workloads.make(cfg, seed=0, with_dy=True)
+        x, w, dy = (workloads.as_f32(t) for t in (wl.x, wl.w, wl.dy))
+        flops = 2.0 * wl.group_sizes.sum() * wl.K * wl.N
+        if cfg == "full":
+            qr, sr = oracle.quantize_rhs(w)
+            t0 = time.perf_counter()
+            ql, sl = oracle.quantize_lhs(x)
+            oracle.gmm_fp8(ql, sl, qr, sr, wl.group_sizes)
+            put("fp8_fwd_full", flops, time.perf_counter() - t0)
+            del qr, sr, ql, sl
+        t0 = time.perf_counter()
+        oracle.tgmm(x, dy, wl.group_sizes)
+        put("tgmm_bf16" + sfx, flops, time.perf_counter() - t0)
+        t0 = time.perf_counter()
+        oracle.gmm_dx(dy, w, wl.group_sizes)
+        put("dx_bf16" + sfx, flops, time.perf_counter() - t0)
+        del wl, x, w, dy
+    return {"cores": oracle.num_threads(), "cpu": cpu_model(), "rows": rows}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def ceiling(dev):
+    """What this part delivers to any kernel: streaming reads (the library's
+    probe) of a buffer larger than the 8 x 4 MB of L2 but inside the 256 MB
+    Infinity Cache and of one far beyond it, a device copy (torch), the
+    launch-to-launch cost of a one-element kernel in a HIP graph, and
+    hipBLASLt's dense FP8 GEMM of the forward's size (8192 x 2048 x 512, no
+    grouping, no quantisation)."""
+    import torch
+    import moe_grouped_gemm_gmm_amd as gmm
+    out = {}
+    for name, mb in (("read_128MB", 128), ("read_4GB", 4096)):
+        buf = torch.zeros(mb * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+        sink = torch.zeros(mb * 16, dtype=torch.int32, device=dev)
+        us = graph_time_ms(lambda: gmm.probe_stream_read(buf, sink), 20, 3) * 1e3
+        out[name] = {"us": round(us, 2), "GB/s": round(mb * 1048576 / (us * 1e-6) / 1e9, 1),
+                     "kernel": "gmm_probe_stream_read"}
+        del buf, sink
+    src = torch.ones(1024 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    us = graph_time_ms(lambda: dst.copy_(src), 10, 2) * 1e3
+    out["copy_1GB"] = {"us": round(us, 2), "GB/s": round(2 * 1073741824 / (us * 1e-6) / 1e9, 1)}
+    del src, dst
+    one = torch.zeros(1, dtype=torch.float32, device=dev)
+    out["tiny_kernel_launch_us"] = round(graph_time_ms(lambda: one.add_(1.0), 200, 5) * 1e3, 3)
+    try:
+        a = torch.randn(8192, 2048, device=dev).to(torch.float8_e4m3fn)
+        b = torch.randn(512, 2048, device=dev).to(torch.float8_e4m3fn).t()
+        one_s = torch.ones((), device=dev)
+        us = graph_time_ms(lambda: torch._scaled_mm(a, b, scale_a=one_s, scale_b=one_s,
+                                                    out_dtype=torch.bfloat16), 100, 5) * 1e3
+        out["dense_fp8_gemm_8192x2048x512"] = {"us": round(us, 2),
+                                               "tflops": round(2.0 * 8192 * 2048 * 512 / (us * 1e-6) / 1e12, 1)}
+    except Exception as e:   # not offered by this torch build
+        out["dense_fp8_gemm_8192x2048x512"] = {"error": str(e)[:200]}
+    return out
+
+
+def cpu_baseline(wl, gpu_out=None, gpu_bf16_out=None, gpu_us=None, min_seconds: float = 10.0,
+                 max_seconds: float = 30.0):
     """The oracle (as it stands) on the host: LHS quantisation + fp64 grouped
     FP8 matmul of the whole wi-layer forward, repeated until about 10 s of
-    CPU work; the RHS is quantised once, untimed, like on the GPU."""
+    CPU work; the RHS is quantised once, untimed, like on the GPU.
+
+    The same leg reports what its result says about the GPU's: the timed
+    call's output against it (max abs/rel error, SQNR, bf16 ULP: "GEMM Kernel
+    性能优化十问", Q9.2), and the quantisation loss, i.e. the FP8 output against
+    the bf16 kernel's (atol 1e-1, rtol 5e-2) and against the unquantised fp64
+    product (SQNR bands 30 / 20 dB; Q9.1's second layer).  It then times the
+    oracle on the other configurations (oracle_table)."""
+    import numpy as np
     import oracle
     import workloads
     x = workloads.as_f32(wl.x)
-    qr, sr = oracle.quantize_rhs(workloads.as_f32(wl.w))
+    w = workloads.as_f32(wl.w)
+    qr, sr = oracle.quantize_rhs(w)
     flops = 2.0 * float(wl.group_sizes.sum()) * wl.K * wl.N
     reps, total = 0, 0.0
+    ref = None
     while total < min_seconds and (reps == 0 or total + total / reps < max_seconds):
         t0 = time.perf_counter()
         ql, sl = oracle.quantize_lhs(x)
-        oracle.gmm_fp8(ql, sl, qr, sr, wl.group_sizes)
+        ref = oracle.gmm_fp8(ql, sl, qr, sr, wl.group_sizes)
         total += time.perf_counter() - t0
         reps += 1
     sec = total / reps
-    return {"value": flops / sec / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle", "seconds_per_forward": sec, "repetitions": reps,
-            "sample": "whole wi-layer forward (1x128 LHS quantisation + fp64 FP8 GMM over all "
-                      "8192 rows, K=2048, N=512), repeated %d times" % reps}
+    res = {"value": flops / sec / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+           "kind": "oracle", "seconds_per_forward": sec, "repetitions": reps, "cpu": cpu_model(),
+           "sample": "whole wi-layer forward (1x128 LHS quantisation + fp64 FP8 GMM over all "
+                     "8192 rows, K=2048, N=512), repeated %d times" % reps}
+    if gpu_out is not None:
+        res["gpu_output_vs_oracle"] = parity_stats(gpu_out, ref)
+        unq = oracle.gmm(x, w, wl.group_sizes)
+        q = {"sqnr_fp8_vs_unquantised_db": round(10 * np.log10(np.sum(unq ** 2) /
+                                                               np.sum((unq - gpu_out) ** 2)), 2)}
+        if gpu_bf16_out is not None:
+            err = np.abs(gpu_out - gpu_bf16_out)
+            ok = err <= 1e-1 + 5e-2 * np.abs(gpu_bf16_out)
+            q["fp8_vs_bf16_kernel_within_1e-1_5e-2"] = bool(np.all(ok))
+            q["fp8_vs_bf16_kernel_fraction_within"] = float("%.6f" % ok.mean())
+            q["fp8_vs_bf16_kernel_max_abs"] = float("%.4g" % err.max())
+            q["fp8_vs_bf16_kernel_sqnr_db"] = round(10 * np.log10(np.sum(gpu_bf16_out ** 2) /
+                                                                   np.sum(err ** 2)), 2)
+            q["bf16_kernel_vs_unquantised"] = parity_stats(gpu_bf16_out, unq)
+        res["quantisation_loss"] = q
+    res["other_configs"] = oracle_table(gpu_us or {})
+    return res
 
 
 def main() -> int:
@@ -200,6 +380,8 @@ def main() -> int:
     # ---- timed region: K steps (one graph replay), synchronised on both sides
     ms = graph_time_ms(fwd, args.steps, args.warmup)
     tflops = flops / (ms * 1e-3) / 1e12
+    per_call = per_call_us(fwd)
+    gpu_out = out.double().cpu().numpy()
 
     # per-launch duration of the dominant kernel: the graph holds one kernel per
     # step, so the event-timed graph replay divided by K is its average duration.
@@ -235,7 +417,13 @@ def main() -> int:
                      "kernel_avg_us": round(ms * 1e3, 3),
                      "mfma_tflops": round(tflops, 2), "mfma_peak": PEAK_FP8_TFLOPS,
                      "mfma_frac": round(tflops / PEAK_FP8_TFLOPS, 4)},
+        "per_call": per_call,
     }
+    outb0 = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    gmm.gmm_bf16_fwd(x, w, gs, out=outb0)
+    gpu_bf16_out = outb0.double().cpu().numpy()
+    del outb0
+    gpu_us = {}
 
     if not args.no_ops:
         ops = {}
@@ -327,10 +515,12 @@ def main() -> int:
                                   "frac_hbm": round(bbytes / (b_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
                 del dyc, wbc, dwc, dxc, yc
             del wc, xc, gc, qc, sc, oc
+        ops["ceiling"] = ceiling(dev)
         result["ops"] = ops
+        gpu_us = {k: v["us"] for k, v in ops.items() if isinstance(v, dict) and "us" in v}
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl)
+        result["cpu_baseline"] = cpu_baseline(wl, gpu_out, gpu_bf16_out, gpu_us)
         result["cpu_baseline"]["value"] = float("%.6g" % result["cpu_baseline"]["value"])
 
     print(json.dumps(result))

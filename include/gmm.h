@@ -146,6 +146,17 @@ GMM_API int gmm_get_tile_config(int op, int64_t M, int64_t K, int64_t N, int64_t
                                 int lhs_dtype, int out_dtype, gmm_tile_config *cfg);
 
 /*
+ * gmm_probe_stream_read -- a platform probe, not part of the grouped
+ *   matmul: reads `bytes` of buf with one 64 KB slice per workgroup and
+ *   16-byte loads, so that the caller can time the streaming rate this part
+ *   delivers from its caches and from HBM ("GEMM Kernel 性能优化十问", Q10,
+ *   step 0: measure the platform's bandwidth first).  bytes: a positive
+ *   multiple of 65536.  sink: bytes/65536 uint32 words (written only in the
+ *   unlikely case that a slice's words XOR to 0x9e3779b9).
+ */
+GMM_API int gmm_probe_stream_read(const void *buf, int64_t bytes, uint32_t *sink, void *stream);
+
+/*
  * gmm_device_status -- the device status word the last grouped call wrote
  *   into ws (0 = group_sizes kept the contract; else GMM_DEV_* bits), copied
  *   to *status once the work queued on `stream` before it has finished.

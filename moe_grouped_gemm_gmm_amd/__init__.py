@@ -22,7 +22,7 @@ GMM_MAX_GROUPS = 4096
  OP_DX) = range(7)
 DEV_SUM_GT_M, DEV_NEGATIVE_SIZE = 1, 2
 EXPORTS = ("gmm_status_string", "gmm_last_error", "gmm_workspace_bytes", "gmm_device_status",
-           "gmm_set_tile_config", "gmm_get_tile_config",
+           "gmm_set_tile_config", "gmm_get_tile_config", "gmm_probe_stream_read",
            "gmm_group_metadata", "gmm_quantize_lhs", "gmm_quantize_rhs", "gmm_pack_rhs",
            "gmm_quant_scales", "gmm_fp8_fwd", "gmm_fp8_fwd_swiglu", "gmm_bf16_fwd", "tgmm_bf16",
            "gmm_bf16_dx", "gmm_quantize_rhs_mxfp4", "gmm_fp8_mxfp4_fwd", "gmm_fp8_fwd_noalloc")
@@ -63,6 +63,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gmm_workspace_bytes.argtypes = [I, I64, I64, I64, I64]
     lib.gmm_device_status.argtypes = [P, P, P]
     lib.gmm_set_tile_config.argtypes = [I, P]
+    lib.gmm_probe_stream_read.argtypes = [P, I64, P, P]
     lib.gmm_get_tile_config.argtypes = [I, I64, I64, I64, I64, I, I, P]
     lib.gmm_group_metadata.argtypes = [P, I64, I64, I64, P, P, I64, P, P, SZ, P]
     lib.gmm_quantize_lhs.argtypes = [P, I, I64, I64, P, P, P]
@@ -128,6 +129,14 @@ def device_status(ws: torch.Tensor) -> int:
     out = ctypes.c_int32(-1)
     _check(lib.gmm_device_status(_ptr(ws), ctypes.byref(out), _stream(ws)))
     return int(out.value)
+
+
+def probe_stream_read(buf: torch.Tensor, sink: torch.Tensor) -> None:
+    """Platform probe: stream-read all of buf (a multiple of 64 KB) on the
+    current stream; sink holds buf.nbytes / 65536 uint32 words."""
+    lib = load_library()
+    _check(lib.gmm_probe_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                     _stream(buf)))
 
 
 def set_tile_config(op: int, cfg: Optional[dict]) -> None:

@@ -14,7 +14,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libgmm.so")
 SOURCES = ["gmm_api.cpp", "gmm_config.cpp", "gmm_quant.hip", "gmm_fp8.hip", "gmm_bf16.hip",
-           "gmm_noalloc.hip"]
+           "gmm_noalloc.hip", "gmm_probe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

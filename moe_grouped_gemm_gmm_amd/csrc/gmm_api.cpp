@@ -182,6 +182,15 @@ int gmm_get_tile_config(int op, int64_t M, int64_t K, int64_t N, int64_t G, int 
     return GMM_OK;
 }
 
+int gmm_probe_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream) {
+    constexpr int64_t kSlice = 64 * 1024;
+    if (bytes < kSlice || bytes % kSlice != 0 || bytes / kSlice > kMaxDim)
+        return fail(GMM_ERR_SHAPE, "bytes=%lld must be a positive multiple of 65536", (long long)bytes);
+    GMM_TRY(check_ptr(buf, "buf"));
+    GMM_TRY(check_ptr(sink, "sink"));
+    return hip_status(gmm::launch_probe_stream_read(buf, bytes, sink, (hipStream_t)stream));
+}
+
 int gmm_device_status(const void* ws, int32_t* status, void* stream) {
     GMM_TRY(check_ptr(ws, "ws"));
     if (status == nullptr) return fail(GMM_ERR_NULL, "status is NULL");

@@ -30,6 +30,11 @@ inline int device_cus() {
 constexpr size_t kNoallocScratchBytes = 4096;
 hipError_t noalloc_scratch(void** ptr, size_t* bytes);
 
+// Streaming read of `bytes` (a multiple of 64 KB) with one 64 KB slice per
+// workgroup; sink has one word per slice.
+hipError_t launch_probe_stream_read(const void* buf, int64_t bytes, uint32_t* sink,
+                                    hipStream_t stream);
+
 hipError_t launch_group_metadata(const int32_t* group_sizes, int G, int M, int tm,
                                  int32_t* offsets, int32_t* work, int capacity,
                                  int32_t* num_work, int32_t* status, hipStream_t stream);

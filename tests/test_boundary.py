@@ -31,7 +31,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_symbols()
-    assert len(names) == 19
+    assert len(names) == 20
     assert sorted(names) == sorted(gmm.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
@@ -238,3 +238,11 @@ def test_tile_config_rejections(lib):
     finally:
         assert lib.gmm_set_tile_config(1, None) == OK
     assert fp8(lib, N=256, M=0) == OK
+
+
+def test_probe_rejections(lib):
+    p = lib.gmm_probe_stream_read
+    assert p(P(A), 1000, P(A), None) == SHAPE
+    assert p(P(A), 0, P(A), None) == SHAPE
+    assert p(None, 65536, P(A), None) == NULL
+    assert p(P(A), 65536, P(MIS), None) == ALIGN
