@@ -33,8 +33,15 @@ bool rr_fits(int64_t K, int64_t N, int tn, bool out_bf16, bool write_q) {
     return tn == 512 ? K <= 1024 : (tn == 256 && K <= 2048 && out_bf16);
 }
 
-bool resolve_fp8(const TileConfig& f, int64_t M, int64_t K, int64_t N, int64_t G, bool out_bf16,
-                 bool write_q, TileConfig* c, const char** why) {
+// FP8 warp-specialised kernel: 1 consecutive items per XCD, 2 each group's
+// items on one XCD (one column tile, G within one 64-lane scan).  The
+// library takes 2 when the LHS is quantised in the kernel (wi shape: 18.49
+// -> 18.25 us, no group's weights fetched into two L2s) and 1 for LHS codes
+// (17.30 -> 17.6 us: the busiest XCD gets one item more).
+bool group_aligned_fits(int64_t N, int64_t G) { return N == 512 && G <= 64; }
+
+bool resolve_fp8(const TileConfig& f, int64_t M, int64_t K, int64_t N, int64_t G, int lhs_kind,
+                 bool out_bf16, bool write_q, TileConfig* c, const char** why) {
     *c = TileConfig{};
     if (!any_set(f)) {   // the library's own choice
         if (N % 512 == 0 && N >= 1024 && rr_fits(K, N, 512, out_bf16, write_q)) {
@@ -49,12 +56,14 @@ bool resolve_fp8(const TileConfig& f, int64_t M, int64_t K, int64_t N, int64_t G
             c->kernel = kKerWs;
             c->waves = write_q ? 8 : 16;
             c->depth = 1;
+            c->placement = lhs_kind != 0 && c->waves == 16 && group_aligned_fits(N, G) ? 2 : 1;
         } else {
             c->kernel = kKerUniform;
         }
         return true;
     }
-    if (f.residency || f.placement) return fail(why, "residency/placement apply to the bf16 calls");
+    if (f.residency) return fail(why, "residency applies to the bf16 calls");
+    if (f.placement && f.kernel != kKerWs) return fail(why, "placement applies to the warp-specialised kernel");
     switch (f.kernel) {
         case kKerWs:
             if (N % 512 != 0) return fail(why, "the warp-specialised kernel needs N % 512 == 0");
@@ -67,6 +76,9 @@ bool resolve_fp8(const TileConfig& f, int64_t M, int64_t K, int64_t N, int64_t G
             c->depth = f.depth ? f.depth : 1;
             if (write_q && c->waves != 8) return fail(why, "writing the LHS codes takes the 8-wave form");
             if (c->depth == 2 && c->waves != 12) return fail(why, "two steps of weights in flight need 12 waves");
+            c->placement = f.placement ? f.placement : 1;
+            if (c->placement == 2 && !(c->waves == 16 && group_aligned_fits(N, G)))
+                return fail(why, "group-aligned placement needs 16 waves, N == 512 and G <= 64");
             return true;
         case kKerUniform:
             if (f.waves || f.depth) return fail(why, "waves/depth apply to the warp-specialised kernel");
@@ -175,10 +187,9 @@ void set_tile_override(int op, const TileConfig* cfg) {
 
 bool resolve_tile_config(int op, int64_t M, int64_t K, int64_t N, int64_t G, int lhs_kind,
                          bool out_bf16, bool write_q, TileConfig* out, const char** why) {
-    (void)lhs_kind;
     const TileConfig f = tile_override(op);
     switch (op) {
-        case kOpFp8Fwd: return resolve_fp8(f, M, K, N, G, out_bf16, write_q, out, why);
+        case kOpFp8Fwd: return resolve_fp8(f, M, K, N, G, lhs_kind, out_bf16, write_q, out, why);
         case kOpFp8Swiglu: return resolve_swiglu(f, M, N, G, out, why);
         case kOpFp8Mxfp4: return resolve_mxfp4(f, K, N, out, why);
         case kOpBf16Fwd:

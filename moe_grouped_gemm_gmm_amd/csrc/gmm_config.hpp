@@ -24,7 +24,9 @@ struct TileConfig {
     int tile_n;     // FP8 columns per workgroup tile: 128, 256 or 512
     int depth;      // warp-specialised FP8: steps of weights in flight (1, 2)
     int residency;  // bf16: workgroups per CU the registers allow (2, 3)
-    int placement;  // tgmm: 1 groups contiguous per XCD, 2 spread over XCDs by size class
+    int placement;  // warp-specialised FP8: 1 consecutive items per XCD, 2 each group's items
+                    // on one XCD; tgmm: 1 groups contiguous per XCD, 2 spread over XCDs by
+                    // size class
 };
 
 // The override set for op (all zero when none); set_tile_override(op, NULL)

@@ -259,6 +259,57 @@ __device__ __forceinline__ WorkItem find_work_item(const int32_t* __restrict__ g
     return it;
 }
 
+// Group-aligned XCD placement of work items, for grids that hold every item
+// at once (one workgroup per CU) and one column tile per row tile, G <= 64.
+// Blocks run on XCD b % 8; each XCD has `slots` blocks (b / 8 < slots).
+// Every group's items go to one XCD (the XCD whose eighth of the item range
+// holds the group's midpoint), so a group's weights are fetched into one L2
+// only; items (tail items included, after the groups) keep their order
+// within an XCD.  An XCD given more items than slots passes the surplus, in
+// order, to the spare slots of the XCDs before and after it in XCD order.
+// Returns the item index of block b, or -1 (no item).  One wave; every lane
+// gets the result.
+__device__ __forceinline__ int group_aligned_item(const int32_t* __restrict__ group_sizes, int G,
+                                                  int M, int tm, int slots, int b) {
+    const int lane = lane_id();
+    const GroupChunk ch = group_chunk(group_sizes, G, M, 0, 0);
+    const int c = ch.hi > ch.lo ? (ch.hi - 1) / tm - ch.lo / tm + 1 : 0;
+    const int inclc = wave_incl_scan(c);
+    const int W = inclc - c;                                   // first item of group `lane`
+    const int total = min(ch.next_carry, M);
+    const int Tg = lane_value(inclc, 63);                      // items of the groups
+    const int T = Tg + (total < M ? (M + tm - 1) / tm - total / tm : 0);   // and the tail's
+    // XCD of each group: the eighth of [0, T) holding its items' midpoint
+    const int xg = T > 0 ? min(7, (8 * (2 * W + c)) / (2 * T)) : 0;
+    int start[9];
+    start[0] = 0;
+    start[8] = T;
+#pragma unroll
+    for (int x = 1; x < 8; ++x) {
+        const unsigned long long m = __ballot(lane < G && c > 0 && xg >= x);
+        // no group from x on: XCD x starts where the tail items start
+        start[x] = m ? lane_value(W, __ffsll((long long)m) - 1) : Tg;
+    }
+#pragma unroll
+    for (int x = 1; x < 8; ++x) start[x] = max(start[x], start[x - 1]);
+    const int x = b % kNumXcd, i = b / kNumXcd;
+    const int n = start[x + 1] - start[x];
+    if (i < min(n, slots)) return start[x] + i;
+    if (n >= slots) return -1;
+    // spare slot of XCD x: rank among all spare slots, then the surplus item of that rank
+    int rank = i - n;
+#pragma unroll
+    for (int y = 0; y < 8; ++y)
+        if (y < x) rank += max(slots - (start[y + 1] - start[y]), 0);
+#pragma unroll
+    for (int y = 0; y < 8; ++y) {
+        const int extra = max(start[y + 1] - start[y] - slots, 0);
+        if (rank < extra) return start[y] + slots + rank;
+        rank -= extra;
+    }
+    return -1;
+}
+
 // Upper bound of the work-item count for M rows, G groups, tile height tm.
 __host__ __device__ inline int64_t max_work_items(int64_t M, int64_t G, int64_t tm) {
     return (M + tm - 1) / tm + G + 1;

@@ -47,6 +47,7 @@
 //    a lane owns one output row and four consecutive columns, which makes the
 //    row factor one scalar per block and lets the epilogue store 8-byte (bf16)
 //    or 16-byte (fp32) runs directly.
+#include <algorithm>
 #include <type_traits>
 
 #include "gmm_config.hpp"
@@ -559,7 +560,7 @@ __global__ __launch_bounds__(64 * NW, NW / 4) void fp8_fwd_ws_kernel(   // TM = 
     const uint8_t* __restrict__ rhs, const void* __restrict__ rhs_scale_v,
     const int32_t* __restrict__ group_sizes, int M, int K, int N, int G, void* __restrict__ out,
     uint8_t* __restrict__ q_out, float* __restrict__ s_out, int ntiles_n, int nblocks,
-    int32_t* __restrict__ status) {
+    int32_t* __restrict__ status, int placement) {
     static_assert(TM == 64 || TM == 48, "64- or 48-row tiles");
     static_assert(NW == 8 || NW == 12 || NW == 16, "8, 12 or 16 waves");
     static_assert(NP == 4 || NP == 8, "4 or 8 producer waves");
@@ -590,10 +591,16 @@ __global__ __launch_bounds__(64 * NW, NW / 4) void fp8_fwd_ws_kernel(   // TM = 
 
     const int tid = threadIdx.x, lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int L = xcd_remap(blockIdx.x, nblocks);
-    const int w = L / ntiles_n, nt = L % ntiles_n;
+    // placement 2: each group's items on one XCD (one column tile, G <= 64,
+    // nblocks = 8 x slots); else consecutive items on one XCD
+    const int L = placement == 2 ? 0 : xcd_remap(blockIdx.x, nblocks);
+    const int nt = placement == 2 ? 0 : L % ntiles_n;
     if (wave == 0) {
-        const WorkItem it = find_work_item(group_sizes, G, M, TM, w);
+        const int w = placement == 2
+            ? group_aligned_item(group_sizes, G, M, TM, nblocks / kNumXcd, blockIdx.x)
+            : L / ntiles_n;
+        WorkItem it{-1, 0, 0, 0};
+        if (w >= 0) it = find_work_item(group_sizes, G, M, TM, w);
         if (lane == 0) s_item = it;
     } else if (wave == 1 && blockIdx.x == 0) {   // the call's device status word
         const int st = group_status(group_sizes, G, M);
@@ -1058,18 +1065,22 @@ template <int KIND, int TM, bool WRITE_Q, int NW = 8, int TN = 512, bool B4 = fa
           int BD = 1>
 hipError_t launch_ws(const void* lhs, const float* lhs_scale, const uint8_t* rhs,
                      const void* rhs_scale, const int32_t* group_sizes, int M, int K, int N, int G,
-                     void* out, bool out_bf16, uint8_t* q_out, float* scale_out, int32_t* status, hipStream_t stream) {
+                     void* out, bool out_bf16, uint8_t* q_out, float* scale_out, int32_t* status, hipStream_t stream,
+                     int placement = 1) {
     const int ntiles_n = N / TN;
     const int64_t items = max_work_items(M, G, TM);
-    const int nblocks = (int)(items * ntiles_n);
+    // group-aligned placement: kNumXcd x slots blocks, slots >= ceil(items / 8)
+    const int nblocks = placement == 2
+        ? kNumXcd * (int)std::max<int64_t>((items + kNumXcd - 1) / kNumXcd, device_cus() / kNumXcd)
+        : (int)(items * ntiles_n);
     if (out_bf16)
         hipLaunchKernelGGL((fp8_fwd_ws_kernel<KIND, true, TM, WRITE_Q, NW, TN, B4, NP, BD>), dim3(nblocks),
                            dim3(64 * NW), 0, stream, lhs, lhs_scale, rhs, rhs_scale, group_sizes, M,
-                           K, N, G, out, q_out, scale_out, ntiles_n, nblocks, status);
+                           K, N, G, out, q_out, scale_out, ntiles_n, nblocks, status, placement);
     else
         hipLaunchKernelGGL((fp8_fwd_ws_kernel<KIND, false, TM, WRITE_Q, NW, TN, B4, NP, BD>), dim3(nblocks),
                            dim3(64 * NW), 0, stream, lhs, lhs_scale, rhs, rhs_scale, group_sizes, M,
-                           K, N, G, out, q_out, scale_out, ntiles_n, nblocks, status);
+                           K, N, G, out, q_out, scale_out, ntiles_n, nblocks, status, placement);
     return hipGetLastError();
 }
 
@@ -1159,7 +1170,8 @@ hipError_t launch_kind(const TileConfig& cfg, const void* lhs, const float* lhs_
                                              out, out_bf16, q_out, scale_out, status, stream);
         if (cfg.waves == 16)
             return launch_ws<KIND, 48, false, 16>(lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N,
-                                                  G, out, out_bf16, nullptr, nullptr, status, stream);
+                                                  G, out, out_bf16, nullptr, nullptr, status, stream,
+                                                  cfg.placement);
         if (cfg.waves == 12 && cfg.depth == 2)
             return launch_ws<KIND, 48, false, 12, 512, false, 4, 2>(
                 lhs, lhs_scale, rhs, rhs_scale, group_sizes, M, K, N, G, out, out_bf16, nullptr,

@@ -11,7 +11,8 @@ The configuration space of each phase is what the kernels offer through
 gmm_set_tile_config (include/gmm.h):
 
   fp8_fwd, fp8_fwd_prequant  warp-specialised kernel (8, 12 or 16 waves; 12 waves
-                             with one or two K steps of weights in flight),
+                             with one or two K steps of weights in flight; 16
+                             waves with each group's items on one XCD),
                              uniform kernel (tile_m 48/64 x tile_n 128/256/512),
                              row-resident sweep (tile_n 512 or 256)
   mxfp4_fwd                  warp-specialised tile_n 512/256/128, row-resident
@@ -71,6 +72,7 @@ def space(phase: str) -> List[Dict[str, int]]:
     if phase in ("fp8_fwd", "fp8_fwd_prequant"):
         for waves in (16, 12, 8):
             out.append({"kernel": 1, "waves": waves})
+        out.append({"kernel": 1, "waves": 16, "placement": 2})
         out.append({"kernel": 1, "waves": 12, "depth": 2})
         for tn in (512, 256, 128):
             for tm in (48, 64):

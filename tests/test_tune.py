@@ -18,6 +18,7 @@ def test_space_and_names():
     fp8 = tune.space("fp8_fwd")
     assert {c.get("kernel") for c in fp8[1:]} == {1, 2, 3}
     assert {c["waves"] for c in fp8 if c.get("kernel") == 1} == {8, 12, 16}
+    assert {c.get("placement") for c in fp8 if c.get("kernel") == 1} == {None, 2}
     assert {(c["tile_m"], c["tile_n"]) for c in fp8 if c.get("kernel") == 2} == {
         (m, n) for m in (48, 64) for n in (128, 256, 512)}
     assert [c.get("placement") for c in tune.space("tgmm")] == [None, 1, 2, 1, 2]
@@ -47,7 +48,9 @@ def test_library_default_choices():
                         gmm.OP_BF16_FWD, gmm.OP_TGMM, gmm.OP_DX)
     nz = lambda d: {k: v for k, v in d.items() if v}
     assert nz(gmm.get_tile_config(F, 8192, 2048, 512, 32)) == {
-        "kernel": 1, "waves": 16, "tile_m": 48, "tile_n": 512, "depth": 1}
+        "kernel": 1, "waves": 16, "tile_m": 48, "tile_n": 512, "depth": 1, "placement": 2}
+    assert gmm.get_tile_config(F, 8192, 2048, 512, 32, lhs_dtype=gmm.GMM_E4M3)["placement"] == 1
+    assert gmm.get_tile_config(F, 4096, 2048, 512, 100)["placement"] == 1   # G beyond one scan chunk
     assert nz(gmm.get_tile_config(F, 8192, 512, 2048, 32)) == {"kernel": 3, "tile_m": 48, "tile_n": 512}
     assert nz(gmm.get_tile_config(F, 65536, 2048, 512, 256)) == {"kernel": 2, "tile_m": 64, "tile_n": 512}
     assert nz(gmm.get_tile_config(S, 8192, 2048, 512, 32)) == {"kernel": 2, "tile_m": 48, "tile_n": 256}
