@@ -29,19 +29,39 @@ namespace {
 
 constexpr int kT = 128;      // output tile (rows and cols)
 constexpr int kR = 64;       // reduction depth per LDS stage
-constexpr int kPadD = 8;     // bf16 padding of a direct [128][64] tile (144-byte rows)
-constexpr int kPadT = 16;    // bf16 padding of a transposed [64][128] tile (288-byte rows: the
-                             // four rows one 16-lane group reads land on disjoint banks)
+// LDS row pitches, chosen by measurement on gfx950 (bytes per CU per clock,
+// 16 waves reading one pattern in a loop):
+//  - direct [128][64] tiles: 160-byte rows.  A ds_read_b128 of 16 rows at one
+//    16-byte chunk runs at ~205 B/clk with this pitch (as fast as a fully
+//    contiguous read), ~120 with 144-byte rows and ~63 with unpadded ones.
+//  - transposed [64][128] tiles: 288-byte rows.  The ds_read_b64_tr_b16
+//    reads of the lane groups that the LDS serves together must land 32
+//    banks apart (see read_tr): ~200 B/clk then, ~115 when they collide.
+constexpr int kPadD = 16;    // bf16 padding of a direct [128][64] tile
+constexpr int kPadT = 16;    // bf16 padding of a transposed [64][128] tile
 
 enum Mode { kFwd = 0, kDx = 1, kTgmm = 2 };
 
-// Transposed fragment: 8 reduction-consecutive values of column `col` from a
-// [r][col] LDS tile via two ds_read_b64_tr_b16.  Within each 16-lane group,
-// lane i supplies the address of row r0 + i/4, columns c0 + 4*(i%4) .. +3 and
-// receives column c0 + i of rows r0 .. r0+3.
-__device__ __forceinline__ v8bf read_tr(const uint16_t* tile, int stride, int r0, int c0, int lr) {
-    const uint16_t* p0 = tile + (r0 + (lr >> 2)) * stride + c0 + (lr & 3) * 4;
-    const uint16_t* p1 = p0 + 4 * stride;
+// Transposed fragment of 32-deep reduction block s: the 8 values of column
+// c0 + lr (lr = lane % 16) that lane group lg = lane / 16 feeds to the MFMA,
+// from a [r][col] LDS tile via two ds_read_b64_tr_b16.  Within each 16-lane
+// group, lane i supplies the address of row r + i/4, columns c0 + 4*(i%4)
+// .. +3 and receives column c0 + i of rows r .. r+3.
+//  - natural order: group lg takes rows 8lg .. 8lg+7 of the block (two reads
+//    4 rows apart).  Groups 0 and 1 (and 2 and 3), which the LDS serves in
+//    one pass, then read rows 8 apart, 8 x 288 bytes = a multiple of the
+//    256-byte bank period: a 2-way bank conflict.
+//  - spread order: group lg takes rows 4lg .. 4lg+3 and 16+4lg .. 16+4lg+3.
+//    Groups served together read rows 4 apart, 32 banks apart, conflict
+//    free.  The MFMA sums over the 32 reduction slots, so any bijection of
+//    block rows onto slots gives the same dot product as long as both
+//    operands use it; only a call whose other operand is also read here
+//    (tgmm) can use it.
+template <bool kSpread>
+__device__ __forceinline__ v8bf read_tr(const uint16_t* tile, int stride, int s, int lg, int c0, int lr) {
+    const int r = s * 32 + (kSpread ? 4 : 8) * lg;
+    const uint16_t* p0 = tile + (r + (lr >> 2)) * stride + c0 + (lr & 3) * 4;
+    const uint16_t* p1 = p0 + (kSpread ? 16 : 4) * stride;
     const v4bf lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((GMM_LDS v4bf*)(p0));
     const v4bf hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((GMM_LDS v4bf*)(p1));
     return v8bf{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -65,11 +85,11 @@ struct Frag4 {
     u32x4 d[4];
 };
 
-// Direct [128 rows][64] slice (8 chunks per row, LDS rows of 144 bytes):
+// Direct [128 rows][64] slice (8 chunks per row, LDS rows of 160 bytes):
 // instruction c of wave w covers rows R..R+3 and R+8..R+11 with
 // R = 16*((4w+c)/2) + 4*((4w+c)%2); lanes 8q..8q+7 take row
-// R + q/2 + 8*(q%2), chunks 0..7 (a 16-lane group: rows R+p and R+p+8, whose
-// 144-byte pitches put them 8 bank groups apart).
+// R + q/2 + 8*(q%2), chunks 0..7 (whole 128-byte row segments per 8 lanes;
+// ds_write_b128 runs at the same ~78 B/clk/CU for every pattern measured).
 __device__ __forceinline__ int direct_row(int c) {
     const int t = threadIdx.x, combo = (t >> 6) * 4 + c, q = (t & 63) >> 3;
     return 16 * (combo >> 1) + 4 * (combo & 1) + (q >> 1) + 8 * (q & 1);
@@ -262,6 +282,7 @@ __global__ __launch_bounds__(256, MINB) void bf16_gemm_kernel(
     int ntiles_c, int ntiles_r, int nblocks, int placement, int32_t* __restrict__ status) {
     constexpr bool A_TR = MODE == kTgmm;
     constexpr bool B_TR = MODE != kDx;
+    constexpr bool kSpread = A_TR && B_TR;   // both operands transposed: spread reduction order
     __shared__ __attribute__((aligned(16))) uint16_t sA[kTileElems];
     __shared__ __attribute__((aligned(16))) uint16_t sB[kTileElems];
     __shared__ int s_info[4];
@@ -374,14 +395,14 @@ __global__ __launch_bounds__(256, MINB) void bf16_gemm_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 if constexpr (A_TR)
-                    af[i] = read_tr(sA, kT + kPadT, s * 32 + lg * 8, wm * 64 + i * 16, lr);
+                    af[i] = read_tr<kSpread>(sA, kT + kPadT, s, lg, wm * 64 + i * 16, lr);
                 else
                     af[i] = read_direct(sA, kR + kPadD, wm * 64 + i * 16 + lr, s * 32 + lg * 8);
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 if constexpr (B_TR)
-                    bf[j] = read_tr(sB, kT + kPadT, s * 32 + lg * 8, wn * 64 + j * 16, lr);
+                    bf[j] = read_tr<kSpread>(sB, kT + kPadT, s, lg, wn * 64 + j * 16, lr);
                 else
                     bf[j] = read_direct(sB, kR + kPadD, wn * 64 + j * 16 + lr, s * 32 + lg * 8);
             }
