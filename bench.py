@@ -86,6 +86,32 @@ def copy_reference() -> int:
     return 0
 
 
+def counter_pass() -> int:
+    """Every benchmarked op three times, eagerly, at the wi / backward shape
+    and the production shape, and nothing else: a short workload for counter
+    collection (rocprofv3 --pmc), where each dispatch is counted on its own."""
+    import torch
+    import moe_grouped_gemm_gmm_amd as gmm
+    import workloads
+    gmm.load_library()
+    dev = torch.device("cuda:0")
+    for name in ("wi", "full"):
+        wl = workloads.make(name, seed=0, with_dy=True)
+        x = wl.x.to(dev)
+        gs = torch.from_numpy(wl.group_sizes).to(dev)
+        w = wl.w.to(dev)
+        dy = wl.dy.to(dev)
+        rq, rs = gmm.gmm_quantize_rhs(w)
+        for _ in range(3):
+            gmm.gmm_fp8_fwd(x, rq, rs, gs)
+            gmm.gmm_bf16_fwd(x, w, gs)
+            gmm.tgmm_bf16(x, dy, gs)
+            gmm.gmm_bf16_dx(dy, w, gs)
+        torch.cuda.synchronize()
+        print(json.dumps({"counter_pass": name, "M": wl.M, "K": wl.K, "N": wl.N, "G": wl.G}), flush=True)
+    return 0
+
+
 def graph_time_ms(fn, steps: int, warmup: int, settle_s: float = 0.06) -> float:
     """Average ms per call: W eager calls, then K calls captured in one HIP
     graph, replayed untimed for at least `settle_s` seconds (the GPU clock
@@ -333,6 +359,12 @@ def cpu_baseline(wl, gpu_out=None, gpu_bf16_out=None, gpu_us=None, min_seconds: 
             q["fp8_vs_bf16_kernel_sqnr_db"] = round(10 * np.log10(np.sum(gpu_bf16_out ** 2) /
                                                                    np.sum(err ** 2)), 2)
             q["bf16_kernel_vs_unquantised"] = parity_stats(gpu_bf16_out, unq)
+        # the same bar between the oracle's own FP8 result and the unquantised
+        # product: what the quantisation itself does, with no kernel involved
+        oerr = np.abs(ref - unq)
+        q["oracle_fp8_vs_unquantised_fraction_within_1e-1_5e-2"] = float(
+            "%.6f" % (oerr <= 1e-1 + 5e-2 * np.abs(unq)).mean())
+        q["oracle_fp8_vs_unquantised_max_abs"] = float("%.4g" % oerr.max())
         res["quantisation_loss"] = q
     res["other_configs"] = oracle_table(gpu_us or {})
     return res
@@ -347,9 +379,13 @@ def main() -> int:
     ap.add_argument("--no-ops", action="store_true", help="time only the FP8 forward")
     ap.add_argument("--copy-reference", action="store_true",
                     help="run only a plain 256 MiB copy (counter scaling for the traffic figure)")
+    ap.add_argument("--counter-pass", action="store_true",
+                    help="run every op three times at the wi and production shapes, untimed (for --pmc runs)")
     args = ap.parse_args()
     if args.copy_reference:
         return copy_reference()
+    if args.counter_pass:
+        return counter_pass()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(expert parallelism would run this per-GPU kernel on each rank's shard)",
