@@ -54,6 +54,8 @@ def _load():
     lib.oracle_quantize_rhs_mxfp4.argtypes = [P, I, I, I, P, P]
     lib.oracle_gmm_fp8_mxfp4.argtypes = [P, P, P, P, P, I, I, I, I, P]
     lib.oracle_quant_scales.argtypes = [P, I, P, P]
+    lib.oracle_quantize_rhs_int4.argtypes = [P, I, I, I, P, P]
+    lib.oracle_gmm_fp8_int4.argtypes = [P, P, P, P, P, I, I, I, I, P]
     lib.oracle_num_threads.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -204,6 +206,40 @@ def gmm_fp8_mxfp4(ql, sl, q4, e8, group_sizes):
     out = np.empty((M, N), dtype=np.float64)
     lib.oracle_gmm_fp8_mxfp4(pql, psl, pq4, pe8, pg, M, K, N, G,
                              out.ctypes.data_as(ctypes.c_void_p))
+    return out
+
+
+def quantize_rhs_int4(w):
+    """int4 weights: w [G,K,N] -> (codes [G,K,N] int8 in [-8, 7], scales
+    [G,K/128,N/128] fp32), one scale per 128x128 block, s = a/7."""
+    lib = _load()
+    w, pw = _c(w, np.float32)
+    G, K, N = w.shape
+    assert K % QBLOCK == 0 and N % QBLOCK == 0
+    q = np.empty((G, K, N), dtype=np.int8)
+    s = np.empty((G, K // QBLOCK, N // QBLOCK), dtype=np.float32)
+    lib.oracle_quantize_rhs_int4(pw, G, K, N, q.ctypes.data_as(ctypes.c_void_p),
+                                 s.ctypes.data_as(ctypes.c_void_p))
+    return q, s
+
+
+def gmm_fp8_int4(ql, sl, q4, sr, group_sizes):
+    """fp64 GMM of FP8 1x128 LHS codes/scales against int4 weights with
+    128x128 block scales."""
+    lib = _load()
+    ql, pql = _c(ql, np.uint8)
+    sl, psl = _c(sl, np.float32)
+    q4, pq4 = _c(q4, np.int8)
+    sr, psr = _c(sr, np.float32)
+    gs, pg = _c(group_sizes, np.int32)
+    M, K = ql.shape
+    G, K2, N = q4.shape
+    assert K == K2 and K % QBLOCK == 0 and N % QBLOCK == 0
+    assert sr.shape == (G, K // QBLOCK, N // QBLOCK)
+    assert gs.size == G and int(gs.sum()) <= M
+    out = np.empty((M, N), dtype=np.float64)
+    lib.oracle_gmm_fp8_int4(pql, psl, pq4, psr, pg, M, K, N, G,
+                            out.ctypes.data_as(ctypes.c_void_p))
     return out
 
 

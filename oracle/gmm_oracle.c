@@ -65,6 +65,14 @@
  *    per-block inner sum is exact in fp64 here too (each product has at
  *    most 6 significant bits and the exponents of 128 of them span far
  *    fewer than 53 - 6 - 7 binades for any finite scaled input).
+ *  - int4 weights ([V2s] names the type, nothing more): codes are signed
+ *    4-bit integers in [-8, 7] with the FP8 path's 128x128 RHS blocks and
+ *    fp32 block scales [Q2]; the quantiser is [V2q]'s recipe with the int4
+ *    maximum 7 in place of 448: s = a/7, inv = (s == 0 ? 0 : 1/s), code =
+ *    round-half-even(w*inv) clamped to [-8, 7] (|w*inv| <= 7 for this
+ *    quantiser, so its codes are the symmetric [-7, 7]; -8 can only come
+ *    from another quantiser).  The LHS keeps the FP8 1x128 recipe.  The
+ *    per-block inner sum is exact in fp64 (integer codes times e4m3 values).
  *
  * Parity pins: every function here is checked in tests/test_oracle_*.py
  * against something other than itself (torch's float8_e4m3fn cast, numpy
@@ -375,6 +383,110 @@ void oracle_gmm_fp8(const uint8_t *ql, const float *sl, const uint8_t *qr,
         }
         free(part);
         free(lrow);
+    }
+    free(gid);
+}
+
+/* ------------------------------------------------- int4 weights -- */
+
+/* One 128x128 int4 block ([V2s] with the [V2q] recipe; reading above):
+ * s = a/7, inv = (s == 0 ? 0 : 1/s), code = round-half-even(w*inv) in
+ * [-8, 7].  Each step one IEEE fp32 operation; nearbyintf rounds half to
+ * even in the default rounding mode. */
+static float quantize_block_int4(const float *vals, int n, int8_t *codes)
+{
+    float a = 0.0f, s, inv;
+    int i;
+    for (i = 0; i < n; ++i) {
+        float v = fabsf(vals[i]);
+        if (v > a)
+            a = v;
+    }
+    s = a / 7.0f;
+    inv = (s == 0.0f) ? 0.0f : 1.0f / s;
+    for (i = 0; i < n; ++i) {
+        float y = nearbyintf(vals[i] * inv);
+        if (y > 7.0f)
+            y = 7.0f;
+        if (y < -8.0f)
+            y = -8.0f;
+        codes[i] = (int8_t)y;
+    }
+    return s;
+}
+
+/* w: [G,K,N] fp32 -> codes [G,K,N] int8 (values in [-8, 7]) and scales
+ * [G,K/128,N/128] fp32, one per 128x128 block as for the FP8 RHS [Q2]. */
+void oracle_quantize_rhs_int4(const float *w, int64_t G, int64_t K, int64_t N,
+                              int8_t *q, float *scale)
+{
+    int64_t kb_n = K / QBLOCK, nb_n = N / QBLOCK;
+    int64_t t, total = G * kb_n * nb_n;
+#pragma omp parallel for schedule(static)
+    for (t = 0; t < total; ++t) {
+        int64_t g = t / (kb_n * nb_n);
+        int64_t kb = (t / nb_n) % kb_n;
+        int64_t nb = t % nb_n;
+        float *vals = (float *)malloc(sizeof(float) * QBLOCK * QBLOCK);
+        int8_t *codes = (int8_t *)malloc(QBLOCK * QBLOCK);
+        int64_t i, j;
+        for (i = 0; i < QBLOCK; ++i)
+            for (j = 0; j < QBLOCK; ++j)
+                vals[i * QBLOCK + j] =
+                    w[(g * K + kb * QBLOCK + i) * N + nb * QBLOCK + j];
+        scale[t] = quantize_block_int4(vals, QBLOCK * QBLOCK, codes);
+        for (i = 0; i < QBLOCK; ++i)
+            for (j = 0; j < QBLOCK; ++j)
+                q[(g * K + kb * QBLOCK + i) * N + nb * QBLOCK + j] =
+                    codes[i * QBLOCK + j];
+        free(vals);
+        free(codes);
+    }
+}
+
+/* out[m,n] = sum_b ( sum_{k in block b} dec(ql[m,k]) * q4[g,k,n] )
+ *                   * scale_l[m,b] * scale_r[g,b,n/128]
+ * for m in group g; rows past the total are 0 ([Q2], [Q3], [V1s], [V2s],
+ * [GG], [V2z]).  ql: [M,K] E4M3 codes, sl: [M,K/128], q4: [G,K,N] int4
+ * values (int8), sr: [G,K/128,N/128]; out: [M,N] fp64. */
+void oracle_gmm_fp8_int4(const uint8_t *ql, const float *sl, const int8_t *q4,
+                         const float *sr, const int32_t *group_sizes, int64_t M,
+                         int64_t K, int64_t N, int64_t G, double *out)
+{
+    int64_t nkb = K / QBLOCK, nnb = N / QBLOCK, m;
+    int32_t *gid = (int32_t *)malloc(sizeof(int32_t) * (M > 0 ? M : 1));
+    double lut[256];
+    int c;
+    for (c = 0; c < 256; ++c)
+        lut[c] = oracle_e4m3_decode((uint8_t)c);
+    row_groups(group_sizes, G, M, gid);
+#pragma omp parallel
+    {
+        double *part = (double *)malloc(sizeof(double) * N);
+#pragma omp for schedule(dynamic, 4)
+        for (m = 0; m < M; ++m) {
+            int64_t g = gid[m], b, k, n;
+            double *o = out + m * N;
+            for (n = 0; n < N; ++n)
+                o[n] = 0.0;
+            if (g >= G)
+                continue;
+            for (b = 0; b < nkb; ++b) {
+                double s_l = (double)sl[m * nkb + b];
+                for (n = 0; n < N; ++n)
+                    part[n] = 0.0;
+                for (k = 0; k < QBLOCK; ++k) {
+                    double a = lut[ql[m * K + b * QBLOCK + k]];
+                    const int8_t *wr = q4 + (g * K + b * QBLOCK + k) * N;
+                    for (n = 0; n < N; ++n)
+                        part[n] += a * (double)wr[n];
+                }
+                for (n = 0; n < N; ++n)
+                    o[n] += part[n] * s_l *
+                            (double)sr[(g * nkb + b) * nnb + n / QBLOCK];
+            }
+        }
+        free(part);
     }
     free(gid);
 }
