@@ -75,7 +75,8 @@ typedef enum {
     GMM_OP_FP8_MXFP4_FWD = 3,  /* gmm_fp8_mxfp4_fwd */
     GMM_OP_BF16_FWD = 4,       /* gmm_bf16_fwd */
     GMM_OP_TGMM = 5,           /* tgmm_bf16 */
-    GMM_OP_DX = 6              /* gmm_bf16_dx */
+    GMM_OP_DX = 6,             /* gmm_bf16_dx */
+    GMM_OP_FP8_INT4_FWD = 7    /* gmm_fp8_int4_fwd */
 } gmm_op;
 
 /* Bits of the device status word a grouped call writes into its workspace. */
@@ -107,7 +108,8 @@ GMM_API size_t gmm_workspace_bytes(int op, int64_t M, int64_t K, int64_t N, int6
  * tilings of their own; Q8: the tiling is found by searching).  In an
  * override a 0 field means "the library's choice"; gmm_get_tile_config
  * returns a resolved configuration (the fields the call uses set).
- *   FP8 forwards (GMM_OP_FP8_FWD, _SWIGLU, _MXFP4_FWD):
+ *   FP8 forwards (GMM_OP_FP8_FWD, _SWIGLU, _MXFP4_FWD, _INT4_FWD; the int4
+ *   forward: warp-specialised only, tile_n 512/256/128):
  *     kernel    1 warp-specialised (48 x 512 tiles: 8, 12 or 16 waves, MXFP4:
  *                 16 waves of tile_n 128/256/512 columns), 2 uniform (tile_m
  *                 48/64 rows, tile_n 128/256/512 columns; the only kernel of
@@ -285,6 +287,59 @@ GMM_API int gmm_quantize_rhs_mxfp4(const void *w, int w_dtype, int64_t G, int64_
  */
 GMM_API int gmm_fp8_mxfp4_fwd(const void *lhs, int lhs_dtype, const float *lhs_scale,
                 const uint8_t *rhs_q, const uint8_t *rhs_scale,
+                const int32_t *group_sizes, int64_t M, int64_t K, int64_t N,
+                int64_t G, void *out, int out_dtype, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * gmm_quantize_rhs_int4 -- int4 quantisation of the expert weights (done
+ *   once, offline).  "实现差距：GMM Kernel（V1 vs V2）", sections 3.4 and 4.1
+ *   list int4 beside float4_e2m1fn as sub-byte RHS types and give no scale
+ *   format; this library keeps the FP8 path's 128x128 blocks and the section
+ *   3.3 recipe with the int4 maximum 7: a = max |w| of the block, s = a/7,
+ *   inv = (s == 0 ? 0 : 1/s) (each correctly rounded fp32), code =
+ *   round-half-even(w * inv) in [-7, 7].
+ * w:     [G,K,N], w_dtype GMM_BF16 or GMM_F32.
+ * q:     G*K*N/2 bytes of two's-complement int4 codes in the packed order
+ *        gmm_fp8_int4_fwd reads: slab c = (g*N/16 + n/16)*K/128 + k/128 is
+ *        1024 bytes; lane l = 16*((k%128)/32) + n%16 owns bytes c*1024 + 16l
+ *        .. +15 holding rows j = k%32 of its column, byte 4d + i carrying
+ *        row j = 8d + i in its low nibble and row 8d + 4 + i in its high one.
+ * scale: [G,K/128,N/128] fp32.
+ * K and N must be multiples of 128.  Errors as for gmm_quantize_rhs.
+ */
+GMM_API int gmm_quantize_rhs_int4(const void *w, int w_dtype, int64_t G, int64_t K,
+                    int64_t N, uint8_t *q, float *scale, void *stream);
+
+/*
+ * gmm_pack_rhs_int4 -- int4 codes made elsewhere, one int8 value in [-8, 7]
+ *   per weight in the logical [G,K,N] row-major layout (with [G,K/128,N/128]
+ *   fp32 block scales, which gmm_fp8_int4_fwd takes unchanged), rewritten in
+ *   the packed order gmm_quantize_rhs_int4 writes.  Values outside [-8, 7]
+ *   keep their low 4 bits.
+ * q: [G,K,N] int8.  packed: G*K*N/2 bytes, not overlapping q.
+ * K and N must be multiples of 128; 1 <= G <= GMM_MAX_GROUPS.
+ */
+GMM_API int gmm_pack_rhs_int4(const int8_t *q, int64_t G, int64_t K, int64_t N,
+                              uint8_t *packed, void *stream);
+
+/*
+ * gmm_fp8_int4_fwd -- grouped matmul forward of a 1x128 FP8 LHS against
+ *   int4 weights with 128x128 block scales.
+ *   out[m,n] = sum_b sl[m,b] * sr[g,b,n/128] * sum_{k in block b} ql[m,k] q4[g,k,n]
+ *   for m in group g, accumulated in fp32; rows past the total are 0.  The
+ *   forward of gmm_fp8_fwd with the weights in the int4 type of
+ *   "实现差距：GMM Kernel（V1 vs V2）", sections 3.4 and 4.1; the codes are
+ *   expanded to E4M3 (exact for every int4 value) in registers.
+ * lhs, lhs_dtype, lhs_scale: as for gmm_fp8_fwd.
+ * rhs_q:     packed int4 codes (gmm_quantize_rhs_int4 or gmm_pack_rhs_int4).
+ * rhs_scale: [G,K/128,N/128] fp32.
+ * out:       [M,N], GMM_BF16 or GMM_F32.
+ * K and N must be multiples of 128; 1 <= G <= GMM_MAX_GROUPS.
+ * ws, ws_bytes: at least gmm_workspace_bytes(GMM_OP_FP8_INT4_FWD, ...).
+ * Errors: as for gmm_fp8_fwd.
+ */
+GMM_API int gmm_fp8_int4_fwd(const void *lhs, int lhs_dtype, const float *lhs_scale,
+                const uint8_t *rhs_q, const float *rhs_scale,
                 const int32_t *group_sizes, int64_t M, int64_t K, int64_t N,
                 int64_t G, void *out, int out_dtype, void *ws, size_t ws_bytes, void *stream);
 

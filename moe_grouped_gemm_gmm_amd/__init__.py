@@ -19,13 +19,14 @@ GMM_F32, GMM_BF16, GMM_E4M3 = 0, 1, 2
 GMM_MAX_GROUPS = 4096
 # operations (gmm_workspace_bytes) and device status bits (gmm_device_status)
 (OP_METADATA, OP_FP8_FWD, OP_FP8_FWD_SWIGLU, OP_FP8_MXFP4_FWD, OP_BF16_FWD, OP_TGMM,
- OP_DX) = range(7)
+ OP_DX, OP_FP8_INT4_FWD) = range(8)
 DEV_SUM_GT_M, DEV_NEGATIVE_SIZE = 1, 2
 EXPORTS = ("gmm_status_string", "gmm_last_error", "gmm_workspace_bytes", "gmm_device_status",
            "gmm_set_tile_config", "gmm_get_tile_config", "gmm_probe_stream_read",
            "gmm_group_metadata", "gmm_quantize_lhs", "gmm_quantize_rhs", "gmm_pack_rhs",
            "gmm_quant_scales", "gmm_fp8_fwd", "gmm_fp8_fwd_swiglu", "gmm_bf16_fwd", "tgmm_bf16",
-           "gmm_bf16_dx", "gmm_quantize_rhs_mxfp4", "gmm_fp8_mxfp4_fwd", "gmm_fp8_fwd_noalloc")
+           "gmm_bf16_dx", "gmm_quantize_rhs_mxfp4", "gmm_fp8_mxfp4_fwd", "gmm_fp8_fwd_noalloc",
+           "gmm_quantize_rhs_int4", "gmm_pack_rhs_int4", "gmm_fp8_int4_fwd")
 
 _lib = None
 
@@ -78,6 +79,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gmm_bf16_dx.argtypes = [P, P, P, I64, I64, I64, I64, P, I, P, SZ, P]
     lib.gmm_quantize_rhs_mxfp4.argtypes = [P, I, I64, I64, I64, P, P, P]
     lib.gmm_fp8_mxfp4_fwd.argtypes = [P, I, P, P, P, P, I64, I64, I64, I64, P, I, P, SZ, P]
+    lib.gmm_quantize_rhs_int4.argtypes = [P, I, I64, I64, I64, P, P, P]
+    lib.gmm_pack_rhs_int4.argtypes = [P, I64, I64, I64, P, P]
+    lib.gmm_fp8_int4_fwd.argtypes = [P, I, P, P, P, P, I64, I64, I64, I64, P, I, P, SZ, P]
     for name in EXPORTS[3:]:
         getattr(lib, name).restype = I
     _lib = lib
@@ -259,6 +263,54 @@ def gmm_fp8_mxfp4_fwd(lhs: torch.Tensor, rhs_q: torch.Tensor, rhs_scale: torch.T
     _check(lib.gmm_fp8_mxfp4_fwd(_ptr(lhs), _dt(lhs), _ptr(lhs_scale), _ptr(rhs_q),
                                  _ptr(rhs_scale), _ptr(group_sizes), M, K, N, G, _ptr(out),
                                  _dt(out), wsp, wsb, _stream(lhs)))
+    return out
+
+
+def gmm_quantize_rhs_int4(w: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
+    """int4 quantisation of w [G,K,N] -> (packed two's-complement codes uint8
+    [G, N/16, K/128, 1024], scales f32 [G, K/128, N/128]), in the order
+    gmm_fp8_int4_fwd reads (include/gmm.h, gmm_quantize_rhs_int4)."""
+    lib = load_library()
+    G, K, N = w.shape
+    q = torch.empty((G, max(N // 16, 0), max(K // 128, 0), 1024), dtype=torch.uint8, device=w.device)
+    s = torch.empty((G, max(K // 128, 0), max(N // 128, 0)), dtype=torch.float32, device=w.device)
+    _check(lib.gmm_quantize_rhs_int4(_ptr(w), _dt(w), G, K, N, _ptr(q), _ptr(s), _stream(w)))
+    return q, s
+
+
+def gmm_pack_rhs_int4(q: torch.Tensor) -> torch.Tensor:
+    """int4 codes made elsewhere (int8 values in [-8, 7], [G,K,N]) -> the packed
+    order gmm_fp8_int4_fwd reads, uint8 [G, N/16, K/128, 1024]."""
+    lib = load_library()
+    if q.dtype != torch.int8:
+        raise ValueError("int4 codes are passed as int8, got %s" % q.dtype)
+    G, K, N = q.shape
+    packed = torch.empty((G, max(N // 16, 0), max(K // 128, 0), 1024), dtype=torch.uint8,
+                         device=q.device)
+    _check(lib.gmm_pack_rhs_int4(_ptr(q), G, K, N, _ptr(packed), _stream(q)))
+    return packed
+
+
+def gmm_fp8_int4_fwd(lhs: torch.Tensor, rhs_q: torch.Tensor, rhs_scale: torch.Tensor,
+                     group_sizes: torch.Tensor, lhs_scale: Optional[torch.Tensor] = None,
+                     out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None,
+                     ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """GMM of a 1x128 FP8 LHS (bf16/fp32 quantised in-kernel, or uint8 codes with
+    lhs_scale [M,K/128]) against int4 weights from gmm_quantize_rhs_int4 (or
+    gmm_pack_rhs_int4 with their [G,K/128,N/128] scales)."""
+    lib = load_library()
+    M, K = lhs.shape
+    G, N16, KB, chunk = rhs_q.shape
+    N = N16 * 16
+    if chunk != 1024 or KB * 128 != K or tuple(rhs_scale.shape) != (G, KB, N // 128):
+        raise ValueError("rhs_q %s / rhs_scale %s do not match K=%d"
+                         % (tuple(rhs_q.shape), tuple(rhs_scale.shape), K))
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=lhs.device)
+    ws, wsp, wsb = _ws(ws, OP_FP8_INT4_FWD, M, K, N, G, lhs.device)
+    _check(lib.gmm_fp8_int4_fwd(_ptr(lhs), _dt(lhs), _ptr(lhs_scale), _ptr(rhs_q),
+                                _ptr(rhs_scale), _ptr(group_sizes), M, K, N, G, _ptr(out),
+                                _dt(out), wsp, wsb, _stream(lhs)))
     return out
 
 

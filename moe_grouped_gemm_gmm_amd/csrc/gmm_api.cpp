@@ -142,6 +142,7 @@ size_t gmm_workspace_bytes(int op, int64_t M, int64_t K, int64_t N, int64_t G) {
         case GMM_OP_BF16_FWD:
         case GMM_OP_TGMM:
         case GMM_OP_DX:
+        case GMM_OP_FP8_INT4_FWD:
             return kWsStatusBytes;
         default:
             return 0;
@@ -149,7 +150,7 @@ size_t gmm_workspace_bytes(int op, int64_t M, int64_t K, int64_t N, int64_t G) {
 }
 
 int gmm_set_tile_config(int op, const gmm_tile_config* cfg) {
-    if (op < GMM_OP_FP8_FWD || op > GMM_OP_DX)
+    if (op < GMM_OP_FP8_FWD || op > GMM_OP_FP8_INT4_FWD)
         return fail(GMM_ERR_SHAPE, "op %d has no tile configuration", op);
     if (cfg == nullptr) {
         gmm::set_tile_override(op, nullptr);
@@ -171,7 +172,7 @@ int gmm_set_tile_config(int op, const gmm_tile_config* cfg) {
 
 int gmm_get_tile_config(int op, int64_t M, int64_t K, int64_t N, int64_t G, int lhs_dtype,
                         int out_dtype, gmm_tile_config* cfg) {
-    if (op < GMM_OP_FP8_FWD || op > GMM_OP_DX)
+    if (op < GMM_OP_FP8_FWD || op > GMM_OP_FP8_INT4_FWD)
         return fail(GMM_ERR_SHAPE, "op %d has no tile configuration", op);
     if (cfg == nullptr) return fail(GMM_ERR_NULL, "cfg is NULL");
     GMM_TRY(check_out_dtype(out_dtype, "out"));
@@ -315,6 +316,66 @@ int gmm_fp8_mxfp4_fwd(const void* lhs, int lhs_dtype, const float* lhs_scale,
                                                 (int)M, (int)K, (int)N, (int)G, out,
                                                 out_dtype == GMM_BF16, ws_status(ws),
                                                 (hipStream_t)stream));
+}
+
+int gmm_quantize_rhs_int4(const void* w, int w_dtype, int64_t G, int64_t K, int64_t N, uint8_t* q,
+                          float* scale, void* stream) {
+    if (w_dtype != GMM_BF16 && w_dtype != GMM_F32)
+        return fail(GMM_ERR_DTYPE, "w dtype %d is not GMM_BF16 or GMM_F32", w_dtype);
+    if (G < 1 || G > GMM_MAX_GROUPS)
+        return fail(GMM_ERR_SHAPE, "G=%lld outside [1, %d]", (long long)G, GMM_MAX_GROUPS);
+    GMM_TRY(check_mult(K, 128, "K"));
+    GMM_TRY(check_mult(N, 128, "N"));
+    if (G * (K / 128) * (N / 128) > kMaxDim) return fail(GMM_ERR_SHAPE, "too many blocks");
+    GMM_TRY(check_ptr(w, "w"));
+    GMM_TRY(check_ptr(q, "q"));
+    GMM_TRY(check_ptr(scale, "scale"));
+    return hip_status(gmm::launch_quantize_rhs_int4(w, w_dtype == GMM_BF16, G, K, N, q, scale,
+                                                    (hipStream_t)stream));
+}
+
+int gmm_pack_rhs_int4(const int8_t* q, int64_t G, int64_t K, int64_t N, uint8_t* packed, void* stream) {
+    if (G < 1 || G > GMM_MAX_GROUPS)
+        return fail(GMM_ERR_SHAPE, "G=%lld outside [1, %d]", (long long)G, GMM_MAX_GROUPS);
+    GMM_TRY(check_mult(K, 128, "K"));
+    GMM_TRY(check_mult(N, 128, "N"));
+    if (G * (N / 16) * (K / 128) > kMaxDim) return fail(GMM_ERR_SHAPE, "too many slabs");
+    GMM_TRY(check_ptr(q, "q"));
+    GMM_TRY(check_ptr(packed, "packed"));
+    const uintptr_t a = (uintptr_t)q, b = (uintptr_t)packed;
+    const uintptr_t na = (uintptr_t)(G * K * N), nb = na / 2;
+    if (a < b + nb && b < a + na) return fail(GMM_ERR_SHAPE, "packed overlaps q");
+    return hip_status(gmm::launch_pack_rhs_int4(q, G, K, N, packed, (hipStream_t)stream));
+}
+
+int gmm_fp8_int4_fwd(const void* lhs, int lhs_dtype, const float* lhs_scale, const uint8_t* rhs_q,
+                     const float* rhs_scale, const int32_t* group_sizes, int64_t M, int64_t K, int64_t N,
+                     int64_t G, void* out, int out_dtype, void* ws, size_t ws_bytes, void* stream) {
+    int kind;
+    if (lhs_dtype == GMM_E4M3) kind = 0;
+    else if (lhs_dtype == GMM_BF16) kind = 1;
+    else if (lhs_dtype == GMM_F32) kind = 2;
+    else return fail(GMM_ERR_DTYPE, "lhs dtype %d unsupported", lhs_dtype);
+    GMM_TRY(check_out_dtype(out_dtype, "out"));
+    GMM_TRY(check_groups(M, G));
+    GMM_TRY(check_mult(K, 128, "K"));
+    GMM_TRY(check_mult(N, 128, "N"));
+    GMM_TRY(check_ptr(lhs, "lhs"));
+    GMM_TRY(check_ptr(rhs_q, "rhs_q"));
+    GMM_TRY(check_ptr(rhs_scale, "rhs_scale"));
+    GMM_TRY(check_ptr(group_sizes, "group_sizes"));
+    GMM_TRY(check_ptr(out, "out"));
+    if (kind == 0) GMM_TRY(check_ptr(lhs_scale, "lhs_scale"));
+    else if (lhs_scale != nullptr) return fail(GMM_ERR_DTYPE, "lhs_scale given with an unquantised lhs");
+    const int64_t blocks = ((M + 47) / 48 + G + 1) * (N / 128);
+    if (blocks > kMaxDim) return fail(GMM_ERR_SHAPE, "grid too large");
+    GMM_TRY(check_ws(ws, ws_bytes, gmm_workspace_bytes(GMM_OP_FP8_INT4_FWD, M, K, N, G)));
+    gmm::TileConfig cfg;
+    GMM_TRY(resolve(GMM_OP_FP8_INT4_FWD, M, K, N, G, kind, out_dtype == GMM_BF16, false, &cfg));
+    if (M == 0) return GMM_OK;
+    return hip_status(gmm::launch_fp8_int4_fwd(cfg, lhs, kind, lhs_scale, rhs_q, rhs_scale, group_sizes,
+                                               (int)M, (int)K, (int)N, (int)G, out, out_dtype == GMM_BF16,
+                                               ws_status(ws), (hipStream_t)stream));
 }
 
 }  // extern "C"

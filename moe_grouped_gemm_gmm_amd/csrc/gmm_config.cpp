@@ -139,6 +139,22 @@ bool resolve_mxfp4(const TileConfig& f, int64_t K, int64_t N, TileConfig* c, con
     return true;
 }
 
+// int4 weights: the warp-specialised kernel only (16 waves, 48-row tiles),
+// tile_n the widest of 512/256/128 dividing N unless set.
+bool resolve_int4(const TileConfig& f, int64_t N, TileConfig* c, const char** why) {
+    *c = TileConfig{};
+    if ((f.kernel && f.kernel != kKerWs) || (f.waves && f.waves != 16) || (f.tile_m && f.tile_m != 48) ||
+        f.depth || f.residency || f.placement)
+        return fail(why, "the int4 forward sets only tile_n (warp-specialised, 16 waves, 48 rows)");
+    c->kernel = kKerWs;
+    c->waves = 16;
+    c->tile_m = 48;
+    c->tile_n = f.tile_n ? f.tile_n : (N % 512 == 0 ? 512 : (N % 256 == 0 ? 256 : 128));
+    if ((c->tile_n != 128 && c->tile_n != 256 && c->tile_n != 512) || N % c->tile_n != 0)
+        return fail(why, "tile_n must be 128, 256 or 512 and divide N");
+    return true;
+}
+
 bool resolve_swiglu(const TileConfig& f, int64_t M, int64_t N, int64_t G, TileConfig* c,
                     const char** why) {
     *c = TileConfig{};
@@ -192,6 +208,7 @@ bool resolve_tile_config(int op, int64_t M, int64_t K, int64_t N, int64_t G, int
         case kOpFp8Fwd: return resolve_fp8(f, M, K, N, G, lhs_kind, out_bf16, write_q, out, why);
         case kOpFp8Swiglu: return resolve_swiglu(f, M, N, G, out, why);
         case kOpFp8Mxfp4: return resolve_mxfp4(f, K, N, out, why);
+        case kOpFp8Int4: return resolve_int4(f, N, out, why);
         case kOpBf16Fwd:
         case kOpTgmm:
         case kOpDx: return resolve_bf16(op, f, M, K, N, G, out, why);

@@ -10,7 +10,7 @@ namespace gmm {
 
 // Operation ids (the gmm_op values of gmm.h).
 enum Op { kOpMetadata = 0, kOpFp8Fwd = 1, kOpFp8Swiglu = 2, kOpFp8Mxfp4 = 3, kOpBf16Fwd = 4,
-          kOpTgmm = 5, kOpDx = 6, kNumOps = 7 };
+          kOpTgmm = 5, kOpDx = 6, kOpFp8Int4 = 7, kNumOps = 8 };
 
 // FP8 forward kernels.
 enum Fp8Kernel { kKerAuto = 0, kKerWs = 1, kKerUniform = 2, kKerRowResident = 3 };

@@ -51,12 +51,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // residual a - 7y (one FMA) and one more FMA.  This equals the IEEE quotient
 // for every fp32 significand (checked exhaustively over a binade, which
 // covers every exponent since division by 7 commutes with powers of two).
-__device__ __forceinline__ float quant_scale(float a) {
+__device__ __forceinline__ float quant_scale7(float a) {   // RN(a / 7)
     constexpr float kInv7 = 0.142857149243354797363281250f;  // RN(1/7)
     const float y = __fmul_rn(a, kInv7);
     const float r = __builtin_fmaf(-y, 7.0f, a);
-    return __fmul_rn(__builtin_fmaf(r, kInv7, y), 0.015625f);
+    return __builtin_fmaf(r, kInv7, y);
 }
+__device__ __forceinline__ float quant_scale(float a) { return __fmul_rn(quant_scale7(a), 0.015625f); }
 
 // inv = RN(1/s), or 0 when s == 0.  The hardware reciprocal estimate refined
 // by one FMA Newton step equals the IEEE quotient 1/s for every significand
@@ -77,6 +78,35 @@ __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
     int r = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __float_as_int(a), false);
     r = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, r, true);
     return (uint32_t)r;
+}
+
+// int4 weights.  The scale of a 128x128 block is RN(a/7) (quant_scale7; 7 =
+// the largest int4 magnitude the quantiser uses) with inverse quant_inv, whose
+// reciprocal is normal for every in-contract a, and a code is the weight
+// times the inverse rounded half to even, clamped to [-8, 7].
+__device__ __forceinline__ int int4_code(float w, float inv) {
+    const float y = __builtin_rintf(w * inv);
+    return (int)fminf(fmaxf(y, -8.0f), 7.0f);
+}
+
+// Four int4 codes (two's complement, one in the low 4 bits of each byte;
+// the high bits are ignored) -> their four E4M3 codes, byte for byte.  Every
+// integer in [-8, 7] is exact in E4M3: one byte permutation looks up the
+// non-negative codes, one the negative ones, and the sign bit of each nibble
+// picks between them.  The pick mask comes from a third permutation whose
+// selector bytes are 12 (-> 0x00) or 13 (-> 0xFF), v_perm_b32's constant
+// selectors (a multiply would also spread the bit, at a quarter of the rate).
+__device__ __forceinline__ uint32_t int4_to_e4m3x4(uint32_t nib) {
+    constexpr uint32_t kPos03 = 0x44403800u;   // E4M3 of 0, 1, 2, 3 (bytes 0..3)
+    constexpr uint32_t kPos47 = 0x4E4C4A48u;   // 4, 5, 6, 7
+    constexpr uint32_t kNeg03 = 0xCACCCED0u;   // -8, -7, -6, -5 (low 3 bits 0..3)
+    constexpr uint32_t kNeg47 = 0xB8C0C4C8u;   // -4, -3, -2, -1 (low 3 bits 4..7)
+    const uint32_t idx = nib & 0x07070707u;
+    const uint32_t pos = __builtin_amdgcn_perm(kPos47, kPos03, idx);
+    const uint32_t neg = __builtin_amdgcn_perm(kNeg47, kNeg03, idx);
+    const uint32_t sel = ((nib >> 3) & 0x01010101u) | 0x0C0C0C0Cu;
+    const uint32_t mask = __builtin_amdgcn_perm(0u, 0u, sel);   // 0xFF where the nibble is negative
+    return (pos & ~mask) | (neg & mask);
 }
 
 // --------------------------------------------------------- wave helpers --

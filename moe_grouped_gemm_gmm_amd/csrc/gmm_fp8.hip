@@ -553,8 +553,14 @@ __global__ __launch_bounds__(kThreads, 2) void fp8_fwd_kernel(
 // the FMA factor is the LHS scale alone.  The producers store the LHS codes
 // with K runs 1<->2 and 5<->6 of 16 exchanged (the MFMA's K grouping for an
 // FP4 first operand, which the packed weights follow).
+// I4: int4 weights (same sections: int4 is the other sub-byte RHS type) with
+// the FP8 path's 128x128 fp32 block scales, packed at 16 bytes per lane and
+// block step (quantize_rhs_int4_kernel), TN = 512, 256 or 128.  gfx950 has
+// no MFMA taking int4, so each consumer expands its codes to E4M3 in
+// registers (int4_to_e4m3x4: every int4 value is exact in E4M3) right before
+// the block's MFMAs; the rest is the FP8 path.
 template <int KIND, bool OUT_BF16, int TM, bool WRITE_Q, int NW = 8, int TN = 512, bool B4 = false,
-          int NP = NW / 2, int BD = 1>
+          int NP = NW / 2, int BD = 1, bool I4 = false>
 __global__ __launch_bounds__(64 * NW, NW / 4) void fp8_fwd_ws_kernel(   // TM = 48 (64 spills)
     const void* __restrict__ lhs, const float* __restrict__ lhs_scale,
     const uint8_t* __restrict__ rhs, const void* __restrict__ rhs_scale_v,
@@ -564,8 +570,9 @@ __global__ __launch_bounds__(64 * NW, NW / 4) void fp8_fwd_ws_kernel(   // TM = 
     static_assert(TM == 64 || TM == 48, "64- or 48-row tiles");
     static_assert(NW == 8 || NW == 12 || NW == 16, "8, 12 or 16 waves");
     static_assert(NP == 4 || NP == 8, "4 or 8 producer waves");
-    static_assert(B4 ? (NW == 16 && NP == 8 && (TN == 512 || TN == 256 || TN == 128)) : TN == 512,
-                  "FP8 weights: 512 columns; MXFP4: 16 waves, 512/256/128 columns");
+    static_assert((B4 || I4) ? (NW == 16 && NP == 8 && (TN == 512 || TN == 256 || TN == 128)) : TN == 512,
+                  "FP8 weights: 512 columns; MXFP4 and int4: 16 waves, 512/256/128 columns");
+    static_assert(!(B4 && I4), "one weight type");
     constexpr int MB = TM / 16;
     constexpr int NC = NW - NP;            // consumer waves
     static_assert(NC == 4 || NC == 8, "4 or 8 consumer waves");
@@ -643,7 +650,7 @@ __global__ __launch_bounds__(64 * NW, NW / 4) void fp8_fwd_ws_kernel(   // TM = 
             qvalid[h] = qgrow[h] >= it.lo && qgrow[h] < it.hi;
             qlrow[h] = qvalid[h] ? qgrow[h] : it.lo;
         }
-        const float* srl = B4 ? nullptr : rhs_scale + (int64_t)g * nkb * nnb + n0 / kQBlock + min(qchunk, 3);
+        const float* srl = B4 ? nullptr : rhs_scale + (int64_t)g * nkb * nnb + n0 / kQBlock + min(qchunk, TN / kQBlock - 1);
         struct Stage2 {
             RawA<KIND> raw[HP];
             float sr;
@@ -710,7 +717,7 @@ __global__ __launch_bounds__(64 * NW, NW / 4) void fp8_fwd_ws_kernel(   // TM = 
     const int lr = lane & 15, lc = lane >> 4;
     const int ncol0 = n0 + CWID * cw;
     const int cslot = B4 ? 0 : (CWID * cw) / 128;   // the wave's 128-column scale block
-    const uint8_t* bptr = rhs + ((int64_t)g * (N / 16) + ncol0 / 16) * nkb * (B4 ? 1024 : 2048) + lane * 16;
+    const uint8_t* bptr = rhs + ((int64_t)g * (N / 16) + ncol0 / 16) * nkb * (B4 || I4 ? 1024 : 2048) + lane * 16;
     const uint8_t* eptr = B4 ? rhs_e8 + ((int64_t)g * (N / 16) + ncol0 / 16) * nkb * 64 + lane : nullptr;
     v4f acc[MB][NBC];
 #pragma unroll
@@ -722,10 +729,10 @@ __global__ __launch_bounds__(64 * NW, NW / 4) void fp8_fwd_ws_kernel(   // TM = 
     v8i b[BD][NBC];
     int be[BD][NBC];
     auto load_b1 = [&](int s, int j, int kb) {
-        if constexpr (B4) {
+        if constexpr (B4 || I4) {
             const v4i lo = *reinterpret_cast<const v4i*>(bptr + ((int64_t)j * nkb + kb) * 1024);
             b[s][j] = __builtin_shufflevector(lo, lo, 0, 1, 2, 3, -1, -1, -1, -1);
-            be[s][j] = eptr[((int64_t)j * nkb + kb) * 64];
+            if constexpr (B4) be[s][j] = eptr[((int64_t)j * nkb + kb) * 64];
         } else {
             const uint8_t* q = bptr + ((int64_t)j * nkb + kb) * 2048;
             const uint4 lo = *reinterpret_cast<const uint4*>(q);
@@ -754,6 +761,15 @@ __global__ __launch_bounds__(64 * NW, NW / 4) void fp8_fwd_ws_kernel(   // TM = 
         }
 #pragma unroll
         for (int j = 0; j < NBC; ++j) {
+            v8i bj = bs[j];
+            if constexpr (I4) {   // 32 int4 codes (4 dwords) -> 32 E4M3 codes (8 dwords)
+#pragma unroll
+                for (int d = 3; d >= 0; --d) {
+                    const uint32_t x = (uint32_t)bs[j][d];
+                    bj[2 * d] = (int)int4_to_e4m3x4(x);
+                    bj[2 * d + 1] = (int)int4_to_e4m3x4(x >> 4);
+                }
+            }
 #pragma unroll
             for (int i = 0; i < MB; ++i) {
                 v4f pr;
@@ -762,7 +778,7 @@ __global__ __launch_bounds__(64 * NW, NW / 4) void fp8_fwd_ws_kernel(   // TM = 
                         bs[j], af[i], v4f{0.f, 0.f, 0.f, 0.f}, 4, 0, 0, bes[j], 0, 127);
                 else
                     pr = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        bs[j], af[i], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+                        bj, af[i], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(pr[r], cf[i], acc[i][j][r]);
             }
@@ -1062,7 +1078,7 @@ hipError_t launch_wsn(const void* lhs, const float* lhs_scale, const uint8_t* rh
 }
 
 template <int KIND, int TM, bool WRITE_Q, int NW = 8, int TN = 512, bool B4 = false, int NP = NW / 2,
-          int BD = 1>
+          int BD = 1, bool I4 = false>
 hipError_t launch_ws(const void* lhs, const float* lhs_scale, const uint8_t* rhs,
                      const void* rhs_scale, const int32_t* group_sizes, int M, int K, int N, int G,
                      void* out, bool out_bf16, uint8_t* q_out, float* scale_out, int32_t* status, hipStream_t stream,
@@ -1074,11 +1090,11 @@ hipError_t launch_ws(const void* lhs, const float* lhs_scale, const uint8_t* rhs
         ? kNumXcd * (int)std::max<int64_t>((items + kNumXcd - 1) / kNumXcd, device_cus() / kNumXcd)
         : (int)(items * ntiles_n);
     if (out_bf16)
-        hipLaunchKernelGGL((fp8_fwd_ws_kernel<KIND, true, TM, WRITE_Q, NW, TN, B4, NP, BD>), dim3(nblocks),
+        hipLaunchKernelGGL((fp8_fwd_ws_kernel<KIND, true, TM, WRITE_Q, NW, TN, B4, NP, BD, I4>), dim3(nblocks),
                            dim3(64 * NW), 0, stream, lhs, lhs_scale, rhs, rhs_scale, group_sizes, M,
                            K, N, G, out, q_out, scale_out, ntiles_n, nblocks, status, placement);
     else
-        hipLaunchKernelGGL((fp8_fwd_ws_kernel<KIND, false, TM, WRITE_Q, NW, TN, B4, NP, BD>), dim3(nblocks),
+        hipLaunchKernelGGL((fp8_fwd_ws_kernel<KIND, false, TM, WRITE_Q, NW, TN, B4, NP, BD, I4>), dim3(nblocks),
                            dim3(64 * NW), 0, stream, lhs, lhs_scale, rhs, rhs_scale, group_sizes, M,
                            K, N, G, out, q_out, scale_out, ntiles_n, nblocks, status, placement);
     return hipGetLastError();
@@ -1109,6 +1125,26 @@ hipError_t launch_mxfp4_kind(const TileConfig& cfg, const void* lhs, const float
     return launch_ws<KIND, 48, false, 16, 128, true>(lhs, lhs_scale, rhs_q, rhs_e8, group_sizes, M,
                                                      K, N, G, out, out_bf16, nullptr, nullptr,
                                                      status, stream);
+}
+
+// int4 weights: the warp-specialised kernel with 48-row tiles of cfg.tile_n
+// columns.
+template <int KIND>
+hipError_t launch_int4_kind(const TileConfig& cfg, const void* lhs, const float* lhs_scale,
+                            const uint8_t* rhs_q, const float* rhs_scale, const int32_t* group_sizes,
+                            int M, int K, int N, int G, void* out, bool out_bf16, int32_t* status,
+                            hipStream_t stream) {
+    if (cfg.tile_n == 512)
+        return launch_ws<KIND, 48, false, 16, 512, false, 8, 1, true>(lhs, lhs_scale, rhs_q, rhs_scale,
+                                                                      group_sizes, M, K, N, G, out, out_bf16,
+                                                                      nullptr, nullptr, status, stream);
+    if (cfg.tile_n == 256)
+        return launch_ws<KIND, 48, false, 16, 256, false, 8, 1, true>(lhs, lhs_scale, rhs_q, rhs_scale,
+                                                                      group_sizes, M, K, N, G, out, out_bf16,
+                                                                      nullptr, nullptr, status, stream);
+    return launch_ws<KIND, 48, false, 16, 128, false, 8, 1, true>(lhs, lhs_scale, rhs_q, rhs_scale,
+                                                                  group_sizes, M, K, N, G, out, out_bf16,
+                                                                  nullptr, nullptr, status, stream);
 }
 
 template <int KIND, int WN, int TM, bool WRITE_Q, bool SWIGLU = false>
@@ -1246,6 +1282,23 @@ hipError_t launch_fp8_mxfp4_fwd(const TileConfig& cfg, const void* lhs, int lhs_
         default:
             return launch_mxfp4_kind<kLhsF32>(cfg, lhs, nullptr, rhs_q, rhs_scale, group_sizes, M, K, N,
                                               G, out, out_bf16, status, stream);
+    }
+}
+
+hipError_t launch_fp8_int4_fwd(const TileConfig& cfg, const void* lhs, int lhs_kind, const float* lhs_scale,
+                               const uint8_t* rhs_q, const float* rhs_scale,
+                               const int32_t* group_sizes, int M, int K, int N, int G, void* out,
+                               bool out_bf16, int32_t* status, hipStream_t stream) {
+    switch (lhs_kind) {
+        case kLhsE4M3:
+            return launch_int4_kind<kLhsE4M3>(cfg, lhs, lhs_scale, rhs_q, rhs_scale, group_sizes, M, K, N, G,
+                                              out, out_bf16, status, stream);
+        case kLhsBF16:
+            return launch_int4_kind<kLhsBF16>(cfg, lhs, nullptr, rhs_q, rhs_scale, group_sizes, M, K, N, G,
+                                              out, out_bf16, status, stream);
+        default:
+            return launch_int4_kind<kLhsF32>(cfg, lhs, nullptr, rhs_q, rhs_scale, group_sizes, M, K, N, G,
+                                             out, out_bf16, status, stream);
     }
 }
 

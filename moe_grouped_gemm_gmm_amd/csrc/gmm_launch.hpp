@@ -60,6 +60,14 @@ hipError_t launch_quant_scales(const float* amax, int64_t n, float* scale, float
 hipError_t launch_quantize_rhs_mxfp4(const void* w, bool w_bf16, int64_t G, int64_t K, int64_t N,
                                      uint8_t* q, uint8_t* scale, hipStream_t stream);
 
+// int4 weights (codes in [-8, 7], 128x128 fp32 block scales s = a/7) in the
+// forward's packed operand order (G*K*N/2 bytes); and int4 codes made
+// elsewhere (int8 values, logical [G,K,N]) into that order.
+hipError_t launch_quantize_rhs_int4(const void* w, bool w_bf16, int64_t G, int64_t K, int64_t N,
+                                    uint8_t* q, float* scale, hipStream_t stream);
+hipError_t launch_pack_rhs_int4(const int8_t* q, int64_t G, int64_t K, int64_t N, uint8_t* packed,
+                                hipStream_t stream);
+
 // lhs_kind: 0 = E4M3 codes + lhs_scale, 1 = bf16, 2 = fp32.
 hipError_t launch_fp8_fwd(const TileConfig& cfg, const void* lhs, int lhs_kind, const float* lhs_scale,
                           const uint8_t* rhs, const float* rhs_scale,
@@ -79,6 +87,12 @@ hipError_t launch_fp8_mxfp4_fwd(const TileConfig& cfg, const void* lhs, int lhs_
                                 const uint8_t* rhs_q, const uint8_t* rhs_scale,
                                 const int32_t* group_sizes, int M, int K, int N, int G, void* out,
                                 bool out_bf16, int32_t* status, hipStream_t stream);
+
+// FP8 (1x128) LHS against packed int4 weights with 128x128 fp32 block scales.
+hipError_t launch_fp8_int4_fwd(const TileConfig& cfg, const void* lhs, int lhs_kind, const float* lhs_scale,
+                               const uint8_t* rhs_q, const float* rhs_scale,
+                               const int32_t* group_sizes, int M, int K, int N, int G, void* out,
+                               bool out_bf16, int32_t* status, hipStream_t stream);
 
 hipError_t launch_bf16_fwd(const TileConfig& cfg, const void* lhs, const void* rhs, const int32_t* group_sizes, int M,
                            int K, int N, int G, void* out, bool out_bf16, int32_t* status, hipStream_t stream);

@@ -232,6 +232,123 @@ hipError_t launch_pack_rhs(const uint8_t* q, int64_t G, int64_t K, int64_t N, ui
     return hipGetLastError();
 }
 
+// ------------------------------------------------------- int4 weights --
+// int4 codes ("实现差距：GMM Kernel（V1 vs V2）", sections 3.4 and 4.1 name
+// int4 among the sub-byte RHS types) with the FP8 path's 128x128 blocks and
+// fp32 scales; the packed order is the FP8 one at half the bytes: per
+// (expert g, 16-column block, 128-K step) a 1 KB slab [64 lanes][16 bytes],
+// lane l = 16 * ((k % 128) / 32) + n % 16 holding the 32 codes of column n
+// and rows 128 kb + 32 (l / 16) + j, two per byte: dword d, byte i holds row
+// j = 8d + i in its low nibble and row 8d + 4 + i in its high nibble, so
+// that expanding a dword's low and then high nibbles gives the E4M3 operand
+// bytes of rows 8d .. 8d+7 in order (int4_to_e4m3x4).
+
+// Byte offset of the 16-byte run of column n, rows k0 .. k0+31 (k0 % 32 == 0).
+__device__ __forceinline__ int64_t int4_packed_offset(int g, int n, int k0, int N, int K) {
+    const int nb16 = n >> 4, lr = n & 15, kb = k0 >> 7, lc = (k0 & 127) >> 5;
+    return ((((int64_t)g * (N >> 4) + nb16) * (K >> 7) + kb) * 64 + lc * 16 + lr) * 16;
+}
+
+// 32 codes of one run (c[j], rows j = 0..31) -> the run's 16 bytes.
+__device__ __forceinline__ uint4 int4_run(const int* c) {
+    uint32_t d[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        uint32_t v = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            v |= ((uint32_t)(c[8 * q + i] & 15) | ((uint32_t)(c[8 * q + 4 + i] & 15) << 4)) << (8 * i);
+        d[q] = v;
+    }
+    return make_uint4(d[0], d[1], d[2], d[3]);
+}
+
+// One workgroup per (g, kb, nb) 128x128 block; thread t owns column
+// nb*128 + t % 128 and the 64 rows of half t / 128 (two 32-row runs).
+template <bool BF16>
+__global__ __launch_bounds__(256) void quantize_rhs_int4_kernel(const void* __restrict__ w, int K, int N,
+                                                                uint8_t* __restrict__ q,
+                                                                float* __restrict__ scale) {
+    __shared__ float wave_max[4];
+    const int nkb = K / kQBlock, nnb = N / kQBlock;
+    const int blk = blockIdx.x;
+    const int g = blk / (nkb * nnb), kb = (blk / nnb) % nkb, nb = blk % nnb;
+    const int t = threadIdx.x, n = nb * kQBlock + (t & 127), k0 = kb * kQBlock + (t >> 7) * 64;
+    float v[64];
+    const int64_t base = ((int64_t)g * K + k0) * N + n;
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+        if constexpr (BF16)
+            v[i] = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(w)[base + (int64_t)i * N] << 16);
+        else
+            v[i] = reinterpret_cast<const float*>(w)[base + (int64_t)i * N];
+    }
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 64; ++i) a = fmaxf(a, fabsf(v[i]));
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) a = fmaxf(a, __shfl_xor(a, d, 64));
+    if (lane_id() == 0) wave_max[t >> 6] = a;
+    __syncthreads();
+    a = fmaxf(fmaxf(wave_max[0], wave_max[1]), fmaxf(wave_max[2], wave_max[3]));
+    const float s = quant_scale7(a);
+    const float inv = quant_inv(s);
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        int c[32];
+#pragma unroll
+        for (int j = 0; j < 32; ++j) c[j] = int4_code(v[32 * r + j], inv);
+        *reinterpret_cast<uint4*>(q + int4_packed_offset(g, n, k0 + 32 * r, N, K)) = int4_run(c);
+    }
+    if (t == 0) scale[blk] = s;
+}
+
+// int4 codes made elsewhere (int8 values in [-8, 7], logical [G,K,N]) into the
+// packed order.  One workgroup per 1 KB slab: 128 threads stage the slab's
+// 128 rows x 16 columns in LDS, then 64 of them write one 16-byte run each.
+__global__ __launch_bounds__(128) void pack_rhs_int4_kernel(const int8_t* __restrict__ q, int K, int N,
+                                                            uint8_t* __restrict__ packed) {
+    __shared__ int8_t tile[kQBlock][16 + 4];
+    const int nkb = K / kQBlock, nn16 = N / 16;
+    const int64_t slab = blockIdx.x;               // (g * N/16 + nb) * K/128 + kb
+    const int kb = (int)(slab % nkb);
+    const int64_t gnb = slab / nkb;
+    const int nb = (int)(gnb % nn16);
+    const int64_t g = gnb / nn16;
+    const int t = threadIdx.x;
+    const uint4 row = *reinterpret_cast<const uint4*>(q + (g * K + kb * kQBlock + t) * N + nb * 16);
+    const uint32_t words[4] = {row.x, row.y, row.z, row.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint32_t*>(&tile[t][4 * i]) = words[i];
+    __syncthreads();
+    if (t >= 64) return;
+    const int col = t & 15, j0 = 32 * (t >> 4);
+    int c[32];
+#pragma unroll
+    for (int j = 0; j < 32; ++j) c[j] = tile[j0 + j][col];
+    *reinterpret_cast<uint4*>(packed + slab * 1024 + t * 16) = int4_run(c);
+}
+
+hipError_t launch_quantize_rhs_int4(const void* w, bool bf16, int64_t G, int64_t K, int64_t N, uint8_t* q,
+                                    float* scale, hipStream_t stream) {
+    const int64_t blocks = G * (K / kQBlock) * (N / kQBlock);
+    if (bf16)
+        hipLaunchKernelGGL(quantize_rhs_int4_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, w,
+                           (int)K, (int)N, q, scale);
+    else
+        hipLaunchKernelGGL(quantize_rhs_int4_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream, w,
+                           (int)K, (int)N, q, scale);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_rhs_int4(const int8_t* q, int64_t G, int64_t K, int64_t N, uint8_t* packed,
+                                hipStream_t stream) {
+    const int64_t slabs = G * (N / 16) * (K / kQBlock);
+    hipLaunchKernelGGL(pack_rhs_int4_kernel, dim3((unsigned)slabs), dim3(128), 0, stream, q, (int)K,
+                       (int)N, packed);
+    return hipGetLastError();
+}
+
 // ---------------------------------------------- the recipe's scale pair --
 // s = a/448 and inv = (s == 0 ? 0 : 1/s) for a list of block abs-maxima,
 // through the same device routines every quantiser above and the fused

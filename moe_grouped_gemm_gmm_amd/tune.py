@@ -16,6 +16,7 @@ gmm_set_tile_config (include/gmm.h):
                              uniform kernel (tile_m 48/64 x tile_n 128/256/512),
                              row-resident sweep (tile_n 512 or 256)
   mxfp4_fwd                  warp-specialised tile_n 512/256/128, row-resident
+  int4_fwd                   warp-specialised tile_n 512/256/128
   swiglu                     tile_m 48/64
   bf16_fwd, dx               residency 2/3 workgroups per CU
   tgmm                       residency 2/3 x placement (whole groups per XCD,
@@ -45,7 +46,7 @@ from typing import Callable, Dict, List, Optional, Sequence, Tuple
 
 import numpy as np
 
-PHASES = ("fp8_fwd", "fp8_fwd_prequant", "mxfp4_fwd", "swiglu", "bf16_fwd", "tgmm", "dx")
+PHASES = ("fp8_fwd", "fp8_fwd_prequant", "mxfp4_fwd", "int4_fwd", "swiglu", "bf16_fwd", "tgmm", "dx")
 BF16_PHASES = ("bf16_fwd", "tgmm", "dx")
 
 # Q9.4 stages: (atol, rtol, minimum SNR in dB)
@@ -55,7 +56,7 @@ VERIFY_TOP = 3
 
 # gmm_op of each phase
 _OPS = {"fp8_fwd": 1, "fp8_fwd_prequant": 1, "swiglu": 2, "mxfp4_fwd": 3, "bf16_fwd": 4,
-        "tgmm": 5, "dx": 6}
+        "tgmm": 5, "dx": 6, "int4_fwd": 7}
 
 
 def op_of(phase: str) -> int:
@@ -83,6 +84,9 @@ def space(phase: str) -> List[Dict[str, int]]:
         for tn in (512, 256, 128):
             out.append({"kernel": 1, "tile_n": tn})
         out.append({"kernel": 3})
+    elif phase == "int4_fwd":
+        for tn in (512, 256, 128):
+            out.append({"kernel": 1, "tile_n": tn})
     elif phase == "swiglu":
         for tm in (48, 64):
             out.append({"tile_m": tm})
@@ -182,6 +186,10 @@ class Problem:
             q4, e8 = gmm.gmm_quantize_rhs_mxfp4(w)
             out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
             fn = lambda: gmm.gmm_fp8_mxfp4_fwd(x, q4, e8, gs, out=out, ws=ws)
+        elif phase == "int4_fwd":
+            qi, si = gmm.gmm_quantize_rhs_int4(w)
+            out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            fn = lambda: gmm.gmm_fp8_int4_fwd(x, qi, si, gs, out=out, ws=ws)
         else:
             q, s = gmm.gmm_quantize_rhs(w)
             out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)

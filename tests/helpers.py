@@ -116,3 +116,26 @@ def pack_mxfp4(codes: np.ndarray, e8: np.ndarray):
     qp = (pairs[..., 0] | (pairs[..., 1] << 4)).astype(np.uint8).reshape(G, N16, KB, 1024)
     s = e8.reshape(G, KB, 4, N16, 16).transpose(0, 3, 1, 2, 4)[:, :, :, _SWAP2]
     return qp, np.ascontiguousarray(s).reshape(G, N16, KB, 64).astype(np.uint8)
+
+
+def unpack_int4(qp: np.ndarray) -> np.ndarray:
+    """Packed int4 weights (include/gmm.h, gmm_quantize_rhs_int4) -> codes
+    [G, K, N] int8.  qp: [G, N/16, K/128, 1024]; lane l of a slab holds
+    column l % 16 and rows 32*(l/16) + j, byte 4d + i carrying j = 8d + i in
+    its low nibble and j = 8d + 4 + i in its high one."""
+    G, N16, KB, _ = qp.shape
+    b = qp.reshape(G, N16, KB, 4, 16, 4, 4)                   # lane group, column, d, i
+    nib = np.stack([b & 15, b >> 4], axis=-2)                  # ..., d, half, i -> j = 8d + 4 half + i
+    v = ((nib.astype(np.int16) ^ 8) - 8).astype(np.int8).reshape(G, N16, KB, 4, 16, 32)
+    return np.ascontiguousarray(v.transpose(0, 2, 3, 5, 1, 4)).reshape(G, KB * 128, N16 * 16)
+
+
+def pack_int4(codes: np.ndarray) -> np.ndarray:
+    """Inverse of unpack_int4 (codes in [-8, 7])."""
+    G, K, N = codes.shape
+    KB, N16 = K // 128, N // 16
+    v = (codes.astype(np.int16) & 15).astype(np.uint8)
+    lanes = v.reshape(G, KB, 4, 32, N16, 16).transpose(0, 4, 1, 2, 5, 3)      # g nb kb lc lr j
+    parts = lanes.reshape(G, N16, KB, 4, 16, 4, 2, 4)                          # j = 8d + 4 half + i
+    byte = parts[..., 0, :] | (parts[..., 1, :] << 4)
+    return np.ascontiguousarray(byte).reshape(G, N16, KB, 1024).astype(np.uint8)

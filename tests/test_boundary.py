@@ -31,7 +31,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_symbols()
-    assert len(names) == 20
+    assert len(names) == 23
     assert sorted(names) == sorted(gmm.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
@@ -142,6 +142,44 @@ def test_quantize_mxfp4_rejections(lib):
     assert r(P(A), 0, 2, 128, 128, P(A), P(MIS), None) == ALIGN
 
 
+def i4(lib, lhs=A, lhs_dt=1, lhs_scale=0, rhs=A, rhs_scale=A, gs=A, M=256, K=256, N=256, G=4,
+       out=A, out_dt=1, ws=A, wsb=WSB):
+    return lib.gmm_fp8_int4_fwd(P(lhs), lhs_dt, P(lhs_scale), P(rhs), P(rhs_scale), P(gs), M, K,
+                                N, G, P(out), out_dt, P(ws), wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(lhs=0), NULL), (dict(rhs=0), NULL), (dict(rhs_scale=0), NULL), (dict(gs=0), NULL),
+    (dict(out=0), NULL), (dict(out=MIS), ALIGN), (dict(rhs_scale=MIS), ALIGN),
+    (dict(K=200), SHAPE), (dict(N=100), SHAPE), (dict(G=0), SHAPE), (dict(M=-1), SHAPE),
+    (dict(lhs_dt=2), NULL), (dict(lhs_scale=A), DTYPE), (dict(out_dt=2), DTYPE), (dict(lhs_dt=5), DTYPE),
+    (dict(M=0), OK), (dict(ws=0), WORKSPACE), (dict(ws=MIS), ALIGN), (dict(wsb=8), WORKSPACE),
+])
+def test_fp8_int4_fwd_rejections(lib, kw, status):
+    assert i4(lib, **kw) == status
+    if status:
+        assert lib.gmm_last_error()
+
+
+def test_int4_quantize_and_pack_rejections(lib):
+    r = lib.gmm_quantize_rhs_int4
+    assert r(P(A), 1, 2, 128, 200, P(A), P(A), None) == SHAPE
+    assert r(P(A), 1, 2, 100, 128, P(A), P(A), None) == SHAPE
+    assert r(P(A), 1, 0, 128, 128, P(A), P(A), None) == SHAPE
+    assert r(P(A), 2, 2, 128, 128, P(A), P(A), None) == DTYPE
+    assert r(P(A), 0, 2, 128, 128, None, P(A), None) == NULL
+    assert r(P(A), 0, 2, 128, 128, P(A), P(MIS), None) == ALIGN
+    p = lib.gmm_pack_rhs_int4
+    B = A + 0x100000
+    assert p(P(A), 2, 128, 200, P(B), None) == SHAPE
+    assert p(P(A), 2, 100, 128, P(B), None) == SHAPE
+    assert p(P(A), 0, 128, 128, P(B), None) == SHAPE
+    assert p(None, 2, 128, 128, P(B), None) == NULL
+    assert p(P(A), 2, 128, 128, P(MIS), None) == ALIGN
+    assert p(P(A), 2, 128, 128, P(A + 4096), None) == SHAPE       # packed overlaps q
+    assert b"overlaps" in lib.gmm_last_error()
+
+
 def test_quantize_rejections(lib):
     q = lib.gmm_quantize_lhs
     assert q(P(A), 1, 16, 100, P(A), P(A), None) == SHAPE
@@ -183,9 +221,9 @@ def test_metadata_rejections(lib):
 
 
 def test_workspace_bytes(lib):
-    for op in range(7):
+    for op in range(8):
         assert lib.gmm_workspace_bytes(op, 65536, 2048, 512, 256) == WSB
-    assert lib.gmm_workspace_bytes(7, 1, 128, 128, 1) == 0
+    assert lib.gmm_workspace_bytes(8, 1, 128, 128, 1) == 0
     assert lib.gmm_workspace_bytes(-1, 1, 128, 128, 1) == 0
     assert lib.gmm_status_string(WORKSPACE) == b"workspace missing or too small"
 
@@ -224,7 +262,7 @@ def test_binding_raises_on_error(lib):
 def test_tile_config_rejections(lib):
     c = gmm.TileConfig(kernel=1, waves=16)
     assert lib.gmm_set_tile_config(0, ctypes.byref(c)) == SHAPE      # metadata has no tiles
-    assert lib.gmm_set_tile_config(7, ctypes.byref(c)) == SHAPE
+    assert lib.gmm_set_tile_config(8, ctypes.byref(c)) == SHAPE
     bad = gmm.TileConfig(kernel=4)
     assert lib.gmm_set_tile_config(1, ctypes.byref(bad)) == SHAPE
     assert lib.gmm_get_tile_config(1, 256, 256, 256, 4, 1, 1, None) == NULL

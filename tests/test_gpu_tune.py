@@ -34,6 +34,9 @@ def oracle_reference(p: tune.Problem) -> np.ndarray:
     if p.phase == "mxfp4_fwd":
         q4, e8 = oracle.quantize_rhs_mxfp4(w)
         return oracle.gmm_fp8_mxfp4(ql, sl, q4, e8, gs)
+    if p.phase == "int4_fwd":
+        qi, si = oracle.quantize_rhs_int4(w)
+        return oracle.gmm_fp8_int4(ql, sl, qi, si, gs)
     qr, sr = oracle.quantize_rhs(w)
     if p.phase == "swiglu":
         return oracle.gmm_fp8_swiglu(ql, sl, qr, sr, gs)
@@ -45,6 +48,7 @@ CASES = [
     ("fp8_fwd", (8192, 512, 2048, 32)),
     ("fp8_fwd_prequant", (700, 512, 1024, 6)), ("fp8_fwd_prequant", (8192, 2048, 512, 32)),
     ("mxfp4_fwd", (700, 512, 1024, 6)), ("mxfp4_fwd", (8192, 2048, 512, 32)),
+    ("int4_fwd", (700, 512, 1024, 6)), ("int4_fwd", (8192, 2048, 512, 32)),
     ("swiglu", (700, 512, 512, 6)), ("swiglu", (8192, 2048, 512, 32)),
     ("bf16_fwd", (900, 256, 512, 6)), ("dx", (900, 256, 512, 6)), ("tgmm", (900, 256, 512, 6)),
     ("tgmm", (8192, 2048, 512, 32)),
