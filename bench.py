@@ -538,6 +538,15 @@ def main() -> int:
         ops["fp8_mxfp4_fwd"] = {"us": round(m_us, 3), "tflops": round(flops / (m_us * 1e-6) / 1e12, 2),
                                 "GB/s": round(mbytes / (m_us * 1e-6) / 1e9, 1),
                                 "frac_hbm": round(mbytes / (m_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+        # and against int4 weights (codes expanded to E4M3 in registers;
+        # 128x128 fp32 block scales): half the weight bytes of FP8
+        qi, si = gmm.gmm_quantize_rhs_int4(w)
+        i_us = graph_time_ms(lambda: gmm.gmm_fp8_int4_fwd(x, qi, si, gs, out=out4), 100, 10) * 1e3
+        ibytes = total * K * 2 + G * K * N // 2 + G * (K // 128) * (N // 128) * 4 + M * N * 2 + G * 4
+        ops["fp8_int4_fwd"] = {"us": round(i_us, 3), "tflops": round(flops / (i_us * 1e-6) / 1e12, 2),
+                               "GB/s": round(ibytes / (i_us * 1e-6) / 1e9, 1),
+                               "frac_hbm": round(ibytes / (i_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+        del q4, s4, qi, si
         # the other forward configurations: wo layer (K=512, N=2048; the
         # row-resident sweep) and the production shape (M=65536, G=256,
         # Zipf routing; 604 MB, beyond the 256 MB Infinity Cache)

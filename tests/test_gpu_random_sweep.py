@@ -1,7 +1,7 @@
 """Seeded random sweep of small grouped problems on the GPU against the oracle:
 random M, K, N, G, group-size patterns (empty groups, size-1 groups, one
 dominant group, rows past the total), LHS dtype and output dtype, for the
-FP8-weight and MXFP4-weight forwards.  In-kernel codes and scales bit for
+FP8-weight, MXFP4-weight and int4-weight forwards.  In-kernel codes and scales bit for
 bit (in the half of the FP8 cases that ask for them); outputs within |gpu - ref| <= 1e-3 max(1, rms(ref)) + 1e-2 |ref| and
 SQNR > 40 dB (the weights' scale is drawn up to N(0, 1), where outputs are
 ~20x those of the pages' normalised data, so the absolute term scales with
@@ -91,3 +91,19 @@ def test_mxfp4_forward_random(seed):
     o = to_np64(out)
     assert (o[int(wl.group_sizes.sum()):] == 0).all()
     assert_fp8_parity_scaled(o, ref, "random mxfp4 %d (M=%d K=%d N=%d G=%d)" % (seed, wl.M, wl.K, wl.N, wl.G))
+
+
+@pytest.mark.parametrize("seed", range(CASES))
+def test_int4_forward_random(seed):
+    wl, out_dtype = random_problem(seed)
+    qi, si = gmm.gmm_quantize_rhs_int4(wl.w.to(DEV))
+    gs = torch.from_numpy(wl.group_sizes).to(DEV)
+    out = torch.full((wl.M, wl.N), float("nan"), dtype=out_dtype, device=DEV)
+    gmm.gmm_fp8_int4_fwd(wl.x.to(DEV), qi, si, gs, out=out)
+    torch.cuda.synchronize()
+    ql, sl = oracle.quantize_lhs(workloads.as_f32(wl.x))
+    oq, osr = oracle.quantize_rhs_int4(workloads.as_f32(wl.w))
+    ref = oracle.gmm_fp8_int4(ql, sl, oq, osr, wl.group_sizes)
+    o = to_np64(out)
+    assert (o[int(wl.group_sizes.sum()):] == 0).all()
+    assert_fp8_parity_scaled(o, ref, "random int4 %d (M=%d K=%d N=%d G=%d)" % (seed, wl.M, wl.K, wl.N, wl.G))
