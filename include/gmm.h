@@ -123,7 +123,10 @@ GMM_API size_t gmm_workspace_bytes(int op, int64_t M, int64_t K, int64_t N, int6
  *   bf16 calls (GMM_OP_BF16_FWD, _TGMM, _DX): residency 2 or 3 (workgroups
  *     per CU the register allocation allows); tgmm placement 1 (each XCD
  *     takes whole groups) or 2 (every group spread over the 8 XCDs, groups
- *     in decreasing size class; needs a multiple of 8 tiles per group).
+ *     in decreasing size class; needs a multiple of 8 tiles per group);
+ *     forward and dX placement 1 (128-row tiles aligned to absolute rows)
+ *     or 2 (tiles starting at each group's first row: no tile straddles
+ *     two groups).
  */
 typedef struct {
     int32_t kernel, waves, tile_m, tile_n, depth, residency, placement;

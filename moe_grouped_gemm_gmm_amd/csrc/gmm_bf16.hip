@@ -315,13 +315,15 @@ __global__ __launch_bounds__(256, MINB) void bf16_gemm_kernel(
         const int w = L / ntiles_c;
         c0 = (L % ntiles_c) * kT;
         if (wave == 0) {
-            const WorkItem it = find_work_item(group_sizes, G, M, kT, w);
+            // placement 2: row tiles start at each group's first row
+            const WorkItem it = placement == 2 ? find_work_item<true>(group_sizes, G, M, kT, w)
+                                               : find_work_item(group_sizes, G, M, kT, w);
             if (lane == 0) { s_info[0] = it.g; s_info[1] = it.tile; s_info[2] = it.lo; s_info[3] = it.hi; }
         }
         __syncthreads();
         g = s_info[0];
         if (g < 0) return;
-        row0 = s_info[1] * kT;
+        row0 = s_info[1] < 0 ? s_info[2] : s_info[1] * kT;
         lo = s_info[2];
         hi = s_info[3];
         red_lo = 0;

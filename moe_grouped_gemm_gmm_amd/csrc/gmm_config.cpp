@@ -183,8 +183,15 @@ bool resolve_bf16(int op, const TileConfig& f, int64_t M, int64_t K, int64_t N, 
         if (f.placement == 2 && ((K / 128) * (N / 128)) % 8 != 0)
             return fail(why, "spreading a group over the XCDs needs a multiple of 8 tiles per group");
         c->placement = f.placement;   // 0: decided in the kernel from the group sizes
-    } else if (f.placement) {
-        return fail(why, "placement applies to tgmm");
+    } else {
+        // forward and dX: 1 row tiles aligned to absolute rows, 2 row tiles
+        // starting at each group's first row.  Group-start tiles leave fewer
+        // partly used tiles, which pays once the grid takes more than two
+        // rounds of the chip at three workgroups per CU (measured: production
+        // shape dX 284 -> 275 us, forward 264 -> 257 us; at the backward shape
+        // the same or 0.5% slower)
+        if (f.placement && f.placement != 1 && f.placement != 2) return fail(why, "placement is 1 or 2");
+        c->placement = f.placement ? f.placement : (nblocks > 6 * (int64_t)device_cus() ? 2 : 1);
     }
     return true;
 }

@@ -26,7 +26,8 @@ struct TileConfig {
     int residency;  // bf16: workgroups per CU the registers allow (2, 3)
     int placement;  // warp-specialised FP8: 1 consecutive items per XCD, 2 each group's items
                     // on one XCD; tgmm: 1 groups contiguous per XCD, 2 spread over XCDs by
-                    // size class
+                    // size class; bf16 forward and dX: 1 row tiles aligned to absolute rows,
+                    // 2 row tiles starting at each group's first row
 };
 
 // The override set for op (all zero when none); set_tile_override(op, NULL)

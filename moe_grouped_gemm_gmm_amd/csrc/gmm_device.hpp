@@ -252,12 +252,21 @@ struct WorkItem {
     int g, tile, lo, hi;
 };
 
+// GROUP_TILES: tiles start at each group's first row instead (group g's
+// rows [o, o + s) give ceil(s / tm) items [o + t tm, min(o + s, o + (t+1) tm)),
+// the rows past the total ceil((M - total) / tm) more from `total` on), so
+// no item straddles a tile boundary: fewer items with partly used rows
+// (about half a tile fewer per group).  `tile` is then -1 and the item's
+// rows start at `lo`.  Both mappings give at most max_work_items items.
+template <bool GROUP_TILES = false>
 __device__ __forceinline__ WorkItem find_work_item(const int32_t* __restrict__ group_sizes, int G,
                                                    int M, int tm, int w) {
     int carry_rows = 0, carry_items = 0;
     for (int base = 0; base < G; base += 64) {
         const GroupChunk ch = group_chunk(group_sizes, G, M, base, carry_rows);
-        const int c = ch.hi > ch.lo ? (ch.hi - 1) / tm - ch.lo / tm + 1 : 0;
+        const int c = ch.hi > ch.lo ? (GROUP_TILES ? (ch.hi - ch.lo + tm - 1) / tm
+                                                   : (ch.hi - 1) / tm - ch.lo / tm + 1)
+                                    : 0;
         const int inclc = wave_incl_scan(c);
         const int W = carry_items + inclc - c;
         const bool own = c > 0 && w >= W && w < W + c;
@@ -267,12 +276,18 @@ __device__ __forceinline__ WorkItem find_work_item(const int32_t* __restrict__ g
             const int glo = lane_value(ch.lo, src);
             const int ghi = lane_value(ch.hi, src);
             const int gW = lane_value(W, src);
-            const int t = glo / tm + (w - gW);
             WorkItem it;
             it.g = base + src;
-            it.tile = t;
-            it.lo = max(glo, t * tm);
-            it.hi = min(ghi, (t + 1) * tm);
+            if constexpr (GROUP_TILES) {
+                it.tile = -1;
+                it.lo = glo + (w - gW) * tm;
+                it.hi = min(ghi, it.lo + tm);
+            } else {
+                const int t = glo / tm + (w - gW);
+                it.tile = t;
+                it.lo = max(glo, t * tm);
+                it.hi = min(ghi, (t + 1) * tm);
+            }
             return it;
         }
         carry_rows = ch.next_carry;
@@ -280,11 +295,17 @@ __device__ __forceinline__ WorkItem find_work_item(const int32_t* __restrict__ g
     }
     WorkItem it;
     const int total = min(carry_rows, M);
-    const int t = total / tm + (w - carry_items);
     it.g = G;
-    it.tile = t;
-    it.lo = max(total, t * tm);
-    it.hi = min(M, (t + 1) * tm);
+    if constexpr (GROUP_TILES) {
+        it.tile = -1;
+        it.lo = total + (w - carry_items) * tm;
+        it.hi = min(M, it.lo + tm);
+    } else {
+        const int t = total / tm + (w - carry_items);
+        it.tile = t;
+        it.lo = max(total, t * tm);
+        it.hi = min(M, (t + 1) * tm);
+    }
     if (it.lo >= it.hi) it.g = -1;
     return it;
 }

@@ -18,7 +18,8 @@ gmm_set_tile_config (include/gmm.h):
   mxfp4_fwd                  warp-specialised tile_n 512/256/128, row-resident
   int4_fwd                   warp-specialised tile_n 512/256/128
   swiglu                     tile_m 48/64
-  bf16_fwd, dx               residency 2/3 workgroups per CU
+  bf16_fwd, dx               residency 2/3 workgroups per CU x row tiles aligned to
+                             absolute rows or to each group's first row
   tgmm                       residency 2/3 x placement (whole groups per XCD,
                              groups spread over the XCDs)
 
@@ -96,7 +97,8 @@ def space(phase: str) -> List[Dict[str, int]]:
                 out.append({"residency": res, "placement": pl})
     else:
         for res in (2, 3):
-            out.append({"residency": res})
+            for pl in (1, 2):
+                out.append({"residency": res, "placement": pl})
     return out
 
 

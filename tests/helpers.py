@@ -139,3 +139,21 @@ def pack_int4(codes: np.ndarray) -> np.ndarray:
     parts = lanes.reshape(G, N16, KB, 4, 16, 4, 2, 4)                          # j = 8d + 4 half + i
     byte = parts[..., 0, :] | (parts[..., 1, :] << 4)
     return np.ascontiguousarray(byte).reshape(G, N16, KB, 1024).astype(np.uint8)
+
+
+class tile_config:
+    """Context manager: a tile configuration override for one op, restored
+    to the library's choice on exit (cfg None or {} keeps the default)."""
+
+    def __init__(self, op: int, cfg):
+        self.op, self.cfg = op, cfg
+
+    def __enter__(self):
+        import moe_grouped_gemm_gmm_amd as gmm
+        gmm.set_tile_config(self.op, self.cfg or None)
+        return self
+
+    def __exit__(self, *exc):
+        import moe_grouped_gemm_gmm_amd as gmm
+        gmm.set_tile_config(self.op, None)
+        return False

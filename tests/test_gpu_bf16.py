@@ -8,7 +8,7 @@ import torch
 import moe_grouped_gemm_gmm_amd as gmm
 import oracle
 import workloads
-from helpers import assert_bf16_parity, to_np64
+from helpers import assert_bf16_parity, tile_config, to_np64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -30,10 +30,13 @@ def _gs(wl):
 
 @pytest.mark.parametrize("M,K,N,gs", EDGE)
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
-def test_bf16_fwd_edges(M, K, N, gs, out_dtype):
+@pytest.mark.parametrize("placement", [1, 2])
+def test_bf16_fwd_edges(M, K, N, gs, out_dtype, placement):
+    """placement 2: row tiles start at each group's first row."""
     wl = workloads.custom(M, K, N, gs, seed=M + 3 * K, w_std=0.05)
     out = torch.full((M, N), float("nan"), dtype=out_dtype, device=DEV)
-    gmm.gmm_bf16_fwd(wl.x.to(DEV), wl.w.to(DEV), _gs(wl), out=out)
+    with tile_config(gmm.OP_BF16_FWD, {"placement": placement}):
+        gmm.gmm_bf16_fwd(wl.x.to(DEV), wl.w.to(DEV), _gs(wl), out=out)
     ref = oracle.gmm(workloads.as_f32(wl.x), workloads.as_f32(wl.w), wl.group_sizes)
     o = to_np64(out)
     assert (o[int(wl.group_sizes.sum()):] == 0).all()
@@ -42,10 +45,12 @@ def test_bf16_fwd_edges(M, K, N, gs, out_dtype):
 
 @pytest.mark.parametrize("M,K,N,gs", EDGE)
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
-def test_dx_edges(M, K, N, gs, out_dtype):
+@pytest.mark.parametrize("placement", [1, 2])
+def test_dx_edges(M, K, N, gs, out_dtype, placement):
     wl = workloads.custom(M, K, N, gs, seed=M + 5 * K, w_std=0.05, with_dy=True)
     out = torch.full((M, K), float("nan"), dtype=out_dtype, device=DEV)
-    gmm.gmm_bf16_dx(wl.dy.to(DEV), wl.w.to(DEV), _gs(wl), out=out)
+    with tile_config(gmm.OP_DX, {"placement": placement}):
+        gmm.gmm_bf16_dx(wl.dy.to(DEV), wl.w.to(DEV), _gs(wl), out=out)
     ref = oracle.gmm_dx(workloads.as_f32(wl.dy), workloads.as_f32(wl.w), wl.group_sizes)
     o = to_np64(out)
     assert (o[int(wl.group_sizes.sum()):] == 0).all()
@@ -143,14 +148,16 @@ def test_tgmm_many_groups_mixed_sizes_every_group_written():
 
 
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
-def test_dx_straddling_tiles_ragged_tail(out_dtype):
+@pytest.mark.parametrize("placement", [1, 2])
+def test_dx_straddling_tiles_ragged_tail(out_dtype, placement):
     """dX over several 128-row tiles with straddling groups, a ragged tail and
     K spanning several column tiles; rows past the total are zero."""
     gs = [70, 0, 129, 200, 1, 0, 33]
     M = int(sum(gs)) + 50
     wl = workloads.custom(M, 512, 384, gs, seed=123, w_std=0.05, with_dy=True)
     out = torch.full((M, 512), float("nan"), dtype=out_dtype, device=DEV)
-    gmm.gmm_bf16_dx(wl.dy.to(DEV), wl.w.to(DEV), _gs(wl), out=out)
+    with tile_config(gmm.OP_DX, {"placement": placement}):
+        gmm.gmm_bf16_dx(wl.dy.to(DEV), wl.w.to(DEV), _gs(wl), out=out)
     ref = oracle.gmm_dx(workloads.as_f32(wl.dy), workloads.as_f32(wl.w), wl.group_sizes)
     o = to_np64(out)
     assert (o[int(sum(gs)):] == 0).all()

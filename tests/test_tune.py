@@ -22,6 +22,7 @@ def test_space_and_names():
     assert {(c["tile_m"], c["tile_n"]) for c in fp8 if c.get("kernel") == 2} == {
         (m, n) for m in (48, 64) for n in (128, 256, 512)}
     assert [c.get("placement") for c in tune.space("tgmm")] == [None, 1, 2, 1, 2]
+    assert [c.get("placement") for c in tune.space("dx")] == [None, 1, 2, 1, 2]
     with pytest.raises(ValueError):
         tune.space("nope")
 
@@ -55,9 +56,11 @@ def test_library_default_choices():
     assert nz(gmm.get_tile_config(F, 65536, 2048, 512, 256)) == {"kernel": 2, "tile_m": 64, "tile_n": 512}
     assert nz(gmm.get_tile_config(S, 8192, 2048, 512, 32)) == {"kernel": 2, "tile_m": 48, "tile_n": 256}
     assert nz(gmm.get_tile_config(X, 8192, 2048, 512, 32))["kernel"] == 1
-    assert nz(gmm.get_tile_config(B, 8192, 2048, 512, 32)) == {"residency": 2}
+    assert nz(gmm.get_tile_config(B, 8192, 2048, 512, 32)) == {"residency": 2, "placement": 1}
     assert nz(gmm.get_tile_config(T, 65536, 2048, 512, 256)) == {"residency": 3}
-    assert nz(gmm.get_tile_config(D, 8192, 2048, 512, 32)) == {"residency": 3}
+    assert nz(gmm.get_tile_config(D, 8192, 2048, 512, 32)) == {"residency": 3, "placement": 2}
+    assert nz(gmm.get_tile_config(D, 65536, 2048, 512, 256)) == {"residency": 3, "placement": 2}
+    assert nz(gmm.get_tile_config(B, 65536, 2048, 512, 256)) == {"residency": 3, "placement": 2}
 
 
 def test_set_tile_config_checks_fields_and_fit():
