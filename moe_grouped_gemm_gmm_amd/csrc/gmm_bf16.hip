@@ -457,10 +457,274 @@ __global__ __launch_bounds__(256, MINB) void bf16_gemm_kernel(
     }
 }
 
+// ------------------------------------------------------------ wide tiles --
+// The same three products on 256x256 output tiles: 8 waves (2 x 4), each
+// owning 128 x 64 (8 x 4 MFMA blocks, 128 fp32 accumulators), one workgroup
+// per CU.  Each 64-deep step stages 32 KB of each operand, as the 128 x 128
+// tile does, for four times the MFMA work: half the L2 reads and LDS writes
+// per FLOP, and a quarter fewer LDS reads (128 x 64 wave tiles).  Rows of
+// the forward and dX come in 256-row items that start at each group's first
+// row; tgmm's tiles are (256 K) x (256 N) per group.  Needs the tile's
+// column count (N forward, K dX, K and N tgmm) to be a multiple of 256.
+constexpr int kTW = 256;                      // wide tile (rows and cols)
+constexpr int kPadTW = 16;                    // transposed [64][256] rows of 544 bytes: rows
+                                              // 4 apart land 32 banks apart, as with 288 bytes
+constexpr int kWideDirect = kTW * (kR + kPadD);       // bf16 elements of a direct [256][64] tile
+constexpr int kWideTrans = kR * (kTW + kPadTW);       // of a transposed [64][256] tile
+constexpr int kWideElems = kWideDirect > kWideTrans ? kWideDirect : kWideTrans;
+
+// Chunks of a 256-row direct or 256-column transposed slice per thread.
+template <int NWV>
+struct WideSlice {
+    static constexpr int kThreads = 64 * NWV;
+    static constexpr int kChunks = 2048 / kThreads;   // 16-byte chunks per thread and operand
+    // Direct [256][64]: instruction c of wave w covers the rows direct_row
+    // gives for combo kChunks*w + c (combos 0..31 tile the 256 rows).
+    __device__ static int direct_row(int c) {
+        const int t = threadIdx.x, combo = (t >> 6) * kChunks + c, q = (t & 63) >> 3;
+        return 16 * (combo >> 1) + 4 * (combo & 1) + (q >> 1) + 8 * (q & 1);
+    }
+    // Transposed [64][256]: chunk c*kThreads + t is row (c*kThreads + t)/32,
+    // chunk t%32 (a 16-lane group writes 256 contiguous bytes).
+    __device__ static int trans_row(int c) { return (c * kThreads + (int)threadIdx.x) >> 5; }
+    __device__ static int trans_chunk() { return threadIdx.x & 31; }
+};
+
+// NWV waves as 2 x NWV/2.  Launched with 8 waves of 128 x 64 (128
+// accumulators each, two waves per SIMD).  4 waves of 128 x 128 (256
+// accumulators, one wave per SIMD) compile, but the compiler then moves the
+// accumulators between VGPRs and AGPRs inside the K loop (over 800 copies),
+// so that form is not launched.
+template <int MODE, bool OUT_BF16, int NWV>
+__global__ __launch_bounds__(64 * NWV, 1) void bf16_wide_kernel(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
+    const int32_t* __restrict__ group_sizes, int M, int K, int N, int G, void* __restrict__ out,
+    int ntiles_c, int ntiles_r, int nblocks, int placement, int32_t* __restrict__ status) {
+    using WS = WideSlice<NWV>;
+    constexpr int kThr = WS::kThreads, CH = WS::kChunks;
+    constexpr int NJ = 256 / (NWV / 2) / 16;        // 16-column blocks per wave (4 or 8)
+    constexpr int WC = 16 * NJ;                     // wave tile columns (64 or 128)
+    constexpr bool A_TR = MODE == kTgmm;
+    constexpr bool B_TR = MODE != kDx;
+    constexpr bool kSpread = A_TR && B_TR;
+    constexpr int SA = A_TR ? kTW + kPadTW : kR + kPadD;   // LDS row pitches (elements)
+    constexpr int SB = B_TR ? kTW + kPadTW : kR + kPadD;
+    __shared__ __attribute__((aligned(16))) uint16_t sA[kWideElems];
+    __shared__ __attribute__((aligned(16))) uint16_t sB[kWideElems];
+    __shared__ int s_info[4];
+
+    const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+    const int L = xcd_remap(blockIdx.x, nblocks);
+    const int out_cols = MODE == kDx ? K : N;
+    if (wave == 1 && blockIdx.x == 0) {   // the call's device status word
+        const int st = group_status(group_sizes, G, M);
+        if (lane == 0) status[0] = st;
+    }
+
+    int g, row0, lo, hi, c0, red_lo, red_hi;
+    if constexpr (MODE == kTgmm) {
+        if (wave == 0) {
+            const TgmmTile tt = tgmm_tile(group_sizes, G, M, ntiles_r * ntiles_c, L, placement);
+            if (lane == 0) { s_info[0] = tt.row_lo; s_info[1] = tt.row_hi; s_info[2] = tt.g; s_info[3] = tt.t; }
+        }
+        __syncthreads();
+        red_lo = s_info[0];
+        red_hi = s_info[1];
+        g = s_info[2];
+        if (g < 0) return;
+        row0 = (s_info[3] / ntiles_c) * kTW;   // k tile
+        c0 = (s_info[3] % ntiles_c) * kTW;     // n tile
+        lo = row0;
+        hi = row0 + kTW;
+    } else {
+        const int w = L / ntiles_c;
+        c0 = (L % ntiles_c) * kTW;
+        if (wave == 0) {
+            const WorkItem it = find_work_item<true>(group_sizes, G, M, kTW, w);
+            if (lane == 0) { s_info[0] = it.g; s_info[1] = it.lo; s_info[2] = it.hi; }
+        }
+        __syncthreads();
+        g = s_info[0];
+        if (g < 0) return;
+        lo = s_info[1];
+        hi = s_info[2];
+        row0 = lo;
+        red_lo = 0;
+        red_hi = MODE == kFwd ? K : N;
+        if (g == G) {  // rows past the last group: zeros
+            const int rows = hi - lo;
+            for (int e = tid; e < rows * (kTW / 8); e += kThr) {
+                const int r = lo + e / (kTW / 8), c = c0 + (e % (kTW / 8)) * 8;
+                if constexpr (OUT_BF16)
+                    *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + (int64_t)r * out_cols + c) = make_uint4(0, 0, 0, 0);
+                else {
+                    float4* p = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + (int64_t)r * out_cols + c);
+                    p[0] = make_float4(0, 0, 0, 0);
+                    p[1] = make_float4(0, 0, 0, 0);
+                }
+            }
+            return;
+        }
+    }
+
+    const int wm = wave / (NWV / 2), wn = wave % (NWV / 2);
+    const int lr = lane & 15, lg = lane >> 4;
+    v4f acc[8][NJ];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    // Global -> registers for reduction range [r0, r0 + 64), as in the
+    // 128 x 128 kernel (clamped in-bounds rows; tgmm rows past the group's
+    // end zeroed when written to LDS).
+    const int lda = MODE == kFwd ? K : N;
+    const uint16_t* wg = B + (int64_t)(MODE == kTgmm ? 0 : g) * K * N;
+    const int dch = direct_chunk() * 8, tch = WS::trans_chunk() * 8;
+    u32x4 fa[CH], fb[CH];
+    auto fetch = [&](int r0) {
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            if constexpr (MODE == kTgmm) {
+                const int m = min(r0 + WS::trans_row(c), red_hi - 1);
+                fa[c] = *reinterpret_cast<const u32x4*>(A + (int64_t)m * K + row0 + tch);   // x[m][k0..]
+                fb[c] = *reinterpret_cast<const u32x4*>(B + (int64_t)m * N + c0 + tch);     // dy[m][n0..]
+            } else {
+                const int arow = min(max(row0 + WS::direct_row(c), lo), hi - 1);
+                fa[c] = *reinterpret_cast<const u32x4*>(A + (int64_t)arow * lda + r0 + dch);
+                if constexpr (MODE == kFwd)   // w[g][k][n0..]
+                    fb[c] = *reinterpret_cast<const u32x4*>(wg + (int64_t)(r0 + WS::trans_row(c)) * N + c0 + tch);
+                else                          // w[g][k0+c][n]
+                    fb[c] = *reinterpret_cast<const u32x4*>(wg + (int64_t)(c0 + WS::direct_row(c)) * N + r0 + dch);
+            }
+        }
+    };
+    auto put = [&](uint16_t* tile, const u32x4* f, bool trans, int r0) {
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            if (trans) {
+                const int r = WS::trans_row(c);
+                const bool valid = MODE != kTgmm || r0 + r < red_hi;
+                *reinterpret_cast<u32x4*>(tile + r * (kTW + kPadTW) + WS::trans_chunk() * 8) =
+                    valid ? f[c] : u32x4{0u, 0u, 0u, 0u};
+            } else {
+                *reinterpret_cast<u32x4*>(tile + WS::direct_row(c) * (kR + kPadD) + direct_chunk() * 8) = f[c];
+            }
+        }
+    };
+
+    if (red_lo < red_hi) fetch(red_lo);
+    for (int r0 = red_lo; r0 < red_hi; r0 += kR) {
+        put(sA, fa, A_TR, r0);
+        put(sB, fb, B_TR, r0);
+        __syncthreads();
+        if (r0 + kR < red_hi) fetch(r0 + kR);
+#pragma unroll
+        for (int s = 0; s < kR / 32; ++s) {
+            v8bf bf[NJ], af[8];
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                if constexpr (B_TR)
+                    bf[j] = read_tr<kSpread>(sB, SB, s, lg, wn * WC + j * 16, lr);
+                else
+                    bf[j] = read_direct(sB, SB, wn * WC + j * 16 + lr, s * 32 + lg * 8);
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                if constexpr (A_TR)
+                    af[i] = read_tr<kSpread>(sA, SA, s, lg, wm * 128 + i * 16, lr);
+                else
+                    af[i] = read_direct(sA, SA, wm * 128 + i * 16 + lr, s * 32 + lg * 8);
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int j = 0; j < NJ; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
+        }
+        __syncthreads();
+    }
+
+    // ---- epilogue.  Lane (lr, lg) of block (i, j) holds row 16i + lr and
+    //      columns 16j + 4lg .. +3 of the wave's 128 x WC block.  bf16:
+    //      staged through LDS by RW waves at a time (128 rows of WC + 8
+    //      elements each) and stored as whole rows; fp32: one 16-byte store
+    //      per lane and block.  Rows outside [lo, hi) skipped.
+    const int64_t obase = MODE == kTgmm ? (int64_t)g * K * N : 0;
+    const int col0 = c0 + wn * WC;
+    if constexpr (OUT_BF16) {
+        constexpr int kEpiRow = WC + 8;
+        constexpr int RW = NWV == 8 ? 4 : 2;             // waves staging per round
+        static_assert((RW / 2) * 128 * kEpiRow <= kWideElems, "a round's staging fits the LDS tiles");
+        constexpr int LPR = WC * 2 / 16;                 // lanes per staged row on the way out
+        constexpr int RPP = 64 / LPR;                    // rows per pass
+#pragma unroll
+        for (int round = 0; round < NWV / RW; ++round) {
+            if (wave / RW == round) {
+                const int r = wave % RW;
+                uint16_t* ep = (r < RW / 2 ? sA : sB) + (r % (RW / 2)) * 128 * kEpiRow;
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+#pragma unroll
+                    for (int j = 0; j < NJ; ++j)
+                        *reinterpret_cast<uint2*>(ep + (16 * i + lr) * kEpiRow + 16 * j + 4 * lg) =
+                            make_uint2(pack_bf16x2(acc[i][j][0], acc[i][j][1]), pack_bf16x2(acc[i][j][2], acc[i][j][3]));
+                __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+                const int orow = lane / LPR, ocol = (lane % LPR) * 8;
+#pragma unroll
+                for (int q = 0; q < 128 / RPP; ++q) {
+                    const int rr = RPP * q + orow;
+                    const uint4 v = *reinterpret_cast<const uint4*>(ep + rr * kEpiRow + ocol);
+                    const int row = row0 + wm * 128 + rr;
+                    if (row >= lo && row < hi)
+                        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + obase + (int64_t)row * out_cols + col0 + ocol) = v;
+                }
+            }
+            if (round + 1 < NWV / RW) __syncthreads();   // this round's staging read before reuse
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int row = row0 + wm * 128 + i * 16 + lr;
+            if (row < lo || row >= hi) continue;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+                *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + obase + (int64_t)row * out_cols + col0 + 16 * j + 4 * lg) =
+                    make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+        }
+    }
+}
+
+template <int MODE, int NWV>
+hipError_t launch_wide(const void* A, const void* B, const int32_t* group_sizes, int M, int K, int N, int G,
+                       void* out, bool out_bf16, int placement, int32_t* status, hipStream_t stream) {
+    int ntiles_c, ntiles_r = 0;
+    int64_t nblocks;
+    if constexpr (MODE == kTgmm) {
+        ntiles_r = K / kTW;
+        ntiles_c = N / kTW;
+        nblocks = (int64_t)G * ntiles_r * ntiles_c;
+    } else {
+        ntiles_c = (MODE == kFwd ? N : K) / kTW;
+        nblocks = max_work_items(M, G, kTW) * ntiles_c;
+    }
+    const uint16_t* a = reinterpret_cast<const uint16_t*>(A);
+    const uint16_t* b = reinterpret_cast<const uint16_t*>(B);
+    if (out_bf16)
+        hipLaunchKernelGGL((bf16_wide_kernel<MODE, true, NWV>), dim3((unsigned)nblocks), dim3(64 * NWV), 0, stream,
+                           a, b, group_sizes, M, K, N, G, out, ntiles_c, ntiles_r, (int)nblocks, placement, status);
+    else
+        hipLaunchKernelGGL((bf16_wide_kernel<MODE, false, NWV>), dim3((unsigned)nblocks), dim3(64 * NWV), 0, stream,
+                           a, b, group_sizes, M, K, N, G, out, ntiles_c, ntiles_r, (int)nblocks, placement, status);
+    return hipGetLastError();
+}
+
 template <int MODE>
 hipError_t launch_mode(const TileConfig& cfg, const void* A, const void* B,
                        const int32_t* group_sizes, int M, int K, int N, int G, void* out,
                        bool out_bf16, int32_t* status, hipStream_t stream) {
+    if (cfg.kernel == 2)
+        return launch_wide<MODE, 8>(A, B, group_sizes, M, K, N, G, out, out_bf16, cfg.placement, status, stream);
     int ntiles_c, ntiles_r = 0;
     int64_t nblocks;
     if constexpr (MODE == kTgmm) {

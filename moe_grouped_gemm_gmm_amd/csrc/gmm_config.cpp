@@ -172,8 +172,31 @@ bool resolve_swiglu(const TileConfig& f, int64_t M, int64_t N, int64_t G, TileCo
 bool resolve_bf16(int op, const TileConfig& f, int64_t M, int64_t K, int64_t N, int64_t G,
                   TileConfig* c, const char** why) {
     *c = TileConfig{};
-    if (f.kernel || f.waves || f.tile_m || f.tile_n || f.depth)
-        return fail(why, "the bf16 calls set residency (and tgmm placement) only");
+    if (f.waves || f.tile_m || f.tile_n || f.depth)
+        return fail(why, "the bf16 calls set kernel, residency and placement only");
+    if (f.kernel && f.kernel != 1 && f.kernel != 2) return fail(why, "bf16 kernels are 1 (128 x 128) or 2 (256 x 256)");
+    if (f.kernel == 2) {
+        // 256 x 256 tiles, 8 waves, one workgroup per CU; forward and dX rows
+        // in items starting at each group's first row
+        const int64_t cols = op == kOpTgmm ? K : (op == kOpDx ? K : N);
+        if (cols % 256 != 0 || (op == kOpTgmm && N % 256 != 0))
+            return fail(why, "256 x 256 tiles need the tiled dimensions to be multiples of 256");
+        if (f.residency && f.residency != 1) return fail(why, "the 256 x 256 kernel runs one workgroup per CU");
+        c->kernel = 2;
+        c->waves = 8;
+        c->residency = 1;
+        if (op == kOpTgmm) {
+            if (f.placement && f.placement != 1 && f.placement != 2) return fail(why, "placement is 1 or 2");
+            if (f.placement == 2 && ((K / 256) * (N / 256)) % 8 != 0)
+                return fail(why, "spreading a group over the XCDs needs a multiple of 8 tiles per group");
+            c->placement = f.placement;
+        } else {
+            if (f.placement && f.placement != 2) return fail(why, "the 256 x 256 kernel starts tiles at each group");
+            c->placement = 2;
+        }
+        return true;
+    }
+    c->kernel = 1;
     if (f.residency && f.residency != 2 && f.residency != 3) return fail(why, "residency is 2 or 3");
     const int64_t nblocks = op == kOpTgmm ? G * (K / 128) * (N / 128)
                                           : items(M, G, 128) * ((op == kOpDx ? K : N) / 128);

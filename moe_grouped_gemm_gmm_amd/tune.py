@@ -18,10 +18,12 @@ gmm_set_tile_config (include/gmm.h):
   mxfp4_fwd                  warp-specialised tile_n 512/256/128, row-resident
   int4_fwd                   warp-specialised tile_n 512/256/128
   swiglu                     tile_m 48/64
-  bf16_fwd, dx               residency 2/3 workgroups per CU x row tiles aligned to
-                             absolute rows or to each group's first row
-  tgmm                       residency 2/3 x placement (whole groups per XCD,
-                             groups spread over the XCDs)
+  bf16_fwd, dx               128 x 128 tiles: residency 2/3 workgroups per CU x row
+                             tiles aligned to absolute rows or to each group's first
+                             row; 256 x 256 tiles (8 waves, one workgroup per CU)
+  tgmm                       128 x 128 tiles: residency 2/3 x placement (whole groups
+                             per XCD, groups spread over the XCDs); 256 x 256 tiles x
+                             placement
 
 The space is small enough to enumerate, so the search is exhaustive rather
 than evolutionary.  Stages (Q9.4):
@@ -95,10 +97,13 @@ def space(phase: str) -> List[Dict[str, int]]:
         for res in (2, 3):
             for pl in (1, 2):
                 out.append({"residency": res, "placement": pl})
+        for pl in (1, 2):
+            out.append({"kernel": 2, "placement": pl})
     else:
         for res in (2, 3):
             for pl in (1, 2):
                 out.append({"residency": res, "placement": pl})
+        out.append({"kernel": 2})
     return out
 
 

@@ -21,8 +21,9 @@ def test_space_and_names():
     assert {c.get("placement") for c in fp8 if c.get("kernel") == 1} == {None, 2}
     assert {(c["tile_m"], c["tile_n"]) for c in fp8 if c.get("kernel") == 2} == {
         (m, n) for m in (48, 64) for n in (128, 256, 512)}
-    assert [c.get("placement") for c in tune.space("tgmm")] == [None, 1, 2, 1, 2]
-    assert [c.get("placement") for c in tune.space("dx")] == [None, 1, 2, 1, 2]
+    assert [c.get("placement") for c in tune.space("tgmm")] == [None, 1, 2, 1, 2, 1, 2]
+    assert [c.get("placement") for c in tune.space("dx")] == [None, 1, 2, 1, 2, None]
+    assert {c.get("kernel") for c in tune.space("dx")} == {None, 2}
     with pytest.raises(ValueError):
         tune.space("nope")
 
@@ -39,6 +40,9 @@ def test_candidates_follow_the_shape():
     assert "kernel=3" in mx and "kernel=1,tile_n=512" in mx
     tg = {tune.config_name(c) for c in tune.candidates("tgmm", (700, 256, 256, 6))}
     assert "placement=2,residency=3" not in tg         # 4 tiles per group cannot spread over 8 XCDs
+    assert "kernel=2,placement=1" in tg and "kernel=2,placement=2" not in tg
+    dx = {tune.config_name(c) for c in tune.candidates("dx", (700, 384, 256, 6))}
+    assert "kernel=2" not in dx                        # 256 x 256 tiles need K % 256 == 0
     assert "placement=1,residency=2" in tg
 
 
@@ -56,11 +60,12 @@ def test_library_default_choices():
     assert nz(gmm.get_tile_config(F, 65536, 2048, 512, 256)) == {"kernel": 2, "tile_m": 64, "tile_n": 512}
     assert nz(gmm.get_tile_config(S, 8192, 2048, 512, 32)) == {"kernel": 2, "tile_m": 48, "tile_n": 256}
     assert nz(gmm.get_tile_config(X, 8192, 2048, 512, 32))["kernel"] == 1
-    assert nz(gmm.get_tile_config(B, 8192, 2048, 512, 32)) == {"residency": 2, "placement": 1}
-    assert nz(gmm.get_tile_config(T, 65536, 2048, 512, 256)) == {"residency": 3}
-    assert nz(gmm.get_tile_config(D, 8192, 2048, 512, 32)) == {"residency": 3, "placement": 2}
-    assert nz(gmm.get_tile_config(D, 65536, 2048, 512, 256)) == {"residency": 3, "placement": 2}
-    assert nz(gmm.get_tile_config(B, 65536, 2048, 512, 256)) == {"residency": 3, "placement": 2}
+    assert nz(gmm.get_tile_config(B, 8192, 2048, 512, 32)) == {"kernel": 1, "residency": 2, "placement": 1}
+    assert nz(gmm.get_tile_config(T, 65536, 2048, 512, 256)) == {"kernel": 1, "residency": 3}
+    assert nz(gmm.get_tile_config(D, 8192, 2048, 512, 32)) == {"kernel": 1, "residency": 3, "placement": 2}
+    assert nz(gmm.get_tile_config(D, 65536, 2048, 512, 256)) == {"kernel": 1, "residency": 3, "placement": 2}
+    assert nz(gmm.get_tile_config(B, 65536, 2048, 512, 256)) == {"kernel": 1, "residency": 3, "placement": 2}
+    assert all(v in (1, 2, 3) for v in gmm.get_tile_config(D, 8192, 2048, 512, 32).values() if v)
 
 
 def test_set_tile_config_checks_fields_and_fit():
