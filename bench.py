@@ -87,26 +87,48 @@ def copy_reference() -> int:
 
 
 def counter_pass() -> int:
-    """Every benchmarked op three times, eagerly, at the wi / backward shape
-    and the production shape, and nothing else: a short workload for counter
-    collection (rocprofv3 --pmc), where each dispatch is counted on its own."""
+    """Every benchmarked op three times, eagerly, and nothing else: a short
+    workload for counter collection (rocprofv3 --pmc), where each dispatch is
+    counted on its own.  wi / backward shape: the FP8 forward (bf16 and
+    pre-quantised LHS), the LHS quantiser, the fused gate+up (with the
+    re-quantised activation), MXFP4 and int4 weights, the bf16 forward, tgmm
+    and dX; wo layer: the FP8 forward; production shape: the FP8 forward,
+    bf16 forward, tgmm and dX."""
     import torch
     import moe_grouped_gemm_gmm_amd as gmm
     import workloads
     gmm.load_library()
     dev = torch.device("cuda:0")
-    for name in ("wi", "full"):
+    for name in ("wi", "wo", "full"):
         wl = workloads.make(name, seed=0, with_dy=True)
         x = wl.x.to(dev)
         gs = torch.from_numpy(wl.group_sizes).to(dev)
         w = wl.w.to(dev)
         dy = wl.dy.to(dev)
         rq, rs = gmm.gmm_quantize_rhs(w)
+        extra = []
+        if name == "wi":
+            ql, sl = gmm.gmm_quantize_lhs(x)
+            q4, s4 = gmm.gmm_quantize_rhs_mxfp4(w)
+            qi, si = gmm.gmm_quantize_rhs_int4(w)
+            gu = workloads.make("wi_gate_up", seed=0)
+            guq, gus = gmm.gmm_quantize_rhs(gu.w.to(dev))
+            act_q = torch.empty((wl.M, wl.N), dtype=torch.uint8, device=dev)
+            act_s = torch.empty((wl.M, wl.N // 128), dtype=torch.float32, device=dev)
+            extra = [lambda: gmm.gmm_quantize_lhs(x),
+                     lambda: gmm.gmm_fp8_fwd(ql, rq, rs, gs, lhs_scale=sl),
+                     lambda: gmm.gmm_fp8_fwd_swiglu(x, guq, gus, gs),
+                     lambda: gmm.gmm_fp8_fwd_swiglu(x, guq, gus, gs, act_q=act_q, act_scale=act_s),
+                     lambda: gmm.gmm_fp8_mxfp4_fwd(x, q4, s4, gs),
+                     lambda: gmm.gmm_fp8_int4_fwd(x, qi, si, gs)]
         for _ in range(3):
             gmm.gmm_fp8_fwd(x, rq, rs, gs)
-            gmm.gmm_bf16_fwd(x, w, gs)
-            gmm.tgmm_bf16(x, dy, gs)
-            gmm.gmm_bf16_dx(dy, w, gs)
+            if name != "wo":
+                gmm.gmm_bf16_fwd(x, w, gs)
+                gmm.tgmm_bf16(x, dy, gs)
+                gmm.gmm_bf16_dx(dy, w, gs)
+            for fn in extra:
+                fn()
         torch.cuda.synchronize()
         print(json.dumps({"counter_pass": name, "M": wl.M, "K": wl.K, "N": wl.N, "G": wl.G}), flush=True)
     return 0
