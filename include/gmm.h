@@ -120,13 +120,23 @@ GMM_API size_t gmm_workspace_bytes(int op, int64_t M, int64_t K, int64_t N, int6
  *     waves     warp-specialised: 8 (the one form that also writes the LHS
  *                 codes), 12 or 16.
  *     depth     warp-specialised, 12 waves: K steps of weights in flight, 1 or 2.
- *   bf16 calls (GMM_OP_BF16_FWD, _TGMM, _DX): residency 2 or 3 (workgroups
- *     per CU the register allocation allows); tgmm placement 1 (each XCD
- *     takes whole groups) or 2 (every group spread over the 8 XCDs, groups
- *     in decreasing size class; needs a multiple of 8 tiles per group);
- *     forward and dX placement 1 (128-row tiles aligned to absolute rows)
- *     or 2 (tiles starting at each group's first row: no tile straddles
- *     two groups).
+ *   bf16 calls (GMM_OP_BF16_FWD, _TGMM, _DX):
+ *     kernel    1 128 x 128 tiles, operands staged through registers;
+ *                 2 256 x 256 tiles (8 waves, one workgroup per CU; the
+ *                 tiled dimensions multiples of 256; forward / dX rows
+ *                 from each group's first row); 3 128 x 128 tiles fed by
+ *                 load-to-LDS into a ring of LDS stages.
+ *     residency kernel 1: 2 or 3 (workgroups per CU the register
+ *                 allocation allows); kernel 2: 1; kernel 3: follows depth
+ *                 (2 for 2 stages, 1 for 3 or 4), only restated.
+ *     depth     kernel 3 only: LDS stages of 64-deep slices, 2, 3 or 4
+ *                 (slices in flight = depth - 1).
+ *     placement tgmm: 1 (each XCD takes whole groups) or 2 (every group
+ *                 spread over the 8 XCDs, groups in decreasing size class;
+ *                 needs a multiple of 8 tiles per group); forward and dX:
+ *                 1 (row tiles aligned to absolute rows) or 2 (tiles
+ *                 starting at each group's first row: no tile straddles
+ *                 two groups).
  */
 typedef struct {
     int32_t kernel, waves, tile_m, tile_n, depth, residency, placement;

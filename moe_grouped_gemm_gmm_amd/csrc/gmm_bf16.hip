@@ -265,6 +265,80 @@ __device__ inline TgmmTile tgmm_tile(const int32_t* __restrict__ group_sizes, in
     return out;
 }
 
+// What one workgroup computes: output rows [lo, hi) of the tile starting at
+// row0 (forward / dX: rows of group g; tgmm: a K tile of group g's dW),
+// columns c0 .. c0 + TILE, reduction range [red_lo, red_hi).
+struct TileItem {
+    int g, row0, lo, hi, c0, red_lo, red_hi;
+};
+
+// The prologue every bf16 kernel shares: block 0 writes the call's device
+// status word, wave 0 finds the work item (tgmm: the group and tile of
+// tgmm_tile; forward / dX: find_work_item over TILE-row items, placement 2
+// starting them at each group's first row) and the workgroup reads it from
+// s_info.  False when the workgroup has nothing more to do: no item, or rows
+// past the last group, which it has written as zeros.
+template <int MODE, bool OUT_BF16, int TILE, int NTHR>
+__device__ __forceinline__ bool tile_item(const int32_t* __restrict__ group_sizes, int M, int K, int N, int G,
+                                          void* __restrict__ out, int ntiles_c, int ntiles_r, int nblocks,
+                                          int placement, int32_t* __restrict__ status, int* s_info, TileItem& it) {
+    const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+    const int L = xcd_remap(blockIdx.x, nblocks);
+    const int out_cols = MODE == kDx ? K : N;
+    if (wave == 1 && blockIdx.x == 0) {   // the call's device status word
+        const int st = group_status(group_sizes, G, M);
+        if (lane == 0) status[0] = st;
+    }
+    if constexpr (MODE == kTgmm) {
+        if (wave == 0) {
+            const TgmmTile tt = tgmm_tile(group_sizes, G, M, ntiles_r * ntiles_c, L, placement);
+            if (lane == 0) { s_info[0] = tt.row_lo; s_info[1] = tt.row_hi; s_info[2] = tt.g; s_info[3] = tt.t; }
+        }
+        __syncthreads();
+        it.red_lo = s_info[0];
+        it.red_hi = s_info[1];
+        it.g = s_info[2];
+        if (it.g < 0) return false;
+        it.row0 = (s_info[3] / ntiles_c) * TILE;   // k tile
+        it.c0 = (s_info[3] % ntiles_c) * TILE;     // n tile
+        it.lo = it.row0;
+        it.hi = it.row0 + TILE;
+        return true;
+    } else {
+        const int w = L / ntiles_c;
+        it.c0 = (L % ntiles_c) * TILE;
+        if (wave == 0) {
+            // placement 2: row tiles start at each group's first row
+            const WorkItem wi = placement == 2 ? find_work_item<true>(group_sizes, G, M, TILE, w)
+                                               : find_work_item(group_sizes, G, M, TILE, w);
+            if (lane == 0) { s_info[0] = wi.g; s_info[1] = wi.tile; s_info[2] = wi.lo; s_info[3] = wi.hi; }
+        }
+        __syncthreads();
+        it.g = s_info[0];
+        if (it.g < 0) return false;
+        it.row0 = s_info[1] < 0 ? s_info[2] : s_info[1] * TILE;
+        it.lo = s_info[2];
+        it.hi = s_info[3];
+        it.red_lo = 0;
+        it.red_hi = MODE == kFwd ? K : N;
+        if (it.g == G) {  // rows past the last group: zeros
+            const int rows = it.hi - it.lo;
+            for (int e = tid; e < rows * (TILE / 8); e += NTHR) {
+                const int r = it.lo + e / (TILE / 8), c = it.c0 + (e % (TILE / 8)) * 8;
+                if constexpr (OUT_BF16)
+                    *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + (int64_t)r * out_cols + c) = make_uint4(0, 0, 0, 0);
+                else {
+                    float4* p = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + (int64_t)r * out_cols + c);
+                    p[0] = make_float4(0, 0, 0, 0);
+                    p[1] = make_float4(0, 0, 0, 0);
+                }
+            }
+            return false;
+        }
+        return true;
+    }
+}
+
 constexpr int kTileElems = (kT * (kR + kPadD) > kR * (kT + kPadT)) ? kT * (kR + kPadD) : kR * (kT + kPadT);
 
 // MINB: the minimum waves per SIMD the register allocation must allow (the
@@ -288,61 +362,12 @@ __global__ __launch_bounds__(256, MINB) void bf16_gemm_kernel(
     __shared__ int s_info[4];
 
     const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-    const int L = xcd_remap(blockIdx.x, nblocks);
     const int out_cols = MODE == kDx ? K : N;
-    if (wave == 1 && blockIdx.x == 0) {   // the call's device status word
-        const int st = group_status(group_sizes, G, M);
-        if (lane == 0) status[0] = st;
-    }
-
-    // ---- what this workgroup computes
-    int g, row0, lo, hi, c0, red_lo, red_hi;
-    if constexpr (MODE == kTgmm) {
-        if (wave == 0) {
-            const TgmmTile tt = tgmm_tile(group_sizes, G, M, ntiles_r * ntiles_c, L, placement);
-            if (lane == 0) { s_info[0] = tt.row_lo; s_info[1] = tt.row_hi; s_info[2] = tt.g; s_info[3] = tt.t; }
-        }
-        __syncthreads();
-        red_lo = s_info[0];
-        red_hi = s_info[1];
-        g = s_info[2];
-        if (g < 0) return;
-        row0 = (s_info[3] / ntiles_c) * kT;   // k tile
-        c0 = (s_info[3] % ntiles_c) * kT;     // n tile
-        lo = row0;
-        hi = row0 + kT;
-    } else {
-        const int w = L / ntiles_c;
-        c0 = (L % ntiles_c) * kT;
-        if (wave == 0) {
-            // placement 2: row tiles start at each group's first row
-            const WorkItem it = placement == 2 ? find_work_item<true>(group_sizes, G, M, kT, w)
-                                               : find_work_item(group_sizes, G, M, kT, w);
-            if (lane == 0) { s_info[0] = it.g; s_info[1] = it.tile; s_info[2] = it.lo; s_info[3] = it.hi; }
-        }
-        __syncthreads();
-        g = s_info[0];
-        if (g < 0) return;
-        row0 = s_info[1] < 0 ? s_info[2] : s_info[1] * kT;
-        lo = s_info[2];
-        hi = s_info[3];
-        red_lo = 0;
-        red_hi = MODE == kFwd ? K : N;
-        if (g == G) {  // rows past the last group: zeros
-            const int rows = hi - lo;
-            for (int e = tid; e < rows * (kT / 8); e += 256) {
-                const int r = lo + e / (kT / 8), c = c0 + (e % (kT / 8)) * 8;
-                if constexpr (OUT_BF16)
-                    *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + (int64_t)r * out_cols + c) = make_uint4(0, 0, 0, 0);
-                else {
-                    float4* p = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + (int64_t)r * out_cols + c);
-                    p[0] = make_float4(0, 0, 0, 0);
-                    p[1] = make_float4(0, 0, 0, 0);
-                }
-            }
-            return;
-        }
-    }
+    TileItem it;
+    if (!tile_item<MODE, OUT_BF16, kT, 256>(group_sizes, M, K, N, G, out, ntiles_c, ntiles_r, nblocks, placement,
+                                            status, s_info, it))
+        return;
+    const int g = it.g, row0 = it.row0, lo = it.lo, hi = it.hi, c0 = it.c0, red_lo = it.red_lo, red_hi = it.red_hi;
 
     const int wm = wave >> 1, wn = wave & 1;
     const int lr = lane & 15, lg = lane >> 4;
@@ -457,6 +482,390 @@ __global__ __launch_bounds__(256, MINB) void bf16_gemm_kernel(
     }
 }
 
+// ---------------------------------------------------- DMA-fed 128 x 128 --
+// The same three products on the 128 x 128 tile and wave layout as above,
+// with the operands moved from global memory to LDS by the load-to-LDS
+// instructions of gfx950 (global_load_lds_dwordx4: each lane's 16 bytes land
+// at the instruction's LDS base + 16 x lane) into a ring of S stages, each
+// holding one RD-deep slice of both operands.  The loads of slice t + S - 1
+// are issued as soon as every wave has finished reading the stage they
+// overwrite, so S - 1 slices are in flight while slice t is multiplied,
+// without any registers held for them; each slice costs one workgroup
+// barrier.  RES workgroups share a CU; the slice depth is 64 when RES rings
+// of 64-deep stages (32 KB each) fit the 160 KB of LDS, else 32 (16 KB):
+//   S x RES:  2 x 2, 3 x 1, 4 x 1 -> 64-deep;  3 x 2, 3 x 3, 4 x 2 -> 32-deep.
+// More resident waves hide more of each wave's stalls (the barrier, the LDS
+// reads); deeper rings keep more bytes in flight per workgroup.
+//
+// A load-to-LDS instruction writes 1 KB of contiguous LDS, so the stage rows
+// cannot be padded; the bank spread comes from XOR swizzles instead:
+//  - direct [128][RD] slices (2 RD-byte rows): the 16-byte chunk c of row R
+//    sits at chunk c ^ dkey(R), dkey = R % 8 for 128-byte rows, (R / 4) % 4
+//    for 64-byte rows.  A ds_read_b128 of 16 rows at one chunk then reads as
+//    fast as the padded 160-byte rows (measured ~205 B/clk/CU for the first;
+//    the second puts 16 rows on 16 distinct 16-byte bank groups).
+//  - transposed [RD][128] slices (256-byte rows): the 32-byte chunk k of row
+//    r sits at chunk k ^ key(r).  The two lane groups the LDS serves
+//    together read 8 rows at one chunk (read_tr's row sets), and key takes 8
+//    distinct values on each such set: r % 8 for the spread order, r % 4 +
+//    4 (bit 3 of r) for the natural one.
+// tgmm's last slice may run past the group's rows: the loads there are
+// clamped to its last row, and the fragments' rows past the end are zeroed
+// in registers before the MFMAs.
+
+template <int S, int RES>
+struct DmaShape {
+    static constexpr int kRD = RES * S * 32768 <= 163840 - 1024 ? 64 : 32;   // slice depth
+    static constexpr int kSlice = kT * kRD;               // bf16 elements of one operand's slice
+    static constexpr int kInstr = kSlice * 2 / 1024 / 4;  // load-to-LDS instructions per wave and operand
+    static constexpr int kChunks = kRD / 8;               // 16-byte chunks per direct row
+    static constexpr int kRows = 64 / kChunks;            // direct rows per instruction
+};
+
+// s_waitcnt vmcnt(N), the other counters untouched.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// A workgroup barrier that leaves the vector memory counter alone (the
+// release fence of __syncthreads waits for every load in flight, load-to-LDS
+// ones included).  The wavefront fences keep the compiler from moving LDS
+// accesses across it; the lgkmcnt wait completes this wave's LDS reads first.
+__device__ __forceinline__ void stage_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <bool kSpread>
+__device__ __forceinline__ int trans_key(int r) {
+    return kSpread ? (r & 7) : ((r & 3) | ((r >> 1) & 4));
+}
+
+template <int RD>
+__device__ __forceinline__ int direct_key(int R) {
+    return RD == 64 ? (R & 7) : ((R >> 2) & 3);
+}
+
+// Direct fragment: 8 reduction values at chunk `chunk` of row `row`.
+template <int RD>
+__device__ __forceinline__ v8bf swz_read_direct(const uint16_t* tile, int row, int chunk) {
+    return *reinterpret_cast<const v8bf*>(tile + row * RD + 8 * (chunk ^ direct_key<RD>(row)));
+}
+
+// The transposed reads of one operand's slice: fragments i = 0..3 of NB
+// 32-deep blocks, two ds_read_b64_tr_b16 each, as read_tr lays them out.
+// addr[i] is the LDS byte address of fragment i's first read in block 0;
+// the second read sits HALF bytes on (rows +4 natural, +16 spread: the same
+// key, so the same swizzled chunk), block 1 8192 bytes on (rows +32).  One
+// asm block that waits for its own reads before it ends (the
+// ds_read_b64_tr_b16 builtin makes the compiler drain every load-to-LDS load
+// in flight before it, which would flatten the ring).
+typedef unsigned long long u64;
+typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
+template <int NB, int HALF>
+__device__ __forceinline__ void tr_slice(v8bf (&f)[2][4], const unsigned (&addr)[4]) {
+    if constexpr (NB == 2) {
+        u64 o[16];
+        asm volatile(
+            "ds_read_b64_tr_b16 %0, %16\n\t"
+            "ds_read_b64_tr_b16 %1, %16 offset:%20\n\t"
+            "ds_read_b64_tr_b16 %2, %16 offset:8192\n\t"
+            "ds_read_b64_tr_b16 %3, %16 offset:%21\n\t"
+            "ds_read_b64_tr_b16 %4, %17\n\t"
+            "ds_read_b64_tr_b16 %5, %17 offset:%20\n\t"
+            "ds_read_b64_tr_b16 %6, %17 offset:8192\n\t"
+            "ds_read_b64_tr_b16 %7, %17 offset:%21\n\t"
+            "ds_read_b64_tr_b16 %8, %18\n\t"
+            "ds_read_b64_tr_b16 %9, %18 offset:%20\n\t"
+            "ds_read_b64_tr_b16 %10, %18 offset:8192\n\t"
+            "ds_read_b64_tr_b16 %11, %18 offset:%21\n\t"
+            "ds_read_b64_tr_b16 %12, %19\n\t"
+            "ds_read_b64_tr_b16 %13, %19 offset:%20\n\t"
+            "ds_read_b64_tr_b16 %14, %19 offset:8192\n\t"
+            "ds_read_b64_tr_b16 %15, %19 offset:%21\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]),
+              "=&v"(o[7]), "=&v"(o[8]), "=&v"(o[9]), "=&v"(o[10]), "=&v"(o[11]), "=&v"(o[12]), "=&v"(o[13]),
+              "=&v"(o[14]), "=&v"(o[15])
+            : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]), "i"(HALF), "i"(8192 + HALF)
+            : "memory");
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f[0][i] = __builtin_bit_cast(v8bf, u64x2{o[4 * i], o[4 * i + 1]});
+            f[1][i] = __builtin_bit_cast(v8bf, u64x2{o[4 * i + 2], o[4 * i + 3]});
+        }
+    } else {
+        u64 o[8];
+        asm volatile(
+            "ds_read_b64_tr_b16 %0, %8\n\t"
+            "ds_read_b64_tr_b16 %1, %8 offset:%12\n\t"
+            "ds_read_b64_tr_b16 %2, %9\n\t"
+            "ds_read_b64_tr_b16 %3, %9 offset:%12\n\t"
+            "ds_read_b64_tr_b16 %4, %10\n\t"
+            "ds_read_b64_tr_b16 %5, %10 offset:%12\n\t"
+            "ds_read_b64_tr_b16 %6, %11\n\t"
+            "ds_read_b64_tr_b16 %7, %11 offset:%12\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]),
+              "=&v"(o[7])
+            : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]), "i"(HALF)
+            : "memory");
+#pragma unroll
+        for (int i = 0; i < 4; ++i) f[0][i] = __builtin_bit_cast(v8bf, u64x2{o[2 * i], o[2 * i + 1]});
+    }
+}
+
+// LDS byte address (relative to the slice) of the first read of the
+// transposed fragment at columns c0 .. c0+15 in block 0, for this lane.
+template <bool kSpread>
+__device__ __forceinline__ unsigned tr_addr(int lg, int c0, int lr) {
+    const int r = (kSpread ? 4 : 8) * lg + (lr >> 2);
+    return (unsigned)(2 * (r * kT + 16 * ((c0 >> 4) ^ trans_key<kSpread>(r)) + (lr & 3) * 4));
+}
+
+// A transposed fragment of block s with the reduction rows at or past
+// `valid` zeroed (element e holds row r + e for e < 4 and r1 + e - 4 after,
+// as read).
+template <bool kSpread>
+__device__ __forceinline__ v8bf zero_rows_past(v8bf v, int s, int lg, int valid) {
+    const int r = s * 32 + (kSpread ? 4 : 8) * lg;
+    const int r1 = r + (kSpread ? 16 : 4);
+    u32x4 w = __builtin_bit_cast(u32x4, v);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int row = (q < 2 ? r : r1) + 2 * (q & 1);
+        w[q] &= (row < valid ? 0x0000FFFFu : 0u) | (row + 1 < valid ? 0xFFFF0000u : 0u);
+    }
+    return __builtin_bit_cast(v8bf, w);
+}
+
+template <int MODE, bool OUT_BF16, int S, int RES>
+__global__ __launch_bounds__(256, RES) void bf16_dma_kernel(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
+    const int32_t* __restrict__ group_sizes, int M, int K, int N, int G, void* __restrict__ out,
+    int ntiles_c, int ntiles_r, int nblocks, int placement, int32_t* __restrict__ status) {
+    using D = DmaShape<S, RES>;
+    constexpr int RD = D::kRD, kSl = D::kSlice, NI = D::kInstr, NB = RD / 32;
+    static_assert(S >= 2 && S <= 4 && RES >= 1 && RES <= 3, "2 to 4 stages, 1 to 3 workgroups per CU");
+    static_assert(RES * S * 2 * kSl * 2 <= 163840 - 1024, "the rings of RES workgroups fit the LDS");
+    constexpr int kEpiRow = 64 + 8;   // bf16 epilogue staging row (144 bytes)
+    static_assert(!OUT_BF16 || 4 * 64 * kEpiRow <= S * 2 * kSl, "epilogue staging fits the ring");
+    constexpr bool A_TR = MODE == kTgmm;
+    constexpr bool B_TR = MODE != kDx;
+    constexpr bool kSpread = A_TR && B_TR;
+    __shared__ __attribute__((aligned(1024))) uint16_t ring[S * 2 * kSl];
+    __shared__ int s_info[4];
+
+    const int tid = threadIdx.x, lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int out_cols = MODE == kDx ? K : N;
+    TileItem it;
+    if (!tile_item<MODE, OUT_BF16, kT, 256>(group_sizes, M, K, N, G, out, ntiles_c, ntiles_r, nblocks, placement,
+                                            status, s_info, it))
+        return;
+    const int g = it.g, row0 = it.row0, lo = it.lo, hi = it.hi, c0 = it.c0, red_lo = it.red_lo, red_hi = it.red_hi;
+
+    // ---- this lane's share of a slice: NI load-to-LDS instructions per
+    //      operand and wave, instruction i of wave w filling LDS bytes
+    //      [1024 j, 1024 (j + 1)) of the operand's slice, j = NI w + i.
+    //  direct:     kRows rows per instruction, kChunks lanes per row: lane l
+    //              writes row kRows j + l / kChunks at chunk position
+    //              l % kChunks, so it loads chunk (l % kChunks) ^ dkey(row).
+    //  transposed: rows 4j .. 4j+3; lane l writes row 4j + l/16 at 32-byte
+    //              position (l % 16)/2, half l % 2, so it loads 32-byte
+    //              chunk ((l % 16)/2) ^ key(row), half l % 2.
+    const int lda = MODE == kFwd ? K : N;
+    const uint16_t* wg = B + (int64_t)(MODE == kTgmm ? 0 : g) * K * N;
+    int64_t a_off[NI], b_off[NI];   // element offsets of the slice at reduction index 0
+    int t_row[NI];                  // transposed operands: the slice row each instruction fills
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int j = NI * wave + i;
+        const int R = D::kRows * j + lane / D::kChunks;                 // direct slice row
+        const int dchunk = (lane % D::kChunks) ^ direct_key<RD>(R);
+        const int r = 4 * j + (lane >> 4);                              // transposed slice row
+        const int tcol = 16 * (((lane & 15) >> 1) ^ trans_key<kSpread>(r)) + 8 * (lane & 1);
+        t_row[i] = r;
+        if constexpr (MODE == kTgmm) {
+            a_off[i] = row0 + tcol;                          // x[m][k tile]
+            b_off[i] = c0 + tcol;                            // dy[m][n tile]
+        } else {
+            const int arow = min(max(row0 + R, lo), hi - 1);
+            a_off[i] = (int64_t)arow * lda + 8 * dchunk;     // x or dy rows
+            if constexpr (MODE == kFwd)
+                b_off[i] = c0 + tcol;                        // w[g][k][n tile]
+            else
+                b_off[i] = (int64_t)(c0 + R) * N + 8 * dchunk;   // w[g][k tile][n]
+        }
+    }
+    auto issue = [&](int t, int stage) {
+        const int r0 = red_lo + t * RD;
+        uint16_t* sa = ring + stage * 2 * kSl;
+        uint16_t* sb = sa + kSl;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const uint16_t* pa;
+            const uint16_t* pb;
+            if constexpr (MODE == kTgmm) {
+                const int64_t m = min(r0 + t_row[i], red_hi - 1);
+                pa = A + m * K + a_off[i];
+                pb = B + m * N + b_off[i];
+            } else {
+                pa = A + a_off[i] + r0;
+                if constexpr (MODE == kFwd)
+                    pb = wg + (int64_t)(r0 + t_row[i]) * N + b_off[i];
+                else
+                    pb = wg + b_off[i] + r0;
+            }
+            __builtin_amdgcn_global_load_lds(pa, (GMM_LDS void*)(sa + (NI * wave + i) * 512), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(pb, (GMM_LDS void*)(sb + (NI * wave + i) * 512), 16, 0, 0);
+        }
+    };
+
+    const int wm = (tid >> 6) >> 1, wn = (tid >> 6) & 1;
+    const int lr = lane & 15, lg = lane >> 4;
+    v4f acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    // transposed fragments' lane addresses within a slice (bytes)
+    constexpr int kHalf = (kSpread ? 16 : 4) * kT * 2;
+    const unsigned ring_lds = (unsigned)(uintptr_t)(GMM_LDS uint16_t*)ring;
+    unsigned a_tr[4], b_tr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        a_tr[i] = tr_addr<kSpread>(lg, wm * 64 + i * 16, lr);
+        b_tr[i] = tr_addr<kSpread>(lg, wn * 64 + i * 16, lr);
+    }
+
+    const int nsl = (red_hi - red_lo + RD - 1) / RD;
+    // unrolled: with a loop of load-to-LDS issues here the compiler's wait
+    // insertion drains every load before each LDS read of the main loop
+#pragma unroll
+    for (int t = 0; t < S - 1; ++t)
+        if (t < nsl) issue(t, t);
+    int stage = 0;
+    for (int t = 0; t < nsl; ++t) {
+        // slice t landed in this wave's share once at most the loads of
+        // slices t+1 .. t+S-2 (2 NI per slice) are outstanding; the barrier
+        // then covers every wave's share, and every wave's reads of the
+        // stage the next issue overwrites (slice t - 1's)
+        if (t + S - 2 < nsl) wait_vmem<2 * NI * (S - 2)>(); else wait_vmem<0>();
+        stage_barrier();
+        if (t + S - 1 < nsl) issue(t + S - 1, stage == 0 ? S - 1 : stage - 1);
+        const uint16_t* ta = ring + stage * 2 * kSl;
+        const uint16_t* tb = ta + kSl;
+        const unsigned sbase = ring_lds + (unsigned)(stage * 2 * kSl * 2);
+        v8bf atr[2][4], btr[2][4];
+        if constexpr (A_TR) {
+            const unsigned ad[4] = {sbase + a_tr[0], sbase + a_tr[1], sbase + a_tr[2], sbase + a_tr[3]};
+            tr_slice<NB, kHalf>(atr, ad);
+        }
+        if constexpr (B_TR) {
+            const unsigned bs = sbase + (unsigned)(kSl * 2);
+            const unsigned bd[4] = {bs + b_tr[0], bs + b_tr[1], bs + b_tr[2], bs + b_tr[3]};
+            tr_slice<NB, kHalf>(btr, bd);
+        }
+        const int valid = red_hi - (red_lo + t * RD);   // tgmm: real rows of this slice
+#pragma unroll
+        for (int s = 0; s < NB; ++s) {
+            v8bf af[4], bf[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if constexpr (A_TR)
+                    af[i] = atr[s][i];
+                else
+                    af[i] = swz_read_direct<RD>(ta, wm * 64 + i * 16 + lr, s * 4 + lg);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if constexpr (B_TR)
+                    bf[j] = btr[s][j];
+                else
+                    bf[j] = swz_read_direct<RD>(tb, wn * 64 + j * 16 + lr, s * 4 + lg);
+            }
+            if constexpr (MODE == kTgmm) {
+                if (valid < RD) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) af[i] = zero_rows_past<kSpread>(af[i], s, lg, valid);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) bf[j] = zero_rows_past<kSpread>(bf[j], s, lg, valid);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
+        }
+        stage = stage == S - 1 ? 0 : stage + 1;
+    }
+    __syncthreads();   // every load landed (the last wait was vmcnt(0)) and every read done
+
+    // ---- epilogue, as the kernel above, staged in the ring
+    const int64_t obase = MODE == kTgmm ? (int64_t)g * K * N : 0;
+    const int col0 = c0 + wn * 64;
+    if constexpr (OUT_BF16) {
+        uint16_t* ep = ring + (tid >> 6) * 64 * kEpiRow;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                *reinterpret_cast<uint2*>(ep + (16 * i + lr) * kEpiRow + 16 * j + 4 * lg) =
+                    make_uint2(pack_bf16x2(acc[i][j][0], acc[i][j][1]), pack_bf16x2(acc[i][j][2], acc[i][j][3]));
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        const int orow = lane >> 3, ocol = (lane & 7) * 8;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int r = 8 * q + orow;
+            const uint4 v = *reinterpret_cast<const uint4*>(ep + r * kEpiRow + ocol);
+            const int row = row0 + wm * 64 + r;
+            if (row >= lo && row < hi)
+                *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + obase + (int64_t)row * out_cols + col0 + ocol) = v;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = row0 + wm * 64 + i * 16 + lr;
+            if (row < lo || row >= hi) continue;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + obase + (int64_t)row * out_cols + col0 + 16 * j + 4 * lg) =
+                    make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+        }
+    }
+}
+
+template <int MODE, int S, int RES>
+hipError_t launch_dma(const void* A, const void* B, const int32_t* group_sizes, int M, int K, int N, int G,
+                      void* out, bool out_bf16, int placement, int32_t* status, hipStream_t stream) {
+    int ntiles_c, ntiles_r = 0;
+    int64_t nblocks;
+    if constexpr (MODE == kTgmm) {
+        ntiles_r = K / kT;
+        ntiles_c = N / kT;
+        nblocks = (int64_t)G * ntiles_r * ntiles_c;
+    } else {
+        ntiles_c = (MODE == kFwd ? N : K) / kT;
+        nblocks = max_work_items(M, G, kT) * ntiles_c;
+    }
+    const uint16_t* a = reinterpret_cast<const uint16_t*>(A);
+    const uint16_t* b = reinterpret_cast<const uint16_t*>(B);
+    if (out_bf16)
+        hipLaunchKernelGGL((bf16_dma_kernel<MODE, true, S, RES>), dim3((unsigned)nblocks), dim3(256), 0, stream,
+                           a, b, group_sizes, M, K, N, G, out, ntiles_c, ntiles_r, (int)nblocks, placement, status);
+    else
+        hipLaunchKernelGGL((bf16_dma_kernel<MODE, false, S, RES>), dim3((unsigned)nblocks), dim3(256), 0, stream,
+                           a, b, group_sizes, M, K, N, G, out, ntiles_c, ntiles_r, (int)nblocks, placement, status);
+    return hipGetLastError();
+}
+
 // ------------------------------------------------------------ wide tiles --
 // The same three products on 256x256 output tiles: 8 waves (2 x 4), each
 // owning 128 x 64 (8 x 4 MFMA blocks, 128 fp32 accumulators), one workgroup
@@ -514,58 +923,13 @@ __global__ __launch_bounds__(64 * NWV, 1) void bf16_wide_kernel(
     __shared__ int s_info[4];
 
     const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-    const int L = xcd_remap(blockIdx.x, nblocks);
     const int out_cols = MODE == kDx ? K : N;
-    if (wave == 1 && blockIdx.x == 0) {   // the call's device status word
-        const int st = group_status(group_sizes, G, M);
-        if (lane == 0) status[0] = st;
-    }
-
-    int g, row0, lo, hi, c0, red_lo, red_hi;
-    if constexpr (MODE == kTgmm) {
-        if (wave == 0) {
-            const TgmmTile tt = tgmm_tile(group_sizes, G, M, ntiles_r * ntiles_c, L, placement);
-            if (lane == 0) { s_info[0] = tt.row_lo; s_info[1] = tt.row_hi; s_info[2] = tt.g; s_info[3] = tt.t; }
-        }
-        __syncthreads();
-        red_lo = s_info[0];
-        red_hi = s_info[1];
-        g = s_info[2];
-        if (g < 0) return;
-        row0 = (s_info[3] / ntiles_c) * kTW;   // k tile
-        c0 = (s_info[3] % ntiles_c) * kTW;     // n tile
-        lo = row0;
-        hi = row0 + kTW;
-    } else {
-        const int w = L / ntiles_c;
-        c0 = (L % ntiles_c) * kTW;
-        if (wave == 0) {
-            const WorkItem it = find_work_item<true>(group_sizes, G, M, kTW, w);
-            if (lane == 0) { s_info[0] = it.g; s_info[1] = it.lo; s_info[2] = it.hi; }
-        }
-        __syncthreads();
-        g = s_info[0];
-        if (g < 0) return;
-        lo = s_info[1];
-        hi = s_info[2];
-        row0 = lo;
-        red_lo = 0;
-        red_hi = MODE == kFwd ? K : N;
-        if (g == G) {  // rows past the last group: zeros
-            const int rows = hi - lo;
-            for (int e = tid; e < rows * (kTW / 8); e += kThr) {
-                const int r = lo + e / (kTW / 8), c = c0 + (e % (kTW / 8)) * 8;
-                if constexpr (OUT_BF16)
-                    *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + (int64_t)r * out_cols + c) = make_uint4(0, 0, 0, 0);
-                else {
-                    float4* p = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + (int64_t)r * out_cols + c);
-                    p[0] = make_float4(0, 0, 0, 0);
-                    p[1] = make_float4(0, 0, 0, 0);
-                }
-            }
-            return;
-        }
-    }
+    TileItem it;
+    // forward / dX rows come in items starting at each group's first row
+    if (!tile_item<MODE, OUT_BF16, kTW, kThr>(group_sizes, M, K, N, G, out, ntiles_c, ntiles_r, nblocks,
+                                              MODE == kTgmm ? placement : 2, status, s_info, it))
+        return;
+    const int g = it.g, row0 = it.row0, lo = it.lo, hi = it.hi, c0 = it.c0, red_lo = it.red_lo, red_hi = it.red_hi;
 
     const int wm = wave / (NWV / 2), wn = wave % (NWV / 2);
     const int lr = lane & 15, lg = lane >> 4;
@@ -725,6 +1089,15 @@ hipError_t launch_mode(const TileConfig& cfg, const void* A, const void* B,
                        bool out_bf16, int32_t* status, hipStream_t stream) {
     if (cfg.kernel == 2)
         return launch_wide<MODE, 8>(A, B, group_sizes, M, K, N, G, out, out_bf16, cfg.placement, status, stream);
+    if (cfg.kernel == 3) {   // (depth, residency) pairs as gmm_config.cpp accepts them
+        const int d = cfg.depth, r = cfg.residency;
+        if (d == 2) return launch_dma<MODE, 2, 2>(A, B, group_sizes, M, K, N, G, out, out_bf16, cfg.placement, status, stream);
+        if (d == 3 && r == 1) return launch_dma<MODE, 3, 1>(A, B, group_sizes, M, K, N, G, out, out_bf16, cfg.placement, status, stream);
+        if (d == 3 && r == 2) return launch_dma<MODE, 3, 2>(A, B, group_sizes, M, K, N, G, out, out_bf16, cfg.placement, status, stream);
+        if (d == 3) return launch_dma<MODE, 3, 3>(A, B, group_sizes, M, K, N, G, out, out_bf16, cfg.placement, status, stream);
+        if (r == 1) return launch_dma<MODE, 4, 1>(A, B, group_sizes, M, K, N, G, out, out_bf16, cfg.placement, status, stream);
+        return launch_dma<MODE, 4, 2>(A, B, group_sizes, M, K, N, G, out, out_bf16, cfg.placement, status, stream);
+    }
     int ntiles_c, ntiles_r = 0;
     int64_t nblocks;
     if constexpr (MODE == kTgmm) {

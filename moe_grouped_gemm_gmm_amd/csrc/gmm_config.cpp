@@ -172,9 +172,11 @@ bool resolve_swiglu(const TileConfig& f, int64_t M, int64_t N, int64_t G, TileCo
 bool resolve_bf16(int op, const TileConfig& f, int64_t M, int64_t K, int64_t N, int64_t G,
                   TileConfig* c, const char** why) {
     *c = TileConfig{};
-    if (f.waves || f.tile_m || f.tile_n || f.depth)
-        return fail(why, "the bf16 calls set kernel, residency and placement only");
-    if (f.kernel && f.kernel != 1 && f.kernel != 2) return fail(why, "bf16 kernels are 1 (128 x 128) or 2 (256 x 256)");
+    if (f.waves || f.tile_m || f.tile_n)
+        return fail(why, "the bf16 calls set kernel, residency, depth and placement only");
+    if (f.kernel && (f.kernel < 1 || f.kernel > 3))
+        return fail(why, "bf16 kernels are 1 (128 x 128), 2 (256 x 256) or 3 (128 x 128 fed by load-to-LDS)");
+    if (f.depth && f.kernel && f.kernel != 3) return fail(why, "depth applies to bf16 kernel 3 only");
     if (f.kernel == 2) {
         // 256 x 256 tiles, 8 waves, one workgroup per CU; forward and dX rows
         // in items starting at each group's first row
@@ -196,11 +198,34 @@ bool resolve_bf16(int op, const TileConfig& f, int64_t M, int64_t K, int64_t N, 
         }
         return true;
     }
-    c->kernel = 1;
-    if (f.residency && f.residency != 2 && f.residency != 3) return fail(why, "residency is 2 or 3");
     const int64_t nblocks = op == kOpTgmm ? G * (K / 128) * (N / 128)
                                           : items(M, G, 128) * ((op == kOpDx ? K : N) / 128);
-    c->residency = f.residency ? f.residency : (nblocks <= 2 * (int64_t)device_cus() ? 2 : 3);
+    const int64_t cus = device_cus();
+    // The library's kernel: depth implies 3, residency alone 1.  Otherwise 3
+    // (3 stages of 32-deep slices, three workgroups per CU) for tgmm and for
+    // forward / dX grids of at most eight workgroups per CU, 1 beyond (measured
+    // against kernel 1's best: backward shape forward 39.9 -> 33.9 us, tgmm
+    // 32.3 -> 30.3, dX 37.4 -> 36.1; production shape tgmm 303 -> 294, but
+    // forward 254 -> 265 and dX 273 -> 286 with 12 or more per CU).
+    const int kernel = f.kernel ? f.kernel
+                                : (f.depth ? 3 : (f.residency ? 1 : (op == kOpTgmm || nblocks <= 8 * cus ? 3 : 1)));
+    if (kernel == 3) {
+        // LDS stages x workgroups per CU: 64-deep slices (32 KB stages) when
+        // the rings fit, else 32-deep (16 KB): 2 x 2, 3 x 1, 4 x 1 (64-deep),
+        // 3 x 2, 3 x 3, 4 x 2 (32-deep)
+        if (f.depth && (f.depth < 2 || f.depth > 4)) return fail(why, "depth (LDS stages) is 2, 3 or 4");
+        c->kernel = 3;
+        c->depth = f.depth ? f.depth : 3;
+        const int def = c->depth == 2 ? 2 : (c->depth == 3 ? 3 : 2);
+        const int res = f.residency ? f.residency : def;
+        const bool ok = c->depth == 2 ? res == 2 : (c->depth == 3 ? res >= 1 && res <= 3 : res == 1 || res == 2);
+        if (!ok) return fail(why, "kernel 3 pairs depth 2 with residency 2, 3 with 1-3, 4 with 1-2");
+        c->residency = res;
+    } else {
+        c->kernel = 1;
+        if (f.residency && f.residency != 2 && f.residency != 3) return fail(why, "residency is 2 or 3");
+        c->residency = f.residency ? f.residency : (nblocks <= 2 * cus ? 2 : 3);
+    }
     if (op == kOpTgmm) {
         if (f.placement && f.placement != 1 && f.placement != 2) return fail(why, "placement is 1 or 2");
         if (f.placement == 2 && ((K / 128) * (N / 128)) % 8 != 0)
@@ -214,7 +239,7 @@ bool resolve_bf16(int op, const TileConfig& f, int64_t M, int64_t K, int64_t N, 
         // shape dX 284 -> 275 us, forward 264 -> 257 us; at the backward shape
         // the same or 0.5% slower)
         if (f.placement && f.placement != 1 && f.placement != 2) return fail(why, "placement is 1 or 2");
-        c->placement = f.placement ? f.placement : (nblocks > 6 * (int64_t)device_cus() ? 2 : 1);
+        c->placement = f.placement ? f.placement : (kernel == 1 && nblocks > 6 * cus ? 2 : 1);
     }
     return true;
 }

@@ -20,10 +20,12 @@ gmm_set_tile_config (include/gmm.h):
   swiglu                     tile_m 48/64
   bf16_fwd, dx               128 x 128 tiles: residency 2/3 workgroups per CU x row
                              tiles aligned to absolute rows or to each group's first
-                             row; 256 x 256 tiles (8 waves, one workgroup per CU)
+                             row; 256 x 256 tiles (8 waves, one workgroup per CU);
+                             128 x 128 tiles fed by load-to-LDS: (LDS stages,
+                             workgroups per CU) pairs x row placement
   tgmm                       128 x 128 tiles: residency 2/3 x placement (whole groups
                              per XCD, groups spread over the XCDs); 256 x 256 tiles x
-                             placement
+                             placement; load-to-LDS tiles, (stages, workgroups) x placement
 
 The space is small enough to enumerate, so the search is exhaustive rather
 than evolutionary.  Stages (Q9.4):
@@ -51,6 +53,8 @@ import numpy as np
 
 PHASES = ("fp8_fwd", "fp8_fwd_prequant", "mxfp4_fwd", "int4_fwd", "swiglu", "bf16_fwd", "tgmm", "dx")
 BF16_PHASES = ("bf16_fwd", "tgmm", "dx")
+# load-to-LDS bf16 kernel: (LDS stages, workgroups per CU)
+DMA_PAIRS = ((2, 2), (3, 1), (4, 1), (3, 2), (3, 3), (4, 2))
 
 # Q9.4 stages: (atol, rtol, minimum SNR in dB)
 STRICT = (1e-3, 1e-2, 30.0)
@@ -99,11 +103,17 @@ def space(phase: str) -> List[Dict[str, int]]:
                 out.append({"residency": res, "placement": pl})
         for pl in (1, 2):
             out.append({"kernel": 2, "placement": pl})
+        for depth, res in DMA_PAIRS:
+            for pl in (1, 2):
+                out.append({"kernel": 3, "depth": depth, "residency": res, "placement": pl})
     else:
         for res in (2, 3):
             for pl in (1, 2):
                 out.append({"residency": res, "placement": pl})
         out.append({"kernel": 2})
+        for depth, res in DMA_PAIRS:
+            for pl in (1, 2):
+                out.append({"kernel": 3, "depth": depth, "residency": res, "placement": pl})
     return out
 
 

@@ -31,11 +31,13 @@ def _gs(wl):
 @pytest.mark.parametrize("M,K,N,gs", EDGE)
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("placement", [1, 2])
-def test_bf16_fwd_edges(M, K, N, gs, out_dtype, placement):
-    """placement 2: row tiles start at each group's first row."""
+@pytest.mark.parametrize("kernel", [1, 3])
+def test_bf16_fwd_edges(M, K, N, gs, out_dtype, placement, kernel):
+    """placement 2: row tiles start at each group's first row; kernel 1
+    register-staged, 3 load-to-LDS (its default stages)."""
     wl = workloads.custom(M, K, N, gs, seed=M + 3 * K, w_std=0.05)
     out = torch.full((M, N), float("nan"), dtype=out_dtype, device=DEV)
-    with tile_config(gmm.OP_BF16_FWD, {"placement": placement}):
+    with tile_config(gmm.OP_BF16_FWD, {"kernel": kernel, "placement": placement}):
         gmm.gmm_bf16_fwd(wl.x.to(DEV), wl.w.to(DEV), _gs(wl), out=out)
     ref = oracle.gmm(workloads.as_f32(wl.x), workloads.as_f32(wl.w), wl.group_sizes)
     o = to_np64(out)
@@ -46,10 +48,11 @@ def test_bf16_fwd_edges(M, K, N, gs, out_dtype, placement):
 @pytest.mark.parametrize("M,K,N,gs", EDGE)
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("placement", [1, 2])
-def test_dx_edges(M, K, N, gs, out_dtype, placement):
+@pytest.mark.parametrize("kernel", [1, 3])
+def test_dx_edges(M, K, N, gs, out_dtype, placement, kernel):
     wl = workloads.custom(M, K, N, gs, seed=M + 5 * K, w_std=0.05, with_dy=True)
     out = torch.full((M, K), float("nan"), dtype=out_dtype, device=DEV)
-    with tile_config(gmm.OP_DX, {"placement": placement}):
+    with tile_config(gmm.OP_DX, {"kernel": kernel, "placement": placement}):
         gmm.gmm_bf16_dx(wl.dy.to(DEV), wl.w.to(DEV), _gs(wl), out=out)
     ref = oracle.gmm_dx(workloads.as_f32(wl.dy), workloads.as_f32(wl.w), wl.group_sizes)
     o = to_np64(out)
@@ -59,11 +62,13 @@ def test_dx_edges(M, K, N, gs, out_dtype, placement):
 
 @pytest.mark.parametrize("M,K,N,gs", EDGE)
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
-def test_tgmm_edges(M, K, N, gs, out_dtype):
+@pytest.mark.parametrize("kernel", [1, 3])
+def test_tgmm_edges(M, K, N, gs, out_dtype, kernel):
     wl = workloads.custom(M, K, N, gs, seed=M + 7 * K, with_dy=True)
     G = len(gs)
     out = torch.full((G, K, N), float("nan"), dtype=out_dtype, device=DEV)
-    gmm.tgmm_bf16(wl.x.to(DEV), wl.dy.to(DEV), _gs(wl), out=out)
+    with tile_config(gmm.OP_TGMM, {"kernel": kernel}):
+        gmm.tgmm_bf16(wl.x.to(DEV), wl.dy.to(DEV), _gs(wl), out=out)
     ref = oracle.tgmm(workloads.as_f32(wl.x), workloads.as_f32(wl.dy), wl.group_sizes)
     o = to_np64(out)
     for g in range(G):
@@ -149,23 +154,25 @@ def test_tgmm_many_groups_mixed_sizes_every_group_written():
 
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("placement", [1, 2])
-def test_dx_straddling_tiles_ragged_tail(out_dtype, placement):
+@pytest.mark.parametrize("kernel", [1, 3])
+def test_dx_straddling_tiles_ragged_tail(out_dtype, placement, kernel):
     """dX over several 128-row tiles with straddling groups, a ragged tail and
     K spanning several column tiles; rows past the total are zero."""
     gs = [70, 0, 129, 200, 1, 0, 33]
     M = int(sum(gs)) + 50
     wl = workloads.custom(M, 512, 384, gs, seed=123, w_std=0.05, with_dy=True)
     out = torch.full((M, 512), float("nan"), dtype=out_dtype, device=DEV)
-    with tile_config(gmm.OP_DX, {"placement": placement}):
+    with tile_config(gmm.OP_DX, {"kernel": kernel, "placement": placement}):
         gmm.gmm_bf16_dx(wl.dy.to(DEV), wl.w.to(DEV), _gs(wl), out=out)
     ref = oracle.gmm_dx(workloads.as_f32(wl.dy), workloads.as_f32(wl.w), wl.group_sizes)
     o = to_np64(out)
     assert (o[int(sum(gs)):] == 0).all()
-    assert_bf16_parity(o, ref, "dx register path")
+    assert_bf16_parity(o, ref, "dx straddling")
 
 
 @pytest.mark.parametrize("skewed", [True, False])
-def test_tgmm_more_than_256_groups(skewed):
+@pytest.mark.parametrize("kernel", [1, 3])
+def test_tgmm_more_than_256_groups(skewed, kernel):
     """300 groups: tgmm's placement reads the sizes chunk by chunk from
     memory (above 256 groups), both with the skewed-routing placement (one
     group of 3000 rows, 8 tiles per group) and the default one."""
@@ -181,7 +188,8 @@ def test_tgmm_more_than_256_groups(skewed):
     wl = workloads.custom(M, 512, 256, sizes.tolist(), seed=133, with_dy=True)
     G = len(sizes)
     out = torch.full((G, 512, 256), float("nan"), dtype=torch.float32, device=DEV)
-    gmm.tgmm_bf16(wl.x.to(DEV), wl.dy.to(DEV), _gs(wl), out=out)
+    with tile_config(gmm.OP_TGMM, {"kernel": kernel}):
+        gmm.tgmm_bf16(wl.x.to(DEV), wl.dy.to(DEV), _gs(wl), out=out)
     ref = oracle.tgmm(workloads.as_f32(wl.x), workloads.as_f32(wl.dy), wl.group_sizes)
     o = to_np64(out)
     assert not np.isnan(o).any()
@@ -194,13 +202,15 @@ def test_tgmm_more_than_256_groups(skewed):
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
 def test_bf16_fwd_multi_round_grid(out_dtype):
     """A forward grid of more than two workgroups per CU (4096 rows, 2048
-    columns: 624 blocks), which takes the variant compiled for three resident
-    workgroups per CU; straddling groups, an empty one and a ragged tail."""
+    columns: 624 blocks), which takes kernel 1's variant compiled for three
+    resident workgroups per CU; straddling groups, an empty one and a ragged
+    tail."""
     gs = [700, 0, 1313, 1, 1000, 999]
     M = int(sum(gs)) + 83
     wl = workloads.custom(M, 256, 2048, gs, seed=211, w_std=0.05)
     out = torch.full((M, 2048), float("nan"), dtype=out_dtype, device=DEV)
-    gmm.gmm_bf16_fwd(wl.x.to(DEV), wl.w.to(DEV), _gs(wl), out=out)
+    with tile_config(gmm.OP_BF16_FWD, {"kernel": 1}):
+        gmm.gmm_bf16_fwd(wl.x.to(DEV), wl.w.to(DEV), _gs(wl), out=out)
     ref = oracle.gmm(workloads.as_f32(wl.x), workloads.as_f32(wl.w), wl.group_sizes)
     o = to_np64(out)
     assert (o[int(sum(gs)):] == 0).all()

@@ -21,9 +21,11 @@ def test_space_and_names():
     assert {c.get("placement") for c in fp8 if c.get("kernel") == 1} == {None, 2}
     assert {(c["tile_m"], c["tile_n"]) for c in fp8 if c.get("kernel") == 2} == {
         (m, n) for m in (48, 64) for n in (128, 256, 512)}
-    assert [c.get("placement") for c in tune.space("tgmm")] == [None, 1, 2, 1, 2, 1, 2]
-    assert [c.get("placement") for c in tune.space("dx")] == [None, 1, 2, 1, 2, None]
-    assert {c.get("kernel") for c in tune.space("dx")} == {None, 2}
+    assert [c.get("placement") for c in tune.space("tgmm")] == [None, 1, 2, 1, 2, 1, 2] + [1, 2] * 6
+    assert [c.get("placement") for c in tune.space("dx")] == [None, 1, 2, 1, 2, None] + [1, 2] * 6
+    assert {c.get("kernel") for c in tune.space("dx")} == {None, 2, 3}
+    assert {(c["depth"], c["residency"]) for c in tune.space("bf16_fwd") if c.get("kernel") == 3} == set(
+        tune.DMA_PAIRS)
     with pytest.raises(ValueError):
         tune.space("nope")
 
@@ -44,6 +46,48 @@ def test_candidates_follow_the_shape():
     dx = {tune.config_name(c) for c in tune.candidates("dx", (700, 384, 256, 6))}
     assert "kernel=2" not in dx                        # 256 x 256 tiles need K % 256 == 0
     assert "placement=1,residency=2" in tg
+    assert "depth=3,kernel=3,placement=1,residency=3" in tg
+    assert "depth=3,kernel=3,placement=2,residency=3" not in tg
+    assert {"depth=%d,kernel=3,placement=%d,residency=%d" % (d, p, r)
+            for d, r in tune.DMA_PAIRS for p in (1, 2)} <= dx
+
+
+def test_bf16_load_to_lds_kernel_config():
+    """kernel 3: depth = LDS stages, residency = workgroups per CU, in the
+    pairs the LDS holds (2 x 2, 3 x 1-3, 4 x 1-2; default 3 x 3); depth is
+    rejected on the other bf16 kernels."""
+    B, T = gmm.OP_BF16_FWD, gmm.OP_TGMM
+    nz = lambda d: {k: v for k, v in d.items() if v}
+    try:
+        gmm.set_tile_config(B, {"kernel": 3})
+        assert nz(gmm.get_tile_config(B, 8192, 2048, 512, 32)) == {
+            "kernel": 3, "depth": 3, "residency": 3, "placement": 1}
+        # kernel 3 keeps row tiles aligned to absolute rows at any grid size
+        # (production shape forward 265 us against 282 with group-start tiles)
+        assert nz(gmm.get_tile_config(B, 65536, 2048, 512, 256))["placement"] == 1
+        for d, r in tune.DMA_PAIRS:
+            gmm.set_tile_config(B, {"kernel": 3, "depth": d, "residency": r})
+            assert gmm.get_tile_config(B, 8192, 2048, 512, 32)["residency"] == r
+        gmm.set_tile_config(B, {"kernel": 3, "depth": 2})
+        assert gmm.get_tile_config(B, 8192, 2048, 512, 32)["residency"] == 2
+        gmm.set_tile_config(B, {"kernel": 3, "depth": 4})
+        assert gmm.get_tile_config(B, 8192, 2048, 512, 32)["residency"] == 2
+        for bad in ({"kernel": 3, "depth": 5}, {"kernel": 3, "depth": 1}, {"kernel": 3, "depth": 2, "residency": 3},
+                    {"kernel": 3, "depth": 4, "residency": 3}, {"kernel": 3, "depth": 2, "residency": 1},
+                    {"kernel": 1, "depth": 2}, {"kernel": 2, "depth": 2}, {"kernel": 4}):
+            with pytest.raises(gmm.GmmError):
+                gmm.set_tile_config(B, bad)
+                gmm.get_tile_config(B, 8192, 2048, 512, 32)
+        gmm.set_tile_config(B, {"depth": 2})              # depth alone: kernel 3
+        assert nz(gmm.get_tile_config(B, 8192, 2048, 512, 32))["kernel"] == 3
+        gmm.set_tile_config(B, {"residency": 2})          # residency alone: kernel 1
+        assert nz(gmm.get_tile_config(B, 8192, 2048, 512, 32)) == {"kernel": 1, "residency": 2, "placement": 1}
+        gmm.set_tile_config(T, {"kernel": 3, "depth": 3, "placement": 2})
+        assert nz(gmm.get_tile_config(T, 8192, 2048, 512, 32)) == {
+            "kernel": 3, "depth": 3, "residency": 3, "placement": 2}
+    finally:
+        gmm.set_tile_config(B, None)
+        gmm.set_tile_config(T, None)
 
 
 def test_library_default_choices():
@@ -60,9 +104,13 @@ def test_library_default_choices():
     assert nz(gmm.get_tile_config(F, 65536, 2048, 512, 256)) == {"kernel": 2, "tile_m": 64, "tile_n": 512}
     assert nz(gmm.get_tile_config(S, 8192, 2048, 512, 32)) == {"kernel": 2, "tile_m": 48, "tile_n": 256}
     assert nz(gmm.get_tile_config(X, 8192, 2048, 512, 32))["kernel"] == 1
-    assert nz(gmm.get_tile_config(B, 8192, 2048, 512, 32)) == {"kernel": 1, "residency": 2, "placement": 1}
-    assert nz(gmm.get_tile_config(T, 65536, 2048, 512, 256)) == {"kernel": 1, "residency": 3}
-    assert nz(gmm.get_tile_config(D, 8192, 2048, 512, 32)) == {"kernel": 1, "residency": 3, "placement": 2}
+    # bf16: the load-to-LDS kernel (3 stages x 3 workgroups per CU) for tgmm and for
+    # forward / dX grids of at most 8 workgroups per CU, the register-staged one beyond
+    dma = {"kernel": 3, "depth": 3, "residency": 3}
+    assert nz(gmm.get_tile_config(B, 8192, 2048, 512, 32)) == dict(dma, placement=1)
+    assert nz(gmm.get_tile_config(T, 65536, 2048, 512, 256)) == dma
+    assert nz(gmm.get_tile_config(T, 8192, 2048, 512, 32)) == dma
+    assert nz(gmm.get_tile_config(D, 8192, 2048, 512, 32)) == dict(dma, placement=1)
     assert nz(gmm.get_tile_config(D, 65536, 2048, 512, 256)) == {"kernel": 1, "residency": 3, "placement": 2}
     assert nz(gmm.get_tile_config(B, 65536, 2048, 512, 256)) == {"kernel": 1, "residency": 3, "placement": 2}
     assert all(v in (1, 2, 3) for v in gmm.get_tile_config(D, 8192, 2048, 512, 32).values() if v)
