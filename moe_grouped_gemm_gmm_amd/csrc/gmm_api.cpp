@@ -162,7 +162,7 @@ int gmm_set_tile_config(int op, const gmm_tile_config* cfg) {
             if (v == o) return true;
         return false;
     };
-    if (!in(c.kernel, {0, 1, 2, 3}) || !in(c.waves, {0, 8, 12, 16}) || !in(c.tile_m, {0, 48, 64}) ||
+    if (!in(c.kernel, {0, 1, 2, 3}) || !in(c.waves, {0, 4, 8, 12, 16}) || !in(c.tile_m, {0, 48, 64}) ||
         !in(c.tile_n, {0, 128, 256, 512}) || !in(c.depth, {0, 1, 2, 3, 4}) || !in(c.residency, {0, 1, 2, 3}) ||
         !in(c.placement, {0, 1, 2}))
         return fail(GMM_ERR_SHAPE, "a tile configuration field is out of range");

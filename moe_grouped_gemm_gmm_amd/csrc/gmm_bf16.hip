@@ -267,18 +267,19 @@ __device__ inline TgmmTile tgmm_tile(const int32_t* __restrict__ group_sizes, in
 
 // What one workgroup computes: output rows [lo, hi) of the tile starting at
 // row0 (forward / dX: rows of group g; tgmm: a K tile of group g's dW),
-// columns c0 .. c0 + TILE, reduction range [red_lo, red_hi).
+// columns c0 .. c0 + TC, reduction range [red_lo, red_hi).
 struct TileItem {
     int g, row0, lo, hi, c0, red_lo, red_hi;
 };
 
 // The prologue every bf16 kernel shares: block 0 writes the call's device
 // status word, wave 0 finds the work item (tgmm: the group and tile of
-// tgmm_tile; forward / dX: find_work_item over TILE-row items, placement 2
-// starting them at each group's first row) and the workgroup reads it from
-// s_info.  False when the workgroup has nothing more to do: no item, or rows
-// past the last group, which it has written as zeros.
-template <int MODE, bool OUT_BF16, int TILE, int NTHR>
+// tgmm_tile over TR x TC tiles; forward / dX: find_work_item over TR-row
+// items, placement 2 starting them at each group's first row, TC columns)
+// and the workgroup reads it from s_info.  False when the workgroup has
+// nothing more to do: no item, or rows past the last group, which it has
+// written as zeros.
+template <int MODE, bool OUT_BF16, int TR, int TC, int NTHR>
 __device__ __forceinline__ bool tile_item(const int32_t* __restrict__ group_sizes, int M, int K, int N, int G,
                                           void* __restrict__ out, int ntiles_c, int ntiles_r, int nblocks,
                                           int placement, int32_t* __restrict__ status, int* s_info, TileItem& it) {
@@ -299,32 +300,32 @@ __device__ __forceinline__ bool tile_item(const int32_t* __restrict__ group_size
         it.red_hi = s_info[1];
         it.g = s_info[2];
         if (it.g < 0) return false;
-        it.row0 = (s_info[3] / ntiles_c) * TILE;   // k tile
-        it.c0 = (s_info[3] % ntiles_c) * TILE;     // n tile
+        it.row0 = (s_info[3] / ntiles_c) * TR;   // k tile
+        it.c0 = (s_info[3] % ntiles_c) * TC;     // n tile
         it.lo = it.row0;
-        it.hi = it.row0 + TILE;
+        it.hi = it.row0 + TR;
         return true;
     } else {
         const int w = L / ntiles_c;
-        it.c0 = (L % ntiles_c) * TILE;
+        it.c0 = (L % ntiles_c) * TC;
         if (wave == 0) {
             // placement 2: row tiles start at each group's first row
-            const WorkItem wi = placement == 2 ? find_work_item<true>(group_sizes, G, M, TILE, w)
-                                               : find_work_item(group_sizes, G, M, TILE, w);
+            const WorkItem wi = placement == 2 ? find_work_item<true>(group_sizes, G, M, TR, w)
+                                               : find_work_item(group_sizes, G, M, TR, w);
             if (lane == 0) { s_info[0] = wi.g; s_info[1] = wi.tile; s_info[2] = wi.lo; s_info[3] = wi.hi; }
         }
         __syncthreads();
         it.g = s_info[0];
         if (it.g < 0) return false;
-        it.row0 = s_info[1] < 0 ? s_info[2] : s_info[1] * TILE;
+        it.row0 = s_info[1] < 0 ? s_info[2] : s_info[1] * TR;
         it.lo = s_info[2];
         it.hi = s_info[3];
         it.red_lo = 0;
         it.red_hi = MODE == kFwd ? K : N;
         if (it.g == G) {  // rows past the last group: zeros
             const int rows = it.hi - it.lo;
-            for (int e = tid; e < rows * (TILE / 8); e += NTHR) {
-                const int r = it.lo + e / (TILE / 8), c = it.c0 + (e % (TILE / 8)) * 8;
+            for (int e = tid; e < rows * (TC / 8); e += NTHR) {
+                const int r = it.lo + e / (TC / 8), c = it.c0 + (e % (TC / 8)) * 8;
                 if constexpr (OUT_BF16)
                     *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + (int64_t)r * out_cols + c) = make_uint4(0, 0, 0, 0);
                 else {
@@ -364,8 +365,8 @@ __global__ __launch_bounds__(256, MINB) void bf16_gemm_kernel(
     const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
     const int out_cols = MODE == kDx ? K : N;
     TileItem it;
-    if (!tile_item<MODE, OUT_BF16, kT, 256>(group_sizes, M, K, N, G, out, ntiles_c, ntiles_r, nblocks, placement,
-                                            status, s_info, it))
+    if (!tile_item<MODE, OUT_BF16, kT, kT, 256>(group_sizes, M, K, N, G, out, ntiles_c, ntiles_r, nblocks, placement,
+                                                status, s_info, it))
         return;
     const int g = it.g, row0 = it.row0, lo = it.lo, hi = it.hi, c0 = it.c0, red_lo = it.red_lo, red_hi = it.red_hi;
 
@@ -500,10 +501,10 @@ __global__ __launch_bounds__(256, MINB) void bf16_gemm_kernel(
 // A load-to-LDS instruction writes 1 KB of contiguous LDS, so the stage rows
 // cannot be padded; the bank spread comes from XOR swizzles instead:
 //  - direct [128][RD] slices (2 RD-byte rows): the 16-byte chunk c of row R
-//    sits at chunk c ^ dkey(R), dkey = R % 8 for 128-byte rows, (R / 4) % 4
+//    sits at chunk c ^ dkey(R), dkey = R % 8 for 128-byte rows, (R / 2) % 4
 //    for 64-byte rows.  A ds_read_b128 of 16 rows at one chunk then reads as
-//    fast as the padded 160-byte rows (measured ~205 B/clk/CU for the first;
-//    the second puts 16 rows on 16 distinct 16-byte bank groups).
+//    fast as the padded 160-byte rows (measured ~203 and ~202 B/clk/CU; with
+//    (R / 4) % 4, R % 4 or no swizzle the 64-byte rows read at 117-125).
 //  - transposed [RD][128] slices (256-byte rows): the 32-byte chunk k of row
 //    r sits at chunk k ^ key(r).  The two lane groups the LDS serves
 //    together read 8 rows at one chunk (read_tr's row sets), and key takes 8
@@ -513,13 +514,20 @@ __global__ __launch_bounds__(256, MINB) void bf16_gemm_kernel(
 // clamped to its last row, and the fragments' rows past the end are zeroed
 // in registers before the MFMAs.
 
-template <int S, int RES>
+template <int S, int RES, int WM>
 struct DmaShape {
-    static constexpr int kRD = RES * S * 32768 <= 163840 - 1024 ? 64 : 32;   // slice depth
-    static constexpr int kSlice = kT * kRD;               // bf16 elements of one operand's slice
-    static constexpr int kInstr = kSlice * 2 / 1024 / 4;  // load-to-LDS instructions per wave and operand
-    static constexpr int kChunks = kRD / 8;               // 16-byte chunks per direct row
-    static constexpr int kRows = 64 / kChunks;            // direct rows per instruction
+    static constexpr int kTR = 64 * WM;                  // tile rows (the A operand's dimension)
+    static constexpr int kTC = kT;                       // tile columns (the B operand's)
+    static constexpr int kWaves = 2 * WM;
+    static constexpr int kStage64 = (kTR + kTC) * 64 * 2;   // bytes of a 64-deep stage
+    static constexpr int kRD = RES * S * kStage64 <= 163840 - 1024 ? 64 : 32;   // slice depth
+    static constexpr int kSliceA = kTR * kRD;            // bf16 elements of A's slice
+    static constexpr int kSliceB = kTC * kRD;            // of B's
+    static constexpr int kStage = kSliceA + kSliceB;
+    static constexpr int kInstrA = kSliceA * 2 / 1024 / kWaves;   // load-to-LDS instructions per wave
+    static constexpr int kInstrB = kSliceB * 2 / 1024 / kWaves;
+    static constexpr int kChunks = kRD / 8;              // 16-byte chunks per direct row
+    static constexpr int kRows = 64 / kChunks;           // direct rows per instruction
 };
 
 // s_waitcnt vmcnt(N), the other counters untouched.
@@ -547,7 +555,7 @@ __device__ __forceinline__ int trans_key(int r) {
 
 template <int RD>
 __device__ __forceinline__ int direct_key(int R) {
-    return RD == 64 ? (R & 7) : ((R >> 2) & 3);
+    return RD == 64 ? (R & 7) : ((R >> 1) & 3);
 }
 
 // Direct fragment: 8 reduction values at chunk `chunk` of row `row`.
@@ -560,38 +568,38 @@ __device__ __forceinline__ v8bf swz_read_direct(const uint16_t* tile, int row, i
 // 32-deep blocks, two ds_read_b64_tr_b16 each, as read_tr lays them out.
 // addr[i] is the LDS byte address of fragment i's first read in block 0;
 // the second read sits HALF bytes on (rows +4 natural, +16 spread: the same
-// key, so the same swizzled chunk), block 1 8192 bytes on (rows +32).  One
+// key, so the same swizzled chunk), block 1 BLK bytes on (rows +32).  One
 // asm block that waits for its own reads before it ends (the
 // ds_read_b64_tr_b16 builtin makes the compiler drain every load-to-LDS load
 // in flight before it, which would flatten the ring).
 typedef unsigned long long u64;
 typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
-template <int NB, int HALF>
+template <int NB, int HALF, int BLK>
 __device__ __forceinline__ void tr_slice(v8bf (&f)[2][4], const unsigned (&addr)[4]) {
     if constexpr (NB == 2) {
         u64 o[16];
         asm volatile(
             "ds_read_b64_tr_b16 %0, %16\n\t"
             "ds_read_b64_tr_b16 %1, %16 offset:%20\n\t"
-            "ds_read_b64_tr_b16 %2, %16 offset:8192\n\t"
-            "ds_read_b64_tr_b16 %3, %16 offset:%21\n\t"
+            "ds_read_b64_tr_b16 %2, %16 offset:%21\n\t"
+            "ds_read_b64_tr_b16 %3, %16 offset:%22\n\t"
             "ds_read_b64_tr_b16 %4, %17\n\t"
             "ds_read_b64_tr_b16 %5, %17 offset:%20\n\t"
-            "ds_read_b64_tr_b16 %6, %17 offset:8192\n\t"
-            "ds_read_b64_tr_b16 %7, %17 offset:%21\n\t"
+            "ds_read_b64_tr_b16 %6, %17 offset:%21\n\t"
+            "ds_read_b64_tr_b16 %7, %17 offset:%22\n\t"
             "ds_read_b64_tr_b16 %8, %18\n\t"
             "ds_read_b64_tr_b16 %9, %18 offset:%20\n\t"
-            "ds_read_b64_tr_b16 %10, %18 offset:8192\n\t"
-            "ds_read_b64_tr_b16 %11, %18 offset:%21\n\t"
+            "ds_read_b64_tr_b16 %10, %18 offset:%21\n\t"
+            "ds_read_b64_tr_b16 %11, %18 offset:%22\n\t"
             "ds_read_b64_tr_b16 %12, %19\n\t"
             "ds_read_b64_tr_b16 %13, %19 offset:%20\n\t"
-            "ds_read_b64_tr_b16 %14, %19 offset:8192\n\t"
-            "ds_read_b64_tr_b16 %15, %19 offset:%21\n\t"
+            "ds_read_b64_tr_b16 %14, %19 offset:%21\n\t"
+            "ds_read_b64_tr_b16 %15, %19 offset:%22\n\t"
             "s_waitcnt lgkmcnt(0)"
             : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]),
               "=&v"(o[7]), "=&v"(o[8]), "=&v"(o[9]), "=&v"(o[10]), "=&v"(o[11]), "=&v"(o[12]), "=&v"(o[13]),
               "=&v"(o[14]), "=&v"(o[15])
-            : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]), "i"(HALF), "i"(8192 + HALF)
+            : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]), "i"(HALF), "i"(BLK), "i"(BLK + HALF)
             : "memory");
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -620,11 +628,12 @@ __device__ __forceinline__ void tr_slice(v8bf (&f)[2][4], const unsigned (&addr)
 }
 
 // LDS byte address (relative to the slice) of the first read of the
-// transposed fragment at columns c0 .. c0+15 in block 0, for this lane.
-template <bool kSpread>
+// transposed fragment at columns c0 .. c0+15 in block 0, for this lane, in
+// a slice of PITCH-element rows.
+template <bool kSpread, int PITCH>
 __device__ __forceinline__ unsigned tr_addr(int lg, int c0, int lr) {
     const int r = (kSpread ? 4 : 8) * lg + (lr >> 2);
-    return (unsigned)(2 * (r * kT + 16 * ((c0 >> 4) ^ trans_key<kSpread>(r)) + (lr & 3) * 4));
+    return (unsigned)(2 * (r * PITCH + 16 * ((c0 >> 4) ^ trans_key<kSpread>(r)) + (lr & 3) * 4));
 }
 
 // A transposed fragment of block s with the reduction rows at or past
@@ -643,86 +652,124 @@ __device__ __forceinline__ v8bf zero_rows_past(v8bf v, int s, int lg, int valid)
     return __builtin_bit_cast(v8bf, w);
 }
 
-template <int MODE, bool OUT_BF16, int S, int RES>
-__global__ __launch_bounds__(256, RES) void bf16_dma_kernel(
+// Where a lane's load-to-LDS instruction j of one operand's slice reads
+// from, relative to the slice's first reduction index.  The instruction
+// fills LDS bytes [1024 j, 1024 (j + 1)) of the slice; lane l's 16 bytes go
+// to byte 16 l of that kilobyte.
+//  direct (rows of 2 RD bytes): kRows rows per instruction, kChunks lanes
+//    per row; lane l writes row kRows j + l / kChunks at chunk position
+//    l % kChunks, so it loads chunk (l % kChunks) ^ dkey(row): `row` and
+//    the element offset `col` of that chunk within the row.
+//  transposed (rows of 2 PITCH bytes): 512 / PITCH rows per instruction,
+//    PITCH / 8 lanes per row; lane l writes row (512 / PITCH) j + l / (PITCH
+//    / 8) at 32-byte position p = (l % (PITCH / 8)) / 2, half l % 2, so it
+//    loads 32-byte chunk p ^ key(row), half l % 2: `row` (a reduction index
+//    within the slice) and `col`, the element offset within the tile.
+struct DmaLane {
+    int row, col;
+};
+template <int RD, int CHUNKS, int ROWS>
+__device__ __forceinline__ DmaLane dma_direct(int j, int lane) {
+    const int R = ROWS * j + lane / CHUNKS;
+    return DmaLane{R, 8 * ((lane % CHUNKS) ^ direct_key<RD>(R))};
+}
+template <bool kSpread, int PITCH>
+__device__ __forceinline__ DmaLane dma_trans(int j, int lane) {
+    constexpr int kLanesPerRow = PITCH / 8;
+    const int r = (512 / PITCH) * j + lane / kLanesPerRow;
+    const int p = (lane % kLanesPerRow) >> 1;
+    return DmaLane{r, 16 * (p ^ trans_key<kSpread>(r)) + 8 * (lane & 1)};
+}
+
+// WM x 2 waves of 64 x 64: a (64 WM) x 128 tile, WM = 2 or 4.  The second
+// launch bound is waves per SIMD: RES workgroups of WM / 2 waves per SIMD.
+template <int MODE, bool OUT_BF16, int S, int RES, int WM>
+__global__ __launch_bounds__(128 * WM, RES * WM / 2) void bf16_dma_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
     const int32_t* __restrict__ group_sizes, int M, int K, int N, int G, void* __restrict__ out,
     int ntiles_c, int ntiles_r, int nblocks, int placement, int32_t* __restrict__ status) {
-    using D = DmaShape<S, RES>;
-    constexpr int RD = D::kRD, kSl = D::kSlice, NI = D::kInstr, NB = RD / 32;
+    using D = DmaShape<S, RES, WM>;
+    constexpr int RD = D::kRD, TR = D::kTR, TC = D::kTC, NW = D::kWaves, NB = RD / 32;
+    constexpr int NIA = D::kInstrA, NIB = D::kInstrB, kSt = D::kStage;
+    static_assert(WM == 2 || WM == 4, "2 or 4 wave rows");
     static_assert(S >= 2 && S <= 4 && RES >= 1 && RES <= 3, "2 to 4 stages, 1 to 3 workgroups per CU");
-    static_assert(RES * S * 2 * kSl * 2 <= 163840 - 1024, "the rings of RES workgroups fit the LDS");
+    static_assert(RES * S * kSt * 2 <= 163840 - 1024, "the rings of RES workgroups fit the LDS");
+    static_assert(NIA >= 1 && NIB >= 1 && NIA * NW * 512 == D::kSliceA && NIB * NW * 512 == D::kSliceB,
+                  "whole load-to-LDS instructions per wave");
     constexpr int kEpiRow = 64 + 8;   // bf16 epilogue staging row (144 bytes)
-    static_assert(!OUT_BF16 || 4 * 64 * kEpiRow <= S * 2 * kSl, "epilogue staging fits the ring");
+    static_assert(!OUT_BF16 || NW * 64 * kEpiRow <= S * kSt, "epilogue staging fits the ring");
     constexpr bool A_TR = MODE == kTgmm;
     constexpr bool B_TR = MODE != kDx;
     constexpr bool kSpread = A_TR && B_TR;
-    __shared__ __attribute__((aligned(1024))) uint16_t ring[S * 2 * kSl];
+    __shared__ __attribute__((aligned(1024))) uint16_t ring[S * kSt];
     __shared__ int s_info[4];
 
     const int tid = threadIdx.x, lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int out_cols = MODE == kDx ? K : N;
     TileItem it;
-    if (!tile_item<MODE, OUT_BF16, kT, 256>(group_sizes, M, K, N, G, out, ntiles_c, ntiles_r, nblocks, placement,
-                                            status, s_info, it))
+    if (!tile_item<MODE, OUT_BF16, TR, TC, 64 * NW>(group_sizes, M, K, N, G, out, ntiles_c, ntiles_r, nblocks,
+                                                    placement, status, s_info, it))
         return;
     const int g = it.g, row0 = it.row0, lo = it.lo, hi = it.hi, c0 = it.c0, red_lo = it.red_lo, red_hi = it.red_hi;
 
-    // ---- this lane's share of a slice: NI load-to-LDS instructions per
-    //      operand and wave, instruction i of wave w filling LDS bytes
-    //      [1024 j, 1024 (j + 1)) of the operand's slice, j = NI w + i.
-    //  direct:     kRows rows per instruction, kChunks lanes per row: lane l
-    //              writes row kRows j + l / kChunks at chunk position
-    //              l % kChunks, so it loads chunk (l % kChunks) ^ dkey(row).
-    //  transposed: rows 4j .. 4j+3; lane l writes row 4j + l/16 at 32-byte
-    //              position (l % 16)/2, half l % 2, so it loads 32-byte
-    //              chunk ((l % 16)/2) ^ key(row), half l % 2.
+    // ---- this lane's share of a slice: NIA load-to-LDS instructions of A
+    //      and NIB of B per wave, instruction i of wave w being j = N w + i
+    //      of its operand (dma_direct / dma_trans)
     const int lda = MODE == kFwd ? K : N;
     const uint16_t* wg = B + (int64_t)(MODE == kTgmm ? 0 : g) * K * N;
-    int64_t a_off[NI], b_off[NI];   // element offsets of the slice at reduction index 0
-    int t_row[NI];                  // transposed operands: the slice row each instruction fills
+    int64_t a_off[NIA], b_off[NIB];   // element offsets of the slice at reduction index 0
+    int a_row[NIA], b_row[NIB];       // transposed operands: the slice row each instruction fills
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-        const int j = NI * wave + i;
-        const int R = D::kRows * j + lane / D::kChunks;                 // direct slice row
-        const int dchunk = (lane % D::kChunks) ^ direct_key<RD>(R);
-        const int r = 4 * j + (lane >> 4);                              // transposed slice row
-        const int tcol = 16 * (((lane & 15) >> 1) ^ trans_key<kSpread>(r)) + 8 * (lane & 1);
-        t_row[i] = r;
+    for (int i = 0; i < NIA; ++i) {
+        const int j = NIA * wave + i;
         if constexpr (MODE == kTgmm) {
-            a_off[i] = row0 + tcol;                          // x[m][k tile]
-            b_off[i] = c0 + tcol;                            // dy[m][n tile]
+            const DmaLane d = dma_trans<kSpread, TR>(j, lane);
+            a_row[i] = d.row;
+            a_off[i] = row0 + d.col;                            // x[m][k tile]
         } else {
-            const int arow = min(max(row0 + R, lo), hi - 1);
-            a_off[i] = (int64_t)arow * lda + 8 * dchunk;     // x or dy rows
-            if constexpr (MODE == kFwd)
-                b_off[i] = c0 + tcol;                        // w[g][k][n tile]
-            else
-                b_off[i] = (int64_t)(c0 + R) * N + 8 * dchunk;   // w[g][k tile][n]
+            const DmaLane d = dma_direct<RD, D::kChunks, D::kRows>(j, lane);
+            a_row[i] = 0;
+            const int arow = min(max(row0 + d.row, lo), hi - 1);
+            a_off[i] = (int64_t)arow * lda + d.col;             // x or dy rows
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < NIB; ++i) {
+        const int j = NIB * wave + i;
+        if constexpr (MODE == kDx) {
+            const DmaLane d = dma_direct<RD, D::kChunks, D::kRows>(j, lane);
+            b_row[i] = 0;
+            b_off[i] = (int64_t)(c0 + d.row) * N + d.col;       // w[g][k tile][n]
+        } else {
+            const DmaLane d = dma_trans<kSpread, TC>(j, lane);
+            b_row[i] = d.row;
+            b_off[i] = c0 + d.col;                              // w[g][k][n tile] or dy[m][n tile]
         }
     }
     auto issue = [&](int t, int stage) {
         const int r0 = red_lo + t * RD;
-        uint16_t* sa = ring + stage * 2 * kSl;
-        uint16_t* sb = sa + kSl;
+        uint16_t* sa = ring + stage * kSt;
+        uint16_t* sb = sa + D::kSliceA;
 #pragma unroll
-        for (int i = 0; i < NI; ++i) {
+        for (int i = 0; i < NIA; ++i) {
             const uint16_t* pa;
-            const uint16_t* pb;
-            if constexpr (MODE == kTgmm) {
-                const int64_t m = min(r0 + t_row[i], red_hi - 1);
-                pa = A + m * K + a_off[i];
-                pb = B + m * N + b_off[i];
-            } else {
+            if constexpr (MODE == kTgmm)
+                pa = A + (int64_t)min(r0 + a_row[i], red_hi - 1) * K + a_off[i];
+            else
                 pa = A + a_off[i] + r0;
-                if constexpr (MODE == kFwd)
-                    pb = wg + (int64_t)(r0 + t_row[i]) * N + b_off[i];
-                else
-                    pb = wg + b_off[i] + r0;
-            }
-            __builtin_amdgcn_global_load_lds(pa, (GMM_LDS void*)(sa + (NI * wave + i) * 512), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(pb, (GMM_LDS void*)(sb + (NI * wave + i) * 512), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(pa, (GMM_LDS void*)(sa + (NIA * wave + i) * 512), 16, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < NIB; ++i) {
+            const uint16_t* pb;
+            if constexpr (MODE == kTgmm)
+                pb = B + (int64_t)min(r0 + b_row[i], red_hi - 1) * N + b_off[i];
+            else if constexpr (MODE == kFwd)
+                pb = wg + (int64_t)(r0 + b_row[i]) * N + b_off[i];
+            else
+                pb = wg + b_off[i] + r0;
+            __builtin_amdgcn_global_load_lds(pb, (GMM_LDS void*)(sb + (NIB * wave + i) * 512), 16, 0, 0);
         }
     };
 
@@ -735,13 +782,14 @@ __global__ __launch_bounds__(256, RES) void bf16_dma_kernel(
         for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
     // transposed fragments' lane addresses within a slice (bytes)
-    constexpr int kHalf = (kSpread ? 16 : 4) * kT * 2;
+    constexpr int kHalfA = (kSpread ? 16 : 4) * TR * 2, kBlkA = 32 * TR * 2;
+    constexpr int kHalfB = (kSpread ? 16 : 4) * TC * 2, kBlkB = 32 * TC * 2;
     const unsigned ring_lds = (unsigned)(uintptr_t)(GMM_LDS uint16_t*)ring;
     unsigned a_tr[4], b_tr[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        a_tr[i] = tr_addr<kSpread>(lg, wm * 64 + i * 16, lr);
-        b_tr[i] = tr_addr<kSpread>(lg, wn * 64 + i * 16, lr);
+        a_tr[i] = tr_addr<kSpread, TR>(lg, wm * 64 + i * 16, lr);
+        b_tr[i] = tr_addr<kSpread, TC>(lg, wn * 64 + i * 16, lr);
     }
 
     const int nsl = (red_hi - red_lo + RD - 1) / RD;
@@ -753,24 +801,24 @@ __global__ __launch_bounds__(256, RES) void bf16_dma_kernel(
     int stage = 0;
     for (int t = 0; t < nsl; ++t) {
         // slice t landed in this wave's share once at most the loads of
-        // slices t+1 .. t+S-2 (2 NI per slice) are outstanding; the barrier
-        // then covers every wave's share, and every wave's reads of the
-        // stage the next issue overwrites (slice t - 1's)
-        if (t + S - 2 < nsl) wait_vmem<2 * NI * (S - 2)>(); else wait_vmem<0>();
+        // slices t+1 .. t+S-2 (NIA + NIB per slice) are outstanding; the
+        // barrier then covers every wave's share, and every wave's reads of
+        // the stage the next issue overwrites (slice t - 1's)
+        if (t + S - 2 < nsl) wait_vmem<(NIA + NIB) * (S - 2)>(); else wait_vmem<0>();
         stage_barrier();
         if (t + S - 1 < nsl) issue(t + S - 1, stage == 0 ? S - 1 : stage - 1);
-        const uint16_t* ta = ring + stage * 2 * kSl;
-        const uint16_t* tb = ta + kSl;
-        const unsigned sbase = ring_lds + (unsigned)(stage * 2 * kSl * 2);
+        const uint16_t* ta = ring + stage * kSt;
+        const uint16_t* tb = ta + D::kSliceA;
+        const unsigned sbase = ring_lds + (unsigned)(stage * kSt * 2);
         v8bf atr[2][4], btr[2][4];
         if constexpr (A_TR) {
             const unsigned ad[4] = {sbase + a_tr[0], sbase + a_tr[1], sbase + a_tr[2], sbase + a_tr[3]};
-            tr_slice<NB, kHalf>(atr, ad);
+            tr_slice<NB, kHalfA, kBlkA>(atr, ad);
         }
         if constexpr (B_TR) {
-            const unsigned bs = sbase + (unsigned)(kSl * 2);
+            const unsigned bs = sbase + (unsigned)(D::kSliceA * 2);
             const unsigned bd[4] = {bs + b_tr[0], bs + b_tr[1], bs + b_tr[2], bs + b_tr[3]};
-            tr_slice<NB, kHalf>(btr, bd);
+            tr_slice<NB, kHalfB, kBlkB>(btr, bd);
         }
         const int valid = red_hi - (red_lo + t * RD);   // tgmm: real rows of this slice
 #pragma unroll
@@ -842,27 +890,30 @@ __global__ __launch_bounds__(256, RES) void bf16_dma_kernel(
     }
 }
 
-template <int MODE, int S, int RES>
+template <int MODE, int S, int RES, int WM>
 hipError_t launch_dma(const void* A, const void* B, const int32_t* group_sizes, int M, int K, int N, int G,
                       void* out, bool out_bf16, int placement, int32_t* status, hipStream_t stream) {
+    constexpr int TR = 64 * WM;
     int ntiles_c, ntiles_r = 0;
     int64_t nblocks;
     if constexpr (MODE == kTgmm) {
-        ntiles_r = K / kT;
+        ntiles_r = K / TR;
         ntiles_c = N / kT;
         nblocks = (int64_t)G * ntiles_r * ntiles_c;
     } else {
         ntiles_c = (MODE == kFwd ? N : K) / kT;
-        nblocks = max_work_items(M, G, kT) * ntiles_c;
+        nblocks = max_work_items(M, G, TR) * ntiles_c;
     }
     const uint16_t* a = reinterpret_cast<const uint16_t*>(A);
     const uint16_t* b = reinterpret_cast<const uint16_t*>(B);
     if (out_bf16)
-        hipLaunchKernelGGL((bf16_dma_kernel<MODE, true, S, RES>), dim3((unsigned)nblocks), dim3(256), 0, stream,
-                           a, b, group_sizes, M, K, N, G, out, ntiles_c, ntiles_r, (int)nblocks, placement, status);
+        hipLaunchKernelGGL((bf16_dma_kernel<MODE, true, S, RES, WM>), dim3((unsigned)nblocks), dim3(128 * WM), 0,
+                           stream, a, b, group_sizes, M, K, N, G, out, ntiles_c, ntiles_r, (int)nblocks, placement,
+                           status);
     else
-        hipLaunchKernelGGL((bf16_dma_kernel<MODE, false, S, RES>), dim3((unsigned)nblocks), dim3(256), 0, stream,
-                           a, b, group_sizes, M, K, N, G, out, ntiles_c, ntiles_r, (int)nblocks, placement, status);
+        hipLaunchKernelGGL((bf16_dma_kernel<MODE, false, S, RES, WM>), dim3((unsigned)nblocks), dim3(128 * WM), 0,
+                           stream, a, b, group_sizes, M, K, N, G, out, ntiles_c, ntiles_r, (int)nblocks, placement,
+                           status);
     return hipGetLastError();
 }
 
@@ -926,7 +977,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void bf16_wide_kernel(
     const int out_cols = MODE == kDx ? K : N;
     TileItem it;
     // forward / dX rows come in items starting at each group's first row
-    if (!tile_item<MODE, OUT_BF16, kTW, kThr>(group_sizes, M, K, N, G, out, ntiles_c, ntiles_r, nblocks,
+    if (!tile_item<MODE, OUT_BF16, kTW, kTW, kThr>(group_sizes, M, K, N, G, out, ntiles_c, ntiles_r, nblocks,
                                               MODE == kTgmm ? placement : 2, status, s_info, it))
         return;
     const int g = it.g, row0 = it.row0, lo = it.lo, hi = it.hi, c0 = it.c0, red_lo = it.red_lo, red_hi = it.red_hi;
@@ -1089,14 +1140,15 @@ hipError_t launch_mode(const TileConfig& cfg, const void* A, const void* B,
                        bool out_bf16, int32_t* status, hipStream_t stream) {
     if (cfg.kernel == 2)
         return launch_wide<MODE, 8>(A, B, group_sizes, M, K, N, G, out, out_bf16, cfg.placement, status, stream);
-    if (cfg.kernel == 3) {   // (depth, residency) pairs as gmm_config.cpp accepts them
+    if (cfg.kernel == 3) {   // (waves, depth, residency) as gmm_config.cpp accepts them
         const int d = cfg.depth, r = cfg.residency;
-        if (d == 2) return launch_dma<MODE, 2, 2>(A, B, group_sizes, M, K, N, G, out, out_bf16, cfg.placement, status, stream);
-        if (d == 3 && r == 1) return launch_dma<MODE, 3, 1>(A, B, group_sizes, M, K, N, G, out, out_bf16, cfg.placement, status, stream);
-        if (d == 3 && r == 2) return launch_dma<MODE, 3, 2>(A, B, group_sizes, M, K, N, G, out, out_bf16, cfg.placement, status, stream);
-        if (d == 3) return launch_dma<MODE, 3, 3>(A, B, group_sizes, M, K, N, G, out, out_bf16, cfg.placement, status, stream);
-        if (r == 1) return launch_dma<MODE, 4, 1>(A, B, group_sizes, M, K, N, G, out, out_bf16, cfg.placement, status, stream);
-        return launch_dma<MODE, 4, 2>(A, B, group_sizes, M, K, N, G, out, out_bf16, cfg.placement, status, stream);
+        if (cfg.waves == 8) return launch_dma<MODE, 3, 2, 4>(A, B, group_sizes, M, K, N, G, out, out_bf16, cfg.placement, status, stream);
+        if (d == 2) return launch_dma<MODE, 2, 2, 2>(A, B, group_sizes, M, K, N, G, out, out_bf16, cfg.placement, status, stream);
+        if (d == 3 && r == 1) return launch_dma<MODE, 3, 1, 2>(A, B, group_sizes, M, K, N, G, out, out_bf16, cfg.placement, status, stream);
+        if (d == 3 && r == 2) return launch_dma<MODE, 3, 2, 2>(A, B, group_sizes, M, K, N, G, out, out_bf16, cfg.placement, status, stream);
+        if (d == 3) return launch_dma<MODE, 3, 3, 2>(A, B, group_sizes, M, K, N, G, out, out_bf16, cfg.placement, status, stream);
+        if (r == 1) return launch_dma<MODE, 4, 1, 2>(A, B, group_sizes, M, K, N, G, out, out_bf16, cfg.placement, status, stream);
+        return launch_dma<MODE, 4, 2, 2>(A, B, group_sizes, M, K, N, G, out, out_bf16, cfg.placement, status, stream);
     }
     int ntiles_c, ntiles_r = 0;
     int64_t nblocks;

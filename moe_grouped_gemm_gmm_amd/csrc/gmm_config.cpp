@@ -72,6 +72,9 @@ bool resolve_fp8(const TileConfig& f, int64_t M, int64_t K, int64_t N, int64_t G
             c->kernel = kKerWs;
             c->tile_m = 48;
             c->tile_n = 512;
+            if (f.waves && f.waves != 8 && f.waves != 12 && f.waves != 16)
+                return fail(why, "the warp-specialised kernel runs 8, 12 or 16 waves");
+            if (f.depth && f.depth != 1 && f.depth != 2) return fail(why, "depth (weight steps in flight) is 1 or 2");
             c->waves = f.waves ? f.waves : (write_q ? 8 : 16);
             c->depth = f.depth ? f.depth : 1;
             if (write_q && c->waves != 8) return fail(why, "writing the LHS codes takes the 8-wave form");
@@ -172,8 +175,10 @@ bool resolve_swiglu(const TileConfig& f, int64_t M, int64_t N, int64_t G, TileCo
 bool resolve_bf16(int op, const TileConfig& f, int64_t M, int64_t K, int64_t N, int64_t G,
                   TileConfig* c, const char** why) {
     *c = TileConfig{};
-    if (f.waves || f.tile_m || f.tile_n)
-        return fail(why, "the bf16 calls set kernel, residency, depth and placement only");
+    if (f.tile_m || f.tile_n)
+        return fail(why, "the bf16 calls set kernel, waves, residency, depth and placement only");
+    if (f.waves && (f.kernel != 3 || (f.waves != 4 && f.waves != 8)))
+        return fail(why, "waves (4 or 8) applies to bf16 kernel 3 only");
     if (f.kernel && (f.kernel < 1 || f.kernel > 3))
         return fail(why, "bf16 kernels are 1 (128 x 128), 2 (256 x 256) or 3 (128 x 128 fed by load-to-LDS)");
     if (f.depth && f.kernel && f.kernel != 3) return fail(why, "depth applies to bf16 kernel 3 only");
@@ -198,8 +203,17 @@ bool resolve_bf16(int op, const TileConfig& f, int64_t M, int64_t K, int64_t N, 
         }
         return true;
     }
-    const int64_t nblocks = op == kOpTgmm ? G * (K / 128) * (N / 128)
-                                          : items(M, G, 128) * ((op == kOpDx ? K : N) / 128);
+    // kernel 3 with 8 waves: 256-row tiles (tgmm: 256 K-rows), 128 columns.
+    // The library's tgmm takes them whenever K allows (no padded rows there:
+    // backward shape 31.3 -> 30.4 us, production shape 295 -> 275 us); the
+    // forward and dX keep 128-row items (256-row items pad the rows of
+    // groups near 256 rows: backward-shape forward 34 -> 50 us).
+    const bool tgmm8 = op == kOpTgmm && !f.kernel && !f.waves && !f.depth && !f.residency && K % 256 == 0;
+    const int waves = f.waves ? f.waves : (tgmm8 ? 8 : 0);
+    const int64_t tr = waves == 8 ? 256 : 128;
+    if (op == kOpTgmm && K % tr != 0) return fail(why, "8-wave tgmm tiles need K to be a multiple of 256");
+    const int64_t nblocks = op == kOpTgmm ? G * (K / tr) * (N / 128)
+                                          : items(M, G, tr) * ((op == kOpDx ? K : N) / 128);
     const int64_t cus = device_cus();
     // The library's kernel: depth implies 3, residency alone 1.  Otherwise 3
     // (3 stages of 32-deep slices, three workgroups per CU) for tgmm and for
@@ -213,13 +227,17 @@ bool resolve_bf16(int op, const TileConfig& f, int64_t M, int64_t K, int64_t N, 
         // LDS stages x workgroups per CU: 64-deep slices (32 KB stages) when
         // the rings fit, else 32-deep (16 KB): 2 x 2, 3 x 1, 4 x 1 (64-deep),
         // 3 x 2, 3 x 3, 4 x 2 (32-deep)
+        // 8 waves (256 x 128 tiles): 3 stages of 32-deep slices, 2 per CU
         if (f.depth && (f.depth < 2 || f.depth > 4)) return fail(why, "depth (LDS stages) is 2, 3 or 4");
         c->kernel = 3;
+        c->waves = waves ? waves : 4;
         c->depth = f.depth ? f.depth : 3;
-        const int def = c->depth == 2 ? 2 : (c->depth == 3 ? 3 : 2);
+        const int def = c->waves == 8 ? 2 : (c->depth == 2 ? 2 : (c->depth == 3 ? 3 : 2));
         const int res = f.residency ? f.residency : def;
-        const bool ok = c->depth == 2 ? res == 2 : (c->depth == 3 ? res >= 1 && res <= 3 : res == 1 || res == 2);
-        if (!ok) return fail(why, "kernel 3 pairs depth 2 with residency 2, 3 with 1-3, 4 with 1-2");
+        const bool ok = c->waves == 8 ? c->depth == 3 && res == 2
+                                      : (c->depth == 2 ? res == 2 : (c->depth == 3 ? res >= 1 && res <= 3 : res == 1 || res == 2));
+        if (!ok)
+            return fail(why, "kernel 3 pairs depth 2 with residency 2, 3 with 1-3, 4 with 1-2; with 8 waves depth 3, residency 2");
         c->residency = res;
     } else {
         c->kernel = 1;
@@ -228,7 +246,7 @@ bool resolve_bf16(int op, const TileConfig& f, int64_t M, int64_t K, int64_t N, 
     }
     if (op == kOpTgmm) {
         if (f.placement && f.placement != 1 && f.placement != 2) return fail(why, "placement is 1 or 2");
-        if (f.placement == 2 && ((K / 128) * (N / 128)) % 8 != 0)
+        if (f.placement == 2 && ((K / tr) * (N / 128)) % 8 != 0)
             return fail(why, "spreading a group over the XCDs needs a multiple of 8 tiles per group");
         c->placement = f.placement;   // 0: decided in the kernel from the group sizes
     } else {

@@ -22,10 +22,11 @@ gmm_set_tile_config (include/gmm.h):
                              tiles aligned to absolute rows or to each group's first
                              row; 256 x 256 tiles (8 waves, one workgroup per CU);
                              128 x 128 tiles fed by load-to-LDS: (LDS stages,
-                             workgroups per CU) pairs x row placement
+                             workgroups per CU) pairs x row placement, and its
+                             8-wave 256 x 128 tiles x row placement
   tgmm                       128 x 128 tiles: residency 2/3 x placement (whole groups
                              per XCD, groups spread over the XCDs); 256 x 256 tiles x
-                             placement; load-to-LDS tiles, (stages, workgroups) x placement
+                             placement; load-to-LDS tiles, (stages, workgroups) and 8 waves x placement
 
 The space is small enough to enumerate, so the search is exhaustive rather
 than evolutionary.  Stages (Q9.4):
@@ -106,6 +107,8 @@ def space(phase: str) -> List[Dict[str, int]]:
         for depth, res in DMA_PAIRS:
             for pl in (1, 2):
                 out.append({"kernel": 3, "depth": depth, "residency": res, "placement": pl})
+        for pl in (1, 2):
+            out.append({"kernel": 3, "waves": 8, "placement": pl})
     else:
         for res in (2, 3):
             for pl in (1, 2):
@@ -114,6 +117,8 @@ def space(phase: str) -> List[Dict[str, int]]:
         for depth, res in DMA_PAIRS:
             for pl in (1, 2):
                 out.append({"kernel": 3, "depth": depth, "residency": res, "placement": pl})
+        for pl in (1, 2):
+            out.append({"kernel": 3, "waves": 8, "placement": pl})
     return out
 
 

@@ -21,11 +21,12 @@ def test_space_and_names():
     assert {c.get("placement") for c in fp8 if c.get("kernel") == 1} == {None, 2}
     assert {(c["tile_m"], c["tile_n"]) for c in fp8 if c.get("kernel") == 2} == {
         (m, n) for m in (48, 64) for n in (128, 256, 512)}
-    assert [c.get("placement") for c in tune.space("tgmm")] == [None, 1, 2, 1, 2, 1, 2] + [1, 2] * 6
-    assert [c.get("placement") for c in tune.space("dx")] == [None, 1, 2, 1, 2, None] + [1, 2] * 6
+    assert [c.get("placement") for c in tune.space("tgmm")] == [None, 1, 2, 1, 2, 1, 2] + [1, 2] * 7
+    assert [c.get("placement") for c in tune.space("dx")] == [None, 1, 2, 1, 2, None] + [1, 2] * 7
+    assert [c.get("waves") for c in tune.space("bf16_fwd") if c.get("kernel") == 3].count(8) == 2
     assert {c.get("kernel") for c in tune.space("dx")} == {None, 2, 3}
-    assert {(c["depth"], c["residency"]) for c in tune.space("bf16_fwd") if c.get("kernel") == 3} == set(
-        tune.DMA_PAIRS)
+    assert {(c["depth"], c["residency"]) for c in tune.space("bf16_fwd")
+            if c.get("kernel") == 3 and "depth" in c} == set(tune.DMA_PAIRS)
     with pytest.raises(ValueError):
         tune.space("nope")
 
@@ -50,6 +51,10 @@ def test_candidates_follow_the_shape():
     assert "depth=3,kernel=3,placement=2,residency=3" not in tg
     assert {"depth=%d,kernel=3,placement=%d,residency=%d" % (d, p, r)
             for d, r in tune.DMA_PAIRS for p in (1, 2)} <= dx
+    assert "kernel=3,placement=1,waves=8" in dx
+    assert "kernel=3,placement=1,waves=8" in tg
+    tg384 = {tune.config_name(c) for c in tune.candidates("tgmm", (700, 384, 256, 6))}
+    assert "kernel=3,placement=1,waves=8" not in tg384   # 8-wave tgmm tiles need K % 256 == 0
 
 
 def test_bf16_load_to_lds_kernel_config():
@@ -61,7 +66,7 @@ def test_bf16_load_to_lds_kernel_config():
     try:
         gmm.set_tile_config(B, {"kernel": 3})
         assert nz(gmm.get_tile_config(B, 8192, 2048, 512, 32)) == {
-            "kernel": 3, "depth": 3, "residency": 3, "placement": 1}
+            "kernel": 3, "waves": 4, "depth": 3, "residency": 3, "placement": 1}
         # kernel 3 keeps row tiles aligned to absolute rows at any grid size
         # (production shape forward 265 us against 282 with group-start tiles)
         assert nz(gmm.get_tile_config(B, 65536, 2048, 512, 256))["placement"] == 1
@@ -84,10 +89,31 @@ def test_bf16_load_to_lds_kernel_config():
         assert nz(gmm.get_tile_config(B, 8192, 2048, 512, 32)) == {"kernel": 1, "residency": 2, "placement": 1}
         gmm.set_tile_config(T, {"kernel": 3, "depth": 3, "placement": 2})
         assert nz(gmm.get_tile_config(T, 8192, 2048, 512, 32)) == {
-            "kernel": 3, "depth": 3, "residency": 3, "placement": 2}
+            "kernel": 3, "waves": 4, "depth": 3, "residency": 3, "placement": 2}
+        # 8 waves: 256 x 128 tiles, 3 stages, two workgroups per CU
+        gmm.set_tile_config(B, {"kernel": 3, "waves": 8})
+        assert nz(gmm.get_tile_config(B, 8192, 2048, 512, 32)) == {
+            "kernel": 3, "waves": 8, "depth": 3, "residency": 2, "placement": 1}
+        gmm.set_tile_config(T, {"kernel": 3, "waves": 8})
+        assert gmm.get_tile_config(T, 8192, 2048, 512, 32)["waves"] == 8
+        with pytest.raises(gmm.GmmError):
+            gmm.get_tile_config(T, 8192, 384, 512, 32)       # K not a multiple of 256
+        gmm.set_tile_config(T, {"kernel": 3, "waves": 8, "placement": 2})
+        with pytest.raises(gmm.GmmError):                    # 2 x 2 tiles per group cannot spread over 8 XCDs
+            gmm.get_tile_config(T, 8192, 512, 256, 32)
+        assert gmm.get_tile_config(T, 8192, 2048, 512, 32)["placement"] == 2
+        for bad in ({"kernel": 3, "waves": 8, "depth": 2}, {"kernel": 3, "waves": 8, "residency": 3},
+                    {"kernel": 3, "waves": 6}, {"kernel": 1, "waves": 8}, {"waves": 4}):
+            with pytest.raises(gmm.GmmError):
+                gmm.set_tile_config(B, bad)
+                gmm.get_tile_config(B, 8192, 2048, 512, 32)
+        with pytest.raises(gmm.GmmError):                    # the FP8 forward has no 4-wave form
+            gmm.set_tile_config(gmm.OP_FP8_FWD, {"kernel": 1, "waves": 4})
+            gmm.get_tile_config(gmm.OP_FP8_FWD, 8192, 2048, 512, 32)
     finally:
         gmm.set_tile_config(B, None)
         gmm.set_tile_config(T, None)
+        gmm.set_tile_config(gmm.OP_FP8_FWD, None)
 
 
 def test_library_default_choices():
@@ -104,16 +130,19 @@ def test_library_default_choices():
     assert nz(gmm.get_tile_config(F, 65536, 2048, 512, 256)) == {"kernel": 2, "tile_m": 64, "tile_n": 512}
     assert nz(gmm.get_tile_config(S, 8192, 2048, 512, 32)) == {"kernel": 2, "tile_m": 48, "tile_n": 256}
     assert nz(gmm.get_tile_config(X, 8192, 2048, 512, 32))["kernel"] == 1
-    # bf16: the load-to-LDS kernel (3 stages x 3 workgroups per CU) for tgmm and for
-    # forward / dX grids of at most 8 workgroups per CU, the register-staged one beyond
-    dma = {"kernel": 3, "depth": 3, "residency": 3}
+    # bf16: the load-to-LDS kernel (3 stages x 3 workgroups per CU) for forward / dX
+    # grids of at most 8 workgroups per CU, the register-staged one beyond
+    dma = {"kernel": 3, "waves": 4, "depth": 3, "residency": 3}
     assert nz(gmm.get_tile_config(B, 8192, 2048, 512, 32)) == dict(dma, placement=1)
-    assert nz(gmm.get_tile_config(T, 65536, 2048, 512, 256)) == dma
-    assert nz(gmm.get_tile_config(T, 8192, 2048, 512, 32)) == dma
+    # tgmm: the 8-wave 256 x 128 tiles when K is a multiple of 256
+    dma8 = {"kernel": 3, "waves": 8, "depth": 3, "residency": 2}
+    assert nz(gmm.get_tile_config(T, 65536, 2048, 512, 256)) == dma8
+    assert nz(gmm.get_tile_config(T, 8192, 2048, 512, 32)) == dma8
+    assert nz(gmm.get_tile_config(T, 8192, 384, 512, 32)) == dma
     assert nz(gmm.get_tile_config(D, 8192, 2048, 512, 32)) == dict(dma, placement=1)
     assert nz(gmm.get_tile_config(D, 65536, 2048, 512, 256)) == {"kernel": 1, "residency": 3, "placement": 2}
     assert nz(gmm.get_tile_config(B, 65536, 2048, 512, 256)) == {"kernel": 1, "residency": 3, "placement": 2}
-    assert all(v in (1, 2, 3) for v in gmm.get_tile_config(D, 8192, 2048, 512, 32).values() if v)
+    assert all(v in (1, 2, 3, 4) for v in gmm.get_tile_config(D, 8192, 2048, 512, 32).values() if v)
 
 
 def test_set_tile_config_checks_fields_and_fit():
