@@ -514,11 +514,11 @@ __global__ __launch_bounds__(256, MINB) void bf16_gemm_kernel(
 // clamped to its last row, and the fragments' rows past the end are zeroed
 // in registers before the MFMAs.
 
-template <int S, int RES, int WM>
+template <int S, int RES, int WM, int WN>
 struct DmaShape {
     static constexpr int kTR = 64 * WM;                  // tile rows (the A operand's dimension)
-    static constexpr int kTC = kT;                       // tile columns (the B operand's)
-    static constexpr int kWaves = 2 * WM;
+    static constexpr int kTC = 64 * WN;                  // tile columns (the B operand's)
+    static constexpr int kWaves = WM * WN;
     static constexpr int kStage64 = (kTR + kTC) * 64 * 2;   // bytes of a 64-deep stage
     static constexpr int kRD = RES * S * kStage64 <= 163840 - 1024 ? 64 : 32;   // slice depth
     static constexpr int kSliceA = kTR * kRD;            // bf16 elements of A's slice
@@ -681,17 +681,18 @@ __device__ __forceinline__ DmaLane dma_trans(int j, int lane) {
     return DmaLane{r, 16 * (p ^ trans_key<kSpread>(r)) + 8 * (lane & 1)};
 }
 
-// WM x 2 waves of 64 x 64: a (64 WM) x 128 tile, WM = 2 or 4.  The second
-// launch bound is waves per SIMD: RES workgroups of WM / 2 waves per SIMD.
-template <int MODE, bool OUT_BF16, int S, int RES, int WM>
-__global__ __launch_bounds__(128 * WM, RES * WM / 2) void bf16_dma_kernel(
+// WM x WN waves of 64 x 64: a (64 WM) x (64 WN) tile, 2 x 2, 4 x 2 or
+// 2 x 4.  The second launch bound is waves per SIMD: RES workgroups of
+// WM WN / 4 waves per SIMD.
+template <int MODE, bool OUT_BF16, int S, int RES, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN, RES * WM * WN / 4) void bf16_dma_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
     const int32_t* __restrict__ group_sizes, int M, int K, int N, int G, void* __restrict__ out,
     int ntiles_c, int ntiles_r, int nblocks, int placement, int32_t* __restrict__ status) {
-    using D = DmaShape<S, RES, WM>;
+    using D = DmaShape<S, RES, WM, WN>;
     constexpr int RD = D::kRD, TR = D::kTR, TC = D::kTC, NW = D::kWaves, NB = RD / 32;
     constexpr int NIA = D::kInstrA, NIB = D::kInstrB, kSt = D::kStage;
-    static_assert(WM == 2 || WM == 4, "2 or 4 wave rows");
+    static_assert((WM == 2 && WN == 2) || (WM == 4 && WN == 2) || (WM == 2 && WN == 4), "2 x 2, 4 x 2 or 2 x 4 waves");
     static_assert(S >= 2 && S <= 4 && RES >= 1 && RES <= 3, "2 to 4 stages, 1 to 3 workgroups per CU");
     static_assert(RES * S * kSt * 2 <= 163840 - 1024, "the rings of RES workgroups fit the LDS");
     static_assert(NIA >= 1 && NIB >= 1 && NIA * NW * 512 == D::kSliceA && NIB * NW * 512 == D::kSliceB,
@@ -773,7 +774,7 @@ __global__ __launch_bounds__(128 * WM, RES * WM / 2) void bf16_dma_kernel(
         }
     };
 
-    const int wm = (tid >> 6) >> 1, wn = (tid >> 6) & 1;
+    const int wm = (tid >> 6) / WN, wn = (tid >> 6) % WN;
     const int lr = lane & 15, lg = lane >> 4;
     v4f acc[4][4];
 #pragma unroll
@@ -890,28 +891,28 @@ __global__ __launch_bounds__(128 * WM, RES * WM / 2) void bf16_dma_kernel(
     }
 }
 
-template <int MODE, int S, int RES, int WM>
+template <int MODE, int S, int RES, int WM, int WN>
 hipError_t launch_dma(const void* A, const void* B, const int32_t* group_sizes, int M, int K, int N, int G,
                       void* out, bool out_bf16, int placement, int32_t* status, hipStream_t stream) {
-    constexpr int TR = 64 * WM;
+    constexpr int TR = 64 * WM, TC = 64 * WN;
     int ntiles_c, ntiles_r = 0;
     int64_t nblocks;
     if constexpr (MODE == kTgmm) {
         ntiles_r = K / TR;
-        ntiles_c = N / kT;
+        ntiles_c = N / TC;
         nblocks = (int64_t)G * ntiles_r * ntiles_c;
     } else {
-        ntiles_c = (MODE == kFwd ? N : K) / kT;
+        ntiles_c = (MODE == kFwd ? N : K) / TC;
         nblocks = max_work_items(M, G, TR) * ntiles_c;
     }
     const uint16_t* a = reinterpret_cast<const uint16_t*>(A);
     const uint16_t* b = reinterpret_cast<const uint16_t*>(B);
     if (out_bf16)
-        hipLaunchKernelGGL((bf16_dma_kernel<MODE, true, S, RES, WM>), dim3((unsigned)nblocks), dim3(128 * WM), 0,
+        hipLaunchKernelGGL((bf16_dma_kernel<MODE, true, S, RES, WM, WN>), dim3((unsigned)nblocks), dim3(64 * WM * WN), 0,
                            stream, a, b, group_sizes, M, K, N, G, out, ntiles_c, ntiles_r, (int)nblocks, placement,
                            status);
     else
-        hipLaunchKernelGGL((bf16_dma_kernel<MODE, false, S, RES, WM>), dim3((unsigned)nblocks), dim3(128 * WM), 0,
+        hipLaunchKernelGGL((bf16_dma_kernel<MODE, false, S, RES, WM, WN>), dim3((unsigned)nblocks), dim3(64 * WM * WN), 0,
                            stream, a, b, group_sizes, M, K, N, G, out, ntiles_c, ntiles_r, (int)nblocks, placement,
                            status);
     return hipGetLastError();
@@ -1142,13 +1143,15 @@ hipError_t launch_mode(const TileConfig& cfg, const void* A, const void* B,
         return launch_wide<MODE, 8>(A, B, group_sizes, M, K, N, G, out, out_bf16, cfg.placement, status, stream);
     if (cfg.kernel == 3) {   // (waves, depth, residency) as gmm_config.cpp accepts them
         const int d = cfg.depth, r = cfg.residency;
-        if (cfg.waves == 8) return launch_dma<MODE, 3, 2, 4>(A, B, group_sizes, M, K, N, G, out, out_bf16, cfg.placement, status, stream);
-        if (d == 2) return launch_dma<MODE, 2, 2, 2>(A, B, group_sizes, M, K, N, G, out, out_bf16, cfg.placement, status, stream);
-        if (d == 3 && r == 1) return launch_dma<MODE, 3, 1, 2>(A, B, group_sizes, M, K, N, G, out, out_bf16, cfg.placement, status, stream);
-        if (d == 3 && r == 2) return launch_dma<MODE, 3, 2, 2>(A, B, group_sizes, M, K, N, G, out, out_bf16, cfg.placement, status, stream);
-        if (d == 3) return launch_dma<MODE, 3, 3, 2>(A, B, group_sizes, M, K, N, G, out, out_bf16, cfg.placement, status, stream);
-        if (r == 1) return launch_dma<MODE, 4, 1, 2>(A, B, group_sizes, M, K, N, G, out, out_bf16, cfg.placement, status, stream);
-        return launch_dma<MODE, 4, 2, 2>(A, B, group_sizes, M, K, N, G, out, out_bf16, cfg.placement, status, stream);
+        if (cfg.waves == 8 && cfg.tile_n == 256)
+            return launch_dma<MODE, 3, 2, 2, 4>(A, B, group_sizes, M, K, N, G, out, out_bf16, cfg.placement, status, stream);
+        if (cfg.waves == 8) return launch_dma<MODE, 3, 2, 4, 2>(A, B, group_sizes, M, K, N, G, out, out_bf16, cfg.placement, status, stream);
+        if (d == 2) return launch_dma<MODE, 2, 2, 2, 2>(A, B, group_sizes, M, K, N, G, out, out_bf16, cfg.placement, status, stream);
+        if (d == 3 && r == 1) return launch_dma<MODE, 3, 1, 2, 2>(A, B, group_sizes, M, K, N, G, out, out_bf16, cfg.placement, status, stream);
+        if (d == 3 && r == 2) return launch_dma<MODE, 3, 2, 2, 2>(A, B, group_sizes, M, K, N, G, out, out_bf16, cfg.placement, status, stream);
+        if (d == 3) return launch_dma<MODE, 3, 3, 2, 2>(A, B, group_sizes, M, K, N, G, out, out_bf16, cfg.placement, status, stream);
+        if (r == 1) return launch_dma<MODE, 4, 1, 2, 2>(A, B, group_sizes, M, K, N, G, out, out_bf16, cfg.placement, status, stream);
+        return launch_dma<MODE, 4, 2, 2, 2>(A, B, group_sizes, M, K, N, G, out, out_bf16, cfg.placement, status, stream);
     }
     int ntiles_c, ntiles_r = 0;
     int64_t nblocks;

@@ -175,10 +175,11 @@ bool resolve_swiglu(const TileConfig& f, int64_t M, int64_t N, int64_t G, TileCo
 bool resolve_bf16(int op, const TileConfig& f, int64_t M, int64_t K, int64_t N, int64_t G,
                   TileConfig* c, const char** why) {
     *c = TileConfig{};
-    if (f.tile_m || f.tile_n)
-        return fail(why, "the bf16 calls set kernel, waves, residency, depth and placement only");
+    if (f.tile_m) return fail(why, "the bf16 calls set kernel, waves, tile_n, residency, depth and placement only");
     if (f.waves && (f.kernel != 3 || (f.waves != 4 && f.waves != 8)))
         return fail(why, "waves (4 or 8) applies to bf16 kernel 3 only");
+    if (f.tile_n && (f.waves != 8 || (f.tile_n != 128 && f.tile_n != 256)))
+        return fail(why, "tile_n (128 or 256) applies to bf16 kernel 3 with 8 waves");
     if (f.kernel && (f.kernel < 1 || f.kernel > 3))
         return fail(why, "bf16 kernels are 1 (128 x 128), 2 (256 x 256) or 3 (128 x 128 fed by load-to-LDS)");
     if (f.depth && f.kernel && f.kernel != 3) return fail(why, "depth applies to bf16 kernel 3 only");
@@ -203,26 +204,45 @@ bool resolve_bf16(int op, const TileConfig& f, int64_t M, int64_t K, int64_t N, 
         }
         return true;
     }
-    // kernel 3 with 8 waves: 256-row tiles (tgmm: 256 K-rows), 128 columns.
-    // The library's tgmm takes them whenever K allows (no padded rows there:
-    // backward shape 31.3 -> 30.4 us, production shape 295 -> 275 us); the
-    // forward and dX keep 128-row items (256-row items pad the rows of
-    // groups near 256 rows: backward-shape forward 34 -> 50 us).
-    const bool tgmm8 = op == kOpTgmm && !f.kernel && !f.waves && !f.depth && !f.residency && K % 256 == 0;
-    const int waves = f.waves ? f.waves : (tgmm8 ? 8 : 0);
-    const int64_t tr = waves == 8 ? 256 : 128;
-    if (op == kOpTgmm && K % tr != 0) return fail(why, "8-wave tgmm tiles need K to be a multiple of 256");
-    const int64_t nblocks = op == kOpTgmm ? G * (K / tr) * (N / 128)
-                                          : items(M, G, tr) * ((op == kOpDx ? K : N) / 128);
+    // The library's choice (no kernel, waves, tile_n, depth or residency set;
+    // placement may be), from measurements against kernel 1's best on one box:
+    //  - tgmm: kernel 3 with 8 waves in 256 x 128 tiles when K is a multiple
+    //    of 256, else 128 x 128 (backward shape 32.3 -> 30.4 us, production
+    //    shape 303 -> 271 us);
+    //  - forward / dX grids of at most eight 128 x 128 workgroups per CU:
+    //    kernel 3, 128 x 128 tiles, 3 stages, three workgroups per CU
+    //    (backward shape forward 39.9 -> 33.9 us, dX 37.4 -> 36.1);
+    //  - larger forward / dX grids: kernel 3 with 8 waves in 128 x 256 tiles,
+    //    which halve the re-reads of the row operand (production shape
+    //    forward 257 -> 234 us, dX 273 -> 261); kernel 1 if the tiled
+    //    columns are not a multiple of 256.
+    // 256-row tiles pad the rows of groups near 256 rows, so the forward and
+    // dX never take them by default (backward-shape forward 34 -> 50 us).
+    // Set fields: depth implies kernel 3, residency alone kernel 1.
     const int64_t cus = device_cus();
-    // The library's kernel: depth implies 3, residency alone 1.  Otherwise 3
-    // (3 stages of 32-deep slices, three workgroups per CU) for tgmm and for
-    // forward / dX grids of at most eight workgroups per CU, 1 beyond (measured
-    // against kernel 1's best: backward shape forward 39.9 -> 33.9 us, tgmm
-    // 32.3 -> 30.3, dX 37.4 -> 36.1; production shape tgmm 303 -> 294, but
-    // forward 254 -> 265 and dX 273 -> 286 with 12 or more per CU).
-    const int kernel = f.kernel ? f.kernel
-                                : (f.depth ? 3 : (f.residency ? 1 : (op == kOpTgmm || nblocks <= 8 * cus ? 3 : 1)));
+    const int64_t cols = op == kOpDx ? K : N;
+    const int64_t nb128 = op == kOpTgmm ? G * (K / 128) * (N / 128) : items(M, G, 128) * (cols / 128);
+    int kernel = f.kernel, waves = f.waves, tile_n = f.tile_n;
+    if (!f.kernel && !f.waves && !f.tile_n && !f.depth && !f.residency) {
+        kernel = 3;
+        if (op == kOpTgmm) {
+            if (K % 256 == 0) waves = 8, tile_n = 128;
+        } else if (nb128 > 8 * cus) {
+            if (cols % 256 == 0)
+                waves = 8, tile_n = 256;
+            else
+                kernel = 1;
+        }
+    } else if (!kernel) {
+        kernel = f.depth ? 3 : 1;
+    }
+    // kernel 3 with 8 waves: 256 x 128 tiles (tile_n 128; tgmm: 256 K-rows)
+    // or 128 x 256 (tile_n 256)
+    const int64_t tc = waves == 8 && tile_n == 256 ? 256 : 128;
+    const int64_t tr = waves == 8 && tc == 128 ? 256 : 128;
+    if (op == kOpTgmm && K % tr != 0) return fail(why, "256 x 128 tgmm tiles need K to be a multiple of 256");
+    if (cols % tc != 0) return fail(why, "128 x 256 tiles need the tiled columns to be a multiple of 256");
+    const int64_t nblocks = op == kOpTgmm ? G * (K / tr) * (N / tc) : items(M, G, tr) * (cols / tc);
     if (kernel == 3) {
         // LDS stages x workgroups per CU: 64-deep slices (32 KB stages) when
         // the rings fit, else 32-deep (16 KB): 2 x 2, 3 x 1, 4 x 1 (64-deep),
@@ -231,6 +251,7 @@ bool resolve_bf16(int op, const TileConfig& f, int64_t M, int64_t K, int64_t N, 
         if (f.depth && (f.depth < 2 || f.depth > 4)) return fail(why, "depth (LDS stages) is 2, 3 or 4");
         c->kernel = 3;
         c->waves = waves ? waves : 4;
+        c->tile_n = c->waves == 8 ? (int)tc : 0;
         c->depth = f.depth ? f.depth : 3;
         const int def = c->waves == 8 ? 2 : (c->depth == 2 ? 2 : (c->depth == 3 ? 3 : 2));
         const int res = f.residency ? f.residency : def;
@@ -246,18 +267,20 @@ bool resolve_bf16(int op, const TileConfig& f, int64_t M, int64_t K, int64_t N, 
     }
     if (op == kOpTgmm) {
         if (f.placement && f.placement != 1 && f.placement != 2) return fail(why, "placement is 1 or 2");
-        if (f.placement == 2 && ((K / tr) * (N / 128)) % 8 != 0)
+        if (f.placement == 2 && ((K / tr) * (N / tc)) % 8 != 0)
             return fail(why, "spreading a group over the XCDs needs a multiple of 8 tiles per group");
         c->placement = f.placement;   // 0: decided in the kernel from the group sizes
     } else {
         // forward and dX: 1 row tiles aligned to absolute rows, 2 row tiles
         // starting at each group's first row.  Group-start tiles leave fewer
         // partly used tiles, which pays once the grid takes more than two
-        // rounds of the chip at three workgroups per CU (measured: production
-        // shape dX 284 -> 275 us, forward 264 -> 257 us; at the backward shape
-        // the same or 0.5% slower)
+        // rounds of the chip (kernel 1, production shape: dX 284 -> 275 us,
+        // forward 264 -> 257 us; kernel 3's 128 x 256 tiles: dX 263 -> 261,
+        // forward the same); kernel 3's 128 x 128 tiles keep 1 (production
+        // forward 265 against 282 us)
         if (f.placement && f.placement != 1 && f.placement != 2) return fail(why, "placement is 1 or 2");
-        c->placement = f.placement ? f.placement : (kernel == 1 && nblocks > 6 * cus ? 2 : 1);
+        const bool big = nblocks > 6 * cus && (kernel == 1 || waves == 8);
+        c->placement = f.placement ? f.placement : (big ? 2 : 1);
     }
     return true;
 }

@@ -23,10 +23,11 @@ gmm_set_tile_config (include/gmm.h):
                              row; 256 x 256 tiles (8 waves, one workgroup per CU);
                              128 x 128 tiles fed by load-to-LDS: (LDS stages,
                              workgroups per CU) pairs x row placement, and its
-                             8-wave 256 x 128 tiles x row placement
+                             8-wave 256 x 128 and 128 x 256 tiles x row placement
   tgmm                       128 x 128 tiles: residency 2/3 x placement (whole groups
                              per XCD, groups spread over the XCDs); 256 x 256 tiles x
-                             placement; load-to-LDS tiles, (stages, workgroups) and 8 waves x placement
+                             placement; load-to-LDS tiles, (stages, workgroups) and both 8-wave
+                             shapes x placement
 
 The space is small enough to enumerate, so the search is exhaustive rather
 than evolutionary.  Stages (Q9.4):
@@ -109,6 +110,8 @@ def space(phase: str) -> List[Dict[str, int]]:
                 out.append({"kernel": 3, "depth": depth, "residency": res, "placement": pl})
         for pl in (1, 2):
             out.append({"kernel": 3, "waves": 8, "placement": pl})
+        for pl in (1, 2):
+            out.append({"kernel": 3, "waves": 8, "tile_n": 256, "placement": pl})
     else:
         for res in (2, 3):
             for pl in (1, 2):
@@ -119,6 +122,8 @@ def space(phase: str) -> List[Dict[str, int]]:
                 out.append({"kernel": 3, "depth": depth, "residency": res, "placement": pl})
         for pl in (1, 2):
             out.append({"kernel": 3, "waves": 8, "placement": pl})
+        for pl in (1, 2):
+            out.append({"kernel": 3, "waves": 8, "tile_n": 256, "placement": pl})
     return out
 
 

@@ -1,6 +1,7 @@
 """GPU parity of the load-to-LDS bf16 kernel (tile configuration kernel=3:
 every accepted pair of depth = LDS stages and residency = workgroups per CU,
-so both slice depths, 64 and 32, and the 8-wave 256 x 128 tiles) for the
+so both slice depths, 64 and 32, and the 8-wave 256 x 128 and 128 x 256
+tiles) for the
 forward, dX and tgmm against the fp64 oracle, at the bf16 bar |gpu - ref| <= 1e-3 + 2e-2 |ref| ("GEMM Kernel
 性能优化十问", Q5: the backward is unquantised bf16 with fp32 accumulation):
 ragged and empty groups, single rows, groups spanning several 128-row
@@ -31,8 +32,18 @@ CASES = [
 ]
 PAIRS = [(2, 2), (3, 1), (4, 1), (3, 2), (3, 3), (4, 2)]   # (depth, residency)
 # every kernel-3 form: the (depth, residency) pairs of 4 waves, and 8 waves
-FORMS = [{"depth": d, "residency": r} for d, r in PAIRS] + [{"waves": 8}]
-FORM_IDS = ["d%dr%d" % p for p in PAIRS] + ["w8"]
+FORMS = [{"depth": d, "residency": r} for d, r in PAIRS] + [{"waves": 8}, {"waves": 8, "tile_n": 256}]
+FORM_IDS = ["d%dr%d" % p for p in PAIRS] + ["w8", "w8n256"]
+
+
+def _fits(form, rows_k, cols):
+    """Whether a form's tiles fit: 256 x 128 tgmm tiles need K % 256 == 0
+    (rows_k), 128 x 256 tiles the tiled columns % 256 == 0 (cols)."""
+    if form.get("tile_n") == 256:
+        return cols % 256 == 0
+    if form.get("waves") == 8:
+        return rows_k is None or rows_k % 256 == 0
+    return True
 
 
 def _gs(wl):
@@ -44,6 +55,8 @@ def _gs(wl):
 @pytest.mark.parametrize("form", FORMS, ids=FORM_IDS)
 @pytest.mark.parametrize("placement", [1, 2])
 def test_forward(M, K, N, gs, out_dtype, form, placement):
+    if not _fits(form, None, N):
+        pytest.skip("128 x 256 tiles need N % 256 == 0 (the library rejects this N)")
     wl = workloads.custom(M, K, N, gs, seed=M + K + form.get("depth", 8), w_std=0.05)
     out = torch.full((M, N), float("nan"), dtype=out_dtype, device=DEV)
     with tile_config(gmm.OP_BF16_FWD, dict(form, kernel=3, placement=placement)):
@@ -59,6 +72,8 @@ def test_forward(M, K, N, gs, out_dtype, form, placement):
 @pytest.mark.parametrize("form", FORMS, ids=FORM_IDS)
 @pytest.mark.parametrize("placement", [1, 2])
 def test_dx(M, K, N, gs, out_dtype, form, placement):
+    if not _fits(form, None, K):
+        pytest.skip("128 x 256 tiles need K % 256 == 0 (the library rejects this K)")
     wl = workloads.custom(M, K, N, gs, seed=M + 2 * K + form.get("depth", 8), w_std=0.05, with_dy=True)
     out = torch.full((M, K), float("nan"), dtype=out_dtype, device=DEV)
     with tile_config(gmm.OP_DX, dict(form, kernel=3, placement=placement)):
@@ -74,8 +89,8 @@ def test_dx(M, K, N, gs, out_dtype, form, placement):
 @pytest.mark.parametrize("form", FORMS, ids=FORM_IDS)
 @pytest.mark.parametrize("placement", [0, 1])
 def test_tgmm(M, K, N, gs, out_dtype, form, placement):
-    if form.get("waves") == 8 and K % 256:
-        pytest.skip("8-wave tgmm tiles are 256 K-rows high (the library rejects this K)")
+    if not _fits(form, K, N):
+        pytest.skip("this form's tgmm tiles do not divide K x N (the library rejects the shape)")
     wl = workloads.custom(M, K, N, gs, seed=M + 3 * K + form.get("depth", 8), with_dy=True)
     G = len(gs)
     out = torch.full((G, K, N), float("nan"), dtype=out_dtype, device=DEV)
@@ -100,7 +115,7 @@ def test_tgmm_slice_tail_reads_nothing_past_the_group(form):
     Huge values in the rows past the total, and infinities written into the
     next group's rows of x for a call that only sees group 0's rows, must not
     reach any output."""
-    wl = workloads.custom(300, 256, 128, [100, 150], seed=31, with_dy=True)
+    wl = workloads.custom(300, 256, 256, [100, 150], seed=31, with_dy=True)
     x = wl.x.clone()
     x[250:] = 1e30
     with tile_config(gmm.OP_TGMM, dict(form, kernel=3)):
@@ -152,7 +167,7 @@ def test_production_shape_full():
     ref_dx = oracle.gmm_dx(dys, ws, wl.group_sizes)
     ref_dw = oracle.tgmm(xs, dys, wl.group_sizes)
     ref_y = oracle.gmm(xs, ws, wl.group_sizes)
-    for cfg in ({"kernel": 3}, {"kernel": 3, "waves": 8}):
+    for cfg in ({"kernel": 3}, {"kernel": 3, "waves": 8}, {"kernel": 3, "waves": 8, "tile_n": 256}):
         with tile_config(gmm.OP_DX, cfg):
             dx = gmm.gmm_bf16_dx(dy, w, g)
         with tile_config(gmm.OP_TGMM, cfg):

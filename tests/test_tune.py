@@ -21,9 +21,9 @@ def test_space_and_names():
     assert {c.get("placement") for c in fp8 if c.get("kernel") == 1} == {None, 2}
     assert {(c["tile_m"], c["tile_n"]) for c in fp8 if c.get("kernel") == 2} == {
         (m, n) for m in (48, 64) for n in (128, 256, 512)}
-    assert [c.get("placement") for c in tune.space("tgmm")] == [None, 1, 2, 1, 2, 1, 2] + [1, 2] * 7
-    assert [c.get("placement") for c in tune.space("dx")] == [None, 1, 2, 1, 2, None] + [1, 2] * 7
-    assert [c.get("waves") for c in tune.space("bf16_fwd") if c.get("kernel") == 3].count(8) == 2
+    assert [c.get("placement") for c in tune.space("tgmm")] == [None, 1, 2, 1, 2, 1, 2] + [1, 2] * 8
+    assert [c.get("placement") for c in tune.space("dx")] == [None, 1, 2, 1, 2, None] + [1, 2] * 8
+    assert [c.get("waves") for c in tune.space("bf16_fwd") if c.get("kernel") == 3].count(8) == 4
     assert {c.get("kernel") for c in tune.space("dx")} == {None, 2, 3}
     assert {(c["depth"], c["residency"]) for c in tune.space("bf16_fwd")
             if c.get("kernel") == 3 and "depth" in c} == set(tune.DMA_PAIRS)
@@ -52,6 +52,9 @@ def test_candidates_follow_the_shape():
     assert {"depth=%d,kernel=3,placement=%d,residency=%d" % (d, p, r)
             for d, r in tune.DMA_PAIRS for p in (1, 2)} <= dx
     assert "kernel=3,placement=1,waves=8" in dx
+    assert "kernel=3,placement=1,tile_n=256,waves=8" not in dx          # 128 x 256 dX tiles need K % 256 == 0
+    dx512 = {tune.config_name(c) for c in tune.candidates("dx", (700, 512, 256, 6))}
+    assert "kernel=3,placement=1,tile_n=256,waves=8" in dx512
     assert "kernel=3,placement=1,waves=8" in tg
     tg384 = {tune.config_name(c) for c in tune.candidates("tgmm", (700, 384, 256, 6))}
     assert "kernel=3,placement=1,waves=8" not in tg384   # 8-wave tgmm tiles need K % 256 == 0
@@ -93,7 +96,7 @@ def test_bf16_load_to_lds_kernel_config():
         # 8 waves: 256 x 128 tiles, 3 stages, two workgroups per CU
         gmm.set_tile_config(B, {"kernel": 3, "waves": 8})
         assert nz(gmm.get_tile_config(B, 8192, 2048, 512, 32)) == {
-            "kernel": 3, "waves": 8, "depth": 3, "residency": 2, "placement": 1}
+            "kernel": 3, "waves": 8, "tile_n": 128, "depth": 3, "residency": 2, "placement": 1}
         gmm.set_tile_config(T, {"kernel": 3, "waves": 8})
         assert gmm.get_tile_config(T, 8192, 2048, 512, 32)["waves"] == 8
         with pytest.raises(gmm.GmmError):
@@ -102,8 +105,15 @@ def test_bf16_load_to_lds_kernel_config():
         with pytest.raises(gmm.GmmError):                    # 2 x 2 tiles per group cannot spread over 8 XCDs
             gmm.get_tile_config(T, 8192, 512, 256, 32)
         assert gmm.get_tile_config(T, 8192, 2048, 512, 32)["placement"] == 2
+        gmm.set_tile_config(B, {"kernel": 3, "waves": 8, "tile_n": 256})     # 128 x 256 tiles
+        assert nz(gmm.get_tile_config(B, 8192, 2048, 512, 32)) == {
+            "kernel": 3, "waves": 8, "tile_n": 256, "depth": 3, "residency": 2, "placement": 1}
+        with pytest.raises(gmm.GmmError):
+            gmm.get_tile_config(B, 8192, 2048, 384, 32)      # N not a multiple of 256
         for bad in ({"kernel": 3, "waves": 8, "depth": 2}, {"kernel": 3, "waves": 8, "residency": 3},
-                    {"kernel": 3, "waves": 6}, {"kernel": 1, "waves": 8}, {"waves": 4}):
+                    {"kernel": 3, "waves": 6}, {"kernel": 1, "waves": 8}, {"waves": 4},
+                    {"kernel": 3, "tile_n": 256}, {"kernel": 3, "waves": 4, "tile_n": 256},
+                    {"kernel": 3, "waves": 8, "tile_n": 512}, {"kernel": 3, "waves": 8, "tile_m": 128}):
             with pytest.raises(gmm.GmmError):
                 gmm.set_tile_config(B, bad)
                 gmm.get_tile_config(B, 8192, 2048, 512, 32)
@@ -131,17 +141,21 @@ def test_library_default_choices():
     assert nz(gmm.get_tile_config(S, 8192, 2048, 512, 32)) == {"kernel": 2, "tile_m": 48, "tile_n": 256}
     assert nz(gmm.get_tile_config(X, 8192, 2048, 512, 32))["kernel"] == 1
     # bf16: the load-to-LDS kernel (3 stages x 3 workgroups per CU) for forward / dX
-    # grids of at most 8 workgroups per CU, the register-staged one beyond
+    # grids of at most 8 workgroups per CU
     dma = {"kernel": 3, "waves": 4, "depth": 3, "residency": 3}
     assert nz(gmm.get_tile_config(B, 8192, 2048, 512, 32)) == dict(dma, placement=1)
     # tgmm: the 8-wave 256 x 128 tiles when K is a multiple of 256
-    dma8 = {"kernel": 3, "waves": 8, "depth": 3, "residency": 2}
+    dma8 = {"kernel": 3, "waves": 8, "tile_n": 128, "depth": 3, "residency": 2}
     assert nz(gmm.get_tile_config(T, 65536, 2048, 512, 256)) == dma8
     assert nz(gmm.get_tile_config(T, 8192, 2048, 512, 32)) == dma8
     assert nz(gmm.get_tile_config(T, 8192, 384, 512, 32)) == dma
     assert nz(gmm.get_tile_config(D, 8192, 2048, 512, 32)) == dict(dma, placement=1)
-    assert nz(gmm.get_tile_config(D, 65536, 2048, 512, 256)) == {"kernel": 1, "residency": 3, "placement": 2}
-    assert nz(gmm.get_tile_config(B, 65536, 2048, 512, 256)) == {"kernel": 1, "residency": 3, "placement": 2}
+    # larger forward / dX grids: the 8-wave 128 x 256 tiles, row tiles from each group's start
+    wide = {"kernel": 3, "waves": 8, "tile_n": 256, "depth": 3, "residency": 2, "placement": 2}
+    assert nz(gmm.get_tile_config(D, 65536, 2048, 512, 256)) == wide
+    assert nz(gmm.get_tile_config(B, 65536, 2048, 512, 256)) == wide
+    # ... and kernel 1 where the tiled columns are not a multiple of 256
+    assert nz(gmm.get_tile_config(B, 65536, 2048, 384, 256)) == {"kernel": 1, "residency": 3, "placement": 2}
     assert all(v in (1, 2, 3, 4) for v in gmm.get_tile_config(D, 8192, 2048, 512, 32).values() if v)
 
 
