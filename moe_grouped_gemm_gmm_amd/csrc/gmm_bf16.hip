@@ -530,24 +530,6 @@ struct DmaShape {
     static constexpr int kRows = 64 / kChunks;           // direct rows per instruction
 };
 
-// s_waitcnt vmcnt(N), the other counters untouched.
-template <int N>
-__device__ __forceinline__ void wait_vmem() {
-    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
-}
-
-// A workgroup barrier that leaves the vector memory counter alone (the
-// release fence of __syncthreads waits for every load in flight, load-to-LDS
-// ones included).  The wavefront fences keep the compiler from moving LDS
-// accesses across it; the lgkmcnt wait completes this wave's LDS reads first.
-__device__ __forceinline__ void stage_barrier() {
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 template <bool kSpread>
 __device__ __forceinline__ int trans_key(int r) {
     return kSpread ? (r & 7) : ((r & 3) | ((r >> 1) & 4));

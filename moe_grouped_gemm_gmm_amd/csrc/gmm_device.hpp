@@ -366,6 +366,24 @@ __host__ __device__ inline int64_t max_work_items(int64_t M, int64_t G, int64_t 
     return (M + tm - 1) / tm + G + 1;
 }
 
+// s_waitcnt vmcnt(N), the other counters untouched.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// A workgroup barrier that leaves the vector memory counter alone (the
+// release fence of __syncthreads waits for every load in flight, load-to-LDS
+// ones included, which would drain a ring of such loads).  The wavefront fences keep the compiler from moving LDS
+// accesses across it; the lgkmcnt wait completes this wave's LDS reads first.
+__device__ __forceinline__ void stage_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // ----------------------------------------------------------- XCD remap --
 // Workgroups are dispatched round-robin over the 8 XCDs (block b runs on XCD
 // b % 8), each with its own L2.  Remap so that consecutive logical ids run on
