@@ -609,6 +609,79 @@ __device__ __forceinline__ void tr_slice(v8bf (&f)[2][4], const unsigned (&addr)
     }
 }
 
+// Both operands' transposed reads of a 32-deep slice (tgmm) in one asm
+// block, so the slice waits on the LDS once: fragments i = 0..3 of A at
+// aa[i] (second read HALF_A bytes on) and of B at ba[i] (HALF_B on).
+template <int HALF_A, int HALF_B>
+__device__ __forceinline__ void tr_slice_pair(v8bf (&fa)[4], v8bf (&fb)[4], const unsigned (&aa)[4],
+                                              const unsigned (&ba)[4]) {
+    u64 o[16];
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %16\n\t"
+        "ds_read_b64_tr_b16 %1, %16 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %2, %17\n\t"
+        "ds_read_b64_tr_b16 %3, %17 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %4, %18\n\t"
+        "ds_read_b64_tr_b16 %5, %18 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %6, %19\n\t"
+        "ds_read_b64_tr_b16 %7, %19 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %8, %20\n\t"
+        "ds_read_b64_tr_b16 %9, %20 offset:%25\n\t"
+        "ds_read_b64_tr_b16 %10, %21\n\t"
+        "ds_read_b64_tr_b16 %11, %21 offset:%25\n\t"
+        "ds_read_b64_tr_b16 %12, %22\n\t"
+        "ds_read_b64_tr_b16 %13, %22 offset:%25\n\t"
+        "ds_read_b64_tr_b16 %14, %23\n\t"
+        "ds_read_b64_tr_b16 %15, %23 offset:%25\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]),
+          "=&v"(o[7]), "=&v"(o[8]), "=&v"(o[9]), "=&v"(o[10]), "=&v"(o[11]), "=&v"(o[12]), "=&v"(o[13]),
+          "=&v"(o[14]), "=&v"(o[15])
+        : "v"(aa[0]), "v"(aa[1]), "v"(aa[2]), "v"(aa[3]), "v"(ba[0]), "v"(ba[1]), "v"(ba[2]), "v"(ba[3]),
+          "i"(HALF_A), "i"(HALF_B)
+        : "memory");
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        fa[i] = __builtin_bit_cast(v8bf, u64x2{o[2 * i], o[2 * i + 1]});
+        fb[i] = __builtin_bit_cast(v8bf, u64x2{o[8 + 2 * i], o[8 + 2 * i + 1]});
+    }
+}
+
+// The forward's reads of a 32-deep slice in one asm block (one wait): A's
+// four direct fragments (16 bytes at da[i]) and B's transposed ones (at
+// ba[i], second read HALF_B bytes on).
+template <int HALF_B>
+__device__ __forceinline__ void direct_tr_slice(v8bf (&fa)[4], v8bf (&fb)[4], const unsigned (&da)[4],
+                                                const unsigned (&ba)[4]) {
+    v4i d0, d1, d2, d3;
+    u64 o[8];
+    asm volatile(
+        "ds_read_b128 %0, %12\n\t"
+        "ds_read_b128 %1, %13\n\t"
+        "ds_read_b128 %2, %14\n\t"
+        "ds_read_b128 %3, %15\n\t"
+        "ds_read_b64_tr_b16 %4, %16\n\t"
+        "ds_read_b64_tr_b16 %5, %16 offset:%20\n\t"
+        "ds_read_b64_tr_b16 %6, %17\n\t"
+        "ds_read_b64_tr_b16 %7, %17 offset:%20\n\t"
+        "ds_read_b64_tr_b16 %8, %18\n\t"
+        "ds_read_b64_tr_b16 %9, %18 offset:%20\n\t"
+        "ds_read_b64_tr_b16 %10, %19\n\t"
+        "ds_read_b64_tr_b16 %11, %19 offset:%20\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(d0), "=&v"(d1), "=&v"(d2), "=&v"(d3), "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]),
+          "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7])
+        : "v"(da[0]), "v"(da[1]), "v"(da[2]), "v"(da[3]), "v"(ba[0]), "v"(ba[1]), "v"(ba[2]), "v"(ba[3]),
+          "i"(HALF_B)
+        : "memory");
+    fa[0] = __builtin_bit_cast(v8bf, d0);
+    fa[1] = __builtin_bit_cast(v8bf, d1);
+    fa[2] = __builtin_bit_cast(v8bf, d2);
+    fa[3] = __builtin_bit_cast(v8bf, d3);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fb[i] = __builtin_bit_cast(v8bf, u64x2{o[2 * i], o[2 * i + 1]});
+}
+
 // LDS byte address (relative to the slice) of the first read of the
 // transposed fragment at columns c0 .. c0+15 in block 0, for this lane, in
 // a slice of PITCH-element rows.
@@ -768,11 +841,13 @@ __global__ __launch_bounds__(64 * WM * WN, RES * WM * WN / 4) void bf16_dma_kern
     constexpr int kHalfA = (kSpread ? 16 : 4) * TR * 2, kBlkA = 32 * TR * 2;
     constexpr int kHalfB = (kSpread ? 16 : 4) * TC * 2, kBlkB = 32 * TC * 2;
     const unsigned ring_lds = (unsigned)(uintptr_t)(GMM_LDS uint16_t*)ring;
-    unsigned a_tr[4], b_tr[4];
+    unsigned a_tr[4], b_tr[4], a_dir[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         a_tr[i] = tr_addr<kSpread, TR>(lg, wm * 64 + i * 16, lr);
         b_tr[i] = tr_addr<kSpread, TC>(lg, wn * 64 + i * 16, lr);
+        const int row = wm * 64 + i * 16 + lr;   // direct A fragment i of block 0 (swz_read_direct)
+        a_dir[i] = (unsigned)(2 * (row * RD + 8 * (lg ^ direct_key<RD>(row))));
     }
 
     const int nsl = (red_hi - red_lo + RD - 1) / RD;
@@ -794,14 +869,24 @@ __global__ __launch_bounds__(64 * WM * WN, RES * WM * WN / 4) void bf16_dma_kern
         const uint16_t* tb = ta + D::kSliceA;
         const unsigned sbase = ring_lds + (unsigned)(stage * kSt * 2);
         v8bf atr[2][4], btr[2][4];
-        if constexpr (A_TR) {
-            const unsigned ad[4] = {sbase + a_tr[0], sbase + a_tr[1], sbase + a_tr[2], sbase + a_tr[3]};
-            tr_slice<NB, kHalfA, kBlkA>(atr, ad);
-        }
-        if constexpr (B_TR) {
-            const unsigned bs = sbase + (unsigned)(D::kSliceA * 2);
+        const unsigned bs = sbase + (unsigned)(D::kSliceA * 2);
+        if constexpr (!A_TR && B_TR && NB == 1) {   // forward, 32-deep: one wait for both operands
+            const unsigned ad[4] = {sbase + a_dir[0], sbase + a_dir[1], sbase + a_dir[2], sbase + a_dir[3]};
             const unsigned bd[4] = {bs + b_tr[0], bs + b_tr[1], bs + b_tr[2], bs + b_tr[3]};
-            tr_slice<NB, kHalfB, kBlkB>(btr, bd);
+            direct_tr_slice<kHalfB>(atr[0], btr[0], ad, bd);
+        } else if constexpr (A_TR && B_TR && NB == 1) {   // tgmm, 32-deep: one wait for both operands
+            const unsigned ad[4] = {sbase + a_tr[0], sbase + a_tr[1], sbase + a_tr[2], sbase + a_tr[3]};
+            const unsigned bd[4] = {bs + b_tr[0], bs + b_tr[1], bs + b_tr[2], bs + b_tr[3]};
+            tr_slice_pair<kHalfA, kHalfB>(atr[0], btr[0], ad, bd);
+        } else {
+            if constexpr (A_TR) {
+                const unsigned ad[4] = {sbase + a_tr[0], sbase + a_tr[1], sbase + a_tr[2], sbase + a_tr[3]};
+                tr_slice<NB, kHalfA, kBlkA>(atr, ad);
+            }
+            if constexpr (B_TR) {
+                const unsigned bd[4] = {bs + b_tr[0], bs + b_tr[1], bs + b_tr[2], bs + b_tr[3]};
+                tr_slice<NB, kHalfB, kBlkB>(btr, bd);
+            }
         }
         const int valid = red_hi - (red_lo + t * RD);   // tgmm: real rows of this slice
 #pragma unroll
@@ -809,7 +894,7 @@ __global__ __launch_bounds__(64 * WM * WN, RES * WM * WN / 4) void bf16_dma_kern
             v8bf af[4], bf[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                if constexpr (A_TR)
+                if constexpr (A_TR || (B_TR && NB == 1))   // read above (the forward's fused reads)
                     af[i] = atr[s][i];
                 else
                     af[i] = swz_read_direct<RD>(ta, wm * 64 + i * 16 + lr, s * 4 + lg);
