@@ -206,9 +206,12 @@ bool resolve_bf16(int op, const TileConfig& f, int64_t M, int64_t K, int64_t N, 
     }
     // The library's choice (no kernel, waves, tile_n, depth or residency set;
     // placement may be), from measurements against kernel 1's best on one box:
-    //  - tgmm: kernel 3 with 8 waves in 256 x 128 tiles when K is a multiple
-    //    of 256, else 128 x 128 (backward shape 32.3 -> 30.4 us, production
-    //    shape 303 -> 271 us);
+    //  - tgmm: kernel 3 with 8 waves in 256 x 128 tiles for 128 or more
+    //    groups when K is a multiple of 256 (production shape 303 -> 271 us),
+    //    else 128 x 128: with few groups a skewed routing leaves the largest
+    //    group's tiles on the critical path, and halving their area halves it
+    //    (32 groups, Zipf(1.1) routing: 45.6 us with 256 x 128, 37.3 with
+    //    128 x 128; uniform routing 29.2 against 28.4);
     //  - forward / dX grids of at most eight 128 x 128 workgroups per CU:
     //    kernel 3, 128 x 128 tiles, 3 stages, three workgroups per CU
     //    (backward shape forward 39.9 -> 33.9 us, dX 37.4 -> 36.1);
@@ -226,7 +229,7 @@ bool resolve_bf16(int op, const TileConfig& f, int64_t M, int64_t K, int64_t N, 
     if (!f.kernel && !f.waves && !f.tile_n && !f.depth && !f.residency) {
         kernel = 3;
         if (op == kOpTgmm) {
-            if (K % 256 == 0) waves = 8, tile_n = 128;
+            if (K % 256 == 0 && G >= 128) waves = 8, tile_n = 128;
         } else if (nb128 > 8 * cus) {
             if (cols % 256 == 0)
                 waves = 8, tile_n = 256;

@@ -144,11 +144,12 @@ def test_library_default_choices():
     # grids of at most 8 workgroups per CU
     dma = {"kernel": 3, "waves": 4, "depth": 3, "residency": 3}
     assert nz(gmm.get_tile_config(B, 8192, 2048, 512, 32)) == dict(dma, placement=1)
-    # tgmm: the 8-wave 256 x 128 tiles when K is a multiple of 256
+    # tgmm: the 8-wave 256 x 128 tiles for 128 or more groups when K is a multiple of 256
     dma8 = {"kernel": 3, "waves": 8, "tile_n": 128, "depth": 3, "residency": 2}
     assert nz(gmm.get_tile_config(T, 65536, 2048, 512, 256)) == dma8
-    assert nz(gmm.get_tile_config(T, 8192, 2048, 512, 32)) == dma8
-    assert nz(gmm.get_tile_config(T, 8192, 384, 512, 32)) == dma
+    assert nz(gmm.get_tile_config(T, 65536, 2048, 512, 128)) == dma8
+    assert nz(gmm.get_tile_config(T, 8192, 2048, 512, 32)) == dma
+    assert nz(gmm.get_tile_config(T, 65536, 384, 512, 256)) == dma
     assert nz(gmm.get_tile_config(D, 8192, 2048, 512, 32)) == dict(dma, placement=1)
     # larger forward / dX grids: the 8-wave 128 x 256 tiles, row tiles from each group's start
     wide = {"kernel": 3, "waves": 8, "tile_n": 256, "depth": 3, "residency": 2, "placement": 2}
