@@ -284,13 +284,13 @@ __device__ __forceinline__ bool tile_item(const int32_t* __restrict__ group_size
                                           void* __restrict__ out, int ntiles_c, int ntiles_r, int nblocks,
                                           int placement, int32_t* __restrict__ status, int* s_info, TileItem& it) {
     const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-    const int L = xcd_remap(blockIdx.x, nblocks);
     const int out_cols = MODE == kDx ? K : N;
     if (wave == 1 && blockIdx.x == 0) {   // the call's device status word
         const int st = group_status(group_sizes, G, M);
         if (lane == 0) status[0] = st;
     }
     if constexpr (MODE == kTgmm) {
+        const int L = xcd_remap(blockIdx.x, nblocks);
         if (wave == 0) {
             const TgmmTile tt = tgmm_tile(group_sizes, G, M, ntiles_r * ntiles_c, L, placement);
             if (lane == 0) { s_info[0] = tt.row_lo; s_info[1] = tt.row_hi; s_info[2] = tt.g; s_info[3] = tt.t; }
@@ -306,17 +306,26 @@ __device__ __forceinline__ bool tile_item(const int32_t* __restrict__ group_size
         it.hi = it.row0 + TR;
         return true;
     } else {
-        const int w = L / ntiles_c;
-        it.c0 = (L % ntiles_c) * TC;
         if (wave == 0) {
-            // placement 2: row tiles start at each group's first row
-            const WorkItem wi = placement == 2 ? find_work_item<true>(group_sizes, G, M, TR, w)
-                                               : find_work_item(group_sizes, G, M, TR, w);
-            if (lane == 0) { s_info[0] = wi.g; s_info[1] = wi.tile; s_info[2] = wi.lo; s_info[3] = wi.hi; }
+            // placement 2: row tiles start at each group's first row.  The
+            // (row item, column tile) pairs that exist are dealt evenly over
+            // the XCDs, a row item's column tiles on one XCD.
+            const int count = (placement == 2 ? work_item_count<true>(group_sizes, G, M, TR)
+                                              : work_item_count(group_sizes, G, M, TR)) * ntiles_c;
+            const int L = xcd_balance(blockIdx.x, count);
+            WorkItem wi{-1, 0, 0, 0};
+            if (L >= 0)
+                wi = placement == 2 ? find_work_item<true>(group_sizes, G, M, TR, L / ntiles_c)
+                                    : find_work_item(group_sizes, G, M, TR, L / ntiles_c);
+            if (lane == 0) {
+                s_info[0] = wi.g; s_info[1] = wi.tile; s_info[2] = wi.lo; s_info[3] = wi.hi;
+                s_info[4] = L < 0 ? 0 : L % ntiles_c;
+            }
         }
         __syncthreads();
         it.g = s_info[0];
         if (it.g < 0) return false;
+        it.c0 = s_info[4] * TC;
         it.row0 = s_info[1] < 0 ? s_info[2] : s_info[1] * TR;
         it.lo = s_info[2];
         it.hi = s_info[3];
@@ -327,11 +336,11 @@ __device__ __forceinline__ bool tile_item(const int32_t* __restrict__ group_size
             for (int e = tid; e < rows * (TC / 8); e += NTHR) {
                 const int r = it.lo + e / (TC / 8), c = it.c0 + (e % (TC / 8)) * 8;
                 if constexpr (OUT_BF16)
-                    *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + (int64_t)r * out_cols + c) = make_uint4(0, 0, 0, 0);
+                    store_out(reinterpret_cast<uint16_t*>(out) + (int64_t)r * out_cols + c, make_uint4(0, 0, 0, 0));
                 else {
                     float4* p = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + (int64_t)r * out_cols + c);
-                    p[0] = make_float4(0, 0, 0, 0);
-                    p[1] = make_float4(0, 0, 0, 0);
+                    store_out(p, make_float4(0, 0, 0, 0));
+                    store_out(p + 1, make_float4(0, 0, 0, 0));
                 }
             }
             return false;
@@ -360,7 +369,7 @@ __global__ __launch_bounds__(256, MINB) void bf16_gemm_kernel(
     constexpr bool kSpread = A_TR && B_TR;   // both operands transposed: spread reduction order
     __shared__ __attribute__((aligned(16))) uint16_t sA[kTileElems];
     __shared__ __attribute__((aligned(16))) uint16_t sB[kTileElems];
-    __shared__ int s_info[4];
+    __shared__ int s_info[5];
 
     const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
     const int out_cols = MODE == kDx ? K : N;
@@ -468,7 +477,7 @@ __global__ __launch_bounds__(256, MINB) void bf16_gemm_kernel(
             const uint4 v = *reinterpret_cast<const uint4*>(ep + r * kEpiRow + ocol);
             const int row = row0 + wm * 64 + r;
             if (row >= lo && row < hi)
-                *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + obase + (int64_t)row * out_cols + col0 + ocol) = v;
+                store_out(reinterpret_cast<uint16_t*>(out) + obase + (int64_t)row * out_cols + col0 + ocol, v);
         }
     } else {
 #pragma unroll
@@ -477,8 +486,8 @@ __global__ __launch_bounds__(256, MINB) void bf16_gemm_kernel(
             if (row < lo || row >= hi) continue;
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + obase + (int64_t)row * out_cols + col0 + 16 * j + 4 * lg) =
-                    make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+                store_out(reinterpret_cast<float*>(out) + obase + (int64_t)row * out_cols + col0 + 16 * j + 4 * lg,
+                    make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]));
         }
     }
 }
@@ -758,7 +767,7 @@ __global__ __launch_bounds__(64 * WM * WN, RES * WM * WN / 4) void bf16_dma_kern
     constexpr bool B_TR = MODE != kDx;
     constexpr bool kSpread = A_TR && B_TR;
     __shared__ __attribute__((aligned(1024))) uint16_t ring[S * kSt];
-    __shared__ int s_info[4];
+    __shared__ int s_info[5];
 
     const int tid = threadIdx.x, lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -943,7 +952,7 @@ __global__ __launch_bounds__(64 * WM * WN, RES * WM * WN / 4) void bf16_dma_kern
             const uint4 v = *reinterpret_cast<const uint4*>(ep + r * kEpiRow + ocol);
             const int row = row0 + wm * 64 + r;
             if (row >= lo && row < hi)
-                *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + obase + (int64_t)row * out_cols + col0 + ocol) = v;
+                store_out(reinterpret_cast<uint16_t*>(out) + obase + (int64_t)row * out_cols + col0 + ocol, v);
         }
     } else {
 #pragma unroll
@@ -952,8 +961,8 @@ __global__ __launch_bounds__(64 * WM * WN, RES * WM * WN / 4) void bf16_dma_kern
             if (row < lo || row >= hi) continue;
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + obase + (int64_t)row * out_cols + col0 + 16 * j + 4 * lg) =
-                    make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+                store_out(reinterpret_cast<float*>(out) + obase + (int64_t)row * out_cols + col0 + 16 * j + 4 * lg,
+                    make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]));
         }
     }
 }
@@ -1039,7 +1048,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void bf16_wide_kernel(
     constexpr int SB = B_TR ? kTW + kPadTW : kR + kPadD;
     __shared__ __attribute__((aligned(16))) uint16_t sA[kWideElems];
     __shared__ __attribute__((aligned(16))) uint16_t sB[kWideElems];
-    __shared__ int s_info[4];
+    __shared__ int s_info[5];
 
     const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
     const int out_cols = MODE == kDx ? K : N;
@@ -1160,7 +1169,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void bf16_wide_kernel(
                     const uint4 v = *reinterpret_cast<const uint4*>(ep + rr * kEpiRow + ocol);
                     const int row = row0 + wm * 128 + rr;
                     if (row >= lo && row < hi)
-                        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + obase + (int64_t)row * out_cols + col0 + ocol) = v;
+                        store_out(reinterpret_cast<uint16_t*>(out) + obase + (int64_t)row * out_cols + col0 + ocol, v);
                 }
             }
             if (round + 1 < NWV / RW) __syncthreads();   // this round's staging read before reuse
@@ -1172,8 +1181,8 @@ __global__ __launch_bounds__(64 * NWV, 1) void bf16_wide_kernel(
             if (row < lo || row >= hi) continue;
 #pragma unroll
             for (int j = 0; j < NJ; ++j)
-                *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + obase + (int64_t)row * out_cols + col0 + 16 * j + 4 * lg) =
-                    make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+                store_out(reinterpret_cast<float*>(out) + obase + (int64_t)row * out_cols + col0 + 16 * j + 4 * lg,
+                    make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]));
         }
     }
 }

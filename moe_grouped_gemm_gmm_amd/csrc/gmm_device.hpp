@@ -366,6 +366,26 @@ __host__ __device__ inline int64_t max_work_items(int64_t M, int64_t G, int64_t 
     return (M + tm - 1) / tm + G + 1;
 }
 
+// Stores of a kernel's results.  Each result line is written once and not
+// read again by the kernel that writes it, so the stores carry the
+// non-temporal hint: the lines stream out of L2 as they are written instead
+// of staying dirty there until the write-back at the end of the kernel,
+// which every workgroup would otherwise wait for at once.
+__device__ __forceinline__ void store_out(void* p, uint4 v) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, static_cast<u32x4*>(p));
+}
+__device__ __forceinline__ void store_out(void* p, uint2 v) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    __builtin_nontemporal_store(u32x2{v.x, v.y}, static_cast<u32x2*>(p));
+}
+__device__ __forceinline__ void store_out(void* p, float4 v) {
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    __builtin_nontemporal_store(f32x4{v.x, v.y, v.z, v.w}, static_cast<f32x4*>(p));
+}
+__device__ __forceinline__ void store_out(uint32_t* p, uint32_t v) { __builtin_nontemporal_store(v, p); }
+__device__ __forceinline__ void store_out(float* p, float v) { __builtin_nontemporal_store(v, p); }
+
 // s_waitcnt vmcnt(N), the other counters untouched.
 template <int N>
 __device__ __forceinline__ void wait_vmem() {
@@ -394,6 +414,41 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
     const int x = bid % kNumXcd, i = bid / kNumXcd;
     const int start = x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per;
     return start + i;
+}
+
+// The same contiguous runs, dealt over the `count` logical ids that have
+// work instead of the whole grid.  A grid sized for the worst case holds
+// more blocks than items; remapping the whole grid would leave its spare
+// blocks, and so the idle share, on the last XCDs (at 65536 rows and 256
+// groups, 244 of 1538 blocks: one XCD without any work).  XCD x takes
+// count / 8 ids (one more for the first count % 8 XCDs) on its first slots;
+// returns block bid's id, or -1 for the slots past its XCD's run.  Needs
+// count <= nblocks, which max_work_items guarantees for the callers.
+__device__ __forceinline__ int xcd_balance(int bid, int count) {
+    const int per = count / kNumXcd, rem = count % kNumXcd;
+    const int x = bid % kNumXcd, i = bid / kNumXcd;
+    if (i >= per + (x < rem ? 1 : 0)) return -1;
+    const int start = x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per;
+    return start + i;
+}
+
+// Number of work items find_work_item<GROUP_TILES> defines for tile height
+// tm: every group's items, then the items of the rows past the clamped
+// total.  One wave; every lane gets the result.
+template <bool GROUP_TILES = false>
+__device__ __forceinline__ int work_item_count(const int32_t* __restrict__ group_sizes, int G, int M, int tm) {
+    int carry_rows = 0, items = 0;
+    for (int base = 0; base < G; base += 64) {
+        const GroupChunk ch = group_chunk(group_sizes, G, M, base, carry_rows);
+        const int c = ch.hi > ch.lo ? (GROUP_TILES ? (ch.hi - ch.lo + tm - 1) / tm
+                                                   : (ch.hi - 1) / tm - ch.lo / tm + 1)
+                                    : 0;
+        items += lane_value(wave_incl_scan(c), 63);
+        carry_rows = ch.next_carry;
+    }
+    const int total = min(carry_rows, M);
+    if (total >= M) return items;
+    return items + (GROUP_TILES ? (M - total + tm - 1) / tm : (M + tm - 1) / tm - total / tm);
 }
 
 }  // namespace gmm

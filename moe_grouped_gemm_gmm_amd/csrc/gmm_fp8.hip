@@ -216,11 +216,16 @@ __global__ __launch_bounds__(kThreads, 2) void fp8_fwd_kernel(
 
     const int tid = threadIdx.x, lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int L = xcd_remap(blockIdx.x, nblocks);
-    const int w = L / ntiles_n, nt = L % ntiles_n;
+    __shared__ int s_nt;
     if (wave == 0) {
-        const WorkItem it = find_work_item(group_sizes, G, M, TM, w);
-        if (lane == 0) s_item = it;
+        // the (row item, column tile) pairs that exist, dealt evenly over the XCDs
+        const int L = xcd_balance(blockIdx.x, work_item_count(group_sizes, G, M, TM) * ntiles_n);
+        WorkItem it{-1, 0, 0, 0};
+        if (L >= 0) it = find_work_item(group_sizes, G, M, TM, L / ntiles_n);
+        if (lane == 0) {
+            s_item = it;
+            s_nt = L < 0 ? 0 : L % ntiles_n;
+        }
     } else if (wave == 1 && blockIdx.x == 0) {   // the call's device status word
         const int st = group_status(group_sizes, G, M);
         if (lane == 0) status[0] = st;
@@ -228,6 +233,7 @@ __global__ __launch_bounds__(kThreads, 2) void fp8_fwd_kernel(
     __syncthreads();
     const WorkItem it = s_item;
     if (it.g < 0) return;
+    const int nt = s_nt;
     const int n0 = nt * TN;
 
     if (it.g == G) {  // rows past the last group: zeros
@@ -235,17 +241,17 @@ __global__ __launch_bounds__(kThreads, 2) void fp8_fwd_kernel(
         constexpr int V = 16 / OUT_BYTES;  // elements per 16-byte store
         for (int e = tid; e < rows * (TN / V); e += kThreads) {
             const int r = it.lo + e / (TN / V), c = n0 + (e % (TN / V)) * V;
-            *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(out) + ((int64_t)r * N + c) * OUT_BYTES) =
-                make_uint4(0, 0, 0, 0);
+            store_out(reinterpret_cast<uint8_t*>(out) + ((int64_t)r * N + c) * OUT_BYTES,
+                make_uint4(0, 0, 0, 0));
         }
         if (SWIGLU && q_out != nullptr) {   // their activation codes and scales too
             for (int e = tid; e < rows * (TN / 16); e += kThreads) {
                 const int r = it.lo + e / (TN / 16), c = n0 + (e % (TN / 16)) * 16;
-                *reinterpret_cast<uint4*>(q_out + (int64_t)r * N + c) = make_uint4(0, 0, 0, 0);
+                store_out(q_out + (int64_t)r * N + c, make_uint4(0, 0, 0, 0));
             }
             for (int e = tid; e < rows * (TN / kQBlock); e += kThreads) {
                 const int r = it.lo + e / (TN / kQBlock), b = n0 / kQBlock + e % (TN / kQBlock);
-                s_out[(int64_t)r * (N / kQBlock) + b] = 0.0f;
+                store_out(&s_out[(int64_t)r * (N / kQBlock) + b], 0.0f);
             }
         }
         return;
@@ -304,8 +310,8 @@ __global__ __launch_bounds__(kThreads, 2) void fp8_fwd_kernel(
         if (write_q) {
 #pragma unroll
             for (int p = 0; p < kNP; ++p)
-                *reinterpret_cast<uint2*>(q_out + qgrow * K + kb * kTK + qchunk * 8 + p * 8 * kLPR) = codes[p];
-            if (qchunk == 0) s_out[qgrow * nkb + kb] = s;
+                store_out(q_out + qgrow * K + kb * kTK + qchunk * 8 + p * 8 * kLPR, codes[p]);
+            if (qchunk == 0) store_out(&s_out[qgrow * nkb + kb], s);
         }
     };
     auto load_b = [&](v8i (&b)[NB], int kb) {
@@ -437,7 +443,7 @@ __global__ __launch_bounds__(kThreads, 2) void fp8_fwd_kernel(
                 const uint4 v = *reinterpret_cast<const uint4*>(&ep[r][ocol]);
                 const int grow = row0 + r;
                 if (grow >= it.lo && grow < it.hi)
-                    *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(out) + ((int64_t)grow * N + ncol0) * 2 + ocol) = v;
+                    store_out(reinterpret_cast<uint8_t*>(out) + ((int64_t)grow * N + ncol0) * 2 + ocol, v);
             }
         } else {
 #pragma unroll
@@ -446,8 +452,8 @@ __global__ __launch_bounds__(kThreads, 2) void fp8_fwd_kernel(
                 if (grow < it.lo || grow >= it.hi) continue;
 #pragma unroll
                 for (int jj = 0; jj < 2; ++jj)
-                    *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + (int64_t)grow * N + ncol0 + 16 * jj + 4 * lc) =
-                        make_float4(h[i][jj][0], h[i][jj][1], h[i][jj][2], h[i][jj][3]);
+                    store_out(reinterpret_cast<float*>(out) + (int64_t)grow * N + ncol0 + 16 * jj + 4 * lc,
+                        make_float4(h[i][jj][0], h[i][jj][1], h[i][jj][2], h[i][jj][3]));
             }
         }
         if (q_out != nullptr) {
@@ -477,9 +483,9 @@ __global__ __launch_bounds__(kThreads, 2) void fp8_fwd_kernel(
                 if (grow < it.lo || grow >= it.hi) continue;
 #pragma unroll
                 for (int jj = 0; jj < 2; ++jj)
-                    *reinterpret_cast<uint32_t*>(q_out + (int64_t)grow * N + ncol0 + 16 * jj + 4 * lc) =
-                        e4m3x4(h[i][jj][0] * inv, h[i][jj][1] * inv, h[i][jj][2] * inv, h[i][jj][3] * inv);
-                if (wave == w0 && lc == 0) s_out[(int64_t)grow * (N / kQBlock) + n0 / kQBlock + wave / 4] = sa;
+                    store_out(reinterpret_cast<uint32_t*>(q_out + (int64_t)grow * N + ncol0 + 16 * jj + 4 * lc),
+                        e4m3x4(h[i][jj][0] * inv, h[i][jj][1] * inv, h[i][jj][2] * inv, h[i][jj][3] * inv));
+                if (wave == w0 && lc == 0) store_out(&s_out[(int64_t)grow * (N / kQBlock) + n0 / kQBlock + wave / 4], sa);
             }
         }
         return;
@@ -510,7 +516,7 @@ __global__ __launch_bounds__(kThreads, 2) void fp8_fwd_kernel(
             const uint4 v = *reinterpret_cast<const uint4*>(&ep[r][ocol]);
             const int grow = row0 + r;
             if (grow >= it.lo && grow < it.hi)
-                *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(out) + ((int64_t)grow * N + ncol0) * 2 + ocol) = v;
+                store_out(reinterpret_cast<uint8_t*>(out) + ((int64_t)grow * N + ncol0) * 2 + ocol, v);
         }
     } else {
 #pragma unroll
@@ -520,8 +526,8 @@ __global__ __launch_bounds__(kThreads, 2) void fp8_fwd_kernel(
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
                 const int64_t o = (int64_t)grow * N + ncol0 + 16 * j + 4 * lc;
-                *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + o) =
-                    make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+                store_out(reinterpret_cast<float*>(out) + o,
+                    make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]));
             }
         }
     }
@@ -600,6 +606,8 @@ __global__ __launch_bounds__(64 * NW, NW / 4) void fp8_fwd_ws_kernel(   // TM = 
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     // placement 2: each group's items on one XCD (one column tile, G <= 64,
     // nblocks = 8 x slots); else consecutive items on one XCD
+    // (the library picks this kernel when every item fits on the chip at
+    // once, so the spare blocks of the consecutive mapping cost no time)
     const int L = placement == 2 ? 0 : xcd_remap(blockIdx.x, nblocks);
     const int nt = placement == 2 ? 0 : L % ntiles_n;
     if (wave == 0) {
@@ -622,8 +630,8 @@ __global__ __launch_bounds__(64 * NW, NW / 4) void fp8_fwd_ws_kernel(   // TM = 
         constexpr int V = 16 / OUT_BYTES;
         for (int e = tid; e < rows * (TN / V); e += kThr) {
             const int r = it.lo + e / (TN / V), c = n0 + (e % (TN / V)) * V;
-            *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(out) + ((int64_t)r * N + c) * OUT_BYTES) =
-                make_uint4(0, 0, 0, 0);
+            store_out(reinterpret_cast<uint8_t*>(out) + ((int64_t)r * N + c) * OUT_BYTES,
+                make_uint4(0, 0, 0, 0));
         }
         return;
     }
@@ -682,8 +690,8 @@ __global__ __launch_bounds__(64 * NW, NW / 4) void fp8_fwd_ws_kernel(   // TM = 
                 if (WRITE_Q && nt == 0 && qvalid[h]) {
 #pragma unroll
                     for (int q = 0; q < kNP; ++q)
-                        *reinterpret_cast<uint2*>(q_out + qgrow[h] * K + kb * kTK + qchunk * 8 + q * 8 * kLPR) = codes[q];
-                    if (qchunk == 0) s_out[qgrow[h] * nkb + kb] = s;
+                        store_out(q_out + qgrow[h] * K + kb * kTK + qchunk * 8 + q * 8 * kLPR, codes[q]);
+                    if (qchunk == 0) store_out(&s_out[qgrow[h] * nkb + kb], s);
                 }
             }
         };
@@ -820,7 +828,7 @@ __global__ __launch_bounds__(64 * NW, NW / 4) void fp8_fwd_ws_kernel(   // TM = 
         const uint4 v = *reinterpret_cast<const uint4*>(&ep[r][ocol]);
         const int grow = row0 + r;
         if (grow >= it.lo && grow < it.hi)
-            *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(out) + ((int64_t)grow * N + ncol0) * OUT_BYTES + ocol) = v;
+            store_out(reinterpret_cast<uint8_t*>(out) + ((int64_t)grow * N + ncol0) * OUT_BYTES + ocol, v);
     }
 }
 
@@ -861,9 +869,11 @@ __global__ __launch_bounds__(1024, 4) void fp8_fwd_wsn_kernel(
 
     const int tid = threadIdx.x, lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int w = xcd_remap(blockIdx.x, nblocks);
     if (wave == 0) {
-        const WorkItem it = find_work_item(group_sizes, G, M, TM, w);
+        // the items that exist, dealt evenly over the XCDs
+        const int w = xcd_balance(blockIdx.x, work_item_count(group_sizes, G, M, TM));
+        WorkItem it{-1, 0, 0, 0};
+        if (w >= 0) it = find_work_item(group_sizes, G, M, TM, w);
         if (lane == 0) s_item = it;
     } else if (wave == 1 && blockIdx.x == 0) {   // the call's device status word
         const int st = group_status(group_sizes, G, M);
@@ -877,8 +887,8 @@ __global__ __launch_bounds__(1024, 4) void fp8_fwd_wsn_kernel(
         const int per_row = N * OUT_BYTES / 16;
         for (int e = tid; e < rows * per_row; e += kThr) {
             const int r = it.lo + e / per_row, c = e % per_row;
-            *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(out) + (int64_t)r * N * OUT_BYTES + c * 16) =
-                make_uint4(0, 0, 0, 0);
+            store_out(reinterpret_cast<uint8_t*>(out) + (int64_t)r * N * OUT_BYTES + c * 16,
+                make_uint4(0, 0, 0, 0));
         }
         return;
     }
@@ -1034,9 +1044,9 @@ __global__ __launch_bounds__(1024, 4) void fp8_fwd_wsn_kernel(
             const int grow = row0 + r;
             if (grow >= it.lo && grow < it.hi) {
                 if constexpr (B4 && !FIRST && OUT_BF16)
-                    *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(out) + ((int64_t)grow * N + ncol0) * OUT_BYTES + ocol) = v;
+                    store_out(reinterpret_cast<uint8_t*>(out) + ((int64_t)grow * N + ncol0) * OUT_BYTES + ocol, v);
                 else
-                    *reinterpret_cast<uint4*>(obase + (int64_t)(RPI * q) * N * OUT_BYTES + olane) = v;
+                    store_out(obase + (int64_t)(RPI * q) * N * OUT_BYTES + olane, v);
             }
         }
         // the staging rows are rewritten by the next tile's epilogue only

@@ -117,8 +117,8 @@ __global__ __launch_bounds__(256) void quantize_lhs_kernel(const void* __restric
             codes.x = e4m3x4(v[u][0] * inv, v[u][1] * inv, v[u][2] * inv, v[u][3] * inv);
             codes.y = e4m3x4(v[u][4] * inv, v[u][5] * inv, v[u][6] * inv, v[u][7] * inv);
             if (blk < nblk) {
-                *reinterpret_cast<uint2*>(q + blk * kQBlock + sub * 8) = codes;
-                if (sub == 0) scale[blk] = s;
+                store_out(q + blk * kQBlock + sub * 8, codes);
+                if (sub == 0) store_out(&scale[blk], s);
             }
         }
     }
