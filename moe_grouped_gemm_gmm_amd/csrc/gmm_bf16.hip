@@ -310,16 +310,13 @@ __device__ __forceinline__ bool tile_item(const int32_t* __restrict__ group_size
             // placement 2: row tiles start at each group's first row.  The
             // (row item, column tile) pairs that exist are dealt evenly over
             // the XCDs, a row item's column tiles on one XCD.
-            const int count = (placement == 2 ? work_item_count<true>(group_sizes, G, M, TR)
-                                              : work_item_count(group_sizes, G, M, TR)) * ntiles_c;
-            const int L = xcd_balance(blockIdx.x, count);
-            WorkItem wi{-1, 0, 0, 0};
-            if (L >= 0)
-                wi = placement == 2 ? find_work_item<true>(group_sizes, G, M, TR, L / ntiles_c)
-                                    : find_work_item(group_sizes, G, M, TR, L / ntiles_c);
+            int col;
+            const WorkItem wi = placement == 2
+                ? balanced_work_item<true>(group_sizes, G, M, TR, ntiles_c, blockIdx.x, col)
+                : balanced_work_item(group_sizes, G, M, TR, ntiles_c, blockIdx.x, col);
             if (lane == 0) {
                 s_info[0] = wi.g; s_info[1] = wi.tile; s_info[2] = wi.lo; s_info[3] = wi.hi;
-                s_info[4] = L < 0 ? 0 : L % ntiles_c;
+                s_info[4] = col;
             }
         }
         __syncthreads();

@@ -203,12 +203,9 @@ struct GroupChunk {
     bool negative;   // some group of the chunk has a negative size
 };
 
-__device__ __forceinline__ GroupChunk group_chunk(const int32_t* __restrict__ group_sizes, int G,
-                                                  int M, int base, int carry) {
-    const int lane = lane_id();
+// The chunk from the lane's raw size (0 past G), already loaded.
+__device__ __forceinline__ GroupChunk group_chunk_of(int raw, int M, int carry) {
     const uint32_t cap = (uint32_t)M + 1u;
-    const int g = base + lane;
-    const int raw = g < G ? group_sizes[g] : 0;
     const uint32_t s = (uint32_t)min(max(raw, 0), M + 1);   // cap: a lone group past M still saturates
     const uint32_t incl = wave_incl_scan_sat(s, cap);
     const uint32_t excl = wave_shift_up(incl);
@@ -218,6 +215,12 @@ __device__ __forceinline__ GroupChunk group_chunk(const int32_t* __restrict__ gr
     c.next_carry = (int)min((uint32_t)carry + (uint32_t)lane_value((int)incl, 63), cap);
     c.negative = __ballot(raw < 0) != 0ull;
     return c;
+}
+
+__device__ __forceinline__ GroupChunk group_chunk(const int32_t* __restrict__ group_sizes, int G,
+                                                  int M, int base, int carry) {
+    const int g = base + lane_id();
+    return group_chunk_of(g < G ? group_sizes[g] : 0, M, carry);
 }
 
 // Bits of the device status word that grouped kernels write (see gmm.h).
@@ -258,56 +261,77 @@ struct WorkItem {
 // no item straddles a tile boundary: fewer items with partly used rows
 // (about half a tile fewer per group).  `tile` is then -1 and the item's
 // rows start at `lo`.  Both mappings give at most max_work_items items.
-template <bool GROUP_TILES = false>
-__device__ __forceinline__ WorkItem find_work_item(const int32_t* __restrict__ group_sizes, int G,
-                                                   int M, int tm, int w) {
-    int carry_rows = 0, carry_items = 0;
-    for (int base = 0; base < G; base += 64) {
-        const GroupChunk ch = group_chunk(group_sizes, G, M, base, carry_rows);
-        const int c = ch.hi > ch.lo ? (GROUP_TILES ? (ch.hi - ch.lo + tm - 1) / tm
-                                                   : (ch.hi - 1) / tm - ch.lo / tm + 1)
-                                    : 0;
-        const int inclc = wave_incl_scan(c);
-        const int W = carry_items + inclc - c;
-        const bool own = c > 0 && w >= W && w < W + c;
-        const unsigned long long mask = __ballot(own);
-        if (mask) {
-            const int src = __ffsll((long long)mask) - 1;
-            const int glo = lane_value(ch.lo, src);
-            const int ghi = lane_value(ch.hi, src);
-            const int gW = lane_value(W, src);
-            WorkItem it;
-            it.g = base + src;
-            if constexpr (GROUP_TILES) {
-                it.tile = -1;
-                it.lo = glo + (w - gW) * tm;
-                it.hi = min(ghi, it.lo + tm);
-            } else {
-                const int t = glo / tm + (w - gW);
-                it.tile = t;
-                it.lo = max(glo, t * tm);
-                it.hi = min(ghi, (t + 1) * tm);
-            }
-            return it;
-        }
-        carry_rows = ch.next_carry;
-        carry_items += lane_value(inclc, 63);
-    }
+// Items of a group with clamped rows [lo, hi).
+template <bool GROUP_TILES>
+__device__ __forceinline__ int group_items(int lo, int hi, int tm) {
+    return hi > lo ? (GROUP_TILES ? (hi - lo + tm - 1) / tm : (hi - 1) / tm - lo / tm + 1) : 0;
+}
+
+// Items of the rows [total, M) past the clamped total.
+template <bool GROUP_TILES>
+__device__ __forceinline__ int tail_items(int total, int M, int tm) {
+    return total >= M ? 0 : (GROUP_TILES ? (M - total + tm - 1) / tm : (M + tm - 1) / tm - total / tm);
+}
+
+// Item w, given that it is the item w - gW of the group g with clamped rows
+// [glo, ghi) (GROUP_TILES: tiles from glo; else tiles at multiples of tm).
+template <bool GROUP_TILES>
+__device__ __forceinline__ WorkItem group_item(int g, int glo, int ghi, int gW, int tm, int w) {
     WorkItem it;
-    const int total = min(carry_rows, M);
+    it.g = g;
+    if constexpr (GROUP_TILES) {
+        it.tile = -1;
+        it.lo = glo + (w - gW) * tm;
+        it.hi = min(ghi, it.lo + tm);
+    } else {
+        const int t = glo / tm + (w - gW);
+        it.tile = t;
+        it.lo = max(glo, t * tm);
+        it.hi = min(ghi, (t + 1) * tm);
+    }
+    return it;
+}
+
+// Tail item w (the items of the groups number items) for the rows past the
+// clamped total; g < 0 when it holds no row.
+template <bool GROUP_TILES>
+__device__ __forceinline__ WorkItem tail_item(int G, int M, int total, int items, int tm, int w) {
+    WorkItem it;
     it.g = G;
     if constexpr (GROUP_TILES) {
         it.tile = -1;
-        it.lo = total + (w - carry_items) * tm;
+        it.lo = total + (w - items) * tm;
         it.hi = min(M, it.lo + tm);
     } else {
-        const int t = total / tm + (w - carry_items);
+        const int t = total / tm + (w - items);
         it.tile = t;
         it.lo = max(total, t * tm);
         it.hi = min(M, (t + 1) * tm);
     }
     if (it.lo >= it.hi) it.g = -1;
     return it;
+}
+
+template <bool GROUP_TILES = false>
+__device__ __forceinline__ WorkItem find_work_item(const int32_t* __restrict__ group_sizes, int G,
+                                                   int M, int tm, int w) {
+    int carry_rows = 0, carry_items = 0;
+    for (int base = 0; base < G; base += 64) {
+        const GroupChunk ch = group_chunk(group_sizes, G, M, base, carry_rows);
+        const int c = group_items<GROUP_TILES>(ch.lo, ch.hi, tm);
+        const int inclc = wave_incl_scan(c);
+        const int W = carry_items + inclc - c;
+        const bool own = c > 0 && w >= W && w < W + c;
+        const unsigned long long mask = __ballot(own);
+        if (mask) {
+            const int src = __ffsll((long long)mask) - 1;
+            return group_item<GROUP_TILES>(base + src, lane_value(ch.lo, src), lane_value(ch.hi, src),
+                                           lane_value(W, src), tm, w);
+        }
+        carry_rows = ch.next_carry;
+        carry_items += lane_value(inclc, 63);
+    }
+    return tail_item<GROUP_TILES>(G, M, min(carry_rows, M), carry_items, tm, w);
 }
 
 // Group-aligned XCD placement of work items, for grids that hold every item
@@ -324,7 +348,7 @@ __device__ __forceinline__ int group_aligned_item(const int32_t* __restrict__ gr
                                                   int M, int tm, int slots, int b) {
     const int lane = lane_id();
     const GroupChunk ch = group_chunk(group_sizes, G, M, 0, 0);
-    const int c = ch.hi > ch.lo ? (ch.hi - 1) / tm - ch.lo / tm + 1 : 0;
+    const int c = group_items<false>(ch.lo, ch.hi, tm);
     const int inclc = wave_incl_scan(c);
     const int W = inclc - c;                                   // first item of group `lane`
     const int total = min(ch.next_carry, M);
@@ -359,6 +383,38 @@ __device__ __forceinline__ int group_aligned_item(const int32_t* __restrict__ gr
         rank -= extra;
     }
     return -1;
+}
+
+// find_work_item(group_aligned_item(...)) in one pass over group_sizes.  A
+// block inside its XCD's own run (every working block unless some XCD has
+// more items than slots) needs only the first items of its XCD and the
+// next, and the owner of its item is found in the chunk already scanned;
+// the other blocks take the full mapping.  The work item, g < 0: none.
+__device__ __forceinline__ WorkItem group_aligned_work_item(const int32_t* __restrict__ group_sizes, int G,
+                                                           int M, int tm, int slots, int b) {
+    const int lane = lane_id();
+    const GroupChunk ch = group_chunk(group_sizes, G, M, 0, 0);
+    const int c = group_items<false>(ch.lo, ch.hi, tm);
+    const int inclc = wave_incl_scan(c);
+    const int W = inclc - c;
+    const int total = min(ch.next_carry, M);
+    const int Tg = lane_value(inclc, 63);
+    const int T = Tg + tail_items<false>(total, M, tm);
+    const int xg = T > 0 ? min(7, (8 * (2 * W + c)) / (2 * T)) : 0;
+    // XCD y's first item: that of its first group (xg is non-decreasing in
+    // the group index, so these starts are too), else where the tail starts
+    auto first_of = [&](int y) {
+        const unsigned long long m = __ballot(lane < G && c > 0 && xg >= y);
+        return m ? lane_value(W, __ffsll((long long)m) - 1) : Tg;
+    };
+    const int x = b % kNumXcd, i = b / kNumXcd;
+    const int s0 = x == 0 ? 0 : first_of(x);
+    const int s1 = x == kNumXcd - 1 ? T : first_of(x + 1);
+    const int w = i < min(s1 - s0, slots) ? s0 + i : group_aligned_item(group_sizes, G, M, tm, slots, b);
+    if (w < 0) return WorkItem{-1, 0, 0, 0};
+    if (w >= Tg) return tail_item<false>(G, M, total, Tg, tm, w);
+    const int src = __ffsll((long long)__ballot(c > 0 && w >= W && w < W + c)) - 1;
+    return group_item<false>(src, lane_value(ch.lo, src), lane_value(ch.hi, src), lane_value(W, src), tm, w);
 }
 
 // Upper bound of the work-item count for M rows, G groups, tile height tm.
@@ -440,15 +496,65 @@ __device__ __forceinline__ int work_item_count(const int32_t* __restrict__ group
     int carry_rows = 0, items = 0;
     for (int base = 0; base < G; base += 64) {
         const GroupChunk ch = group_chunk(group_sizes, G, M, base, carry_rows);
-        const int c = ch.hi > ch.lo ? (GROUP_TILES ? (ch.hi - ch.lo + tm - 1) / tm
-                                                   : (ch.hi - 1) / tm - ch.lo / tm + 1)
-                                    : 0;
-        items += lane_value(wave_incl_scan(c), 63);
+        items += lane_value(wave_incl_scan(group_items<GROUP_TILES>(ch.lo, ch.hi, tm)), 63);
         carry_rows = ch.next_carry;
     }
-    const int total = min(carry_rows, M);
-    if (total >= M) return items;
-    return items + (GROUP_TILES ? (M - total + tm - 1) / tm : (M + tm - 1) / tm - total / tm);
+    return items + tail_items<GROUP_TILES>(min(carry_rows, M), M, tm);
+}
+
+// find_work_item<GROUP_TILES> of block b's id under xcd_balance over the
+// (item, column tile) pairs that exist, ntiles column tiles per item, in
+// one pass over group_sizes: the item (g < 0: none) and, in col, its column
+// tile.  Up to 256 groups the clamped ranges and item offsets stay in
+// registers, one load per 64 groups, all issued before the first scan (a
+// serial chain of dependent loads and scans is what a workgroup's prologue
+// waits on); beyond, work_item_count and find_work_item.
+template <bool GROUP_TILES = false>
+__device__ __forceinline__ WorkItem balanced_work_item(const int32_t* __restrict__ group_sizes, int G, int M,
+                                                       int tm, int ntiles, int b, int& col) {
+    col = 0;
+    if (G > 256) {
+        const int L = xcd_balance(b, work_item_count<GROUP_TILES>(group_sizes, G, M, tm) * ntiles);
+        if (L < 0) return WorkItem{-1, 0, 0, 0};
+        col = L % ntiles;
+        return find_work_item<GROUP_TILES>(group_sizes, G, M, tm, L / ntiles);
+    }
+    const int lane = lane_id();
+    int raw[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) raw[k] = 64 * k + lane < G ? group_sizes[64 * k + lane] : 0;
+    int lo[4], hi[4], cn[4], W[4];
+    int carry = 0, items = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        lo[k] = hi[k] = cn[k] = W[k] = 0;
+        if (64 * k < G) {
+            const GroupChunk ch = group_chunk_of(raw[k], M, carry);
+            lo[k] = ch.lo;
+            hi[k] = ch.hi;
+            carry = ch.next_carry;
+            cn[k] = group_items<GROUP_TILES>(ch.lo, ch.hi, tm);
+            const int incl = wave_incl_scan(cn[k]);
+            W[k] = items + incl - cn[k];
+            items += lane_value(incl, 63);
+        }
+    }
+    const int total = min(carry, M);
+    const int L = xcd_balance(b, (items + tail_items<GROUP_TILES>(total, M, tm)) * ntiles);
+    if (L < 0) return WorkItem{-1, 0, 0, 0};
+    const int w = L / ntiles;
+    col = L % ntiles;
+    if (w >= items) return tail_item<GROUP_TILES>(G, M, total, items, tm, w);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const unsigned long long m = __ballot(cn[k] > 0 && w >= W[k] && w < W[k] + cn[k]);
+        if (m) {
+            const int src = __ffsll((long long)m) - 1;
+            return group_item<GROUP_TILES>(64 * k + src, lane_value(lo[k], src), lane_value(hi[k], src),
+                                           lane_value(W[k], src), tm, w);
+        }
+    }
+    return WorkItem{-1, 0, 0, 0};   // not reached: w < items has an owner
 }
 
 }  // namespace gmm

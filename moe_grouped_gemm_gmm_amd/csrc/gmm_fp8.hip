@@ -219,12 +219,11 @@ __global__ __launch_bounds__(kThreads, 2) void fp8_fwd_kernel(
     __shared__ int s_nt;
     if (wave == 0) {
         // the (row item, column tile) pairs that exist, dealt evenly over the XCDs
-        const int L = xcd_balance(blockIdx.x, work_item_count(group_sizes, G, M, TM) * ntiles_n);
-        WorkItem it{-1, 0, 0, 0};
-        if (L >= 0) it = find_work_item(group_sizes, G, M, TM, L / ntiles_n);
+        int col;
+        const WorkItem it = balanced_work_item(group_sizes, G, M, TM, ntiles_n, blockIdx.x, col);
         if (lane == 0) {
             s_item = it;
-            s_nt = L < 0 ? 0 : L % ntiles_n;
+            s_nt = col;
         }
     } else if (wave == 1 && blockIdx.x == 0) {   // the call's device status word
         const int st = group_status(group_sizes, G, M);
@@ -611,11 +610,9 @@ __global__ __launch_bounds__(64 * NW, NW / 4) void fp8_fwd_ws_kernel(   // TM = 
     const int L = placement == 2 ? 0 : xcd_remap(blockIdx.x, nblocks);
     const int nt = placement == 2 ? 0 : L % ntiles_n;
     if (wave == 0) {
-        const int w = placement == 2
-            ? group_aligned_item(group_sizes, G, M, TM, nblocks / kNumXcd, blockIdx.x)
-            : L / ntiles_n;
-        WorkItem it{-1, 0, 0, 0};
-        if (w >= 0) it = find_work_item(group_sizes, G, M, TM, w);
+        const WorkItem it = placement == 2
+            ? group_aligned_work_item(group_sizes, G, M, TM, nblocks / kNumXcd, blockIdx.x)
+            : find_work_item(group_sizes, G, M, TM, L / ntiles_n);
         if (lane == 0) s_item = it;
     } else if (wave == 1 && blockIdx.x == 0) {   // the call's device status word
         const int st = group_status(group_sizes, G, M);
@@ -871,9 +868,8 @@ __global__ __launch_bounds__(1024, 4) void fp8_fwd_wsn_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     if (wave == 0) {
         // the items that exist, dealt evenly over the XCDs
-        const int w = xcd_balance(blockIdx.x, work_item_count(group_sizes, G, M, TM));
-        WorkItem it{-1, 0, 0, 0};
-        if (w >= 0) it = find_work_item(group_sizes, G, M, TM, w);
+        int col;
+        const WorkItem it = balanced_work_item(group_sizes, G, M, TM, 1, blockIdx.x, col);
         if (lane == 0) s_item = it;
     } else if (wave == 1 && blockIdx.x == 0) {   // the call's device status word
         const int st = group_status(group_sizes, G, M);
