@@ -483,8 +483,8 @@ __global__ __launch_bounds__(256, MINB) void bf16_gemm_kernel(
             if (row < lo || row >= hi) continue;
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                store_out(reinterpret_cast<float*>(out) + obase + (int64_t)row * out_cols + col0 + 16 * j + 4 * lg,
-                    make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]));
+                *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + obase + (int64_t)row * out_cols + col0 + 16 * j + 4 * lg) =
+                    make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
         }
     }
 }
@@ -958,8 +958,8 @@ __global__ __launch_bounds__(64 * WM * WN, RES * WM * WN / 4) void bf16_dma_kern
             if (row < lo || row >= hi) continue;
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                store_out(reinterpret_cast<float*>(out) + obase + (int64_t)row * out_cols + col0 + 16 * j + 4 * lg,
-                    make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]));
+                *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + obase + (int64_t)row * out_cols + col0 + 16 * j + 4 * lg) =
+                    make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
         }
     }
 }
@@ -1178,8 +1178,8 @@ __global__ __launch_bounds__(64 * NWV, 1) void bf16_wide_kernel(
             if (row < lo || row >= hi) continue;
 #pragma unroll
             for (int j = 0; j < NJ; ++j)
-                store_out(reinterpret_cast<float*>(out) + obase + (int64_t)row * out_cols + col0 + 16 * j + 4 * lg,
-                    make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]));
+                *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + obase + (int64_t)row * out_cols + col0 + 16 * j + 4 * lg) =
+                    make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
         }
     }
 }

@@ -279,11 +279,12 @@ bool resolve_bf16(int op, const TileConfig& f, int64_t M, int64_t K, int64_t N, 
         // partly used tiles, which pays once the grid takes more than two
         // rounds of the chip (kernel 1, production shape: dX 284 -> 275 us,
         // forward 264 -> 257 us; kernel 3's 128 x 256 tiles: dX 263 -> 261,
-        // forward the same); kernel 3's 128 x 128 tiles keep 1 (production
-        // forward 265 against 282 us)
+        // forward the same), and for dX at every size since the grid is dealt
+        // by the items that exist (backward shape 31.7 -> 28.4 us); the
+        // forward's smaller grids keep 1 (backward shape 32.4 against 33.8 us)
         if (f.placement && f.placement != 1 && f.placement != 2) return fail(why, "placement is 1 or 2");
         const bool big = nblocks > 6 * cus && (kernel == 1 || waves == 8);
-        c->placement = f.placement ? f.placement : (big ? 2 : 1);
+        c->placement = f.placement ? f.placement : (big || op == kOpDx ? 2 : 1);
     }
     return true;
 }

@@ -426,7 +426,9 @@ __host__ __device__ inline int64_t max_work_items(int64_t M, int64_t G, int64_t 
 // read again by the kernel that writes it, so the stores carry the
 // non-temporal hint: the lines stream out of L2 as they are written instead
 // of staying dirty there until the write-back at the end of the kernel,
-// which every workgroup would otherwise wait for at once.
+// which every workgroup would otherwise wait for at once.  Meant for stores
+// whose wave covers whole lines; scattered pieces of lines stay plain
+// stores, which L2 merges.
 __device__ __forceinline__ void store_out(void* p, uint4 v) {
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, static_cast<u32x4*>(p));
@@ -439,7 +441,6 @@ __device__ __forceinline__ void store_out(void* p, float4 v) {
     typedef float f32x4 __attribute__((ext_vector_type(4)));
     __builtin_nontemporal_store(f32x4{v.x, v.y, v.z, v.w}, static_cast<f32x4*>(p));
 }
-__device__ __forceinline__ void store_out(uint32_t* p, uint32_t v) { __builtin_nontemporal_store(v, p); }
 __device__ __forceinline__ void store_out(float* p, float v) { __builtin_nontemporal_store(v, p); }
 
 // s_waitcnt vmcnt(N), the other counters untouched.

@@ -150,7 +150,7 @@ def test_library_default_choices():
     assert nz(gmm.get_tile_config(T, 65536, 2048, 512, 128)) == dma8
     assert nz(gmm.get_tile_config(T, 8192, 2048, 512, 32)) == dma
     assert nz(gmm.get_tile_config(T, 65536, 384, 512, 256)) == dma
-    assert nz(gmm.get_tile_config(D, 8192, 2048, 512, 32)) == dict(dma, placement=1)
+    assert nz(gmm.get_tile_config(D, 8192, 2048, 512, 32)) == dict(dma, placement=2)   # dX: group-start rows
     # larger forward / dX grids: the 8-wave 128 x 256 tiles, row tiles from each group's start
     wide = {"kernel": 3, "waves": 8, "tile_n": 256, "depth": 3, "residency": 2, "placement": 2}
     assert nz(gmm.get_tile_config(D, 65536, 2048, 512, 256)) == wide
