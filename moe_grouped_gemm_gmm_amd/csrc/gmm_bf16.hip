@@ -187,11 +187,16 @@ __device__ inline TgmmTile tgmm_tile(const int32_t* __restrict__ group_sizes, in
         cnt2 += __popcll(__ballot(c == 2));
     };
     if (inreg) {
+        // all four loads issued before the first scan: a chain of dependent
+        // load round trips is what this prologue would otherwise wait on
+        int raw[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) raw[c] = group_size_at(group_sizes, G, 64 * c + lane_id());
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             glo[c] = ghi[c] = 0;
             if (64 * c < G) {
-                const GroupChunk ch = group_chunk(group_sizes, G, M, 64 * c, carry);
+                const GroupChunk ch = group_chunk_of(raw[c], M, carry);
                 glo[c] = ch.lo;
                 ghi[c] = ch.hi;
                 carry = ch.next_carry;

@@ -217,10 +217,18 @@ __device__ __forceinline__ GroupChunk group_chunk_of(int raw, int M, int carry) 
     return c;
 }
 
+// group_sizes[g], 0 for g >= G (G >= 1), as an unconditional load of an
+// in-bounds index and a select: a conditional load compiles to a branch,
+// and the compiler waits for the load at the join, so loads meant to be in
+// flight together would each make a round trip of their own.
+__device__ __forceinline__ int group_size_at(const int32_t* __restrict__ group_sizes, int G, int g) {
+    const int v = group_sizes[min(g, G - 1)];
+    return g < G ? v : 0;
+}
+
 __device__ __forceinline__ GroupChunk group_chunk(const int32_t* __restrict__ group_sizes, int G,
                                                   int M, int base, int carry) {
-    const int g = base + lane_id();
-    return group_chunk_of(g < G ? group_sizes[g] : 0, M, carry);
+    return group_chunk_of(group_size_at(group_sizes, G, base + lane_id()), M, carry);
 }
 
 // Bits of the device status word that grouped kernels write (see gmm.h).
@@ -523,7 +531,7 @@ __device__ __forceinline__ WorkItem balanced_work_item(const int32_t* __restrict
     const int lane = lane_id();
     int raw[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) raw[k] = 64 * k + lane < G ? group_sizes[64 * k + lane] : 0;
+    for (int k = 0; k < 4; ++k) raw[k] = group_size_at(group_sizes, G, 64 * k + lane);
     int lo[4], hi[4], cn[4], W[4];
     int carry = 0, items = 0;
 #pragma unroll
