@@ -124,19 +124,30 @@ GMM_API size_t gmm_workspace_bytes(int op, int64_t M, int64_t K, int64_t N, int6
  *     kernel    1 128 x 128 tiles, operands staged through registers;
  *                 2 256 x 256 tiles (8 waves, one workgroup per CU; the
  *                 tiled dimensions multiples of 256; forward / dX rows
- *                 from each group's first row); 3 128 x 128 tiles fed by
- *                 load-to-LDS into a ring of LDS stages.
- *     residency kernel 1: 2 or 3 (workgroups per CU the register
- *                 allocation allows); kernel 2: 1; kernel 3: follows depth
- *                 (2 for 2 stages, 1 for 3 or 4), only restated.
- *     depth     kernel 3 only: LDS stages of 64-deep slices, 2, 3 or 4
- *                 (slices in flight = depth - 1).
+ *                 from each group's first row); 3 tiles fed by
+ *                 load-to-LDS into a ring of LDS stages, 64 x 64 per wave
+ *                 (the library's choice for every bf16 call it can take).
+ *     waves     kernel 3: 4 (128 x 128 tiles) or 8 (256 x 128, or 128 x 256
+ *                 with tile_n 256; tgmm's 256 rows are K rows and need K a
+ *                 multiple of 256, the 256 columns a multiple of 256 tiled
+ *                 columns).
+ *     tile_n    kernel 3 with 8 waves: 128 or 256 (see waves).
+ *     depth     kernel 3: LDS stages, 2, 3 or 4 (slices in flight = depth -
+ *                 1; slices 64 deep when the rings of all resident
+ *                 workgroups fit the LDS, else 32).
+ *     residency workgroups per CU the register allocation allows.  Kernel 1:
+ *                 2 or 3; kernel 2: 1; kernel 3 with 4 waves: 2 with depth
+ *                 2, 1-3 with depth 3, 1-2 with depth 4; with 8 waves:
+ *                 depth 3 and residency 2.
  *     placement tgmm: 1 (each XCD takes whole groups) or 2 (every group
  *                 spread over the 8 XCDs, groups in decreasing size class;
- *                 needs a multiple of 8 tiles per group); forward and dX:
- *                 1 (row tiles aligned to absolute rows) or 2 (tiles
- *                 starting at each group's first row: no tile straddles
- *                 two groups).
+ *                 needs a multiple of 8 tiles per group); left 0, each
+ *                 call decides from the group sizes (2 when the largest
+ *                 group holds more than four times the mean rows).  Forward
+ *                 and dX: 1 (row tiles aligned to absolute rows) or 2
+ *                 (tiles starting at each group's first row: no tile
+ *                 straddles two groups); the library takes 2 for dX and
+ *                 for large forward grids.
  */
 typedef struct {
     int32_t kernel, waves, tile_m, tile_n, depth, residency, placement;
