@@ -215,3 +215,34 @@ def test_bf16_fwd_multi_round_grid(out_dtype):
     o = to_np64(out)
     assert (o[int(sum(gs)):] == 0).all()
     assert_bf16_parity(o, ref, "bf16 fwd multi-round")
+
+
+@pytest.mark.parametrize("G", [130, 300])
+@pytest.mark.parametrize("placement", [1, 2])
+@pytest.mark.parametrize("kernel", [1, 3])
+def test_fwd_dx_many_groups(G, placement, kernel):
+    """130 groups (a partly filled third chunk of 64 in the prologue's
+    register scan) and 300 (past the 256 held in registers: the two-pass
+    work-item lookup): the forward and dX against the oracle, with empty
+    groups and rows past the total."""
+    r = workloads.rng(161, G)
+    gs = r.integers(0, 14, G).astype(np.int64)
+    gs[::11] = 0
+    M = int(gs.sum()) + 29
+    wl = workloads.custom(M, 256, 256, gs.tolist(), seed=163 + G, w_std=0.05, with_dy=True)
+    total = int(gs.sum())
+    cfg = {"kernel": kernel, "placement": placement}
+    out = torch.full((M, 256), float("nan"), dtype=torch.bfloat16, device=DEV)
+    with tile_config(gmm.OP_BF16_FWD, cfg):
+        gmm.gmm_bf16_fwd(wl.x.to(DEV), wl.w.to(DEV), _gs(wl), out=out)
+    o = to_np64(out)
+    assert (o[total:] == 0).all()
+    assert_bf16_parity(o, oracle.gmm(workloads.as_f32(wl.x), workloads.as_f32(wl.w), wl.group_sizes),
+                       "fwd G=%d" % G)
+    dx = torch.full((M, 256), float("nan"), dtype=torch.bfloat16, device=DEV)
+    with tile_config(gmm.OP_DX, cfg):
+        gmm.gmm_bf16_dx(wl.dy.to(DEV), wl.w.to(DEV), _gs(wl), out=dx)
+    o = to_np64(dx)
+    assert (o[total:] == 0).all()
+    assert_bf16_parity(o, oracle.gmm_dx(workloads.as_f32(wl.dy), workloads.as_f32(wl.w), wl.group_sizes),
+                       "dx G=%d" % G)

@@ -186,3 +186,23 @@ def test_bench_launch_configuration(name):
     total = int(wl.group_sizes.sum())
     assert (o[total:] == 0).all()
     assert_fp8_parity(o, ref, name + " bench launch")
+
+
+@pytest.mark.parametrize("G", [130, 300])
+@pytest.mark.parametrize("N", [128, 512])
+def test_groups_past_one_and_four_chunks(G, N):
+    """130 groups (a partly filled third chunk of 64 in the prologue's
+    register scan) and 300 (past the 256 held in registers: the two-pass
+    work-item lookup), with empty groups and rows past the total: every
+    output row against the oracle, with and without the in-kernel codes."""
+    r = workloads.rng(151, G)
+    gs = r.integers(0, 14, G).astype(np.int64)
+    gs[::11] = 0
+    M = int(gs.sum()) + 29
+    wl = workloads.custom(M, 256, N, gs.tolist(), seed=157 + G + N)
+    check_full(wl, torch.bfloat16)
+    out, _, _ = run_fp8(wl, torch.bfloat16, want_q=False)
+    ref, _, _ = oracle_fp8(wl)
+    o = to_np64(out)
+    assert (o[int(gs.sum()):] == 0).all()
+    assert_fp8_parity(o, ref, "G=%d N=%d" % (G, N))
