@@ -409,7 +409,7 @@ def main() -> int:
     if args.counter_pass:
         return counter_pass()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(expert parallelism would run this per-GPU kernel on each rank's shard)",
               file=sys.stderr)
         return 2
