@@ -1,7 +1,8 @@
 """Seeded random sweep of small grouped problems on the GPU against the oracle:
 random M, K, N, G, group-size patterns (empty groups, size-1 groups, one
 dominant group, rows past the total), LHS dtype and output dtype, for the
-FP8-weight, MXFP4-weight and int4-weight forwards.  In-kernel codes and scales bit for
+FP8-weight, MXFP4-weight and int4-weight forwards and the fused gate+up
+SwiGLU forward.  In-kernel codes and scales bit for
 bit (in the half of the FP8 cases that ask for them); outputs within |gpu - ref| <= 1e-3 max(1, rms(ref)) + 1e-2 |ref| and
 SQNR > 40 dB (the weights' scale is drawn up to N(0, 1), where outputs are
 ~20x those of the pages' normalised data, so the absolute term scales with
@@ -21,13 +22,7 @@ DEV = "cuda:0"
 CASES = 24
 
 
-def random_problem(seed):
-    r = workloads.rng(1000 + seed, 9)
-    K = 128 * int(r.integers(1, 9))
-    N = 128 * int(r.choice([1, 2, 3, 4, 6, 8]))
-    G = int(r.choice([1, 2, 3, 7, 16, 40]))
-    total = int(r.integers(1, 900))
-    pattern = seed % 4
+def group_sizes(r, G, total, pattern):
     if pattern == 0:                                     # uniform routing
         gs = r.multinomial(total, np.full(G, 1.0 / G))
     elif pattern == 1:                                   # one dominant expert
@@ -41,7 +36,16 @@ def random_problem(seed):
     else:                                                # Zipf-like popularity
         p = 1.0 / np.arange(1, G + 1) ** 1.1
         gs = r.multinomial(total, p / p.sum())
-    gs = gs.astype(np.int32)
+    return gs.astype(np.int32)
+
+
+def random_problem(seed):
+    r = workloads.rng(1000 + seed, 9)
+    K = 128 * int(r.integers(1, 9))
+    N = 128 * int(r.choice([1, 2, 3, 4, 6, 8]))
+    G = int(r.choice([1, 2, 3, 7, 16, 40]))
+    total = int(r.integers(1, 900))
+    gs = group_sizes(r, G, total, seed % 4)
     M = int(gs.sum()) + int(r.integers(0, 70))           # rows past the total
     dtype = torch.bfloat16 if seed % 3 else torch.float32
     out_dtype = torch.float32 if seed % 2 else torch.bfloat16
@@ -107,3 +111,44 @@ def test_int4_forward_random(seed):
     o = to_np64(out)
     assert (o[int(wl.group_sizes.sum()):] == 0).all()
     assert_fp8_parity_scaled(o, ref, "random int4 %d (M=%d K=%d N=%d G=%d)" % (seed, wl.M, wl.K, wl.N, wl.G))
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_swiglu_forward_random(seed):
+    """Fused gate+up ("实现差距：GMM Kernel（V1 vs V2）", sections 3.5 and 4.2):
+    N activation columns (a multiple of 256) from [G,K,2N] gate|up weights;
+    with fp32 output the 1x128 re-quantisation of the activation too, bit for
+    bit against the oracle's quantiser applied to the kernel's fp32 values."""
+    r = workloads.rng(5000 + seed, 9)
+    K = 128 * int(r.integers(1, 9))
+    N = 256 * int(r.integers(1, 4))
+    G = int(r.choice([1, 2, 3, 7, 16, 40]))
+    gs = group_sizes(r, G, int(r.integers(1, 900)), seed % 4)
+    M = int(gs.sum()) + int(r.integers(0, 70))
+    dtype = torch.bfloat16 if seed % 3 else torch.float32
+    out_dtype = torch.float32 if seed % 2 else torch.bfloat16
+    wl = workloads.custom(M, K, 2 * N, gs, seed=6000 + seed, w_std=float(r.choice([0.02, 0.05, 0.5])),
+                          dtype=dtype)
+    rq, rs = gmm.gmm_quantize_rhs(wl.w.to(DEV))
+    g = torch.from_numpy(gs).to(DEV)
+    out = torch.full((M, N), float("nan"), dtype=out_dtype, device=DEV)
+    with_act = out_dtype == torch.float32
+    aq = asc = None
+    if with_act:
+        aq = torch.full((M, N), 0x55, dtype=torch.uint8, device=DEV)
+        asc = torch.full((M, N // 128), float("nan"), dtype=torch.float32, device=DEV)
+    gmm.gmm_fp8_fwd_swiglu(wl.x.to(DEV), rq, rs, g, out=out, act_q=aq, act_scale=asc)
+    torch.cuda.synchronize()
+    ql, sl = oracle.quantize_lhs(workloads.as_f32(wl.x))
+    qr, sr = oracle.quantize_rhs(workloads.as_f32(wl.w))
+    ref = oracle.gmm_fp8_swiglu(ql, sl, qr, sr, gs)
+    o = to_np64(out)
+    total = int(gs.sum())
+    what = "random swiglu %d (M=%d K=%d N=%d G=%d)" % (seed, M, K, N, G)
+    assert (o[total:] == 0).all(), what
+    assert_fp8_parity_scaled(o, ref, what)
+    if with_act:
+        q_ref, s_ref = oracle.quantize_lhs(out[:total].float().cpu().numpy())
+        assert np.array_equal(aq[:total].cpu().numpy(), q_ref), what
+        assert np.array_equal(asc[:total].cpu().numpy().view(np.uint32), s_ref.view(np.uint32)), what
+        assert (aq[total:].cpu().numpy() == 0).all() and (asc[total:].cpu().numpy() == 0).all(), what
