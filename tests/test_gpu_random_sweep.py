@@ -1,9 +1,10 @@
 """Seeded random sweep of small grouped problems on the GPU against the oracle:
 random M, K, N, G, group-size patterns (empty groups, size-1 groups, one
-dominant group, rows past the total), LHS dtype and output dtype, for the
-FP8-weight, MXFP4-weight and int4-weight forwards and the fused gate+up
-SwiGLU forward.  In-kernel codes and scales bit for
-bit (in the half of the FP8 cases that ask for them); outputs within |gpu - ref| <= 1e-3 max(1, rms(ref)) + 1e-2 |ref| and
+dominant group, rows past the total), LHS dtype (bf16, fp32, or E4M3 codes
+with scales) and output dtype, for the FP8-weight, MXFP4-weight and
+int4-weight forwards and the fused gate+up SwiGLU forward.  In-kernel codes
+and scales bit for bit (in the half of the FP8 cases that ask for them);
+outputs within |gpu - ref| <= 1e-3 max(1, rms(ref)) + 1e-2 |ref| and
 SQNR > 40 dB (the weights' scale is drawn up to N(0, 1), where outputs are
 ~20x those of the pages' normalised data, so the absolute term scales with
 the output's RMS); rows past the total zero.
@@ -79,6 +80,27 @@ def test_fp8_forward_random(seed):
     o = to_np64(out)
     assert (o[total:] == 0).all()
     assert_fp8_parity_scaled(o, ref, "random %d (M=%d K=%d N=%d G=%d)" % (seed, wl.M, wl.K, wl.N, wl.G))
+
+
+@pytest.mark.parametrize("seed", range(CASES))
+def test_fp8_forward_prequantised_random(seed):
+    """The same problems with the LHS handed in as E4M3 codes and 1x128
+    scales (gmm_quantize_lhs output): the kernels that skip the in-kernel
+    quantisation, against the same oracle product."""
+    wl, out_dtype = random_problem(seed)
+    rq, rs = gmm.gmm_quantize_rhs(wl.w.to(DEV))
+    gs = torch.from_numpy(wl.group_sizes).to(DEV)
+    ql_d, sl_d = gmm.gmm_quantize_lhs(wl.x.to(DEV))
+    out = torch.full((wl.M, wl.N), float("nan"), dtype=out_dtype, device=DEV)
+    gmm.gmm_fp8_fwd(ql_d, rq, rs, gs, lhs_scale=sl_d, out=out)
+    torch.cuda.synchronize()
+    ql, sl = oracle.quantize_lhs(workloads.as_f32(wl.x))
+    assert np.array_equal(ql_d.cpu().numpy(), ql) and np.array_equal(sl_d.cpu().numpy(), sl)
+    qr, sr = oracle.quantize_rhs(workloads.as_f32(wl.w))
+    ref = oracle.gmm_fp8(ql, sl, qr, sr, wl.group_sizes)
+    o = to_np64(out)
+    assert (o[int(wl.group_sizes.sum()):] == 0).all()
+    assert_fp8_parity_scaled(o, ref, "random prequantised %d (M=%d K=%d N=%d G=%d)" % (seed, wl.M, wl.K, wl.N, wl.G))
 
 
 @pytest.mark.parametrize("seed", range(CASES))
